@@ -1,0 +1,224 @@
+"""Block manager model — oracle for the host allocator.
+
+What the pages fix:
+* [course] §2 "The insight": a pool of same-size physical blocks in GPU
+  memory; blocks are allocated on demand as a sequence grows and freed
+  immediately when it finishes; each sequence's block table maps its
+  logical positions to scattered physical blocks. At most one block per
+  sequence is partially filled.
+* [note] 最小模型 ("minimal model"): growing a request only allocates one more
+  block; a finished request releases its own blocks.
+* [note] section "block size 是容量与 kernel 的共同参数": a request of
+  ``seq_len`` tokens needs ceil(seq_len / block_size) blocks.
+* [course] §2 "The bonus: block sharing (copy-on-write)" and §3 "Mental
+  Model": sequences with a common prefix point at the same physical blocks
+  (seq A -> [b3][b7][b1], seq B -> [b3][b9]); only the differing block is
+  copied when they diverge.
+* [note] section prefix sharing 的边界: sharing is governed by reference
+  counts and copy-on-write happens only when a branch writes.
+* [course] §4 "Hitchhiker's Guide" and §11: the pool is finite; at the
+  limit the caller queues or rejects.
+
+Readings where the pages leave the choice open:
+* Which free block is handed out: a LIFO stack whose first pop returns
+  ``free_order[0]``; released blocks are pushed back, the sequence's blocks
+  in logical order (so its last block is the next one popped).
+* Copy-on-write: when a sequence writes into its partially filled last
+  block while that block's refcount is above 1, the WRITER gets a fresh
+  block (popped before its growth blocks) and the pair (old, new) is
+  reported for a whole-block copy; the other holders keep the old block;
+  the last holder writes in place. Full blocks are never written.
+* Pool exhaustion: the whole request fails and nothing changes.
+* A batch of allocations is all-or-nothing and may not name a sequence
+  twice; requests are applied in the given order.
+
+This model applies a request to a copy of the state and commits only if it
+completes — all-or-nothing by construction.
+"""
+from __future__ import annotations
+
+import copy
+from typing import Dict, List, Sequence, Tuple
+
+
+class AllocError(Exception):
+    code = "error"
+
+
+class OutOfBlocks(AllocError):
+    code = "out_of_blocks"
+
+
+class UnknownSeq(AllocError):
+    code = "unknown_seq"
+
+
+class SeqExists(AllocError):
+    code = "seq_exists"
+
+
+class InvalidArgument(AllocError):
+    code = "invalid_argument"
+
+
+def blocks_for(length: int, block_size: int) -> int:
+    """ceil(length / block_size) ([note] block size section)."""
+    return -(-int(length) // int(block_size))
+
+
+def capacity(pool_blocks: int, context_len: int, block_size: int) -> int:
+    """Concurrent sequences of ``context_len`` tokens a pool holds:
+    pool_blocks // blocks_per_seq ([course] §4 and §11: seqs ~ pool
+    blocks / blocks per sequence)."""
+    return int(pool_blocks) // blocks_for(context_len, block_size)
+
+
+def naive_waste(used_tokens: int, reserved_tokens: int) -> float:
+    """Fraction of a contiguous max-context reservation left unused
+    ([course] §2 primer, internal fragmentation)."""
+    return 1.0 - used_tokens / reserved_tokens
+
+
+def paged_waste_tokens(length: int, block_size: int) -> int:
+    """Unused slots of a paged sequence: the tail of its last block."""
+    return blocks_for(length, block_size) * block_size - int(length)
+
+
+class _State:
+    def __init__(self, num_blocks: int, free_order: Sequence[int]):
+        self.stack: List[int] = list(reversed([int(b) for b in free_order]))  # top = end
+        self.refcnt: List[int] = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lens: Dict[int, int] = {}
+        self.cow_copies = 0
+        self.forks = 0
+
+
+class BlockAllocatorModel:
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise InvalidArgument("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise InvalidArgument("free_order must be a permutation of 0..num_blocks-1")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        self.st = _State(num_blocks, order)
+
+    # -- queries -------------------------------------------------------
+    @property
+    def refcnt(self) -> List[int]:
+        return list(self.st.refcnt)
+
+    @property
+    def free_stack(self) -> List[int]:
+        """Free block ids from the bottom of the stack to its top."""
+        return list(self.st.stack)
+
+    def table(self, seq: int) -> List[int]:
+        if seq not in self.st.tables:
+            raise UnknownSeq(seq)
+        return list(self.st.tables[seq])
+
+    def length(self, seq: int) -> int:
+        if seq not in self.st.lens:
+            raise UnknownSeq(seq)
+        return self.st.lens[seq]
+
+    def seqs(self) -> List[int]:
+        return list(self.st.tables)
+
+    def stats(self) -> dict:
+        rc = self.st.refcnt
+        return dict(num_blocks=self.num_blocks, num_free=len(self.st.stack),
+                    num_used=sum(1 for r in rc if r > 0), num_shared=sum(1 for r in rc if r > 1),
+                    cow_copies=self.st.cow_copies, forks=self.st.forks,
+                    num_seqs=len(self.st.tables))
+
+    # -- operations ----------------------------------------------------
+    @staticmethod
+    def _pop(st: _State) -> int:
+        if not st.stack:
+            raise OutOfBlocks("pool exhausted")
+        return st.stack.pop()
+
+    def _grow(self, st: _State, seq: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
+        bs = self.block_size
+        if n < 0:
+            raise InvalidArgument("negative token count")
+        if seq not in st.tables:
+            st.tables[seq] = []
+            st.lens[seq] = 0
+        table = st.tables[seq]
+        length = st.lens[seq]
+        cows: List[Tuple[int, int]] = []
+        if n > 0 and length % bs != 0 and st.refcnt[table[-1]] > 1:
+            old = table[-1]
+            new = self._pop(st)
+            st.refcnt[old] -= 1
+            st.refcnt[new] = 1
+            table[-1] = new
+            cows.append((old, new))
+            st.cow_copies += 1
+        while len(table) < blocks_for(length + n, bs):
+            blk = self._pop(st)
+            st.refcnt[blk] = 1
+            table.append(blk)
+        slots = [table[t // bs] * bs + t % bs for t in range(length, length + n)]
+        st.lens[seq] = length + n
+        return slots, cows
+
+    def alloc(self, seq: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
+        """Room for ``n`` more tokens of ``seq`` (created if unknown).
+        Returns (slots of the new tokens, copy-on-write pairs)."""
+        return self.alloc_batch([seq], [n])
+
+    def alloc_batch(self, seqs: Sequence[int], ns: Sequence[int]):
+        if len(seqs) != len(ns):
+            raise InvalidArgument("length mismatch")
+        if len(set(seqs)) != len(seqs):
+            raise InvalidArgument("a sequence appears twice in one batch")
+        st = copy.deepcopy(self.st)
+        slots: List[int] = []
+        cows: List[Tuple[int, int]] = []
+        for seq, n in zip(seqs, ns):
+            s_slots, s_cows = self._grow(st, seq, int(n))
+            slots += s_slots
+            cows += s_cows
+        self.st = st
+        return slots, cows
+
+    def fork(self, parent: int, child: int) -> None:
+        """``child`` starts as a copy of ``parent``'s table; every block gains
+        one reference."""
+        if child in self.st.tables:
+            raise SeqExists(child)
+        if parent not in self.st.tables:
+            raise UnknownSeq(parent)
+        self.st.tables[child] = list(self.st.tables[parent])
+        self.st.lens[child] = self.st.lens[parent]
+        for blk in self.st.tables[child]:
+            self.st.refcnt[blk] += 1
+        self.st.forks += 1
+
+    def free(self, seq: int) -> None:
+        """Release ``seq``: each block (logical order) loses one reference and
+        goes back on the free stack when none is left."""
+        if seq not in self.st.tables:
+            raise UnknownSeq(seq)
+        for blk in self.st.tables.pop(seq):
+            self.st.refcnt[blk] -= 1
+            if self.st.refcnt[blk] == 0:
+                self.st.stack.append(blk)
+        del self.st.lens[seq]
+
+    def pack(self, seqs: Sequence[int], max_blocks: int, pad: int = -1):
+        """(tables [n][max_blocks] padded with ``pad``, context lengths [n])."""
+        tables, lens = [], []
+        for seq in seqs:
+            t = self.table(seq)
+            if len(t) > max_blocks:
+                raise InvalidArgument("table wider than max_blocks")
+            tables.append(t + [pad] * (max_blocks - len(t)))
+            lens.append(self.length(seq))
+        return tables, lens
