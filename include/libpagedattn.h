@@ -1,0 +1,261 @@
+/*
+ * libpagedattn — paged KV cache and PagedAttention decode for AMD MI355X (gfx950).
+ *
+ * A plain C ABI: host pointers, device pointers and sizes only. Device
+ * memory is always owned by the caller; the library never allocates device
+ * memory. Host block-manager state is owned by the library behind an opaque
+ * handle.
+ *
+ * Pages cited (by title and section):
+ *   [course] "PagedAttention" — Phase 7 · Document 04 · Production Serving
+ *            (ai-engineer-zt0.pages.dev, llm-mastery/07-production-serving)
+ *   [note]   "PagedAttention" — LLM study note in Chinese
+ *            (lux-666-github-io.pages.dev)
+ *   [intent] "Building Intent-Aware Configuration for LLM Serving"
+ *            (marcusacosta.dev)
+ *
+ * Error convention ([intent] "Enforcing policy at the device boundary",
+ * "Extending the Rust SDK contract"): an explicit request either does what
+ * it asks or returns a specific status with a message from pa_last_error();
+ * nothing silently falls back to another path. Unsupported shapes or dtypes
+ * return PA_ERR_UNSUPPORTED, never a slower substitute. Every status-
+ * returning call validates its arguments before it touches any state or
+ * launches any kernel; on an error return no state has changed.
+ *
+ * Threading: a pa_bm handle is not thread-safe (the caller serialises
+ * calls on one handle). Device calls are thread-safe and asynchronous on
+ * the caller's stream (a hipStream_t passed as void*; NULL = the default
+ * stream). They never synchronise the host unless the environment
+ * variable PA_DEBUG=1 is set, in which case device-side inputs are copied
+ * back and validated before launch (slow; for debugging only).
+ */
+#ifndef LIBPAGEDATTN_H
+#define LIBPAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad shape, misaligned pointer */
+  PA_ERR_OUT_OF_BLOCKS = 2,    /* the pool cannot hold the request; nothing changed */
+  PA_ERR_UNKNOWN_SEQ = 3,      /* the sequence id is not live */
+  PA_ERR_SEQ_EXISTS = 4,       /* fork target already live */
+  PA_ERR_UNSUPPORTED = 5,      /* dtype / head_dim / block_size / group combination not built */
+  PA_ERR_DEVICE = 6,           /* a HIP call failed (launch error, bad stream) */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F16 = 0,      /* IEEE binary16 */
+  PA_BF16 = 1,     /* bfloat16 */
+  PA_F32 = 2,      /* IEEE binary32 */
+  PA_FP8_E4M3 = 3, /* OCP FP8 E4M3 (e4m3fn: bias 7, max 448, no inf), per-tensor scale */
+} pa_dtype;
+
+/* Static string for a status code. */
+const char* pa_status_string(pa_status status);
+/* Detail of the last error on the calling thread ("" if none). Valid until
+ * the next library call on this thread. */
+const char* pa_last_error(void);
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Host block manager.
+ *
+ * [course] §2 "The insight": the KV cache is a pool of same-size physical
+ * blocks; blocks are allocated on demand as a sequence grows and freed as
+ * soon as it finishes; each sequence's block table maps its logical token
+ * positions to scattered physical blocks. [note] 最小模型: growth takes one
+ * more block, release returns the sequence's own blocks; [note] block-size
+ * section: a sequence of L tokens holds ceil(L / block_size) blocks.
+ * [course] §2 "The bonus: block sharing (copy-on-write)" and [note] prefix
+ * sharing section: forked sequences share physical blocks under reference
+ * counts, and a block is copied only when a branch writes into it.
+ *
+ * Choices the pages leave open, fixed here:
+ *  - Free blocks form a LIFO stack. A fresh manager pops
+ *    initial_free_order[0] first (NULL = 0, 1, 2, ...). pa_free pushes a
+ *    sequence's blocks in logical order as their refcount reaches zero.
+ *  - Copy-on-write: when a sequence appends to a partially filled last
+ *    block whose refcount is > 1, the writer receives a fresh block (popped
+ *    before any growth blocks) and a (src, dst) pair is reported; the
+ *    caller must run pa_copy_blocks on those pairs before
+ *    pa_reshape_and_cache writes into dst (same stream order suffices).
+ *  - Allocation is all-or-nothing: PA_ERR_OUT_OF_BLOCKS leaves every
+ *    table, refcount and the free stack unchanged; the caller queues,
+ *    rejects or preempts ([course] §11 "at the limit: queue/reject").
+ *  - A slot is phys_block * block_size + offset_in_block (int64).
+ * ---------------------------------------------------------------------- */
+typedef struct pa_bm pa_bm;
+
+typedef struct pa_bm_stats {
+  int32_t num_blocks; /* pool size */
+  int32_t num_free;   /* blocks on the free stack */
+  int32_t num_used;   /* blocks with refcount > 0 */
+  int32_t num_shared; /* blocks with refcount > 1 */
+  int32_t num_seqs;   /* live sequences */
+  int32_t reserved;
+  int64_t cow_copies; /* copy-on-write pairs reported so far */
+  int64_t forks;      /* successful pa_fork calls */
+} pa_bm_stats;
+
+/* Create a manager for a pool of num_blocks blocks of block_size tokens.
+ * initial_free_order: host int32[num_blocks], a permutation of
+ * 0..num_blocks-1 (copied), or NULL. *out receives the handle. */
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                       pa_bm** out);
+/* Destroy a manager (NULL is a no-op). */
+void pa_bm_destroy(pa_bm* bm);
+
+/* Make room for num_new_tokens (>= 0) more tokens of seq_id, creating the
+ * sequence if it is not live. slot_mapping: host int64[num_new_tokens]
+ * receives the slots of the new tokens in token order (may be NULL when
+ * num_new_tokens == 0). If the write needs a copy-on-write, *num_cow = 1
+ * and (*cow_src, *cow_dst) is the pair; otherwise *num_cow = 0. */
+pa_status pa_alloc(pa_bm* bm, int64_t seq_id, int32_t num_new_tokens, int64_t* slot_mapping,
+                   int32_t* cow_src, int32_t* cow_dst, int32_t* num_cow);
+
+/* pa_alloc for n distinct sequences at once, applied in array order and
+ * all-or-nothing as a whole. seq_ids: host int64[n]; num_new_tokens: host
+ * int32[n]; slot_mapping: host int64[sum(num_new_tokens)] receives each
+ * sequence's new slots, concatenated in array order; cow_pairs: host
+ * int32[n][2] receives (src, dst) pairs; *num_cow receives their count.
+ * A sequence id may appear only once (PA_ERR_INVALID_ARGUMENT). */
+pa_status pa_alloc_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n, const int32_t* num_new_tokens,
+                         int64_t* slot_mapping, int32_t* cow_pairs, int32_t* num_cow);
+
+/* Release seq_id: every block loses one reference ([note] 最小模型, release). */
+pa_status pa_free(pa_bm* bm, int64_t seq_id);
+
+/* child_id becomes a live sequence sharing every block of parent_id
+ * (refcount + 1 each); [course] §2 "The bonus", parallel sampling / beam. */
+pa_status pa_fork(pa_bm* bm, int64_t parent_id, int64_t child_id);
+
+/* Context length and block count of a live sequence (either may be NULL). */
+pa_status pa_seq_info(const pa_bm* bm, int64_t seq_id, int32_t* context_len, int32_t* num_blocks);
+
+/* Copy a live sequence's block table (logical order) into host
+ * int32[capacity]; *n receives its length. capacity < length ->
+ * PA_ERR_INVALID_ARGUMENT. */
+pa_status pa_seq_blocks(const pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_t capacity, int32_t* n);
+
+/* Pack the tables of n live sequences into host int32[n][max_blocks]
+ * (row i = seq_ids[i], padded with `pad`) and their lengths into host
+ * int32[n]. A table longer than max_blocks -> PA_ERR_INVALID_ARGUMENT
+ * (outputs unspecified). context_lens may be NULL. */
+pa_status pa_pack_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                               int32_t pad, int32_t* tables, int32_t* context_lens);
+
+pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out);
+/* Refcount of every block: host int32[num_blocks]. */
+pa_status pa_bm_refcounts(const pa_bm* bm, int32_t* out);
+/* Free stack from bottom to top (the top is popped next): host
+ * int32[capacity]; *n receives the count. */
+pa_status pa_bm_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity, int32_t* n);
+
+/* ------------------------------------------------------------------------
+ * Device KV pool descriptor (caller-owned device memory).
+ *
+ * [course] §2 "The insight": each physical block holds BLOCK tokens of K
+ * and V laid out K[BLOCK][HEADS][HEAD_DIM], V[BLOCK][HEADS][HEAD_DIM]. Here:
+ * element (blk, t, h, d) of K is at k[blk * block_stride + (t * num_kv_heads
+ * + h) * head_dim + d], and likewise for V with v. block_stride (elements)
+ * >= block_size * num_kv_heads * head_dim; separate K and V pools use
+ * exactly that, the page's interleaved KVBlock uses twice that with
+ * v = k + block_size * num_kv_heads * head_dim.
+ * Requirements: k and v 16-byte aligned; head_dim a multiple of 16;
+ * block_stride * element size a multiple of 16 bytes.
+ * fp8 pools store E4M3 codes of value / scale with one fp32 scale per
+ * tensor (k_scale, v_scale > 0); 16-bit pools ignore the scales.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_kv_cache {
+  void* k;
+  void* v;
+  int64_t block_stride;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  pa_dtype dtype; /* PA_F16, PA_BF16 or PA_FP8_E4M3 */
+  float k_scale;
+  float v_scale;
+} pa_kv_cache;
+
+/* Write the K/V rows of T new tokens into their slots ([course] §2 primer:
+ * each request's KV grows one token at a time; [course] §2 "The insight").
+ * k_new, v_new: device [T][num_kv_heads][head_dim], contiguous, 16-byte
+ * aligned, of src_dtype. slot_mapping: device int64[T]; token i goes to
+ * block slot/block_size, row slot%block_size; a negative slot skips the
+ * token; a slot >= num_blocks*block_size is skipped as well (PA_DEBUG=1
+ * reports it as PA_ERR_INVALID_ARGUMENT). 16-bit pools take sources of
+ * the same dtype and store the bits unchanged. fp8 pools take F16, BF16 or
+ * F32 sources and store encode(float32(x) * (1.0f / scale)): round to
+ * nearest even, saturating to +-448, NaN kept. Slots must be distinct
+ * (two tokens writing one slot race). */
+pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* k_new, const void* v_new,
+                               pa_dtype src_dtype, const int64_t* slot_mapping, int32_t T, void* stream);
+
+/* Copy whole blocks, K and V: block pairs[i][1] := block pairs[i][0]
+ * ([course] §2 "The bonus": only the differing block is copied; [note]
+ * prefix sharing section: copy-on-write when a branch writes). pairs:
+ * device int32[N][2] (src, dst). Pairs run concurrently: every dst must be
+ * distinct and no dst may be a src of the same call. Pairs with an id
+ * outside [0, num_blocks) are skipped (PA_DEBUG=1 reports them). N == 0 is
+ * a no-op. */
+pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* pairs, int32_t N, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention through the block tables ([course] §2 "The insight":
+ * the kernel follows the table to gather K/V during the dot product;
+ * [note] 最小模型: physical blocks are read in logical token order; [note]
+ * "why it works": the result is ordinary attention).
+ *
+ * For each sequence s < B with L = context_lens[s] and each query head h
+ * (KV head g = h / (Hq / num_kv_heads)):
+ *   z_t = scale * q[s][h] . K_t[g]          for t in [0, L)
+ *   out[s][h] = sum_t softmax(z)_t * V_t[g]  (zeros when L == 0)
+ * where token t of s is row t % block_size of physical block
+ * block_tables[s][t / block_size]. fp8 pools use K = code value * k_scale
+ * and V = code value * v_scale.
+ *
+ * q: device [B][Hq][head_dim] of q_dtype (F16 or BF16; for F16/BF16 pools
+ * it must equal the pool dtype). out: device [B][Hq][head_dim] of
+ * out_dtype (F16, BF16 or F32). block_tables: device int32[B][max_blocks];
+ * entries past ceil(L / block_size) are never read. context_lens: device
+ * int32[B]. max_context_len: an upper bound on every context_lens[s]
+ * (sizes the launch); it must be <= max_blocks * block_size. A sequence
+ * whose length exceeds it is processed only up to it (PA_DEBUG=1 reports
+ * it). Table entries outside [0, num_blocks) are read as block 0 (no
+ * out-of-bounds access; PA_DEBUG=1 reports them).
+ *
+ * partition_size: 0 = one workgroup per (sequence, KV head) walks the whole
+ * context; > 0 (a multiple of 16) splits each context into partitions of
+ * that many tokens, one workgroup each, merged by a log-sum-exp reduction.
+ * The split needs a workspace of pa_decode_workspace_size(...) bytes
+ * (device, 256-byte aligned, contents need no initialisation); 0 bytes
+ * otherwise (workspace may be NULL).
+ *
+ * Supported (else PA_ERR_UNSUPPORTED): head_dim 64 or 128; block_size 8,
+ * 16 or 32; Hq / num_kv_heads in {1, 2, 4, 8}; pool F16 with q F16, pool
+ * BF16 with q BF16, pool FP8_E4M3 with q BF16.
+ * ---------------------------------------------------------------------- */
+size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                                int32_t partition_size);
+
+pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
+                    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                    int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBPAGEDATTN_H */

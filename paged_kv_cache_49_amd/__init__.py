@@ -1,0 +1,323 @@
+"""Python binding for libpagedattn: paged KV cache and PagedAttention decode
+on AMD MI355X (gfx950).
+
+The functions here only marshal arguments (tensor pointers, dtype codes,
+the current HIP stream) into the C ABI declared in include/libpagedattn.h;
+every step of the path runs in the library's host C++ and HIP kernels.
+Device tensors come from PyTorch (memory and streams only). A missing
+library raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import PaBmStats, PaKvCache, lib
+
+__all__ = [
+    "PagedAttnError", "OutOfBlocks", "UnknownSeq", "SeqExists", "Unsupported", "InvalidArgument",
+    "DeviceError", "BlockManager", "KVCache", "reshape_and_cache", "copy_blocks", "decode",
+    "decode_workspace_size", "lib",
+]
+
+
+class PagedAttnError(RuntimeError):
+    status = -1
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class InvalidArgument(PagedAttnError):
+    pass
+
+
+class OutOfBlocks(PagedAttnError):
+    pass
+
+
+class UnknownSeq(PagedAttnError):
+    pass
+
+
+class SeqExists(PagedAttnError):
+    pass
+
+
+class Unsupported(PagedAttnError):
+    pass
+
+
+class DeviceError(PagedAttnError):
+    pass
+
+
+_ERRORS = {
+    _lib.PA_ERR_INVALID_ARGUMENT: InvalidArgument,
+    _lib.PA_ERR_OUT_OF_BLOCKS: OutOfBlocks,
+    _lib.PA_ERR_UNKNOWN_SEQ: UnknownSeq,
+    _lib.PA_ERR_SEQ_EXISTS: SeqExists,
+    _lib.PA_ERR_UNSUPPORTED: Unsupported,
+    _lib.PA_ERR_DEVICE: DeviceError,
+}
+
+
+def _status_name(status: int) -> str:
+    return lib().pa_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != _lib.PA_OK:
+        msg = lib().pa_last_error().decode()
+        raise _ERRORS.get(status, PagedAttnError)(status, msg)
+
+
+_DTYPE_CODES = {
+    torch.float16: _lib.PA_F16,
+    torch.bfloat16: _lib.PA_BF16,
+    torch.float32: _lib.PA_F32,
+    torch.uint8: _lib.PA_FP8_E4M3,
+    torch.float8_e4m3fn: _lib.PA_FP8_E4M3,
+}
+_NAMES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}
+
+
+def _code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE_CODES[t.dtype]
+    except KeyError:
+        raise Unsupported(_lib.PA_ERR_UNSUPPORTED, f"tensor dtype {t.dtype}") from None
+
+
+def _dev(t: Optional[torch.Tensor], name: str) -> int:
+    """Device pointer of a GPU tensor (never copies host data to the device)."""
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _host_i64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+
+
+def _host_i32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+# ---------------------------------------------------------------------------
+# host block manager
+
+
+class BlockManager:
+    """Owns a pa_bm handle (see include/libpagedattn.h for the semantics)."""
+
+    def __init__(self, num_blocks: int, block_size: int, initial_free_order=None):
+        h = ctypes.c_void_p()
+        order = None if initial_free_order is None else _host_i32(initial_free_order)
+        _check(lib().pa_bm_create(int(num_blocks), int(block_size), None if order is None else _ptr(order),
+                                  ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib().pa_bm_destroy(h)
+            self._h = None
+
+    def alloc(self, seq_id: int, num_new_tokens: int) -> Tuple[np.ndarray, list]:
+        slots = np.empty(max(int(num_new_tokens), 0), dtype=np.int64)
+        src, dst, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_alloc(self._h, int(seq_id), int(num_new_tokens), _ptr(slots) if slots.size else None,
+                              ctypes.byref(src), ctypes.byref(dst), ctypes.byref(n)))
+        return slots, ([(src.value, dst.value)] if n.value else [])
+
+    def alloc_batch(self, seq_ids, num_new_tokens, slot_out: Optional[np.ndarray] = None,
+                    cow_out: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """Returns (slots int64[sum], cow pairs int32[k][2]). ``slot_out`` /
+        ``cow_out`` may be preallocated (e.g. numpy views of pinned memory)."""
+        ids = _host_i64(seq_ids)
+        nt = _host_i32(num_new_tokens)
+        total = int(np.clip(nt, 0, None).sum())
+        slots = np.empty(total, np.int64) if slot_out is None else slot_out
+        cows = np.empty((max(len(ids), 1), 2), np.int32) if cow_out is None else cow_out
+        n = ctypes.c_int32()
+        _check(lib().pa_alloc_batch(self._h, _ptr(ids), len(ids), _ptr(nt), _ptr(slots) if total else None,
+                                    _ptr(cows), ctypes.byref(n)))
+        return slots[:total], cows[: n.value]
+
+    def free(self, seq_id: int) -> None:
+        _check(lib().pa_free(self._h, int(seq_id)))
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        _check(lib().pa_fork(self._h, int(parent_id), int(child_id)))
+
+    def seq_info(self, seq_id: int) -> Tuple[int, int]:
+        L, nb = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_seq_info(self._h, int(seq_id), ctypes.byref(L), ctypes.byref(nb)))
+        return L.value, nb.value
+
+    def seq_blocks(self, seq_id: int) -> list:
+        _, nb = self.seq_info(seq_id)
+        out = np.empty(max(nb, 1), np.int32)
+        n = ctypes.c_int32()
+        _check(lib().pa_seq_blocks(self._h, int(seq_id), _ptr(out), nb, ctypes.byref(n)))
+        return out[: n.value].tolist()
+
+    def pack(self, seq_ids, max_blocks: int, pad: int = -1, tables: Optional[np.ndarray] = None,
+             context_lens: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+        ids = _host_i64(seq_ids)
+        if tables is None:
+            tables = np.empty((len(ids), max_blocks), np.int32)
+        if context_lens is None:
+            context_lens = np.empty(len(ids), np.int32)
+        _check(lib().pa_pack_block_tables(self._h, _ptr(ids), len(ids), int(max_blocks), int(pad),
+                                          _ptr(tables), _ptr(context_lens)))
+        return tables, context_lens
+
+    def stats(self) -> dict:
+        s = PaBmStats()
+        _check(lib().pa_bm_stats_get(self._h, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in PaBmStats._fields_ if f != "reserved"}
+
+    def refcounts(self) -> list:
+        out = np.empty(self.num_blocks, np.int32)
+        _check(lib().pa_bm_refcounts(self._h, _ptr(out)))
+        return out.tolist()
+
+    def free_stack(self) -> list:
+        out = np.empty(self.num_blocks, np.int32)
+        n = ctypes.c_int32()
+        _check(lib().pa_bm_free_stack(self._h, _ptr(out), self.num_blocks, ctypes.byref(n)))
+        return out[: n.value].tolist()
+
+
+# ---------------------------------------------------------------------------
+# device pool
+
+
+@dataclasses.dataclass
+class KVCache:
+    """A paged KV pool in device memory: K and V tensors whose block b starts
+    at element b * block_stride, each block [block_size][num_kv_heads][head_dim]."""
+
+    k: torch.Tensor
+    v: torch.Tensor
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    head_dim: int
+    block_stride: int
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @classmethod
+    def allocate(cls, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                 kv_dtype: str = "bf16", device="cuda", layout: str = "split", k_scale: float = 1.0,
+                 v_scale: float = 1.0, fill: Optional[float] = None) -> "KVCache":
+        """``layout="split"``: separate K and V pools; ``"interleaved"``: one
+        buffer of blocks each holding K then V."""
+        dt = _NAMES[kv_dtype]
+        be = block_size * num_kv_heads * head_dim
+        if layout == "split":
+            k = torch.empty(num_blocks * be, dtype=dt, device=device)
+            v = torch.empty(num_blocks * be, dtype=dt, device=device)
+            stride = be
+        elif layout == "interleaved":
+            buf = torch.empty(num_blocks * 2 * be, dtype=dt, device=device)
+            k = buf
+            v = buf[be:]
+            stride = 2 * be
+        else:
+            raise ValueError(layout)
+        if fill is not None:
+            k.fill_(fill)
+            v.fill_(fill)
+        return cls(k, v, num_blocks, block_size, num_kv_heads, head_dim, stride, k_scale, v_scale)
+
+    @property
+    def dtype_code(self) -> int:
+        return _code(self.k)
+
+    def desc(self) -> PaKvCache:
+        if not (self.k.is_cuda and self.v.is_cuda):
+            raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, "pool tensors must be on the device")
+        return PaKvCache(self.k.data_ptr(), self.v.data_ptr(), int(self.block_stride), int(self.num_blocks),
+                         int(self.block_size), int(self.num_kv_heads), int(self.head_dim), self.dtype_code,
+                         float(self.k_scale), float(self.v_scale))
+
+    def block_view(self, which: str = "k") -> torch.Tensor:
+        """[num_blocks][block_size][num_kv_heads][head_dim] view of K or V."""
+        t = self.k if which == "k" else self.v
+        be = self.block_size * self.num_kv_heads * self.head_dim
+        return t.as_strided((self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim),
+                            (self.block_stride, self.num_kv_heads * self.head_dim, self.head_dim, 1))
+
+
+# ---------------------------------------------------------------------------
+# device operations
+
+
+def reshape_and_cache(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                      stream=None) -> None:
+    desc = cache.desc()
+    T = int(slot_mapping.numel())
+    _check(lib().pa_reshape_and_cache(ctypes.byref(desc), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                      _code(k_new), _dev(slot_mapping, "slot_mapping"), T, _stream(stream)))
+
+
+def copy_blocks(cache: KVCache, pairs: torch.Tensor, stream=None) -> None:
+    desc = cache.desc()
+    n = int(pairs.numel() // 2)
+    _check(lib().pa_copy_blocks(ctypes.byref(desc), _dev(pairs, "pairs") if n else None, n, _stream(stream)))
+
+
+def decode_workspace_size(batch: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                          partition_size: int) -> int:
+    return int(lib().pa_decode_workspace_size(int(batch), int(num_q_heads), int(head_dim),
+                                              int(max_context_len), int(partition_size)))
+
+
+def decode(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+           max_context_len: int, scale: float, partition_size: int = 0, out: Optional[torch.Tensor] = None,
+           out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Paged decode attention; returns ``out`` [B][Hq][D]. A workspace is
+    allocated with torch when the split needs one and none is given."""
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    need = decode_workspace_size(B, Hq, D, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    desc = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode(ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
+                           _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
+                           _dev(context_lens, "context_lens"), int(B), int(Hq), int(max_context_len),
+                           float(scale), int(partition_size), _dev(workspace, "workspace"), ws_bytes,
+                           _stream(stream)))
+    return out

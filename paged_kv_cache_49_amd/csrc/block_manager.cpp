@@ -1,0 +1,298 @@
+// Host block manager: free stack, refcounts, per-sequence block tables,
+// fork with copy-on-write, release.
+//
+// [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
+// [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
+//
+// [course] §2 "The insight": blocks are allocated on demand and freed as
+// soon as a sequence finishes; the per-sequence table maps logical positions
+// to physical blocks. [note] block-size section: ceil(L / block_size) blocks
+// per sequence. [course] §2 "The bonus" and [note] prefix sharing section:
+// forked sequences share blocks under refcounts; a block is copied only when
+// a branch writes into it. The choices the pages leave open (LIFO order,
+// writer-gets-the-copy, all-or-nothing) are documented in libpagedattn.h.
+//
+// Every mutating entry point first plans the whole request against the
+// current state (blocks needed, including copy-on-write copies, checked
+// against the free count), and only then applies it, so a failure leaves
+// the state untouched.
+#include <climits>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "internal.h"
+
+struct pa_bm {
+  struct Seq {
+    int32_t len = 0;
+    std::vector<int32_t> blocks;  // logical order
+  };
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // back() is popped next
+  std::vector<int32_t> refcnt;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t cow_copies = 0;
+  int64_t forks = 0;
+
+  int64_t blocks_for(int64_t len) const { return (len + block_size - 1) / block_size; }
+  int32_t pop() {
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    return b;
+  }
+};
+
+namespace {
+
+using pa::fail;
+
+#define PA_GUARD_BEGIN try {
+#define PA_GUARD_END                                                        \
+  }                                                                         \
+  catch (const std::bad_alloc&) {                                           \
+    return fail(PA_ERR_INVALID_ARGUMENT, "host memory allocation failed");  \
+  }
+
+pa_status plan_and_apply(pa_bm* bm, const int64_t* ids, int32_t n, const int32_t* ntok, int64_t* slots,
+                         int32_t* cow_pairs, int32_t* num_cow) {
+  const int32_t bs = bm->block_size;
+  // ---- plan: validate and count blocks (growth + copy-on-write copies)
+  std::unordered_set<int64_t> seen;
+  seen.reserve(static_cast<size_t>(n) * 2);
+  std::unordered_map<int32_t, int32_t> pending;  // shared tail -> copies already planned from it
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (ntok[i] < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_new_tokens[%d] = %d is negative", i, ntok[i]);
+    if (!seen.insert(ids[i]).second)
+      return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld appears twice in one batch", (long long)ids[i]);
+    auto it = bm->seqs.find(ids[i]);
+    const int64_t len = it == bm->seqs.end() ? 0 : it->second.len;
+    if (len + ntok[i] > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld would exceed INT32_MAX tokens", (long long)ids[i]);
+    need += bm->blocks_for(len + ntok[i]) - bm->blocks_for(len);
+    if (ntok[i] > 0 && len % bs != 0) {
+      const int32_t tail = it->second.blocks.back();
+      int32_t& already = pending[tail];
+      if (bm->refcnt[tail] - already > 1) {
+        ++need;
+        ++already;
+      }
+    }
+  }
+  if (need > static_cast<int64_t>(bm->free_stack.size()))
+    return fail(PA_ERR_OUT_OF_BLOCKS, "request needs %lld blocks, %zu free of %d", (long long)need,
+                bm->free_stack.size(), bm->num_blocks);
+
+  // ---- apply: cannot fail from here on (capacity reserved up front)
+  int32_t ncow = 0;
+  int64_t out = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    pa_bm::Seq& s = bm->seqs[ids[i]];
+    const int32_t add = ntok[i];
+    if (add > 0 && s.len % bs != 0 && bm->refcnt[s.blocks.back()] > 1) {
+      const int32_t old = s.blocks.back();
+      const int32_t fresh = bm->pop();
+      --bm->refcnt[old];
+      bm->refcnt[fresh] = 1;
+      s.blocks.back() = fresh;
+      cow_pairs[2 * ncow] = old;
+      cow_pairs[2 * ncow + 1] = fresh;
+      ++ncow;
+      ++bm->cow_copies;
+    }
+    const int64_t want = bm->blocks_for(static_cast<int64_t>(s.len) + add);
+    while (static_cast<int64_t>(s.blocks.size()) < want) {
+      const int32_t b = bm->pop();
+      bm->refcnt[b] = 1;
+      s.blocks.push_back(b);
+    }
+    for (int32_t t = s.len; t < s.len + add; ++t)
+      slots[out++] = static_cast<int64_t>(s.blocks[t / bs]) * bs + t % bs;
+    s.len += add;
+  }
+  *num_cow = ncow;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order, pa_bm** out) {
+  pa::clear_error();
+  if (out == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks = %d must be positive", num_blocks);
+  if (block_size <= 0 || block_size > (1 << 20))
+    return fail(PA_ERR_INVALID_ARGUMENT, "block_size = %d must be in [1, 2^20]", block_size);
+  PA_GUARD_BEGIN
+  pa_bm* bm = new pa_bm();
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->refcnt.assign(num_blocks, 0);
+  bm->free_stack.resize(num_blocks);
+  if (initial_free_order != nullptr) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = initial_free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete bm;
+        return fail(PA_ERR_INVALID_ARGUMENT, "initial_free_order is not a permutation (entry %d = %d)", i, b);
+      }
+      seen[b] = 1;
+    }
+  }
+  // the stack's top (back) is the first block handed out
+  for (int32_t i = 0; i < num_blocks; ++i)
+    bm->free_stack[num_blocks - 1 - i] = initial_free_order ? initial_free_order[i] : i;
+  *out = bm;
+  return PA_OK;
+  PA_GUARD_END
+}
+
+void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+pa_status pa_alloc_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n, const int32_t* num_new_tokens,
+                         int64_t* slot_mapping, int32_t* cow_pairs, int32_t* num_cow) {
+  pa::clear_error();
+  if (bm == nullptr || num_cow == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or num_cow is NULL");
+  if (n < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n = %d is negative", n);
+  if (n > 0 && (seq_ids == nullptr || num_new_tokens == nullptr || cow_pairs == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "seq_ids, num_new_tokens or cow_pairs is NULL");
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) total += num_new_tokens[i] > 0 ? num_new_tokens[i] : 0;
+  if (total > 0 && slot_mapping == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "slot_mapping is NULL");
+  PA_GUARD_BEGIN
+  return plan_and_apply(bm, seq_ids, n, num_new_tokens, slot_mapping, cow_pairs, num_cow);
+  PA_GUARD_END
+}
+
+pa_status pa_alloc(pa_bm* bm, int64_t seq_id, int32_t num_new_tokens, int64_t* slot_mapping, int32_t* cow_src,
+                   int32_t* cow_dst, int32_t* num_cow) {
+  pa::clear_error();
+  if (cow_src == nullptr || cow_dst == nullptr || num_cow == nullptr)
+    return fail(PA_ERR_INVALID_ARGUMENT, "cow_src, cow_dst or num_cow is NULL");
+  int32_t pair[2] = {-1, -1};
+  const pa_status st = pa_alloc_batch(bm, &seq_id, 1, &num_new_tokens, slot_mapping, pair, num_cow);
+  if (st == PA_OK) {
+    *cow_src = pair[0];
+    *cow_dst = pair[1];
+  }
+  return st;
+}
+
+pa_status pa_free(pa_bm* bm, int64_t seq_id) {
+  pa::clear_error();
+  if (bm == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm is NULL");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_id);
+  PA_GUARD_BEGIN
+  bm->free_stack.reserve(bm->num_blocks);
+  for (int32_t b : it->second.blocks)
+    if (--bm->refcnt[b] == 0) bm->free_stack.push_back(b);
+  bm->seqs.erase(it);
+  return PA_OK;
+  PA_GUARD_END
+}
+
+pa_status pa_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
+  pa::clear_error();
+  if (bm == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm is NULL");
+  if (bm->seqs.count(child_id)) return fail(PA_ERR_SEQ_EXISTS, "sequence %lld is already live", (long long)child_id);
+  auto it = bm->seqs.find(parent_id);
+  if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)parent_id);
+  PA_GUARD_BEGIN
+  pa_bm::Seq copy = it->second;
+  for (int32_t b : copy.blocks) ++bm->refcnt[b];
+  bm->seqs.emplace(child_id, std::move(copy));
+  ++bm->forks;
+  return PA_OK;
+  PA_GUARD_END
+}
+
+pa_status pa_seq_info(const pa_bm* bm, int64_t seq_id, int32_t* context_len, int32_t* num_blocks) {
+  pa::clear_error();
+  if (bm == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm is NULL");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_id);
+  if (context_len) *context_len = it->second.len;
+  if (num_blocks) *num_blocks = static_cast<int32_t>(it->second.blocks.size());
+  return PA_OK;
+}
+
+pa_status pa_seq_blocks(const pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_t capacity, int32_t* n) {
+  pa::clear_error();
+  if (bm == nullptr || n == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or n is NULL");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_id);
+  const int32_t len = static_cast<int32_t>(it->second.blocks.size());
+  if (capacity < len || (len > 0 && blocks == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "capacity %d < table length %d", capacity, len);
+  if (len > 0) std::memcpy(blocks, it->second.blocks.data(), sizeof(int32_t) * len);
+  *n = len;
+  return PA_OK;
+}
+
+pa_status pa_pack_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t pad,
+                               int32_t* tables, int32_t* context_lens) {
+  pa::clear_error();
+  if (bm == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm is NULL");
+  if (n < 0 || max_blocks < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n = %d, max_blocks = %d", n, max_blocks);
+  if (n > 0 && (seq_ids == nullptr || (tables == nullptr && max_blocks > 0)))
+    return fail(PA_ERR_INVALID_ARGUMENT, "seq_ids or tables is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_ids[i]);
+    const auto& blocks = it->second.blocks;
+    const int32_t len = static_cast<int32_t>(blocks.size());
+    if (len > max_blocks)
+      return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld holds %d blocks > max_blocks %d", (long long)seq_ids[i],
+                  len, max_blocks);
+    int32_t* row = tables + static_cast<int64_t>(i) * max_blocks;
+    if (len > 0) std::memcpy(row, blocks.data(), sizeof(int32_t) * len);
+    for (int32_t j = len; j < max_blocks; ++j) row[j] = pad;
+    if (context_lens) context_lens[i] = it->second.len;
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out) {
+  pa::clear_error();
+  if (bm == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or out is NULL");
+  pa_bm_stats s{};
+  s.num_blocks = bm->num_blocks;
+  s.num_free = static_cast<int32_t>(bm->free_stack.size());
+  for (int32_t r : bm->refcnt) {
+    s.num_used += r > 0;
+    s.num_shared += r > 1;
+  }
+  s.num_seqs = static_cast<int32_t>(bm->seqs.size());
+  s.cow_copies = bm->cow_copies;
+  s.forks = bm->forks;
+  *out = s;
+  return PA_OK;
+}
+
+pa_status pa_bm_refcounts(const pa_bm* bm, int32_t* out) {
+  pa::clear_error();
+  if (bm == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or out is NULL");
+  std::memcpy(out, bm->refcnt.data(), sizeof(int32_t) * bm->num_blocks);
+  return PA_OK;
+}
+
+pa_status pa_bm_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity, int32_t* n) {
+  pa::clear_error();
+  if (bm == nullptr || n == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or n is NULL");
+  const int32_t len = static_cast<int32_t>(bm->free_stack.size());
+  if (capacity < len || (len > 0 && out == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "capacity %d < free count %d", capacity, len);
+  if (len > 0) std::memcpy(out, bm->free_stack.data(), sizeof(int32_t) * len);
+  *n = len;
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// Device-side types and conversions shared by the HIP kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Storage-type tags (what one element of a pool / tensor is).
+struct F16 {
+  static constexpr int kBytes = 2;
+};
+struct BF16 {
+  static constexpr int kBytes = 2;
+};
+struct FP8 {
+  static constexpr int kBytes = 1;
+};
+
+// ---- scalar conversions --------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// OCP E4M3 (e4m3fn) encode of an fp32 value: round to nearest, ties to even,
+// saturate to +-448 (also for +-inf), NaN -> 0x7f with the sign kept.
+// Normal range [2^-6, 448): the 23-bit fp32 mantissa is rounded to 3 bits;
+// a carry out of the mantissa bumps the exponent, which is the right
+// result. Below 2^-6 the value is a multiple of 2^-9: scale by 2^9 (exact)
+// and round to an integer 0..8 (8 is the smallest normal, code 0x08).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;  // >= 448
+  if (a < 0x3c800000u) {                      // < 2^-6
+    const float f = __uint_as_float(a) * 512.0f;
+    return sign | static_cast<uint32_t>(__builtin_rintf(f));
+  }
+  const uint32_t e = (a >> 23) - 120u;  // biased e4m3 exponent, 1..15
+  uint32_t code = (e << 3) | ((a >> 20) & 7u);
+  const uint32_t rem = a & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ++code;
+  return sign | code;
+}
+
+// E4M3 byte -> fp32 value. Codes with a zero exponent field are m * 2^-9
+// (an exact int-to-float and power-of-two product); the others become an
+// fp32 with the same mantissa and the exponent rebased from bias 7 to 127.
+// (NaN codes are never stored from finite data; they decode to 480.)
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  const uint32_t em = byte & 0x7fu;
+  const float mag = em < 8u ? static_cast<float>(em) * 0x1p-9f : __uint_as_float((em << 20) + (120u << 23));
+  return (byte & 0x80u) ? -mag : mag;
+}
+
+// Four E4M3 bytes packed in a dword -> bf16 pairs (exact: every E4M3 value
+// is a bf16 value). Returns two dwords, each holding two bf16.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  u32x2 r;
+  r.x = (f32_to_bf16_bits(e4m3_to_f32(w & 0xffu))) | (f32_to_bf16_bits(e4m3_to_f32((w >> 8) & 0xffu)) << 16);
+  r.y = (f32_to_bf16_bits(e4m3_to_f32((w >> 16) & 0xffu))) | (f32_to_bf16_bits(e4m3_to_f32(w >> 24)) << 16);
+  return r;
+}
+
+// ---- wave-level reductions (wave64) ----------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---- 16x16x32 MFMA on 8-element operands held as 4 dwords -----------------
+
+template <typename T>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c);
+
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x32<BF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// Output element conversion by runtime dtype code (0 f16, 1 bf16, 2 f32).
+__device__ __forceinline__ void store_out(void* out, int64_t idx, int dtype, float v) {
+  if (dtype == 2) {
+    static_cast<float*>(out)[idx] = v;
+  } else if (dtype == 1) {
+    static_cast<uint16_t*>(out)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  } else {
+    static_cast<uint16_t*>(out)[idx] = static_cast<uint16_t>(f32_to_f16_bits(v));
+  }
+}
+
+}  // namespace pa

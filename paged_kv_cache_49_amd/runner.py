@@ -1,0 +1,123 @@
+"""Host-side sequencing of library calls for a batch of sequences.
+
+``PagedBatch`` ties one BlockManager (host tables) to one or more KVCache
+pools (e.g. one per attention layer, all indexed by the same block tables)
+and runs the serving loop's steps through the C ABI:
+
+  prefill(seq, K, V)   allocate L slots, write every layer's K/V rows
+  fork(parent, child)  share all blocks (refcounts)
+  step(...)            one decode step for a batch: allocate one slot per
+                       sequence (copy-on-write pairs included), upload the
+                       slot mapping / pairs / tables / lengths in a single
+                       host-to-device copy from pinned memory, then per layer
+                       pa_copy_blocks -> pa_reshape_and_cache -> pa_decode
+
+The metadata staging area is double-buffered: a buffer is refilled only
+after the copy issued from it two steps earlier has completed (HIP event),
+so the host can run ahead of the device without overwriting data in flight.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import BlockManager, KVCache, copy_blocks, decode, decode_workspace_size, reshape_and_cache
+
+
+class _Staging:
+    """Pinned host buffer + device buffer with the step metadata layout:
+    slots int64[B] | cow int32[B][2] | lens int32[B] | tables int32[B][W]."""
+
+    def __init__(self, batch: int, max_blocks: int, device):
+        self.B, self.W = batch, max_blocks
+        n32 = 2 * batch + 2 * batch + batch + batch * max_blocks
+        self.host = torch.empty(n32, dtype=torch.int32, pin_memory=True)
+        self.dev = torch.empty(n32, dtype=torch.int32, device=device)
+        h = self.host.numpy()
+        self.slots_np = h[: 2 * batch].view(np.int64)
+        self.cow_np = h[2 * batch: 4 * batch].reshape(batch, 2)
+        self.lens_np = h[4 * batch: 5 * batch]
+        self.tables_np = h[5 * batch:].reshape(batch, max_blocks)
+        d = self.dev
+        self.slots = d[: 2 * batch].view(torch.int64)
+        self.cow = d[2 * batch: 4 * batch].view(batch, 2)
+        self.lens = d[4 * batch: 5 * batch]
+        self.tables = d[5 * batch:].view(batch, max_blocks)
+        self.event: Optional[torch.cuda.Event] = None
+
+
+class PagedBatch:
+    def __init__(self, bm: BlockManager, caches: Sequence[KVCache], max_blocks: int, batch: int,
+                 device="cuda", pad: int = -1):
+        self.bm = bm
+        self.caches = list(caches)
+        self.max_blocks = int(max_blocks)
+        self.device = device
+        self.pad = int(pad)
+        self._stage = [_Staging(batch, self.max_blocks, device) for _ in range(2)]
+        self._turn = 0
+        self.last_cow_count = 0
+
+    # -- setup ---------------------------------------------------------------
+    def prefill(self, seq_id: int, ks: Sequence[torch.Tensor], vs: Sequence[torch.Tensor]) -> np.ndarray:
+        """Append len(ks[0]) tokens to ``seq_id`` and write layer i's rows
+        ks[i], vs[i] ([L][Hkv][D]). Returns the slots (host)."""
+        L = int(ks[0].shape[0])
+        slots, cows = self.bm.alloc(seq_id, L)
+        if cows:
+            pairs = torch.tensor(cows, dtype=torch.int32, device=self.device)
+            for c in self.caches:
+                copy_blocks(c, pairs)
+        if L:
+            sd = torch.from_numpy(slots).to(self.device)
+            for c, k, v in zip(self.caches, ks, vs):
+                reshape_and_cache(c, k.to(self.device, non_blocking=False).contiguous(),
+                                  v.to(self.device, non_blocking=False).contiguous(), sd)
+        return slots
+
+    def fork(self, parent: int, child: int) -> None:
+        self.bm.fork(parent, child)
+
+    def tables(self, seq_ids: Sequence[int]):
+        """Device (tables, lens) of ``seq_ids`` (synchronous upload)."""
+        t, l = self.bm.pack(seq_ids, self.max_blocks, self.pad)
+        return (torch.from_numpy(t).to(self.device), torch.from_numpy(l).to(self.device), int(l.max(initial=0)))
+
+    # -- one decode step -----------------------------------------------------
+    def step(self, seq_ids: np.ndarray, k_new: Sequence[torch.Tensor], v_new: Sequence[torch.Tensor],
+             q: Sequence[torch.Tensor], outs: Sequence[torch.Tensor], scale: float, partition_size: int,
+             workspace: Optional[torch.Tensor] = None, ones: Optional[np.ndarray] = None) -> int:
+        """Append one token to each of ``seq_ids`` in every layer and run
+        decode attention for it. Returns the batch's max context length."""
+        st = self._stage[self._turn]
+        self._turn ^= 1
+        if st.event is not None:
+            st.event.synchronize()
+        B = len(seq_ids)
+        if ones is None:
+            ones = np.ones(B, np.int32)
+        _, cows = self.bm.alloc_batch(seq_ids, ones, slot_out=st.slots_np, cow_out=st.cow_np)
+        ncow = len(cows)
+        self.bm.pack(seq_ids, self.max_blocks, self.pad, tables=st.tables_np, context_lens=st.lens_np)
+        max_ctx = int(st.lens_np[:B].max(initial=0))
+        st.dev.copy_(st.host, non_blocking=True)
+        if st.event is None:
+            st.event = torch.cuda.Event()
+        st.event.record()
+        self.last_cow_count = ncow
+        tables = st.tables if B == st.B else st.tables[:B]
+        lens = st.lens[:B]
+        for i, c in enumerate(self.caches):
+            if ncow:
+                copy_blocks(c, st.cow[:ncow])
+            reshape_and_cache(c, k_new[i], v_new[i], st.slots[:B])
+            decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i], workspace=workspace)
+        return max_ctx
+
+
+def workspace_for(batch: int, num_q_heads: int, head_dim: int, max_context_len: int, partition_size: int,
+                  device="cuda") -> Optional[torch.Tensor]:
+    n = decode_workspace_size(batch, num_q_heads, head_dim, max_context_len, partition_size)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None

@@ -1,0 +1,72 @@
+"""GPU-side setup for parity tests: builds a workload's cache through the
+library (block manager -> slot writes), and reads pools back as storage
+bits. Nothing here computes an expected value; expected values come from
+``oracle`` via tests/helpers.py."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_cache_49_amd as pa
+from paged_kv_cache_49_amd.runner import PagedBatch
+
+_TORCH = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+
+def say(*a):
+    """Name the case before a GPU step (flushed, so a fault still shows it)."""
+    print(*a, file=sys.stderr, flush=True)
+
+
+def poison_fill(kv_dtype: str):
+    """Fill value for unused pool memory: NaN (the E4M3 NaN code for fp8)."""
+    return 0x7F if kv_dtype == "fp8" else float("nan")
+
+
+def poison_bits(kv_dtype: str) -> int:
+    if kv_dtype == "fp8":
+        return 0x7F
+    return int(torch.full((1,), float("nan"), dtype=_TORCH[kv_dtype]).view(torch.int16).item()) & 0xFFFF
+
+
+def pool_bits(cache: pa.KVCache, which: str) -> np.ndarray:
+    t = cache.block_view(which).contiguous().cpu()
+    if t.dtype == torch.uint8:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def set_pool_bits(cache: pa.KVCache, which: str, bits: np.ndarray) -> None:
+    src = torch.from_numpy(np.ascontiguousarray(bits))
+    if cache.k.dtype != torch.uint8:
+        src = src.view(torch.int16).view(cache.k.dtype)
+    cache.block_view(which).copy_(src.to(cache.k.device))
+
+
+def device_setup(wl, layout="split", max_blocks=None, pad=-1, poison=True, free_order=None):
+    """Allocate and write every sequence of ``wl`` through the library.
+    Returns (batch, cache, tables, lens, max_ctx)."""
+    from tests.helpers import max_blocks_for
+    ks, vs = wl.kv_scales()
+    order = wl.free_order if free_order is None else free_order
+    bm = pa.BlockManager(wl.num_blocks, wl.block_size, order)
+    cache = pa.KVCache.allocate(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
+                                layout=layout, k_scale=ks, v_scale=vs,
+                                fill=poison_fill(wl.kv_dtype) if poison else 0)
+    if max_blocks is None:
+        max_blocks = max_blocks_for(wl.lengths, wl.block_size)
+    batch = PagedBatch(bm, [cache], max_blocks, wl.batch, pad=pad)
+    for s in range(wl.batch):
+        k, v = wl.kv(s)
+        batch.prefill(s, [k], [v])
+    tables, lens, max_ctx = batch.tables(list(range(wl.batch)))
+    return batch, cache, tables, lens, max_ctx
+
+
+def run_decode(wl, cache, tables, lens, max_ctx, partition_size, out_dtype=torch.float32):
+    q = wl.q().cuda()
+    out = pa.decode(cache, q, tables, lens, max_ctx, wl.scale, partition_size, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out.float().cpu().double().numpy()

@@ -20,12 +20,12 @@ def max_blocks_for(lengths, block_size, extra=0):
     return max(1, max((oalloc.blocks_for(int(n), block_size) for n in lengths), default=1) + extra)
 
 
-def oracle_setup(wl, max_blocks=None, pad=-1):
+def oracle_setup(wl, max_blocks=None, pad=-1, fill=0):
     """Allocate every sequence of ``wl`` in the allocator model and write its
     K/V through the slot model. Returns (alloc, kpool, vpool, tables, lens)."""
     alloc = oalloc.BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
-    kpool = ocache.empty_pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
-    vpool = ocache.empty_pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
+    kpool = ocache.empty_pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, fill)
+    vpool = ocache.empty_pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype, fill)
     ks, vs = wl.kv_scales()
     for s in range(wl.batch):
         slots, cows = alloc.alloc(s, int(wl.lengths[s]))

@@ -1,0 +1,221 @@
+"""The C ABI on the CPU: the library loads and exports every function the
+header declares; the host block manager matches the oracle's allocator model
+bit for bit (tables, slots, copy-on-write pairs, refcounts, free stack,
+statistics) under random operation sequences; host-side argument checks of
+the device entry points fail before any device call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import paged_kv_cache_49_amd as pa
+from paged_kv_cache_49_amd import _lib
+from oracle import allocator as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libpagedattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(pa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 19
+    handle = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), f"{n} declared in libpagedattn.h but not exported"
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+    assert pa.lib().pa_abi_version() == 1
+
+
+def test_status_strings():
+    for code, name in [(0, "PA_OK"), (2, "PA_ERR_OUT_OF_BLOCKS"), (5, "PA_ERR_UNSUPPORTED")]:
+        assert pa.lib().pa_status_string(code).decode() == name
+
+
+_EXC = {A.OutOfBlocks: pa.OutOfBlocks, A.UnknownSeq: pa.UnknownSeq, A.SeqExists: pa.SeqExists,
+        A.InvalidArgument: pa.InvalidArgument}
+
+
+def _same_state(bm: pa.BlockManager, m: A.BlockAllocatorModel):
+    assert bm.free_stack() == m.free_stack
+    assert bm.refcounts() == m.refcnt
+    for s in m.seqs():
+        assert bm.seq_blocks(s) == m.table(s)
+        assert bm.seq_info(s) == (m.length(s), len(m.table(s)))
+    st_lib, st_mod = bm.stats(), m.stats()
+    for k in ("num_blocks", "num_free", "num_used", "num_shared", "cow_copies", "forks", "num_seqs"):
+        assert st_lib[k] == st_mod[k], k
+
+
+def _run(fn_lib, fn_mod):
+    try:
+        r_mod = fn_mod()
+        err_mod = None
+    except A.AllocError as e:
+        err_mod = type(e)
+    if err_mod is None:
+        return fn_lib(), r_mod
+    with pytest.raises(_EXC[err_mod]):
+        fn_lib()
+    return None, None
+
+
+_ops = st.lists(
+    st.one_of(
+        st.tuples(st.just("alloc"), st.integers(0, 6), st.integers(0, 20)),
+        st.tuples(st.just("fork"), st.integers(0, 6), st.integers(0, 6)),
+        st.tuples(st.just("free"), st.integers(0, 6), st.just(0)),
+        st.tuples(st.just("batch"), st.lists(st.integers(0, 6), max_size=5),
+                  st.lists(st.integers(0, 9), min_size=5, max_size=5)),
+    ),
+    max_size=60,
+)
+
+
+@settings(max_examples=400, deadline=None)
+@given(ops=_ops, bs=st.sampled_from([1, 2, 4, 16]), nb=st.integers(1, 40), seed=st.integers(0, 2 ** 16))
+def test_block_manager_matches_model(ops, bs, nb, seed):
+    order = np.random.default_rng(seed).permutation(nb).tolist()
+    bm = pa.BlockManager(nb, bs, order)
+    m = A.BlockAllocatorModel(nb, bs, order)
+    for op in ops:
+        if op[0] == "alloc":
+            got, want = _run(lambda: bm.alloc(op[1], op[2]), lambda: m.alloc(op[1], op[2]))
+            if got is not None:
+                assert got[0].tolist() == want[0] and got[1] == want[1]
+        elif op[0] == "fork":
+            _run(lambda: bm.fork(op[1], op[2]), lambda: m.fork(op[1], op[2]))
+        elif op[0] == "free":
+            _run(lambda: bm.free(op[1]), lambda: m.free(op[1]))
+        else:
+            ids, ns = op[1], op[2][: len(op[1])]
+            got, want = _run(lambda: bm.alloc_batch(ids, ns), lambda: m.alloc_batch(ids, ns))
+            if got is not None:
+                assert got[0].tolist() == want[0]
+                assert [tuple(p) for p in got[1].tolist()] == want[1]
+        _same_state(bm, m)
+    live = m.seqs()
+    if live:
+        t_lib, l_lib = bm.pack(live, max_blocks=64, pad=-7)
+        t_mod, l_mod = m.pack(live, 64, -7)
+        assert t_lib.tolist() == t_mod and l_lib.tolist() == l_mod
+
+
+def test_worked_examples_through_the_library():
+    # "PagedAttention" LLM note, 最小模型: table 0->7, 1->2, 2->9
+    bm = pa.BlockManager(10, 16, [7, 2, 9, 0, 1, 3, 4, 5, 6, 8])
+    bm.alloc(0, 48)
+    assert bm.seq_blocks(0) == [7, 2, 9]
+    # course page §3 Mental Model: A -> [b3][b7][b1], B -> [b3][b9]
+    bm = pa.BlockManager(12, 16, [3, 7, 1, 9] + [b for b in range(12) if b not in (3, 7, 1, 9)])
+    bm.alloc(10, 16)
+    bm.fork(10, 11)
+    bm.alloc(10, 32)
+    bm.alloc(11, 16)
+    assert bm.seq_blocks(10) == [3, 7, 1] and bm.seq_blocks(11) == [3, 9] and bm.refcounts()[3] == 2
+    # course page §13 Q4: 10,000 blocks of 16 tokens hold 39 sequences of 4k tokens
+    bm = pa.BlockManager(10000, 16)
+    n = 0
+    with pytest.raises(pa.OutOfBlocks):
+        while True:
+            bm.alloc(n, 4096)
+            n += 1
+    assert n == 39 and bm.stats()["num_free"] == 16
+
+
+def test_block_manager_error_paths():
+    with pytest.raises(pa.InvalidArgument):
+        pa.BlockManager(0, 16)
+    with pytest.raises(pa.InvalidArgument):
+        pa.BlockManager(4, 0)
+    with pytest.raises(pa.InvalidArgument):
+        pa.BlockManager(3, 4, [0, 0, 1])
+    bm = pa.BlockManager(4, 4)
+    with pytest.raises(pa.InvalidArgument):
+        bm.alloc(1, -1)
+    with pytest.raises(pa.UnknownSeq):
+        bm.free(5)
+    with pytest.raises(pa.UnknownSeq):
+        bm.fork(5, 6)
+    bm.alloc(1, 9)
+    with pytest.raises(pa.SeqExists):
+        bm.fork(1, 1)
+    with pytest.raises(pa.InvalidArgument):
+        bm.alloc_batch([2, 2], [1, 1])
+    with pytest.raises(pa.InvalidArgument):
+        bm.pack([1], max_blocks=2)
+    with pytest.raises(pa.OutOfBlocks) as ei:
+        bm.alloc(2, 8)
+    assert "needs 2 blocks, 1 free" in str(ei.value)
+    assert bm.stats()["num_seqs"] == 1  # the failed request created nothing
+
+
+def _fake_cache(**kw):
+    d = dict(k=0x1000, v=0x2000, num_blocks=10, block_size=16, num_kv_heads=8, head_dim=128,
+             dtype=_lib.PA_BF16, k_scale=1.0, v_scale=1.0)
+    d.update(kw)
+    d.setdefault("block_stride", d["block_size"] * d["num_kv_heads"] * d["head_dim"])
+    return _lib.PaKvCache(**d)
+
+
+def _decode_status(cache, **kw):
+    a = dict(out=0x3000, out_dtype=_lib.PA_BF16, q=0x4000, q_dtype=_lib.PA_BF16, tables=0x5000, max_blocks=8,
+             lens=0x6000, B=2, Hq=32, max_ctx=128, scale=0.1, part=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return pa.lib().pa_decode(ctypes.byref(cache), a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["tables"],
+                              a["max_blocks"], a["lens"], a["B"], a["Hq"], a["max_ctx"], a["scale"], a["part"],
+                              a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,cache_kw,want", [
+    (dict(), dict(head_dim=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(), dict(block_size=64), _lib.PA_ERR_UNSUPPORTED),
+    (dict(Hq=24), dict(), _lib.PA_ERR_UNSUPPORTED),          # group 3
+    (dict(Hq=30), dict(), _lib.PA_ERR_INVALID_ARGUMENT),     # not a multiple of Hkv
+    (dict(q_dtype=_lib.PA_F16), dict(), _lib.PA_ERR_UNSUPPORTED),
+    (dict(out_dtype=_lib.PA_FP8_E4M3), dict(), _lib.PA_ERR_UNSUPPORTED),
+    (dict(max_ctx=129), dict(), _lib.PA_ERR_INVALID_ARGUMENT),   # > max_blocks * bs
+    (dict(part=24), dict(), _lib.PA_ERR_INVALID_ARGUMENT),       # not a multiple of 16
+    (dict(part=64), dict(), _lib.PA_ERR_INVALID_ARGUMENT),       # split needs a workspace
+    (dict(q=0x4001), dict(), _lib.PA_ERR_INVALID_ARGUMENT),      # misaligned
+    (dict(scale=float("nan")), dict(), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(), dict(block_stride=100), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(), dict(dtype=_lib.PA_F32), _lib.PA_ERR_UNSUPPORTED),
+    (dict(), dict(dtype=_lib.PA_FP8_E4M3, k_scale=0.0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), dict(), _lib.PA_OK),                             # empty batch: nothing to do
+])
+def test_decode_rejects_bad_arguments_before_launch(kw, cache_kw, want):
+    assert _decode_status(_fake_cache(**cache_kw), **kw) == want
+    if want != _lib.PA_OK:
+        assert pa.lib().pa_last_error().decode() != ""
+
+
+def test_workspace_size():
+    f = pa.decode_workspace_size
+    assert f(64, 32, 128, 4096, 0) == 0
+    assert f(64, 32, 128, 512, 512) == 0
+    rows = 64 * 32 * 8
+    assert f(64, 32, 128, 4096, 512) == 2 * ((rows * 4 + 255) // 256 * 256) + rows * 128 * 4
+
+
+def test_cache_ops_reject_bad_arguments_before_launch():
+    c = _fake_cache()
+    L = pa.lib()
+    assert L.pa_reshape_and_cache(ctypes.byref(c), 0x1000, 0x2000, _lib.PA_F16, 0x3000, 4, None) == \
+        _lib.PA_ERR_UNSUPPORTED  # a bf16 pool takes bf16 sources
+    assert L.pa_reshape_and_cache(ctypes.byref(c), 0x1000, 0x2000, _lib.PA_BF16, 0x3000, -1, None) == \
+        _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_reshape_and_cache(ctypes.byref(c), 0x1000, 0x2000, _lib.PA_BF16, 0x3000, 0, None) == _lib.PA_OK
+    assert L.pa_copy_blocks(ctypes.byref(c), None, 3, None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_copy_blocks(ctypes.byref(c), None, 0, None) == _lib.PA_OK
+    c8 = _fake_cache(dtype=_lib.PA_FP8_E4M3, k_scale=0.01, v_scale=0.01)
+    assert L.pa_reshape_and_cache(ctypes.byref(c8), 0x1000, 0x2000, _lib.PA_FP8_E4M3, 0x3000, 4, None) == \
+        _lib.PA_ERR_UNSUPPORTED
