@@ -48,12 +48,11 @@ def write(k_pool: np.ndarray, v_pool: np.ndarray, k_new: torch.Tensor, v_new: to
     bs = k_pool.shape[1]
     kb = storage_bits(k_new, kv_dtype, k_scale)
     vb = storage_bits(v_new, kv_dtype, v_scale)
-    for i, slot in enumerate(np.asarray(slots, dtype=np.int64)):
-        if slot < 0:
-            continue
-        blk, off = divmod(int(slot), bs)
-        k_pool[blk, off] = kb[i]
-        v_pool[blk, off] = vb[i]
+    slots = np.asarray(slots, dtype=np.int64)
+    keep = slots >= 0
+    blk, off = np.divmod(slots[keep], bs)
+    k_pool[blk, off] = kb[keep]
+    v_pool[blk, off] = vb[keep]
 
 
 def copy(k_pool: np.ndarray, v_pool: np.ndarray, pairs) -> None:
