@@ -70,6 +70,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--layers", type=int, default=4)
     p.add_argument("--partition-size", type=int, default=512)
+    p.add_argument("--v-layout", choices=["dim", "token"], default="dim",
+                   help="in-block V layout: dim-major (matrix-core PV) or the token-major KVBlock layout")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -159,7 +161,8 @@ def main():
 
     # ---- setup: every layer's pool written through the library
     bm = pa.BlockManager(num_blocks, bs, wl.free_order)
-    caches = [pa.KVCache.allocate(num_blocks, bs, Hkv, D, "bf16", device=dev) for _ in range(layers)]
+    caches = [pa.KVCache.allocate(num_blocks, bs, Hkv, D, "bf16", device=dev, v_layout=args.v_layout)
+              for _ in range(layers)]
     batch = PagedBatch(bm, caches, max_blocks, B, device=dev, pad=0)
     gen = torch.Generator(device=dev).manual_seed(4902)
     for s in range(B):
@@ -221,7 +224,7 @@ def main():
             "workload": "GQA decode batch: 64 seqs, context U[512,4096], 32 q heads / 8 KV heads, head_dim 128, "
                         "block 16, bf16; one decode step per layer, layers share block tables",
             "batch": B, "layers": layers, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
-            "block_size": bs, "partition_size": args.partition_size,
+            "block_size": bs, "partition_size": args.partition_size, "v_layout": args.v_layout,
             "mean_context": round(float(lens_before.mean()) + (K + 1) / 2, 1),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

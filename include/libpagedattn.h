@@ -164,17 +164,33 @@ pa_status pa_bm_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity, int3
  * Device KV pool descriptor (caller-owned device memory).
  *
  * [course] §2 "The insight": each physical block holds BLOCK tokens of K
- * and V laid out K[BLOCK][HEADS][HEAD_DIM], V[BLOCK][HEADS][HEAD_DIM]. Here:
- * element (blk, t, h, d) of K is at k[blk * block_stride + (t * num_kv_heads
- * + h) * head_dim + d], and likewise for V with v. block_stride (elements)
- * >= block_size * num_kv_heads * head_dim; separate K and V pools use
- * exactly that, the page's interleaved KVBlock uses twice that with
- * v = k + block_size * num_kv_heads * head_dim.
+ * and V laid out K[BLOCK][HEADS][HEAD_DIM], V[BLOCK][HEADS][HEAD_DIM].
+ * K always uses that token-major layout: element (blk, t, h, d) of K is at
+ *   k[blk * block_stride + (t * num_kv_heads + h) * head_dim + d].
+ * V uses the layout named by v_layout:
+ *   PA_LAYOUT_TOKEN_MAJOR (the page's V[BLOCK][HEADS][HEAD_DIM]):
+ *     v[blk * block_stride + (t * num_kv_heads + h) * head_dim + d]
+ *   PA_LAYOUT_DIM_MAJOR (V[HEADS][HEAD_DIM][BLOCK], the tokens of one head
+ *     dimension contiguous; the V-cache layout vLLM uses for the same reason):
+ *     v[blk * block_stride + (h * head_dim + d) * block_size + t]
+ * The dim-major V layout lets the decode kernel feed V straight into the
+ * matrix cores (the softmax-weighted sum contracts over tokens); [note]
+ * block-size section: the best block granularity depends on the attention
+ * kernel's vectorisation. Both layouts are supported explicitly; neither
+ * falls back to the other.
+ * block_stride (elements) >= block_size * num_kv_heads * head_dim; separate
+ * K and V pools use exactly that, the page's interleaved KVBlock uses twice
+ * that with v = k + block_size * num_kv_heads * head_dim.
  * Requirements: k and v 16-byte aligned; head_dim a multiple of 16;
  * block_stride * element size a multiple of 16 bytes.
  * fp8 pools store E4M3 codes of value / scale with one fp32 scale per
  * tensor (k_scale, v_scale > 0); 16-bit pools ignore the scales.
  * ---------------------------------------------------------------------- */
+typedef enum pa_layout {
+  PA_LAYOUT_TOKEN_MAJOR = 0, /* [block][heads][head_dim] */
+  PA_LAYOUT_DIM_MAJOR = 1,   /* [heads][head_dim][block] (V only) */
+} pa_layout;
+
 typedef struct pa_kv_cache {
   void* k;
   void* v;
@@ -183,7 +199,8 @@ typedef struct pa_kv_cache {
   int32_t block_size;
   int32_t num_kv_heads;
   int32_t head_dim;
-  pa_dtype dtype; /* PA_F16, PA_BF16 or PA_FP8_E4M3 */
+  pa_dtype dtype;     /* PA_F16, PA_BF16 or PA_FP8_E4M3 */
+  pa_layout v_layout; /* in-block layout of V */
   float k_scale;
   float v_scale;
 } pa_kv_cache;

@@ -219,10 +219,15 @@ class BlockManager:
 # device pool
 
 
+_V_LAYOUTS = {"token": _lib.PA_LAYOUT_TOKEN_MAJOR, "dim": _lib.PA_LAYOUT_DIM_MAJOR}
+
+
 @dataclasses.dataclass
 class KVCache:
     """A paged KV pool in device memory: K and V tensors whose block b starts
-    at element b * block_stride, each block [block_size][num_kv_heads][head_dim]."""
+    at element b * block_stride. K blocks are [block_size][num_kv_heads]
+    [head_dim]; V blocks are that too (``v_layout="token"``) or
+    [num_kv_heads][head_dim][block_size] (``v_layout="dim"``)."""
 
     k: torch.Tensor
     v: torch.Tensor
@@ -233,11 +238,12 @@ class KVCache:
     block_stride: int
     k_scale: float = 1.0
     v_scale: float = 1.0
+    v_layout: str = "token"
 
     @classmethod
     def allocate(cls, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  kv_dtype: str = "bf16", device="cuda", layout: str = "split", k_scale: float = 1.0,
-                 v_scale: float = 1.0, fill: Optional[float] = None) -> "KVCache":
+                 v_scale: float = 1.0, fill: Optional[float] = None, v_layout: str = "token") -> "KVCache":
         """``layout="split"``: separate K and V pools; ``"interleaved"``: one
         buffer of blocks each holding K then V."""
         dt = _NAMES[kv_dtype]
@@ -256,7 +262,9 @@ class KVCache:
         if fill is not None:
             k.fill_(fill)
             v.fill_(fill)
-        return cls(k, v, num_blocks, block_size, num_kv_heads, head_dim, stride, k_scale, v_scale)
+        if v_layout not in _V_LAYOUTS:
+            raise ValueError(v_layout)
+        return cls(k, v, num_blocks, block_size, num_kv_heads, head_dim, stride, k_scale, v_scale, v_layout)
 
     @property
     def dtype_code(self) -> int:
@@ -267,14 +275,18 @@ class KVCache:
             raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, "pool tensors must be on the device")
         return PaKvCache(self.k.data_ptr(), self.v.data_ptr(), int(self.block_stride), int(self.num_blocks),
                          int(self.block_size), int(self.num_kv_heads), int(self.head_dim), self.dtype_code,
-                         float(self.k_scale), float(self.v_scale))
+                         _V_LAYOUTS[self.v_layout], float(self.k_scale), float(self.v_scale))
 
     def block_view(self, which: str = "k") -> torch.Tensor:
-        """[num_blocks][block_size][num_kv_heads][head_dim] view of K or V."""
+        """Logical [num_blocks][block_size][num_kv_heads][head_dim] view of K
+        or V (a strided view of the pool in either V layout)."""
         t = self.k if which == "k" else self.v
-        be = self.block_size * self.num_kv_heads * self.head_dim
-        return t.as_strided((self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim),
-                            (self.block_stride, self.num_kv_heads * self.head_dim, self.head_dim, 1))
+        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        if which == "v" and self.v_layout == "dim":
+            strides = (self.block_stride, 1, self.head_dim * self.block_size, self.block_size)
+        else:
+            strides = (self.block_stride, self.num_kv_heads * self.head_dim, self.head_dim, 1)
+        return t.as_strided(shape, strides)
 
 
 # ---------------------------------------------------------------------------

@@ -26,6 +26,9 @@ PA_BF16 = 1
 PA_F32 = 2
 PA_FP8_E4M3 = 3
 
+PA_LAYOUT_TOKEN_MAJOR = 0
+PA_LAYOUT_DIM_MAJOR = 1
+
 
 class PaKvCache(ctypes.Structure):
     _fields_ = [
@@ -37,6 +40,7 @@ class PaKvCache(ctypes.Structure):
         ("num_kv_heads", c_int32),
         ("head_dim", c_int32),
         ("dtype", c_int),
+        ("v_layout", c_int),
         ("k_scale", c_float),
         ("v_scale", c_float),
     ]

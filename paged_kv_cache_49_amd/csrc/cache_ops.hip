@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new, const int64_t* __restrict__ slots,
     int64_t total_items, int32_t chunks_per_row, int32_t row_elems, void* __restrict__ k_pool,
     void* __restrict__ v_pool, int64_t block_stride, int32_t block_size, int64_t num_slots, float k_inv,
-    float v_inv) {
+    float v_inv, int32_t v_dim_major) {
   const int64_t item = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (item >= total_items) return;
   const int64_t per_token = 2 * static_cast<int64_t>(chunks_per_row);
@@ -48,11 +48,20 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
   const int64_t src_elem = token * row_elems + static_cast<int64_t>(chunk) * 8;
   const void* src = is_v ? v_new : k_new;
   void* dst = is_v ? v_pool : k_pool;
+  // dim-major V: element (h*D + d) of the row goes to block offset (h*D + d) * bs + t
+  const bool scatter = is_v && v_dim_major;
+  const int64_t sc_elem = blk * block_stride + static_cast<int64_t>(chunk) * 8 * block_size + off;
 
   if constexpr (!kToFp8) {
     // same 16-bit dtype: move the bits
     const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + src_elem);
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + dst_elem) = v;
+    if (scatter) {
+      uint16_t* d = static_cast<uint16_t*>(dst) + sc_elem;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[e * block_size] = static_cast<uint16_t>(v[e / 2] >> (16 * (e % 2)));
+    } else {
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + dst_elem) = v;
+    }
   } else {
     float x[8];
     if constexpr (Src::kBytes == 4) {
@@ -75,10 +84,16 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
       }
     }
     const float inv = is_v ? v_inv : k_inv;
-    u32x2 packed = {0u, 0u};
+    if (scatter) {
+      uint8_t* d = static_cast<uint8_t*>(dst) + sc_elem;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed[i / 4] |= f32_to_e4m3(x[i] * inv) << (8 * (i % 4));
-    *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(dst) + dst_elem) = packed;
+      for (int i = 0; i < 8; ++i) d[i * block_size] = static_cast<uint8_t>(f32_to_e4m3(x[i] * inv));
+    } else {
+      u32x2 packed = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) packed[i / 4] |= f32_to_e4m3(x[i] * inv) << (8 * (i % 4));
+      *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(dst) + dst_elem) = packed;
+    }
   }
 }
 
@@ -141,6 +156,8 @@ int elem_bytes(pa_dtype t) {
 pa_status validate_cache(const pa_kv_cache* c) {
   if (c == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "cache is NULL");
   if (c->k == nullptr || c->v == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "cache k or v is NULL");
+  if (c->v_layout != PA_LAYOUT_TOKEN_MAJOR && c->v_layout != PA_LAYOUT_DIM_MAJOR)
+    return fail(PA_ERR_INVALID_ARGUMENT, "v_layout %d is not a pa_layout", (int)c->v_layout);
   if (c->dtype != PA_F16 && c->dtype != PA_BF16 && c->dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "pool dtype %d: pools hold F16, BF16 or FP8_E4M3", (int)c->dtype);
   if (c->num_blocks <= 0 || c->block_size <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
@@ -208,7 +225,8 @@ pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* k_new, cons
 #define PA_LAUNCH_RC(SRC, FP8)                                                                                 \
   hipLaunchKernelGGL((pa::reshape_and_cache_kernel<SRC, FP8>), dim3(static_cast<uint32_t>(grid)),            \
                      dim3(pa::kThreads), 0, s, k_new, v_new, slot_mapping, items, chunks, row_elems, cache->k, \
-                     cache->v, cache->block_stride, cache->block_size, num_slots, kinv, vinv)
+                     cache->v, cache->block_stride, cache->block_size, num_slots, kinv, vinv,  \
+                     cache->v_layout == PA_LAYOUT_DIM_MAJOR ? 1 : 0)
   if (!to_fp8) {
     PA_LAUNCH_RC(pa::SrcF16, false);
   } else if (src_dtype == PA_F32) {

@@ -57,6 +57,7 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(const ReduceParams p
   for (int i = 0; i < np; ++i) mmax = fmaxf(mmax, m[i]);
   for (int d = threadIdx.x; d < p.head_dim; d += blockDim.x) {
     float num = 0.f, den = 0.f;
+#pragma unroll 8
     for (int i = 0; i < np; ++i) {
       const float w = l[i] * __builtin_amdgcn_exp2f(m[i] - mmax);
       den += w;
@@ -121,7 +122,7 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
   if (!dtype_ok)
     return fail(PA_ERR_UNSUPPORTED, "pool dtype %d with q dtype %d: supported are F16/F16, BF16/BF16, FP8/BF16",
                 (int)cache->dtype, (int)q_dtype);
-  const pa::DecodeLaunch launch = pa::find_decode(cache->dtype, D, bs, G);
+  const pa::DecodeLaunch launch = pa::find_decode(cache->dtype, cache->v_layout, D, bs, G);
   if (launch == nullptr)
     return fail(PA_ERR_UNSUPPORTED,
                 "no decode kernel for head_dim %d, block_size %d, group %d (built: head_dim 64/128, block_size "
@@ -196,7 +197,9 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
   prm.v_scale = fp8 ? cache->v_scale : 1.0f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch(prm, dim3(static_cast<uint32_t>(P), hkv, B), s);
+  const int64_t wgs = P * hkv * B;
+  if (wgs > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many workgroups (%lld)", (long long)wgs);
+  hipError_t e = launch(prm, dim3(static_cast<uint32_t>(wgs)), s);
   if (e != hipSuccess) return fail(PA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
   if (P > 1) {
     pa::ReduceParams r{};

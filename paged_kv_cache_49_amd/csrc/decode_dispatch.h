@@ -15,12 +15,19 @@ using DecodeLaunch = hipError_t (*)(const DecodeParams&, dim3 grid, hipStream_t 
 DecodeLaunch find_decode_f16(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_bf16(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_fp8(int head_dim, int block_size, int group);
+// kernels for dim-major V blocks (PV on the matrix cores)
+DecodeLaunch find_decode_vt_f16(int head_dim, int block_size, int group);
+DecodeLaunch find_decode_vt_bf16(int head_dim, int block_size, int group);
+DecodeLaunch find_decode_vt_fp8(int head_dim, int block_size, int group);
 
-inline DecodeLaunch find_decode(pa_dtype pool, int head_dim, int block_size, int group) {
+inline DecodeLaunch find_decode(pa_dtype pool, pa_layout v_layout, int head_dim, int block_size, int group) {
+  const bool vt = v_layout == PA_LAYOUT_DIM_MAJOR;
   switch (pool) {
-    case PA_F16: return find_decode_f16(head_dim, block_size, group);
-    case PA_BF16: return find_decode_bf16(head_dim, block_size, group);
-    case PA_FP8_E4M3: return find_decode_fp8(head_dim, block_size, group);
+    case PA_F16: return vt ? find_decode_vt_f16(head_dim, block_size, group) : find_decode_f16(head_dim, block_size, group);
+    case PA_BF16:
+      return vt ? find_decode_vt_bf16(head_dim, block_size, group) : find_decode_bf16(head_dim, block_size, group);
+    case PA_FP8_E4M3:
+      return vt ? find_decode_vt_fp8(head_dim, block_size, group) : find_decode_fp8(head_dim, block_size, group);
     default: return nullptr;
   }
 }

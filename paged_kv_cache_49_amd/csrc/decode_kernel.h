@@ -1,5 +1,5 @@
-// Paged decode attention, gfx950: one workgroup per (context partition,
-// KV head, sequence).
+// Paged decode attention, gfx950: one wave64 workgroup per (context
+// partition, KV head, sequence).
 //
 // [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
 // [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
@@ -9,27 +9,35 @@
 // visited in logical token order; [note] "why it works": the result is
 // ordinary attention): for the G query heads h of KV head g and the tokens
 // t of one partition,
-//     z_t = scale * q_h . K_t,   m = max z,   l = sum 2^(z' - m'),
-//     o_h = sum_t 2^(z'_t - m') V_t / l        (z' = z * log2 e)
+//     z'_t = log2(e) * scale * q_h . K_t,   m' >= max z',
+//     l = sum_t 2^(z'_t - m'),   o_h = sum_t 2^(z'_t - m') V_t / l
 // Partitions of one sequence are merged by decode_reduce_kernel.
 //
-// Workgroup layout (256 threads = 4 wave64):
-//  * the partition is walked in chunks of kChunk tokens; for each chunk the
-//    slice of the block table it needs is staged in LDS once (ids outside
-//    the pool or past ceil(L/bs) read block 0, so no access leaves the pool)
-//  * QK: each wave takes 16-token tiles; K rows are loaded straight from
-//    the pool in MFMA operand layout (lane = token column n = lane%16,
-//    head-dim slice j = lane/16, 16-byte loads) and multiplied against the
-//    group's q rows (rows 0..G-1 of a 16-row A operand) with
-//    v_mfma_f32_16x16x32_{bf16,f16}; lane (n, j) then holds the logits of
-//    token n for heads 4j..4j+3. Logits go to LDS.
-//  * softmax: chunk max per head (wave reduce + LDS), weights 2^(z'-m')
-//    written back in place, running max / sum rescaled once per chunk.
-//  * PV: lanes split a V row into 8-element pieces (D/8 lanes per row,
-//    64/(D/8) rows per instruction, 16-byte loads for 16-bit pools) and
-//    accumulate G x 8 fp32 partial outputs with FMAs.
-//  * epilogue: partial outputs summed across the rows of a wave (lane
-//    shuffles) and across waves (LDS), divided by the sum.
+// The wave walks the partition's 16-token tiles in order; nothing in the
+// kernel waits on another wave:
+//  * start: the context length, the group's q rows and the first block-table
+//    entries are requested together (one memory latency before the first
+//    K/V request).
+//  * block ids: the wave holds the block-table entries of the current chunk
+//    (up to 64 blocks) in one VGPR, lane i = entry i; a tile's id is read
+//    with v_readlane (block >= 16 tokens: one id per tile) or ds_bpermute
+//    (8-token blocks). Ids outside the pool or past ceil(L / bs) read
+//    block 0, so no access leaves the pool.
+//  * loads: a tile's K rows are loaded in MFMA B-operand layout (lane =
+//    token n = lane % 16, head-dim slice j = lane / 16, 16-byte loads) and
+//    its V rows in PV layout (D/8 lanes per row, 8 elements each); the next
+//    tile's K and V are requested before the current tile is processed.
+//  * QK: v_mfma_f32_16x16x32_{bf16,f16} with the group's q rows as rows
+//    0..G-1 of the A operand; lane (n, j) then holds the logits of token n
+//    for heads 4j..4j+3.
+//  * online softmax per wave: tile maxima by 16-lane DPP row reductions; the
+//    running max m' moves only when a tile exceeds it by more than 2^8
+//    (then the accumulators are rescaled), which keeps every weight below
+//    2^8 and makes rescales rare; weights go through a wave-private LDS
+//    slot to the PV lanes.
+//  * PV on VALU: G x 8 fp32 accumulators per lane.
+//  * epilogue: the rows of the wave are combined with lane shuffles and the
+//    lanes of one row store the G x D result (or the partition's partial).
 // Masking uses selects (never multiply-by-zero), so NaN in unused cache
 // slots cannot leak into the result.
 #pragma once
@@ -46,7 +54,7 @@ struct DecodeParams {
   const void* k_pool;
   const void* v_pool;
   void* out;
-  float* part_m;  // [B][Hq][num_partitions]   running max (log2 domain)
+  float* part_m;  // [B][Hq][num_partitions]   reference max (log2 domain)
   float* part_l;  // [B][Hq][num_partitions]   sum of weights
   float* part_o;  // [B][Hq][num_partitions][D] normalised partial output
   const int32_t* block_tables;
@@ -56,7 +64,7 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t max_blocks;
-  int32_t len_cap;         // min(max_context_len, max_blocks * block_size)
+  int32_t len_cap;         // max_context_len (<= max_blocks * block_size)
   int32_t partition_size;  // tokens per partition; 0 = whole context
   int32_t num_partitions;  // grid.x
   int32_t out_dtype;       // 0 f16, 1 bf16, 2 f32
@@ -66,45 +74,99 @@ struct DecodeParams {
 
 template <typename KV, int D, int BS, int G>
 struct DecodeCfg {
-  static constexpr int kWaves = 4;
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kChunk = 512;
-  static constexpr int kKSteps = D / 32;  // MFMAs per 16-token tile
-  static constexpr int kLpr = D / 8;      // lanes per V row in PV
-  static constexpr int kTpi = 64 / kLpr;  // V rows per PV instruction
-  static constexpr int kTblSlots = kChunk / BS + 2;
-  static constexpr int kLogits = kChunk * G;
-  static constexpr int kOutPartials = kWaves * G * D;
-  static constexpr int kScratch = kLogits > kOutPartials ? kLogits : kOutPartials;
+  static constexpr int kB = KV::kBytes;
+  static constexpr int kThreads = 64;  // one wave per workgroup
+  static constexpr int kKSteps = D / 32;                        // MFMAs per 16-token tile
+  static constexpr int kKLoads = kB == 2 ? kKSteps : kKSteps / 2;  // 16-byte K loads per lane per tile
+  static constexpr int kLpr = D / 8;                            // lanes per V row in PV
+  static constexpr int kRpi = 64 / kLpr;                        // V rows per PV step
+  static constexpr int kPvi = 16 / kRpi;                        // PV steps per tile
+  static constexpr int kChunk = 64 * BS - (BS > 16 ? BS : 0);   // tokens whose block ids fit one VGPR
+  static constexpr int kHRows = (G + 3) / 4;                    // MFMA output rows holding real heads
+  static constexpr float kSlack = 8.0f;                         // log2 headroom before a rescale
   static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
   static_assert(G >= 1 && G <= 8, "group size 1..8");
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size 8, 16 or 32");
+  static_assert(kChunk % 16 == 0, "chunks are whole tiles");
 };
 
 // Head-dim offset of the 8 elements lane group j feeds to QK MFMA step i.
-// Any assignment works as long as q and K use the same one; this one makes
-// each 16-byte load contiguous (16-bit: 32i + 8j; fp8: one 16-byte load of
-// 16 dims serves steps 2a and 2a+1).
+// Any assignment works as long as q and K use the same one. 16-bit: 32i + 8j
+// (each load instruction reads 64 contiguous bytes of every token row);
+// fp8: one 16-byte load of 16 dims serves steps 2a and 2a+1.
 template <int KVBytes>
 __device__ __forceinline__ constexpr int qk_dim(int i, int j) {
   return KVBytes == 2 ? 32 * i + 8 * j : 64 * (i / 2) + 16 * j + 8 * (i % 2);
 }
 
-template <typename KV, typename QT, int D, int BS, int G>
-__global__ __launch_bounds__(256) void paged_decode_kernel(const DecodeParams p) {
-  using C = DecodeCfg<KV, D, BS, G>;
-  constexpr int kB = KV::kBytes;
-  __shared__ float s_buf[C::kScratch];
-  __shared__ int32_t s_tbl[C::kTblSlots];
-  __shared__ float s_red[C::kWaves][G];
-  __shared__ float s_sum[C::kWaves][G];
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+// max / sum over the 16 lanes of each DPP row (row_ror 8, 4, 2, 1); every
+// lane of the row ends with the row's result.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0x128>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x122>(v));
+  return fmaxf(v, dpp_f<0x121>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0x128>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x122>(v);
+  return v + dpp_f<0x121>(v);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// LDS written by some lanes of a wave and read by others: LDS operations of
+// one wave complete in order; this keeps the compiler from reordering them.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Per-lane V pieces: `type` = 8 token-major elements (PV on VALU),
+// `raw_dm` = 4 tokens of one head dim from a dim-major block.
+template <typename KV>
+struct VVecT {
+  using type = u32x4;
+  using raw_dm = u32x2;
+};
+template <>
+struct VVecT<FP8> {
+  using type = u32x2;
+  using raw_dm = uint32_t;
+};
+
+template <typename KV, typename QT, int D, int BS, int G>
+__global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) {
+  using C = DecodeCfg<KV, D, BS, G>;
+  constexpr int kB = C::kB;
+  using VVec = typename VVecT<KV>::type;
+  __shared__ float s_p[16 * G];
+
+  // 1-D grid in partition-major order: workgroup w -> (part, seq, kv head).
+  // Consecutive workgroups are dealt round-robin to the 8 XCDs, so each XCD
+  // receives the same mix of partition indices (late partitions of short
+  // sequences are empty; a partition-fastest order would pile all first
+  // partitions onto one XCD).
+  const int pairs = static_cast<int>(gridDim.x) / p.num_partitions;  // B * Hkv
+  const int part = static_cast<int>(blockIdx.x) / pairs;
+  const int pr = static_cast<int>(blockIdx.x) - part * pairs;
+  const int s = pr / p.num_kv_heads;
+  const int g = pr - s * p.num_kv_heads;
+  const int lane = threadIdx.x;
+  const int32_t* bt = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
+  // issued together with the length: the first chunk's block-table entries
+  // (in-bounds of the table row; masked once the length is known)
+  const int blk_first = p.partition_size > 0 ? part * p.partition_size / BS : 0;
+  const int id_first = blk_first + lane < p.max_blocks ? bt[blk_first + lane] : 0;
 
   int L = p.context_lens[s];
   L = L < p.len_cap ? L : p.len_cap;
@@ -114,21 +176,23 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(const DecodeParams p)
   if (part >= (nparts > 0 ? nparts : 1)) return;
   const int64_t head0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(g) * G;
   if (L == 0) {
-    for (int i = tid; i < G * D; i += C::kThreads) store_out(p.out, head0 * D + i, p.out_dtype, 0.f);
+    for (int i = lane; i < G * D; i += C::kThreads) store_out(p.out, head0 * D + i, p.out_dtype, 0.f);
     return;
   }
   const int tok_begin = part * ps;
   const int tok_end = min(L, tok_begin + ps);
 
+  const int col = lane & 15, j = lane >> 4;         // MFMA layout: token column, head-dim slice / head row
+  const int vrow = lane / C::kLpr, vcc = lane % C::kLpr;  // PV layout: row in step, 8-element piece
+
   // q rows of the group as MFMA A operands (rows >= G are zero)
   u32x4 qa[C::kKSteps];
   {
-    const int h = lane & 15, j = lane >> 4;
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (h < G ? h : 0)) * D;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
 #pragma unroll
     for (int i = 0; i < C::kKSteps; ++i) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
-      qa[i] = h < G ? v : u32x4{0u, 0u, 0u, 0u};
+      qa[i] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -138,189 +202,215 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(const DecodeParams p)
   const int64_t tok_bytes = static_cast<int64_t>(p.num_kv_heads) * D * kB;
   const int64_t head_bytes = static_cast<int64_t>(g) * D * kB;
   const int nvalid_blk = (L + BS - 1) / BS;
-  const int32_t* bt = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
 
+  float m_w[G];  // running reference max per head (uniform across the wave)
+  float l_r[4];  // per-lane partial sums, MFMA output layout
   float acc[G][8];
-  float m_run[G], l_th[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_th[h] = 0.f;
+    m_w[h] = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) l_r[r] = 0.f;
 
   for (int c0 = tok_begin; c0 < tok_end; c0 += C::kChunk) {
     const int n = min(C::kChunk, tok_end - c0);
     const int ntiles = (n + 15) >> 4;
-    const int first_blk = c0 / BS;
-    const int nblk = (c0 + ntiles * 16 - 1) / BS - first_blk + 1;
-    for (int i = tid; i < nblk; i += C::kThreads) {
-      const int bi = first_blk + i;
-      int32_t id = bi < nvalid_blk ? bt[bi] : 0;
-      s_tbl[i] = static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks) ? id : 0;
+    const int blk0 = c0 / BS;
+    const int nblk = (c0 + ntiles * 16 - 1) / BS - blk0 + 1;  // <= 64
+    int ids;
+    {
+      const int bi = blk0 + lane;
+      const int id = c0 == tok_begin ? id_first : (bi < p.max_blocks ? bt[bi] : 0);
+      ids = (lane < nblk && bi < nvalid_blk && static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks)) ? id : 0;
     }
-    __syncthreads();
 
-    // ---- QK on MFMA: 16-token tiles, one per wave per step
-    for (int tile = wave; tile < ntiles; tile += C::kWaves) {
-      const int col = lane & 15, j = lane >> 4;
-      const int t = c0 + tile * 16 + col;
-      const int32_t phys = s_tbl[t / BS - first_blk];
-      const char* krow = kbase + phys * blk_bytes + (t % BS) * tok_bytes + head_bytes;
+    // row pointers of one token for K (lane's column) and V (lane's PV row)
+    auto phys_of = [&](int t) -> int {
+      if constexpr (BS >= 16) {
+        return __builtin_amdgcn_readlane(ids, (t & ~15) / BS - blk0);
+      } else {
+        return __shfl(ids, t / BS - blk0, 64);
+      }
+    };
+    auto load_tile = [&](int tile, u32x4 (&kr)[C::kKLoads], VVec (&vr)[C::kPvi]) {
+      const int tb = c0 + tile * 16;
+      {
+        const int t = tb + col;
+        const char* krow = kbase + phys_of(t) * blk_bytes + (t % BS) * tok_bytes + head_bytes;
+#pragma unroll
+        for (int i = 0; i < C::kKLoads; ++i) {
+          const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
+          kr[i] = *reinterpret_cast<const u32x4*>(krow + off);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < C::kPvi; ++it) {
+        const int t = tb + it * C::kRpi + vrow;
+        const char* vr_ = vbase + phys_of(t) * blk_bytes + (t % BS) * tok_bytes + head_bytes + vcc * 8 * kB;
+        vr[it] = *reinterpret_cast<const VVec*>(vr_);
+      }
+    };
+
+    u32x4 kc[C::kKLoads], kn[C::kKLoads];
+    VVec vc[C::kPvi], vn[C::kPvi];
+    load_tile(0, kc, vc);
+    for (int tile = 0; tile < ntiles; ++tile) {
+      // request the next tile (the last tile re-requests itself: a cache hit)
+      load_tile(tile + 1 < ntiles ? tile + 1 : tile, kn, vn);
+      const int tb = c0 + tile * 16;
+
+      // ---- QK on MFMA
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (kB == 2) {
-        u32x4 kb[C::kKSteps];
 #pragma unroll
-        for (int i = 0; i < C::kKSteps; ++i) kb[i] = *reinterpret_cast<const u32x4*>(krow + 2 * qk_dim<2>(i, j));
-#pragma unroll
-        for (int i = 0; i < C::kKSteps; ++i) sacc = mfma_16x16x32<QT>(qa[i], kb[i], sacc);
+        for (int i = 0; i < C::kKSteps; ++i) sacc = mfma_16x16x32<QT>(qa[i], kc[i], sacc);
       } else {
-        u32x4 kb[C::kKSteps / 2];
 #pragma unroll
-        for (int a = 0; a < C::kKSteps / 2; ++a)
-          kb[a] = *reinterpret_cast<const u32x4*>(krow + qk_dim<1>(2 * a, j));
-#pragma unroll
-        for (int a = 0; a < C::kKSteps / 2; ++a) {
-          const u32x2 b0 = e4m3x4_to_bf16x4(kb[a].x), b1 = e4m3x4_to_bf16x4(kb[a].y);
-          const u32x2 b2 = e4m3x4_to_bf16x4(kb[a].z), b3 = e4m3x4_to_bf16x4(kb[a].w);
+        for (int a = 0; a < C::kKLoads; ++a) {
+          const u32x2 b0 = e4m3x4_to_bf16x4(kc[a].x), b1 = e4m3x4_to_bf16x4(kc[a].y);
+          const u32x2 b2 = e4m3x4_to_bf16x4(kc[a].z), b3 = e4m3x4_to_bf16x4(kc[a].w);
           sacc = mfma_16x16x32<QT>(qa[2 * a], u32x4{b0.x, b0.y, b1.x, b1.y}, sacc);
           sacc = mfma_16x16x32<QT>(qa[2 * a + 1], u32x4{b2.x, b2.y, b3.x, b3.y}, sacc);
         }
       }
-      const bool valid = t < tok_end;
+      const bool kval = tb + col < tok_end;
+      float sv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * j + r;
-        if (h < G) s_buf[(tile * 16 + col) * G + h] = valid ? sacc[r] * p.qk_scale_log2 : -INFINITY;
-      }
-    }
-    __syncthreads();
+      for (int r = 0; r < 4; ++r) sv[r] = kval ? sacc[r] * p.qk_scale_log2 : -INFINITY;
 
-    // ---- softmax over the chunk: max, weights, running sums
-    float mloc[G];
+      // ---- online softmax
+      float mt[G];
+      {
+        float mx[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
-    for (int t = tid; t < ntiles * 16; t += C::kThreads) {
+        for (int r = 0; r < 4; ++r) mx[r] = row16_max(sv[r]);
 #pragma unroll
-      for (int h = 0; h < G; ++h) mloc[h] = fmaxf(mloc[h], s_buf[t * G + h]);
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mloc[h] = wave_max(mloc[h]);
-      if (lane == 0) s_red[wave][h] = mloc[h];
-    }
-    __syncthreads();
-    float alpha[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mc = s_red[0][h];
-#pragma unroll
-      for (int w = 1; w < C::kWaves; ++w) mc = fmaxf(mc, s_red[w][h]);
-      const float mn = fmaxf(m_run[h], mc);
-      alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - mn);
-      m_run[h] = mn;
-    }
-    float lsum[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) lsum[h] = 0.f;
-    for (int t = tid; t < ntiles * 16; t += C::kThreads) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float e = __builtin_amdgcn_exp2f(s_buf[t * G + h] - m_run[h]);
-        s_buf[t * G + h] = e;
-        lsum[h] += e;
+        for (int h = 0; h < G; ++h) mt[h] = readlane_f(mx[h % 4], 16 * (h / 4));
       }
-    }
+      bool rescale = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      l_th[h] = l_th[h] * alpha[h] + lsum[h];
+      for (int h = 0; h < G; ++h) rescale |= mt[h] > m_w[h] + C::kSlack;
+      if (rescale) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-    }
-    __syncthreads();
-
-    // ---- PV on VALU: each lane owns 8 head-dim elements of one row
-    {
-      const int row = lane / C::kLpr;
-      const int cc = lane % C::kLpr;
-      for (int tile = wave; tile < ntiles; tile += C::kWaves) {
+        for (int h = 0; h < G; ++h) {
+          if (mt[h] > m_w[h] + C::kSlack) {
+            const float a = __builtin_amdgcn_exp2f(m_w[h] - mt[h]);
+            m_w[h] = mt[h];
 #pragma unroll
-        for (int it = 0; it < 16 / C::kTpi; ++it) {
-          const int tr = tile * 16 + it * C::kTpi + row;
-          const int t = c0 + tr;
-          const int32_t phys = s_tbl[t / BS - first_blk];
-          const char* vrow = vbase + phys * blk_bytes + (t % BS) * tok_bytes + head_bytes + cc * 8 * kB;
-          float vf[8];
-          if constexpr (kB == 2) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(vrow);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if constexpr (__is_same(KV, BF16)) {
-                vf[2 * e] = bf16_lo(w[e]);
-                vf[2 * e + 1] = bf16_hi(w[e]);
-              } else {
-                vf[2 * e] = f16_lo(w[e]);
-                vf[2 * e + 1] = f16_hi(w[e]);
-              }
-            }
-          } else {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(vrow);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vf[e] = e4m3_to_f32((w[e / 4] >> (8 * (e % 4))) & 0xffu);
+            for (int e = 0; e < 8; ++e) acc[h][e] *= a;
+            l_r[h % 4] *= (j == h / 4) ? a : 1.0f;
           }
-          const bool valid = t < tok_end;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vf[e] = valid ? vf[e] : 0.f;
-          float wt[G];
-#pragma unroll
-          for (int h = 0; h < G; ++h) wt[h] = s_buf[tr * G + h];
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wt[h], vf[e], acc[h][e]);
         }
       }
+      float pw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float mh = m_w[r < G ? r : 0];
+        if constexpr (G > 4) mh = j == 1 ? m_w[4 + r] : mh;
+        pw[r] = __builtin_amdgcn_exp2f(sv[r] - mh);
+        l_r[r] += pw[r];
+      }
+      if (j < C::kHRows) {
+        float* dst = &s_p[col * G + 4 * j];
+        if constexpr (G >= 4) {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{pw[0], pw[1], pw[2], pw[3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < G; ++r) dst[r] = pw[r];
+        }
+      }
+      wave_lds_sync();
+
+      // ---- PV on VALU
+      const bool tail = tb + 16 > tok_end;
+#pragma unroll
+      for (int it = 0; it < C::kPvi; ++it) {
+        const int tr = it * C::kRpi + vrow;
+        float vf[8];
+        if constexpr (kB == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (__is_same(KV, BF16)) {
+              vf[2 * e] = bf16_lo(vc[it][e]);
+              vf[2 * e + 1] = bf16_hi(vc[it][e]);
+            } else {
+              vf[2 * e] = f16_lo(vc[it][e]);
+              vf[2 * e + 1] = f16_hi(vc[it][e]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vf[e] = e4m3_to_f32((vc[it][e / 4] >> (8 * (e % 4))) & 0xffu);
+        }
+        if (tail) {
+          const bool ok = tb + tr < tok_end;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vf[e] = ok ? vf[e] : 0.f;
+        }
+        float w[G];
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+          for (int h4 = 0; h4 < G; h4 += 4) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&s_p[tr * G + h4]);
+            w[h4] = w4.x;
+            w[h4 + 1] = w4.y;
+            w[h4 + 2] = w4.z;
+            w[h4 + 3] = w4.w;
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h) w[h] = s_p[tr * G + h];
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w[h], vf[e], acc[h][e]);
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < C::kKLoads; ++i) kc[i] = kn[i];
+#pragma unroll
+      for (int i = 0; i < C::kPvi; ++i) vc[i] = vn[i];
     }
-    __syncthreads();
   }
 
-  // ---- epilogue: combine rows within a wave, then waves through LDS
+  // ---- epilogue: sums over the 16 lanes of each head row, partial outputs
+  // over the kRpi rows of the PV layout, then lanes 0..kLpr-1 store.
+  float lw[G];
+  {
+    float ls[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls[r] = row16_sum(l_r[r]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) lw[h] = readlane_f(ls[h % 4], 16 * (h / 4));
+  }
 #pragma unroll
   for (int off = C::kLpr; off < 64; off <<= 1)
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float v = wave_sum(l_th[h]);
-    if (lane == 0) s_sum[wave][h] = v;
-  }
   if (lane < C::kLpr) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      const float inv = p.v_scale / lw[h];
+      float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_buf[(wave * G + h) * D + lane * 8 + e] = acc[h][e];
-  }
-  __syncthreads();
-  for (int i = tid; i < G * D; i += C::kThreads) {
-    const int h = i / D, d = i % D;
-    float o = 0.f, l = 0.f;
-#pragma unroll
-    for (int w = 0; w < C::kWaves; ++w) {
-      o += s_buf[(w * G + h) * D + d];
-      l += s_sum[w][h];
-    }
-    const float val = o / l * p.v_scale;
-    if (nparts == 1) {
-      store_out(p.out, (head0 + h) * D + d, p.out_dtype, val);
-    } else {
-      const int64_t pi = (head0 + h) * p.num_partitions + part;
-      p.part_o[pi * D + d] = val;
-      if (d == 0) {
-        p.part_m[pi] = m_run[h];
-        p.part_l[pi] = l;
+      for (int e = 0; e < 8; ++e) o[e] = acc[h][e] * inv;
+      if (nparts == 1) {
+        store_out8(p.out, (head0 + h) * D + lane * 8, p.out_dtype, o);
+      } else {
+        const int64_t pi = (head0 + h) * p.num_partitions + part;
+        float* po = p.part_o + pi * D + lane * 8;
+        *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        if (lane == 0) {
+          p.part_m[pi] = m_w[h];
+          p.part_l[pi] = lw[h];
+        }
       }
     }
   }

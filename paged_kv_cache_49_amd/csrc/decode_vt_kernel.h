@@ -1,0 +1,342 @@
+// Paged decode attention for pools whose V blocks are dim-major
+// (V[heads][head_dim][block]): both products on the matrix cores.
+//
+// [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
+// [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
+// Same result as paged_decode_kernel (see decode_kernel.h for what is
+// computed and for the block-table, partition and masking rules); only the
+// data flow differs. One wave64 workgroup per (partition, sequence, KV head).
+//
+// Per 16-token tile:
+//  * S^T = K q^T with v_mfma_f32_16x16x32 (A = the tile's K rows, one token
+//    per lane row, 8 head dims per lane; B = the group's q rows, padded to 16
+//    heads with zeros). Lane (h = lane % 16, j = lane / 16) ends up holding
+//    the logits of head h for tokens 4j..4j+3 of the tile.
+//  * online softmax per head: the tile max is a 4-register max and two
+//    cross-row lane exchanges; the running max moves only past a 2^8 slack.
+//  * the weights are already in the A-operand layout of v_mfma_f32_16x16x16
+//    (row = head, k = 4 tokens per lane), so PV needs no data movement: each
+//    weight is split into a high and a low 16-bit part (hi + lo carries ~16
+//    mantissa bits) and both are multiplied against V.
+//  * V: dim-major blocks give each lane the 4 consecutive tokens of one head
+//    dimension as one 8-byte load (a 16-dim tile of a 16-token block is 512
+//    contiguous bytes), which is exactly the B operand (k = tokens, n = dim).
+//  * acc: one 16x16 fp32 tile per 16 head dims, rows = heads.
+// Unused weight rows (heads >= G) are zero; V elements of tokens past the
+// end are zeroed with masks (never multiplied by a zero weight), so NaN in
+// unused cache slots cannot reach the result.
+#pragma once
+
+#include "decode_kernel.h"
+
+namespace pa {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x16<BF16>(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
+                                                    0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma_16x16x16<F16>(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
+                                                0);
+}
+
+// Two fp32 values -> one dword of two 16-bit values (round to nearest even),
+// and the exact fp32 value of each half.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float a, float b);
+template <>
+__device__ __forceinline__ uint32_t pack2<BF16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+template <typename T>
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  if constexpr (__is_same(T, BF16)) return bf16_lo(w);
+  return f16_lo(w);
+}
+template <typename T>
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  if constexpr (__is_same(T, BF16)) return bf16_hi(w);
+  return f16_hi(w);
+}
+
+template <typename KV, typename QT, int D, int BS, int G>
+__global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams p) {
+  using C = DecodeCfg<KV, D, BS, G>;
+  constexpr int kB = C::kB;
+  constexpr int kNT = D / 16;  // 16-dim output tiles
+  static_assert(G <= 16, "at most 16 query heads per KV head");
+  using VRaw = typename VVecT<KV>::raw_dm;
+  __shared__ float s_out[G * D];
+
+  const int pairs = static_cast<int>(gridDim.x) / p.num_partitions;  // B * Hkv
+  const int part = static_cast<int>(blockIdx.x) / pairs;
+  const int pr = static_cast<int>(blockIdx.x) - part * pairs;
+  const int s = pr / p.num_kv_heads;
+  const int g = pr - s * p.num_kv_heads;
+  const int lane = threadIdx.x;
+  const int32_t* bt = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
+  const int blk_first = p.partition_size > 0 ? part * p.partition_size / BS : 0;
+  const int id_first = blk_first + lane < p.max_blocks ? bt[blk_first + lane] : 0;
+
+  int L = p.context_lens[s];
+  L = L < p.len_cap ? L : p.len_cap;
+  L = L > 0 ? L : 0;
+  const int ps = p.partition_size > 0 ? p.partition_size : (L > 0 ? L : 1);
+  const int nparts = (L + ps - 1) / ps;
+  if (part >= (nparts > 0 ? nparts : 1)) return;
+  const int64_t head0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(g) * G;
+  if (L == 0) {
+    for (int i = lane; i < G * D; i += 64) store_out(p.out, head0 * D + i, p.out_dtype, 0.f);
+    return;
+  }
+  const int tok_begin = part * ps;
+  const int tok_end = min(L, tok_begin + ps);
+  const int col = lane & 15, j = lane >> 4;
+
+  // q rows as the B operand of S^T = K q^T (columns >= G are zero)
+  u32x4 qb[C::kKSteps];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
+#pragma unroll
+    for (int i = 0; i < C::kKSteps; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
+      qb[i] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const char* kbase = static_cast<const char*>(p.k_pool);
+  const char* vbase = static_cast<const char*>(p.v_pool);
+  const int64_t blk_bytes = p.block_stride * kB;
+  const int64_t tok_bytes = static_cast<int64_t>(p.num_kv_heads) * D * kB;
+  const int64_t khead_bytes = static_cast<int64_t>(g) * D * kB;
+  // lane's V run inside a block: head dim (g*D + col) of the first n-tile, token 4j
+  const int64_t vlane_bytes = (static_cast<int64_t>(g) * D + col) * BS * kB;
+  const uint32_t voff_lane = static_cast<uint32_t>(vlane_bytes + 4 * j * kB);
+  // lane's K row inside a 16-token tile: token col, head g, first head-dim slice
+  const uint32_t koff_lane = static_cast<uint32_t>(col * tok_bytes + khead_bytes + qk_dim<kB>(0, j) * kB);
+  constexpr int kVTileBytes = 16 * BS * kB;  // one 16-dim n-tile of a block
+  const int nvalid_blk = (L + BS - 1) / BS;
+
+  float m_w = -INFINITY;  // running reference max of head `col` (log2 domain)
+  float l_w = 0.f;        // this lane's share of head `col`'s weight sum
+  f32x4 acc[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = tok_begin; c0 < tok_end; c0 += C::kChunk) {
+    const int n = min(C::kChunk, tok_end - c0);
+    const int ntiles = (n + 15) >> 4;
+    const int blk0 = c0 / BS;
+    const int nblk = (c0 + ntiles * 16 - 1) / BS - blk0 + 1;  // <= 64
+    int ids;
+    {
+      const int bi = blk0 + lane;
+      const int id = c0 == tok_begin ? id_first : (bi < p.max_blocks ? bt[bi] : 0);
+      ids = (lane < nblk && bi < nvalid_blk && static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks)) ? id
+                                                                                                                 : 0;
+    }
+    auto phys_of = [&](int t) -> int {
+      if constexpr (BS >= 16) {
+        return __builtin_amdgcn_readlane(ids, (t & ~15) / BS - blk0);
+      } else {
+        return __shfl(ids, t / BS - blk0, 64);
+      }
+    };
+    // K rows: block base (uniform for blocks >= 16 tokens) + per-lane offset
+    auto load_k = [&](int tile, u32x4 (&kr)[C::kKLoads]) {
+      const int tb = c0 + tile * 16;
+      const int t = tb + col;
+      const char* krow;
+      if constexpr (BS >= 16) {
+        const char* base = kbase + static_cast<int64_t>(phys_of(tb)) * blk_bytes + (tb % BS) * tok_bytes;
+        krow = base + koff_lane;
+      } else {
+        krow = kbase + static_cast<int64_t>(phys_of(t)) * blk_bytes + (t % BS) * tok_bytes + khead_bytes;
+      }
+#pragma unroll
+      for (int i = 0; i < C::kKLoads; ++i) {
+        const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
+        kr[i] = *reinterpret_cast<const u32x4*>(krow + (BS >= 16 ? off - qk_dim<kB>(0, j) * kB : off));
+      }
+    };
+    // V runs: 4 tokens of one head dim per lane and n-tile
+    auto load_v = [&](int tile, VRaw (&vr)[kNT]) {
+      const int tb = c0 + tile * 16;
+      const int t = tb + 4 * j;
+      const char* vrun;
+      if constexpr (BS >= 16) {
+        vrun = vbase + static_cast<int64_t>(phys_of(tb)) * blk_bytes + (tb % BS) * kB + voff_lane;
+      } else {
+        vrun = vbase + static_cast<int64_t>(phys_of(t)) * blk_bytes + vlane_bytes + (t % BS) * kB;
+      }
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VRaw*>(vrun + nt * kVTileBytes);
+    };
+
+    // Loads are staggered over single buffers: K(t+1) is requested right
+    // after QK(t) has consumed K(t), and V(t+1) right after PV(t) has
+    // consumed V(t). Loads complete in order, so QK(t+1) waits only for
+    // K(t+1) while V(t+1) is still in flight, and vice versa.
+    u32x4 kr[C::kKLoads];
+    VRaw vr[kNT];
+    load_k(0, kr);
+    load_v(0, vr);
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int tb = c0 + tile * 16;
+      const int next = tile + 1 < ntiles ? tile + 1 : tile;  // a missing next tile re-requests this one
+      // ---- S^T = K q^T
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kB == 2) {
+#pragma unroll
+        for (int i = 0; i < C::kKSteps; ++i) sacc = mfma_16x16x32<QT>(kr[i], qb[i], sacc);
+      } else {
+#pragma unroll
+        for (int a = 0; a < C::kKLoads; ++a) {
+          const u32x2 b0 = e4m3x4_to_bf16x4(kr[a].x), b1 = e4m3x4_to_bf16x4(kr[a].y);
+          const u32x2 b2 = e4m3x4_to_bf16x4(kr[a].z), b3 = e4m3x4_to_bf16x4(kr[a].w);
+          sacc = mfma_16x16x32<QT>(u32x4{b0.x, b0.y, b1.x, b1.y}, qb[2 * a], sacc);
+          sacc = mfma_16x16x32<QT>(u32x4{b2.x, b2.y, b3.x, b3.y}, qb[2 * a + 1], sacc);
+        }
+      }
+      load_k(next, kr);
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = tb + 4 * j + r < tok_end ? sacc[r] * p.qk_scale_log2 : -INFINITY;
+
+      // ---- online softmax (head = col)
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const bool need = col < G && mx > m_w + C::kSlack;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float a = need ? __builtin_amdgcn_exp2f(m_w - mx) : 1.0f;
+        m_w = need ? mx : m_w;
+        l_w *= a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(a, 4 * j + r, 64);  // factor of head 4j + r (held by lane 4j + r)
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) acc[nt][r] *= ar;
+        }
+      }
+      float pw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pw[r] = col < G ? __builtin_amdgcn_exp2f(sv[r] - m_w) : 0.f;
+        l_w += pw[r];
+      }
+      const uint32_t h0 = pack2<QT>(pw[0], pw[1]), h1 = pack2<QT>(pw[2], pw[3]);
+      const uint32_t l0 = pack2<QT>(pw[0] - half_lo<QT>(h0), pw[1] - half_hi<QT>(h0));
+      const uint32_t l1 = pack2<QT>(pw[2] - half_lo<QT>(h1), pw[3] - half_hi<QT>(h1));
+      const u32x2 phi = {h0, h1}, plo = {l0, l1};
+
+      // ---- PV: acc[h][d] += sum_t w[h][t] V[t][d]
+      u32x2 vmask = {0xffffffffu, 0xffffffffu};
+      if (tb + 16 > tok_end) {
+        const int t = tb + 4 * j;
+        vmask.x = (t < tok_end ? 0xffffu : 0u) | (t + 1 < tok_end ? 0xffff0000u : 0u);
+        vmask.y = (t + 2 < tok_end ? 0xffffu : 0u) | (t + 3 < tok_end ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        u32x2 vop;
+        if constexpr (kB == 2) {
+          vop = vr[nt];
+        } else {
+          vop = e4m3x4_to_bf16x4(vr[nt]);
+        }
+        vop.x &= vmask.x;
+        vop.y &= vmask.y;
+        acc[nt] = mfma_16x16x16<QT>(phi, vop, acc[nt]);
+        acc[nt] = mfma_16x16x16<QT>(plo, vop, acc[nt]);
+      }
+      load_v(next, vr);
+    }
+  }
+
+  // ---- epilogue: weight sums per head, then acc / l through LDS for wide stores
+  float l_head = l_w + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_w), 0x401F));
+  l_head += __shfl_xor(l_head, 32, 64);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * j + r;
+    const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
+    if (h < G) {
+      const float inv = p.v_scale / lr;
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) s_out[h * D + nt * 16 + col] = acc[nt][r] * inv;
+    }
+  }
+  wave_lds_sync();
+  for (int i = lane * 8; i < G * D; i += 64 * 8) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = s_out[i + e];
+    const int h = i / D, d = i % D;
+    if (nparts == 1) {
+      store_out8(p.out, (head0 + h) * D + d, p.out_dtype, o);
+    } else {
+      const int64_t pi = (head0 + h) * p.num_partitions + part;
+      float* po = p.part_o + pi * D + d;
+      *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    }
+  }
+  if (nparts > 1 && lane < G) {
+    const int64_t pi = (head0 + lane) * p.num_partitions + part;
+    p.part_m[pi] = m_w;
+    p.part_l[pi] = l_head;
+  }
+}
+
+template <typename KV, typename QT, int D, int BS, int G>
+hipError_t launch_decode_vt(const DecodeParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_decode_vt_kernel<KV, QT, D, BS, G>), grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename KV, typename QT, int D, int BS>
+DecodeLaunch select_decode_vt_g(int G) {
+  switch (G) {
+    case 1: return &launch_decode_vt<KV, QT, D, BS, 1>;
+    case 2: return &launch_decode_vt<KV, QT, D, BS, 2>;
+    case 4: return &launch_decode_vt<KV, QT, D, BS, 4>;
+    case 8: return &launch_decode_vt<KV, QT, D, BS, 8>;
+    default: return nullptr;
+  }
+}
+
+template <typename KV, typename QT, int D>
+DecodeLaunch select_decode_vt_bs(int BS, int G) {
+  switch (BS) {
+    case 8: return select_decode_vt_g<KV, QT, D, 8>(G);
+    case 16: return select_decode_vt_g<KV, QT, D, 16>(G);
+    case 32: return select_decode_vt_g<KV, QT, D, 32>(G);
+    default: return nullptr;
+  }
+}
+
+template <typename KV, typename QT>
+DecodeLaunch select_decode_vt(int D, int BS, int G) {
+  switch (D) {
+    case 64: return select_decode_vt_bs<KV, QT, 64>(BS, G);
+    case 128: return select_decode_vt_bs<KV, QT, 128>(BS, G);
+    default: return nullptr;
+  }
+}
+
+}  // namespace pa

@@ -131,4 +131,23 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, int dtype, flo
   }
 }
 
+// Eight consecutive output elements (16-byte aligned for 16-bit outputs,
+// 32-byte aligned for fp32) by runtime dtype code.
+__device__ __forceinline__ void store_out8(void* out, int64_t idx, int dtype, const float (&v)[8]) {
+  if (dtype == 2) {
+    float* o = static_cast<float*>(out) + idx;
+    *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = dtype == 1 ? f32_to_bf16_bits(v[2 * i]) : f32_to_f16_bits(v[2 * i]);
+      const uint32_t hi = dtype == 1 ? f32_to_bf16_bits(v[2 * i + 1]) : f32_to_f16_bits(v[2 * i + 1]);
+      w[i] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx) = w;
+  }
+}
+
 }  // namespace pa

@@ -45,7 +45,7 @@ def set_pool_bits(cache: pa.KVCache, which: str, bits: np.ndarray) -> None:
     cache.block_view(which).copy_(src.to(cache.k.device))
 
 
-def device_setup(wl, layout="split", max_blocks=None, pad=-1, poison=True, free_order=None):
+def device_setup(wl, layout="split", max_blocks=None, pad=-1, poison=True, free_order=None, v_layout="token"):
     """Allocate and write every sequence of ``wl`` through the library.
     Returns (batch, cache, tables, lens, max_ctx)."""
     from tests.helpers import max_blocks_for
@@ -54,7 +54,7 @@ def device_setup(wl, layout="split", max_blocks=None, pad=-1, poison=True, free_
     bm = pa.BlockManager(wl.num_blocks, wl.block_size, order)
     cache = pa.KVCache.allocate(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
                                 layout=layout, k_scale=ks, v_scale=vs,
-                                fill=poison_fill(wl.kv_dtype) if poison else 0)
+                                fill=poison_fill(wl.kv_dtype) if poison else 0, v_layout=v_layout)
     if max_blocks is None:
         max_blocks = max_blocks_for(wl.lengths, wl.block_size)
     batch = PagedBatch(bm, [cache], max_blocks, wl.batch, pad=pad)

@@ -160,7 +160,7 @@ def test_block_manager_error_paths():
 
 def _fake_cache(**kw):
     d = dict(k=0x1000, v=0x2000, num_blocks=10, block_size=16, num_kv_heads=8, head_dim=128,
-             dtype=_lib.PA_BF16, k_scale=1.0, v_scale=1.0)
+             dtype=_lib.PA_BF16, v_layout=_lib.PA_LAYOUT_TOKEN_MAJOR, k_scale=1.0, v_scale=1.0)
     d.update(kw)
     d.setdefault("block_stride", d["block_size"] * d["num_kv_heads"] * d["head_dim"])
     return _lib.PaKvCache(**d)
@@ -189,6 +189,7 @@ def _decode_status(cache, **kw):
     (dict(scale=float("nan")), dict(), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(), dict(block_stride=100), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(), dict(dtype=_lib.PA_F32), _lib.PA_ERR_UNSUPPORTED),
+    (dict(), dict(v_layout=7), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(), dict(dtype=_lib.PA_FP8_E4M3, k_scale=0.0), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(B=0), dict(), _lib.PA_OK),                             # empty batch: nothing to do
 ])

@@ -29,11 +29,12 @@ def _random_bits(shape, dtype, rng):
 
 @pytest.mark.parametrize("kv_dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("layout", ["split", "interleaved"])
-def test_reshape_and_cache_bit_exact(gpu, kv_dtype, layout):
-    say(f"reshape_and_cache {kv_dtype} {layout}")
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_reshape_and_cache_bit_exact(gpu, kv_dtype, layout, v_layout):
+    say(f"reshape_and_cache {kv_dtype} {layout} v={v_layout}")
     rng = np.random.default_rng(1)
     nb, bs, hkv, d = 13, 16, 4, 64
-    cache = pa.KVCache.allocate(nb, bs, hkv, d, kv_dtype, layout=layout)
+    cache = pa.KVCache.allocate(nb, bs, hkv, d, kv_dtype, layout=layout, v_layout=v_layout)
     kb0 = _random_bits((nb, bs, hkv, d), kv_dtype, rng)
     vb0 = _random_bits((nb, bs, hkv, d), kv_dtype, rng)
     set_pool_bits(cache, "k", kb0)
@@ -65,12 +66,13 @@ def _fp8_sources(rng, T, hkv, d):
 
 @pytest.mark.parametrize("src", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("scale", [1.0, 0.0137])
-def test_reshape_and_cache_fp8_bit_exact(gpu, src, scale):
-    say(f"reshape_and_cache fp8 from {src} scale {scale}")
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_reshape_and_cache_fp8_bit_exact(gpu, src, scale, v_layout):
+    say(f"reshape_and_cache fp8 from {src} scale {scale} v={v_layout}")
     rng = np.random.default_rng(2)
     nb, bs, hkv, d = 6, 8, 2, 128
     ks, vs = scale, scale * 2
-    cache = pa.KVCache.allocate(nb, bs, hkv, d, "fp8", k_scale=ks, v_scale=vs, fill=0x7F)
+    cache = pa.KVCache.allocate(nb, bs, hkv, d, "fp8", k_scale=ks, v_scale=vs, fill=0x7F, v_layout=v_layout)
     T = 20
     x = _fp8_sources(rng, T, hkv, d)
     k_new = x.to(_T[src])
@@ -85,12 +87,14 @@ def test_reshape_and_cache_fp8_bit_exact(gpu, src, scale):
     assert np.array_equal(pool_bits(cache, "v"), vw)
 
 
-@pytest.mark.parametrize("kv_dtype,layout", [("bf16", "split"), ("f16", "interleaved"), ("fp8", "split")])
-def test_copy_blocks_bit_exact(gpu, kv_dtype, layout):
-    say(f"copy_blocks {kv_dtype} {layout}")
+@pytest.mark.parametrize("kv_dtype,layout,v_layout", [("bf16", "split", "token"), ("f16", "interleaved", "token"),
+                                                      ("fp8", "split", "token"), ("bf16", "interleaved", "dim")])
+def test_copy_blocks_bit_exact(gpu, kv_dtype, layout, v_layout):
+    say(f"copy_blocks {kv_dtype} {layout} v={v_layout}")
     rng = np.random.default_rng(3)
     nb, bs, hkv, d = 20, 16, 8, 128
-    cache = pa.KVCache.allocate(nb, bs, hkv, d, kv_dtype, layout=layout, k_scale=0.1, v_scale=0.1)
+    cache = pa.KVCache.allocate(nb, bs, hkv, d, kv_dtype, layout=layout, k_scale=0.1, v_scale=0.1,
+                                v_layout=v_layout)
     kb0 = _random_bits((nb, bs, hkv, d), kv_dtype, rng)
     vb0 = _random_bits((nb, bs, hkv, d), kv_dtype, rng)
     set_pool_bits(cache, "k", kb0)
@@ -107,11 +111,12 @@ def test_copy_blocks_bit_exact(gpu, kv_dtype, layout):
 @pytest.mark.parametrize("wl", [synth.tiny_decode(), synth.random_case(5, [3, 40, 16, 77], 8, 2, 128, 8, "fp8"),
                                 synth.random_case(6, [33, 1, 64], 4, 4, 64, 32, "bf16")],
                          ids=["tiny", "fp8-bs8", "bf16-bs32"])
-def test_library_setup_matches_oracle_pool(gpu, wl):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_library_setup_matches_oracle_pool(gpu, wl, v_layout):
     """Allocator + slot writes through the library give the oracle's pool
     bit for bit (poisoned unused memory included) and the same tables."""
-    say(f"setup {wl.name}")
-    batch, cache, tables, lens, _ = device_setup(wl)
+    say(f"setup {wl.name} v={v_layout}")
+    batch, cache, tables, lens, _ = device_setup(wl, v_layout=v_layout)
     torch.cuda.synchronize()
     alloc, kp_ref, vp_ref, t_ref, l_ref = H.oracle_setup(wl, fill=poison_bits(wl.kv_dtype))
     assert np.array_equal(tables.cpu().numpy(), t_ref) and np.array_equal(lens.cpu().numpy(), l_ref)

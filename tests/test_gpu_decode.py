@@ -32,10 +32,11 @@ def _check(wl, partition_size, out_dtype=torch.float32, **setup):
     return got, ref
 
 
-def test_tiny_config(gpu):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_tiny_config(gpu, v_layout):
     wl = synth.tiny_decode()
     for out_dtype in (torch.float32, torch.float16):
-        got, _ = _check(wl, 0, out_dtype)
+        got, _ = _check(wl, 0, out_dtype, v_layout=v_layout)
         k, v = wl.kv(0)  # the 1-token sequence returns its only V row exactly (G = 1)
         assert np.array_equal(got[0], v[0].double().numpy())
 
@@ -53,64 +54,81 @@ CASES = [
 
 
 @pytest.mark.parametrize("kv,D,bs,G,parts", CASES, ids=lambda c: str(c))
-def test_parity_sweep(gpu, kv, D, bs, G, parts):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_parity_sweep(gpu, kv, D, bs, G, parts, v_layout):
     hkv = 2
     wl = synth.random_case(1000 + D + bs + G, LENGTHS, G * hkv, hkv, D, bs, kv)
-    outs = [_check(wl, p)[0] for p in parts]
+    outs = [_check(wl, p, v_layout=v_layout)[0] for p in parts]
     for o in outs[1:]:  # split and unsplit agree to the same tolerance
         H.assert_close(o, outs[0], what="split vs unsplit")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
-def test_16bit_outputs(gpu, out_dtype):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_16bit_outputs(gpu, out_dtype, v_layout):
     wl = synth.random_case(77, [5, 300, 900], 8, 2, 128, 16, "bf16")
-    _check(wl, 256, out_dtype)
+    _check(wl, 256, out_dtype, v_layout=v_layout)
 
 
-def test_single_token_is_exact(gpu):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_single_token_is_exact(gpu, v_layout):
     wl = synth.random_case(78, [1, 1, 1], 16, 2, 128, 16, "bf16")
-    got, _ = _check(wl, 0)
+    got, _ = _check(wl, 0, v_layout=v_layout)
     for s in range(3):
         v = wl.kv(s)[1][0].double().numpy()  # [Hkv][D]
         assert np.array_equal(got[s], np.repeat(v, 8, axis=0))
 
 
-def test_empty_sequences_give_zeros(gpu):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_empty_sequences_give_zeros(gpu, v_layout):
     wl = synth.random_case(79, [0, 700, 0, 33], 8, 2, 128, 16, "bf16")
     for part in (0, 256):
-        got, _ = _check(wl, part)
+        got, _ = _check(wl, part, v_layout=v_layout)
         assert np.array_equal(got[0], np.zeros_like(got[0])) and np.array_equal(got[2], got[0])
 
 
-def test_physical_placement_is_invisible(gpu):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_physical_placement_is_invisible(gpu, v_layout):
     """Re-placing every block under another permutation gives bit-identical
     outputs: the arithmetic follows logical token order only."""
     wl = synth.random_case(80, [37, 600, 1300, 16], 16, 4, 128, 16, "bf16", headroom=1.0)
     outs = []
     for seed in range(3):
         order = np.random.default_rng(seed).permutation(wl.num_blocks).astype(np.int32)
-        _, cache, tables, lens, max_ctx = device_setup(wl, free_order=order)
+        _, cache, tables, lens, max_ctx = device_setup(wl, free_order=order, v_layout=v_layout)
         outs.append(run_decode(wl, cache, tables, lens, max_ctx, 512))
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
-def test_layouts_and_padding_are_invisible(gpu):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_layouts_and_padding_are_invisible(gpu, v_layout):
     wl = synth.random_case(81, [129, 700, 5], 8, 2, 128, 16, "bf16")
-    a = run_decode(wl, *device_setup(wl, layout="split")[1:], 256)
-    b = run_decode(wl, *device_setup(wl, layout="interleaved", pad=2 ** 30, max_blocks=80)[1:], 256)
+    a = run_decode(wl, *device_setup(wl, layout="split", v_layout=v_layout)[1:], 256)
+    b = run_decode(wl, *device_setup(wl, layout="interleaved", pad=2 ** 30, max_blocks=80, v_layout=v_layout)[1:], 256)
     assert np.array_equal(a, b)
 
 
-def test_block_size_sweep_on_same_logical_data(gpu):
+def test_v_layouts_agree(gpu):
+    """The token-major and dim-major V paths compute the same attention."""
+    wl = synth.random_case(86, [3, 129, 700, 1500], 32, 8, 128, 16, "bf16")
+    a = run_decode(wl, *device_setup(wl, v_layout="token")[1:], 512)
+    b = run_decode(wl, *device_setup(wl, v_layout="dim")[1:], 512)
+    H.assert_close(a, b)
+    H.assert_close(b, H.oracle_contiguous(wl))
+
+
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_block_size_sweep_on_same_logical_data(gpu, v_layout):
     outs = []
     for bs in (8, 16, 32):
         wl = synth.random_case(82, [3, 250, 1000], 16, 2, 128, bs, "bf16")  # values do not depend on bs
-        outs.append(_check(wl, 0)[0])
+        outs.append(_check(wl, 0, v_layout=v_layout)[0])
     H.assert_close(outs[1], outs[0])
     H.assert_close(outs[2], outs[0])
 
 
-def test_needle_follows_logical_order(gpu):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_needle_follows_logical_order(gpu, v_layout):
     """One key is a scaled copy of the (shared) query; every other key is 0.
     The output must be that token's V row, for every logical position."""
     L, hkv, D, G = 96, 1, 128, 4
@@ -124,20 +142,21 @@ def test_needle_follows_logical_order(gpu):
         k[t_star, 0] = 30.0 / (wl.scale * float(qd @ qd)) * qv
         v = torch.randn(L, hkv, D)
         wl._kv_cache[s] = (k.bfloat16(), v.bfloat16())
-    got, _ = _check(wl, 32)
+    got, _ = _check(wl, 32, v_layout=v_layout)
     for s, t_star in enumerate([0, 1, 15, 16, 17, 47, 80, 95]):
         want = wl.kv(s)[1][t_star, 0].double().numpy()
         assert np.abs(got[s] - want).max() < 1e-3
 
 
-def test_forked_sequences_are_bit_identical(gpu):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_forked_sequences_are_bit_identical(gpu, v_layout):
     """Sequences sharing every block (fork) with equal queries give
     bit-identical outputs; a copy-on-write append by one of them leaves the
     others' outputs unchanged, bit for bit."""
     hkv, G, D, bs = 8, 4, 128, 16
     wl = synth.random_case(84, [1000], G * hkv, hkv, D, bs, "bf16", headroom=0.0, min_blocks=200)
     bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
-    cache = pa.KVCache.allocate(wl.num_blocks, bs, hkv, D, "bf16", fill=float("nan"))
+    cache = pa.KVCache.allocate(wl.num_blocks, bs, hkv, D, "bf16", fill=float("nan"), v_layout=v_layout)
     batch = PagedBatch(bm, [cache], 80, 4)
     k, v = wl.kv(0)
     batch.prefill(0, [k], [v])  # 1000 tokens: the last block is partial
@@ -166,11 +185,12 @@ def test_forked_sequences_are_bit_identical(gpu):
     H.assert_close(out1[2].double().numpy(), ref)
 
 
-def test_lengths_beyond_max_context_are_clamped(gpu):
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_lengths_beyond_max_context_are_clamped(gpu, v_layout):
     """A sequence longer than max_context_len is read only up to it (no
     out-of-range access); the others are unaffected."""
     wl = synth.random_case(85, [300, 90], 8, 2, 128, 16, "bf16")
-    _, cache, tables, lens, _ = device_setup(wl)
+    _, cache, tables, lens, _ = device_setup(wl, v_layout=v_layout)
     got = run_decode(wl, cache, tables, lens, 128, 64)
     short = synth.random_case(85, [300, 90], 8, 2, 128, 16, "bf16")
     k, v = wl.kv(0)
