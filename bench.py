@@ -12,8 +12,10 @@ One step = one decode step of the whole path: the host block manager
 allocates one slot per sequence (pa_alloc_batch; copy-on-write pairs, none
 here), packs the tables, one pinned host-to-device copy carries slots /
 pairs / tables / lengths, then per layer pa_copy_blocks (if pairs) ->
-pa_reshape_and_cache (the new token's K/V) -> pa_decode (partition kernel +
-log-sum-exp reduce). Inputs are resident in HBM before timing starts.
+pa_reshape_and_cache (the new token's K/V) -> pa_decode (by default the
+balanced split: one persistent kernel over the resident workgroups, then the
+log-sum-exp merge of sequences cut between them). Inputs are resident in HBM
+before timing starts.
 
 Printed: one JSON line. ``value`` = KV bytes the decode calls of the timed
 steps must read (2 * L * Hkv * D * 2 per sequence and layer, valid tokens
@@ -38,7 +40,9 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) + decode tokens/s"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["decode_kernel.h", "decode.hip", "device_common.h", "decode_bf16.hip"]
+# sources of the kernels a bf16 pa_decode call runs (balanced split and partitions)
+KERNEL_SOURCES = ["decode_sk_kernel.h", "decode_vt_kernel.h", "decode_kernel.h", "decode_dispatch.h", "decode.hip",
+                  "device_common.h", "decode_sk_bf16.hip", "decode_vt_bf16.hip"]
 
 
 def kernel_hash() -> str:
@@ -69,7 +73,8 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--layers", type=int, default=4)
-    p.add_argument("--partition-size", type=int, default=512)
+    p.add_argument("--partition-size", type=int, default=-1,
+                   help="-1: balanced split (default); 0: no split; >0: partitions of that many tokens")
     p.add_argument("--v-layout", choices=["dim", "token"], default="dim",
                    help="in-block V layout: dim-major (matrix-core PV) or the token-major KVBlock layout")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -118,7 +123,7 @@ def cpu_baseline(wl, seconds: float):
         oatt.paged_decode(q, kp, vp, tables, lens, wl.scale, wl.block_size, wl.kv_dtype)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 8:
+        if el >= seconds or reps >= 200:
             break
     return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
@@ -175,7 +180,7 @@ def main():
     k_new = [torch.randn(B, Hkv, D, generator=gen, device=dev).bfloat16() for _ in range(layers)]
     v_new = [torch.randn(B, Hkv, D, generator=gen, device=dev).bfloat16() for _ in range(layers)]
     outs = [torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev) for _ in range(layers)]
-    ws = workspace_for(B, Hq, D, max_blocks * bs, args.partition_size, device=dev)
+    ws = workspace_for(B, Hq, Hkv, D, max_blocks * bs, args.partition_size, device=dev)
     ids = np.arange(B, dtype=np.int64)
     ones = np.ones(B, np.int32)
     torch.cuda.synchronize()
@@ -233,7 +238,8 @@ def main():
         "pa_decode_us": round(call_s * 1e6, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode (paged_decode_kernel + decode_reduce_kernel)",
+            "kernel": ("pa_decode (paged_decode_sk_kernel + decode_sk_merge_kernel)" if args.partition_size < 0
+                       else "pa_decode (partition kernel + decode_reduce_kernel)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

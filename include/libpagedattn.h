@@ -28,6 +28,8 @@
  * stream). They never synchronise the host unless the environment
  * variable PA_DEBUG=1 is set, in which case device-side inputs are copied
  * back and validated before launch (slow; for debugging only).
+ * PA_SK_WGS=n caps the grid of the balanced decode split at n workgroups
+ * (for tests of the split itself; the result is the same up to rounding).
  */
 #ifndef LIBPAGEDATTN_H
 #define LIBPAGEDATTN_H
@@ -39,7 +41,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -252,19 +254,38 @@ pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* pairs, int32_t
  * it). Table entries outside [0, num_blocks) are read as block 0 (no
  * out-of-bounds access; PA_DEBUG=1 reports them).
  *
- * partition_size: 0 = one workgroup per (sequence, KV head) walks the whole
- * context; > 0 (a multiple of 16) splits each context into partitions of
- * that many tokens, one workgroup each, merged by a log-sum-exp reduction.
- * The split needs a workspace of pa_decode_workspace_size(...) bytes
- * (device, 256-byte aligned, contents need no initialisation); 0 bytes
- * otherwise (workspace may be NULL).
+ * partition_size: how the work is divided over workgroups (the result is
+ * the same up to fp32 rounding order):
+ *   0      one workgroup per (sequence, KV head) walks the whole context;
+ *   > 0    (a multiple of 16) each context is cut into partitions of that
+ *          many tokens, one workgroup each, merged by a log-sum-exp
+ *          reduction;
+ *   PA_PARTITION_BALANCED  the batch's 16-token tiles (all sequences and KV
+ *          heads) are divided evenly over the workgroups the device holds at
+ *          once, each walking its share across sequence boundaries;
+ *          sequences cut between workgroups are merged as above. Pools with
+ *          dim-major V only (else PA_ERR_UNSUPPORTED). A workgroup serves
+ *          HW KV heads (the largest divisor of num_kv_heads up to 8) and
+ *          keeps B + 1 ints and HW * G * head_dim floats in 64 KiB of LDS,
+ *          which bounds B (12287 for 8 KV heads, G = 4, head_dim 128;
+ *          beyond it PA_ERR_UNSUPPORTED). The grid depends on the current
+ *          device's CU count, so size the workspace on the device that runs
+ *          the call.
+ * Splits need a workspace of pa_decode_workspace_size(...) bytes (device,
+ * 256-byte aligned, contents need no initialisation); 0 bytes otherwise
+ * (workspace may be NULL).
  *
  * Supported (else PA_ERR_UNSUPPORTED): head_dim 64 or 128; block_size 8,
  * 16 or 32; Hq / num_kv_heads in {1, 2, 4, 8}; pool F16 with q F16, pool
  * BF16 with q BF16, pool FP8_E4M3 with q BF16.
  * ---------------------------------------------------------------------- */
-size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
-                                int32_t partition_size);
+#define PA_PARTITION_BALANCED (-1)
+
+/* Workspace bytes pa_decode needs for these sizes and partition_size (0
+ * when no workspace is needed or the sizes are invalid). For
+ * PA_PARTITION_BALANCED it reads the current device's CU count. */
+size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size);
 
 pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
                     const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,

@@ -22,7 +22,7 @@ from ._lib import PaBmStats, PaKvCache, lib
 __all__ = [
     "PagedAttnError", "OutOfBlocks", "UnknownSeq", "SeqExists", "Unsupported", "InvalidArgument",
     "DeviceError", "BlockManager", "KVCache", "reshape_and_cache", "copy_blocks", "decode",
-    "decode_workspace_size", "lib",
+    "decode_workspace_size", "lib", "BALANCED",
 ]
 
 
@@ -307,9 +307,14 @@ def copy_blocks(cache: KVCache, pairs: torch.Tensor, stream=None) -> None:
     _check(lib().pa_copy_blocks(ctypes.byref(desc), _dev(pairs, "pairs") if n else None, n, _stream(stream)))
 
 
-def decode_workspace_size(batch: int, num_q_heads: int, head_dim: int, max_context_len: int,
+#: partition_size value selecting the balanced split (dim-major V pools)
+BALANCED = _lib.PA_PARTITION_BALANCED
+
+
+def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
                           partition_size: int) -> int:
-    return int(lib().pa_decode_workspace_size(int(batch), int(num_q_heads), int(head_dim),
+    """Workspace bytes of pa_decode (for BALANCED: on the current device)."""
+    return int(lib().pa_decode_workspace_size(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim),
                                               int(max_context_len), int(partition_size)))
 
 
@@ -322,14 +327,16 @@ def decode(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
-    need = decode_workspace_size(B, Hq, D, max_context_len, partition_size)
+    with torch.cuda.device(q.device):
+        need = decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, partition_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     desc = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pa_decode(ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
-                           _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
-                           _dev(context_lens, "context_lens"), int(B), int(Hq), int(max_context_len),
-                           float(scale), int(partition_size), _dev(workspace, "workspace"), ws_bytes,
-                           _stream(stream)))
+    with torch.cuda.device(q.device):
+        _check(lib().pa_decode(ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
+                               _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
+                               _dev(context_lens, "context_lens"), int(B), int(Hq), int(max_context_len),
+                               float(scale), int(partition_size), _dev(workspace, "workspace"), ws_bytes,
+                               _stream(stream)))
     return out

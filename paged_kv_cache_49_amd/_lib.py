@@ -29,6 +29,9 @@ PA_FP8_E4M3 = 3
 PA_LAYOUT_TOKEN_MAJOR = 0
 PA_LAYOUT_DIM_MAJOR = 1
 
+PA_PARTITION_BALANCED = -1
+PA_ABI_VERSION = 2
+
 
 class PaKvCache(ctypes.Structure):
     _fields_ = [
@@ -82,7 +85,7 @@ SIGNATURES = {
     "pa_bm_free_stack": (c_int, [_P, _P, c_int32, _I32P]),
     "pa_reshape_and_cache": (c_int, [POINTER(PaKvCache), _P, _P, c_int, _P, c_int32, _P]),
     "pa_copy_blocks": (c_int, [POINTER(PaKvCache), _P, c_int32, _P]),
-    "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode": (c_int, [POINTER(PaKvCache), _P, c_int, _P, c_int, _P, c_int32, _P, c_int32, c_int32,
                           c_int32, c_float, c_int32, _P, c_size_t, _P]),
 }
@@ -105,7 +108,7 @@ def lib() -> ctypes.CDLL:
                 fn = getattr(handle, name)
                 fn.restype = res
                 fn.argtypes = args
-            if handle.pa_abi_version() != 1:
+            if handle.pa_abi_version() != PA_ABI_VERSION:
                 raise RuntimeError("libpagedattn ABI version mismatch")
             _lib = handle
     return _lib

@@ -13,9 +13,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <vector>
 
 #include "decode_kernel.h"
+#include "decode_sk_kernel.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -67,6 +69,104 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(const ReduceParams p
   }
 }
 
+// Merge the partial pieces of segments whose units span several
+// workgroups, and write zeros for sequences without tokens. grid = (B,
+// head groups); each thread handles 8 head dims of one query head of the
+// group. Pieces are merged in workgroup order.
+struct SkMergeParams {
+  const float* piece_m;
+  const float* piece_l;
+  const float* piece_o;
+  const int32_t* prefix;  // [B + 1]
+  void* out;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t heads_per_wg;
+  int32_t num_head_groups;
+  int32_t group;  // G
+  int32_t head_dim;
+  int32_t num_wgs;  // W of the main launch
+  int32_t out_dtype;
+};
+
+// One workgroup per (head group, sequence) segment, one thread per 8 head
+// dims of one query head. Segment units [fu, lu] lie in the ranges of
+// workgroups wf..wl: wf's piece is its slot 1 when wf's range starts before
+// fu (the segment starts inside it), every other piece is slot 0. Ranges
+// are never empty when U >= W.
+__global__ __launch_bounds__(1024) void decode_sk_merge_kernel(const SkMergeParams p) {
+  const int s = static_cast<int>(blockIdx.x) % p.batch;
+  const int hg = static_cast<int>(blockIdx.x) / p.batch;
+  const int HWG = p.heads_per_wg * p.group;  // query heads per head group
+  const int D = p.head_dim;
+  const int T = p.prefix[p.batch];
+  const int f = p.prefix[s];
+  const int nt = p.prefix[s + 1] - f;
+  const int64_t head0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(hg) * HWG;
+  const int i = static_cast<int>(threadIdx.x) * 8;
+  if (i >= HWG * D) return;
+  const int h = i / D, d = i % D;
+  if (nt == 0) {
+    const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    store_out8(p.out, (head0 + h) * D + d, p.out_dtype, z);
+    return;
+  }
+  const int U = T * p.num_head_groups;
+  const int W = p.num_wgs;
+  const int fu = hg * T + f;
+  const int wf = sk_owner(fu, U, W), wl = sk_owner(fu + nt - 1, U, W);
+  if (wf == wl) return;  // stored by its workgroup
+  const bool may_be_empty = U < W;
+  const bool first_is_slot1 = sk_range_start(wf, U, W) < fu;
+  // pieces are read 8 at a time (one round of loads) and merged with a
+  // running maximum, so a segment with up to 8 pieces costs one round trip
+  constexpr int kChunk = 8;
+  float run_m = -INFINITY, den = 0.f;
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int w0 = wf; w0 <= wl; w0 += kChunk) {
+    float pm[kChunk], pl[kChunk];
+    f32x4 pa_[kChunk], pb_[kChunk];
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const int wv = w0 + k;
+      bool valid = wv <= wl;
+      if (valid && may_be_empty && wv > wf) valid = sk_range_start(wv, U, W) != sk_range_start(wv + 1, U, W);
+      const int slot = wv == wf && first_is_slot1 ? 1 : 0;
+      const int64_t pi = (static_cast<int64_t>(valid ? wv : wf) * 2 + (valid ? slot : (first_is_slot1 ? 1 : 0))) * HWG + h;
+      pm[k] = valid ? p.piece_m[pi] : -INFINITY;
+      pl[k] = p.piece_l[pi];
+      const f32x4* po = reinterpret_cast<const f32x4*>(p.piece_o + pi * D + d);
+      pa_[k] = po[0];
+      pb_[k] = po[1];
+    }
+    float cm = run_m;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) cm = fmaxf(cm, pm[k]);
+    const float r = __builtin_amdgcn_exp2f(run_m - cm);  // 0 on the first chunk (run_m = -inf)
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) num[e] *= r;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float wt = pl[k] * __builtin_amdgcn_exp2f(pm[k] - cm);  // 0 for unused slots (pm = -inf)
+      den += wt;
+      num[0] = fmaf(wt, pa_[k].x, num[0]);
+      num[1] = fmaf(wt, pa_[k].y, num[1]);
+      num[2] = fmaf(wt, pa_[k].z, num[2]);
+      num[3] = fmaf(wt, pa_[k].w, num[3]);
+      num[4] = fmaf(wt, pb_[k].x, num[4]);
+      num[5] = fmaf(wt, pb_[k].y, num[5]);
+      num[6] = fmaf(wt, pb_[k].z, num[6]);
+      num[7] = fmaf(wt, pb_[k].w, num[7]);
+    }
+    run_m = cm;
+  }
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = num[e] / den;
+  store_out8(p.out, (head0 + h) * D + d, p.out_dtype, o);
+}
+
 int out_code(pa_dtype t) { return t == PA_F32 ? 2 : (t == PA_BF16 ? 1 : 0); }
 
 int64_t partitions_for(int32_t max_context_len, int32_t partition_size) {
@@ -80,16 +180,152 @@ size_t workspace_bytes_for(int64_t B, int64_t Hq, int64_t D, int64_t P) {
   return 2 * align_up(rows * sizeof(float)) + align_up(rows * D * sizeof(float));
 }
 
+// ---- balanced split
+// At most kSkWavesPerCu waves of the balanced kernel per CU: it bounds the
+// grid, so the piece buffers can be sized before the launch.
+constexpr int kSkWavesPerCu = 32;
+constexpr size_t kSkMaxLds = 64 * 1024;
+
+// KV heads per workgroup: the largest divisor of num_kv_heads up to 8
+int sk_heads_per_wg(int hkv) {
+  for (int hw = 8; hw > 1; --hw)
+    if (hkv % hw == 0) return hw;
+  return 1;
+}
+
+// CUs of the current device (cached per device)
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
+}
+
+struct SkLayout {
+  size_t prefix, m, l, o, total;  // byte offsets and total size
+};
+
+// workspace of the balanced split: tile prefix [B + 1], then per piece row
+// (workgroup, slot, query head of the group) m, l and o[D]
+SkLayout sk_layout(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int cus) {
+  const int64_t G = Hq / hkv;
+  // W * HW <= cus * kSkWavesPerCu, and a workgroup holds 2 * HW * G rows
+  const size_t rows = static_cast<size_t>(cus) * kSkWavesPerCu * 2 * G;
+  SkLayout L{};
+  L.prefix = 0;
+  L.m = align_up(static_cast<size_t>(B + 1) * sizeof(int32_t));
+  L.l = L.m + align_up(rows * sizeof(float));
+  L.o = L.l + align_up(rows * sizeof(float));
+  L.total = L.o + align_up(rows * D * sizeof(float));
+  return L;
+}
+
 }  // namespace
+
+// The balanced split: one launch of the persistent kernel over the device's
+// resident workgroups, then the merge of sequences cut between them. The
+// arguments are validated by pa_decode.
+pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, const void* q,
+                          const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                          int32_t num_q_heads, int32_t max_context_len, float qk_scale_log2, float v_scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int32_t hkv = cache->num_kv_heads;
+  const int32_t D = cache->head_dim;
+  const int32_t G = num_q_heads / hkv;
+  const SkLaunch launch = find_decode_sk(cache->dtype, D, cache->block_size, G);
+  if (launch == nullptr)
+    return fail(PA_ERR_UNSUPPORTED, "no balanced decode kernel for head_dim %d, block_size %d, group %d", D,
+                cache->block_size, G);
+  const int HW = sk_heads_per_wg(hkv);
+  const int n_hg = hkv / HW;
+  if (sk_lds_bytes(B, HW, G, D) > kSkMaxLds)
+    return fail(PA_ERR_UNSUPPORTED, "B = %d is too large for the balanced split (use partition_size > 0)", B);
+  // units (16-token tiles x head groups) must stay below 2^31
+  if (static_cast<int64_t>(B) * ((static_cast<int64_t>(max_context_len) + 15) / 16) * n_hg > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "B x max_context_len is too large for the balanced split");
+  if (workspace == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "the balanced split needs a workspace");
+  const int cus = device_cus();
+  if (cus <= 0) return fail(PA_ERR_DEVICE, "cannot read the device's CU count");
+  const SkLayout lay = sk_layout(B, num_q_heads, hkv, D, cus);
+  if (workspace == nullptr || workspace_bytes < lay.total)
+    return fail(PA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed (got %zu)", lay.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  SkParams p{};
+  p.q = q;
+  p.k_pool = cache->k;
+  p.v_pool = cache->v;
+  p.out = out;
+  p.piece_m = reinterpret_cast<float*>(ws + lay.m);
+  p.piece_l = reinterpret_cast<float*>(ws + lay.l);
+  p.piece_o = reinterpret_cast<float*>(ws + lay.o);
+  p.prefix_out = reinterpret_cast<int32_t*>(ws + lay.prefix);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.block_stride = cache->block_stride;
+  p.num_blocks = cache->num_blocks;
+  p.num_kv_heads = hkv;
+  p.num_q_heads = num_q_heads;
+  p.max_blocks = max_blocks;
+  p.len_cap = max_context_len;
+  p.batch = B;
+  p.heads_per_wg = HW;
+  p.num_head_groups = n_hg;
+  p.out_dtype = out_code;
+  p.qk_scale_log2 = qk_scale_log2;
+  p.v_scale = v_scale;
+  int max_wgs = cus * kSkWavesPerCu / HW;
+  if (const char* cap = std::getenv("PA_SK_WGS")) {
+    const int v = std::atoi(cap);
+    if (v > 0 && v < max_wgs) max_wgs = v;
+  }
+  int wgs = 0;
+  hipError_t e = launch(p, cus, max_wgs, stream, &wgs);
+  if (e != hipSuccess) return fail(PA_ERR_DEVICE, "balanced decode launch: %s", hipGetErrorString(e));
+  SkMergeParams m{};
+  m.piece_m = p.piece_m;
+  m.piece_l = p.piece_l;
+  m.piece_o = p.piece_o;
+  m.prefix = p.prefix_out;
+  m.out = out;
+  m.batch = B;
+  m.num_q_heads = num_q_heads;
+  m.heads_per_wg = HW;
+  m.num_head_groups = n_hg;
+  m.group = G;
+  m.head_dim = D;
+  m.num_wgs = wgs;
+  m.out_dtype = out_code;
+  // one thread per 8 head dims of each query head of a head group
+  const int merge_threads = (HW * G * D / 8 + 63) / 64 * 64;
+  hipLaunchKernelGGL(decode_sk_merge_kernel, dim3(B * n_hg), dim3(merge_threads), 0, stream, m);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_DEVICE, "balanced decode merge launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 }  // namespace pa
 
 using pa::fail;
 
 extern "C" {
 
-size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
-                                int32_t partition_size) {
-  if (B <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size) {
+  if (B <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  if (partition_size == PA_PARTITION_BALANCED) {
+    if (num_q_heads % num_kv_heads != 0) return 0;
+    const int cus = pa::device_cus();
+    if (cus <= 0) return 0;
+    return pa::sk_layout(B, num_q_heads, num_kv_heads, head_dim, cus).total;
+  }
+  if (max_context_len == 0) return 0;
   return pa::workspace_bytes_for(B, num_q_heads, head_dim, pa::partitions_for(max_context_len, partition_size));
 }
 
@@ -136,10 +372,14 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks) * bs)
     return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len %d > max_blocks %d * block_size %d", max_context_len,
                 max_blocks, bs);
-  if (partition_size < 0 || partition_size % 16 != 0)
-    return fail(PA_ERR_INVALID_ARGUMENT, "partition_size %d must be 0 or a positive multiple of 16", partition_size);
+  const bool balanced = partition_size == PA_PARTITION_BALANCED;
+  if (!balanced && (partition_size < 0 || partition_size % 16 != 0))
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "partition_size %d must be 0, a positive multiple of 16 or PA_PARTITION_BALANCED", partition_size);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (hkv > 65535 || B > 65535) return fail(PA_ERR_INVALID_ARGUMENT, "B and num_kv_heads must be <= 65535");
+  if (balanced && cache->v_layout != PA_LAYOUT_DIM_MAJOR)
+    return fail(PA_ERR_UNSUPPORTED, "PA_PARTITION_BALANCED needs a pool with dim-major V blocks");
   const int64_t P = pa::partitions_for(max_context_len, partition_size);
   if (P > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many partitions");
   const size_t need = pa::workspace_bytes_for(B, num_q_heads, D, P);
@@ -169,6 +409,15 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
     }
   }
 
+  const int out_c = pa::out_code(out_dtype);
+  const bool fp8 = cache->dtype == PA_FP8_E4M3;
+  const float qk_scale_log2 = scale * (fp8 ? cache->k_scale : 1.0f) * 1.44269504088896340736f;
+  const float v_scale = fp8 ? cache->v_scale : 1.0f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (balanced) return pa::decode_balanced(cache, out, out_c, q, block_tables, max_blocks, context_lens, B,
+                                           num_q_heads, max_context_len, qk_scale_log2, v_scale, workspace,
+                                           workspace_bytes, s);
+
   pa::DecodeParams prm{};
   prm.q = q;
   prm.k_pool = cache->k;
@@ -191,12 +440,9 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
   prm.len_cap = max_context_len;
   prm.partition_size = P > 1 ? partition_size : 0;
   prm.num_partitions = static_cast<int32_t>(P);
-  prm.out_dtype = pa::out_code(out_dtype);
-  const bool fp8 = cache->dtype == PA_FP8_E4M3;
-  prm.qk_scale_log2 = scale * (fp8 ? cache->k_scale : 1.0f) * 1.44269504088896340736f;
-  prm.v_scale = fp8 ? cache->v_scale : 1.0f;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  prm.out_dtype = out_c;
+  prm.qk_scale_log2 = qk_scale_log2;
+  prm.v_scale = v_scale;
   const int64_t wgs = P * hkv * B;
   if (wgs > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many workgroups (%lld)", (long long)wgs);
   hipError_t e = launch(prm, dim3(static_cast<uint32_t>(wgs)), s);

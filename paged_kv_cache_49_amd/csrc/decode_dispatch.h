@@ -11,6 +11,11 @@ namespace pa {
 
 struct DecodeParams;
 using DecodeLaunch = hipError_t (*)(const DecodeParams&, dim3 grid, hipStream_t stream);
+// balanced split (dim-major V only): the launcher sizes the grid from the
+// device's CU count and the kernel's occupancy, at most max_wgs workgroups,
+// and reports the grid it used in *wgs
+struct SkParams;
+using SkLaunch = hipError_t (*)(const SkParams&, int cus, int max_wgs, hipStream_t stream, int* wgs);
 
 DecodeLaunch find_decode_f16(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_bf16(int head_dim, int block_size, int group);
@@ -19,6 +24,19 @@ DecodeLaunch find_decode_fp8(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_vt_f16(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_vt_bf16(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_vt_fp8(int head_dim, int block_size, int group);
+
+SkLaunch find_decode_sk_f16(int head_dim, int block_size, int group);
+SkLaunch find_decode_sk_bf16(int head_dim, int block_size, int group);
+SkLaunch find_decode_sk_fp8(int head_dim, int block_size, int group);
+
+inline SkLaunch find_decode_sk(pa_dtype pool, int head_dim, int block_size, int group) {
+  switch (pool) {
+    case PA_F16: return find_decode_sk_f16(head_dim, block_size, group);
+    case PA_BF16: return find_decode_sk_bf16(head_dim, block_size, group);
+    case PA_FP8_E4M3: return find_decode_sk_fp8(head_dim, block_size, group);
+    default: return nullptr;
+  }
+}
 
 inline DecodeLaunch find_decode(pa_dtype pool, pa_layout v_layout, int head_dim, int block_size, int group) {
   const bool vt = v_layout == PA_LAYOUT_DIM_MAJOR;

@@ -1,0 +1,9 @@
+// Balanced-split decode kernels for FP8 E4M3 pools (q BF16) with dim-major V blocks:
+// head_dim 64/128, block size 8/16/32, query-head group 1/2/4/8.
+#include "decode_sk_kernel.h"
+
+namespace pa {
+SkLaunch find_decode_sk_fp8(int head_dim, int block_size, int group) {
+  return select_decode_sk<FP8, BF16>(head_dim, block_size, group);
+}
+}  // namespace pa

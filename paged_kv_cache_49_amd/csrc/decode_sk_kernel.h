@@ -1,0 +1,491 @@
+// Paged decode attention over dim-major V blocks with the whole batch's
+// work divided evenly over persistent workgroups (balanced split).
+//
+// [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
+// [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
+// Same result as the other decode kernels (decode_kernel.h states what is
+// computed: softmax attention of each query head over its sequence's tokens
+// in logical order, gathered through the block table); the per-tile data
+// flow (QK and PV on the matrix cores, online softmax) is that of
+// decode_vt_kernel.h.
+//
+// Work units are 16-token tiles, numbered head group-major, then sequence,
+// then tile: unit = hg * T + prefix[s] + tile, T = total tiles of the batch.
+// A head group is HW consecutive KV heads; a workgroup has HW waves and wave
+// i serves KV head hg * HW + i, so one unit reads all HW heads of a 16-token
+// block row at once (a whole block when HW = num_kv_heads). The grid holds
+// W workgroups, about as many as are resident at once; workgroup w takes the
+// units [w U / W, (w + 1) U / W), so all of them stream the same number of
+// tiles, and a wave walks from one sequence into the next without ending.
+//
+// Per workgroup:
+//  * plan: tiles per sequence (lengths clamped to the launch bound) and
+//    their exclusive prefix go to LDS; workgroup 0 also copies the prefix
+//    out for the merge kernel.
+//  * unit batches: lane i of a batch resolves unit ub + i to its sequence,
+//    tile, length, head group and block id(s); the batch after it is
+//    requested one batch ahead, so block-table reads never stall the loads.
+//  * a 3-deep register ring keeps the K and V loads of two tiles in flight
+//    while a third tile is computed.
+//  * a (head group, sequence) segment that ends inside the range is
+//    normalised and stored directly; a segment cut by the range's start or
+//    end leaves a partial (m, l, o) piece in slot 0 (it reaches back to the
+//    range start) or slot 1 (it starts inside the range), which
+//    decode_sk_merge_kernel combines with the pieces of the neighbouring
+//    workgroups (the log-sum-exp merge described in decode.hip).
+#pragma once
+
+#include "decode_vt_kernel.h"
+
+namespace pa {
+
+struct SkParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  void* out;
+  float* piece_m;       // [W][2][HW * G]
+  float* piece_l;       // [W][2][HW * G]
+  float* piece_o;       // [W][2][HW * G][D]
+  int32_t* prefix_out;  // [B + 1] tile prefix, written by workgroup 0
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int64_t block_stride;  // elements
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t max_blocks;
+  int32_t len_cap;
+  int32_t batch;
+  int32_t heads_per_wg;     // HW
+  int32_t num_head_groups;  // num_kv_heads / HW
+  int32_t out_dtype;
+  float qk_scale_log2;
+  float v_scale;
+};
+
+// first unit of workgroup w's range; the range of w is [start(w), start(w + 1))
+__device__ __forceinline__ int sk_range_start(int w, int U, int W) {
+  return static_cast<int>(static_cast<int64_t>(w) * U / W);
+}
+// the workgroup whose (non-empty) range holds unit u
+__device__ __forceinline__ int sk_owner(int u, int U, int W) {
+  return static_cast<int>((static_cast<int64_t>(u + 1) * W - 1) / U);
+}
+
+// first sequence s with pref[s + 1] > r: the sequence holding tile r of a
+// head group (sequences without tiles are skipped)
+__device__ __forceinline__ int sk_find_seq(const int32_t* pref, int B, int r) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (pref[mid + 1] > r) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// bytes of dynamic LDS: the tile prefix, then per wave one G x D fp32 tile
+inline size_t sk_lds_bytes(int B, int HW, int G, int D) {
+  const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
+  return pref + static_cast<size_t>(HW) * G * D * sizeof(float);
+}
+
+// A unit as the wave sees it (uniform values).
+struct SkUnit {
+  int seq, tile, len, hg;
+};
+
+template <typename KV, typename QT, int D, int BS, int G>
+__global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) {
+  using C = DecodeCfg<KV, D, BS, G>;
+  constexpr int kB = C::kB;
+  constexpr int kNT = D / 16;
+  static_assert(G <= 16, "at most 16 query heads per KV head");
+  using VRaw = typename VVecT<KV>::raw_dm;
+  extern __shared__ int32_t sk_smem[];
+  const int B = p.batch;
+  int32_t* s_pref = sk_smem;  // [B + 1]
+  float* s_out_all = reinterpret_cast<float*>(sk_smem + (B + 1 + 3) / 4 * 4);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int HW = p.heads_per_wg;
+
+  // ---- plan: tiles per sequence, then their exclusive prefix (in place)
+  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    int L = p.context_lens[i];
+    L = L < p.len_cap ? L : p.len_cap;
+    s_pref[i] = L > 0 ? (L + 15) >> 4 : 0;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int per = (B + 63) / 64;
+    const int i0 = lane * per, i1 = min(B, i0 + per);
+    int run = 0;
+    for (int i = i0; i < i1; ++i) run += s_pref[i];
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    int acc_t = incl - run;
+    for (int i = i0; i < i1; ++i) {
+      const int c = s_pref[i];
+      s_pref[i] = acc_t;
+      acc_t += c;
+    }
+    if (lane == 63) s_pref[B] = incl;
+  }
+  __syncthreads();
+  const int T = s_pref[B];
+  const int U = T * p.num_head_groups;  // the launch guarantees U < 2^31
+  const int W = static_cast<int>(gridDim.x);
+  const int w = static_cast<int>(blockIdx.x);
+  if (w == 0)
+    for (int i = threadIdx.x; i <= B; i += blockDim.x) p.prefix_out[i] = s_pref[i];
+  const int u0 = sk_range_start(w, U, W), u1 = sk_range_start(w + 1, U, W);
+  if (u0 >= u1) return;
+
+  float* s_out = s_out_all + wave * G * D;
+  const int col = lane & 15, j = lane >> 4;
+  const int Hkv = p.num_kv_heads;
+  const char* kbase = static_cast<const char*>(p.k_pool);
+  const char* vbase = static_cast<const char*>(p.v_pool);
+  const int64_t blk_bytes = p.block_stride * kB;
+  const int64_t tok_bytes = static_cast<int64_t>(Hkv) * D * kB;
+  constexpr int kVTileBytes = 16 * BS * kB;  // one 16-dim n-tile of a block
+  // lane parts of the addresses: K row `col` (first head-dim slice), V run
+  // of head dim `col` from token 4j
+  const uint32_t koff_lane = static_cast<uint32_t>(col * tok_bytes + qk_dim<kB>(0, j) * kB);
+  const uint32_t voff_lane = static_cast<uint32_t>((col * BS + 4 * j) * kB);
+
+  // ---- unit batches: lane i resolves unit ub + i (ub is uniform). The
+  // length and block ids are kept as loaded (clamped when a unit is read
+  // out), so nothing waits for these loads until the batch is used.
+  struct Batch {
+    int ub;
+    int seq, tile, len, hg, ida, idb;
+  };
+  // Lanes past the range resolve the range's last unit: every lane loads,
+  // so the loads land in the batch registers with no merge that would wait.
+  auto resolve = [&](int ub) -> Batch {
+    Batch b;
+    b.ub = ub;
+    const int u = min(ub + lane, u1 - 1);
+    const int hg = u / T;
+    const int r = u - hg * T;
+    const int s = sk_find_seq(s_pref, B, r);
+    const int t = r - s_pref[s];
+    const int32_t* row = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
+    const int blk_a = BS >= 16 ? (t * 16) / BS : 2 * t;
+    b.len = p.context_lens[s];
+    b.ida = row[blk_a];
+    // the tile's second block; past the sequence's last block its value is
+    // never used (those tokens are masked)
+    b.idb = BS < 16 ? row[min(blk_a + 1, p.max_blocks - 1)] : 0;
+    b.seq = s;
+    b.tile = t;
+    b.hg = hg;
+    return b;
+  };
+  auto block_id = [&](int id) { return static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks) ? id : 0; };
+  // ---- loads of one unit into a ring slot; returns the unit
+  auto load_unit = [&](const Batch& b, int x, u32x4 (&kr)[C::kKLoads], VRaw (&vr)[kNT]) -> SkUnit {
+    const int o = x - b.ub;
+    SkUnit un;
+    un.seq = __builtin_amdgcn_readlane(b.seq, o);
+    un.tile = __builtin_amdgcn_readlane(b.tile, o);
+    un.len = min(__builtin_amdgcn_readlane(b.len, o), p.len_cap);
+    un.hg = __builtin_amdgcn_readlane(b.hg, o);
+    const int ida = block_id(__builtin_amdgcn_readlane(b.ida, o));
+    const int g = un.hg * HW + wave;
+    if constexpr (BS >= 16) {
+      const int tin = (un.tile * 16) % BS;
+      const char* kb = kbase + static_cast<int64_t>(ida) * blk_bytes + tin * tok_bytes + static_cast<int64_t>(g) * D * kB;
+      const char* krow = kb + koff_lane;
+#pragma unroll
+      for (int i = 0; i < C::kKLoads; ++i) {
+        const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
+        kr[i] = *reinterpret_cast<const u32x4*>(krow + off - qk_dim<kB>(0, j) * kB);
+      }
+      const char* vb = vbase + static_cast<int64_t>(ida) * blk_bytes + (static_cast<int64_t>(g) * D * BS + tin) * kB;
+      const char* vrun = vb + voff_lane;
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VRaw*>(vrun + nt * kVTileBytes);
+    } else {
+      // a tile spans two blocks: tokens 0..BS-1 in block A, the rest in B
+      const int idb = block_id(__builtin_amdgcn_readlane(b.idb, o));
+      const int idk = col < BS ? ida : idb;
+      const char* krow = kbase + static_cast<int64_t>(idk) * blk_bytes + (col % BS) * tok_bytes +
+                         static_cast<int64_t>(g) * D * kB;
+#pragma unroll
+      for (int i = 0; i < C::kKLoads; ++i) {
+        const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
+        kr[i] = *reinterpret_cast<const u32x4*>(krow + off);
+      }
+      const int t4 = 4 * j;
+      const int idv = t4 < BS ? ida : idb;
+      const char* vrun = vbase + static_cast<int64_t>(idv) * blk_bytes +
+                         ((static_cast<int64_t>(g) * D + col) * BS + t4 % BS) * kB;
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VRaw*>(vrun + nt * kVTileBytes);
+    }
+    return un;
+  };
+
+  // ---- q rows of a segment as the B operand of S^T = K q^T. Columns >= G
+  // repeat head 0 (finite logits whose weights are forced to zero), so the
+  // loaded values are used as they are and the load is waited for only
+  // where q is first used.
+  auto load_q = [&](int seq, int hg, u32x4 (&dst)[C::kKSteps]) {
+    const int64_t head0 = static_cast<int64_t>(seq) * p.num_q_heads + static_cast<int64_t>(hg * HW + wave) * G;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
+#pragma unroll
+    for (int i = 0; i < C::kKSteps; ++i) dst[i] = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
+  };
+  auto locate = [&](int u, int& seq, int& hg) {
+    hg = u / T;
+    seq = sk_find_seq(s_pref, B, u - hg * T);
+  };
+
+  // ---- segment state: the current segment and the one after it (q prefetched)
+  int seg_seq, seg_hg, nseq = 0, nhg = 0;
+  locate(u0, seg_seq, seg_hg);
+  bool seg_first = true;                                 // reaches back to u0
+  bool seg_begun = u0 == seg_hg * T + s_pref[seg_seq];  // starts inside the range
+  u32x4 qb[C::kKSteps], qn[C::kKSteps];
+  load_q(seg_seq, seg_hg, qb);
+  {
+    const int after = seg_hg * T + s_pref[seg_seq + 1];
+    if (after < u1) {
+      locate(after, nseq, nhg);
+      load_q(nseq, nhg, qn);
+    }
+  }
+
+  float m_w = -INFINITY;  // running reference max of head `col` (log2 domain)
+  float l_w = 0.f;        // this lane's share of head `col`'s weight sum
+  f32x4 acc[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // store the segment that just ended: final output, or a partial piece
+  auto flush = [&](bool complete, int slot) {
+    float l_head = l_w + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_w), 0x401F));
+    l_head += __shfl_xor(l_head, 32, 64);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * j + r;
+      const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
+      if (h < G) {
+        const float inv = p.v_scale / lr;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) s_out[h * D + nt * 16 + col] = acc[nt][r] * inv;
+      }
+    }
+    wave_lds_sync();
+    const int64_t head0 = static_cast<int64_t>(seg_seq) * p.num_q_heads + static_cast<int64_t>(seg_hg * HW + wave) * G;
+    const int64_t pbase = ((static_cast<int64_t>(w) * 2 + slot) * HW + wave) * G;
+    for (int i = lane * 8; i < G * D; i += 64 * 8) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = s_out[i + e];
+      const int h = i / D, d = i % D;
+      if (complete) {
+        store_out8(p.out, (head0 + h) * D + d, p.out_dtype, o);
+      } else {
+        float* po = p.piece_o + (pbase + h) * D + d;
+        *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
+      }
+    }
+    if (!complete && lane < G) {
+      p.piece_m[pbase + lane] = m_w;
+      p.piece_l[pbase + lane] = l_head;
+    }
+    wave_lds_sync();
+  };
+
+  auto compute = [&](int x, const SkUnit& un, const u32x4 (&kr)[C::kKLoads], const VRaw (&vr)[kNT]) {
+    const int tb = un.tile * 16;
+    const int L = un.len;
+    // ---- S^T = K q^T
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kB == 2) {
+#pragma unroll
+      for (int i = 0; i < C::kKSteps; ++i) sacc = mfma_16x16x32<QT>(kr[i], qb[i], sacc);
+    } else {
+#pragma unroll
+      for (int a = 0; a < C::kKLoads; ++a) {
+        const u32x2 b0 = e4m3x4_to_bf16x4(kr[a].x), b1 = e4m3x4_to_bf16x4(kr[a].y);
+        const u32x2 b2 = e4m3x4_to_bf16x4(kr[a].z), b3 = e4m3x4_to_bf16x4(kr[a].w);
+        sacc = mfma_16x16x32<QT>(u32x4{b0.x, b0.y, b1.x, b1.y}, qb[2 * a], sacc);
+        sacc = mfma_16x16x32<QT>(u32x4{b2.x, b2.y, b3.x, b3.y}, qb[2 * a + 1], sacc);
+      }
+    }
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = tb + 4 * j + r < L ? sacc[r] * p.qk_scale_log2 : -INFINITY;
+    // ---- online softmax (head = col)
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool need = col < G && mx > m_w + C::kSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float a = need ? __builtin_amdgcn_exp2f(m_w - mx) : 1.0f;
+      m_w = need ? mx : m_w;
+      l_w *= a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(a, 4 * j + r, 64);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) acc[nt][r] *= ar;
+      }
+    }
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pw[r] = col < G ? __builtin_amdgcn_exp2f(sv[r] - m_w) : 0.f;
+      l_w += pw[r];
+    }
+    const uint32_t h0 = pack2<QT>(pw[0], pw[1]), h1 = pack2<QT>(pw[2], pw[3]);
+    const uint32_t l0 = pack2<QT>(pw[0] - half_lo<QT>(h0), pw[1] - half_hi<QT>(h0));
+    const uint32_t l1 = pack2<QT>(pw[2] - half_lo<QT>(h1), pw[3] - half_hi<QT>(h1));
+    const u32x2 phi = {h0, h1}, plo = {l0, l1};
+    // ---- PV
+    u32x2 vmask = {0xffffffffu, 0xffffffffu};
+    if (tb + 16 > L) {
+      const int t = tb + 4 * j;
+      vmask.x = (t < L ? 0xffffu : 0u) | (t + 1 < L ? 0xffff0000u : 0u);
+      vmask.y = (t + 2 < L ? 0xffffu : 0u) | (t + 3 < L ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      u32x2 vop;
+      if constexpr (kB == 2) {
+        vop = vr[nt];
+      } else {
+        vop = e4m3x4_to_bf16x4(vr[nt]);
+      }
+      vop.x &= vmask.x;
+      vop.y &= vmask.y;
+      acc[nt] = mfma_16x16x16<QT>(phi, vop, acc[nt]);
+      acc[nt] = mfma_16x16x16<QT>(plo, vop, acc[nt]);
+    }
+    // ---- end of a segment: store it, then start the next one at x + 1
+    const bool seq_end = un.tile == ((L + 15) >> 4) - 1;
+    if (seq_end || x + 1 == u1) {
+      flush(seg_begun && seq_end, seg_first ? 0 : 1);
+      if (x + 1 < u1) {
+        seg_seq = nseq;
+        seg_hg = nhg;
+        seg_first = false;
+        seg_begun = true;
+#pragma unroll
+        for (int i = 0; i < C::kKSteps; ++i) qb[i] = qn[i];
+        const int after = seg_hg * T + s_pref[seg_seq + 1];
+        if (after < u1) {
+          locate(after, nseq, nhg);
+          load_q(nseq, nhg, qn);
+        }
+        m_w = -INFINITY;
+        l_w = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  // ---- the ring: units x + 1 and x + 2 in flight while x is computed.
+  // Loads are unconditional: past the range they repeat the last unit (an
+  // L2 hit), so every path through the loop carries the same loads.
+  // Batches: an outer step covers 63 units (21 ring iterations); its batch
+  // holds the units it loads (uk + 2 .. uk + 65), and the next step's batch
+  // is requested when the step starts.
+  u32x4 k0[C::kKLoads], k1[C::kKLoads], k2[C::kKLoads];
+  VRaw v0[kNT], v1[kNT], v2[kNT];
+  const int ulast = u1 - 1;
+  Batch cur = resolve(u0);
+  Batch nxt = resolve(min(u0 + 2, ulast));
+  // the prologue issues its loads in the loop's order (K then V, unit by
+  // unit), so the wait counts the compiler derives for the loop hold on
+  // entry too
+  SkUnit n0 = load_unit(cur, u0, k0, v0);
+  __builtin_amdgcn_sched_barrier(0);
+  SkUnit n1 = load_unit(cur, min(u0 + 1, ulast), k1, v1);
+  __builtin_amdgcn_sched_barrier(0);
+  int uk = u0;
+  do {
+    cur = nxt;
+    nxt = resolve(min(uk + 65, ulast));
+    const int uend = min(uk + 63, u1);
+    int u = uk;
+    do {
+      SkUnit n2 = load_unit(cur, min(u + 2, ulast), k2, v2);
+      compute(u, n0, k0, v0);
+      n0 = load_unit(cur, min(u + 3, ulast), k0, v0);
+      if (u + 1 <= ulast) compute(u + 1, n1, k1, v1);
+      n1 = load_unit(cur, min(u + 4, ulast), k1, v1);
+      if (u + 2 <= ulast) compute(u + 2, n2, k2, v2);
+      u += 3;
+    } while (u < uend);
+    uk += 63;
+  } while (uk <= ulast);
+}
+
+// Launch of the balanced kernel: W = resident workgroups (occupancy x CUs),
+// at most max_wgs. Writes the grid size used to *wgs.
+template <typename KV, typename QT, int D, int BS, int G>
+hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
+  const int HW = p.heads_per_wg;
+  const size_t lds = sk_lds_bytes(p.batch, HW, G, D);
+  // occupancy per (HW, LDS in 4 KiB steps); racing writers store the same value
+  static int cache[9][17];
+  const int lb = static_cast<int>((lds + 4095) / 4096);
+  int occ = (HW <= 8 && lb <= 16) ? cache[HW][lb] : 0;
+  if (occ <= 0) {
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, paged_decode_sk_kernel<KV, QT, D, BS, G>,
+                                                                64 * HW, lds);
+    if (e != hipSuccess) return e;
+    if (occ <= 0) return hipErrorInvalidConfiguration;
+    if (HW <= 8 && lb <= 16) cache[HW][lb] = occ;
+  }
+  int W = cus * occ;
+  W = W < max_wgs ? W : max_wgs;
+  *wgs = W;
+  hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G>), dim3(W), dim3(64 * HW), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <typename KV, typename QT, int D, int BS>
+SkLaunch select_decode_sk_g(int G) {
+  switch (G) {
+    case 1: return &launch_decode_sk<KV, QT, D, BS, 1>;
+    case 2: return &launch_decode_sk<KV, QT, D, BS, 2>;
+    case 4: return &launch_decode_sk<KV, QT, D, BS, 4>;
+    case 8: return &launch_decode_sk<KV, QT, D, BS, 8>;
+    default: return nullptr;
+  }
+}
+
+template <typename KV, typename QT, int D>
+SkLaunch select_decode_sk_bs(int BS, int G) {
+  switch (BS) {
+    case 8: return select_decode_sk_g<KV, QT, D, 8>(G);
+    case 16: return select_decode_sk_g<KV, QT, D, 16>(G);
+    case 32: return select_decode_sk_g<KV, QT, D, 32>(G);
+    default: return nullptr;
+  }
+}
+
+template <typename KV, typename QT>
+SkLaunch select_decode_sk(int D, int BS, int G) {
+  switch (D) {
+    case 64: return select_decode_sk_bs<KV, QT, 64>(BS, G);
+    case 128: return select_decode_sk_bs<KV, QT, 128>(BS, G);
+    default: return nullptr;
+  }
+}
+
+}  // namespace pa

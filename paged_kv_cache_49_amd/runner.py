@@ -126,7 +126,8 @@ class PagedBatch:
         return max_ctx
 
 
-def workspace_for(batch: int, num_q_heads: int, head_dim: int, max_context_len: int, partition_size: int,
-                  device="cuda") -> Optional[torch.Tensor]:
-    n = decode_workspace_size(batch, num_q_heads, head_dim, max_context_len, partition_size)
+def workspace_for(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
+                  partition_size: int, device="cuda") -> Optional[torch.Tensor]:
+    with torch.cuda.device(device):
+        n = decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None

@@ -32,7 +32,10 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(handle, n), f"{n} declared in libpagedattn.h but not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
-    assert pa.lib().pa_abi_version() == 1
+    header_version = int(re.search(r"#define PA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert pa.lib().pa_abi_version() == header_version == _lib.PA_ABI_VERSION
+    assert int(re.search(r"#define PA_PARTITION_BALANCED \((-?\d+)\)", open(HEADER).read()).group(1)) == \
+        _lib.PA_PARTITION_BALANCED
 
 
 def test_status_strings():
@@ -192,6 +195,11 @@ def _decode_status(cache, **kw):
     (dict(), dict(v_layout=7), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(), dict(dtype=_lib.PA_FP8_E4M3, k_scale=0.0), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(B=0), dict(), _lib.PA_OK),                             # empty batch: nothing to do
+    (dict(part=-2), dict(), _lib.PA_ERR_INVALID_ARGUMENT),       # negative, not BALANCED
+    (dict(part=-1), dict(), _lib.PA_ERR_UNSUPPORTED),            # balanced split needs dim-major V
+    (dict(part=-1), dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR), _lib.PA_ERR_INVALID_ARGUMENT),  # no workspace
+    (dict(part=-1, B=20000, max_ctx=16), dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR),
+     _lib.PA_ERR_UNSUPPORTED),                                   # prefix does not fit LDS
 ])
 def test_decode_rejects_bad_arguments_before_launch(kw, cache_kw, want):
     assert _decode_status(_fake_cache(**cache_kw), **kw) == want
@@ -201,10 +209,13 @@ def test_decode_rejects_bad_arguments_before_launch(kw, cache_kw, want):
 
 def test_workspace_size():
     f = pa.decode_workspace_size
-    assert f(64, 32, 128, 4096, 0) == 0
-    assert f(64, 32, 128, 512, 512) == 0
+    assert f(64, 32, 8, 128, 4096, 0) == 0
+    assert f(64, 32, 8, 128, 512, 512) == 0
     rows = 64 * 32 * 8
-    assert f(64, 32, 128, 4096, 512) == 2 * ((rows * 4 + 255) // 256 * 256) + rows * 128 * 4
+    assert f(64, 32, 8, 128, 4096, 512) == 2 * ((rows * 4 + 255) // 256 * 256) + rows * 128 * 4
+    # invalid sizes need nothing
+    assert f(0, 32, 8, 128, 4096, 512) == 0
+    assert f(64, 32, 0, 128, 4096, 512) == 0
 
 
 def test_cache_ops_reject_bad_arguments_before_launch():

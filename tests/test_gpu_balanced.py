@@ -1,0 +1,163 @@
+"""The balanced decode split (partition_size = pa.BALANCED, dim-major V) on
+the GPU against the fp64 oracle.
+
+The split divides the batch's 16-token tiles evenly over the resident
+workgroups and merges sequences cut between them. PA_SK_WGS caps the grid,
+so small inputs still reach every case of the split: one workgroup walking
+many sequences and many unit batches (cap 1), sequences cut between a few
+workgroups (small caps), and workgroups with no units at all (more
+workgroups than tiles). Tolerance as in test_gpu_decode.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_49_amd as pa
+import synth
+from tests import helpers as H
+from tests.gpu_util import device_setup, run_decode, say
+
+pytestmark = pytest.mark.gpu
+
+BAL = pa.BALANCED
+LENGTHS = [1, 15, 16, 17, 100, 511, 512, 513, 1100, 2049]
+
+
+@pytest.fixture
+def wgs(monkeypatch):
+    """set_wgs(n): cap the balanced grid at n workgroups (None: no cap)."""
+    def set_wgs(n):
+        if n is None:
+            monkeypatch.delenv("PA_SK_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_SK_WGS", str(n))
+    return set_wgs
+
+
+def _check(wl, what=""):
+    say(f"balanced {wl.name} kv={wl.kv_dtype} D={wl.head_dim} bs={wl.block_size} Hkv={wl.num_kv_heads} "
+        f"G={wl.group} {what}")
+    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout="dim")
+    got = run_decode(wl, cache, tables, lens, max_ctx, BAL)
+    ma, rl = H.assert_close(got, H.oracle_contiguous(wl), what=f"{wl.name} {what}")
+    say(f"   max-abs {ma:.2e}  rel-L2 {rl:.2e}")
+    return got
+
+
+CASES = [
+    ("bf16", 128, 16, 4),
+    ("f16", 64, 16, 1),
+    ("bf16", 128, 8, 8),
+    ("bf16", 64, 32, 2),
+    ("f16", 128, 32, 4),
+    ("fp8", 128, 16, 8),
+    ("fp8", 64, 8, 4),
+    ("fp8", 128, 32, 1),
+]
+
+
+@pytest.mark.parametrize("cap", [None, 1, 7])
+@pytest.mark.parametrize("hkv", [2, 8])
+@pytest.mark.parametrize("kv,D,bs,G", CASES, ids=lambda c: str(c))
+def test_parity_sweep(gpu, wgs, kv, D, bs, G, hkv, cap):
+    wgs(cap)
+    wl = synth.random_case(2000 + D + bs + G + hkv, LENGTHS, G * hkv, hkv, D, bs, kv)
+    _check(wl, f"cap={cap}")
+
+
+@pytest.mark.parametrize("hkv", [1, 3, 6, 16, 24])
+@pytest.mark.parametrize("cap", [None, 5])
+def test_head_groups(gpu, wgs, hkv, cap):
+    """A workgroup serves the largest divisor of Hkv up to 8 KV heads: one
+    wave (Hkv 1), odd widths (3, 6) and several head groups (16, 24)."""
+    wgs(cap)
+    wl = synth.random_case(2100 + hkv, [40, 700, 3, 1500], 2 * hkv, hkv, 128, 16, "bf16")
+    _check(wl, f"cap={cap}")
+
+
+@pytest.mark.parametrize("cap", [None, 1, 2, 3])
+def test_empty_and_short_sequences(gpu, wgs, cap):
+    """Zero-length sequences give zeros; with the default grid most
+    workgroups get no units at all."""
+    wgs(cap)
+    wl = synth.random_case(2200, [0, 1, 0, 17, 0, 33], 16, 2, 128, 16, "bf16")
+    got = _check(wl, f"cap={cap}")
+    for s in (0, 2, 4):
+        assert np.array_equal(got[s], np.zeros_like(got[s]))
+
+
+def test_all_sequences_empty(gpu):
+    wl = synth.random_case(2201, [0, 0, 0], 16, 2, 128, 16, "bf16", min_blocks=4)
+    got = _check(wl)
+    assert np.array_equal(got, np.zeros_like(got))
+
+
+def test_one_long_sequence_over_every_workgroup(gpu):
+    """One 20000-token sequence: every workgroup holds a piece of it, and
+    the merge combines hundreds of pieces."""
+    wl = synth.random_case(2300, [20000], 8, 2, 128, 16, "bf16")
+    _check(wl)
+
+
+@pytest.mark.parametrize("cap", [1, 2, 3])
+def test_many_unit_batches_per_workgroup(gpu, wgs, cap):
+    """With 1 to 3 workgroups each walks hundreds of units: many 63-unit
+    batches, many sequences, pieces at both ends of every range."""
+    wgs(cap)
+    wl = synth.random_case(2400, [3000, 1500, 700, 1, 16, 250, 4100], 8, 2, 128, 16, "bf16")
+    _check(wl, f"cap={cap}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("cap", [None, 3])
+def test_16bit_outputs(gpu, wgs, out_dtype, cap):
+    wgs(cap)
+    wl = synth.random_case(2500, [5, 300, 900, 2000], 16, 2, 128, 16, "bf16")
+    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout="dim")
+    got = run_decode(wl, cache, tables, lens, max_ctx, BAL, out_dtype)
+    H.assert_close(got, H.oracle_contiguous(wl), what=f"{out_dtype} cap={cap}")
+
+
+def test_agrees_with_partitions_and_is_deterministic(gpu):
+    wl = synth.random_case(2600, [3, 129, 700, 1500, 4000], 32, 8, 128, 16, "bf16")
+    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout="dim")
+    a = run_decode(wl, cache, tables, lens, max_ctx, BAL)
+    b = run_decode(wl, cache, tables, lens, max_ctx, BAL)
+    c = run_decode(wl, cache, tables, lens, max_ctx, 512)
+    assert np.array_equal(a, b)  # the split depends only on the lengths and the grid
+    H.assert_close(a, c, what="balanced vs partitions")
+    H.assert_close(a, H.oracle_contiguous(wl))
+
+
+def test_lengths_beyond_max_context_are_clamped(gpu):
+    wl = synth.random_case(2700, [300, 90], 8, 2, 128, 16, "bf16")
+    _, cache, tables, lens, _ = device_setup(wl, v_layout="dim")
+    got = run_decode(wl, cache, tables, lens, 128, BAL)
+    short = synth.random_case(2700, [300, 90], 8, 2, 128, 16, "bf16")
+    k, v = wl.kv(0)
+    short._kv_cache[0] = (k[:128], v[:128])
+    short._kv_cache[1] = wl.kv(1)
+    short.lengths = np.array([128, 90])
+    H.assert_close(got, H.oracle_contiguous(short))
+
+
+def test_needle_follows_logical_order(gpu, wgs):
+    """One key per sequence matches the query; the output is that token's V
+    row wherever it sits, also when the sequence is cut between workgroups."""
+    wgs(5)
+    L, hkv, D, G = 96, 1, 128, 4
+    wl = synth.random_case(2800, [L] * 8, G * hkv, hkv, D, 16, "bf16", headroom=1.0)
+    qv = torch.randn(D)
+    q = qv.repeat(8, G, 1).bfloat16()
+    wl._q = q
+    qd = q.double()[0, 0]
+    stars = [0, 1, 15, 16, 17, 47, 80, 95]
+    for s, t_star in enumerate(stars):
+        k = torch.zeros(L, hkv, D)
+        k[t_star, 0] = 30.0 / (wl.scale * float(qd @ qd)) * qv
+        v = torch.randn(L, hkv, D)
+        wl._kv_cache[s] = (k.bfloat16(), v.bfloat16())
+    got = _check(wl, "needle")
+    for s, t_star in enumerate(stars):
+        want = wl.kv(s)[1][t_star, 0].double().numpy()
+        assert np.abs(got[s] - want).max() < 1e-3

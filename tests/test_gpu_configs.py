@@ -1,5 +1,5 @@
 """Full-size workloads on the GPU, in the launch configuration bench.py
-times (dim-major V, 512-token partitions), against the fp64 oracle.
+times (dim-major V, balanced split), against the fp64 oracle.
 
 * GQA batch (64 seqs, L ~ U[512,4096], 32/8 heads): every output row.
 * long context (8 seqs, L ~ U[32768,131072]): every sequence, two KV heads
@@ -23,19 +23,20 @@ from tests.gpu_util import device_setup, run_decode, say
 
 pytestmark = pytest.mark.gpu
 
-BENCH_PARTITION = 512
+BENCH_PARTITION = pa.BALANCED
 BENCH_V_LAYOUT = "dim"
 
 
-def test_gqa_batch_full(gpu):
+@pytest.mark.parametrize("part", [BENCH_PARTITION, 512], ids=["balanced", "part512"])
+def test_gqa_batch_full(gpu, part):
     wl = synth.gqa_decode()
-    say(f"gqa batch: {wl.total_tokens()} tokens")
+    say(f"gqa batch: {wl.total_tokens()} tokens, partition {part}")
     _, cache, tables, lens, mx = device_setup(wl, v_layout=BENCH_V_LAYOUT)
-    got = run_decode(wl, cache, tables, lens, mx, BENCH_PARTITION)
+    got = run_decode(wl, cache, tables, lens, mx, part)
     ma, rl = H.assert_close(got, H.oracle_contiguous(wl), what="gqa")
     say(f"   max-abs {ma:.2e} rel-L2 {rl:.2e}")
     # the 16-bit output the bench produces stays within the same bounds
-    got16 = run_decode(wl, cache, tables, lens, mx, BENCH_PARTITION, out_dtype=torch.bfloat16)
+    got16 = run_decode(wl, cache, tables, lens, mx, part, out_dtype=torch.bfloat16)
     H.assert_close(got16, H.oracle_contiguous(wl), what="gqa bf16 out")
 
 
@@ -89,7 +90,7 @@ def test_prefix_sharing_with_copy_on_write(gpu, partial_tail):
     v_new = torch.stack([wl.tail_kv(p, i)[1][-1] for p in range(P) for i in range(S)]).cuda()
     q = wl.q().cuda()
     out = torch.empty(P * S, wl.num_q_heads, D, dtype=torch.float32, device="cuda")
-    ws = torch.empty(pa.decode_workspace_size(P * S, wl.num_q_heads, D, mb * bs, BENCH_PARTITION),
+    ws = torch.empty(pa.decode_workspace_size(P * S, wl.num_q_heads, hkv, D, mb * bs, BENCH_PARTITION),
                      dtype=torch.uint8, device="cuda")
     before = bm.stats()["cow_copies"]
     batch.step(ids, [k_new], [v_new], [q], [out], wl.scale, BENCH_PARTITION, ws)
