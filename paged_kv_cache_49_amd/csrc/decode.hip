@@ -77,87 +77,82 @@ struct SkMergeParams {
   const float* piece_m;
   const float* piece_l;
   const float* piece_o;
-  const int32_t* prefix;  // [B + 1]
+  const int32_t* seg_desc;  // [head groups][B][2]
+  const int32_t* context_lens;
   void* out;
+  int32_t len_cap;
   int32_t batch;
   int32_t num_q_heads;
   int32_t heads_per_wg;
-  int32_t num_head_groups;
   int32_t group;  // G
   int32_t head_dim;
-  int32_t num_wgs;  // W of the main launch
   int32_t out_dtype;
 };
 
 // One workgroup per (head group, sequence) segment, one thread per 8 head
-// dims of one query head. Segment units [fu, lu] lie in the ranges of
-// workgroups wf..wl: wf's piece is its slot 1 when wf's range starts before
-// fu (the segment starts inside it), every other piece is slot 0. Ranges
-// are never empty when U >= W.
+// dims of one query head. The segment's descriptor (written by the
+// balanced kernel, see decode_sk_kernel.h) names the workgroups wf..wl that
+// hold its pieces: wf's in the slot the descriptor gives, the others' in
+// slot 0. Pieces are read 8 at a time (one round of loads) and merged with
+// a running maximum, in workgroup order.
 __global__ __launch_bounds__(1024) void decode_sk_merge_kernel(const SkMergeParams p) {
   const int s = static_cast<int>(blockIdx.x) % p.batch;
   const int hg = static_cast<int>(blockIdx.x) / p.batch;
   const int HWG = p.heads_per_wg * p.group;  // query heads per head group
   const int D = p.head_dim;
-  const int T = p.prefix[p.batch];
-  const int f = p.prefix[s];
-  const int nt = p.prefix[s + 1] - f;
-  const int64_t head0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(hg) * HWG;
   const int i = static_cast<int>(threadIdx.x) * 8;
   if (i >= HWG * D) return;
   const int h = i / D, d = i % D;
-  if (nt == 0) {
+  const int64_t head0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(hg) * HWG;
+  const int L = min(p.context_lens[s], p.len_cap);
+  const int32_t* desc = p.seg_desc + (static_cast<int64_t>(hg) * p.batch + s) * 2;
+  const int32_t d0 = desc[0], d1 = desc[1];
+  if (L <= 0) {
     const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     store_out8(p.out, (head0 + h) * D + d, p.out_dtype, z);
     return;
   }
-  const int U = T * p.num_head_groups;
-  const int W = p.num_wgs;
-  const int fu = hg * T + f;
-  const int wf = sk_owner(fu, U, W), wl = sk_owner(fu + nt - 1, U, W);
-  if (wf == wl) return;  // stored by its workgroup
-  const bool may_be_empty = U < W;
-  const bool first_is_slot1 = sk_range_start(wf, U, W) < fu;
-  // pieces are read 8 at a time (one round of loads) and merged with a
-  // running maximum, so a segment with up to 8 pieces costs one round trip
+  if (d0 == -1) return;  // stored by the workgroup that completed it
+  const int wf = d0 & 0x7fffffff, wl = d1;
+  const int first_slot = static_cast<int>(static_cast<uint32_t>(d0) >> 31);
   constexpr int kChunk = 8;
   float run_m = -INFINITY, den = 0.f;
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int w0 = wf; w0 <= wl; w0 += kChunk) {
     float pm[kChunk], pl[kChunk];
-    f32x4 pa_[kChunk], pb_[kChunk];
+    f32x4 pa[kChunk], pb[kChunk];
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
       const int wv = w0 + k;
-      bool valid = wv <= wl;
-      if (valid && may_be_empty && wv > wf) valid = sk_range_start(wv, U, W) != sk_range_start(wv + 1, U, W);
-      const int slot = wv == wf && first_is_slot1 ? 1 : 0;
-      const int64_t pi = (static_cast<int64_t>(valid ? wv : wf) * 2 + (valid ? slot : (first_is_slot1 ? 1 : 0))) * HWG + h;
+      const bool valid = wv <= wl;
+      const int wr = valid ? wv : wf;  // unused slots read wf's piece with weight 0
+      const int slot = wr == wf ? first_slot : 0;
+      const int64_t pi = (static_cast<int64_t>(wr) * 2 + slot) * HWG + h;
       pm[k] = valid ? p.piece_m[pi] : -INFINITY;
       pl[k] = p.piece_l[pi];
       const f32x4* po = reinterpret_cast<const f32x4*>(p.piece_o + pi * D + d);
-      pa_[k] = po[0];
-      pb_[k] = po[1];
+      pa[k] = po[0];
+      pb[k] = po[1];
     }
     float cm = run_m;
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) cm = fmaxf(cm, pm[k]);
-    const float r = __builtin_amdgcn_exp2f(run_m - cm);  // 0 on the first chunk (run_m = -inf)
+    const float r = __builtin_amdgcn_exp2f(run_m - cm);  // 0 on the first round (run_m = -inf)
     den *= r;
 #pragma unroll
     for (int e = 0; e < 8; ++e) num[e] *= r;
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
-      const float wt = pl[k] * __builtin_amdgcn_exp2f(pm[k] - cm);  // 0 for unused slots (pm = -inf)
+      const float wt = pl[k] * __builtin_amdgcn_exp2f(pm[k] - cm);  // 0 for unused slots and empty ranges
       den += wt;
-      num[0] = fmaf(wt, pa_[k].x, num[0]);
-      num[1] = fmaf(wt, pa_[k].y, num[1]);
-      num[2] = fmaf(wt, pa_[k].z, num[2]);
-      num[3] = fmaf(wt, pa_[k].w, num[3]);
-      num[4] = fmaf(wt, pb_[k].x, num[4]);
-      num[5] = fmaf(wt, pb_[k].y, num[5]);
-      num[6] = fmaf(wt, pb_[k].z, num[6]);
-      num[7] = fmaf(wt, pb_[k].w, num[7]);
+      num[0] = fmaf(wt, pa[k].x, num[0]);
+      num[1] = fmaf(wt, pa[k].y, num[1]);
+      num[2] = fmaf(wt, pa[k].z, num[2]);
+      num[3] = fmaf(wt, pa[k].w, num[3]);
+      num[4] = fmaf(wt, pb[k].x, num[4]);
+      num[5] = fmaf(wt, pb[k].y, num[5]);
+      num[6] = fmaf(wt, pb[k].z, num[6]);
+      num[7] = fmaf(wt, pb[k].w, num[7]);
     }
     run_m = cm;
   }
@@ -206,18 +201,18 @@ int device_cus() {
 }
 
 struct SkLayout {
-  size_t prefix, m, l, o, total;  // byte offsets and total size
+  size_t desc, m, l, o, total;  // byte offsets and total size
 };
 
-// workspace of the balanced split: tile prefix [B + 1], then per piece row
-// (workgroup, slot, query head of the group) m, l and o[D]
+// workspace of the balanced split: merge descriptors [head groups][B][2],
+// then per piece row (workgroup, slot, query head of the group) m, l, o[D]
 SkLayout sk_layout(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int cus) {
   const int64_t G = Hq / hkv;
   // W * HW <= cus * kSkWavesPerCu, and a workgroup holds 2 * HW * G rows
   const size_t rows = static_cast<size_t>(cus) * kSkWavesPerCu * 2 * G;
   SkLayout L{};
-  L.prefix = 0;
-  L.m = align_up(static_cast<size_t>(B + 1) * sizeof(int32_t));
+  L.desc = 0;
+  L.m = align_up(static_cast<size_t>(B) * hkv * 2 * sizeof(int32_t));
   L.l = L.m + align_up(rows * sizeof(float));
   L.o = L.l + align_up(rows * sizeof(float));
   L.total = L.o + align_up(rows * D * sizeof(float));
@@ -265,7 +260,7 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   p.piece_m = reinterpret_cast<float*>(ws + lay.m);
   p.piece_l = reinterpret_cast<float*>(ws + lay.l);
   p.piece_o = reinterpret_cast<float*>(ws + lay.o);
-  p.prefix_out = reinterpret_cast<int32_t*>(ws + lay.prefix);
+  p.seg_desc = reinterpret_cast<int32_t*>(ws + lay.desc);
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.block_stride = cache->block_stride;
@@ -292,15 +287,15 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   m.piece_m = p.piece_m;
   m.piece_l = p.piece_l;
   m.piece_o = p.piece_o;
-  m.prefix = p.prefix_out;
+  m.seg_desc = p.seg_desc;
+  m.context_lens = context_lens;
   m.out = out;
+  m.len_cap = max_context_len;
   m.batch = B;
   m.num_q_heads = num_q_heads;
   m.heads_per_wg = HW;
-  m.num_head_groups = n_hg;
   m.group = G;
   m.head_dim = D;
-  m.num_wgs = wgs;
   m.out_dtype = out_code;
   // one thread per 8 head dims of each query head of a head group
   const int merge_threads = (HW * G * D / 8 + 63) / 64 * 64;

@@ -33,6 +33,11 @@
 //    range start) or slot 1 (it starts inside the range), which
 //    decode_sk_merge_kernel combines with the pieces of the neighbouring
 //    workgroups (the log-sum-exp merge described in decode.hip).
+//  * merge descriptor of a segment: {-1, -} when one workgroup completed it;
+//    else {wf | slot << 31, wl}, written by the workgroups where it starts
+//    (wf, its piece in `slot`) and ends (wl, slot 0). Every workgroup in
+//    between holds a slot-0 piece; a workgroup with no units writes neutral
+//    slot-0 pieces (m = -inf, l = 0, o = 0), so a merge may include it.
 #pragma once
 
 #include "decode_vt_kernel.h"
@@ -47,7 +52,7 @@ struct SkParams {
   float* piece_m;       // [W][2][HW * G]
   float* piece_l;       // [W][2][HW * G]
   float* piece_o;       // [W][2][HW * G][D]
-  int32_t* prefix_out;  // [B + 1] tile prefix, written by workgroup 0
+  int32_t* seg_desc;    // [head groups][B][2] merge descriptors, see below
   const int32_t* block_tables;
   const int32_t* context_lens;
   int64_t block_stride;  // elements
@@ -142,10 +147,18 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   const int U = T * p.num_head_groups;  // the launch guarantees U < 2^31
   const int W = static_cast<int>(gridDim.x);
   const int w = static_cast<int>(blockIdx.x);
-  if (w == 0)
-    for (int i = threadIdx.x; i <= B; i += blockDim.x) p.prefix_out[i] = s_pref[i];
   const int u0 = sk_range_start(w, U, W), u1 = sk_range_start(w + 1, U, W);
-  if (u0 >= u1) return;
+  if (u0 >= u1) {
+    // no units: neutral slot-0 pieces (only when there are fewer units than workgroups)
+    const int rows = HW * G;
+    const int64_t base = static_cast<int64_t>(w) * 2 * rows;
+    for (int i = threadIdx.x; i < rows; i += blockDim.x) {
+      p.piece_m[base + i] = -INFINITY;
+      p.piece_l[base + i] = 0.f;
+    }
+    for (int i = threadIdx.x; i < rows * D; i += blockDim.x) p.piece_o[base * D + i] = 0.f;
+    return;
+  }
 
   float* s_out = s_out_all + wave * G * D;
   const int col = lane & 15, j = lane >> 4;
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // store the segment that just ended: final output, or a partial piece
-  auto flush = [&](bool complete, int slot) {
+  auto flush = [&](bool complete, bool ends_here, int slot) {
     float l_head = l_w + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_w), 0x401F));
     l_head += __shfl_xor(l_head, 32, 64);
 #pragma unroll
@@ -303,6 +316,15 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     if (!complete && lane < G) {
       p.piece_m[pbase + lane] = m_w;
       p.piece_l[pbase + lane] = l_head;
+    }
+    if (wave == 0 && lane == 0) {
+      int32_t* desc = p.seg_desc + (static_cast<int64_t>(seg_hg) * B + seg_seq) * 2;
+      if (complete) {
+        desc[0] = -1;
+      } else {
+        if (seg_begun) desc[0] = static_cast<int32_t>(static_cast<uint32_t>(w) | (static_cast<uint32_t>(slot) << 31));
+        if (ends_here) desc[1] = w;
+      }
     }
     wave_lds_sync();
   };
@@ -376,7 +398,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // ---- end of a segment: store it, then start the next one at x + 1
     const bool seq_end = un.tile == ((L + 15) >> 4) - 1;
     if (seq_end || x + 1 == u1) {
-      flush(seg_begun && seq_end, seg_first ? 0 : 1);
+      flush(seg_begun && seq_end, seq_end, seg_first ? 0 : 1);
       if (x + 1 < u1) {
         seg_seq = nseq;
         seg_hg = nhg;
