@@ -53,18 +53,21 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(bytes_per_launch: float):
-    """HBM traffic of one pa_decode call from the committed counter summary,
-    or None when the kernel sources changed since the counters were taken."""
+def load_traffic():
+    """HBM bytes (read + written) of one pa_decode call from the committed
+    counter summary, and their ratio to the algorithmic bytes of the counted
+    calls; (None, None) when the kernel sources changed since the counters
+    were taken."""
     path = os.path.join(ROOT, "profiles", "decode_gqa_traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if t.get("kernel_hash") != kernel_hash():
-        return None
-    return t.get("hbm_bytes_per_call")
+        return None, None
+    hbm, alg = t.get("hbm_bytes_per_call"), t.get("algorithmic_bytes_per_call_of_counted_run")
+    return hbm, (round(hbm / alg, 4) if hbm and alg else None)
 
 
 def parse():
@@ -207,7 +210,7 @@ def main():
     per_call_bytes = total_bytes / (K * layers)
     call_s = float(durs.mean())
     achieved = per_call_bytes / call_s / 1e9
-    traffic = load_traffic(per_call_bytes)
+    traffic, traffic_ratio = load_traffic()
     value = total_bytes / el / 1e9
     print(f"[bench] {K} steps in {el * 1e3:.2f} ms; pa_decode mean {call_s * 1e6:.1f} us "
           f"(min {durs.min() * 1e6:.1f}, max {durs.max() * 1e6:.1f})", file=sys.stderr, flush=True)
@@ -245,6 +248,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_unit": "bytes per pa_decode call (FETCH_SIZE + WRITE_SIZE, calibrated)",
+            "traffic_per_algorithmic_byte": traffic_ratio,
             "algorithmic_bytes_per_call": round(per_call_bytes),
         },
         "cpu_baseline": None,
