@@ -20,8 +20,15 @@ before timing starts.
 Printed: one JSON line. ``value`` = KV bytes the decode calls of the timed
 steps must read (2 * L * Hkv * D * 2 per sequence and layer, valid tokens
 only) / wall time of those steps. ``roofline`` = the same bytes per pa_decode
-call / its mean duration from HIP events recorded around each call on the
-stream it runs on. ``cpu_baseline`` = the fp64 oracle on the host cores.
+call / its mean duration from HIP events recorded around the first layer's
+pa_decode call of every timed step, on the stream it runs on (an event pair
+around every call would add ~4 us of queue time per call to the steps).
+``cpu_baseline`` = the fp64 oracle on the host cores.
+
+Host-to-device copies (the step's metadata upload) run as blit kernels on
+the compute queue (HSA_ENABLE_SDMA=0, set before the HIP runtime starts):
+a copy on the DMA engine makes the next kernel wait for a cross-engine
+signal, ~20 us per step on MI355X.
 """
 from __future__ import annotations
 
@@ -137,6 +144,7 @@ def cpu_baseline(wl, seconds: float):
 
 def main():
     args = parse()
+    os.environ.setdefault("HSA_ENABLE_SDMA", "0")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (this path has no "
               f"multi-GPU leg: each GPU would run its own share with no exchange)", file=sys.stderr)
@@ -198,7 +206,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(K):
-        batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, decode_events=events)
+        batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, decode_events=events,
+                   event_layers=(0,))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     el = t1 - t0
@@ -207,7 +216,7 @@ def main():
     step_bytes = [layers * kv_row * int((lens_before + i + 1).sum()) for i in range(K)]
     total_bytes = float(sum(step_bytes))
     durs = np.array([a.elapsed_time(b) for a, b in events]) * 1e-3  # seconds
-    per_call_bytes = total_bytes / (K * layers)
+    per_call_bytes = total_bytes / (K * layers)  # every layer of a step reads the same bytes
     call_s = float(durs.mean())
     achieved = per_call_bytes / call_s / 1e9
     traffic, traffic_ratio = load_traffic()

@@ -20,13 +20,16 @@
 //
 // Per workgroup:
 //  * plan: tiles per sequence (lengths clamped to the launch bound) and
-//    their exclusive prefix go to LDS; workgroup 0 also copies the prefix
-//    out for the merge kernel.
+//    their exclusive prefix go to LDS.
 //  * unit batches: lane i of a batch resolves unit ub + i to its sequence,
 //    tile, length, head group and block id(s); the batch after it is
 //    requested one batch ahead, so block-table reads never stall the loads.
-//  * a 3-deep register ring keeps the K and V loads of two tiles in flight
-//    while a third tile is computed.
+//  * a 3-deep register ring keeps the q, K and V loads of two units in
+//    flight while a third unit is computed (q rides in the ring too, so a
+//    new segment never waits on a load issued behind the ring's). The waves
+//    of a workgroup pass a barrier after each unit: without it the oldest
+//    wave of each SIMD takes most issue slots and finishes far ahead, and
+//    the others end alone with few loads in flight.
 //  * a (head group, sequence) segment that ends inside the range is
 //    normalised and stored directly; a segment cut by the range's start or
 //    end leaves a partial (m, l, o) piece in slot 0 (it reaches back to the
@@ -204,7 +207,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   };
   auto block_id = [&](int id) { return static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks) ? id : 0; };
   // ---- loads of one unit into a ring slot; returns the unit
-  auto load_unit = [&](const Batch& b, int x, u32x4 (&kr)[C::kKLoads], VRaw (&vr)[kNT]) -> SkUnit {
+  auto load_unit = [&](const Batch& b, int x, u32x4 (&qr)[C::kKSteps], u32x4 (&kr)[C::kKLoads],
+                       VRaw (&vr)[kNT]) -> SkUnit {
     const int o = x - b.ub;
     SkUnit un;
     un.seq = __builtin_amdgcn_readlane(b.seq, o);
@@ -213,6 +217,17 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     un.hg = __builtin_amdgcn_readlane(b.hg, o);
     const int ida = block_id(__builtin_amdgcn_readlane(b.ida, o));
     const int g = un.hg * HW + wave;
+    // the unit's q rows (B operand of S^T = K q^T); columns >= G repeat head
+    // 0 (finite logits whose weights are forced to zero). Every unit loads
+    // them (cache hits after the first unit of a segment), so each ring slot
+    // carries a fixed number of loads and no wait ever covers more than the
+    // slot it consumes.
+    {
+      const int64_t head0 = static_cast<int64_t>(un.seq) * p.num_q_heads + static_cast<int64_t>(g) * G;
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
+#pragma unroll
+      for (int i = 0; i < C::kKSteps; ++i) qr[i] = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
+    }
     if constexpr (BS >= 16) {
       const int tin = (un.tile * 16) % BS;
       const char* kb = kbase + static_cast<int64_t>(ida) * blk_bytes + tin * tok_bytes + static_cast<int64_t>(g) * D * kB;
@@ -247,35 +262,11 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     return un;
   };
 
-  // ---- q rows of a segment as the B operand of S^T = K q^T. Columns >= G
-  // repeat head 0 (finite logits whose weights are forced to zero), so the
-  // loaded values are used as they are and the load is waited for only
-  // where q is first used.
-  auto load_q = [&](int seq, int hg, u32x4 (&dst)[C::kKSteps]) {
-    const int64_t head0 = static_cast<int64_t>(seq) * p.num_q_heads + static_cast<int64_t>(hg * HW + wave) * G;
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
-#pragma unroll
-    for (int i = 0; i < C::kKSteps; ++i) dst[i] = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
-  };
-  auto locate = [&](int u, int& seq, int& hg) {
-    hg = u / T;
-    seq = sk_find_seq(s_pref, B, u - hg * T);
-  };
-
-  // ---- segment state: the current segment and the one after it (q prefetched)
-  int seg_seq, seg_hg, nseq = 0, nhg = 0;
-  locate(u0, seg_seq, seg_hg);
-  bool seg_first = true;                                 // reaches back to u0
-  bool seg_begun = u0 == seg_hg * T + s_pref[seg_seq];  // starts inside the range
-  u32x4 qb[C::kKSteps], qn[C::kKSteps];
-  load_q(seg_seq, seg_hg, qb);
-  {
-    const int after = seg_hg * T + s_pref[seg_seq + 1];
-    if (after < u1) {
-      locate(after, nseq, nhg);
-      load_q(nseq, nhg, qn);
-    }
-  }
+  // ---- segment state. A segment is the run of units of one (head group,
+  // sequence) inside this workgroup's range; its identity comes with each
+  // unit, so nothing is looked up when one ends and the next begins.
+  bool seg_first = true;  // reaches back to u0
+  bool seg_begun = true;  // starts inside the range (set from the first unit below)
 
   float m_w = -INFINITY;  // running reference max of head `col` (log2 domain)
   float l_w = 0.f;        // this lane's share of head `col`'s weight sum
@@ -284,7 +275,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // store the segment that just ended: final output, or a partial piece
-  auto flush = [&](bool complete, bool ends_here, int slot) {
+  auto flush = [&](int seg_seq, int seg_hg, bool complete, bool ends_here, int slot) {
     float l_head = l_w + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_w), 0x401F));
     l_head += __shfl_xor(l_head, 32, 64);
 #pragma unroll
@@ -329,7 +320,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     wave_lds_sync();
   };
 
-  auto compute = [&](int x, const SkUnit& un, const u32x4 (&kr)[C::kKLoads], const VRaw (&vr)[kNT]) {
+  auto compute = [&](int x, const SkUnit& un, const u32x4 (&qb)[C::kKSteps], const u32x4 (&kr)[C::kKLoads],
+                     const VRaw (&vr)[kNT]) {
     const int tb = un.tile * 16;
     const int L = un.len;
     // ---- S^T = K q^T
@@ -398,19 +390,10 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // ---- end of a segment: store it, then start the next one at x + 1
     const bool seq_end = un.tile == ((L + 15) >> 4) - 1;
     if (seq_end || x + 1 == u1) {
-      flush(seg_begun && seq_end, seq_end, seg_first ? 0 : 1);
+      flush(un.seq, un.hg, seg_begun && seq_end, seq_end, seg_first ? 0 : 1);
       if (x + 1 < u1) {
-        seg_seq = nseq;
-        seg_hg = nhg;
         seg_first = false;
         seg_begun = true;
-#pragma unroll
-        for (int i = 0; i < C::kKSteps; ++i) qb[i] = qn[i];
-        const int after = seg_hg * T + s_pref[seg_seq + 1];
-        if (after < u1) {
-          locate(after, nseq, nhg);
-          load_q(nseq, nhg, qn);
-        }
         m_w = -INFINITY;
         l_w = 0.f;
 #pragma unroll
@@ -425,6 +408,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // Batches: an outer step covers 63 units (21 ring iterations); its batch
   // holds the units it loads (uk + 2 .. uk + 65), and the next step's batch
   // is requested when the step starts.
+  u32x4 q0[C::kKSteps], q1[C::kKSteps], q2[C::kKSteps];
   u32x4 k0[C::kKLoads], k1[C::kKLoads], k2[C::kKLoads];
   VRaw v0[kNT], v1[kNT], v2[kNT];
   const int ulast = u1 - 1;
@@ -433,10 +417,11 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // the prologue issues its loads in the loop's order (K then V, unit by
   // unit), so the wait counts the compiler derives for the loop hold on
   // entry too
-  SkUnit n0 = load_unit(cur, u0, k0, v0);
+  SkUnit n0 = load_unit(cur, u0, q0, k0, v0);
   __builtin_amdgcn_sched_barrier(0);
-  SkUnit n1 = load_unit(cur, min(u0 + 1, ulast), k1, v1);
+  SkUnit n1 = load_unit(cur, min(u0 + 1, ulast), q1, k1, v1);
   __builtin_amdgcn_sched_barrier(0);
+  seg_begun = n0.tile == 0;
   int uk = u0;
   do {
     cur = nxt;
@@ -444,12 +429,15 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     const int uend = min(uk + 63, u1);
     int u = uk;
     do {
-      SkUnit n2 = load_unit(cur, min(u + 2, ulast), k2, v2);
-      compute(u, n0, k0, v0);
-      n0 = load_unit(cur, min(u + 3, ulast), k0, v0);
-      if (u + 1 <= ulast) compute(u + 1, n1, k1, v1);
-      n1 = load_unit(cur, min(u + 4, ulast), k1, v1);
-      if (u + 2 <= ulast) compute(u + 2, n2, k2, v2);
+      SkUnit n2 = load_unit(cur, min(u + 2, ulast), q2, k2, v2);
+      compute(u, n0, q0, k0, v0);
+      __builtin_amdgcn_s_barrier();
+      n0 = load_unit(cur, min(u + 3, ulast), q0, k0, v0);
+      if (u + 1 <= ulast) compute(u + 1, n1, q1, k1, v1);
+      __builtin_amdgcn_s_barrier();
+      n1 = load_unit(cur, min(u + 4, ulast), q1, k1, v1);
+      if (u + 2 <= ulast) compute(u + 2, n2, q2, k2, v2);
+      __builtin_amdgcn_s_barrier();
       u += 3;
     } while (u < uend);
     uk += 63;

@@ -89,11 +89,12 @@ class PagedBatch:
     def step(self, seq_ids: np.ndarray, k_new: Sequence[torch.Tensor], v_new: Sequence[torch.Tensor],
              q: Sequence[torch.Tensor], outs: Sequence[torch.Tensor], scale: float, partition_size: int,
              workspace: Optional[torch.Tensor] = None, ones: Optional[np.ndarray] = None,
-             decode_events: Optional[list] = None) -> int:
+             decode_events: Optional[list] = None, event_layers: Optional[Sequence[int]] = None) -> int:
         """Append one token to each of ``seq_ids`` in every layer and run
         decode attention for it. Returns the batch's max context length.
         With ``decode_events`` (a list), a (start, end) pair of HIP events
-        recorded around each pa_decode call is appended to it."""
+        recorded around the pa_decode call of each layer in
+        ``event_layers`` (default: every layer) is appended to it."""
         st = self._stage[self._turn]
         self._turn ^= 1
         if st.event is not None:
@@ -116,11 +117,12 @@ class PagedBatch:
             if ncow:
                 copy_blocks(c, st.cow[:ncow])
             reshape_and_cache(c, k_new[i], v_new[i], st.slots[:B])
-            if decode_events is not None:
+            timed = decode_events is not None and (event_layers is None or i in event_layers)
+            if timed:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 ev[0].record()
             decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i], workspace=workspace)
-            if decode_events is not None:
+            if timed:
                 ev[1].record()
                 decode_events.append(ev)
         return max_ctx
