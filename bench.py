@@ -11,7 +11,8 @@ the 256 MB Infinity Cache, so every timed decode reads K/V from HBM.
 One step = one decode step of the whole path: the host block manager
 allocates one slot per sequence (pa_alloc_batch; copy-on-write pairs, none
 here), packs the tables, one pinned host-to-device copy carries slots /
-pairs / tables / lengths, then per layer pa_copy_blocks (if pairs) ->
+pairs / tables / lengths (on a copy stream, overlapping the previous step's
+kernels), then per layer pa_copy_blocks (if pairs) ->
 pa_reshape_and_cache (the new token's K/V) -> pa_decode (by default the
 balanced split: one persistent kernel over the resident workgroups, then the
 log-sum-exp merge of sequences cut between them). Inputs are resident in HBM
@@ -24,11 +25,6 @@ call / its mean duration from HIP events recorded around the first layer's
 pa_decode call of every timed step, on the stream it runs on (an event pair
 around every call would add ~4 us of queue time per call to the steps).
 ``cpu_baseline`` = the fp64 oracle on the host cores.
-
-Host-to-device copies (the step's metadata upload) run as blit kernels on
-the compute queue (HSA_ENABLE_SDMA=0, set before the HIP runtime starts):
-a copy on the DMA engine makes the next kernel wait for a cross-engine
-signal, ~20 us per step on MI355X.
 """
 from __future__ import annotations
 
@@ -144,7 +140,6 @@ def cpu_baseline(wl, seconds: float):
 
 def main():
     args = parse()
-    os.environ.setdefault("HSA_ENABLE_SDMA", "0")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (this path has no "
               f"multi-GPU leg: each GPU would run its own share with no exchange)", file=sys.stderr)

@@ -15,6 +15,10 @@ and runs the serving loop's steps through the C ABI:
 The metadata staging area is double-buffered: a buffer is refilled only
 after the copy issued from it two steps earlier has completed (HIP event),
 so the host can run ahead of the device without overwriting data in flight.
+By default the upload runs on a copy stream of its own (default priority):
+it overlaps the previous step's kernels, and the step's first kernel waits
+only for an event that has long fired. The copy into a device buffer waits
+for the kernels of the step that last read it (two steps earlier).
 """
 from __future__ import annotations
 
@@ -45,12 +49,13 @@ class _Staging:
         self.cow = d[2 * batch: 4 * batch].view(batch, 2)
         self.lens = d[4 * batch: 5 * batch]
         self.tables = d[5 * batch:].view(batch, max_blocks)
-        self.event: Optional[torch.cuda.Event] = None
+        self.copied: Optional[torch.cuda.Event] = None    # after the upload into `dev`
+        self.consumed: Optional[torch.cuda.Event] = None  # after the last kernel that read `dev`
 
 
 class PagedBatch:
     def __init__(self, bm: BlockManager, caches: Sequence[KVCache], max_blocks: int, batch: int,
-                 device="cuda", pad: int = -1):
+                 device="cuda", pad: int = -1, upload_stream: bool = True):
         self.bm = bm
         self.caches = list(caches)
         self.max_blocks = int(max_blocks)
@@ -58,6 +63,7 @@ class PagedBatch:
         self.pad = int(pad)
         self._stage = [_Staging(batch, self.max_blocks, device) for _ in range(2)]
         self._turn = 0
+        self._copy_stream = torch.cuda.Stream(device=device) if upload_stream else None
         self.last_cow_count = 0
 
     # -- setup ---------------------------------------------------------------
@@ -97,8 +103,8 @@ class PagedBatch:
         ``event_layers`` (default: every layer) is appended to it."""
         st = self._stage[self._turn]
         self._turn ^= 1
-        if st.event is not None:
-            st.event.synchronize()
+        if st.copied is not None:
+            st.copied.synchronize()  # the pinned buffer's previous upload is done
         B = len(seq_ids)
         if ones is None:
             ones = np.ones(B, np.int32)
@@ -106,10 +112,19 @@ class PagedBatch:
         ncow = len(cows)
         self.bm.pack(seq_ids, self.max_blocks, self.pad, tables=st.tables_np, context_lens=st.lens_np)
         max_ctx = int(st.lens_np[:B].max(initial=0))
-        st.dev.copy_(st.host, non_blocking=True)
-        if st.event is None:
-            st.event = torch.cuda.Event()
-        st.event.record()
+        compute = torch.cuda.current_stream(self.device)
+        if st.copied is None:
+            st.copied, st.consumed = torch.cuda.Event(), torch.cuda.Event()
+        if self._copy_stream is None:
+            st.dev.copy_(st.host, non_blocking=True)
+            st.copied.record(compute)
+        else:
+            cs = self._copy_stream
+            cs.wait_event(st.consumed)  # kernels of the step that last read st.dev (no-op before any record)
+            with torch.cuda.stream(cs):
+                st.dev.copy_(st.host, non_blocking=True)
+            st.copied.record(cs)
+            compute.wait_event(st.copied)
         self.last_cow_count = ncow
         tables = st.tables if B == st.B else st.tables[:B]
         lens = st.lens[:B]
@@ -125,6 +140,7 @@ class PagedBatch:
             if timed:
                 ev[1].record()
                 decode_events.append(ev)
+        st.consumed.record(compute)
         return max_ctx
 
 
