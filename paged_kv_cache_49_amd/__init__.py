@@ -139,13 +139,17 @@ class BlockManager:
         _check(lib().pa_bm_create(int(num_blocks), int(block_size), None if order is None else _ptr(order),
                                   ctypes.byref(h)))
         self._h = h
+        # held here so that destruction at interpreter exit does not depend
+        # on module globals, which may already be gone then
+        self._destroy = lib().pa_bm_destroy
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            lib().pa_bm_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self._h = None
 
     def alloc(self, seq_id: int, num_new_tokens: int) -> Tuple[np.ndarray, list]:
