@@ -22,8 +22,9 @@ Printed: one JSON line. ``value`` = KV bytes the decode calls of the timed
 steps must read (2 * L * Hkv * D * 2 per sequence and layer, valid tokens
 only) / wall time of those steps. ``roofline`` = the same bytes per pa_decode
 call / its mean duration from HIP events recorded around the first layer's
-pa_decode call of every timed step, on the stream it runs on (an event pair
-around every call would add ~4 us of queue time per call to the steps).
+pa_decode call of every timed step, on the stream it runs on. The events
+are created with hipEventDisableSystemFence (see HipTimingEvent): default
+events add a cache write-back and invalidate, ~5 us of idle queue each.
 ``cpu_baseline`` = the fp64 oracle on the host cores.
 """
 from __future__ import annotations
@@ -71,6 +72,56 @@ def load_traffic():
         return None, None
     hbm, alg = t.get("hbm_bytes_per_call"), t.get("algorithmic_bytes_per_call_of_counted_run")
     return hbm, (round(hbm / alg, 4) if hbm and alg else None)
+
+
+class HipTimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence. Recording
+    a default event makes the queue perform a system-scope cache write-back
+    and invalidate, which shows up as several microseconds of idle queue
+    around the timed call and slows the work after it; this flag skips that
+    (the event then only orders the timestamp, which is all a timer needs).
+    The HIP runtime is the one the process already runs (looked up through
+    libpagedattn's dependencies)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+
+        import paged_kv_cache_49_amd as pa
+        if HipTimingEvent._hip is None:
+            hip = pa.lib()
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipTimingEvent._hip = hip
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        import torch
+        rc = self._hip.hipEventRecord(self.h, self._ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "HipTimingEvent") -> float:
+        """Milliseconds from this event to ``end`` (waits for ``end``)."""
+        ms = self._ct.c_float()
+        if self._hip.hipEventSynchronize(end.h) != 0 or \
+                self._hip.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "h", None) is not None and self.h.value and self._hip is not None:
+            self._hip.hipEventDestroy(self.h)
+            self.h = None
 
 
 def parse():
@@ -202,7 +253,7 @@ def main():
     t0 = time.perf_counter()
     for _ in range(K):
         batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, decode_events=events,
-                   event_layers=(0,))
+                   event_layers=(0,), make_event=HipTimingEvent)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     el = t1 - t0

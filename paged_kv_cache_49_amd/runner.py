@@ -95,12 +95,15 @@ class PagedBatch:
     def step(self, seq_ids: np.ndarray, k_new: Sequence[torch.Tensor], v_new: Sequence[torch.Tensor],
              q: Sequence[torch.Tensor], outs: Sequence[torch.Tensor], scale: float, partition_size: int,
              workspace: Optional[torch.Tensor] = None, ones: Optional[np.ndarray] = None,
-             decode_events: Optional[list] = None, event_layers: Optional[Sequence[int]] = None) -> int:
+             decode_events: Optional[list] = None, event_layers: Optional[Sequence[int]] = None,
+             make_event=None) -> int:
         """Append one token to each of ``seq_ids`` in every layer and run
         decode attention for it. Returns the batch's max context length.
         With ``decode_events`` (a list), a (start, end) pair of HIP events
         recorded around the pa_decode call of each layer in
-        ``event_layers`` (default: every layer) is appended to it."""
+        ``event_layers`` (default: every layer) is appended to it; the events
+        come from ``make_event()`` (default: torch timing events), which must
+        return objects with ``record()`` on the current stream."""
         st = self._stage[self._turn]
         self._turn ^= 1
         if st.copied is not None:
@@ -134,7 +137,8 @@ class PagedBatch:
             reshape_and_cache(c, k_new[i], v_new[i], st.slots[:B])
             timed = decode_events is not None and (event_layers is None or i in event_layers)
             if timed:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                mk = make_event or (lambda: torch.cuda.Event(enable_timing=True))
+                ev = (mk(), mk())
                 ev[0].record()
             decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i], workspace=workspace)
             if timed:
