@@ -12,11 +12,12 @@ One step = one decode step of the whole path: the host block manager
 allocates one slot per sequence (pa_alloc_batch; copy-on-write pairs, none
 here), packs the tables, one pinned host-to-device copy carries slots /
 pairs / tables / lengths (on a copy stream, overlapping the previous step's
-kernels), then per layer pa_copy_blocks (if pairs) ->
-pa_reshape_and_cache (the new token's K/V) -> pa_decode (by default the
-balanced split: one persistent kernel over the resident workgroups, then the
-log-sum-exp merge of sequences cut between them). Inputs are resident in HBM
-before timing starts.
+kernels), then per layer pa_copy_blocks (if pairs) -> pa_decode_append: the
+new token's K/V written into its slot and the balanced-split attention over
+the sequence including it, in one launch (one persistent kernel over the
+resident workgroups, then the log-sum-exp merge of sequences cut between
+them). ``--separate-write`` runs pa_reshape_and_cache then pa_decode
+instead. Inputs are resident in HBM before timing starts.
 
 Printed: one JSON line. ``value`` = KV bytes the decode calls of the timed
 steps must read (2 * L * Hkv * D * 2 per sequence and layer, valid tokens
@@ -134,6 +135,9 @@ def parse():
                    help="-1: balanced split (default); 0: no split; >0: partitions of that many tokens")
     p.add_argument("--v-layout", choices=["dim", "token"], default="dim",
                    help="in-block V layout: dim-major (matrix-core PV) or the token-major KVBlock layout")
+    p.add_argument("--separate-write", action="store_true",
+                   help="write the new token with pa_reshape_and_cache, then pa_decode (default with the balanced "
+                        "split: pa_decode_append, both in one launch)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -243,8 +247,9 @@ def main():
     torch.cuda.synchronize()
     print("[bench] setup done", file=sys.stderr, flush=True)
 
+    fused = args.partition_size == pa.BALANCED and args.v_layout == "dim" and not args.separate_write
     for _ in range(W):
-        batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones)
+        batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, fused=fused)
     torch.cuda.synchronize()
     lens_before = L0 + W
 
@@ -253,7 +258,7 @@ def main():
     t0 = time.perf_counter()
     for _ in range(K):
         batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, decode_events=events,
-                   event_layers=(0,), make_event=HipTimingEvent)
+                   event_layers=(0,), make_event=HipTimingEvent, fused=fused)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     el = t1 - t0
@@ -288,6 +293,8 @@ def main():
                         "block 16, bf16; one decode step per layer, layers share block tables",
             "batch": B, "layers": layers, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": bs, "partition_size": args.partition_size, "v_layout": args.v_layout,
+            "step": "pa_decode_append (write + attention, one launch)" if fused else
+                    "pa_reshape_and_cache + pa_decode",
             "mean_context": round(float(lens_before.mean()) + (K + 1) / 2, 1),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -296,8 +303,9 @@ def main():
         "pa_decode_us": round(call_s * 1e6, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("pa_decode (paged_decode_sk_kernel + decode_sk_merge_kernel)" if args.partition_size < 0
-                       else "pa_decode (partition kernel + decode_reduce_kernel)"),
+            "kernel": (("pa_decode_append" if fused else "pa_decode") +
+                       (" (paged_decode_sk_kernel + decode_sk_merge_kernel)" if args.partition_size < 0
+                        else " (partition kernel + decode_reduce_kernel)")),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

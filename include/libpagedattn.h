@@ -292,6 +292,31 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
                     int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * One decode step's cache write and attention in a single launch: the
+ * effect of pa_reshape_and_cache(cache, k_new, v_new, src_dtype,
+ * slot_mapping, B) followed by pa_decode(..., PA_PARTITION_BALANCED, ...)
+ * ([course] §2 primer: the cache grows by one token per decode step, and
+ * that token takes part in the step's own attention). For each sequence s
+ * with L = context_lens[s] >= 1, token L - 1 is the new one: the attention
+ * reads its K/V from k_new[s] / v_new[s] ([B][num_kv_heads][head_dim],
+ * device, the pool's dtype) instead of from the cache, and writes that row
+ * into the cache at slot_mapping[s] (device int64[B]; < 0: no write).
+ * slot_mapping[s] must be the slot of token L - 1 under block_tables[s]
+ * (what pa_alloc returned for it; PA_DEBUG=1 checks it). Run any
+ * copy-on-write pa_copy_blocks of the step first, on the same stream.
+ *
+ * The other arguments, the workspace and the errors are those of pa_decode
+ * with partition_size = PA_PARTITION_BALANCED. F16 and BF16 pools with
+ * dim-major V only (else PA_ERR_UNSUPPORTED); k_new / v_new 16-byte
+ * aligned, slot_mapping 8-byte aligned (else PA_ERR_INVALID_ARGUMENT).
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const void* v_new, pa_dtype src_dtype,
+                           const int64_t* slot_mapping, void* out, pa_dtype out_dtype, const void* q,
+                           pa_dtype q_dtype, const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* context_lens, int32_t B, int32_t num_q_heads, int32_t max_context_len,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -88,6 +88,8 @@ SIGNATURES = {
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode": (c_int, [POINTER(PaKvCache), _P, c_int, _P, c_int, _P, c_int32, _P, c_int32, c_int32,
                           c_int32, c_float, c_int32, _P, c_size_t, _P]),
+    "pa_decode_append": (c_int, [POINTER(PaKvCache), _P, _P, c_int, _P, _P, c_int, _P, c_int, _P, c_int32, _P,
+                                 c_int32, c_int32, c_int32, c_float, _P, c_size_t, _P]),
 }
 
 _lib = None

@@ -224,17 +224,20 @@ SkLayout sk_layout(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int cus) {
 // The balanced split: one launch of the persistent kernel over the device's
 // resident workgroups, then the merge of sequences cut between them. The
 // arguments are validated by pa_decode.
+// With k_new != nullptr it is the append variant (pa_decode_append).
 pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, const void* q,
                           const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
                           int32_t num_q_heads, int32_t max_context_len, float qk_scale_log2, float v_scale,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                          void* workspace, size_t workspace_bytes, hipStream_t stream, const void* k_new = nullptr,
+                          const void* v_new = nullptr, const int64_t* slot_mapping = nullptr) {
   const int32_t hkv = cache->num_kv_heads;
   const int32_t D = cache->head_dim;
   const int32_t G = num_q_heads / hkv;
-  const SkLaunch launch = find_decode_sk(cache->dtype, D, cache->block_size, G);
+  const bool append = k_new != nullptr;
+  const SkLaunch launch = find_decode_sk(cache->dtype, D, cache->block_size, G, append);
   if (launch == nullptr)
-    return fail(PA_ERR_UNSUPPORTED, "no balanced decode kernel for head_dim %d, block_size %d, group %d", D,
-                cache->block_size, G);
+    return fail(PA_ERR_UNSUPPORTED, "no balanced decode%s kernel for pool dtype %d, head_dim %d, block_size %d, group %d",
+                append ? " + append" : "", (int)cache->dtype, D, cache->block_size, G);
   const int HW = sk_heads_per_wg(hkv);
   const int n_hg = hkv / HW;
   if (sk_lds_bytes(B, HW, G, D) > kSkMaxLds)
@@ -275,6 +278,9 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   p.out_dtype = out_code;
   p.qk_scale_log2 = qk_scale_log2;
   p.v_scale = v_scale;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.slot_mapping = slot_mapping;
   int max_wgs = cus * kSkWavesPerCu / HW;
   if (const char* cap = std::getenv("PA_SK_WGS")) {
     const int v = std::atoi(cap);
@@ -324,11 +330,17 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_h
   return pa::workspace_bytes_for(B, num_q_heads, head_dim, pa::partitions_for(max_context_len, partition_size));
 }
 
-pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
-                    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
-                    int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  pa::clear_error();
+}  // extern "C"
+
+namespace pa {
+namespace {
+
+// pa_decode, and pa_decode_append when k_new != nullptr (validated by it)
+pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
+                      const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                      int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping) {
   pa_status st = pa::validate_cache(cache);
   if (st != PA_OK) return st;
   if (B < 0) return fail(PA_ERR_INVALID_ARGUMENT, "B = %d is negative", B);
@@ -409,9 +421,25 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
   const float qk_scale_log2 = scale * (fp8 ? cache->k_scale : 1.0f) * 1.44269504088896340736f;
   const float v_scale = fp8 ? cache->v_scale : 1.0f;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pa::debug_enabled() && k_new != nullptr) {
+    std::vector<int32_t> lens(B), tab(static_cast<size_t>(B) * max_blocks);
+    std::vector<int64_t> slots(B);
+    if (hipMemcpy(lens.data(), context_lens, sizeof(int32_t) * B, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(tab.data(), block_tables, sizeof(int32_t) * tab.size(), hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(slots.data(), slot_mapping, sizeof(int64_t) * B, hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(PA_ERR_DEVICE, "PA_DEBUG: reading block_tables / context_lens / slot_mapping failed");
+    for (int32_t i = 0; i < B; ++i) {
+      if (slots[i] < 0 || lens[i] <= 0) continue;
+      const int32_t t = lens[i] - 1;
+      const int64_t want = static_cast<int64_t>(tab[static_cast<size_t>(i) * max_blocks + t / bs]) * bs + t % bs;
+      if (slots[i] != want)
+        return fail(PA_ERR_INVALID_ARGUMENT, "slot_mapping[%d] = %lld is not the slot of token %d (%lld)", i,
+                    (long long)slots[i], t, (long long)want);
+    }
+  }
   if (balanced) return pa::decode_balanced(cache, out, out_c, q, block_tables, max_blocks, context_lens, B,
                                            num_q_heads, max_context_len, qk_scale_log2, v_scale, workspace,
-                                           workspace_bytes, s);
+                                           workspace_bytes, s, k_new, v_new, slot_mapping);
 
   pa::DecodeParams prm{};
   prm.q = q;
@@ -460,6 +488,47 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
     if (e != hipSuccess) return fail(PA_ERR_DEVICE, "decode reduce launch: %s", hipGetErrorString(e));
   }
   return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
+                    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                    int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  return pa::decode_impl(cache, out, out_dtype, q, q_dtype, block_tables, max_blocks, context_lens, B, num_q_heads,
+                         max_context_len, scale, partition_size, workspace, workspace_bytes, stream, nullptr, nullptr,
+                         nullptr);
+}
+
+pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const void* v_new, pa_dtype src_dtype,
+                           const int64_t* slot_mapping, void* out, pa_dtype out_dtype, const void* q,
+                           pa_dtype q_dtype, const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* context_lens, int32_t B, int32_t num_q_heads, int32_t max_context_len,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  pa_status st = pa::validate_cache(cache);
+  if (st != PA_OK) return st;
+  if (B > 0 && (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "k_new, v_new or slot_mapping is NULL");
+  if (cache->dtype != PA_F16 && cache->dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_append takes F16 or BF16 pools (pool dtype %d)", (int)cache->dtype);
+  if (src_dtype != cache->dtype)
+    return fail(PA_ERR_UNSUPPORTED, "k_new / v_new dtype %d differs from the pool dtype %d", (int)src_dtype,
+                (int)cache->dtype);
+  if (cache->v_layout != PA_LAYOUT_DIM_MAJOR)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_append needs a pool with dim-major V blocks");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(slot_mapping) % 8 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "k_new / v_new must be 16-byte aligned, slot_mapping 8-byte aligned");
+  if (B == 0) return PA_OK;
+  return pa::decode_impl(cache, out, out_dtype, q, q_dtype, block_tables, max_blocks, context_lens, B, num_q_heads,
+                         max_context_len, scale, PA_PARTITION_BALANCED, workspace, workspace_bytes, stream, k_new,
+                         v_new, slot_mapping);
 }
 
 }  // extern "C"

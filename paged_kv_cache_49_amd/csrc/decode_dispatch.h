@@ -25,15 +25,17 @@ DecodeLaunch find_decode_vt_f16(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_vt_bf16(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_vt_fp8(int head_dim, int block_size, int group);
 
-SkLaunch find_decode_sk_f16(int head_dim, int block_size, int group);
-SkLaunch find_decode_sk_bf16(int head_dim, int block_size, int group);
-SkLaunch find_decode_sk_fp8(int head_dim, int block_size, int group);
+// append: the variant that also writes each sequence's newest token
+// (pa_decode_append; 16-bit pools only, nullptr otherwise)
+SkLaunch find_decode_sk_f16(int head_dim, int block_size, int group, bool append);
+SkLaunch find_decode_sk_bf16(int head_dim, int block_size, int group, bool append);
+SkLaunch find_decode_sk_fp8(int head_dim, int block_size, int group, bool append);
 
-inline SkLaunch find_decode_sk(pa_dtype pool, int head_dim, int block_size, int group) {
+inline SkLaunch find_decode_sk(pa_dtype pool, int head_dim, int block_size, int group, bool append) {
   switch (pool) {
-    case PA_F16: return find_decode_sk_f16(head_dim, block_size, group);
-    case PA_BF16: return find_decode_sk_bf16(head_dim, block_size, group);
-    case PA_FP8_E4M3: return find_decode_sk_fp8(head_dim, block_size, group);
+    case PA_F16: return find_decode_sk_f16(head_dim, block_size, group, append);
+    case PA_BF16: return find_decode_sk_bf16(head_dim, block_size, group, append);
+    case PA_FP8_E4M3: return find_decode_sk_fp8(head_dim, block_size, group, append);
     default: return nullptr;
   }
 }

@@ -3,7 +3,7 @@
 #include "decode_sk_kernel.h"
 
 namespace pa {
-SkLaunch find_decode_sk_f16(int head_dim, int block_size, int group) {
-  return select_decode_sk<F16, F16>(head_dim, block_size, group);
+SkLaunch find_decode_sk_f16(int head_dim, int block_size, int group, bool append) {
+  return select_decode_sk<F16, F16>(head_dim, block_size, group, append);
 }
 }  // namespace pa

@@ -21,6 +21,12 @@
 // Per workgroup:
 //  * plan: tiles per sequence (lengths clamped to the launch bound) and
 //    their exclusive prefix go to LDS.
+//  * append variant (AP): the newest token of each sequence (position
+//    L - 1) is not read from the cache but from k_new / v_new, as one extra
+//    unit per sequence holding a single valid row (the "virtual tile"); the
+//    wave that computes it also writes that row into the cache at
+//    slot_mapping[s]. The cache tiles then cover positions 0 .. L - 2. This
+//    is pa_reshape_and_cache followed by pa_decode in one launch.
 //  * unit batches: lane i of a batch resolves unit ub + i to its sequence,
 //    tile, length, head group and block id(s); the batch after it is
 //    requested one batch ahead, so block-table reads never stall the loads.
@@ -56,6 +62,9 @@ struct SkParams {
   float* piece_l;       // [W][2][HW * G]
   float* piece_o;       // [W][2][HW * G][D]
   int32_t* seg_desc;    // [head groups][B][2] merge descriptors, see below
+  const void* k_new;              // append: [B][num_kv_heads][D] (pool dtype)
+  const void* v_new;              // append: [B][num_kv_heads][D]
+  const int64_t* slot_mapping;    // append: [B] cache slot of token L - 1 (< 0: no write)
   const int32_t* block_tables;
   const int32_t* context_lens;
   int64_t block_stride;  // elements
@@ -98,12 +107,15 @@ inline size_t sk_lds_bytes(int B, int HW, int G, int D) {
   return pref + static_cast<size_t>(HW) * G * D * sizeof(float);
 }
 
-// A unit as the wave sees it (uniform values).
+// A unit as the wave sees it (uniform values). len = valid tokens counted
+// from the unit's first position; virt = the append variant's virtual tile,
+// whose slot block / offset are sblk / soff.
 struct SkUnit {
   int seq, tile, len, hg;
+  int virt, sblk, soff;
 };
 
-template <typename KV, typename QT, int D, int BS, int G>
+template <typename KV, typename QT, int D, int BS, int G, bool AP>
 __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
@@ -123,7 +135,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
     int L = p.context_lens[i];
     L = L < p.len_cap ? L : p.len_cap;
-    s_pref[i] = L > 0 ? (L + 15) >> 4 : 0;
+    // append: the cache holds L - 1 tokens, plus the virtual tile
+    s_pref[i] = L > 0 ? (AP ? ((L + 14) >> 4) + 1 : (L + 15) >> 4) : 0;
   }
   __syncthreads();
   if (wave == 0) {
@@ -182,6 +195,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   struct Batch {
     int ub;
     int seq, tile, len, hg, ida, idb;
+    int virt, sblk, soff;  // append only
   };
   // Lanes past the range resolve the range's last unit: every lane loads,
   // so the loads land in the batch registers with no merge that would wait.
@@ -194,9 +208,20 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     const int s = sk_find_seq(s_pref, B, r);
     const int t = r - s_pref[s];
     const int32_t* row = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
-    const int blk_a = BS >= 16 ? (t * 16) / BS : 2 * t;
+    b.virt = AP && t == s_pref[s + 1] - s_pref[s] - 1;
+    // (a virtual tile reads no cache block; its table index could lie past
+    // the table's end)
+    const int blk_a = b.virt ? 0 : (BS >= 16 ? (t * 16) / BS : 2 * t);
     b.len = p.context_lens[s];
     b.ida = row[blk_a];
+    if constexpr (AP) {
+      const int64_t sl = p.slot_mapping[s];
+      b.sblk = sl >= 0 ? static_cast<int>(sl / BS) : -1;
+      b.soff = sl >= 0 ? static_cast<int>(sl % BS) : 0;
+    } else {
+      b.sblk = -1;
+      b.soff = 0;
+    }
     // the tile's second block; past the sequence's last block its value is
     // never used (those tokens are masked)
     b.idb = BS < 16 ? row[min(blk_a + 1, p.max_blocks - 1)] : 0;
@@ -215,6 +240,10 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     un.tile = __builtin_amdgcn_readlane(b.tile, o);
     un.len = min(__builtin_amdgcn_readlane(b.len, o), p.len_cap);
     un.hg = __builtin_amdgcn_readlane(b.hg, o);
+    un.virt = AP ? __builtin_amdgcn_readlane(b.virt, o) : 0;
+    un.sblk = AP ? __builtin_amdgcn_readlane(b.sblk, o) : -1;
+    un.soff = AP ? __builtin_amdgcn_readlane(b.soff, o) : 0;
+    if (AP) un.len = un.virt ? 1 : un.len - 1;  // the virtual tile holds token L - 1 alone
     const int ida = block_id(__builtin_amdgcn_readlane(b.ida, o));
     const int g = un.hg * HW + wave;
     // the unit's q rows (B operand of S^T = K q^T); columns >= G repeat head
@@ -228,37 +257,44 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 #pragma unroll
       for (int i = 0; i < C::kKSteps; ++i) qr[i] = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
     }
+    // K row addresses and V run addresses of the unit's tile: from the cache,
+    // or (append variant) from the newest token's k_new / v_new row. Both
+    // cases issue the same load instructions, so the loads in flight per
+    // ring slot stay fixed and the compiler's waits stay tight.
+    const char* krow;  // lane's K row minus its first head-dim offset (see below)
+    const char* vrun;  // lane's V run for n-tile 0
     if constexpr (BS >= 16) {
       const int tin = (un.tile * 16) % BS;
-      const char* kb = kbase + static_cast<int64_t>(ida) * blk_bytes + tin * tok_bytes + static_cast<int64_t>(g) * D * kB;
-      const char* krow = kb + koff_lane;
-#pragma unroll
-      for (int i = 0; i < C::kKLoads; ++i) {
-        const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
-        kr[i] = *reinterpret_cast<const u32x4*>(krow + off - qk_dim<kB>(0, j) * kB);
-      }
-      const char* vb = vbase + static_cast<int64_t>(ida) * blk_bytes + (static_cast<int64_t>(g) * D * BS + tin) * kB;
-      const char* vrun = vb + voff_lane;
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VRaw*>(vrun + nt * kVTileBytes);
+      krow = kbase + static_cast<int64_t>(ida) * blk_bytes + tin * tok_bytes + static_cast<int64_t>(g) * D * kB +
+             koff_lane - qk_dim<kB>(0, j) * kB;
+      vrun = vbase + static_cast<int64_t>(ida) * blk_bytes + (static_cast<int64_t>(g) * D * BS + tin) * kB + voff_lane;
     } else {
       // a tile spans two blocks: tokens 0..BS-1 in block A, the rest in B
       const int idb = block_id(__builtin_amdgcn_readlane(b.idb, o));
       const int idk = col < BS ? ida : idb;
-      const char* krow = kbase + static_cast<int64_t>(idk) * blk_bytes + (col % BS) * tok_bytes +
-                         static_cast<int64_t>(g) * D * kB;
-#pragma unroll
-      for (int i = 0; i < C::kKLoads; ++i) {
-        const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
-        kr[i] = *reinterpret_cast<const u32x4*>(krow + off);
-      }
+      krow = kbase + static_cast<int64_t>(idk) * blk_bytes + (col % BS) * tok_bytes + static_cast<int64_t>(g) * D * kB;
       const int t4 = 4 * j;
       const int idv = t4 < BS ? ida : idb;
-      const char* vrun = vbase + static_cast<int64_t>(idv) * blk_bytes +
-                         ((static_cast<int64_t>(g) * D + col) * BS + t4 % BS) * kB;
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VRaw*>(vrun + nt * kVTileBytes);
+      vrun = vbase + static_cast<int64_t>(idv) * blk_bytes + ((static_cast<int64_t>(g) * D + col) * BS + t4 % BS) * kB;
     }
+    int vstep = kVTileBytes;
+    if constexpr (AP) {
+      if (un.virt) {
+        // every K row reads the new token's row (rows past the first are
+        // masked); lane (d, j) reads the 4-dim group holding v_new[d] (the
+        // compute step moves element d % 4 into the first token's place)
+        krow = static_cast<const char*>(p.k_new) + (static_cast<int64_t>(un.seq) * Hkv + g) * D * kB;
+        vrun = static_cast<const char*>(p.v_new) + ((static_cast<int64_t>(un.seq) * Hkv + g) * D + (col & ~3)) * kB;
+        vstep = 16 * kB;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::kKLoads; ++i) {
+      const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
+      kr[i] = *reinterpret_cast<const u32x4*>(krow + off);
+    }
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VRaw*>(vrun + nt * vstep);
     return un;
   };
 
@@ -320,9 +356,16 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     wave_lds_sync();
   };
 
+  // append: the new token's element v_new[d] (d = lane's dim) out of the
+  // four-dim group its lane loaded
+  auto virt_v = [&](const u32x2& grp) -> uint32_t {
+    const uint32_t w2 = (col & 2) ? grp.y : grp.x;
+    return (col & 1) ? (w2 >> 16) : (w2 & 0xffffu);
+  };
+
   auto compute = [&](int x, const SkUnit& un, const u32x4 (&qb)[C::kKSteps], const u32x4 (&kr)[C::kKLoads],
                      const VRaw (&vr)[kNT]) {
-    const int tb = un.tile * 16;
+    const int tb = AP && un.virt ? 0 : un.tile * 16;
     const int L = un.len;
     // ---- S^T = K q^T
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -379,6 +422,9 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       u32x2 vop;
       if constexpr (kB == 2) {
         vop = vr[nt];
+        if constexpr (AP) {
+          if (un.virt) vop = u32x2{virt_v(vr[nt]), 0u};
+        }
       } else {
         vop = e4m3x4_to_bf16x4(vr[nt]);
       }
@@ -387,8 +433,26 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       acc[nt] = mfma_16x16x16<QT>(phi, vop, acc[nt]);
       acc[nt] = mfma_16x16x16<QT>(plo, vop, acc[nt]);
     }
+    // ---- append: write the newest token's row into its cache slot
+    if constexpr (AP) {
+      if (un.virt && static_cast<uint32_t>(un.sblk) < static_cast<uint32_t>(p.num_blocks)) {
+        const int g = un.hg * HW + wave;
+        char* kdst = const_cast<char*>(kbase) + static_cast<int64_t>(un.sblk) * blk_bytes + un.soff * tok_bytes +
+                     static_cast<int64_t>(g) * D * kB;
+        if (col == 0) {
+#pragma unroll
+          for (int i = 0; i < C::kKLoads; ++i) *reinterpret_cast<u32x4*>(kdst + qk_dim<kB>(i, j) * kB) = kr[i];
+        }
+        uint16_t* vdst = reinterpret_cast<uint16_t*>(const_cast<char*>(vbase) + static_cast<int64_t>(un.sblk) * blk_bytes) +
+                         (static_cast<int64_t>(g) * D + col) * BS + un.soff;
+        if (j == 0) {
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) vdst[nt * 16 * BS] = static_cast<uint16_t>(virt_v(vr[nt]));
+        }
+      }
+    }
     // ---- end of a segment: store it, then start the next one at x + 1
-    const bool seq_end = un.tile == ((L + 15) >> 4) - 1;
+    const bool seq_end = AP ? un.virt != 0 : un.tile == ((L + 15) >> 4) - 1;
     if (seq_end || x + 1 == u1) {
       flush(un.seq, un.hg, seg_begun && seq_end, seq_end, seg_first ? 0 : 1);
       if (x + 1 < u1) {
@@ -446,16 +510,16 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 
 // Launch of the balanced kernel: W = resident workgroups (occupancy x CUs),
 // at most max_wgs. Writes the grid size used to *wgs.
-template <typename KV, typename QT, int D, int BS, int G>
+template <typename KV, typename QT, int D, int BS, int G, bool AP>
 hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
   const int HW = p.heads_per_wg;
   const size_t lds = sk_lds_bytes(p.batch, HW, G, D);
   // occupancy per (HW, LDS in 4 KiB steps); racing writers store the same value
-  static int cache[9][17];
+  static int cache[9][17];  // per instantiation
   const int lb = static_cast<int>((lds + 4095) / 4096);
   int occ = (HW <= 8 && lb <= 16) ? cache[HW][lb] : 0;
   if (occ <= 0) {
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, paged_decode_sk_kernel<KV, QT, D, BS, G>,
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, paged_decode_sk_kernel<KV, QT, D, BS, G, AP>,
                                                                 64 * HW, lds);
     if (e != hipSuccess) return e;
     if (occ <= 0) return hipErrorInvalidConfiguration;
@@ -464,36 +528,48 @@ hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t
   int W = cus * occ;
   W = W < max_wgs ? W : max_wgs;
   *wgs = W;
-  hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G>), dim3(W), dim3(64 * HW), lds, stream, p);
+  hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G, AP>), dim3(W), dim3(64 * HW), lds, stream, p);
   return hipGetLastError();
 }
 
-template <typename KV, typename QT, int D, int BS>
+template <typename KV, typename QT, int D, int BS, bool AP>
 SkLaunch select_decode_sk_g(int G) {
   switch (G) {
-    case 1: return &launch_decode_sk<KV, QT, D, BS, 1>;
-    case 2: return &launch_decode_sk<KV, QT, D, BS, 2>;
-    case 4: return &launch_decode_sk<KV, QT, D, BS, 4>;
-    case 8: return &launch_decode_sk<KV, QT, D, BS, 8>;
+    case 1: return &launch_decode_sk<KV, QT, D, BS, 1, AP>;
+    case 2: return &launch_decode_sk<KV, QT, D, BS, 2, AP>;
+    case 4: return &launch_decode_sk<KV, QT, D, BS, 4, AP>;
+    case 8: return &launch_decode_sk<KV, QT, D, BS, 8, AP>;
     default: return nullptr;
   }
 }
 
-template <typename KV, typename QT, int D>
+template <typename KV, typename QT, int D, bool AP>
 SkLaunch select_decode_sk_bs(int BS, int G) {
   switch (BS) {
-    case 8: return select_decode_sk_g<KV, QT, D, 8>(G);
-    case 16: return select_decode_sk_g<KV, QT, D, 16>(G);
-    case 32: return select_decode_sk_g<KV, QT, D, 32>(G);
+    case 8: return select_decode_sk_g<KV, QT, D, 8, AP>(G);
+    case 16: return select_decode_sk_g<KV, QT, D, 16, AP>(G);
+    case 32: return select_decode_sk_g<KV, QT, D, 32, AP>(G);
     default: return nullptr;
   }
 }
 
+// append = the fused cache write (16-bit pools only)
 template <typename KV, typename QT>
-SkLaunch select_decode_sk(int D, int BS, int G) {
+SkLaunch select_decode_sk(int D, int BS, int G, bool append) {
+  if (append) {
+    if constexpr (KV::kBytes != 2) {
+      return nullptr;
+    } else {
+      switch (D) {
+        case 64: return select_decode_sk_bs<KV, QT, 64, true>(BS, G);
+        case 128: return select_decode_sk_bs<KV, QT, 128, true>(BS, G);
+        default: return nullptr;
+      }
+    }
+  }
   switch (D) {
-    case 64: return select_decode_sk_bs<KV, QT, 64>(BS, G);
-    case 128: return select_decode_sk_bs<KV, QT, 128>(BS, G);
+    case 64: return select_decode_sk_bs<KV, QT, 64, false>(BS, G);
+    case 128: return select_decode_sk_bs<KV, QT, 128, false>(BS, G);
     default: return nullptr;
   }
 }

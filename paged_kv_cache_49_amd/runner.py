@@ -10,7 +10,10 @@ and runs the serving loop's steps through the C ABI:
                        sequence (copy-on-write pairs included), upload the
                        slot mapping / pairs / tables / lengths in a single
                        host-to-device copy from pinned memory, then per layer
-                       pa_copy_blocks -> pa_reshape_and_cache -> pa_decode
+                       pa_copy_blocks -> pa_reshape_and_cache -> pa_decode,
+                       or with ``fused=True`` pa_copy_blocks ->
+                       pa_decode_append (the write and the attention in one
+                       launch; balanced split, 16-bit pools)
 
 The metadata staging area is double-buffered: a buffer is refilled only
 after the copy issued from it two steps earlier has completed (HIP event),
@@ -27,7 +30,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import BlockManager, KVCache, copy_blocks, decode, decode_workspace_size, reshape_and_cache
+from . import (BALANCED, BlockManager, KVCache, copy_blocks, decode, decode_append, decode_workspace_size,
+               reshape_and_cache)
 
 
 class _Staging:
@@ -96,7 +100,7 @@ class PagedBatch:
              q: Sequence[torch.Tensor], outs: Sequence[torch.Tensor], scale: float, partition_size: int,
              workspace: Optional[torch.Tensor] = None, ones: Optional[np.ndarray] = None,
              decode_events: Optional[list] = None, event_layers: Optional[Sequence[int]] = None,
-             make_event=None) -> int:
+             make_event=None, fused: bool = False) -> int:
         """Append one token to each of ``seq_ids`` in every layer and run
         decode attention for it. Returns the batch's max context length.
         With ``decode_events`` (a list), a (start, end) pair of HIP events
@@ -134,13 +138,20 @@ class PagedBatch:
         for i, c in enumerate(self.caches):
             if ncow:
                 copy_blocks(c, st.cow[:ncow])
-            reshape_and_cache(c, k_new[i], v_new[i], st.slots[:B])
+            if not fused:
+                reshape_and_cache(c, k_new[i], v_new[i], st.slots[:B])
             timed = decode_events is not None and (event_layers is None or i in event_layers)
             if timed:
                 mk = make_event or (lambda: torch.cuda.Event(enable_timing=True))
                 ev = (mk(), mk())
                 ev[0].record()
-            decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i], workspace=workspace)
+            if fused:
+                if partition_size != BALANCED:
+                    raise ValueError("fused steps use the balanced split (partition_size = BALANCED)")
+                decode_append(c, k_new[i], v_new[i], st.slots[:B], q[i], tables, lens, max_ctx, scale, out=outs[i],
+                              workspace=workspace)
+            else:
+                decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i], workspace=workspace)
             if timed:
                 ev[1].record()
                 decode_events.append(ev)

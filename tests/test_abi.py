@@ -207,6 +207,37 @@ def test_decode_rejects_bad_arguments_before_launch(kw, cache_kw, want):
         assert pa.lib().pa_last_error().decode() != ""
 
 
+def _append_status(cache, **kw):
+    a = dict(k_new=0x7000, v_new=0x8000, src=_lib.PA_BF16, slots=0x9000, out=0x3000, out_dtype=_lib.PA_BF16,
+             q=0x4000, q_dtype=_lib.PA_BF16, tables=0x5000, max_blocks=8, lens=0x6000, B=2, Hq=32, max_ctx=128,
+             scale=0.1, ws=None, ws_bytes=0)
+    a.update(kw)
+    return pa.lib().pa_decode_append(ctypes.byref(cache), a["k_new"], a["v_new"], a["src"], a["slots"], a["out"],
+                                     a["out_dtype"], a["q"], a["q_dtype"], a["tables"], a["max_blocks"], a["lens"],
+                                     a["B"], a["Hq"], a["max_ctx"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+_DIM = dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR)
+
+
+@pytest.mark.parametrize("kw,cache_kw,want", [
+    (dict(), dict(), _lib.PA_ERR_UNSUPPORTED),                                    # token-major V
+    (dict(), dict(_DIM, dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1), _lib.PA_ERR_UNSUPPORTED),  # fp8 pool
+    (dict(src=_lib.PA_F16), _DIM, _lib.PA_ERR_UNSUPPORTED),                       # source dtype != pool dtype
+    (dict(k_new=None), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(slots=None), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(v_new=0x8008), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                     # misaligned
+    (dict(slots=0x9004), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                     # misaligned
+    (dict(), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                                 # no workspace
+    (dict(Hq=30), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                            # the checks of pa_decode
+    (dict(B=0), _DIM, _lib.PA_OK),
+])
+def test_decode_append_rejects_bad_arguments_before_launch(kw, cache_kw, want):
+    assert _append_status(_fake_cache(**cache_kw), **kw) == want
+    if want != _lib.PA_OK:
+        assert pa.lib().pa_last_error().decode() != ""
+
+
 def test_workspace_size():
     f = pa.decode_workspace_size
     assert f(64, 32, 8, 128, 4096, 0) == 0

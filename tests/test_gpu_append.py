@@ -1,0 +1,145 @@
+"""pa_decode_append on the GPU: one launch that writes each sequence's newest
+token into its cache slot and runs the balanced decode including it.
+
+Every case prefills L - 1 tokens of each sequence through the library,
+allocates the last token's slot with the block manager, then compares
+
+* the pools after pa_decode_append with the pools after
+  pa_reshape_and_cache of the same rows, bit for bit (the slot write);
+* the output with the oracle's attention over all L tokens (north-star
+  tolerance), and with pa_reshape_and_cache + pa_decode.
+
+Lengths put the new token at the start of a block and of a 16-token tile,
+in the middle of one, and alone (L = 1); PA_SK_WGS caps the grid so the
+new token's tile also falls on a cut between workgroups."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_49_amd as pa
+import synth
+from tests import helpers as H
+from tests.gpu_util import pool_bits, poison_fill, say
+
+pytestmark = pytest.mark.gpu
+
+BAL = pa.BALANCED
+LENGTHS = [1, 2, 16, 17, 33, 100, 129, 512, 513, 1000]
+
+
+@pytest.fixture
+def wgs(monkeypatch):
+    def set_wgs(n):
+        if n is None:
+            monkeypatch.delenv("PA_SK_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_SK_WGS", str(n))
+    return set_wgs
+
+
+def _setup(wl):
+    """Two identical caches holding L - 1 tokens per sequence, the new
+    token's slots, and the device tables / lengths after the allocation."""
+    bm = pa.BlockManager(wl.num_blocks, wl.block_size, wl.free_order)
+    caches = [pa.KVCache.allocate(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
+                                  fill=poison_fill(wl.kv_dtype), v_layout="dim") for _ in range(2)]
+    k_new, v_new, slots = [], [], []
+    for s in range(wl.batch):
+        k, v = wl.kv(s)
+        L = int(wl.lengths[s])
+        sl, cows = bm.alloc(s, L - 1)
+        assert not cows
+        if L > 1:
+            sd = torch.from_numpy(sl).cuda()
+            for c in caches:
+                pa.reshape_and_cache(c, k[:L - 1].cuda(), v[:L - 1].cuda(), sd)
+        sl1, cows = bm.alloc(s, 1)
+        assert not cows
+        slots.append(int(sl1[0]))
+        k_new.append(k[L - 1])
+        v_new.append(v[L - 1])
+    mb = H.max_blocks_for(wl.lengths, wl.block_size)
+    t, l = bm.pack(list(range(wl.batch)), mb, -1)
+    tables = torch.from_numpy(np.asarray(t, np.int32)).cuda()
+    lens = torch.from_numpy(np.asarray(l, np.int32)).cuda()
+    assert np.array_equal(np.asarray(l), wl.lengths)
+    return (caches, torch.stack(k_new).cuda().contiguous(), torch.stack(v_new).cuda().contiguous(),
+            torch.tensor(slots, dtype=torch.int64).cuda(), tables, lens, int(wl.lengths.max()))
+
+
+def _run(wl, what):
+    say(f"append {wl.name} kv={wl.kv_dtype} D={wl.head_dim} bs={wl.block_size} Hkv={wl.num_kv_heads} "
+        f"G={wl.group} {what}")
+    (ca, cb), k_new, v_new, slots, tables, lens, max_ctx = _setup(wl)
+    q = wl.q().cuda()
+    # two launches: the slot write, then the decode
+    pa.reshape_and_cache(ca, k_new, v_new, slots)
+    out_a = pa.decode(ca, q, tables, lens, max_ctx, wl.scale, BAL, out_dtype=torch.float32)
+    # one launch
+    out_b = pa.decode_append(cb, k_new, v_new, slots, q, tables, lens, max_ctx, wl.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for which in ("k", "v"):
+        assert np.array_equal(pool_bits(cb, which), pool_bits(ca, which)), f"{which} pool differs ({what})"
+    ref = H.oracle_contiguous(wl)
+    got_b = out_b.cpu().double().numpy()
+    ma, rl = H.assert_close(got_b, ref, what=f"append {what}")
+    H.assert_close(got_b, out_a.cpu().double().numpy(), what=f"append vs write+decode {what}")
+    say(f"   max-abs {ma:.2e}  rel-L2 {rl:.2e}")
+
+
+CASES = [
+    ("bf16", 128, 16, 4, 8),
+    ("bf16", 128, 8, 8, 2),
+    ("bf16", 64, 32, 1, 4),
+    ("f16", 128, 16, 2, 8),
+    ("f16", 64, 8, 4, 3),
+    ("f16", 128, 32, 8, 1),
+]
+
+
+@pytest.mark.parametrize("cap", [None, 1, 5])
+@pytest.mark.parametrize("kv,D,bs,G,hkv", CASES, ids=lambda c: str(c))
+def test_append_parity(gpu, wgs, kv, D, bs, G, hkv, cap):
+    wgs(cap)
+    wl = synth.random_case(3000 + D + bs + G + hkv, LENGTHS, G * hkv, hkv, D, bs, kv)
+    _run(wl, f"cap={cap}")
+
+
+def test_append_gqa_batch_rows(gpu):
+    """The benchmark's shape (64 sequences, U[512, 4096], 32/8 heads, D 128,
+    bf16), sampled rows against the oracle."""
+    wl = synth.gqa_decode()
+    say("append gqa batch")
+    (ca, cb), k_new, v_new, slots, tables, lens, max_ctx = _setup(wl)
+    q = wl.q().cuda()
+    pa.reshape_and_cache(ca, k_new, v_new, slots)
+    out_b = pa.decode_append(cb, k_new, v_new, slots, q, tables, lens, max_ctx, wl.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for which in ("k", "v"):
+        assert np.array_equal(pool_bits(cb, which), pool_bits(ca, which)), which
+    rows = [0, 1, 17, 31, 32, 50, 63]
+    ref = H.oracle_contiguous(wl, seqs=rows)
+    got = out_b.cpu().double().numpy()
+    H.assert_close(got[rows], ref[rows], what="append gqa rows")
+
+
+def test_append_skipped_slot_and_empty_sequence(gpu):
+    """slot < 0: no write, the token still takes part; L = 0: zero rows."""
+    wl = synth.random_case(3100, [40, 1, 70], 8, 2, 128, 16, "bf16")
+    (ca, cb), k_new, v_new, slots, tables, lens, max_ctx = _setup(wl)
+    before = (pool_bits(cb, "k"), pool_bits(cb, "v"))
+    slots_skip = torch.full_like(slots, -1)
+    q = wl.q().cuda()
+    out = pa.decode_append(cb, k_new, v_new, slots_skip, q, tables, lens, max_ctx, wl.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_bits(cb, "k"), before[0]) and np.array_equal(pool_bits(cb, "v"), before[1])
+    H.assert_close(out.cpu().double().numpy(), H.oracle_contiguous(wl), what="skipped slots")
+    # a zero-length sequence next to appended ones
+    lens0 = lens.clone()
+    lens0[1] = 0
+    out0 = pa.decode_append(cb, k_new, v_new, slots_skip, q, tables, lens0, max_ctx, wl.scale,
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out0.cpu().double().numpy()
+    assert np.array_equal(got[1], np.zeros_like(got[1]))
+    H.assert_close(got[[0, 2]], H.oracle_contiguous(wl, seqs=[0, 2])[[0, 2]], what="with an empty sequence")
