@@ -155,6 +155,24 @@ pa_status pa_seq_blocks(const pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_
 pa_status pa_pack_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
                                int32_t pad, int32_t* tables, int32_t* context_lens);
 
+/* Groups of the batch rows seq_ids[0..n) whose block tables begin with the
+ * same physical blocks — forks of one prompt ([course] §2 "The bonus":
+ * parallel samples share the prompt's blocks; [note] prefix-sharing
+ * section) — for pa_decode_shared. Rows are grouped by their first block;
+ * a group's shared length is the longest run of leading table entries that
+ * all members hold, in whole `granule`-token units (granule = the decode's
+ * partition size, a positive multiple of block_size), and below every
+ * member's length, so each member keeps at least one token of its own.
+ * Groups of one row or with a shared length of 0 are left out; their rows
+ * get shared_len 0. Outputs (host, caller-owned): group_offsets[groups + 1]
+ * (capacity n / 2 + 1 suffices), group_members (batch rows, grouped;
+ * capacity n), shared_len[n] (tokens, per row), *num_groups,
+ * *max_group_size, *max_shared_len. Errors: PA_ERR_UNKNOWN_SEQ,
+ * PA_ERR_INVALID_ARGUMENT. */
+pa_status pa_bm_shared_prefixes(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t granule,
+                                int32_t* group_offsets, int32_t* group_members, int32_t* shared_len,
+                                int32_t* num_groups, int32_t* max_group_size, int32_t* max_shared_len);
+
 pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out);
 /* Refcount of every block: host int32[num_blocks]. */
 pa_status pa_bm_refcounts(const pa_bm* bm, int32_t* out);
@@ -316,6 +334,35 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const vo
                            pa_dtype q_dtype, const int32_t* block_tables, int32_t max_blocks,
                            const int32_t* context_lens, int32_t B, int32_t num_q_heads, int32_t max_context_len,
                            float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention with shared prefixes read once per group ([course] §2
+ * "The bonus": forked sequences share the prompt's blocks; [note]
+ * prefix-sharing section). The result is that of pa_decode with the same
+ * arguments and partition_size; what differs is the K/V traffic: each
+ * partition of a group's shared prefix is read once for all the group's
+ * query rows, instead of once per member.
+ *
+ * Groups (device arrays, typically from pa_bm_shared_prefixes): group gi's
+ * batch rows are group_members[group_offsets[gi] .. group_offsets[gi + 1]);
+ * shared_len[s] (device int32[B]) = tokens at the start of row s that its
+ * whole group shares: the same value for every member, a multiple of
+ * partition_size, below context_lens[s], and the members' tables identical
+ * over those tokens' blocks; 0 for rows in no group. max_group_size >= the
+ * largest group, max_shared_len >= every shared_len (and < max_context_len)
+ * size the launch. PA_DEBUG=1 checks all of this; otherwise a violation
+ * gives wrong results for the rows involved (no out-of-bounds access).
+ *
+ * partition_size: a positive multiple of 16 and of block_size; the
+ * workspace is pa_decode_workspace_size(..., partition_size). Pools with
+ * dim-major V only. Other arguments and errors as pa_decode.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
+                           const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                           int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
+                           const int32_t* group_offsets, const int32_t* group_members, const int32_t* shared_len,
+                           int32_t num_groups, int32_t max_group_size, int32_t max_shared_len, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ from ._lib import PaBmStats, PaKvCache, lib
 __all__ = [
     "PagedAttnError", "OutOfBlocks", "UnknownSeq", "SeqExists", "Unsupported", "InvalidArgument",
     "DeviceError", "BlockManager", "KVCache", "reshape_and_cache", "copy_blocks", "decode",
-    "decode_workspace_size", "decode_append", "lib", "BALANCED",
+    "decode_workspace_size", "decode_append", "decode_shared", "SharedPrefixes", "lib", "BALANCED",
 ]
 
 
@@ -130,6 +130,21 @@ def _ptr(a: np.ndarray) -> int:
 # host block manager
 
 
+@dataclasses.dataclass
+class SharedPrefixes:
+    """Output of BlockManager.shared_prefixes (host arrays): group gi's batch
+    rows are members[offsets[gi]:offsets[gi + 1]]; shared_len[row] tokens."""
+    offsets: np.ndarray
+    members: np.ndarray
+    shared_len: np.ndarray
+    num_groups: int
+    max_group_size: int
+    max_shared_len: int
+
+    def groups(self) -> list:
+        return [self.members[self.offsets[g]:self.offsets[g + 1]].tolist() for g in range(self.num_groups)]
+
+
 class BlockManager:
     """Owns a pa_bm handle (see include/libpagedattn.h for the semantics)."""
 
@@ -201,6 +216,25 @@ class BlockManager:
         _check(lib().pa_pack_block_tables(self._h, _ptr(ids), len(ids), int(max_blocks), int(pad),
                                           _ptr(tables), _ptr(context_lens)))
         return tables, context_lens
+
+    def shared_prefixes(self, seq_ids, granule: int, group_offsets: Optional[np.ndarray] = None,
+                        group_members: Optional[np.ndarray] = None, shared_len: Optional[np.ndarray] = None):
+        """pa_bm_shared_prefixes: groups of the rows of ``seq_ids`` whose
+        tables start with the same blocks. Returns a SharedPrefixes of host
+        arrays (written into the given ones when provided)."""
+        ids = _host_i64(seq_ids)
+        n = len(ids)
+        if group_offsets is None:
+            group_offsets = np.zeros(n // 2 + 1, np.int32)
+        if group_members is None:
+            group_members = np.zeros(max(n, 1), np.int32)
+        if shared_len is None:
+            shared_len = np.zeros(max(n, 1), np.int32)
+        ng, gmax, smax = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_bm_shared_prefixes(self._h, _ptr(ids) if n else None, n, int(granule), _ptr(group_offsets),
+                                           _ptr(group_members), _ptr(shared_len), ctypes.byref(ng),
+                                           ctypes.byref(gmax), ctypes.byref(smax)))
+        return SharedPrefixes(group_offsets, group_members, shared_len, ng.value, gmax.value, smax.value)
 
     def stats(self) -> dict:
         s = PaBmStats()
@@ -372,4 +406,34 @@ def decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot
                                       int(block_tables.shape[1]), _dev(context_lens, "context_lens"), int(B),
                                       int(Hq), int(max_context_len), float(scale), _dev(workspace, "workspace"),
                                       ws_bytes, _stream(stream)))
+    return out
+
+
+def decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                  max_context_len: int, scale: float, partition_size: int, group_offsets: torch.Tensor,
+                  group_members: torch.Tensor, shared_len: torch.Tensor, num_groups: int, max_group_size: int,
+                  max_shared_len: int, out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode_shared: decode with each group's shared prefix read once
+    for all its rows (group arrays on the device, int32). Returns ``out``."""
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    with torch.cuda.device(q.device):
+        need = decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    for name, t in (("group_offsets", group_offsets), ("group_members", group_members), ("shared_len", shared_len)):
+        if t.dtype != torch.int32:
+            raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, f"{name} must be int32")
+    desc = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _check(lib().pa_decode_shared(ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
+                                      _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
+                                      _dev(context_lens, "context_lens"), int(B), int(Hq), int(max_context_len),
+                                      float(scale), int(partition_size), _dev(group_offsets, "group_offsets"),
+                                      _dev(group_members, "group_members"), _dev(shared_len, "shared_len"),
+                                      int(num_groups), int(max_group_size), int(max_shared_len),
+                                      _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
     return out

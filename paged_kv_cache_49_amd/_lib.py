@@ -83,11 +83,14 @@ SIGNATURES = {
     "pa_bm_stats_get": (c_int, [_P, POINTER(PaBmStats)]),
     "pa_bm_refcounts": (c_int, [_P, _P]),
     "pa_bm_free_stack": (c_int, [_P, _P, c_int32, _I32P]),
+    "pa_bm_shared_prefixes": (c_int, [_P, _P, c_int32, c_int32, _P, _P, _P, _I32P, _I32P, _I32P]),
     "pa_reshape_and_cache": (c_int, [POINTER(PaKvCache), _P, _P, c_int, _P, c_int32, _P]),
     "pa_copy_blocks": (c_int, [POINTER(PaKvCache), _P, c_int32, _P]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode": (c_int, [POINTER(PaKvCache), _P, c_int, _P, c_int, _P, c_int32, _P, c_int32, c_int32,
                           c_int32, c_float, c_int32, _P, c_size_t, _P]),
+    "pa_decode_shared": (c_int, [POINTER(PaKvCache), _P, c_int, _P, c_int, _P, c_int32, _P, c_int32, c_int32,
+                                 c_int32, c_float, c_int32, _P, _P, _P, c_int32, c_int32, c_int32, _P, c_size_t, _P]),
     "pa_decode_append": (c_int, [POINTER(PaKvCache), _P, _P, c_int, _P, _P, c_int, _P, c_int, _P, c_int32, _P,
                                  c_int32, c_int32, c_int32, c_float, _P, c_size_t, _P]),
 }

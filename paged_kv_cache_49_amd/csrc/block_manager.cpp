@@ -16,6 +16,7 @@
 // current state (blocks needed, including copy-on-write copies, checked
 // against the free count), and only then applies it, so a failure leaves
 // the state untouched.
+#include <algorithm>
 #include <climits>
 #include <cstring>
 #include <new>
@@ -258,6 +259,68 @@ pa_status pa_pack_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t 
     if (context_lens) context_lens[i] = it->second.len;
   }
   return PA_OK;
+}
+
+pa_status pa_bm_shared_prefixes(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t granule,
+                                int32_t* group_offsets, int32_t* group_members, int32_t* shared_len,
+                                int32_t* num_groups, int32_t* max_group_size, int32_t* max_shared_len) {
+  pa::clear_error();
+  if (bm == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm is NULL");
+  if (n < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n = %d is negative", n);
+  if (granule <= 0 || granule % bm->block_size != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "granule %d must be a positive multiple of block_size %d", granule,
+                bm->block_size);
+  if (num_groups == nullptr || max_group_size == nullptr || max_shared_len == nullptr || group_offsets == nullptr ||
+      (n > 0 && (seq_ids == nullptr || group_members == nullptr || shared_len == nullptr)))
+    return fail(PA_ERR_INVALID_ARGUMENT, "an output or seq_ids is NULL");
+  PA_GUARD_BEGIN
+  std::vector<const pa_bm::Seq*> seqs(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_ids[i]);
+    seqs[i] = &it->second;
+  }
+  // rows by first physical block, groups in order of first appearance
+  std::unordered_map<int32_t, int32_t> group_of;  // first block -> group index
+  std::vector<std::vector<int32_t>> rows;
+  for (int32_t i = 0; i < n; ++i) {
+    shared_len[i] = 0;
+    if (seqs[i]->blocks.empty()) continue;
+    auto ins = group_of.emplace(seqs[i]->blocks[0], static_cast<int32_t>(rows.size()));
+    if (ins.second) rows.emplace_back();
+    rows[ins.first->second].push_back(i);
+  }
+  int32_t ng = 0, used = 0, gmax = 0, smax = 0;
+  group_offsets[0] = 0;
+  for (const auto& r : rows) {
+    if (r.size() < 2) continue;
+    const auto& b0 = seqs[r[0]]->blocks;
+    size_t lcp = b0.size();
+    int32_t min_len = seqs[r[0]]->len;
+    for (size_t m = 1; m < r.size(); ++m) {
+      const auto& bm_ = seqs[r[m]]->blocks;
+      size_t c = 0;
+      while (c < lcp && c < bm_.size() && bm_[c] == b0[c]) ++c;
+      lcp = c;
+      min_len = std::min(min_len, seqs[r[m]]->len);
+    }
+    // whole granules inside the common blocks, leaving every member a token of its own
+    const int64_t limit = std::min<int64_t>(static_cast<int64_t>(lcp) * bm->block_size, min_len - 1);
+    const int32_t shared = static_cast<int32_t>(limit > 0 ? limit / granule * granule : 0);
+    if (shared == 0) continue;
+    for (int32_t row : r) {
+      group_members[used++] = row;
+      shared_len[row] = shared;
+    }
+    group_offsets[++ng] = used;
+    gmax = std::max<int32_t>(gmax, static_cast<int32_t>(r.size()));
+    smax = std::max(smax, shared);
+  }
+  *num_groups = ng;
+  *max_group_size = gmax;
+  *max_shared_len = smax;
+  return PA_OK;
+  PA_GUARD_END
 }
 
 pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out) {

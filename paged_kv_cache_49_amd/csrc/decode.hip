@@ -12,11 +12,13 @@
 // partitions keep one long sequence from serialising on one workgroup.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <vector>
 
 #include "decode_kernel.h"
+#include "decode_shared_kernel.h"
 #include "decode_sk_kernel.h"
 #include "device_common.h"
 #include "internal.h"
@@ -335,12 +337,21 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_h
 namespace pa {
 namespace {
 
-// pa_decode, and pa_decode_append when k_new != nullptr (validated by it)
+// the group structure of pa_decode_shared
+struct SharedArgs {
+  const int32_t* group_offsets;
+  const int32_t* group_members;
+  const int32_t* shared_len;
+  int32_t num_groups, max_group_size, max_shared_len;
+};
+
+// pa_decode; pa_decode_append when k_new != nullptr and pa_decode_shared
+// when sh != nullptr (their own arguments are validated by them)
 pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
                       const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
                       int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
                       void* workspace, size_t workspace_bytes, void* stream, const void* k_new, const void* v_new,
-                      const int64_t* slot_mapping) {
+                      const int64_t* slot_mapping, const SharedArgs* sh = nullptr) {
   pa_status st = pa::validate_cache(cache);
   if (st != PA_OK) return st;
   if (B < 0) return fail(PA_ERR_INVALID_ARGUMENT, "B = %d is negative", B);
@@ -468,7 +479,26 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
   prm.v_scale = v_scale;
   const int64_t wgs = P * hkv * B;
   if (wgs > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many workgroups (%lld)", (long long)wgs);
-  hipError_t e = launch(prm, dim3(static_cast<uint32_t>(wgs)), s);
+  hipError_t e = hipSuccess;
+  if (sh != nullptr && sh->num_groups > 0 && sh->max_shared_len > 0) {
+    // the shared partitions, once per group (see decode_shared_kernel.h)
+    const pa::GroupLaunch glaunch = pa::find_decode_group(cache->dtype, D, bs, G);
+    if (glaunch == nullptr) return fail(PA_ERR_UNSUPPORTED, "no shared-prefix kernel for these shapes");
+    pa::SharedParams sp{};
+    sp.group_offsets = sh->group_offsets;
+    sp.group_members = sh->group_members;
+    sp.shared_len = sh->shared_len;
+    sp.num_groups = sh->num_groups;
+    sp.row_tiles = (sh->max_group_size * G + 15) / 16;
+    sp.shared_parts = sh->max_shared_len / partition_size;
+    const int64_t units = static_cast<int64_t>(sp.shared_parts) * sh->num_groups * hkv;
+    const int64_t gwgs = (units + 7) / 8 * 8 * sp.row_tiles;
+    if (gwgs > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many shared-prefix workgroups (%lld)", (long long)gwgs);
+    e = glaunch(prm, sp, dim3(static_cast<uint32_t>(gwgs)), s);
+    if (e != hipSuccess) return fail(PA_ERR_DEVICE, "shared-prefix launch: %s", hipGetErrorString(e));
+    prm.shared_len = sh->shared_len;
+  }
+  e = launch(prm, dim3(static_cast<uint32_t>(wgs)), s);
   if (e != hipSuccess) return fail(PA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
   if (P > 1) {
     pa::ReduceParams r{};
@@ -529,6 +559,74 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const vo
   return pa::decode_impl(cache, out, out_dtype, q, q_dtype, block_tables, max_blocks, context_lens, B, num_q_heads,
                          max_context_len, scale, PA_PARTITION_BALANCED, workspace, workspace_bytes, stream, k_new,
                          v_new, slot_mapping);
+}
+
+pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
+                           const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                           int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
+                           const int32_t* group_offsets, const int32_t* group_members, const int32_t* shared_len,
+                           int32_t num_groups, int32_t max_group_size, int32_t max_shared_len, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  pa_status st = pa::validate_cache(cache);
+  if (st != PA_OK) return st;
+  if (cache->v_layout != PA_LAYOUT_DIM_MAJOR)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared needs a pool with dim-major V blocks");
+  if (partition_size <= 0 || partition_size % 16 != 0 || partition_size % cache->block_size != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "partition_size %d must be a positive multiple of 16 and of block_size %d",
+                partition_size, cache->block_size);
+  if (num_groups < 0 || max_group_size < 0 || max_shared_len < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "negative num_groups, max_group_size or max_shared_len");
+  if (max_shared_len % partition_size != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_shared_len %d is not a multiple of partition_size %d", max_shared_len,
+                partition_size);
+  if (max_shared_len >= max_context_len && max_shared_len > 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_shared_len %d must be below max_context_len %d", max_shared_len,
+                max_context_len);
+  if (num_groups > 0 && (group_offsets == nullptr || group_members == nullptr || shared_len == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "group_offsets, group_members or shared_len is NULL");
+  if (num_groups > B || max_group_size > B)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_groups %d / max_group_size %d exceed B = %d", num_groups,
+                max_group_size, B);
+  if (B > 0 && num_groups > 0 && pa::debug_enabled()) {
+    std::vector<int32_t> off(num_groups + 1), lens(B), shl(B), tab(static_cast<size_t>(B) * max_blocks);
+    if (hipMemcpy(off.data(), group_offsets, sizeof(int32_t) * off.size(), hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(lens.data(), context_lens, sizeof(int32_t) * B, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(shl.data(), shared_len, sizeof(int32_t) * B, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(tab.data(), block_tables, sizeof(int32_t) * tab.size(), hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(PA_ERR_DEVICE, "PA_DEBUG: reading the group arrays failed");
+    if (off[0] != 0 || off[num_groups] > B) return fail(PA_ERR_INVALID_ARGUMENT, "group_offsets out of range");
+    std::vector<int32_t> mem(off[num_groups]);
+    if (!mem.empty() && hipMemcpy(mem.data(), group_members, sizeof(int32_t) * mem.size(), hipMemcpyDeviceToHost) !=
+                            hipSuccess)
+      return fail(PA_ERR_DEVICE, "PA_DEBUG: reading group_members failed");
+    std::vector<int> in_group(B, 0);
+    const int32_t bs = cache->block_size;
+    for (int32_t gi = 0; gi < num_groups; ++gi) {
+      if (off[gi + 1] < off[gi] || off[gi + 1] - off[gi] > max_group_size)
+        return fail(PA_ERR_INVALID_ARGUMENT, "group %d: bad offsets or larger than max_group_size", gi);
+      if (off[gi + 1] == off[gi]) continue;
+      const int32_t first = mem[off[gi]];
+      for (int32_t m = off[gi]; m < off[gi + 1]; ++m) {
+        const int32_t sq = mem[m];
+        if (sq < 0 || sq >= B || in_group[sq]++)
+          return fail(PA_ERR_INVALID_ARGUMENT, "group %d: member %d out of range or in two groups", gi, sq);
+        if (shl[sq] != shl[first] || shl[sq] % partition_size != 0 || shl[sq] > max_shared_len ||
+            shl[sq] >= std::min(lens[sq], max_context_len))
+          return fail(PA_ERR_INVALID_ARGUMENT, "group %d: shared_len of row %d is inconsistent", gi, sq);
+        for (int32_t b = 0; b < shl[sq] / bs; ++b)
+          if (tab[static_cast<size_t>(sq) * max_blocks + b] != tab[static_cast<size_t>(first) * max_blocks + b])
+            return fail(PA_ERR_INVALID_ARGUMENT, "group %d: rows %d and %d differ at table entry %d", gi, sq, first, b);
+      }
+    }
+    for (int32_t i = 0; i < B; ++i)
+      if (!in_group[i] && shl[i] != 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "row %d is in no group but has shared_len %d", i, shl[i]);
+  }
+  pa::SharedArgs sh{group_offsets, group_members, shared_len, num_groups, max_group_size, max_shared_len};
+  return pa::decode_impl(cache, out, out_dtype, q, q_dtype, block_tables, max_blocks, context_lens, B, num_q_heads,
+                         max_context_len, scale, partition_size, workspace, workspace_bytes, stream, nullptr, nullptr,
+                         nullptr, num_groups > 0 ? &sh : nullptr);
 }
 
 }  // extern "C"

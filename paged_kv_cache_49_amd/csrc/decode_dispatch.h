@@ -27,6 +27,22 @@ DecodeLaunch find_decode_vt_fp8(int head_dim, int block_size, int group);
 
 // append: the variant that also writes each sequence's newest token
 // (pa_decode_append; 16-bit pools only, nullptr otherwise)
+// shared-prefix group kernels (dim-major V)
+struct SharedParams;
+using GroupLaunch = hipError_t (*)(const DecodeParams&, const SharedParams&, dim3 grid, hipStream_t stream);
+GroupLaunch find_decode_group_f16(int head_dim, int block_size, int group);
+GroupLaunch find_decode_group_bf16(int head_dim, int block_size, int group);
+GroupLaunch find_decode_group_fp8(int head_dim, int block_size, int group);
+
+inline GroupLaunch find_decode_group(pa_dtype pool, int head_dim, int block_size, int group) {
+  switch (pool) {
+    case PA_F16: return find_decode_group_f16(head_dim, block_size, group);
+    case PA_BF16: return find_decode_group_bf16(head_dim, block_size, group);
+    case PA_FP8_E4M3: return find_decode_group_fp8(head_dim, block_size, group);
+    default: return nullptr;
+  }
+}
+
 SkLaunch find_decode_sk_f16(int head_dim, int block_size, int group, bool append);
 SkLaunch find_decode_sk_bf16(int head_dim, int block_size, int group, bool append);
 SkLaunch find_decode_sk_fp8(int head_dim, int block_size, int group, bool append);

@@ -70,6 +70,9 @@ struct DecodeParams {
   int32_t out_dtype;       // 0 f16, 1 bf16, 2 f32
   float qk_scale_log2;     // scale * k_scale * log2(e)
   float v_scale;           // 1 for 16-bit pools
+  // pa_decode_shared: tokens at the start of each sequence computed per
+  // group (partitions below it are skipped here); nullptr otherwise
+  const int32_t* shared_len;
 };
 
 template <typename KV, int D, int BS, int G>

@@ -1,0 +1,161 @@
+// Decode over shared prefixes: the blocks a group of sequences shares are
+// read once for all of the group's query rows.
+//
+// [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
+// [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
+// [course] §2 "The bonus" and §3: forked sequences (parallel sampling, beam
+// search) share the prompt's physical blocks through their block tables;
+// [note] prefix-sharing section: sequences with a common prefix point at the
+// same blocks. The attention of each sequence is unchanged (it is still
+// softmax attention over its own tokens in logical order); what changes is
+// how often the shared blocks are read: with the prefix split into
+// partitions, one pass over a shared partition serves every member of the
+// group, because its K/V rows are the same for all of them.
+//
+// pa_decode_shared runs three kernels on the caller's stream:
+//  1. paged_decode_group_kernel: one wave per (shared partition, group, KV
+//     head, row tile). Its 16 q rows are (member, query head) pairs of the
+//     group: row r = member rt * (16 / G) + r / G, head r % G. The partition's
+//     K/V tiles come through the first member's table (the shared entries
+//     are identical in every member's table). Per-row results are written as
+//     partition partials (m, l, o) of each member.
+//  2. paged_decode_vt_kernel with shared_len: the partitions past each
+//     sequence's shared prefix, per sequence as usual.
+//  3. decode_reduce_kernel: the log-sum-exp merge of all partitions.
+// The row tiles of one (partition, group, KV head) are placed on the same
+// XCD, next to each other in dispatch order (workgroups are dealt to the 8
+// XCDs round-robin), so the K/V they all read is fetched from HBM once and
+// served from that XCD's L2 to the others.
+#pragma once
+
+#include "decode_vt_kernel.h"
+
+namespace pa {
+
+struct SharedParams {
+  const int32_t* group_offsets;  // [num_groups + 1] into group_members
+  const int32_t* group_members;  // batch rows of each group's sequences
+  const int32_t* shared_len;     // [B] tokens of the sequence's shared prefix (a multiple of partition_size)
+  int32_t num_groups;
+  int32_t row_tiles;     // ceil(max_group_size * G / 16)
+  int32_t shared_parts;  // max shared_len / partition_size
+};
+
+template <typename KV, typename QT, int D, int BS, int G>
+__global__ __launch_bounds__(64) void paged_decode_group_kernel(const DecodeParams p, const SharedParams sp) {
+  using C = DecodeCfg<KV, D, BS, G>;
+  constexpr int kB = C::kB;
+  constexpr int kNT = D / 16;
+  constexpr int kMembersPerTile = 16 / G;
+  __shared__ float s_out[16 * D];
+
+  // workgroup -> (unit, row tile): unit u's row tiles are workgroups
+  // ((u / 8) * RT + rt) * 8 + u % 8, all on XCD u % 8
+  const int wg = static_cast<int>(blockIdx.x);
+  const int k = wg >> 3;
+  const int rt = k % sp.row_tiles;
+  const int64_t u = static_cast<int64_t>(k / sp.row_tiles) * 8 + (wg & 7);
+  const int Hkv = p.num_kv_heads;
+  if (u >= static_cast<int64_t>(sp.shared_parts) * sp.num_groups * Hkv) return;
+  const int g = static_cast<int>(u % Hkv);
+  const int rest = static_cast<int>(u / Hkv);
+  const int gi = rest % sp.num_groups;
+  const int part = rest / sp.num_groups;
+  const int m0 = sp.group_offsets[gi];
+  const int gsize = sp.group_offsets[gi + 1] - m0;
+  if (gsize <= 0 || rt * kMembersPerTile >= gsize) return;
+  const int first = sp.group_members[m0];
+  const int ps = p.partition_size;
+  const int tok_begin = part * ps;
+  if (tok_begin + ps > sp.shared_len[first]) return;  // past this group's shared prefix
+
+  const int lane = threadIdx.x;
+  const int col = lane & 15, j = lane >> 4;
+  const int32_t* bt = p.block_tables + static_cast<int64_t>(first) * p.max_blocks;
+  const int blk_first = tok_begin / BS;
+  const int id_first = blk_first + lane < p.max_blocks ? bt[blk_first + lane] : 0;
+  int L = p.context_lens[first];
+  L = L < p.len_cap ? L : p.len_cap;
+
+  // this lane's q row: member rt * kMembersPerTile + col / G, head col % G
+  const int mi = rt * kMembersPerTile + col / G;
+  const bool row_ok = mi < gsize;
+  const int seq_r = row_ok ? sp.group_members[m0 + mi] : first;
+  u32x4 qb[C::kKSteps];
+  {
+    const int64_t head = static_cast<int64_t>(seq_r) * p.num_q_heads + static_cast<int64_t>(g) * G + col % G;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + head * D;
+#pragma unroll
+    for (int i = 0; i < C::kKSteps; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
+      qb[i] = row_ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  float m_w = -INFINITY;
+  float l_w = 0.f;
+  f32x4 acc[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  vt_attend<KV, QT, D, BS, G>(p, bt, g, L, tok_begin, tok_begin + ps, id_first, qb, row_ok, m_w, l_w, acc);
+
+  // rows of this tile that belong to members: a prefix of the 16
+  const int nrows = min(16, (gsize - rt * kMembersPerTile) * G);
+  const float l_head = vt_normalise<D>(acc, l_w, p.v_scale, nrows, s_out);
+  // the member (batch row) of each of the lane's output rows
+  for (int i = lane * 8; i < nrows * D; i += 64 * 8) {
+    const int r = i / D, d = i % D;
+    const int seq = sp.group_members[m0 + rt * kMembersPerTile + r / G];
+    const int64_t pi = ((static_cast<int64_t>(seq) * p.num_q_heads + static_cast<int64_t>(g) * G + r % G) *
+                        p.num_partitions) + part;
+    float* po = p.part_o + pi * D + d;
+    *reinterpret_cast<f32x4*>(po) = f32x4{s_out[i], s_out[i + 1], s_out[i + 2], s_out[i + 3]};
+    *reinterpret_cast<f32x4*>(po + 4) = f32x4{s_out[i + 4], s_out[i + 5], s_out[i + 6], s_out[i + 7]};
+  }
+  if (lane < nrows) {
+    const int64_t pi = ((static_cast<int64_t>(seq_r) * p.num_q_heads + static_cast<int64_t>(g) * G + lane % G) *
+                        p.num_partitions) + part;
+    p.part_m[pi] = m_w;
+    p.part_l[pi] = l_head;
+  }
+}
+
+using GroupLaunch = hipError_t (*)(const DecodeParams&, const SharedParams&, dim3 grid, hipStream_t stream);
+
+template <typename KV, typename QT, int D, int BS, int G>
+hipError_t launch_decode_group(const DecodeParams& p, const SharedParams& sp, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_decode_group_kernel<KV, QT, D, BS, G>), grid, dim3(64), 0, stream, p, sp);
+  return hipGetLastError();
+}
+
+template <typename KV, typename QT, int D, int BS>
+GroupLaunch select_decode_group_g(int G) {
+  switch (G) {
+    case 1: return &launch_decode_group<KV, QT, D, BS, 1>;
+    case 2: return &launch_decode_group<KV, QT, D, BS, 2>;
+    case 4: return &launch_decode_group<KV, QT, D, BS, 4>;
+    case 8: return &launch_decode_group<KV, QT, D, BS, 8>;
+    default: return nullptr;
+  }
+}
+
+template <typename KV, typename QT, int D>
+GroupLaunch select_decode_group_bs(int BS, int G) {
+  switch (BS) {
+    case 8: return select_decode_group_g<KV, QT, D, 8>(G);
+    case 16: return select_decode_group_g<KV, QT, D, 16>(G);
+    case 32: return select_decode_group_g<KV, QT, D, 32>(G);
+    default: return nullptr;
+  }
+}
+
+template <typename KV, typename QT>
+GroupLaunch select_decode_group(int D, int BS, int G) {
+  switch (D) {
+    case 64: return select_decode_group_bs<KV, QT, 64>(BS, G);
+    case 128: return select_decode_group_bs<KV, QT, 128>(BS, G);
+    default: return nullptr;
+  }
+}
+
+}  // namespace pa

@@ -73,51 +73,42 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
   return f16_hi(w);
 }
 
+// Attention of one wave's 16 q rows over tokens [tok_begin, tok_end) of a
+// sequence with block table row `bt` and clamped length L (table entries
+// past ceil(L / BS) are never read), KV head g. qb holds the q rows as the
+// B operand of S^T = K q^T; lane row `col` takes part iff row_ok. id_first
+// = table entry (tok_begin / BS + lane), loaded by the caller ahead of time.
+// Leaves, per lane: m_w = running reference max of row `col` (log2 domain),
+// l_w = this lane's share of that row's weight sum, acc = the unnormalised
+// output tile (rows = q rows).
+//
+// Per 16-token tile:
+//  * S^T = K q^T with v_mfma_f32_16x16x32 (A = the tile's K rows, one token
+//    per lane row, 8 head dims per lane). Lane (r = lane % 16, j = lane / 16)
+//    ends up holding the logits of row r for tokens 4j..4j+3 of the tile.
+//  * online softmax per row: the tile max is a 4-register max and two
+//    cross-row lane exchanges; the running max moves only past a 2^8 slack.
+//  * the weights are already in the A-operand layout of v_mfma_f32_16x16x16
+//    (row = q row, k = 4 tokens per lane), so PV needs no data movement:
+//    each weight is split into a high and a low 16-bit part (hi + lo carries
+//    ~16 mantissa bits) and both are multiplied against V.
+//  * V: dim-major blocks give each lane the 4 consecutive tokens of one head
+//    dimension as one 8-byte load (a 16-dim tile of a 16-token block is 512
+//    contiguous bytes), which is exactly the B operand (k = tokens, n = dim).
+//  * loads are staggered over single buffers: K(t+1) is requested right
+//    after QK(t) has consumed K(t), and V(t+1) right after PV(t) has
+//    consumed V(t); loads complete in order, so QK(t+1) waits only for
+//    K(t+1) while V(t+1) is still in flight, and vice versa.
 template <typename KV, typename QT, int D, int BS, int G>
-__global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams p) {
+__device__ __forceinline__ void vt_attend(const DecodeParams& p, const int32_t* bt, int g, int L, int tok_begin,
+                                          int tok_end, int id_first, const u32x4 (&qb)[D / 32], bool row_ok,
+                                          float& m_w, float& l_w, f32x4 (&acc)[D / 16]) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
-  constexpr int kNT = D / 16;  // 16-dim output tiles
-  static_assert(G <= 16, "at most 16 query heads per KV head");
+  constexpr int kNT = D / 16;
   using VRaw = typename VVecT<KV>::raw_dm;
-  __shared__ float s_out[G * D];
-
-  const int pairs = static_cast<int>(gridDim.x) / p.num_partitions;  // B * Hkv
-  const int part = static_cast<int>(blockIdx.x) / pairs;
-  const int pr = static_cast<int>(blockIdx.x) - part * pairs;
-  const int s = pr / p.num_kv_heads;
-  const int g = pr - s * p.num_kv_heads;
-  const int lane = threadIdx.x;
-  const int32_t* bt = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
-  const int blk_first = p.partition_size > 0 ? part * p.partition_size / BS : 0;
-  const int id_first = blk_first + lane < p.max_blocks ? bt[blk_first + lane] : 0;
-
-  int L = p.context_lens[s];
-  L = L < p.len_cap ? L : p.len_cap;
-  L = L > 0 ? L : 0;
-  const int ps = p.partition_size > 0 ? p.partition_size : (L > 0 ? L : 1);
-  const int nparts = (L + ps - 1) / ps;
-  if (part >= (nparts > 0 ? nparts : 1)) return;
-  const int64_t head0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(g) * G;
-  if (L == 0) {
-    for (int i = lane; i < G * D; i += 64) store_out(p.out, head0 * D + i, p.out_dtype, 0.f);
-    return;
-  }
-  const int tok_begin = part * ps;
-  const int tok_end = min(L, tok_begin + ps);
+  const int lane = threadIdx.x & 63;
   const int col = lane & 15, j = lane >> 4;
-
-  // q rows as the B operand of S^T = K q^T (columns >= G are zero)
-  u32x4 qb[C::kKSteps];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
-#pragma unroll
-    for (int i = 0; i < C::kKSteps; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
-      qb[i] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
   const char* kbase = static_cast<const char*>(p.k_pool);
   const char* vbase = static_cast<const char*>(p.v_pool);
   const int64_t blk_bytes = p.block_stride * kB;
@@ -130,12 +121,6 @@ __global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams 
   const uint32_t koff_lane = static_cast<uint32_t>(col * tok_bytes + khead_bytes + qk_dim<kB>(0, j) * kB);
   constexpr int kVTileBytes = 16 * BS * kB;  // one 16-dim n-tile of a block
   const int nvalid_blk = (L + BS - 1) / BS;
-
-  float m_w = -INFINITY;  // running reference max of head `col` (log2 domain)
-  float l_w = 0.f;        // this lane's share of head `col`'s weight sum
-  f32x4 acc[kNT];
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int c0 = tok_begin; c0 < tok_end; c0 += C::kChunk) {
     const int n = min(C::kChunk, tok_end - c0);
@@ -221,7 +206,7 @@ __global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams 
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const bool need = col < G && mx > m_w + C::kSlack;
+      const bool need = row_ok && mx > m_w + C::kSlack;
       if (__builtin_amdgcn_ballot_w64(need)) {
         const float a = need ? __builtin_amdgcn_exp2f(m_w - mx) : 1.0f;
         m_w = need ? mx : m_w;
@@ -236,7 +221,7 @@ __global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams 
       float pw[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pw[r] = col < G ? __builtin_amdgcn_exp2f(sv[r] - m_w) : 0.f;
+        pw[r] = row_ok ? __builtin_amdgcn_exp2f(sv[r] - m_w) : 0.f;
         l_w += pw[r];
       }
       const uint32_t h0 = pack2<QT>(pw[0], pw[1]), h1 = pack2<QT>(pw[2], pw[3]);
@@ -268,20 +253,88 @@ __global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams 
     }
   }
 
-  // ---- epilogue: weight sums per head, then acc / l through LDS for wide stores
+}
+
+// Row sums and normalised rows of a finished vt_attend, in LDS: s_out[r][D]
+// for every row r < nrows (rows = q rows of the wave, LDS owned by the
+// wave). Returns in lane r (r < 16) the weight sum of row r.
+template <int D>
+__device__ __forceinline__ float vt_normalise(const f32x4 (&acc)[D / 16], float l_w, float v_scale, int nrows,
+                                              float* s_out) {
+  constexpr int kNT = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, j = lane >> 4;
   float l_head = l_w + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_w), 0x401F));
   l_head += __shfl_xor(l_head, 32, 64);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * j + r;
-    const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
-    if (h < G) {
-      const float inv = p.v_scale / lr;
+    const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds row h's sum
+    if (h < nrows) {
+      const float inv = v_scale / lr;
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) s_out[h * D + nt * 16 + col] = acc[nt][r] * inv;
     }
   }
   wave_lds_sync();
+  return l_head;
+}
+
+template <typename KV, typename QT, int D, int BS, int G>
+__global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams p) {
+  using C = DecodeCfg<KV, D, BS, G>;
+  constexpr int kB = C::kB;
+  constexpr int kNT = D / 16;  // 16-dim output tiles
+  static_assert(G <= 16, "at most 16 query heads per KV head");
+  __shared__ float s_out[G * D];
+
+  const int pairs = static_cast<int>(gridDim.x) / p.num_partitions;  // B * Hkv
+  const int part = static_cast<int>(blockIdx.x) / pairs;
+  const int pr = static_cast<int>(blockIdx.x) - part * pairs;
+  const int s = pr / p.num_kv_heads;
+  const int g = pr - s * p.num_kv_heads;
+  const int lane = threadIdx.x;
+  const int32_t* bt = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
+  const int blk_first = p.partition_size > 0 ? part * p.partition_size / BS : 0;
+  const int id_first = blk_first + lane < p.max_blocks ? bt[blk_first + lane] : 0;
+
+  int L = p.context_lens[s];
+  L = L < p.len_cap ? L : p.len_cap;
+  L = L > 0 ? L : 0;
+  const int ps = p.partition_size > 0 ? p.partition_size : (L > 0 ? L : 1);
+  const int nparts = (L + ps - 1) / ps;
+  if (part >= (nparts > 0 ? nparts : 1)) return;
+  // partitions of a shared prefix are computed once per group (pa_decode_shared)
+  if (p.shared_len != nullptr && part * ps < p.shared_len[s]) return;
+  const int64_t head0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(g) * G;
+  if (L == 0) {
+    for (int i = lane; i < G * D; i += 64) store_out(p.out, head0 * D + i, p.out_dtype, 0.f);
+    return;
+  }
+  const int tok_begin = part * ps;
+  const int tok_end = min(L, tok_begin + ps);
+  const int col = lane & 15, j = lane >> 4;
+
+  // q rows as the B operand of S^T = K q^T (columns >= G are zero)
+  u32x4 qb[C::kKSteps];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
+#pragma unroll
+    for (int i = 0; i < C::kKSteps; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
+      qb[i] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  float m_w = -INFINITY;
+  float l_w = 0.f;
+  f32x4 acc[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  vt_attend<KV, QT, D, BS, G>(p, bt, g, L, tok_begin, tok_end, id_first, qb, col < G, m_w, l_w, acc);
+
+  // ---- epilogue: normalised rows through LDS for wide stores
+  const float l_head = vt_normalise<D>(acc, l_w, p.v_scale, G, s_out);
   for (int i = lane * 8; i < G * D; i += 64 * 8) {
     float o[8];
 #pragma unroll

@@ -1,0 +1,170 @@
+"""pa_decode_shared on the GPU: each group's shared prefix read once for all
+its rows, against the fp64 oracle and against pa_decode.
+
+Batches are built the way parallel sampling builds them: a prompt is
+prefilled, forked into its samples (shared blocks, refcounts), each sample
+appends tokens of its own (copy-on-write of a partial shared tail block),
+then the groups come from pa_bm_shared_prefixes. Group sizes cover one row
+tile and several (more members than 16 / G), groups of one member (left
+out) and rows without a prompt of their own sharing anything."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_49_amd as pa
+import synth
+from oracle import attention as oatt
+from tests import helpers as H
+from tests.gpu_util import poison_fill, say
+
+pytestmark = pytest.mark.gpu
+
+_T = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _values(rng, shape, kv):
+    return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(_T[kv])
+
+
+def _build(seed, prompts, samples, tail_max, G, hkv, D, bs, kv):
+    """Prefill prompts, fork samples, append tails; returns everything a
+    decode call and the oracle need."""
+    rng = np.random.default_rng(seed)
+    seqs = []  # (prompt, k, v) per batch row, full token-ordered K/V
+    for p, (plen, ns) in enumerate(zip(prompts, samples)):
+        kp, vp = _values(rng, (plen, hkv, D), kv), _values(rng, (plen, hkv, D), kv)
+        for i in range(ns):
+            t = int(rng.integers(1, tail_max + 1))
+            kt, vt = _values(rng, (t, hkv, D), kv), _values(rng, (t, hkv, D), kv)
+            seqs.append((p, kp, vp, kt, vt))
+    B = len(seqs)
+    total = sum(len(x[1]) + len(x[3]) for x in seqs)
+    nb = total // bs + 4 * B + 16
+    bm = pa.BlockManager(nb, bs, np.random.default_rng(seed + 1).permutation(nb).astype(np.int32))
+    cache = pa.KVCache.allocate(nb, bs, hkv, D, kv, fill=poison_fill(kv), v_layout="dim")
+    first_row = {}
+    for row, (p, kp, vp, kt, vt) in enumerate(seqs):
+        if p in first_row:
+            bm.fork(first_row[p], row)
+        else:
+            first_row[p] = row
+            sl, _ = bm.alloc(row, len(kp))
+            pa.reshape_and_cache(cache, kp.cuda(), vp.cuda(), torch.from_numpy(sl).cuda())
+    cows = []
+    for row, (p, kp, vp, kt, vt) in enumerate(seqs):
+        sl, cow = bm.alloc(row, len(kt))
+        if cow:
+            pa.copy_blocks(cache, torch.tensor(cow, dtype=torch.int32).cuda())
+            cows += cow
+        pa.reshape_and_cache(cache, kt.cuda(), vt.cuda(), torch.from_numpy(sl).cuda())
+    mb = max(-(-(len(x[1]) + len(x[3])) // bs) for x in seqs)
+    tables, lens = bm.pack(list(range(B)), mb, -1)
+    q = _values(rng, (B, G * hkv, D), kv)
+    return bm, cache, seqs, tables, lens, q, mb
+
+
+def _oracle(seqs, q, hkv, scale):
+    qd = oatt.to_f64(q)
+    out = np.zeros(qd.shape)
+    for row, (p, kp, vp, kt, vt) in enumerate(seqs):
+        k = oatt.to_f64(torch.cat([kp, kt]))
+        v = oatt.to_f64(torch.cat([vp, vt]))
+        out[row] = oatt.decode_contiguous(qd[row], k, v, scale, hkv)
+    return out
+
+
+def _run(seed, prompts, samples, tail_max, G, hkv, D, bs, kv, ps, what=""):
+    say(f"shared {what}: prompts {prompts} x {samples} G={G} Hkv={hkv} D={D} bs={bs} {kv} ps={ps}")
+    bm, cache, seqs, tables, lens, q, mb = _build(seed, prompts, samples, tail_max, G, hkv, D, bs, kv)
+    B = len(seqs)
+    sp = bm.shared_prefixes(list(range(B)), ps)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    max_ctx = int(lens.max())
+    td, ld, qd = dev(tables), dev(lens), q.cuda()
+    got = pa.decode_shared(cache, qd, td, ld, max_ctx, scale, ps, dev(sp.offsets), dev(sp.members),
+                           dev(sp.shared_len), sp.num_groups, sp.max_group_size, sp.max_shared_len,
+                           out_dtype=torch.float32)
+    plain = pa.decode(cache, qd, td, ld, max_ctx, scale, ps, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = _oracle(seqs, q, hkv, scale)
+    g = got.cpu().double().numpy()
+    ma, rl = H.assert_close(g, ref, what=f"shared {what}")
+    H.assert_close(g, plain.cpu().double().numpy(), what=f"shared vs pa_decode {what}")
+    say(f"   groups {sp.num_groups} (max {sp.max_group_size} rows, {sp.max_shared_len} shared tokens); "
+        f"max-abs {ma:.2e} rel-L2 {rl:.2e}")
+    return sp
+
+
+CASES = [
+    ("bf16", 128, 16, 4, 8, 512),
+    ("bf16", 128, 16, 4, 8, 256),
+    ("bf16", 64, 8, 8, 2, 256),
+    ("f16", 128, 32, 1, 4, 512),
+    ("f16", 64, 16, 2, 3, 128),
+]
+
+
+@pytest.mark.parametrize("kv,D,bs,G,hkv,ps", CASES, ids=lambda c: str(c))
+def test_shared_parity(gpu, kv, D, bs, G, hkv, ps):
+    # prompt lengths: several partitions, under one partition, and one with a
+    # partial last block; 1-member group, 17-member group (> 16 / G rows)
+    sp = _run(4000 + D + bs + G, [1100, 700, 2000, 90, 1301], [3, 1, 17, 4, 5], 80, G, hkv, D, bs, kv, ps,
+              what=f"{kv} D{D} bs{bs} G{G}")
+    assert sp.num_groups >= 2
+
+
+def test_shared_prefix_sharing_workload(gpu):
+    """The 16 prompts x 8 samples workload (2048 + r shared tokens, tails
+    U[0, 256], one new token), partitions of 512, all rows vs the oracle."""
+    wl = synth.prefix_sharing(partial_tail=True)
+    P, S, hkv, D, bs = wl.prompts, wl.samples, wl.num_kv_heads, wl.head_dim, wl.block_size
+    say("shared: prefix-sharing workload")
+    bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
+    cache = pa.KVCache.allocate(wl.num_blocks, bs, hkv, D, "bf16", fill=float("nan"), v_layout="dim")
+    for p in range(P):
+        k, v = wl.prefix_kv(p)
+        sl, _ = bm.alloc(p * S, len(k))
+        pa.reshape_and_cache(cache, k.cuda(), v.cuda(), torch.from_numpy(sl).cuda())
+        for i in range(1, S):
+            bm.fork(p * S, p * S + i)
+    for p in range(P):
+        for i in range(S):
+            kt, vt = wl.tail_kv(p, i)
+            sl, cow = bm.alloc(p * S + i, len(kt))
+            if cow:
+                pa.copy_blocks(cache, torch.tensor(cow, dtype=torch.int32).cuda())
+            pa.reshape_and_cache(cache, kt.cuda(), vt.cuda(), torch.from_numpy(sl).cuda())
+    B = P * S
+    mb = int(-(-(int(wl.prefix_len.max() + wl.tail_len.max()) + 2) // bs))
+    tables, lens = bm.pack(list(range(B)), mb, -1)
+    sp = bm.shared_prefixes(list(range(B)), 512)
+    assert sp.num_groups == P and sp.max_group_size == S and sp.max_shared_len == 2048
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+    q = wl.q().cuda()
+    got = pa.decode_shared(cache, q, dev(tables), dev(lens), int(lens.max()), wl.scale, 512, dev(sp.offsets),
+                           dev(sp.members), dev(sp.shared_len), sp.num_groups, sp.max_group_size, sp.max_shared_len,
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qd = oatt.to_f64(wl.q())
+    ref = np.zeros(qd.shape)
+    for p in range(P):
+        k, v = wl.prefix_kv(p)
+        for i in range(S):
+            kt, vt = wl.tail_kv(p, i)
+            ref[p * S + i] = oatt.decode_contiguous(qd[p * S + i], oatt.to_f64(torch.cat([k, kt])),
+                                                    oatt.to_f64(torch.cat([v, vt])), wl.scale, hkv)
+    ma, rl = H.assert_close(got.cpu().double().numpy(), ref, what="prefix-sharing workload")
+    say(f"   max-abs {ma:.2e} rel-L2 {rl:.2e}")
+
+
+def test_no_groups_is_plain_decode(gpu):
+    """With no group (num_groups = 0) the call is pa_decode."""
+    wl = synth.random_case(4100, [300, 1200, 5], 16, 4, 128, 16, "bf16")
+    from tests.gpu_util import device_setup, run_decode
+    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout="dim")
+    z = torch.zeros(wl.batch + 1, dtype=torch.int32, device="cuda")
+    got = pa.decode_shared(cache, wl.q().cuda(), tables, lens, max_ctx, wl.scale, 256, z, z, z, 0, 0, 0,
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    H.assert_close(got.cpu().double().numpy(), H.oracle_contiguous(wl), what="no groups")
