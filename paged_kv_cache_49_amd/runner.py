@@ -13,7 +13,9 @@ and runs the serving loop's steps through the C ABI:
                        pa_copy_blocks -> pa_reshape_and_cache -> pa_decode,
                        or with ``fused=True`` pa_copy_blocks ->
                        pa_decode_append (the write and the attention in one
-                       launch; balanced split, 16-bit pools)
+                       launch; balanced split, 16-bit pools), or with
+                       ``shared=True`` ... -> pa_decode_shared (each group
+                       of forks reads its shared prefix once)
 
 The metadata staging area is double-buffered: a buffer is refilled only
 after the copy issued from it two steps earlier has completed (HIP event),
@@ -30,29 +32,39 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (BALANCED, BlockManager, KVCache, copy_blocks, decode, decode_append, decode_workspace_size,
-               reshape_and_cache)
+from . import (BALANCED, BlockManager, KVCache, copy_blocks, decode, decode_append, decode_shared,
+               decode_workspace_size, reshape_and_cache)
 
 
 class _Staging:
     """Pinned host buffer + device buffer with the step metadata layout:
-    slots int64[B] | cow int32[B][2] | lens int32[B] | tables int32[B][W]."""
+    slots int64[B] | cow int32[B][2] | lens int32[B] | tables int32[B][W] |
+    shared-prefix groups: offsets int32[B/2+1] | members int32[B] |
+    shared_len int32[B]."""
 
     def __init__(self, batch: int, max_blocks: int, device):
         self.B, self.W = batch, max_blocks
-        n32 = 2 * batch + 2 * batch + batch + batch * max_blocks
+        ng = batch // 2 + 1
+        n32 = 2 * batch + 2 * batch + batch + batch * max_blocks + ng + 2 * batch
         self.host = torch.empty(n32, dtype=torch.int32, pin_memory=True)
         self.dev = torch.empty(n32, dtype=torch.int32, device=device)
         h = self.host.numpy()
         self.slots_np = h[: 2 * batch].view(np.int64)
         self.cow_np = h[2 * batch: 4 * batch].reshape(batch, 2)
         self.lens_np = h[4 * batch: 5 * batch]
-        self.tables_np = h[5 * batch:].reshape(batch, max_blocks)
+        t_end = 5 * batch + batch * max_blocks
+        self.tables_np = h[5 * batch:t_end].reshape(batch, max_blocks)
+        self.goff_np = h[t_end:t_end + ng]
+        self.gmem_np = h[t_end + ng:t_end + ng + batch]
+        self.shl_np = h[t_end + ng + batch:t_end + ng + 2 * batch]
         d = self.dev
         self.slots = d[: 2 * batch].view(torch.int64)
         self.cow = d[2 * batch: 4 * batch].view(batch, 2)
         self.lens = d[4 * batch: 5 * batch]
-        self.tables = d[5 * batch:].view(batch, max_blocks)
+        self.tables = d[5 * batch:t_end].view(batch, max_blocks)
+        self.goff = d[t_end:t_end + ng]
+        self.gmem = d[t_end + ng:t_end + ng + batch]
+        self.shl = d[t_end + ng + batch:t_end + ng + 2 * batch]
         self.copied: Optional[torch.cuda.Event] = None    # after the upload into `dev`
         self.consumed: Optional[torch.cuda.Event] = None  # after the last kernel that read `dev`
 
@@ -100,14 +112,19 @@ class PagedBatch:
              q: Sequence[torch.Tensor], outs: Sequence[torch.Tensor], scale: float, partition_size: int,
              workspace: Optional[torch.Tensor] = None, ones: Optional[np.ndarray] = None,
              decode_events: Optional[list] = None, event_layers: Optional[Sequence[int]] = None,
-             make_event=None, fused: bool = False) -> int:
+             make_event=None, fused: bool = False, shared: bool = False) -> int:
         """Append one token to each of ``seq_ids`` in every layer and run
         decode attention for it. Returns the batch's max context length.
         With ``decode_events`` (a list), a (start, end) pair of HIP events
         recorded around the pa_decode call of each layer in
         ``event_layers`` (default: every layer) is appended to it; the events
         come from ``make_event()`` (default: torch timing events), which must
-        return objects with ``record()`` on the current stream."""
+        return objects with ``record()`` on the current stream.
+
+        ``shared=True``: the rows whose tables start with the same blocks
+        (forks of one prompt) are grouped (pa_bm_shared_prefixes, granule =
+        ``partition_size``) and decoded with pa_decode_shared, which reads
+        each group's shared partitions once."""
         st = self._stage[self._turn]
         self._turn ^= 1
         if st.copied is not None:
@@ -119,6 +136,12 @@ class PagedBatch:
         ncow = len(cows)
         self.bm.pack(seq_ids, self.max_blocks, self.pad, tables=st.tables_np, context_lens=st.lens_np)
         max_ctx = int(st.lens_np[:B].max(initial=0))
+        groups = None
+        if shared:
+            if fused or partition_size <= 0:
+                raise ValueError("shared steps need partition_size > 0 and fused=False")
+            groups = self.bm.shared_prefixes(seq_ids, partition_size, group_offsets=st.goff_np,
+                                             group_members=st.gmem_np, shared_len=st.shl_np)
         compute = torch.cuda.current_stream(self.device)
         if st.copied is None:
             st.copied, st.consumed = torch.cuda.Event(), torch.cuda.Event()
@@ -150,6 +173,10 @@ class PagedBatch:
                     raise ValueError("fused steps use the balanced split (partition_size = BALANCED)")
                 decode_append(c, k_new[i], v_new[i], st.slots[:B], q[i], tables, lens, max_ctx, scale, out=outs[i],
                               workspace=workspace)
+            elif groups is not None:
+                decode_shared(c, q[i], tables, lens, max_ctx, scale, partition_size, st.goff, st.gmem[:B],
+                              st.shl[:B], groups.num_groups, groups.max_group_size, groups.max_shared_len,
+                              out=outs[i], workspace=workspace)
             else:
                 decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i], workspace=workspace)
             if timed:
