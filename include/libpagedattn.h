@@ -350,7 +350,8 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const vo
  * partition_size, below context_lens[s], and the members' tables identical
  * over those tokens' blocks; 0 for rows in no group. max_group_size >= the
  * largest group, max_shared_len >= every shared_len (and < max_context_len)
- * size the launch. PA_DEBUG=1 checks all of this; otherwise a violation
+ * and min_shared_len <= every shared_len (multiples of partition_size; 0
+ * when some row is in no group) size the launch. PA_DEBUG=1 checks all of this; otherwise a violation
  * gives wrong results for the rows involved (no out-of-bounds access).
  *
  * partition_size: a positive multiple of 16 and of block_size; the
@@ -361,8 +362,8 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dty
                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
                            int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
                            const int32_t* group_offsets, const int32_t* group_members, const int32_t* shared_len,
-                           int32_t num_groups, int32_t max_group_size, int32_t max_shared_len, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           int32_t num_groups, int32_t max_group_size, int32_t max_shared_len,
+                           int32_t min_shared_len, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

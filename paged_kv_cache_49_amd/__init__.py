@@ -140,6 +140,7 @@ class SharedPrefixes:
     num_groups: int
     max_group_size: int
     max_shared_len: int
+    min_shared_len: int = 0  # smallest shared_len over the batch rows
 
     def groups(self) -> list:
         return [self.members[self.offsets[g]:self.offsets[g + 1]].tolist() for g in range(self.num_groups)]
@@ -234,7 +235,8 @@ class BlockManager:
         _check(lib().pa_bm_shared_prefixes(self._h, _ptr(ids) if n else None, n, int(granule), _ptr(group_offsets),
                                            _ptr(group_members), _ptr(shared_len), ctypes.byref(ng),
                                            ctypes.byref(gmax), ctypes.byref(smax)))
-        return SharedPrefixes(group_offsets, group_members, shared_len, ng.value, gmax.value, smax.value)
+        smin = int(shared_len[:n].min()) if n else 0
+        return SharedPrefixes(group_offsets, group_members, shared_len, ng.value, gmax.value, smax.value, smin)
 
     def stats(self) -> dict:
         s = PaBmStats()
@@ -412,8 +414,9 @@ def decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot
 def decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                   max_context_len: int, scale: float, partition_size: int, group_offsets: torch.Tensor,
                   group_members: torch.Tensor, shared_len: torch.Tensor, num_groups: int, max_group_size: int,
-                  max_shared_len: int, out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                  max_shared_len: int, min_shared_len: int = 0, out: Optional[torch.Tensor] = None,
+                  out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
     """pa_decode_shared: decode with each group's shared prefix read once
     for all its rows (group arrays on the device, int32). Returns ``out``."""
     B, Hq, D = q.shape
@@ -435,5 +438,5 @@ def decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, c
                                       float(scale), int(partition_size), _dev(group_offsets, "group_offsets"),
                                       _dev(group_members, "group_members"), _dev(shared_len, "shared_len"),
                                       int(num_groups), int(max_group_size), int(max_shared_len),
-                                      _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
+                                      int(min_shared_len), _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
     return out

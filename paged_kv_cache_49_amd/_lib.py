@@ -90,7 +90,8 @@ SIGNATURES = {
     "pa_decode": (c_int, [POINTER(PaKvCache), _P, c_int, _P, c_int, _P, c_int32, _P, c_int32, c_int32,
                           c_int32, c_float, c_int32, _P, c_size_t, _P]),
     "pa_decode_shared": (c_int, [POINTER(PaKvCache), _P, c_int, _P, c_int, _P, c_int32, _P, c_int32, c_int32,
-                                 c_int32, c_float, c_int32, _P, _P, _P, c_int32, c_int32, c_int32, _P, c_size_t, _P]),
+                                 c_int32, c_float, c_int32, _P, _P, _P, c_int32, c_int32, c_int32, c_int32, _P,
+                                 c_size_t, _P]),
     "pa_decode_append": (c_int, [POINTER(PaKvCache), _P, _P, c_int, _P, _P, c_int, _P, c_int, _P, c_int32, _P,
                                  c_int32, c_int32, c_int32, c_float, _P, c_size_t, _P]),
 }

@@ -342,7 +342,7 @@ struct SharedArgs {
   const int32_t* group_offsets;
   const int32_t* group_members;
   const int32_t* shared_len;
-  int32_t num_groups, max_group_size, max_shared_len;
+  int32_t num_groups, max_group_size, max_shared_len, min_shared_len;
 };
 
 // pa_decode; pa_decode_append when k_new != nullptr and pa_decode_shared
@@ -481,7 +481,8 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
   if (wgs > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many workgroups (%lld)", (long long)wgs);
   hipError_t e = hipSuccess;
   if (sh != nullptr && sh->num_groups > 0 && sh->max_shared_len > 0) {
-    // the shared partitions, once per group (see decode_shared_kernel.h)
+    // group units for the shared partitions, then the rest per sequence
+    // (see decode_shared_kernel.h)
     const pa::GroupLaunch glaunch = pa::find_decode_group(cache->dtype, D, bs, G);
     if (glaunch == nullptr) return fail(PA_ERR_UNSUPPORTED, "no shared-prefix kernel for these shapes");
     pa::SharedParams sp{};
@@ -491,14 +492,20 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
     sp.num_groups = sh->num_groups;
     sp.row_tiles = (sh->max_group_size * G + 15) / 16;
     sp.shared_parts = sh->max_shared_len / partition_size;
+    sp.pairs = B * hkv;
     const int64_t units = static_cast<int64_t>(sp.shared_parts) * sh->num_groups * hkv;
     const int64_t gwgs = (units + 7) / 8 * 8 * sp.row_tiles;
-    if (gwgs > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many shared-prefix workgroups (%lld)", (long long)gwgs);
-    e = glaunch(prm, sp, dim3(static_cast<uint32_t>(gwgs)), s);
-    if (e != hipSuccess) return fail(PA_ERR_DEVICE, "shared-prefix launch: %s", hipGetErrorString(e));
+    // partitions past the shared prefix: at most P - min_shared_len / ps per sequence
+    const int64_t twgs = (P - sh->min_shared_len / partition_size) * static_cast<int64_t>(B) * hkv;
+    if (gwgs + twgs > 0x7fffffff)
+      return fail(PA_ERR_INVALID_ARGUMENT, "too many shared-prefix workgroups (%lld)", (long long)(gwgs + twgs));
+    sp.group_wgs = static_cast<int32_t>(gwgs);
     prm.shared_len = sh->shared_len;
+    e = glaunch(prm, sp, dim3(static_cast<uint32_t>(gwgs + twgs)), s);
+    if (e != hipSuccess) return fail(PA_ERR_DEVICE, "shared-prefix launch: %s", hipGetErrorString(e));
+  } else {
+    e = launch(prm, dim3(static_cast<uint32_t>(wgs)), s);
   }
-  e = launch(prm, dim3(static_cast<uint32_t>(wgs)), s);
   if (e != hipSuccess) return fail(PA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
   if (P > 1) {
     pa::ReduceParams r{};
@@ -565,8 +572,8 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dty
                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
                            int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
                            const int32_t* group_offsets, const int32_t* group_members, const int32_t* shared_len,
-                           int32_t num_groups, int32_t max_group_size, int32_t max_shared_len, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           int32_t num_groups, int32_t max_group_size, int32_t max_shared_len,
+                           int32_t min_shared_len, void* workspace, size_t workspace_bytes, void* stream) {
   pa::clear_error();
   pa_status st = pa::validate_cache(cache);
   if (st != PA_OK) return st;
@@ -575,11 +582,12 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dty
   if (partition_size <= 0 || partition_size % 16 != 0 || partition_size % cache->block_size != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "partition_size %d must be a positive multiple of 16 and of block_size %d",
                 partition_size, cache->block_size);
-  if (num_groups < 0 || max_group_size < 0 || max_shared_len < 0)
-    return fail(PA_ERR_INVALID_ARGUMENT, "negative num_groups, max_group_size or max_shared_len");
-  if (max_shared_len % partition_size != 0)
-    return fail(PA_ERR_INVALID_ARGUMENT, "max_shared_len %d is not a multiple of partition_size %d", max_shared_len,
-                partition_size);
+  if (num_groups < 0 || max_group_size < 0 || max_shared_len < 0 || min_shared_len < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "negative num_groups, max_group_size, max_shared_len or min_shared_len");
+  if (max_shared_len % partition_size != 0 || min_shared_len % partition_size != 0 || min_shared_len > max_shared_len)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "min_shared_len %d / max_shared_len %d must be multiples of partition_size %d, min <= max",
+                min_shared_len, max_shared_len, partition_size);
   if (max_shared_len >= max_context_len && max_shared_len > 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "max_shared_len %d must be below max_context_len %d", max_shared_len,
                 max_context_len);
@@ -612,6 +620,7 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dty
         if (sq < 0 || sq >= B || in_group[sq]++)
           return fail(PA_ERR_INVALID_ARGUMENT, "group %d: member %d out of range or in two groups", gi, sq);
         if (shl[sq] != shl[first] || shl[sq] % partition_size != 0 || shl[sq] > max_shared_len ||
+            shl[sq] < min_shared_len ||
             shl[sq] >= std::min(lens[sq], max_context_len))
           return fail(PA_ERR_INVALID_ARGUMENT, "group %d: shared_len of row %d is inconsistent", gi, sq);
         for (int32_t b = 0; b < shl[sq] / bs; ++b)
@@ -619,11 +628,16 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dty
             return fail(PA_ERR_INVALID_ARGUMENT, "group %d: rows %d and %d differ at table entry %d", gi, sq, first, b);
       }
     }
-    for (int32_t i = 0; i < B; ++i)
+    for (int32_t i = 0; i < B; ++i) {
       if (!in_group[i] && shl[i] != 0)
         return fail(PA_ERR_INVALID_ARGUMENT, "row %d is in no group but has shared_len %d", i, shl[i]);
+      if (shl[i] < min_shared_len)
+        return fail(PA_ERR_INVALID_ARGUMENT, "shared_len[%d] = %d is below min_shared_len %d", i, shl[i],
+                    min_shared_len);
+    }
   }
-  pa::SharedArgs sh{group_offsets, group_members, shared_len, num_groups, max_group_size, max_shared_len};
+  pa::SharedArgs sh{group_offsets, group_members, shared_len, num_groups, max_group_size, max_shared_len,
+                    min_shared_len};
   return pa::decode_impl(cache, out, out_dtype, q, q_dtype, block_tables, max_blocks, context_lens, B, num_q_heads,
                          max_context_len, scale, partition_size, workspace, workspace_bytes, stream, nullptr, nullptr,
                          nullptr, num_groups > 0 ? &sh : nullptr);

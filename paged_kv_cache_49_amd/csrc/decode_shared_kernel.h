@@ -12,16 +12,19 @@
 // partitions, one pass over a shared partition serves every member of the
 // group, because its K/V rows are the same for all of them.
 //
-// pa_decode_shared runs three kernels on the caller's stream:
-//  1. paged_decode_group_kernel: one wave per (shared partition, group, KV
-//     head, row tile). Its 16 q rows are (member, query head) pairs of the
-//     group: row r = member rt * (16 / G) + r / G, head r % G. The partition's
-//     K/V tiles come through the first member's table (the shared entries
-//     are identical in every member's table). Per-row results are written as
-//     partition partials (m, l, o) of each member.
-//  2. paged_decode_vt_kernel with shared_len: the partitions past each
-//     sequence's shared prefix, per sequence as usual.
-//  3. decode_reduce_kernel: the log-sum-exp merge of all partitions.
+// pa_decode_shared runs two kernels on the caller's stream:
+//  1. paged_decode_shared_kernel, one wave per workgroup, two kinds of
+//     workgroups in one grid (the short second kind fills the CUs the first
+//     leaves idle):
+//     * group units, one per (shared partition, group, KV head, row tile).
+//       Its 16 q rows are (member, query head) pairs of the group: row r =
+//       member rt * (16 / G) + r / G, head r % G. The partition's K/V tiles
+//       come through the first member's table (the shared entries are
+//       identical in every member's table). Per-row results are written as
+//       partition partials (m, l, o) of each member.
+//     * tail units: the partitions past each sequence's shared prefix, per
+//       (sequence, KV head) as in the partition kernel (vt_unit).
+//  2. decode_reduce_kernel: the log-sum-exp merge of all partitions.
 // The row tiles of one (partition, group, KV head) are placed on the same
 // XCD, next to each other in dispatch order (workgroups are dealt to the 8
 // XCDs round-robin), so the K/V they all read is fetched from HBM once and
@@ -39,19 +42,20 @@ struct SharedParams {
   int32_t num_groups;
   int32_t row_tiles;     // ceil(max_group_size * G / 16)
   int32_t shared_parts;  // max shared_len / partition_size
+  int32_t group_wgs;     // workgroups [0, group_wgs) are group units, the rest tail units
+  int32_t pairs;         // B * num_kv_heads
 };
 
+// One group unit; wg < sp.group_wgs; s_out = the wave's 16 x D floats.
 template <typename KV, typename QT, int D, int BS, int G>
-__global__ __launch_bounds__(64) void paged_decode_group_kernel(const DecodeParams p, const SharedParams sp) {
+__device__ __forceinline__ void group_unit(const DecodeParams& p, const SharedParams& sp, int wg, float* s_out) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
   constexpr int kNT = D / 16;
   constexpr int kMembersPerTile = 16 / G;
-  __shared__ float s_out[16 * D];
 
   // workgroup -> (unit, row tile): unit u's row tiles are workgroups
   // ((u / 8) * RT + rt) * 8 + u % 8, all on XCD u % 8
-  const int wg = static_cast<int>(blockIdx.x);
   const int k = wg >> 3;
   const int rt = k % sp.row_tiles;
   const int64_t u = static_cast<int64_t>(k / sp.row_tiles) * 8 + (wg & 7);
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(64) void paged_decode_group_kernel(const DecodePara
   const int tok_begin = part * ps;
   if (tok_begin + ps > sp.shared_len[first]) return;  // past this group's shared prefix
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int col = lane & 15, j = lane >> 4;
   const int32_t* bt = p.block_tables + static_cast<int64_t>(first) * p.max_blocks;
   const int blk_first = tok_begin / BS;
@@ -120,11 +124,22 @@ __global__ __launch_bounds__(64) void paged_decode_group_kernel(const DecodePara
   }
 }
 
+template <typename KV, typename QT, int D, int BS, int G>
+__global__ __launch_bounds__(64) void paged_decode_shared_kernel(const DecodeParams p, const SharedParams sp) {
+  __shared__ float s_out[16 * D];
+  const int wg = static_cast<int>(blockIdx.x);
+  if (wg < sp.group_wgs) {
+    group_unit<KV, QT, D, BS, G>(p, sp, wg, s_out);
+  } else {
+    vt_unit<KV, QT, D, BS, G>(p, wg - sp.group_wgs, sp.pairs, s_out);
+  }
+}
+
 using GroupLaunch = hipError_t (*)(const DecodeParams&, const SharedParams&, dim3 grid, hipStream_t stream);
 
 template <typename KV, typename QT, int D, int BS, int G>
 hipError_t launch_decode_group(const DecodeParams& p, const SharedParams& sp, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_group_kernel<KV, QT, D, BS, G>), grid, dim3(64), 0, stream, p, sp);
+  hipLaunchKernelGGL((paged_decode_shared_kernel<KV, QT, D, BS, G>), grid, dim3(64), 0, stream, p, sp);
   return hipGetLastError();
 }
 

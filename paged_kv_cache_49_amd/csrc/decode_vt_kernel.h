@@ -280,32 +280,43 @@ __device__ __forceinline__ float vt_normalise(const f32x4 (&acc)[D / 16], float 
   return l_head;
 }
 
+// One (partition, sequence, KV head) unit of the partition kernel. wg =
+// the unit's index in partition-major order over `pairs` = B * Hkv
+// (sequence, head) pairs; s_out = the wave's G x D floats of LDS. With
+// p.shared_len (pa_decode_shared) partition indices count from the
+// sequence's first partition past its shared prefix (the shared ones are
+// computed once per group).
 template <typename KV, typename QT, int D, int BS, int G>
-__global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams p) {
+__device__ __forceinline__ void vt_unit(const DecodeParams& p, int wg, int pairs, float* s_out) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
   constexpr int kNT = D / 16;  // 16-dim output tiles
   static_assert(G <= 16, "at most 16 query heads per KV head");
-  __shared__ float s_out[G * D];
 
-  const int pairs = static_cast<int>(gridDim.x) / p.num_partitions;  // B * Hkv
-  const int part = static_cast<int>(blockIdx.x) / pairs;
-  const int pr = static_cast<int>(blockIdx.x) - part * pairs;
+  const int part0 = wg / pairs;
+  const int pr = wg - part0 * pairs;
   const int s = pr / p.num_kv_heads;
   const int g = pr - s * p.num_kv_heads;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int32_t* bt = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
-  const int blk_first = p.partition_size > 0 ? part * p.partition_size / BS : 0;
-  const int id_first = blk_first + lane < p.max_blocks ? bt[blk_first + lane] : 0;
+  int id_first = 0;
+  if (p.shared_len == nullptr) {
+    // the table entries of the partition, requested together with the length
+    const int blk_first = p.partition_size > 0 ? part0 * p.partition_size / BS : 0;
+    id_first = blk_first + lane < p.max_blocks ? bt[blk_first + lane] : 0;
+  }
 
   int L = p.context_lens[s];
   L = L < p.len_cap ? L : p.len_cap;
   L = L > 0 ? L : 0;
   const int ps = p.partition_size > 0 ? p.partition_size : (L > 0 ? L : 1);
   const int nparts = (L + ps - 1) / ps;
+  const int part = p.shared_len == nullptr ? part0 : part0 + p.shared_len[s] / ps;
   if (part >= (nparts > 0 ? nparts : 1)) return;
-  // partitions of a shared prefix are computed once per group (pa_decode_shared)
-  if (p.shared_len != nullptr && part * ps < p.shared_len[s]) return;
+  if (p.shared_len != nullptr) {
+    const int blk_first = part * ps / BS;
+    id_first = blk_first + lane < p.max_blocks ? bt[blk_first + lane] : 0;
+  }
   const int64_t head0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(g) * G;
   if (L == 0) {
     for (int i = lane; i < G * D; i += 64) store_out(p.out, head0 * D + i, p.out_dtype, 0.f);
@@ -354,6 +365,12 @@ __global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams 
     p.part_m[pi] = m_w;
     p.part_l[pi] = l_head;
   }
+}
+
+template <typename KV, typename QT, int D, int BS, int G>
+__global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams p) {
+  __shared__ float s_out[G * D];
+  vt_unit<KV, QT, D, BS, G>(p, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x) / p.num_partitions, s_out);
 }
 
 template <typename KV, typename QT, int D, int BS, int G>

@@ -176,7 +176,7 @@ class PagedBatch:
             elif groups is not None:
                 decode_shared(c, q[i], tables, lens, max_ctx, scale, partition_size, st.goff, st.gmem[:B],
                               st.shl[:B], groups.num_groups, groups.max_group_size, groups.max_shared_len,
-                              out=outs[i], workspace=workspace)
+                              groups.min_shared_len, out=outs[i], workspace=workspace)
             else:
                 decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i], workspace=workspace)
             if timed:

@@ -241,11 +241,11 @@ def test_decode_append_rejects_bad_arguments_before_launch(kw, cache_kw, want):
 def _shared_status(cache, **kw):
     a = dict(out=0x3000, out_dtype=_lib.PA_BF16, q=0x4000, q_dtype=_lib.PA_BF16, tables=0x5000, max_blocks=64,
              lens=0x6000, B=8, Hq=32, max_ctx=1024, scale=0.1, part=256, off=0x7000, mem=0x8000, shl=0x9000, ng=2,
-             gmax=4, smax=512, ws=None, ws_bytes=0)
+             gmax=4, smax=512, smin=0, ws=None, ws_bytes=0)
     a.update(kw)
     return pa.lib().pa_decode_shared(ctypes.byref(cache), a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["tables"],
                                      a["max_blocks"], a["lens"], a["B"], a["Hq"], a["max_ctx"], a["scale"], a["part"],
-                                     a["off"], a["mem"], a["shl"], a["ng"], a["gmax"], a["smax"], a["ws"],
+                                     a["off"], a["mem"], a["shl"], a["ng"], a["gmax"], a["smax"], a["smin"], a["ws"],
                                      a["ws_bytes"], None)
 
 
@@ -256,6 +256,8 @@ def _shared_status(cache, **kw):
     (dict(part=16), dict(_DIM, block_size=32), _lib.PA_ERR_INVALID_ARGUMENT),  # not a multiple of block_size
     (dict(smax=300), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                # shared length not whole partitions
     (dict(smax=1024), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),               # no token left of its own
+    (dict(smin=768), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                # min above max
+    (dict(smin=100), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                # not whole partitions
     (dict(off=None), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(ng=9), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                    # more groups than rows
     (dict(ng=-1), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),

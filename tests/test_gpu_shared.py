@@ -87,7 +87,7 @@ def _run(seed, prompts, samples, tail_max, G, hkv, D, bs, kv, ps, what=""):
     td, ld, qd = dev(tables), dev(lens), q.cuda()
     got = pa.decode_shared(cache, qd, td, ld, max_ctx, scale, ps, dev(sp.offsets), dev(sp.members),
                            dev(sp.shared_len), sp.num_groups, sp.max_group_size, sp.max_shared_len,
-                           out_dtype=torch.float32)
+                           sp.min_shared_len, out_dtype=torch.float32)
     plain = pa.decode(cache, qd, td, ld, max_ctx, scale, ps, out_dtype=torch.float32)
     torch.cuda.synchronize()
     ref = _oracle(seqs, q, hkv, scale, kv)
@@ -149,7 +149,7 @@ def test_shared_prefix_sharing_workload(gpu):
     q = wl.q().cuda()
     got = pa.decode_shared(cache, q, dev(tables), dev(lens), int(lens.max()), wl.scale, 512, dev(sp.offsets),
                            dev(sp.members), dev(sp.shared_len), sp.num_groups, sp.max_group_size, sp.max_shared_len,
-                           out_dtype=torch.float32)
+                           sp.min_shared_len, out_dtype=torch.float32)
     torch.cuda.synchronize()
     qd = oatt.to_f64(wl.q())
     ref = np.zeros(qd.shape)
@@ -169,7 +169,7 @@ def test_no_groups_is_plain_decode(gpu):
     from tests.gpu_util import device_setup, run_decode
     _, cache, tables, lens, max_ctx = device_setup(wl, v_layout="dim")
     z = torch.zeros(wl.batch + 1, dtype=torch.int32, device="cuda")
-    got = pa.decode_shared(cache, wl.q().cuda(), tables, lens, max_ctx, wl.scale, 256, z, z, z, 0, 0, 0,
+    got = pa.decode_shared(cache, wl.q().cuda(), tables, lens, max_ctx, wl.scale, 256, z, z, z, 0, 0, 0, 0,
                            out_dtype=torch.float32)
     torch.cuda.synchronize()
     H.assert_close(got.cpu().double().numpy(), H.oracle_contiguous(wl), what="no groups")
