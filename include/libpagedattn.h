@@ -155,6 +155,54 @@ pa_status pa_seq_blocks(const pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_
 pa_status pa_pack_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
                                int32_t pad, int32_t* tables, int32_t* context_lens);
 
+/* ------------------------------------------------------------------------
+ * Swapping ([course] §4 and §8: under memory pressure the scheduler may
+ * preempt a sequence by evicting and recomputing it or by swapping its
+ * blocks out; a preemption is a latency event worth counting). The manager
+ * keeps a second pool of host blocks with its own LIFO free stack (first
+ * pop = host block 0). The data move is the caller's: pa_copy_blocks_between
+ * with the reported pairs, between the device pool and a host pool of the
+ * same geometry (pinned host memory the device can address), on the stream
+ * of the decode work, before any later write to the freed blocks.
+ * ---------------------------------------------------------------------- */
+
+/* Size the host pool (num_host_blocks >= 0; 0 = no swapping). Only while no
+ * sequence is swapped out (else PA_ERR_INVALID_ARGUMENT); resets its free
+ * stack. */
+pa_status pa_bm_set_host_pool(pa_bm* bm, int32_t num_host_blocks);
+
+/* Swap out live sequence seq_id: each block of its table, in logical order,
+ * moves to a freshly popped host block; pairs[i] = (device block, host
+ * block) (host int32[capacity][2], capacity >= table length); the device
+ * block loses this sequence's reference (and returns to the free stack at
+ * 0; a block shared with other sequences stays theirs). Afterwards the
+ * sequence is swapped: pa_alloc / pa_fork / pa_pack_block_tables /
+ * pa_bm_shared_prefixes on it fail with PA_ERR_INVALID_ARGUMENT,
+ * pa_seq_blocks reports host block ids, pa_free returns them to the host
+ * pool. All-or-nothing: PA_ERR_OUT_OF_BLOCKS when the host pool lacks
+ * blocks; PA_ERR_UNKNOWN_SEQ; PA_ERR_INVALID_ARGUMENT (already swapped,
+ * capacity). *num_pairs = table length. */
+pa_status pa_swap_out(pa_bm* bm, int64_t seq_id, int32_t* pairs, int32_t capacity, int32_t* num_pairs);
+
+/* Swap a swapped sequence back in: each host block, in logical order, moves
+ * to a freshly popped device block (refcount 1); pairs[i] = (host block,
+ * device block); the host blocks return to the host free stack in logical
+ * order. All-or-nothing: PA_ERR_OUT_OF_BLOCKS when the device pool lacks
+ * blocks; PA_ERR_INVALID_ARGUMENT (not swapped, capacity). */
+pa_status pa_swap_in(pa_bm* bm, int64_t seq_id, int32_t* pairs, int32_t capacity, int32_t* num_pairs);
+
+/* *swapped = 1 if the live sequence is swapped out, else 0. */
+pa_status pa_bm_swap_state(const pa_bm* bm, int64_t seq_id, int32_t* swapped);
+
+/* Host pool size, free host blocks, swapped sequences, and the numbers of
+ * swap-outs and swap-ins so far (any output may be NULL). */
+pa_status pa_bm_host_stats(const pa_bm* bm, int32_t* num_host_blocks, int32_t* num_host_free, int32_t* num_swapped,
+                           int64_t* swap_outs, int64_t* swap_ins);
+
+/* Host free stack from bottom to top (the top is popped next): host
+ * int32[capacity]; *n receives the count. */
+pa_status pa_bm_host_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity, int32_t* n);
+
 /* Groups of the batch rows seq_ids[0..n) whose block tables begin with the
  * same physical blocks — forks of one prompt ([course] §2 "The bonus":
  * parallel samples share the prompt's blocks; [note] prefix-sharing
@@ -247,6 +295,19 @@ pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* k_new, cons
  * outside [0, num_blocks) are skipped (PA_DEBUG=1 reports them). N == 0 is
  * a no-op. */
 pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* pairs, int32_t N, void* stream);
+
+/* Whole-block copies between two pools of the same geometry (block_size,
+ * num_kv_heads, head_dim, dtype, v_layout; block strides may differ):
+ * dst block pairs[i][1] <- src block pairs[i][0], K and V, for i < N. Used
+ * to swap blocks between the device pool and a host pool (pinned host
+ * memory the device can address). pairs: device (or device-addressable)
+ * int32[N][2]; destinations must be distinct and no destination may be a
+ * source of the same call when the pools are the same memory. Pairs with an
+ * id outside its pool are skipped (PA_DEBUG=1 reports them). Errors:
+ * PA_ERR_INVALID_ARGUMENT (descriptors, geometry mismatch, N < 0, NULL
+ * pairs with N > 0), PA_ERR_DEVICE. Asynchronous on `stream`. */
+pa_status pa_copy_blocks_between(const pa_kv_cache* dst, const pa_kv_cache* src, const int32_t* pairs, int32_t N,
+                                 void* stream);
 
 /* ------------------------------------------------------------------------
  * Decode attention through the block tables ([course] §2 "The insight":

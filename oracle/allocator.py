@@ -29,6 +29,15 @@ Readings where the pages leave the choice open:
   reported for a whole-block copy; the other holders keep the old block;
   the last holder writes in place. Full blocks are never written.
 * Pool exhaustion: the whole request fails and nothing changes.
+* Swapping ([course] §4 and §8: under memory pressure a sequence may be
+  preempted by swapping its blocks out): a host pool with its own LIFO free
+  stack whose first pop is host block 0. Swap-out moves the sequence's
+  blocks in logical order to freshly popped host blocks, reporting (device,
+  host) pairs; each device block loses that reference (back on the device
+  stack at 0). Swap-in pops fresh device blocks in logical order, reporting
+  (host, device) pairs, and pushes the host blocks back in logical order.
+  A swapped sequence can only be swapped in, freed (its host blocks go back
+  on the host stack) or queried. Both are all-or-nothing.
 * A batch of allocations is all-or-nothing and may not name a sequence
   twice; requests are applied in the given order.
 
@@ -92,6 +101,11 @@ class _State:
         self.lens: Dict[int, int] = {}
         self.cow_copies = 0
         self.forks = 0
+        self.host_stack: List[int] = []  # top = end
+        self.num_host = 0
+        self.swapped: set = set()
+        self.swap_outs = 0
+        self.swap_ins = 0
 
 
 class BlockAllocatorModel:
@@ -128,6 +142,19 @@ class BlockAllocatorModel:
     def seqs(self) -> List[int]:
         return list(self.st.tables)
 
+    @property
+    def host_free_stack(self) -> List[int]:
+        return list(self.st.host_stack)
+
+    def is_swapped(self, seq: int) -> bool:
+        if seq not in self.st.tables:
+            raise UnknownSeq(seq)
+        return seq in self.st.swapped
+
+    def host_stats(self) -> dict:
+        return dict(num_host_blocks=self.st.num_host, num_host_free=len(self.st.host_stack),
+                    num_swapped=len(self.st.swapped), swap_outs=self.st.swap_outs, swap_ins=self.st.swap_ins)
+
     def stats(self) -> dict:
         rc = self.st.refcnt
         return dict(num_blocks=self.num_blocks, num_free=len(self.st.stack),
@@ -149,6 +176,8 @@ class BlockAllocatorModel:
         if seq not in st.tables:
             st.tables[seq] = []
             st.lens[seq] = 0
+        if seq in st.swapped:
+            raise InvalidArgument("sequence is swapped out")
         table = st.tables[seq]
         length = st.lens[seq]
         cows: List[Tuple[int, int]] = []
@@ -195,6 +224,8 @@ class BlockAllocatorModel:
             raise SeqExists(child)
         if parent not in self.st.tables:
             raise UnknownSeq(parent)
+        if parent in self.st.swapped:
+            raise InvalidArgument("sequence is swapped out")
         self.st.tables[child] = list(self.st.tables[parent])
         self.st.lens[child] = self.st.lens[parent]
         for blk in self.st.tables[child]:
@@ -206,17 +237,73 @@ class BlockAllocatorModel:
         goes back on the free stack when none is left."""
         if seq not in self.st.tables:
             raise UnknownSeq(seq)
-        for blk in self.st.tables.pop(seq):
+        if seq in self.st.swapped:
+            self.st.host_stack.extend(self.st.tables.pop(seq))
+            self.st.swapped.discard(seq)
+        else:
+            for blk in self.st.tables.pop(seq):
+                self.st.refcnt[blk] -= 1
+                if self.st.refcnt[blk] == 0:
+                    self.st.stack.append(blk)
+        del self.st.lens[seq]
+
+    def set_host_pool(self, num_host_blocks: int) -> None:
+        if num_host_blocks < 0:
+            raise InvalidArgument("negative host pool")
+        if len(self.st.host_stack) != self.st.num_host:
+            raise InvalidArgument("host blocks in use")
+        self.st.num_host = int(num_host_blocks)
+        self.st.host_stack = list(range(num_host_blocks - 1, -1, -1))
+
+    def swap_out(self, seq: int) -> List[Tuple[int, int]]:
+        """Move ``seq``'s blocks to the host pool; (device, host) pairs."""
+        if seq not in self.st.tables:
+            raise UnknownSeq(seq)
+        if seq in self.st.swapped:
+            raise InvalidArgument("already swapped out")
+        table = self.st.tables[seq]
+        if len(table) > len(self.st.host_stack):
+            raise OutOfBlocks("host pool exhausted")
+        pairs = []
+        for i, blk in enumerate(table):
+            h = self.st.host_stack.pop()
+            pairs.append((blk, h))
+            table[i] = h
             self.st.refcnt[blk] -= 1
             if self.st.refcnt[blk] == 0:
                 self.st.stack.append(blk)
-        del self.st.lens[seq]
+        self.st.swapped.add(seq)
+        self.st.swap_outs += 1
+        return pairs
+
+    def swap_in(self, seq: int) -> List[Tuple[int, int]]:
+        """Bring ``seq``'s blocks back into fresh device blocks; (host,
+        device) pairs."""
+        if seq not in self.st.tables:
+            raise UnknownSeq(seq)
+        if seq not in self.st.swapped:
+            raise InvalidArgument("not swapped out")
+        table = self.st.tables[seq]
+        if len(table) > len(self.st.stack):
+            raise OutOfBlocks("pool exhausted")
+        pairs = []
+        for i, h in enumerate(table):
+            blk = self.st.stack.pop()
+            self.st.refcnt[blk] = 1
+            pairs.append((h, blk))
+            table[i] = blk
+            self.st.host_stack.append(h)
+        self.st.swapped.discard(seq)
+        self.st.swap_ins += 1
+        return pairs
 
     def pack(self, seqs: Sequence[int], max_blocks: int, pad: int = -1):
         """(tables [n][max_blocks] padded with ``pad``, context lengths [n])."""
         tables, lens = [], []
         for seq in seqs:
             t = self.table(seq)
+            if seq in self.st.swapped:
+                raise InvalidArgument("sequence is swapped out")
             if len(t) > max_blocks:
                 raise InvalidArgument("table wider than max_blocks")
             tables.append(t + [pad] * (max_blocks - len(t)))

@@ -22,7 +22,8 @@ from ._lib import PaBmStats, PaKvCache, lib
 __all__ = [
     "PagedAttnError", "OutOfBlocks", "UnknownSeq", "SeqExists", "Unsupported", "InvalidArgument",
     "DeviceError", "BlockManager", "KVCache", "reshape_and_cache", "copy_blocks", "decode",
-    "decode_workspace_size", "decode_append", "decode_shared", "SharedPrefixes", "lib", "BALANCED",
+    "decode_workspace_size", "decode_append", "decode_shared", "SharedPrefixes", "copy_blocks_between", "lib",
+    "BALANCED",
 ]
 
 
@@ -238,6 +239,45 @@ class BlockManager:
         smin = int(shared_len[:n].min()) if n else 0
         return SharedPrefixes(group_offsets, group_members, shared_len, ng.value, gmax.value, smax.value, smin)
 
+    # -- swapping (host pool) -------------------------------------------
+    def set_host_pool(self, num_host_blocks: int) -> None:
+        _check(lib().pa_bm_set_host_pool(self._h, int(num_host_blocks)))
+
+    def _swap(self, fn, seq_id: int) -> np.ndarray:
+        n_blocks = self.seq_info(seq_id)[1]
+        pairs = np.empty((max(n_blocks, 1), 2), np.int32)
+        n = ctypes.c_int32()
+        _check(fn(self._h, int(seq_id), _ptr(pairs), n_blocks, ctypes.byref(n)))
+        return pairs[: n.value]
+
+    def swap_out(self, seq_id: int) -> np.ndarray:
+        """pa_swap_out: (device block, host block) pairs [n][2]."""
+        return self._swap(lib().pa_swap_out, seq_id)
+
+    def swap_in(self, seq_id: int) -> np.ndarray:
+        """pa_swap_in: (host block, device block) pairs [n][2]."""
+        return self._swap(lib().pa_swap_in, seq_id)
+
+    def is_swapped(self, seq_id: int) -> bool:
+        v = ctypes.c_int32()
+        _check(lib().pa_bm_swap_state(self._h, int(seq_id), ctypes.byref(v)))
+        return bool(v.value)
+
+    def host_stats(self) -> dict:
+        a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        d, e = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().pa_bm_host_stats(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), ctypes.byref(d),
+                                      ctypes.byref(e)))
+        return dict(num_host_blocks=a.value, num_host_free=b.value, num_swapped=c.value, swap_outs=d.value,
+                    swap_ins=e.value)
+
+    def host_free_stack(self) -> list:
+        cap = max(self.host_stats()["num_host_blocks"], 1)
+        out = np.empty(cap, np.int32)
+        n = ctypes.c_int32()
+        _check(lib().pa_bm_host_free_stack(self._h, _ptr(out), cap, ctypes.byref(n)))
+        return out[: n.value].tolist()
+
     def stats(self) -> dict:
         s = PaBmStats()
         _check(lib().pa_bm_stats_get(self._h, ctypes.byref(s)))
@@ -288,12 +328,15 @@ class KVCache:
         buffer of blocks each holding K then V."""
         dt = _NAMES[kv_dtype]
         be = block_size * num_kv_heads * head_dim
+        pinned = str(device) == "pinned"  # a host pool the device addresses directly (swap target)
+        if pinned:
+            device = "cpu"
         if layout == "split":
-            k = torch.empty(num_blocks * be, dtype=dt, device=device)
-            v = torch.empty(num_blocks * be, dtype=dt, device=device)
+            k = torch.empty(num_blocks * be, dtype=dt, device=device, pin_memory=pinned)
+            v = torch.empty(num_blocks * be, dtype=dt, device=device, pin_memory=pinned)
             stride = be
         elif layout == "interleaved":
-            buf = torch.empty(num_blocks * 2 * be, dtype=dt, device=device)
+            buf = torch.empty(num_blocks * 2 * be, dtype=dt, device=device, pin_memory=pinned)
             k = buf
             v = buf[be:]
             stride = 2 * be
@@ -311,8 +354,9 @@ class KVCache:
         return _code(self.k)
 
     def desc(self) -> PaKvCache:
-        if not (self.k.is_cuda and self.v.is_cuda):
-            raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, "pool tensors must be on the device")
+        if not ((self.k.is_cuda and self.v.is_cuda) or (self.k.is_pinned() and self.v.is_pinned())):
+            raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT,
+                                  "pool tensors must be on the device (or in pinned host memory for a host pool)")
         return PaKvCache(self.k.data_ptr(), self.v.data_ptr(), int(self.block_stride), int(self.num_blocks),
                          int(self.block_size), int(self.num_kv_heads), int(self.head_dim), self.dtype_code,
                          _V_LAYOUTS[self.v_layout], float(self.k_scale), float(self.v_scale))
@@ -440,3 +484,21 @@ def decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, c
                                       int(num_groups), int(max_group_size), int(max_shared_len),
                                       int(min_shared_len), _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
     return out
+
+
+def copy_blocks_between(dst: KVCache, src: KVCache, pairs, stream=None) -> None:
+    """pa_copy_blocks_between: dst block pairs[i][1] <- src block
+    pairs[i][0] (K and V). ``pairs`` int32 [N][2], a device tensor or host
+    data (then uploaded first, synchronously)."""
+    if not isinstance(pairs, torch.Tensor):
+        pairs = torch.as_tensor(np.asarray(pairs, np.int32).reshape(-1, 2))
+    if pairs.numel() == 0:
+        return
+    if not pairs.is_cuda:
+        dev = dst.k.device if dst.k.is_cuda else src.k.device
+        pairs = pairs.to(torch.int32).contiguous().to(dev)
+    if pairs.dtype != torch.int32:
+        raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, "pairs must be int32")
+    d, s_ = dst.desc(), src.desc()
+    _check(lib().pa_copy_blocks_between(ctypes.byref(d), ctypes.byref(s_), _dev(pairs, "pairs"), int(pairs.shape[0]),
+                                        _stream(stream)))

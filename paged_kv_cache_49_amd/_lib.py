@@ -83,6 +83,13 @@ SIGNATURES = {
     "pa_bm_stats_get": (c_int, [_P, POINTER(PaBmStats)]),
     "pa_bm_refcounts": (c_int, [_P, _P]),
     "pa_bm_free_stack": (c_int, [_P, _P, c_int32, _I32P]),
+    "pa_bm_set_host_pool": (c_int, [_P, c_int32]),
+    "pa_swap_out": (c_int, [_P, c_int64, _P, c_int32, _I32P]),
+    "pa_swap_in": (c_int, [_P, c_int64, _P, c_int32, _I32P]),
+    "pa_bm_swap_state": (c_int, [_P, c_int64, _I32P]),
+    "pa_bm_host_stats": (c_int, [_P, _I32P, _I32P, _I32P, POINTER(c_int64), POINTER(c_int64)]),
+    "pa_bm_host_free_stack": (c_int, [_P, _P, c_int32, _I32P]),
+    "pa_copy_blocks_between": (c_int, [POINTER(PaKvCache), POINTER(PaKvCache), _P, c_int32, _P]),
     "pa_bm_shared_prefixes": (c_int, [_P, _P, c_int32, c_int32, _P, _P, _P, _I32P, _I32P, _I32P]),
     "pa_reshape_and_cache": (c_int, [POINTER(PaKvCache), _P, _P, c_int, _P, c_int32, _P]),
     "pa_copy_blocks": (c_int, [POINTER(PaKvCache), _P, c_int32, _P]),

@@ -12,6 +12,16 @@
 // a branch writes into it. The choices the pages leave open (LIFO order,
 // writer-gets-the-copy, all-or-nothing) are documented in libpagedattn.h.
 //
+// Swapping ([course] §4 and §8: under memory pressure the scheduler may
+// preempt a sequence by swapping its blocks out): a second, host-side pool
+// of blocks with its own LIFO free stack (first pop = block 0). Swapping
+// out moves every block of a sequence to a fresh host block (a block shared
+// with other sequences loses this reference only; the others keep it on the
+// device) and frees the device blocks; swapping in does the reverse into
+// fresh device blocks. The caller copies the data with
+// pa_copy_blocks_between using the reported pairs. A swapped sequence can
+// only be swapped in, freed or queried.
+//
 // Every mutating entry point first plans the whole request against the
 // current state (blocks needed, including copy-on-write copies, checked
 // against the free count), and only then applies it, so a failure leaves
@@ -29,7 +39,8 @@
 struct pa_bm {
   struct Seq {
     int32_t len = 0;
-    std::vector<int32_t> blocks;  // logical order
+    std::vector<int32_t> blocks;  // logical order; host-pool ids while swapped
+    bool swapped = false;
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
@@ -38,6 +49,10 @@ struct pa_bm {
   std::unordered_map<int64_t, Seq> seqs;
   int64_t cow_copies = 0;
   int64_t forks = 0;
+  int32_t num_host_blocks = 0;
+  std::vector<int32_t> host_free;  // back() is popped next
+  int64_t swap_outs = 0;
+  int64_t swap_ins = 0;
 
   int64_t blocks_for(int64_t len) const { return (len + block_size - 1) / block_size; }
   int32_t pop() {
@@ -71,6 +86,8 @@ pa_status plan_and_apply(pa_bm* bm, const int64_t* ids, int32_t n, const int32_t
     if (!seen.insert(ids[i]).second)
       return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld appears twice in one batch", (long long)ids[i]);
     auto it = bm->seqs.find(ids[i]);
+    if (it != bm->seqs.end() && it->second.swapped)
+      return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is swapped out", (long long)ids[i]);
     const int64_t len = it == bm->seqs.end() ? 0 : it->second.len;
     if (len + ntok[i] > INT32_MAX)
       return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld would exceed INT32_MAX tokens", (long long)ids[i]);
@@ -192,9 +209,13 @@ pa_status pa_free(pa_bm* bm, int64_t seq_id) {
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_id);
   PA_GUARD_BEGIN
-  bm->free_stack.reserve(bm->num_blocks);
-  for (int32_t b : it->second.blocks)
-    if (--bm->refcnt[b] == 0) bm->free_stack.push_back(b);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.blocks) bm->host_free.push_back(h);
+  } else {
+    bm->free_stack.reserve(bm->num_blocks);
+    for (int32_t b : it->second.blocks)
+      if (--bm->refcnt[b] == 0) bm->free_stack.push_back(b);
+  }
   bm->seqs.erase(it);
   return PA_OK;
   PA_GUARD_END
@@ -206,6 +227,8 @@ pa_status pa_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
   if (bm->seqs.count(child_id)) return fail(PA_ERR_SEQ_EXISTS, "sequence %lld is already live", (long long)child_id);
   auto it = bm->seqs.find(parent_id);
   if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)parent_id);
+  if (it->second.swapped)
+    return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is swapped out", (long long)parent_id);
   PA_GUARD_BEGIN
   pa_bm::Seq copy = it->second;
   for (int32_t b : copy.blocks) ++bm->refcnt[b];
@@ -248,6 +271,8 @@ pa_status pa_pack_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t 
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_ids[i]);
+    if (it->second.swapped)
+      return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is swapped out", (long long)seq_ids[i]);
     const auto& blocks = it->second.blocks;
     const int32_t len = static_cast<int32_t>(blocks.size());
     if (len > max_blocks)
@@ -278,6 +303,8 @@ pa_status pa_bm_shared_prefixes(const pa_bm* bm, const int64_t* seq_ids, int32_t
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_ids[i]);
+    if (it->second.swapped)
+      return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is swapped out", (long long)seq_ids[i]);
     seqs[i] = &it->second;
   }
   // rows by first physical block, groups in order of first appearance
@@ -321,6 +348,117 @@ pa_status pa_bm_shared_prefixes(const pa_bm* bm, const int64_t* seq_ids, int32_t
   *max_shared_len = smax;
   return PA_OK;
   PA_GUARD_END
+}
+
+pa_status pa_bm_set_host_pool(pa_bm* bm, int32_t num_host_blocks) {
+  pa::clear_error();
+  if (bm == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm is NULL");
+  if (num_host_blocks < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_host_blocks = %d is negative", num_host_blocks);
+  if (static_cast<int32_t>(bm->host_free.size()) != bm->num_host_blocks)
+    return fail(PA_ERR_INVALID_ARGUMENT, "host blocks are in use by swapped sequences");
+  PA_GUARD_BEGIN
+  std::vector<int32_t> fresh(num_host_blocks);
+  for (int32_t i = 0; i < num_host_blocks; ++i) fresh[i] = num_host_blocks - 1 - i;  // first pop = block 0
+  bm->host_free.swap(fresh);
+  bm->num_host_blocks = num_host_blocks;
+  return PA_OK;
+  PA_GUARD_END
+}
+
+pa_status pa_swap_out(pa_bm* bm, int64_t seq_id, int32_t* pairs, int32_t capacity, int32_t* num_pairs) {
+  pa::clear_error();
+  if (bm == nullptr || num_pairs == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or num_pairs is NULL");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_id);
+  pa_bm::Seq& sq = it->second;
+  if (sq.swapped) return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is already swapped out", (long long)seq_id);
+  const int32_t n = static_cast<int32_t>(sq.blocks.size());
+  if (n > 0 && (pairs == nullptr || capacity < n))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pairs holds %d pairs, %d needed", capacity, n);
+  if (n > static_cast<int32_t>(bm->host_free.size()))
+    return fail(PA_ERR_OUT_OF_BLOCKS, "swap-out needs %d host blocks, %zu free of %d", n, bm->host_free.size(),
+                bm->num_host_blocks);
+  PA_GUARD_BEGIN
+  bm->free_stack.reserve(bm->num_blocks);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = sq.blocks[i];
+    const int32_t h = bm->host_free.back();
+    bm->host_free.pop_back();
+    pairs[2 * i] = b;
+    pairs[2 * i + 1] = h;
+    sq.blocks[i] = h;
+    if (--bm->refcnt[b] == 0) bm->free_stack.push_back(b);
+  }
+  sq.swapped = true;
+  ++bm->swap_outs;
+  *num_pairs = n;
+  return PA_OK;
+  PA_GUARD_END
+}
+
+pa_status pa_swap_in(pa_bm* bm, int64_t seq_id, int32_t* pairs, int32_t capacity, int32_t* num_pairs) {
+  pa::clear_error();
+  if (bm == nullptr || num_pairs == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or num_pairs is NULL");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_id);
+  pa_bm::Seq& sq = it->second;
+  if (!sq.swapped) return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is not swapped out", (long long)seq_id);
+  const int32_t n = static_cast<int32_t>(sq.blocks.size());
+  if (n > 0 && (pairs == nullptr || capacity < n))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pairs holds %d pairs, %d needed", capacity, n);
+  if (n > static_cast<int32_t>(bm->free_stack.size()))
+    return fail(PA_ERR_OUT_OF_BLOCKS, "swap-in needs %d blocks, %zu free of %d", n, bm->free_stack.size(),
+                bm->num_blocks);
+  PA_GUARD_BEGIN
+  bm->host_free.reserve(bm->num_host_blocks);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t h = sq.blocks[i];
+    const int32_t b = bm->pop();
+    bm->refcnt[b] = 1;
+    pairs[2 * i] = h;
+    pairs[2 * i + 1] = b;
+    sq.blocks[i] = b;
+    bm->host_free.push_back(h);
+  }
+  sq.swapped = false;
+  ++bm->swap_ins;
+  *num_pairs = n;
+  return PA_OK;
+  PA_GUARD_END
+}
+
+pa_status pa_bm_swap_state(const pa_bm* bm, int64_t seq_id, int32_t* swapped) {
+  pa::clear_error();
+  if (bm == nullptr || swapped == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or swapped is NULL");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq_id);
+  *swapped = it->second.swapped ? 1 : 0;
+  return PA_OK;
+}
+
+pa_status pa_bm_host_stats(const pa_bm* bm, int32_t* num_host_blocks, int32_t* num_host_free, int32_t* num_swapped,
+                           int64_t* swap_outs, int64_t* swap_ins) {
+  pa::clear_error();
+  if (bm == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm is NULL");
+  int32_t ns = 0;
+  for (const auto& kv : bm->seqs) ns += kv.second.swapped ? 1 : 0;
+  if (num_host_blocks) *num_host_blocks = bm->num_host_blocks;
+  if (num_host_free) *num_host_free = static_cast<int32_t>(bm->host_free.size());
+  if (num_swapped) *num_swapped = ns;
+  if (swap_outs) *swap_outs = bm->swap_outs;
+  if (swap_ins) *swap_ins = bm->swap_ins;
+  return PA_OK;
+}
+
+pa_status pa_bm_host_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity, int32_t* n) {
+  pa::clear_error();
+  if (bm == nullptr || n == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or n is NULL");
+  const int32_t k = static_cast<int32_t>(bm->host_free.size());
+  if (k > 0 && (out == nullptr || capacity < k))
+    return fail(PA_ERR_INVALID_ARGUMENT, "capacity %d < %d host free blocks", capacity, k);
+  for (int32_t i = 0; i < k; ++i) out[i] = bm->host_free[i];
+  *n = k;
+  return PA_OK;
 }
 
 pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out) {

@@ -115,15 +115,26 @@ struct SrcF32 {
 // stores) so several loads are in flight.
 constexpr int kCopyUnroll = 4;
 
-__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const int32_t* __restrict__ pairs, void* k_pool,
-                                                               void* v_pool, int64_t block_stride_bytes,
-                                                               int32_t block_vecs, int32_t num_blocks) {
+// Source and destination pools may differ (pa_copy_blocks_between, e.g. a
+// device pool and a pinned host pool, which the device reads and writes
+// directly); they have the same block geometry, possibly other strides.
+struct CopyPools {
+  const char* src_k;
+  const char* src_v;
+  char* dst_k;
+  char* dst_v;
+  int64_t src_stride_bytes, dst_stride_bytes;
+  int32_t src_blocks, dst_blocks;
+  int32_t block_vecs;  // 16-byte vectors of K (and of V) per block
+};
+
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const int32_t* __restrict__ pairs, const CopyPools c) {
   const int32_t src = pairs[2 * blockIdx.x];
   const int32_t dst = pairs[2 * blockIdx.x + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  char* base = static_cast<char*>(blockIdx.y == 0 ? k_pool : v_pool);
-  const u32x4* s = reinterpret_cast<const u32x4*>(base + src * block_stride_bytes);
-  u32x4* d = reinterpret_cast<u32x4*>(base + dst * block_stride_bytes);
+  if (src < 0 || src >= c.src_blocks || dst < 0 || dst >= c.dst_blocks) return;
+  const u32x4* s = reinterpret_cast<const u32x4*>((blockIdx.y == 0 ? c.src_k : c.src_v) + src * c.src_stride_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>((blockIdx.y == 0 ? c.dst_k : c.dst_v) + dst * c.dst_stride_bytes);
+  const int32_t block_vecs = c.block_vecs;
   for (int32_t i0 = threadIdx.x; i0 < block_vecs; i0 += kThreads * kCopyUnroll) {
     u32x4 v[kCopyUnroll];
 #pragma unroll
@@ -147,6 +158,29 @@ int elem_bytes(pa_dtype t) {
     case PA_FP8_E4M3: return 1;
   }
   return 0;
+}
+
+// whole-block copies src[pairs[i][0]] -> dst[pairs[i][1]], K and V
+// (descriptors validated by the caller)
+pa_status launch_copy(const pa_kv_cache* dst, const pa_kv_cache* src, const int32_t* pairs, int32_t N,
+                      hipStream_t stream) {
+  const int eb = elem_bytes(src->dtype);
+  const int64_t block_bytes = static_cast<int64_t>(src->block_size) * src->num_kv_heads * src->head_dim * eb;
+  if (block_bytes / 16 > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "block too large");
+  CopyPools c{};
+  c.src_k = static_cast<const char*>(src->k);
+  c.src_v = static_cast<const char*>(src->v);
+  c.dst_k = static_cast<char*>(dst->k);
+  c.dst_v = static_cast<char*>(dst->v);
+  c.src_stride_bytes = src->block_stride * eb;
+  c.dst_stride_bytes = dst->block_stride * eb;
+  c.src_blocks = src->num_blocks;
+  c.dst_blocks = dst->num_blocks;
+  c.block_vecs = static_cast<int32_t>(block_bytes / 16);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(N), 2), dim3(kThreads), 0, stream, pairs, c);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_DEVICE, "copy_blocks launch: %s", hipGetErrorString(e));
+  return PA_OK;
 }
 
 }  // namespace
@@ -265,15 +299,36 @@ pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* pairs, int32_t
     for (int32_t b = 0; b < cache->num_blocks; ++b)
       if (is_dst[b] && is_src[b]) return fail(PA_ERR_INVALID_ARGUMENT, "block %d is both a source and a destination", b);
   }
-  const int eb = pa::elem_bytes(cache->dtype);
-  const int64_t block_bytes = static_cast<int64_t>(cache->block_size) * cache->num_kv_heads * cache->head_dim * eb;
-  if (block_bytes / 16 > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "block too large");
-  hipLaunchKernelGGL(pa::copy_blocks_kernel, dim3(static_cast<uint32_t>(N), 2), dim3(pa::kThreads), 0,
-                     static_cast<hipStream_t>(stream), pairs, cache->k, cache->v, cache->block_stride * eb,
-                     static_cast<int32_t>(block_bytes / 16), cache->num_blocks);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PA_ERR_DEVICE, "copy_blocks launch: %s", hipGetErrorString(e));
-  return PA_OK;
+  return pa::launch_copy(cache, cache, pairs, N, static_cast<hipStream_t>(stream));
+}
+
+pa_status pa_copy_blocks_between(const pa_kv_cache* dst, const pa_kv_cache* src, const int32_t* pairs, int32_t N,
+                                 void* stream) {
+  pa::clear_error();
+  pa_status st = pa::validate_cache(dst);
+  if (st != PA_OK) return st;
+  st = pa::validate_cache(src);
+  if (st != PA_OK) return st;
+  if (dst->block_size != src->block_size || dst->num_kv_heads != src->num_kv_heads ||
+      dst->head_dim != src->head_dim || dst->dtype != src->dtype || dst->v_layout != src->v_layout)
+    return fail(PA_ERR_INVALID_ARGUMENT, "the two pools differ in block size, heads, head_dim, dtype or V layout");
+  if (N < 0) return fail(PA_ERR_INVALID_ARGUMENT, "N = %d is negative", N);
+  if (N == 0) return PA_OK;
+  if (pairs == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "pairs is NULL");
+  if (pa::debug_enabled()) {
+    std::vector<int32_t> h(2 * static_cast<size_t>(N));
+    if (hipMemcpy(h.data(), pairs, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(PA_ERR_DEVICE, "PA_DEBUG: reading pairs failed");
+    std::vector<char> is_dst(dst->num_blocks, 0);
+    for (int32_t i = 0; i < N; ++i) {
+      const int32_t a = h[2 * i], b = h[2 * i + 1];
+      if (a < 0 || a >= src->num_blocks || b < 0 || b >= dst->num_blocks)
+        return fail(PA_ERR_INVALID_ARGUMENT, "pair %d = (%d, %d) outside the pools", i, a, b);
+      if (is_dst[b]) return fail(PA_ERR_INVALID_ARGUMENT, "block %d is the destination of two pairs", b);
+      is_dst[b] = 1;
+    }
+  }
+  return pa::launch_copy(dst, src, pairs, N, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

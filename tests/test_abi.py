@@ -112,6 +112,81 @@ def test_block_manager_matches_model(ops, bs, nb, seed):
         assert t_lib.tolist() == t_mod and l_lib.tolist() == l_mod
 
 
+_swap_ops = st.lists(
+    st.one_of(
+        st.tuples(st.just("alloc"), st.integers(0, 5), st.integers(0, 20)),
+        st.tuples(st.just("fork"), st.integers(0, 5), st.integers(0, 5)),
+        st.tuples(st.just("free"), st.integers(0, 5), st.just(0)),
+        st.tuples(st.just("out"), st.integers(0, 5), st.just(0)),
+        st.tuples(st.just("in"), st.integers(0, 5), st.just(0)),
+    ),
+    max_size=60,
+)
+
+
+@settings(max_examples=300, deadline=None)
+@given(ops=_swap_ops, bs=st.sampled_from([1, 4, 16]), nb=st.integers(1, 30), nh=st.integers(0, 30),
+       seed=st.integers(0, 2 ** 16))
+def test_block_manager_swapping_matches_model(ops, bs, nb, nh, seed):
+    """Swap-out / swap-in against the model: pairs, tables (host ids while
+    swapped), refcounts, both free stacks, swap states, all-or-nothing
+    failures, and the operations a swapped sequence refuses."""
+    order = np.random.default_rng(seed).permutation(nb).tolist()
+    bm = pa.BlockManager(nb, bs, order)
+    m = A.BlockAllocatorModel(nb, bs, order)
+    bm.set_host_pool(nh)
+    m.set_host_pool(nh)
+    for op in ops:
+        if op[0] == "alloc":
+            got, want = _run(lambda: bm.alloc(op[1], op[2]), lambda: m.alloc(op[1], op[2]))
+            if got is not None:
+                assert got[0].tolist() == want[0] and got[1] == want[1]
+        elif op[0] == "fork":
+            _run(lambda: bm.fork(op[1], op[2]), lambda: m.fork(op[1], op[2]))
+        elif op[0] == "free":
+            _run(lambda: bm.free(op[1]), lambda: m.free(op[1]))
+        else:
+            f_lib = bm.swap_out if op[0] == "out" else bm.swap_in
+            f_mod = m.swap_out if op[0] == "out" else m.swap_in
+            got, want = _run(lambda: f_lib(op[1]), lambda: f_mod(op[1]))
+            if got is not None:
+                assert [tuple(p) for p in got.tolist()] == want
+        _same_state(bm, m)
+        assert bm.host_free_stack() == m.host_free_stack
+        assert bm.host_stats() == m.host_stats()
+        for s in m.seqs():
+            assert bm.is_swapped(s) == m.is_swapped(s)
+    resident = [s for s in m.seqs() if not m.is_swapped(s)]
+    if resident:
+        t_lib, l_lib = bm.pack(resident, max_blocks=64, pad=-7)
+        t_mod, l_mod = m.pack(resident, 64, -7)
+        assert t_lib.tolist() == t_mod and l_lib.tolist() == l_mod
+
+
+def test_swapped_sequences_refuse_other_operations():
+    bm = pa.BlockManager(8, 4)
+    bm.set_host_pool(8)
+    bm.alloc(1, 10)
+    bm.fork(1, 2)
+    pairs = bm.swap_out(1)
+    assert pairs.tolist() == [[0, 0], [1, 1], [2, 2]] and bm.refcounts()[:3] == [1, 1, 1]
+    for call in (lambda: bm.alloc(1, 1), lambda: bm.fork(1, 3), lambda: bm.pack([1], 4),
+                 lambda: bm.swap_out(1), lambda: bm.shared_prefixes([1, 2], 4)):
+        with pytest.raises(pa.InvalidArgument):
+            call()
+    with pytest.raises(pa.InvalidArgument):
+        bm.swap_in(2)  # resident
+    with pytest.raises(pa.InvalidArgument):
+        bm.set_host_pool(4)  # host blocks in use
+    back = bm.swap_in(1)
+    assert [h for h, _ in back.tolist()] == [0, 1, 2]
+    assert bm.host_stats() == dict(num_host_blocks=8, num_host_free=8, num_swapped=0, swap_outs=1, swap_ins=1)
+    bm.set_host_pool(2)
+    with pytest.raises(pa.OutOfBlocks):
+        bm.swap_out(1)  # 3 blocks, 2 host blocks: nothing changes
+    assert not bm.is_swapped(1) and bm.host_free_stack() == [1, 0]
+
+
 def test_worked_examples_through_the_library():
     # "PagedAttention" LLM note, 最小模型: table 0->7, 1->2, 2->9
     bm = pa.BlockManager(10, 16, [7, 2, 9, 0, 1, 3, 4, 5, 6, 8])
