@@ -203,6 +203,55 @@ pa_status pa_bm_host_stats(const pa_bm* bm, int32_t* num_host_blocks, int32_t* n
  * int32[capacity]; *n receives the count. */
 pa_status pa_bm_host_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity, int32_t* n);
 
+/* ------------------------------------------------------------------------
+ * Prefix caching across requests ([course] §4: sharing across users needs
+ * an identical prefix and prefix caching enabled; §11: enable prefix
+ * caching for common prompts; §9: RadixAttention extends block sharing into
+ * a prefix tree).
+ *
+ * With the cache on, every full block a prompt fills through
+ * pa_alloc_prompt is registered under a 64-bit hash of the token prefix up
+ * to the block's end (the hash chains block by block), with its own tokens
+ * and its parent's hash. A registered block whose refcount drops to 0 keeps
+ * its K/V and becomes evictable (an LRU; a released sequence's registered
+ * blocks enter it in reverse logical order, so the first blocks of a
+ * prefix go last). Every allocation (pa_alloc, pa_alloc_prompt, copy-on-
+ * write, pa_swap_in) takes the free stack first, then evicts the least
+ * recently released cached block (unregistering it). Blocks filled by
+ * decode growth are not registered (their tokens are unknown here).
+ * ---------------------------------------------------------------------- */
+
+/* Turn the prefix cache on or off (off by default). Turning it off forgets
+ * every registration; evictable blocks go onto the free stack in LRU
+ * order. */
+pa_status pa_bm_set_prefix_cache(pa_bm* bm, int32_t enable);
+
+/* Create sequence seq_id for a prompt of n tokens (token_ids: host
+ * int32[n]). Its leading full blocks are reused from the cache while hash,
+ * parent hash and tokens all match (refcount + 1, taken out of the LRU);
+ * the rest are allocated, and its new full blocks registered (a hash
+ * already registered keeps its block). slot_mapping: host int64[n], the
+ * slot of every token; *num_cached = tokens covered by reused blocks — the
+ * caller writes K/V only for tokens num_cached .. n - 1. All-or-nothing:
+ * PA_ERR_OUT_OF_BLOCKS (free + evictable blocks, not counting reused ones,
+ * are too few), PA_ERR_SEQ_EXISTS, PA_ERR_INVALID_ARGUMENT. With the cache
+ * off it is pa_alloc of a new sequence and *num_cached = 0. A 64-bit hash
+ * collision between different prefixes (probability ~2^-64 per lookup)
+ * would share a wrong block; the block's own tokens and its parent hash are
+ * compared exactly. */
+pa_status pa_alloc_prompt(pa_bm* bm, int64_t seq_id, const int32_t* token_ids, int32_t n, int64_t* slot_mapping,
+                          int32_t* num_cached);
+
+/* Registered blocks, evictable ones, and the numbers of full prompt blocks
+ * found / not found in the cache and of evictions so far (any output may
+ * be NULL). */
+pa_status pa_bm_prefix_cache_stats(const pa_bm* bm, int32_t* num_cached_blocks, int32_t* num_evictable,
+                                   int64_t* hits, int64_t* misses, int64_t* evictions);
+
+/* Evictable blocks, the next to be evicted first: host int32[capacity];
+ * *n receives the count. */
+pa_status pa_bm_evictable(const pa_bm* bm, int32_t* out, int32_t capacity, int32_t* n);
+
 /* Groups of the batch rows seq_ids[0..n) whose block tables begin with the
  * same physical blocks — forks of one prompt ([course] §2 "The bonus":
  * parallel samples share the prompt's blocks; [note] prefix-sharing

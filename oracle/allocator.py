@@ -38,6 +38,19 @@ Readings where the pages leave the choice open:
   (host, device) pairs, and pushes the host blocks back in logical order.
   A swapped sequence can only be swapped in, freed (its host blocks go back
   on the host stack) or queried. Both are all-or-nothing.
+* Prefix caching ([course] §4: sharing across users needs an identical
+  prefix and prefix caching enabled; §11: enable it for common prompts):
+  with the cache on, each full block a prompt fills is registered under its
+  whole token prefix (here the exact prefix itself is the key). A prompt
+  reuses registered blocks for its leading full blocks while the prefixes
+  match; its other full blocks are registered unless their prefix already
+  is. A registered block whose refcount drops to 0 keeps its data in an
+  evictable LRU, which a released sequence's registered blocks enter in
+  reverse logical order; unregistered ones go onto the free stack in
+  logical order as before. Every allocation pops the free stack first, then
+  evicts (and unregisters) the LRU's oldest block. Turning the cache off
+  forgets all registrations and moves the LRU, oldest first, onto the free
+  stack.
 * A batch of allocations is all-or-nothing and may not name a sequence
   twice; requests are applied in the given order.
 
@@ -106,6 +119,13 @@ class _State:
         self.swapped: set = set()
         self.swap_outs = 0
         self.swap_ins = 0
+        self.prefix_cache = False
+        self.cached: Dict[tuple, int] = {}  # token prefix -> block
+        self.key_of: Dict[int, tuple] = {}   # block -> its registered prefix
+        self.lru: List[int] = []             # front = evicted next
+        self.hits = 0
+        self.misses = 0
+        self.evictions = 0
 
 
 class BlockAllocatorModel:
@@ -165,9 +185,20 @@ class BlockAllocatorModel:
     # -- operations ----------------------------------------------------
     @staticmethod
     def _pop(st: _State) -> int:
-        if not st.stack:
+        if st.stack:
+            return st.stack.pop()
+        if not st.lru:
             raise OutOfBlocks("pool exhausted")
-        return st.stack.pop()
+        blk = st.lru.pop(0)
+        del st.cached[st.key_of.pop(blk)]
+        st.evictions += 1
+        return blk
+
+    @staticmethod
+    def _release(st: _State, dead: List[int]) -> None:
+        """Blocks (logical order) whose refcount just reached 0."""
+        st.stack.extend(b for b in dead if b not in st.key_of)
+        st.lru.extend(b for b in reversed(dead) if b in st.key_of)
 
     def _grow(self, st: _State, seq: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
         bs = self.block_size
@@ -241,10 +272,12 @@ class BlockAllocatorModel:
             self.st.host_stack.extend(self.st.tables.pop(seq))
             self.st.swapped.discard(seq)
         else:
+            dead = []
             for blk in self.st.tables.pop(seq):
                 self.st.refcnt[blk] -= 1
                 if self.st.refcnt[blk] == 0:
-                    self.st.stack.append(blk)
+                    dead.append(blk)
+            self._release(self.st, dead)
         del self.st.lens[seq]
 
     def set_host_pool(self, num_host_blocks: int) -> None:
@@ -265,13 +298,15 @@ class BlockAllocatorModel:
         if len(table) > len(self.st.host_stack):
             raise OutOfBlocks("host pool exhausted")
         pairs = []
+        dead = []
         for i, blk in enumerate(table):
             h = self.st.host_stack.pop()
             pairs.append((blk, h))
             table[i] = h
             self.st.refcnt[blk] -= 1
             if self.st.refcnt[blk] == 0:
-                self.st.stack.append(blk)
+                dead.append(blk)
+        self._release(self.st, dead)
         self.st.swapped.add(seq)
         self.st.swap_outs += 1
         return pairs
@@ -284,11 +319,11 @@ class BlockAllocatorModel:
         if seq not in self.st.swapped:
             raise InvalidArgument("not swapped out")
         table = self.st.tables[seq]
-        if len(table) > len(self.st.stack):
+        if len(table) > len(self.st.stack) + len(self.st.lru):
             raise OutOfBlocks("pool exhausted")
         pairs = []
         for i, h in enumerate(table):
-            blk = self.st.stack.pop()
+            blk = self._pop(self.st)
             self.st.refcnt[blk] = 1
             pairs.append((h, blk))
             table[i] = blk
@@ -296,6 +331,65 @@ class BlockAllocatorModel:
         self.st.swapped.discard(seq)
         self.st.swap_ins += 1
         return pairs
+
+    # -- prefix caching -------------------------------------------------
+    def set_prefix_cache(self, enable: bool) -> None:
+        if not enable and self.st.prefix_cache:
+            self.st.stack.extend(self.st.lru)
+            self.st.lru = []
+            self.st.cached = {}
+            self.st.key_of = {}
+        self.st.prefix_cache = bool(enable)
+
+    def alloc_prompt(self, seq: int, tokens: Sequence[int]) -> Tuple[List[int], int]:
+        """New sequence ``seq`` for a prompt; (slots of all tokens, tokens
+        covered by reused cached blocks)."""
+        if seq in self.st.tables:
+            raise SeqExists(seq)
+        bs = self.block_size
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        nfull = n // bs
+        st = copy.deepcopy(self.st)
+        hit = []
+        if st.prefix_cache:
+            for i in range(nfull):
+                key = tuple(tokens[: (i + 1) * bs])
+                if key not in st.cached:
+                    break
+                hit.append(st.cached[key])
+        need = blocks_for(n, bs) - len(hit)
+        if need > len(st.stack) + len(st.lru) - sum(1 for b in hit if b in st.lru):
+            raise OutOfBlocks("pool exhausted")
+        table = []
+        for b in hit:
+            if b in st.lru:
+                st.lru.remove(b)
+            st.refcnt[b] += 1
+            table.append(b)
+        for i in range(len(hit), blocks_for(n, bs)):
+            blk = self._pop(st)
+            st.refcnt[blk] = 1
+            table.append(blk)
+            key = tuple(tokens[: (i + 1) * bs])
+            if st.prefix_cache and i < nfull and key not in st.cached:
+                st.cached[key] = blk
+                st.key_of[blk] = key
+        st.tables[seq] = table
+        st.lens[seq] = n
+        if st.prefix_cache:
+            st.hits += len(hit)
+            st.misses += nfull - len(hit)
+        self.st = st
+        return [table[t // bs] * bs + t % bs for t in range(n)], len(hit) * bs
+
+    def prefix_cache_stats(self) -> dict:
+        return dict(num_cached_blocks=len(self.st.cached), num_evictable=len(self.st.lru), hits=self.st.hits,
+                    misses=self.st.misses, evictions=self.st.evictions)
+
+    @property
+    def evictable(self) -> List[int]:
+        return list(self.st.lru)
 
     def pack(self, seqs: Sequence[int], max_blocks: int, pad: int = -1):
         """(tables [n][max_blocks] padded with ``pad``, context lengths [n])."""

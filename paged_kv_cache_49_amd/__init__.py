@@ -239,6 +239,34 @@ class BlockManager:
         smin = int(shared_len[:n].min()) if n else 0
         return SharedPrefixes(group_offsets, group_members, shared_len, ng.value, gmax.value, smax.value, smin)
 
+    # -- prefix caching -------------------------------------------------
+    def set_prefix_cache(self, enable: bool) -> None:
+        _check(lib().pa_bm_set_prefix_cache(self._h, 1 if enable else 0))
+
+    def alloc_prompt(self, seq_id: int, token_ids) -> Tuple[np.ndarray, int]:
+        """pa_alloc_prompt: (slots of all tokens, tokens covered by reused
+        cached blocks)."""
+        toks = _host_i32(token_ids)
+        slots = np.empty(max(len(toks), 1), np.int64)
+        nc = ctypes.c_int32()
+        _check(lib().pa_alloc_prompt(self._h, int(seq_id), _ptr(toks) if len(toks) else None, len(toks),
+                                     _ptr(slots), ctypes.byref(nc)))
+        return slots[: len(toks)], nc.value
+
+    def prefix_cache_stats(self) -> dict:
+        a, b = ctypes.c_int32(), ctypes.c_int32()
+        c, d, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().pa_bm_prefix_cache_stats(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                              ctypes.byref(d), ctypes.byref(e)))
+        return dict(num_cached_blocks=a.value, num_evictable=b.value, hits=c.value, misses=d.value,
+                    evictions=e.value)
+
+    def evictable(self) -> list:
+        out = np.empty(self.num_blocks, np.int32)
+        n = ctypes.c_int32()
+        _check(lib().pa_bm_evictable(self._h, _ptr(out), self.num_blocks, ctypes.byref(n)))
+        return out[: n.value].tolist()
+
     # -- swapping (host pool) -------------------------------------------
     def set_host_pool(self, num_host_blocks: int) -> None:
         _check(lib().pa_bm_set_host_pool(self._h, int(num_host_blocks)))

@@ -90,6 +90,10 @@ SIGNATURES = {
     "pa_bm_host_stats": (c_int, [_P, _I32P, _I32P, _I32P, POINTER(c_int64), POINTER(c_int64)]),
     "pa_bm_host_free_stack": (c_int, [_P, _P, c_int32, _I32P]),
     "pa_copy_blocks_between": (c_int, [POINTER(PaKvCache), POINTER(PaKvCache), _P, c_int32, _P]),
+    "pa_bm_set_prefix_cache": (c_int, [_P, c_int32]),
+    "pa_alloc_prompt": (c_int, [_P, c_int64, _P, c_int32, _P, _I32P]),
+    "pa_bm_prefix_cache_stats": (c_int, [_P, _I32P, _I32P, POINTER(c_int64), POINTER(c_int64), POINTER(c_int64)]),
+    "pa_bm_evictable": (c_int, [_P, _P, c_int32, _I32P]),
     "pa_bm_shared_prefixes": (c_int, [_P, _P, c_int32, c_int32, _P, _P, _P, _I32P, _I32P, _I32P]),
     "pa_reshape_and_cache": (c_int, [POINTER(PaKvCache), _P, _P, c_int, _P, c_int32, _P]),
     "pa_copy_blocks": (c_int, [POINTER(PaKvCache), _P, c_int32, _P]),

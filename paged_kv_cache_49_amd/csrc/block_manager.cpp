@@ -22,6 +22,19 @@
 // pa_copy_blocks_between using the reported pairs. A swapped sequence can
 // only be swapped in, freed or queried.
 //
+// Prefix caching ([course] §4: prefix sharing across requests needs an
+// identical prefix and prefix caching enabled; §11: enable prefix caching
+// for common prompts; §9: RadixAttention extends block sharing into a
+// prefix tree): when enabled, every full block a prompt fills through
+// pa_alloc_prompt is registered under a 64-bit hash of the whole token
+// prefix up to its end (chained block by block) together with its own
+// tokens and its parent's hash. A later prompt walks its full blocks and
+// reuses registered ones as long as hash, parent and tokens all match. A
+// registered block whose refcount drops to 0 keeps its data and joins an
+// evictable LRU (a released sequence's blocks join in reverse logical order,
+// so a prefix's first blocks are evicted last); allocation takes the free
+// stack first and then evicts the least recently released cached block.
+//
 // Every mutating entry point first plans the whole request against the
 // current state (blocks needed, including copy-on-write copies, checked
 // against the free count), and only then applies it, so a failure leaves
@@ -29,6 +42,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstring>
+#include <list>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -53,12 +67,52 @@ struct pa_bm {
   std::vector<int32_t> host_free;  // back() is popped next
   int64_t swap_outs = 0;
   int64_t swap_ins = 0;
+  // prefix cache
+  bool prefix_cache = false;
+  std::unordered_map<uint64_t, int32_t> cached;  // prefix hash -> block
+  std::vector<char> registered;                   // per block
+  std::vector<uint64_t> block_hash, block_parent;
+  std::vector<std::vector<int32_t>> block_tokens;
+  std::list<int32_t> lru;  // evictable registered blocks (refcount 0), front = evicted next
+  std::vector<std::list<int32_t>::iterator> lru_pos;
+  std::vector<char> in_lru;
+  int64_t cache_hits = 0, cache_misses = 0, evictions = 0;
 
   int64_t blocks_for(int64_t len) const { return (len + block_size - 1) / block_size; }
+  // blocks an allocation can take: free ones, then evictable cached ones
+  int64_t available() const { return static_cast<int64_t>(free_stack.size()) + static_cast<int64_t>(lru.size()); }
+  void unregister(int32_t b) {
+    cached.erase(block_hash[b]);
+    registered[b] = 0;
+    block_tokens[b].clear();
+  }
+  void lru_remove(int32_t b) {
+    lru.erase(lru_pos[b]);
+    in_lru[b] = 0;
+  }
   int32_t pop() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+    if (!free_stack.empty()) {
+      int32_t b = free_stack.back();
+      free_stack.pop_back();
+      return b;
+    }
+    const int32_t b = lru.front();  // callers checked available()
+    lru_remove(b);
+    unregister(b);
+    ++evictions;
     return b;
+  }
+  // the blocks of `blocks` (logical order) whose refcount just reached 0:
+  // unregistered ones onto the free stack in logical order, registered ones
+  // into the LRU in reverse logical order
+  void release(const std::vector<int32_t>& dead) {
+    for (int32_t b : dead)
+      if (!registered[b]) free_stack.push_back(b);
+    for (auto it = dead.rbegin(); it != dead.rend(); ++it)
+      if (registered[*it]) {
+        lru_pos[*it] = lru.insert(lru.end(), *it);
+        in_lru[*it] = 1;
+      }
   }
 };
 
@@ -101,9 +155,9 @@ pa_status plan_and_apply(pa_bm* bm, const int64_t* ids, int32_t n, const int32_t
       }
     }
   }
-  if (need > static_cast<int64_t>(bm->free_stack.size()))
-    return fail(PA_ERR_OUT_OF_BLOCKS, "request needs %lld blocks, %zu free of %d", (long long)need,
-                bm->free_stack.size(), bm->num_blocks);
+  if (need > bm->available())
+    return fail(PA_ERR_OUT_OF_BLOCKS, "request needs %lld blocks, %lld free of %d", (long long)need,
+                (long long)bm->available(), bm->num_blocks);
 
   // ---- apply: cannot fail from here on (capacity reserved up front)
   int32_t ncow = 0;
@@ -152,6 +206,12 @@ pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* in
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
   bm->refcnt.assign(num_blocks, 0);
+  bm->registered.assign(num_blocks, 0);
+  bm->block_hash.assign(num_blocks, 0);
+  bm->block_parent.assign(num_blocks, 0);
+  bm->block_tokens.resize(num_blocks);
+  bm->lru_pos.resize(num_blocks);
+  bm->in_lru.assign(num_blocks, 0);
   bm->free_stack.resize(num_blocks);
   if (initial_free_order != nullptr) {
     std::vector<char> seen(num_blocks, 0);
@@ -213,8 +273,10 @@ pa_status pa_free(pa_bm* bm, int64_t seq_id) {
     for (int32_t h : it->second.blocks) bm->host_free.push_back(h);
   } else {
     bm->free_stack.reserve(bm->num_blocks);
+    std::vector<int32_t> dead;
     for (int32_t b : it->second.blocks)
-      if (--bm->refcnt[b] == 0) bm->free_stack.push_back(b);
+      if (--bm->refcnt[b] == 0) dead.push_back(b);
+    bm->release(dead);
   }
   bm->seqs.erase(it);
   return PA_OK;
@@ -380,6 +442,7 @@ pa_status pa_swap_out(pa_bm* bm, int64_t seq_id, int32_t* pairs, int32_t capacit
                 bm->num_host_blocks);
   PA_GUARD_BEGIN
   bm->free_stack.reserve(bm->num_blocks);
+  std::vector<int32_t> dead;
   for (int32_t i = 0; i < n; ++i) {
     const int32_t b = sq.blocks[i];
     const int32_t h = bm->host_free.back();
@@ -387,8 +450,9 @@ pa_status pa_swap_out(pa_bm* bm, int64_t seq_id, int32_t* pairs, int32_t capacit
     pairs[2 * i] = b;
     pairs[2 * i + 1] = h;
     sq.blocks[i] = h;
-    if (--bm->refcnt[b] == 0) bm->free_stack.push_back(b);
+    if (--bm->refcnt[b] == 0) dead.push_back(b);
   }
+  bm->release(dead);
   sq.swapped = true;
   ++bm->swap_outs;
   *num_pairs = n;
@@ -406,8 +470,8 @@ pa_status pa_swap_in(pa_bm* bm, int64_t seq_id, int32_t* pairs, int32_t capacity
   const int32_t n = static_cast<int32_t>(sq.blocks.size());
   if (n > 0 && (pairs == nullptr || capacity < n))
     return fail(PA_ERR_INVALID_ARGUMENT, "pairs holds %d pairs, %d needed", capacity, n);
-  if (n > static_cast<int32_t>(bm->free_stack.size()))
-    return fail(PA_ERR_OUT_OF_BLOCKS, "swap-in needs %d blocks, %zu free of %d", n, bm->free_stack.size(),
+  if (n > bm->available())
+    return fail(PA_ERR_OUT_OF_BLOCKS, "swap-in needs %d blocks, %lld free of %d", n, (long long)bm->available(),
                 bm->num_blocks);
   PA_GUARD_BEGIN
   bm->host_free.reserve(bm->num_host_blocks);
@@ -457,6 +521,132 @@ pa_status pa_bm_host_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity,
   if (k > 0 && (out == nullptr || capacity < k))
     return fail(PA_ERR_INVALID_ARGUMENT, "capacity %d < %d host free blocks", capacity, k);
   for (int32_t i = 0; i < k; ++i) out[i] = bm->host_free[i];
+  *n = k;
+  return PA_OK;
+}
+
+namespace {
+
+// 64-bit mix of a token into a running prefix hash (splitmix64 finaliser)
+uint64_t mix_token(uint64_t h, int32_t t) {
+  uint64_t z = h + 0x9E3779B97F4A7C15ull * (static_cast<uint64_t>(static_cast<uint32_t>(t)) + 1ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+}  // namespace
+
+pa_status pa_bm_set_prefix_cache(pa_bm* bm, int32_t enable) {
+  pa::clear_error();
+  if (bm == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm is NULL");
+  PA_GUARD_BEGIN
+  if (!enable && bm->prefix_cache) {
+    // forget every registration; evictable blocks become free (in LRU order)
+    for (int32_t b : bm->lru) {
+      bm->in_lru[b] = 0;
+      bm->free_stack.push_back(b);
+    }
+    bm->lru.clear();
+    for (int32_t b = 0; b < bm->num_blocks; ++b)
+      if (bm->registered[b]) bm->unregister(b);
+  }
+  bm->prefix_cache = enable != 0;
+  return PA_OK;
+  PA_GUARD_END
+}
+
+pa_status pa_alloc_prompt(pa_bm* bm, int64_t seq_id, const int32_t* token_ids, int32_t n, int64_t* slot_mapping,
+                          int32_t* num_cached) {
+  pa::clear_error();
+  if (bm == nullptr || num_cached == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or num_cached is NULL");
+  if (n < 0) return fail(PA_ERR_INVALID_ARGUMENT, "n = %d is negative", n);
+  if (n > 0 && (token_ids == nullptr || slot_mapping == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "token_ids or slot_mapping is NULL");
+  if (bm->seqs.count(seq_id)) return fail(PA_ERR_SEQ_EXISTS, "sequence %lld is already live", (long long)seq_id);
+  const int32_t bs = bm->block_size;
+  const int32_t nfull = n / bs;
+  PA_GUARD_BEGIN
+  // ---- plan: the longest run of registered leading blocks, then capacity
+  std::vector<uint64_t> key(nfull);
+  uint64_t h = 0;
+  for (int32_t i = 0; i < nfull; ++i) {
+    for (int32_t t = i * bs; t < (i + 1) * bs; ++t) h = mix_token(h, token_ids[t]);
+    key[i] = h;
+  }
+  std::vector<int32_t> hit;
+  int64_t hits_in_lru = 0;
+  if (bm->prefix_cache) {
+    uint64_t parent = 0;
+    for (int32_t i = 0; i < nfull; ++i) {
+      auto f = bm->cached.find(key[i]);
+      if (f == bm->cached.end()) break;
+      const int32_t b = f->second;
+      if (bm->block_parent[b] != parent ||
+          !std::equal(bm->block_tokens[b].begin(), bm->block_tokens[b].end(), token_ids + static_cast<int64_t>(i) * bs))
+        break;
+      hit.push_back(b);
+      hits_in_lru += bm->in_lru[b];
+      parent = key[i];
+    }
+  }
+  const int32_t nhit = static_cast<int32_t>(hit.size());
+  const int64_t need = bm->blocks_for(n) - nhit;
+  if (need > bm->available() - hits_in_lru)
+    return fail(PA_ERR_OUT_OF_BLOCKS, "prompt needs %lld new blocks, %lld free of %d", (long long)need,
+                (long long)(bm->available() - hits_in_lru), bm->num_blocks);
+  // ---- apply
+  pa_bm::Seq sq;
+  sq.len = n;
+  sq.blocks.reserve(static_cast<size_t>(bm->blocks_for(n)));
+  for (int32_t b : hit) {
+    if (bm->in_lru[b]) bm->lru_remove(b);
+    ++bm->refcnt[b];
+    sq.blocks.push_back(b);
+  }
+  for (int64_t i = nhit; i < bm->blocks_for(n); ++i) {
+    const int32_t b = bm->pop();
+    bm->refcnt[b] = 1;
+    sq.blocks.push_back(b);
+    if (bm->prefix_cache && i < nfull && !bm->cached.count(key[i])) {
+      bm->cached.emplace(key[i], b);
+      bm->registered[b] = 1;
+      bm->block_hash[b] = key[i];
+      bm->block_parent[b] = i > 0 ? key[i - 1] : 0;
+      bm->block_tokens[b].assign(token_ids + i * bs, token_ids + (i + 1) * bs);
+    }
+  }
+  for (int32_t t = 0; t < n; ++t) slot_mapping[t] = static_cast<int64_t>(sq.blocks[t / bs]) * bs + t % bs;
+  bm->seqs.emplace(seq_id, std::move(sq));
+  if (bm->prefix_cache) {
+    bm->cache_hits += nhit;
+    bm->cache_misses += nfull - nhit;
+  }
+  *num_cached = nhit * bs;
+  return PA_OK;
+  PA_GUARD_END
+}
+
+pa_status pa_bm_prefix_cache_stats(const pa_bm* bm, int32_t* num_cached_blocks, int32_t* num_evictable,
+                                   int64_t* hits, int64_t* misses, int64_t* evictions) {
+  pa::clear_error();
+  if (bm == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm is NULL");
+  if (num_cached_blocks) *num_cached_blocks = static_cast<int32_t>(bm->cached.size());
+  if (num_evictable) *num_evictable = static_cast<int32_t>(bm->lru.size());
+  if (hits) *hits = bm->cache_hits;
+  if (misses) *misses = bm->cache_misses;
+  if (evictions) *evictions = bm->evictions;
+  return PA_OK;
+}
+
+pa_status pa_bm_evictable(const pa_bm* bm, int32_t* out, int32_t capacity, int32_t* n) {
+  pa::clear_error();
+  if (bm == nullptr || n == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or n is NULL");
+  const int32_t k = static_cast<int32_t>(bm->lru.size());
+  if (k > 0 && (out == nullptr || capacity < k))
+    return fail(PA_ERR_INVALID_ARGUMENT, "capacity %d < %d evictable blocks", capacity, k);
+  int32_t i = 0;
+  for (int32_t b : bm->lru) out[i++] = b;
   *n = k;
   return PA_OK;
 }

@@ -163,6 +163,87 @@ def test_block_manager_swapping_matches_model(ops, bs, nb, nh, seed):
         assert t_lib.tolist() == t_mod and l_lib.tolist() == l_mod
 
 
+_BASES = [[(7 * i + 3 * b) % 5 for i in range(80)] for b in range(3)]  # prompts are prefixes of these
+
+_cache_ops = st.lists(
+    st.one_of(
+        st.tuples(st.just("prompt"), st.integers(0, 7), st.tuples(st.integers(0, 2), st.integers(0, 80))),
+        st.tuples(st.just("alloc"), st.integers(0, 7), st.integers(0, 12)),
+        st.tuples(st.just("fork"), st.integers(0, 7), st.integers(0, 7)),
+        st.tuples(st.just("free"), st.integers(0, 7), st.just(0)),
+        st.tuples(st.just("out"), st.integers(0, 7), st.just(0)),
+        st.tuples(st.just("in"), st.integers(0, 7), st.just(0)),
+        st.tuples(st.just("cache"), st.booleans(), st.just(0)),
+    ),
+    max_size=70,
+)
+
+
+@settings(max_examples=300, deadline=None)
+@given(ops=_cache_ops, bs=st.sampled_from([1, 4, 16]), nb=st.integers(1, 40), seed=st.integers(0, 2 ** 16))
+def test_prefix_cache_matches_model(ops, bs, nb, seed):
+    """Prompt allocation with the prefix cache against the model: reused
+    blocks, slots, cached token counts, registration, the evictable LRU,
+    eviction under pressure, and its interplay with growth, forks, copy-on-
+    write, swapping and freeing."""
+    order = np.random.default_rng(seed).permutation(nb).tolist()
+    bm = pa.BlockManager(nb, bs, order)
+    m = A.BlockAllocatorModel(nb, bs, order)
+    bm.set_host_pool(20)
+    m.set_host_pool(20)
+    bm.set_prefix_cache(True)
+    m.set_prefix_cache(True)
+    for op in ops:
+        if op[0] == "prompt":
+            toks = _BASES[op[2][0]][: op[2][1]]
+            got, want = _run(lambda: bm.alloc_prompt(op[1], toks), lambda: m.alloc_prompt(op[1], toks))
+            if got is not None:
+                assert got[0].tolist() == want[0] and got[1] == want[1]
+        elif op[0] == "alloc":
+            got, want = _run(lambda: bm.alloc(op[1], op[2]), lambda: m.alloc(op[1], op[2]))
+            if got is not None:
+                assert got[0].tolist() == want[0] and got[1] == want[1]
+        elif op[0] == "fork":
+            _run(lambda: bm.fork(op[1], op[2]), lambda: m.fork(op[1], op[2]))
+        elif op[0] == "free":
+            _run(lambda: bm.free(op[1]), lambda: m.free(op[1]))
+        elif op[0] == "cache":
+            bm.set_prefix_cache(op[1])
+            m.set_prefix_cache(op[1])
+        else:
+            f_lib = bm.swap_out if op[0] == "out" else bm.swap_in
+            f_mod = m.swap_out if op[0] == "out" else m.swap_in
+            got, want = _run(lambda: f_lib(op[1]), lambda: f_mod(op[1]))
+            if got is not None:
+                assert [tuple(p) for p in got.tolist()] == want
+        _same_state(bm, m)
+        assert bm.evictable() == m.evictable
+        assert bm.prefix_cache_stats() == m.prefix_cache_stats()
+        assert bm.host_free_stack() == m.host_free_stack
+
+
+def test_prefix_cache_reuse_across_requests():
+    """A finished request's prompt blocks serve the next request with the
+    same prefix; the reused blocks come back in logical order."""
+    bm = pa.BlockManager(16, 4)
+    bm.set_prefix_cache(True)
+    a = list(range(100, 114))                       # 3 full blocks + 2 tokens
+    slots_a, cached = bm.alloc_prompt(1, a)
+    assert cached == 0 and bm.prefix_cache_stats()["num_cached_blocks"] == 3
+    blocks_a = bm.seq_blocks(1)
+    bm.free(1)                                      # full blocks stay, evictable, last block first
+    assert bm.evictable() == blocks_a[:3][::-1]
+    b = a[:8] + [7, 7, 7, 7]                        # shares the first 2 blocks
+    slots_b, cached = bm.alloc_prompt(2, b)
+    assert cached == 8 and bm.seq_blocks(2)[:2] == blocks_a[:2]
+    assert slots_b[:8].tolist() == slots_a[:8].tolist()
+    st = bm.prefix_cache_stats()
+    assert st["hits"] == 2 and st["misses"] == 4 and st["num_evictable"] == 1
+    # pressure: 16 blocks, 3 held by seq 2, 1 evictable; a 13-block prompt evicts it
+    bm.alloc_prompt(3, list(range(200, 252)))
+    assert bm.prefix_cache_stats()["evictions"] == 1 and bm.evictable() == []
+
+
 def test_swapped_sequences_refuse_other_operations():
     bm = pa.BlockManager(8, 4)
     bm.set_host_pool(8)
