@@ -271,6 +271,28 @@ pa_status pa_bm_shared_prefixes(const pa_bm* bm, const int64_t* seq_ids, int32_t
                                 int32_t* num_groups, int32_t* max_group_size, int32_t* max_shared_len);
 
 pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out);
+
+/* KV memory use of the resident sequences, and the two baselines the pages
+ * compare ([course] §2 primer and "The insight": a contiguous max-context
+ * reservation per request wastes most of it, paging wastes at most the
+ * tail of each sequence's last block; §4 and §11: the pool still caps
+ * concurrency, seqs ~ pool blocks / blocks per sequence; the KV usage
+ * fraction is the capacity signal to watch). */
+typedef struct pa_bm_usage {
+  int64_t tokens;         /* sum of the resident sequences' lengths (shared tokens counted per sequence) */
+  int64_t used_slots;     /* block_size x blocks with refcount > 0 */
+  int64_t filled_slots;   /* slots of those blocks some resident sequence fills */
+  int64_t naive_slots;    /* resident sequences x max_context_len (a contiguous reservation each) */
+  int32_t used_blocks;    /* blocks with refcount > 0 */
+  int32_t capacity;       /* sequences of max_context_len tokens the whole pool holds: num_blocks / ceil(max_context_len / block_size) */
+  double usage;           /* used_blocks / num_blocks */
+  double paged_waste;     /* 1 - filled_slots / used_slots (0 when no block is used) */
+  double naive_waste;     /* 1 - tokens / naive_slots (0 when no sequence is resident) */
+} pa_bm_usage;
+
+/* Fill *out for a reservation size of max_context_len tokens (> 0). Swapped
+ * sequences are not resident. Errors: PA_ERR_INVALID_ARGUMENT. */
+pa_status pa_bm_usage_get(const pa_bm* bm, int32_t max_context_len, pa_bm_usage* out);
 /* Refcount of every block: host int32[num_blocks]. */
 pa_status pa_bm_refcounts(const pa_bm* bm, int32_t* out);
 /* Free stack from bottom to top (the top is popped next): host

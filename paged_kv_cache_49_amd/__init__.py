@@ -306,6 +306,12 @@ class BlockManager:
         _check(lib().pa_bm_host_free_stack(self._h, _ptr(out), cap, ctypes.byref(n)))
         return out[: n.value].tolist()
 
+    def usage(self, max_context_len: int) -> dict:
+        """pa_bm_usage_get: KV usage, paged and naive waste, capacity."""
+        u = _lib.PaBmUsage()
+        _check(lib().pa_bm_usage_get(self._h, int(max_context_len), ctypes.byref(u)))
+        return {f: getattr(u, f) for f, _ in _lib.PaBmUsage._fields_}
+
     def stats(self) -> dict:
         s = PaBmStats()
         _check(lib().pa_bm_stats_get(self._h, ctypes.byref(s)))

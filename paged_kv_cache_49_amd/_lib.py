@@ -62,6 +62,20 @@ class PaBmStats(ctypes.Structure):
     ]
 
 
+class PaBmUsage(ctypes.Structure):
+    _fields_ = [
+        ("tokens", c_int64),
+        ("used_slots", c_int64),
+        ("filled_slots", c_int64),
+        ("naive_slots", c_int64),
+        ("used_blocks", c_int32),
+        ("capacity", c_int32),
+        ("usage", ctypes.c_double),
+        ("paged_waste", ctypes.c_double),
+        ("naive_waste", ctypes.c_double),
+    ]
+
+
 _P = c_void_p
 _I32P = POINTER(c_int32)
 _I64P = POINTER(c_int64)
@@ -94,6 +108,7 @@ SIGNATURES = {
     "pa_alloc_prompt": (c_int, [_P, c_int64, _P, c_int32, _P, _I32P]),
     "pa_bm_prefix_cache_stats": (c_int, [_P, _I32P, _I32P, POINTER(c_int64), POINTER(c_int64), POINTER(c_int64)]),
     "pa_bm_evictable": (c_int, [_P, _P, c_int32, _I32P]),
+    "pa_bm_usage_get": (c_int, [_P, c_int32, POINTER(PaBmUsage)]),
     "pa_bm_shared_prefixes": (c_int, [_P, _P, c_int32, c_int32, _P, _P, _P, _I32P, _I32P, _I32P]),
     "pa_reshape_and_cache": (c_int, [POINTER(PaKvCache), _P, _P, c_int, _P, c_int32, _P]),
     "pa_copy_blocks": (c_int, [POINTER(PaKvCache), _P, c_int32, _P]),

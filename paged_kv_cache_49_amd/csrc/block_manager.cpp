@@ -651,6 +651,41 @@ pa_status pa_bm_evictable(const pa_bm* bm, int32_t* out, int32_t capacity, int32
   return PA_OK;
 }
 
+pa_status pa_bm_usage_get(const pa_bm* bm, int32_t max_context_len, pa_bm_usage* out) {
+  pa::clear_error();
+  if (bm == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or out is NULL");
+  if (max_context_len <= 0) return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len = %d must be positive", max_context_len);
+  PA_GUARD_BEGIN
+  const int32_t bs = bm->block_size;
+  std::vector<int32_t> fill(bm->num_blocks, 0);  // slots of each block some resident sequence fills
+  pa_bm_usage u{};
+  int64_t resident = 0;
+  for (const auto& kv : bm->seqs) {
+    const pa_bm::Seq& sq = kv.second;
+    if (sq.swapped) continue;
+    ++resident;
+    u.tokens += sq.len;
+    for (size_t j = 0; j < sq.blocks.size(); ++j) {
+      const int64_t f = std::min<int64_t>(bs, static_cast<int64_t>(sq.len) - static_cast<int64_t>(j) * bs);
+      fill[sq.blocks[j]] = std::max<int32_t>(fill[sq.blocks[j]], static_cast<int32_t>(f));
+    }
+  }
+  for (int32_t b = 0; b < bm->num_blocks; ++b)
+    if (bm->refcnt[b] > 0) {
+      ++u.used_blocks;
+      u.filled_slots += fill[b];
+    }
+  u.used_slots = static_cast<int64_t>(u.used_blocks) * bs;
+  u.naive_slots = resident * max_context_len;
+  u.capacity = static_cast<int32_t>(bm->num_blocks / bm->blocks_for(max_context_len));
+  u.usage = static_cast<double>(u.used_blocks) / bm->num_blocks;
+  u.paged_waste = u.used_slots ? 1.0 - static_cast<double>(u.filled_slots) / u.used_slots : 0.0;
+  u.naive_waste = u.naive_slots ? 1.0 - static_cast<double>(u.tokens) / u.naive_slots : 0.0;
+  *out = u;
+  return PA_OK;
+  PA_GUARD_END
+}
+
 pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out) {
   pa::clear_error();
   if (bm == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or out is NULL");

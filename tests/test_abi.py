@@ -244,6 +244,57 @@ def test_prefix_cache_reuse_across_requests():
     assert bm.prefix_cache_stats()["evictions"] == 1 and bm.evictable() == []
 
 
+def test_usage_worked_examples():
+    """The course page's numbers (tests/golden/course_capacity.json): a
+    100-token request in an 8k contiguous slab wastes ~98.8%; paged, it holds
+    7 blocks with 12 unused slots; 10,000 blocks hold 39 sequences of 4k."""
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "course_capacity.json")))
+    bs = g["block_size"]
+    bm = pa.BlockManager(10000, bs)
+    bm.alloc(1, g["request_tokens"])
+    u = bm.usage(g["slab_tokens"])
+    assert u["naive_waste"] == A.naive_waste(g["request_tokens"], g["slab_tokens"])
+    assert u["used_blocks"] == A.blocks_for(g["request_tokens"], bs) == 7
+    assert u["used_slots"] - u["filled_slots"] == A.paged_waste_tokens(g["request_tokens"], bs) == 12
+    assert bm.usage(4096)["capacity"] == A.capacity(10000, 4096, bs) == 39
+    assert bm.usage(2048)["capacity"] == 78
+
+
+@settings(max_examples=150, deadline=None)
+@given(ops=_swap_ops, bs=st.sampled_from([1, 4, 16]), nb=st.integers(1, 30), ctx=st.integers(1, 200),
+       seed=st.integers(0, 2 ** 16))
+def test_usage_matches_the_model_state(ops, bs, nb, ctx, seed):
+    """Usage figures recomputed from the model's tables: shared blocks count
+    once, a shared block's filled slots are the largest fill of any holder,
+    swapped sequences are not resident."""
+    order = np.random.default_rng(seed).permutation(nb).tolist()
+    bm = pa.BlockManager(nb, bs, order)
+    m = A.BlockAllocatorModel(nb, bs, order)
+    bm.set_host_pool(15)
+    m.set_host_pool(15)
+    for op in ops:
+        f = {"alloc": (lambda: bm.alloc(op[1], op[2]), lambda: m.alloc(op[1], op[2])),
+             "fork": (lambda: bm.fork(op[1], op[2]), lambda: m.fork(op[1], op[2])),
+             "free": (lambda: bm.free(op[1]), lambda: m.free(op[1])),
+             "out": (lambda: bm.swap_out(op[1]), lambda: m.swap_out(op[1])),
+             "in": (lambda: bm.swap_in(op[1]), lambda: m.swap_in(op[1]))}[op[0]]
+        _run(*f)
+    u = bm.usage(ctx)
+    resident = [s for s in m.seqs() if not m.is_swapped(s)]
+    fill = {}
+    for s in resident:
+        L = m.length(s)
+        for j, b in enumerate(m.table(s)):
+            fill[b] = max(fill.get(b, 0), min(bs, L - j * bs))
+    used = [b for b, r in enumerate(m.refcnt) if r > 0]
+    assert u["used_blocks"] == len(used) and u["used_slots"] == len(used) * bs
+    assert u["filled_slots"] == sum(fill.get(b, 0) for b in used)
+    assert u["tokens"] == sum(m.length(s) for s in resident)
+    assert u["naive_slots"] == len(resident) * ctx
+    assert u["capacity"] == A.capacity(nb, ctx, bs)
+
+
 def test_swapped_sequences_refuse_other_operations():
     bm = pa.BlockManager(8, 4)
     bm.set_host_pool(8)
