@@ -346,7 +346,13 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams p) 
           }
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vf[e] = e4m3_to_f32((vc[it][e / 4] >> (8 * (e % 4))) & 0xffu);
+          for (int e = 0; e < 8; e += 4) {
+            const f32x4 f = e4m3x4_to_f32x4(vc[it][e / 4]);
+            vf[e] = f.x;
+            vf[e + 1] = f.y;
+            vf[e + 2] = f.z;
+            vf[e + 3] = f.w;
+          }
         }
         if (tail) {
           const bool ok = tb + tr < tok_end;

@@ -11,6 +11,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Storage-type tags (what one element of a pool / tensor is).
 struct F16 {
@@ -70,23 +72,21 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | code;
 }
 
-// E4M3 byte -> fp32 value. Codes with a zero exponent field are m * 2^-9
-// (an exact int-to-float and power-of-two product); the others become an
-// fp32 with the same mantissa and the exponent rebased from bias 7 to 127.
-// (NaN codes are never stored from finite data; they decode to 480.)
-__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
-  const uint32_t em = byte & 0x7fu;
-  const float mag = em < 8u ? static_cast<float>(em) * 0x1p-9f : __uint_as_float((em << 20) + (120u << 23));
-  return (byte & 0x80u) ? -mag : mag;
+// Four E4M3 bytes packed in a dword -> bf16 pairs, by CDNA4's packed
+// conversion (v_cvt_scalef32_pk_bf16_fp8, scale 1: exact, since every E4M3
+// value is a bf16 value). word_sel picks bytes 0-1 or 2-3. Returns two
+// dwords, each holding two bf16 (byte 0 in the low half of .x).
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-// Four E4M3 bytes packed in a dword -> bf16 pairs (exact: every E4M3 value
-// is a bf16 value). Returns two dwords, each holding two bf16.
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
-  u32x2 r;
-  r.x = (f32_to_bf16_bits(e4m3_to_f32(w & 0xffu))) | (f32_to_bf16_bits(e4m3_to_f32((w >> 8) & 0xffu)) << 16);
-  r.y = (f32_to_bf16_bits(e4m3_to_f32((w >> 16) & 0xffu))) | (f32_to_bf16_bits(e4m3_to_f32(w >> 24)) << 16);
-  return r;
+// Four E4M3 bytes -> four fp32 values (v_cvt_pk_f32_fp8, exact).
+__device__ __forceinline__ f32x4 e4m3x4_to_f32x4(uint32_t w) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  return f32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
 // ---- wave-level reductions (wave64) ----------------------------------------
