@@ -9,11 +9,13 @@
 // flow (QK and PV on the matrix cores, online softmax) is that of
 // decode_vt_kernel.h.
 //
-// Work units are 16-token tiles, numbered head group-major, then sequence,
-// then tile: unit = hg * T + prefix[s] + tile, T = total tiles of the batch.
+// Work units are tiles of TT tokens (16 for 16-bit pools, 32 for fp8 pools,
+// so a unit's K/V is 8 KiB per KV head either way and a ring slot keeps the
+// same bytes in flight), numbered head group-major, then sequence, then
+// tile: unit = hg * T + prefix[s] + tile, T = total tiles of the batch.
 // A head group is HW consecutive KV heads; a workgroup has HW waves and wave
-// i serves KV head hg * HW + i, so one unit reads all HW heads of a 16-token
-// block row at once (a whole block when HW = num_kv_heads). The grid holds
+// i serves KV head hg * HW + i, so one unit reads all HW heads of a tile's
+// block rows at once (a whole block when HW = num_kv_heads). The grid holds
 // W workgroups, about as many as are resident at once; workgroup w takes the
 // units [w U / W, (w + 1) U / W), so all of them stream the same number of
 // tiles, and a wave walks from one sequence into the next without ending.
@@ -121,7 +123,15 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   constexpr int kB = C::kB;
   constexpr int kNT = D / 16;
   static_assert(G <= 16, "at most 16 query heads per KV head");
-  using VRaw = typename VVecT<KV>::raw_dm;
+  // tokens per unit, 16-row QK tiles per unit, scores per lane (lane group
+  // j holds tokens kE * j .. kE * j + kE - 1), blocks one unit spans
+  constexpr int TT = kB == 1 ? 32 : 16;
+  constexpr int kSub = TT / 16;
+  constexpr int kE = TT / 4;
+  constexpr int kTB = BS < TT ? TT / BS : 1;
+  static_assert(!AP || TT == 16, "the append variant is for 16-bit pools");
+  // V of one head dim for the lane's kE tokens: 4 x 16-bit or 8 x fp8
+  using VSlot = u32x2;
   extern __shared__ int32_t sk_smem[];
   const int B = p.batch;
   int32_t* s_pref = sk_smem;  // [B + 1]
@@ -136,7 +146,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     int L = p.context_lens[i];
     L = L < p.len_cap ? L : p.len_cap;
     // append: the cache holds L - 1 tokens, plus the virtual tile
-    s_pref[i] = L > 0 ? (AP ? ((L + 14) >> 4) + 1 : (L + 15) >> 4) : 0;
+    s_pref[i] = L > 0 ? (AP ? ((L + 14) >> 4) + 1 : (L + TT - 1) / TT) : 0;
   }
   __syncthreads();
   if (wave == 0) {
@@ -194,7 +204,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // out), so nothing waits for these loads until the batch is used.
   struct Batch {
     int ub;
-    int seq, tile, len, hg, ida, idb;
+    int seq, tile, len, hg;
+    int id0, id1, id2, id3;  // the tile's blocks (the first kTB)
     int virt, sblk, soff;  // append only
   };
   // Lanes past the range resolve the range's last unit: every lane loads,
@@ -211,9 +222,9 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     b.virt = AP && t == s_pref[s + 1] - s_pref[s] - 1;
     // (a virtual tile reads no cache block; its table index could lie past
     // the table's end)
-    const int blk_a = b.virt ? 0 : (BS >= 16 ? (t * 16) / BS : 2 * t);
+    const int blk_a = b.virt ? 0 : (t * TT) / BS;
     b.len = p.context_lens[s];
-    b.ida = row[blk_a];
+    b.id0 = row[blk_a];
     if constexpr (AP) {
       const int64_t sl = p.slot_mapping[s];
       b.sblk = sl >= 0 ? static_cast<int>(sl / BS) : -1;
@@ -222,9 +233,11 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       b.sblk = -1;
       b.soff = 0;
     }
-    // the tile's second block; past the sequence's last block its value is
-    // never used (those tokens are masked)
-    b.idb = BS < 16 ? row[min(blk_a + 1, p.max_blocks - 1)] : 0;
+    // the tile's further blocks; past the sequence's last block their
+    // values are never used (those tokens are masked)
+    b.id1 = kTB > 1 ? row[min(blk_a + 1, p.max_blocks - 1)] : 0;
+    b.id2 = kTB > 2 ? row[min(blk_a + 2, p.max_blocks - 1)] : 0;
+    b.id3 = kTB > 3 ? row[min(blk_a + 3, p.max_blocks - 1)] : 0;
     b.seq = s;
     b.tile = t;
     b.hg = hg;
@@ -232,8 +245,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   };
   auto block_id = [&](int id) { return static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks) ? id : 0; };
   // ---- loads of one unit into a ring slot; returns the unit
-  auto load_unit = [&](const Batch& b, int x, u32x4 (&qr)[C::kKSteps], u32x4 (&kr)[C::kKLoads],
-                       VRaw (&vr)[kNT]) -> SkUnit {
+  auto load_unit = [&](const Batch& b, int x, u32x4 (&qr)[C::kKSteps], u32x4 (&kr)[kSub * C::kKLoads],
+                       VSlot (&vr)[kNT]) -> SkUnit {
     const int o = x - b.ub;
     SkUnit un;
     un.seq = __builtin_amdgcn_readlane(b.seq, o);
@@ -244,7 +257,28 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     un.sblk = AP ? __builtin_amdgcn_readlane(b.sblk, o) : -1;
     un.soff = AP ? __builtin_amdgcn_readlane(b.soff, o) : 0;
     if (AP) un.len = un.virt ? 1 : un.len - 1;  // the virtual tile holds token L - 1 alone
-    const int ida = block_id(__builtin_amdgcn_readlane(b.ida, o));
+    // the tile's blocks (scalars, not an array: a select over an array
+    // would become a per-lane indexed load from scratch)
+    const int id0 = block_id(__builtin_amdgcn_readlane(b.id0, o));
+    const int id1 = kTB > 1 ? block_id(__builtin_amdgcn_readlane(b.id1, o)) : 0;
+    const int id2 = kTB > 2 ? block_id(__builtin_amdgcn_readlane(b.id2, o)) : 0;
+    const int id3 = kTB > 3 ? block_id(__builtin_amdgcn_readlane(b.id3, o)) : 0;
+    // block i (< kTB) of the tile. The empty asm statements keep the two
+    // halves of the choice apart: the compiler would otherwise turn the
+    // whole select tree into a per-lane indexed load from scratch.
+    auto pick = [&](int i) {
+      if constexpr (kTB == 1) {
+        return id0;
+      } else if constexpr (kTB == 2) {
+        return i ? id1 : id0;
+      } else {
+        int lo = (i & 1) ? id1 : id0;
+        int hi = (i & 1) ? id3 : id2;
+        asm volatile("" : "+v"(lo));
+        asm volatile("" : "+v"(hi));
+        return (i & 2) ? hi : lo;
+      }
+    };
     const int g = un.hg * HW + wave;
     // the unit's q rows (B operand of S^T = K q^T); columns >= G repeat head
     // 0 (finite logits whose weights are forced to zero). Every unit loads
@@ -261,20 +295,32 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // or (append variant) from the newest token's k_new / v_new row. Both
     // cases issue the same load instructions, so the loads in flight per
     // ring slot stay fixed and the compiler's waits stay tight.
-    const char* krow;  // lane's K row minus its first head-dim offset (see below)
+    const char* krow;  // lane's K row (QK tile 0) minus its first head-dim offset (see below)
     const char* vrun;  // lane's V run for n-tile 0
-    if constexpr (BS >= 16) {
+    if constexpr (TT == 32) {
+      // QK tile 0 row `col` is token 8 (col / 4) + col % 4 of the unit and
+      // tile 1 row `col` the token 4 past it (same block), so score lane
+      // group j holds tokens 8j .. 8j + 7 and the PV operand of lane (d, j)
+      // is the run of head dim d over those 8 tokens
+      const int tk = 8 * (col >> 2) + (col & 3);
+      const int tv = 8 * j;
+      const int tin = kTB == 1 ? (un.tile * TT) % BS : 0;
+      const int idk = pick(tk / BS);
+      const int idv = pick(tv / BS);
+      krow = kbase + static_cast<int64_t>(idk) * blk_bytes + (tin + tk % BS) * tok_bytes +
+             static_cast<int64_t>(g) * D * kB;
+      vrun = vbase + static_cast<int64_t>(idv) * blk_bytes + ((static_cast<int64_t>(g) * D + col) * BS + tin + tv % BS) * kB;
+    } else if constexpr (BS >= 16) {
       const int tin = (un.tile * 16) % BS;
-      krow = kbase + static_cast<int64_t>(ida) * blk_bytes + tin * tok_bytes + static_cast<int64_t>(g) * D * kB +
+      krow = kbase + static_cast<int64_t>(id0) * blk_bytes + tin * tok_bytes + static_cast<int64_t>(g) * D * kB +
              koff_lane - qk_dim<kB>(0, j) * kB;
-      vrun = vbase + static_cast<int64_t>(ida) * blk_bytes + (static_cast<int64_t>(g) * D * BS + tin) * kB + voff_lane;
+      vrun = vbase + static_cast<int64_t>(id0) * blk_bytes + (static_cast<int64_t>(g) * D * BS + tin) * kB + voff_lane;
     } else {
-      // a tile spans two blocks: tokens 0..BS-1 in block A, the rest in B
-      const int idb = block_id(__builtin_amdgcn_readlane(b.idb, o));
-      const int idk = col < BS ? ida : idb;
+      // a tile spans two blocks: tokens 0..BS-1 in the first, the rest in the second
+      const int idk = pick(col / BS);
       krow = kbase + static_cast<int64_t>(idk) * blk_bytes + (col % BS) * tok_bytes + static_cast<int64_t>(g) * D * kB;
       const int t4 = 4 * j;
-      const int idv = t4 < BS ? ida : idb;
+      const int idv = pick(t4 / BS);
       vrun = vbase + static_cast<int64_t>(idv) * blk_bytes + ((static_cast<int64_t>(g) * D + col) * BS + t4 % BS) * kB;
     }
     int vstep = kVTileBytes;
@@ -289,12 +335,15 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       }
     }
 #pragma unroll
-    for (int i = 0; i < C::kKLoads; ++i) {
-      const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
-      kr[i] = *reinterpret_cast<const u32x4*>(krow + off);
+    for (int s = 0; s < kSub; ++s) {
+#pragma unroll
+      for (int i = 0; i < C::kKLoads; ++i) {
+        const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
+        kr[s * C::kKLoads + i] = *reinterpret_cast<const u32x4*>(krow + s * 4 * tok_bytes + off);
+      }
     }
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VRaw*>(vrun + nt * vstep);
+    for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VSlot*>(vrun + nt * vstep);
     return un;
   };
 
@@ -363,29 +412,37 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     return (col & 1) ? (w2 >> 16) : (w2 & 0xffffu);
   };
 
-  auto compute = [&](int x, const SkUnit& un, const u32x4 (&qb)[C::kKSteps], const u32x4 (&kr)[C::kKLoads],
-                     const VRaw (&vr)[kNT]) {
-    const int tb = AP && un.virt ? 0 : un.tile * 16;
+  auto compute = [&](int x, const SkUnit& un, const u32x4 (&qb)[C::kKSteps], const u32x4 (&kr)[kSub * C::kKLoads],
+                     const VSlot (&vr)[kNT]) {
+    const int tb = AP && un.virt ? 0 : un.tile * TT;
     const int L = un.len;
-    // ---- S^T = K q^T
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (kB == 2) {
+    // ---- S^T = K q^T, one 16-row tile per kSub; lane (head col, j) gets
+    // the scores of tokens kE * j + e, e = 4 * tile + row
+    f32x4 sacc[kSub];
 #pragma unroll
-      for (int i = 0; i < C::kKSteps; ++i) sacc = mfma_16x16x32<QT>(kr[i], qb[i], sacc);
-    } else {
+    for (int s = 0; s < kSub; ++s) {
+      sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kB == 2) {
 #pragma unroll
-      for (int a = 0; a < C::kKLoads; ++a) {
-        const u32x2 b0 = e4m3x4_to_bf16x4(kr[a].x), b1 = e4m3x4_to_bf16x4(kr[a].y);
-        const u32x2 b2 = e4m3x4_to_bf16x4(kr[a].z), b3 = e4m3x4_to_bf16x4(kr[a].w);
-        sacc = mfma_16x16x32<QT>(u32x4{b0.x, b0.y, b1.x, b1.y}, qb[2 * a], sacc);
-        sacc = mfma_16x16x32<QT>(u32x4{b2.x, b2.y, b3.x, b3.y}, qb[2 * a + 1], sacc);
+        for (int i = 0; i < C::kKSteps; ++i) sacc[s] = mfma_16x16x32<QT>(kr[i], qb[i], sacc[s]);
+      } else {
+#pragma unroll
+        for (int a = 0; a < C::kKLoads; ++a) {
+          const u32x4 kw = kr[s * C::kKLoads + a];
+          const u32x2 b0 = e4m3x4_to_bf16x4(kw.x), b1 = e4m3x4_to_bf16x4(kw.y);
+          const u32x2 b2 = e4m3x4_to_bf16x4(kw.z), b3 = e4m3x4_to_bf16x4(kw.w);
+          sacc[s] = mfma_16x16x32<QT>(u32x4{b0.x, b0.y, b1.x, b1.y}, qb[2 * a], sacc[s]);
+          sacc[s] = mfma_16x16x32<QT>(u32x4{b2.x, b2.y, b3.x, b3.y}, qb[2 * a + 1], sacc[s]);
+        }
       }
     }
-    float sv[4];
+    float sv[kE];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = tb + 4 * j + r < L ? sacc[r] * p.qk_scale_log2 : -INFINITY;
+    for (int e = 0; e < kE; ++e) sv[e] = tb + kE * j + e < L ? sacc[e / 4][e % 4] * p.qk_scale_log2 : -INFINITY;
     // ---- online softmax (head = col)
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < kE; ++e) mx = fmaxf(mx, sv[e]);
     mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const bool need = col < G && mx > m_w + C::kSlack;
@@ -400,38 +457,48 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         for (int nt = 0; nt < kNT; ++nt) acc[nt][r] *= ar;
       }
     }
-    float pw[4];
+    float pw[kE];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pw[r] = col < G ? __builtin_amdgcn_exp2f(sv[r] - m_w) : 0.f;
-      l_w += pw[r];
+    for (int e = 0; e < kE; ++e) {
+      pw[e] = col < G ? __builtin_amdgcn_exp2f(sv[e] - m_w) : 0.f;
+      l_w += pw[e];
     }
-    const uint32_t h0 = pack2<QT>(pw[0], pw[1]), h1 = pack2<QT>(pw[2], pw[3]);
-    const uint32_t l0 = pack2<QT>(pw[0] - half_lo<QT>(h0), pw[1] - half_hi<QT>(h0));
-    const uint32_t l1 = pack2<QT>(pw[2] - half_lo<QT>(h1), pw[3] - half_hi<QT>(h1));
-    const u32x2 phi = {h0, h1}, plo = {l0, l1};
-    // ---- PV
-    u32x2 vmask = {0xffffffffu, 0xffffffffu};
-    if (tb + 16 > L) {
-      const int t = tb + 4 * j;
-      vmask.x = (t < L ? 0xffffu : 0u) | (t + 1 < L ? 0xffff0000u : 0u);
-      vmask.y = (t + 2 < L ? 0xffffu : 0u) | (t + 3 < L ? 0xffff0000u : 0u);
+    // weights as two 16-bit terms (hi + lo), the PV A operand: row = head,
+    // k = the lane's kE tokens
+    uint32_t phi[kE / 2], plo[kE / 2];
+#pragma unroll
+    for (int e = 0; e < kE; e += 2) {
+      phi[e / 2] = pack2<QT>(pw[e], pw[e + 1]);
+      plo[e / 2] = pack2<QT>(pw[e] - half_lo<QT>(phi[e / 2]), pw[e + 1] - half_hi<QT>(phi[e / 2]));
+    }
+    // ---- PV; V elements past the end are zeroed (the pool may hold
+    // anything there, and 0 * NaN would poison the sum)
+    uint32_t vmask[kE / 2];
+#pragma unroll
+    for (int e = 0; e < kE; e += 2) vmask[e / 2] = 0xffffffffu;
+    if (tb + TT > L) {
+      const int t = tb + kE * j;
+#pragma unroll
+      for (int e = 0; e < kE; e += 2)
+        vmask[e / 2] = (t + e < L ? 0xffffu : 0u) | (t + e + 1 < L ? 0xffff0000u : 0u);
     }
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-      u32x2 vop;
-      if constexpr (kB == 2) {
-        vop = vr[nt];
+      if constexpr (TT == 16) {
+        u32x2 vop = vr[nt];
         if constexpr (AP) {
           if (un.virt) vop = u32x2{virt_v(vr[nt]), 0u};
         }
+        vop.x &= vmask[0];
+        vop.y &= vmask[1];
+        acc[nt] = mfma_16x16x16<QT>(u32x2{phi[0], phi[1]}, vop, acc[nt]);
+        acc[nt] = mfma_16x16x16<QT>(u32x2{plo[0], plo[1]}, vop, acc[nt]);
       } else {
-        vop = e4m3x4_to_bf16x4(vr[nt]);
+        const u32x2 b0 = e4m3x4_to_bf16x4(vr[nt].x), b1 = e4m3x4_to_bf16x4(vr[nt].y);
+        const u32x4 vop = {b0.x & vmask[0], b0.y & vmask[1], b1.x & vmask[2], b1.y & vmask[3]};
+        acc[nt] = mfma_16x16x32<QT>(u32x4{phi[0], phi[1], phi[2], phi[3]}, vop, acc[nt]);
+        acc[nt] = mfma_16x16x32<QT>(u32x4{plo[0], plo[1], plo[2], plo[3]}, vop, acc[nt]);
       }
-      vop.x &= vmask.x;
-      vop.y &= vmask.y;
-      acc[nt] = mfma_16x16x16<QT>(phi, vop, acc[nt]);
-      acc[nt] = mfma_16x16x16<QT>(plo, vop, acc[nt]);
     }
     // ---- append: write the newest token's row into its cache slot
     if constexpr (AP) {
@@ -452,7 +519,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       }
     }
     // ---- end of a segment: store it, then start the next one at x + 1
-    const bool seq_end = AP ? un.virt != 0 : un.tile == ((L + 15) >> 4) - 1;
+    const bool seq_end = AP ? un.virt != 0 : un.tile == (L + TT - 1) / TT - 1;
     if (seq_end || x + 1 == u1) {
       flush(un.seq, un.hg, seg_begun && seq_end, seq_end, seg_first ? 0 : 1);
       if (x + 1 < u1) {
@@ -473,8 +540,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // holds the units it loads (uk + 2 .. uk + 65), and the next step's batch
   // is requested when the step starts.
   u32x4 q0[C::kKSteps], q1[C::kKSteps], q2[C::kKSteps];
-  u32x4 k0[C::kKLoads], k1[C::kKLoads], k2[C::kKLoads];
-  VRaw v0[kNT], v1[kNT], v2[kNT];
+  u32x4 k0[kSub * C::kKLoads], k1[kSub * C::kKLoads], k2[kSub * C::kKLoads];
+  VSlot v0[kNT], v1[kNT], v2[kNT];
   const int ulast = u1 - 1;
   Batch cur = resolve(u0);
   Batch nxt = resolve(min(u0 + 2, ulast));

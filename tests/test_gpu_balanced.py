@@ -1,7 +1,8 @@
 """The balanced decode split (partition_size = pa.BALANCED, dim-major V) on
 the GPU against the fp64 oracle.
 
-The split divides the batch's 16-token tiles evenly over the resident
+The split divides the batch's tiles (16 tokens; 32 for fp8 pools) evenly
+over the resident
 workgroups and merges sequences cut between them. PA_SK_WGS caps the grid,
 so small inputs still reach every case of the split: one workgroup walking
 many sequences and many unit batches (cap 1), sequences cut between a few
@@ -63,6 +64,20 @@ CASES = [
 def test_parity_sweep(gpu, wgs, kv, D, bs, G, hkv, cap):
     wgs(cap)
     wl = synth.random_case(2000 + D + bs + G + hkv, LENGTHS, G * hkv, hkv, D, bs, kv)
+    _check(wl, f"cap={cap}")
+
+
+FP8_LENGTHS = [1, 7, 8, 9, 31, 32, 33, 63, 64, 65, 777, 1601]
+
+
+@pytest.mark.parametrize("cap", [None, 1, 5])
+@pytest.mark.parametrize("D,bs,G", [(128, 8, 8), (128, 16, 4), (64, 32, 2), (128, 32, 8), (64, 8, 1)])
+def test_fp8_32_token_units(gpu, wgs, D, bs, G, cap):
+    """fp8 pools take 32-token units (two 16-row QK tiles and one 32-deep PV
+    step per unit): lengths on both sides of multiples of 8, 16 and 32, and
+    units that span 4, 2 or 1 blocks."""
+    wgs(cap)
+    wl = synth.random_case(2600 + D + bs + G, FP8_LENGTHS, 2 * G, 2, D, bs, "fp8")
     _check(wl, f"cap={cap}")
 
 
