@@ -27,6 +27,16 @@ pa_decode call of every timed step, on the stream it runs on. The events
 are created with hipEventDisableSystemFence (see HipTimingEvent): default
 events add a cache write-back and invalidate, ~5 us of idle queue each.
 ``cpu_baseline`` = the fp64 oracle on the host cores.
+
+``--workload long|mixed|prefix`` times decode calls on the other workloads
+instead (the long-context batch, the mixed-length batch with ``--kv`` and
+``--block-size``, the prefix-sharing batch, with ``--shared`` through
+pa_decode_shared): ``--layers`` pools whose K/V are drawn on the device
+(torch's seeded generator; fp8 pools take the scale 6/448, about the amax of
+that many N(0,1) draws) and written through pa_reshape_and_cache, then
+``--steps`` rounds of one call per layer, back to back, timed with HIP
+events. ``value`` = KV bytes per call / mean call time (no host work in the
+timed region); no cpu_baseline.
 """
 from __future__ import annotations
 
@@ -140,6 +150,13 @@ def parse():
                         "split: pa_decode_append, both in one launch)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    p.add_argument("--workload", choices=["gqa", "long", "mixed", "prefix"], default="gqa",
+                   help="gqa: the decode step on the GQA batch (default); others: decode calls on that workload")
+    p.add_argument("--kv", choices=["bf16", "fp8"], default="bf16", help="KV dtype of the mixed workload")
+    p.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32], help="block size of the mixed workload")
+    p.add_argument("--shared", action="store_true",
+                   help="prefix workload: pa_decode_shared with groups of sequences sharing their prefix blocks "
+                        "(--partition-size > 0, default 256)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return p.parse_args()
@@ -193,6 +210,138 @@ def cpu_baseline(wl, seconds: float):
                       f"{el:.1f} s; tokens/s {B * reps / el:.1f}"}
 
 
+def bench_decode_calls(args):
+    """Back-to-back decode calls on the long-context, mixed-length or
+    prefix-sharing workload; prints one JSON line."""
+    import torch
+    import paged_kv_cache_49_amd as pa
+    import synth
+    from paged_kv_cache_49_amd.runner import PagedBatch, workspace_for
+
+    dev = "cuda"
+    layers, K, W = args.layers, args.steps, args.warmup
+    ps = args.partition_size
+    gen = torch.Generator(device=dev).manual_seed(4903)
+    extra = {}
+    if args.workload == "prefix":
+        wl = synth.prefix_sharing(partial_tail=True)
+        P, S = wl.prompts, wl.samples
+        B, Hq, Hkv, D, bs, kv = P * S, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, "bf16"
+        bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
+        caches = [pa.KVCache.allocate(wl.num_blocks, bs, Hkv, D, kv, device=dev, v_layout="dim")
+                  for _ in range(layers)]
+        mb = int(-(-(int(wl.prefix_len.max() + wl.tail_len.max()) + 2) // bs))
+        batch = PagedBatch(bm, caches, mb, B, device=dev)
+        rnd = lambda n: [torch.randn(n, Hkv, D, generator=gen, device=dev).bfloat16() for _ in range(layers)]
+        for p in range(P):
+            n = int(wl.prefix_len[p])
+            batch.prefill(p * S, rnd(n), rnd(n))
+            for i in range(1, S):
+                batch.fork(p * S, p * S + i)
+        for p in range(P):
+            for i in range(S):
+                n = int(wl.tail_len[p, i]) + 1  # tail + the new token
+                batch.prefill(p * S + i, rnd(n), rnd(n))
+        tables, lens, max_ctx = batch.tables(list(range(B)))
+        L = lens.cpu().numpy().astype(np.int64)
+        unique_tokens = int(wl.prefix_len.sum()) + int((wl.tail_len + 1).sum())
+        desc = (f"prefix sharing: {P} prompts x {S} samples, shared prefix 2048 + U[1,15] tokens, tails U[0,256] "
+                f"+ 1 new token, 32 q heads / 8 KV heads, head_dim 128, block 16, bf16")
+        if args.shared:
+            ps = ps if ps > 0 else 256
+            sp = bm.shared_prefixes(list(range(B)), ps)
+            i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+            sargs = (i32(sp.offsets), i32(sp.members), i32(sp.shared_len), sp.num_groups, sp.max_group_size,
+                     sp.max_shared_len, sp.min_shared_len)
+            extra["groups"] = sp.num_groups
+    else:
+        wl = (synth.long_context() if args.workload == "long"
+              else synth.mixed_lengths(block_size=args.block_size, kv_dtype=args.kv))
+        B, Hq, Hkv, D, bs, kv = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.kv_dtype
+        sc = 6.0 / 448.0 if kv == "fp8" else 1.0
+        bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
+        caches = [pa.KVCache.allocate(wl.num_blocks, bs, Hkv, D, kv, device=dev, v_layout="dim", k_scale=sc,
+                                      v_scale=sc) for _ in range(layers)]
+        for s in range(B):
+            n = int(wl.lengths[s])
+            slots, _ = bm.alloc(s, n)
+            sd = torch.from_numpy(slots).to(dev)
+            for c in caches:
+                k = torch.randn(n, Hkv, D, generator=gen, device=dev).bfloat16()
+                v = torch.randn(n, Hkv, D, generator=gen, device=dev).bfloat16()
+                pa.reshape_and_cache(c, k, v, sd)
+        mb = int(-(-int(wl.lengths.max()) // bs))
+        t, l = bm.pack(list(range(B)), mb, -1)
+        tables, lens, max_ctx = torch.from_numpy(t).to(dev), torch.from_numpy(l).to(dev), int(l.max())
+        L = l.astype(np.int64)
+        desc = ("long context: 8 seqs, context U[32768,131072], 32 q heads / 8 KV heads, head_dim 128, block 16, "
+                "bf16" if args.workload == "long" else
+                f"mixed lengths: 256 seqs, context clip(lognormal(ln 1024, 1), 16, 16384), 64 q heads / 8 KV heads, "
+                f"head_dim 128, block {bs}, KV {kv}, q bf16")
+    b = 1 if kv == "fp8" else 2
+    call_bytes = 2 * int(L.sum()) * Hkv * D * b
+    q = torch.randn(B, Hq, D, generator=gen, device=dev).bfloat16()
+    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    ws = workspace_for(B, Hq, Hkv, D, max_ctx, ps, device=dev)
+    if args.workload == "prefix" and args.shared:
+        call = lambda c: pa.decode_shared(c, q, tables, lens, max_ctx, wl.scale, ps, *sargs, out=out, workspace=ws)
+        kernel = "pa_decode_shared (paged_decode_shared_kernel + decode_reduce_kernel)"
+    else:
+        call = lambda c: pa.decode(c, q, tables, lens, max_ctx, wl.scale, ps, out=out, workspace=ws)
+        kernel = ("pa_decode (paged_decode_sk_kernel + decode_sk_merge_kernel)" if ps < 0 else
+                  "pa_decode (partition kernel + decode_reduce_kernel)" if ps > 0 else "pa_decode (one partition)")
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: B={B} tokens={int(L.sum())} layers={layers} KV {call_bytes / 1e6:.0f} MB/call",
+          file=sys.stderr, flush=True)
+    for _ in range(W):
+        for c in caches:
+            call(c)
+    torch.cuda.synchronize()
+    e0, e1 = HipTimingEvent(), HipTimingEvent()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        for c in caches:
+            call(c)
+    e1.record()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    call_s = e0.elapsed_time(e1) * 1e-3 / (K * layers)
+    value = call_bytes / call_s / 1e9
+    print(f"[bench] {K * layers} calls: {call_s * 1e6:.1f} us/call", file=sys.stderr, flush=True)
+    if args.workload == "prefix":
+        extra["unique_kv_gbs"] = round(2 * unique_tokens * Hkv * D * b / call_s / 1e9, 2)
+        extra["unique_kv_note"] = "KV bytes of distinct tokens (shared prefix counted once per prompt) / call time"
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(el / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": kv,
+        "data": "synthetic (seeded lengths and block ids; K/V/q drawn N(0,1) on the device)",
+        "config": {"workload": desc, "batch": B, "layers": layers, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": bs, "partition_size": ps, "v_layout": "dim",
+                   "step": f"{layers} decode calls back to back (one per layer)",
+                   "mean_context": round(float(L.mean()), 1)},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(B / call_s, 1),
+        "decode_tokens_per_s_note": "sequences per second of one layer's call",
+        "pa_decode_us": round(call_s * 1e6, 2),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(value, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_call": call_bytes},
+        "cpu_baseline": None,
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -206,6 +355,10 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+
+    if args.workload != "gqa":
+        bench_decode_calls(args)
         return
 
     import paged_kv_cache_49_amd as pa
