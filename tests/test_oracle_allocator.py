@@ -1,6 +1,8 @@
 """Pins for the allocator model (CPU only): the pages' worked examples, the
-capacity closed forms of the course page's verification questions, and
-invariants under random operation sequences (hypothesis)."""
+capacity closed forms of the course page's verification questions,
+invariants under random operation sequences (hypothesis), and hand-built
+cases for swapping and prefix caching (what a swap must move and free,
+which blocks a repeated or diverging prompt gets back, eviction order)."""
 import json
 import os
 from collections import Counter
@@ -202,3 +204,162 @@ def test_invariants_under_random_operations(ops, bs, nb):
     for s in m.seqs():
         m.free(s)
     assert sorted(m.free_stack) == list(range(nb)) and m.stats()["num_used"] == 0
+
+
+# ---- swapping ([course] §4 and §8: a preempted sequence's blocks can be
+# swapped out and brought back later). Pins: plain counting of what a swap
+# must move and free, on hand-built states.
+
+def _snapshot(m):
+    return (m.seqs(), [m.table(s) for s in m.seqs()], m.free_stack, m.host_free_stack, m.refcnt,
+            m.evictable, m.host_stats())
+
+
+def test_swap_round_trip_restores_the_sequence_and_both_pools():
+    bs = 16
+    m = A.BlockAllocatorModel(40, bs)
+    m.set_host_pool(10)
+    m.alloc(1, 100)  # 7 blocks
+    m.alloc(2, 20)   # 2 blocks
+    t1 = m.table(1)
+    pairs = m.swap_out(1)
+    assert [d for d, _ in pairs] == t1                 # every block, in logical order
+    assert len({h for _, h in pairs}) == 7             # each to its own host block
+    assert len(m.free_stack) == 40 - 2                 # its 7 device blocks are free again
+    assert len(m.host_free_stack) == 3
+    assert m.is_swapped(1) and m.length(1) == 100
+    back = m.swap_in(1)
+    assert [h for h, _ in back] == [h for _, h in pairs]
+    assert len(m.table(1)) == 7 and all(m.refcnt[b] == 1 for b in m.table(1))
+    assert len(m.host_free_stack) == 10 and not m.is_swapped(1)
+    assert m.host_stats()["swap_outs"] == 1 and m.host_stats()["swap_ins"] == 1
+    check_invariants(m)
+
+
+def test_swapping_out_a_fork_leaves_the_shared_blocks_to_the_others():
+    m = A.BlockAllocatorModel(20, 16)
+    m.set_host_pool(8)
+    m.alloc(1, 40)
+    m.fork(1, 2)  # 3 blocks at refcount 2
+    shared = m.table(1)
+    free_before = len(m.free_stack)
+    pairs = m.swap_out(2)
+    assert [d for d, _ in pairs] == shared             # the data still moves (the copy is the swapped one's)
+    assert m.table(1) == shared and all(m.refcnt[b] == 1 for b in shared)
+    assert len(m.free_stack) == free_before            # nothing freed: sequence 1 still holds them
+    m.swap_in(2)
+    assert not set(m.table(2)) & set(shared)           # fresh blocks; the sharing is not restored
+    check_invariants(m)
+
+
+def test_swap_out_and_in_are_all_or_nothing():
+    m = A.BlockAllocatorModel(20, 16)
+    m.set_host_pool(2)
+    m.alloc(1, 40)  # 3 blocks, host pool of 2
+    snap = _snapshot(m)
+    with pytest.raises(A.OutOfBlocks):
+        m.swap_out(1)
+    assert _snapshot(m) == snap and not m.is_swapped(1)
+    m2 = A.BlockAllocatorModel(4, 16)
+    m2.set_host_pool(4)
+    m2.alloc(1, 48)      # 3 of 4 blocks
+    m2.swap_out(1)       # all 4 free
+    m2.alloc(2, 32)      # 2 taken: 2 left < 3
+    snap = _snapshot(m2)
+    with pytest.raises(A.OutOfBlocks):
+        m2.swap_in(1)
+    assert _snapshot(m2) == snap and m2.is_swapped(1)
+
+
+def test_swapped_sequence_refuses_growth_fork_and_pack_and_frees_to_the_host_pool():
+    m = A.BlockAllocatorModel(20, 16)
+    m.set_host_pool(5)
+    m.alloc(1, 33)
+    m.swap_out(1)
+    for op in (lambda: m.alloc(1, 1), lambda: m.fork(1, 2), lambda: m.pack([1], 8), lambda: m.swap_out(1)):
+        with pytest.raises(A.InvalidArgument):
+            op()
+    with pytest.raises(A.InvalidArgument):
+        m.set_host_pool(9)  # host blocks in use
+    m.free(1)
+    assert len(m.host_free_stack) == 5 and len(m.free_stack) == 20
+    with pytest.raises(A.UnknownSeq):
+        m.swap_in(1)
+
+
+# ---- prefix caching ([course] §4: sharing across requests needs an
+# identical prefix; §9 and §11). Pins: which blocks an identical or
+# diverging prompt must get back, and the eviction order, on hand-built
+# prompts.
+
+def check_cache_invariants(m: A.BlockAllocatorModel):
+    rc = m.refcnt
+    refs = Counter(b for s in m.seqs() for b in m.table(s))
+    assert all(rc[b] == refs.get(b, 0) for b in range(m.num_blocks))
+    free = m.free_stack + m.evictable
+    assert len(set(free)) == len(free)
+    assert sorted(free) == [b for b in range(m.num_blocks) if rc[b] == 0]
+
+
+def test_prefix_cache_reuses_exactly_the_common_full_blocks():
+    bs = 4
+    m = A.BlockAllocatorModel(64, bs)
+    m.set_prefix_cache(True)
+    a = list(range(100, 118))  # 18 tokens: 4 full blocks and 2 tokens
+    slots, c = m.alloc_prompt(1, a)
+    ta = m.table(1)
+    assert c == 0 and slots == [ta[t // bs] * bs + t % bs for t in range(18)]
+    # the same prompt: its 4 full blocks, never the partial fifth
+    _, c = m.alloc_prompt(2, a)
+    assert c == 16 and m.table(2)[:4] == ta[:4] and m.table(2)[4] != ta[4]
+    # first difference at token 9 (block 2): blocks 0 and 1 only
+    b = a[:9] + [7] + a[10:]
+    _, c = m.alloc_prompt(3, b)
+    assert c == 8 and m.table(3)[:2] == ta[:2] and m.table(3)[2] not in ta
+    # block 1's tokens behind another block 0: nothing (the key is the whole prefix)
+    _, c = m.alloc_prompt(4, [9, 9, 9, 9] + a[4:])
+    assert c == 0 and not set(m.table(4)) & set(ta)
+    # a prompt that ends on a block boundary reuses all of its blocks
+    _, c = m.alloc_prompt(5, a[:8])
+    assert c == 8 and m.table(5) == ta[:2]
+    st = m.prefix_cache_stats()
+    assert st["hits"] == 4 + 2 + 0 + 2 and st["misses"] == 4 + 0 + 2 + 4 + 0
+    assert [m.refcnt[x] for x in ta[:4]] == [4, 4, 2, 2]
+    check_cache_invariants(m)
+
+
+def test_prefix_cache_evicts_the_least_recently_released_block_first():
+    bs = 2
+    m = A.BlockAllocatorModel(7, bs)
+    m.set_prefix_cache(True)
+    m.alloc_prompt(1, [1, 2, 3, 4, 5, 6])  # 3 full blocks
+    m.alloc_prompt(2, [7, 8, 9, 10])       # 2 full blocks
+    ta, tb = m.table(1), m.table(2)
+    m.free(1)
+    m.free(2)
+    assert m.evictable == ta[::-1] + tb[::-1]  # a prefix leaves the cache from its end
+    assert len(m.free_stack) == 2
+    m.alloc(3, 6)  # 3 blocks: the 2 free ones, then ta[2] evicted
+    assert ta[2] in m.table(3) and m.evictable == ta[1::-1] + tb[::-1]
+    assert m.prefix_cache_stats()["evictions"] == 1
+    _, c = m.alloc_prompt(4, [1, 2, 3, 4, 5, 6])
+    assert c == 4 and m.table(4)[:2] == ta[:2]  # blocks 0 and 1 still cached, block 2 gone
+    check_cache_invariants(m)
+
+
+def test_prefix_cache_off_is_a_plain_allocation():
+    tokens = list(range(37))
+    on, off = A.BlockAllocatorModel(30, 8, list(range(29, -1, -1))), A.BlockAllocatorModel(30, 8, list(range(29, -1, -1)))
+    ref = A.BlockAllocatorModel(30, 8, list(range(29, -1, -1)))
+    off_slots, c = off.alloc_prompt(1, tokens)
+    ref_slots, cows = ref.alloc(1, len(tokens))
+    assert c == 0 and off_slots == ref_slots and not cows and off.table(1) == ref.table(1)
+    _, c = off.alloc_prompt(2, tokens)
+    assert c == 0
+    on.set_prefix_cache(True)
+    on.alloc_prompt(1, tokens)
+    on.free(1)
+    on.set_prefix_cache(False)  # forgets every registration; the blocks go back to the stack
+    assert on.evictable == [] and len(on.free_stack) == 30
+    _, c = on.alloc_prompt(2, tokens)
+    assert c == 0
