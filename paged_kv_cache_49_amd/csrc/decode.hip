@@ -72,9 +72,7 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(const ReduceParams p
 }
 
 // Merge the partial pieces of segments whose units span several
-// workgroups, and write zeros for sequences without tokens. grid = (B,
-// head groups); each thread handles 8 head dims of one query head of the
-// group. Pieces are merged in workgroup order.
+// workgroups, and write zeros for sequences without tokens.
 struct SkMergeParams {
   const float* piece_m;
   const float* piece_l;
@@ -91,61 +89,47 @@ struct SkMergeParams {
   int32_t out_dtype;
 };
 
-// One workgroup per (head group, sequence) segment, one thread per 8 head
-// dims of one query head. The segment's descriptor (written by the
-// balanced kernel, see decode_sk_kernel.h) names the workgroups wf..wl that
-// hold its pieces: wf's in the slot the descriptor gives, the others' in
-// slot 0. Pieces are read 8 at a time (one round of loads) and merged with
-// a running maximum, in workgroup order.
-__global__ __launch_bounds__(1024) void decode_sk_merge_kernel(const SkMergeParams p) {
-  const int s = static_cast<int>(blockIdx.x) % p.batch;
-  const int hg = static_cast<int>(blockIdx.x) / p.batch;
-  const int HWG = p.heads_per_wg * p.group;  // query heads per head group
-  const int D = p.head_dim;
-  const int i = static_cast<int>(threadIdx.x) * 8;
-  if (i >= HWG * D) return;
-  const int h = i / D, d = i % D;
-  const int64_t head0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(hg) * HWG;
-  const int L = min(p.context_lens[s], p.len_cap);
-  const int32_t* desc = p.seg_desc + (static_cast<int64_t>(hg) * p.batch + s) * 2;
-  const int32_t d0 = desc[0], d1 = desc[1];
-  if (L <= 0) {
-    const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    store_out8(p.out, (head0 + h) * D + d, p.out_dtype, z);
-    return;
-  }
-  if (d0 == -1) return;  // stored by the workgroup that completed it
-  const int wf = d0 & 0x7fffffff, wl = d1;
-  const int first_slot = static_cast<int>(static_cast<uint32_t>(d0) >> 31);
+// piece groups of a split merge workgroup: group g takes pieces g, g + 16, ...
+constexpr int kMergeGroups = 16;
+
+// Running log-sum-exp merge of the pieces wf + k_first, wf + k_first +
+// k_step, ... (up to wl) of one segment, query head hq, head dims 8c..8c+7.
+// The segment's descriptor (written by the balanced kernel, see
+// decode_sk_kernel.h) names the workgroups wf..wl that hold its pieces:
+// wf's in slot first_slot, the others' in slot 0. Up to 8 pieces are read
+// per round of loads.
+__device__ __forceinline__ void merge_pieces(const SkMergeParams& p, int HWG, int hq, int c, int wf, int wl,
+                                             int first_slot, int k_first, int k_step, float& run_m, float& den,
+                                             float (&num)[8]) {
   constexpr int kChunk = 8;
-  float run_m = -INFINITY, den = 0.f;
-  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int w0 = wf; w0 <= wl; w0 += kChunk) {
+  const int D = p.head_dim;
+  for (int k0 = k_first; wf + k0 <= wl; k0 += k_step * kChunk) {
     float pm[kChunk], pl[kChunk];
     f32x4 pa[kChunk], pb[kChunk];
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
-      const int wv = w0 + k;
+      const int wv = wf + k0 + k * k_step;
       const bool valid = wv <= wl;
-      const int wr = valid ? wv : wf;  // unused slots read wf's piece with weight 0
+      const int wr = valid ? wv : wf;  // past wl: read wf's piece, weight 0
       const int slot = wr == wf ? first_slot : 0;
-      const int64_t pi = (static_cast<int64_t>(wr) * 2 + slot) * HWG + h;
+      const int64_t pi = (static_cast<int64_t>(wr) * 2 + slot) * HWG + hq;
       pm[k] = valid ? p.piece_m[pi] : -INFINITY;
       pl[k] = p.piece_l[pi];
-      const f32x4* po = reinterpret_cast<const f32x4*>(p.piece_o + pi * D + d);
+      const f32x4* po = reinterpret_cast<const f32x4*>(p.piece_o + pi * D + 8 * c);
       pa[k] = po[0];
       pb[k] = po[1];
     }
     float cm = run_m;
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) cm = fmaxf(cm, pm[k]);
-    const float r = __builtin_amdgcn_exp2f(run_m - cm);  // 0 on the first round (run_m = -inf)
+    // pieces with m = -inf (past wl, or a workgroup without units) weigh 0
+    const float r = run_m > -INFINITY ? __builtin_amdgcn_exp2f(run_m - cm) : 0.f;
     den *= r;
 #pragma unroll
     for (int e = 0; e < 8; ++e) num[e] *= r;
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
-      const float wt = pl[k] * __builtin_amdgcn_exp2f(pm[k] - cm);  // 0 for unused slots and empty ranges
+      const float wt = pm[k] > -INFINITY ? pl[k] * __builtin_amdgcn_exp2f(pm[k] - cm) : 0.f;
       den += wt;
       num[0] = fmaf(wt, pa[k].x, num[0]);
       num[1] = fmaf(wt, pa[k].y, num[1]);
@@ -158,10 +142,75 @@ __global__ __launch_bounds__(1024) void decode_sk_merge_kernel(const SkMergePara
     }
     run_m = cm;
   }
+}
+
+// Two layouts of the merge grid:
+//  * SPLIT = false: one workgroup per (head group, sequence) segment, one
+//    thread per 8 head dims of each query head of the group; a thread walks
+//    all of the segment's pieces (one round of loads per 8). Few
+//    workgroups: right when segments span few workgroups.
+//  * SPLIT = true: one workgroup per (segment, query head), D / 8 threads
+//    per piece group; kMergeGroups piece groups read up to 128 pieces in one
+//    round, and their partial merges are combined through LDS. Right when
+//    segments span many workgroups (few long sequences).
+template <bool SPLIT>
+__global__ __launch_bounds__(1024) void decode_sk_merge_kernel(const SkMergeParams p) {
+  const int HWG = p.heads_per_wg * p.group;  // query heads per head group
+  const int D = p.head_dim;
+  const int tpr = D / 8;
+  const int bx = static_cast<int>(blockIdx.x);
+  const int seg = SPLIT ? bx / HWG : bx;
+  const int s = seg % p.batch;
+  const int hg = seg / p.batch;
+  const int t = static_cast<int>(threadIdx.x);
+  const int hq = SPLIT ? bx % HWG : t / tpr;
+  const int c = t % tpr;
+  const int pg = SPLIT ? t / tpr : 0;
+  if (!SPLIT && hq >= HWG) return;
+  const int64_t orow = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(hg) * HWG + hq;
+  const int L = min(p.context_lens[s], p.len_cap);
+  const int32_t* desc = p.seg_desc + (static_cast<int64_t>(hg) * p.batch + s) * 2;
+  const int32_t d0 = desc[0], d1 = desc[1];
+  if (L <= 0) {
+    if (pg == 0) {
+      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      store_out8(p.out, orow * D + 8 * c, p.out_dtype, z);
+    }
+    return;
+  }
+  if (d0 == -1) return;  // stored by the workgroup that completed it
+  const int wf = d0 & 0x7fffffff, wl = d1;
+  const int first_slot = static_cast<int>(static_cast<uint32_t>(d0) >> 31);
+  float run_m = -INFINITY, den = 0.f;
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  merge_pieces(p, HWG, hq, c, wf, wl, first_slot, pg, SPLIT ? kMergeGroups : 1, run_m, den, num);
+  if constexpr (SPLIT) {
+    __shared__ float s_m[kMergeGroups], s_den[kMergeGroups];
+    __shared__ float s_num[kMergeGroups * 128];
+    if (c == 0) {
+      s_m[pg] = run_m;
+      s_den[pg] = den;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_num[pg * D + 8 * c + e] = num[e];
+    __syncthreads();
+    if (pg != 0) return;
+    float mx = s_m[0];
+    for (int g = 1; g < kMergeGroups; ++g) mx = fmaxf(mx, s_m[g]);
+    den = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) num[e] = 0.f;
+    for (int g = 0; g < kMergeGroups; ++g) {
+      const float w = s_m[g] > -INFINITY ? __builtin_amdgcn_exp2f(s_m[g] - mx) : 0.f;
+      den = fmaf(w, s_den[g], den);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[e] = fmaf(w, s_num[g * D + 8 * c + e], num[e]);
+    }
+  }
   float o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = num[e] / den;
-  store_out8(p.out, (head0 + h) * D + d, p.out_dtype, o);
+  store_out8(p.out, orow * D + 8 * c, p.out_dtype, o);
 }
 
 int out_code(pa_dtype t) { return t == PA_F32 ? 2 : (t == PA_BF16 ? 1 : 0); }
@@ -247,6 +296,9 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   // units (16-token tiles x head groups) must stay below 2^31
   if (static_cast<int64_t>(B) * ((static_cast<int64_t>(max_context_len) + 15) / 16) * n_hg > 0x7fffffffLL)
     return fail(PA_ERR_UNSUPPORTED, "B x max_context_len is too large for the balanced split");
+  // the merge grid: one workgroup of D / 8 * kMergeGroups threads per (sequence, query head)
+  if (static_cast<int64_t>(B) * num_q_heads * (D / 8 * kMergeGroups) > 0xffffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "B x num_q_heads is too large for the balanced split");
   if (workspace == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "the balanced split needs a workspace");
   const int cus = device_cus();
   if (cus <= 0) return fail(PA_ERR_DEVICE, "cannot read the device's CU count");
@@ -305,9 +357,16 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   m.group = G;
   m.head_dim = D;
   m.out_dtype = out_code;
-  // one thread per 8 head dims of each query head of a head group
-  const int merge_threads = (HW * G * D / 8 + 63) / 64 * 64;
-  hipLaunchKernelGGL(decode_sk_merge_kernel, dim3(B * n_hg), dim3(merge_threads), 0, stream, m);
+  // segments that span many workgroups on average (fewer segments than a
+  // quarter of the workgroups) take the split merge
+  if (static_cast<int64_t>(B) * n_hg * 4 < wgs) {
+    const int64_t merge_wgs = static_cast<int64_t>(B) * n_hg * HW * G;
+    hipLaunchKernelGGL(decode_sk_merge_kernel<true>, dim3(static_cast<uint32_t>(merge_wgs)), dim3(D / 8 * kMergeGroups),
+                       0, stream, m);
+  } else {
+    const int merge_threads = (HW * G * D / 8 + 63) / 64 * 64;
+    hipLaunchKernelGGL(decode_sk_merge_kernel<false>, dim3(B * n_hg), dim3(merge_threads), 0, stream, m);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_DEVICE, "balanced decode merge launch: %s", hipGetErrorString(e));
   return PA_OK;
