@@ -28,15 +28,19 @@ are created with hipEventDisableSystemFence (see HipTimingEvent): default
 events add a cache write-back and invalidate, ~5 us of idle queue each.
 ``cpu_baseline`` = the fp64 oracle on the host cores.
 
-``--workload long|mixed|prefix`` times decode calls on the other workloads
-instead (the long-context batch, the mixed-length batch with ``--kv`` and
-``--block-size``, the prefix-sharing batch, with ``--shared`` through
-pa_decode_shared): ``--layers`` pools whose K/V are drawn on the device
-(torch's seeded generator; fp8 pools take the scale 6/448, about the amax of
-that many N(0,1) draws) and written through pa_reshape_and_cache, then
-``--steps`` rounds of one call per layer, back to back, timed with HIP
-events. ``value`` = KV bytes per call / mean call time (no host work in the
-timed region); no cpu_baseline.
+``--workload gqa-calls|long|mixed|prefix`` times decode calls instead (the
+GQA batch through plain pa_decode, the long-context batch, the mixed-length
+batch with ``--kv`` and ``--block-size``, the prefix-sharing batch, with
+``--shared`` through pa_decode_shared): ``--layers`` pools whose K/V are
+drawn on the device (torch's seeded generator; fp8 pools take the scale
+6/448, about the amax of that many N(0,1) draws) and written through
+pa_reshape_and_cache, then ``--steps`` rounds of one call per layer, back to
+back, timed with HIP events (also around layer 0's call of each round, for
+the median and minimum). ``value`` = KV bytes per call / mean call time (no
+host work in the timed region); no cpu_baseline. ``--cold`` adds single
+calls each preceded by a 1 GiB read (cold L2 and Infinity Cache; a write
+instead, ``--cold-write``, leaves dirty lines whose write-back competes
+with the timed call).
 """
 from __future__ import annotations
 
@@ -150,8 +154,15 @@ def parse():
                         "split: pa_decode_append, both in one launch)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
-    p.add_argument("--workload", choices=["gqa", "long", "mixed", "prefix"], default="gqa",
-                   help="gqa: the decode step on the GQA batch (default); others: decode calls on that workload")
+    p.add_argument("--workload", choices=["gqa", "gqa-calls", "long", "mixed", "prefix"], default="gqa",
+                   help="gqa: the decode step on the GQA batch (default); others: decode calls on that workload "
+                        "(gqa-calls: pa_decode on the GQA batch)")
+    p.add_argument("--cold", action="store_true",
+                   help="decode-call workloads: also time --steps single calls, each after reading a 1 GiB buffer "
+                        "(evicts L2 and the Infinity Cache), reported under 'cold'")
+    p.add_argument("--cold-write", action="store_true",
+                   help="with --cold: write the 1 GiB buffer instead of reading it (its dirty lines are then written "
+                        "back during the timed call)")
     p.add_argument("--kv", choices=["bf16", "fp8"], default="bf16", help="KV dtype of the mixed workload")
     p.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32], help="block size of the mixed workload")
     p.add_argument("--shared", action="store_true",
@@ -255,7 +266,7 @@ def bench_decode_calls(args):
                      sp.max_shared_len, sp.min_shared_len)
             extra["groups"] = sp.num_groups
     else:
-        wl = (synth.long_context() if args.workload == "long"
+        wl = (synth.long_context() if args.workload == "long" else synth.gqa_decode() if args.workload == "gqa-calls"
               else synth.mixed_lengths(block_size=args.block_size, kv_dtype=args.kv))
         B, Hq, Hkv, D, bs, kv = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.kv_dtype
         sc = 6.0 / 448.0 if kv == "fp8" else 1.0
@@ -276,6 +287,8 @@ def bench_decode_calls(args):
         L = l.astype(np.int64)
         desc = ("long context: 8 seqs, context U[32768,131072], 32 q heads / 8 KV heads, head_dim 128, block 16, "
                 "bf16" if args.workload == "long" else
+                "GQA decode batch: 64 seqs, context U[512,4096], 32 q heads / 8 KV heads, head_dim 128, block 16, bf16"
+                if args.workload == "gqa-calls" else
                 f"mixed lengths: 256 seqs, context clip(lognormal(ln 1024, 1), 16, 16384), 64 q heads / 8 KV heads, "
                 f"head_dim 128, block {bs}, KV {kv}, q bf16")
     b = 1 if kv == "fp8" else 2
@@ -298,17 +311,48 @@ def bench_decode_calls(args):
             call(c)
     torch.cuda.synchronize()
     e0, e1 = HipTimingEvent(), HipTimingEvent()
+    per = [(HipTimingEvent(), HipTimingEvent()) for _ in range(K)]
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(K):
-        for c in caches:
+    for i in range(K):
+        for li, c in enumerate(caches):
+            if li == 0:
+                per[i][0].record()
             call(c)
+            if li == 0:
+                per[i][1].record()
     e1.record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     call_s = e0.elapsed_time(e1) * 1e-3 / (K * layers)
     value = call_bytes / call_s / 1e9
-    print(f"[bench] {K * layers} calls: {call_s * 1e6:.1f} us/call", file=sys.stderr, flush=True)
+    durs = np.array([a.elapsed_time(b) for a, b in per]) * 1e-3
+    print(f"[bench] {K * layers} calls: {call_s * 1e6:.1f} us/call (layer 0: median {np.median(durs) * 1e6:.1f}, "
+          f"min {durs.min() * 1e6:.1f})", file=sys.stderr, flush=True)
+    extra["pa_decode_us_median"] = round(float(np.median(durs)) * 1e6, 2)
+    extra["pa_decode_us_min"] = round(float(durs.min()) * 1e6, 2)
+    if args.cold:
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+        cold = []
+        for i in range(K):
+            if args.cold_write:
+                scratch.fill_(float(i))
+            else:
+                torch.sum(scratch, dim=0, out=sink)
+            a, b2 = HipTimingEvent(), HipTimingEvent()
+            a.record()
+            call(caches[i % layers])
+            b2.record()
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b2) * 1e-3)
+        cold = np.array(cold)
+        extra["cold"] = {"calls": K, "median_us": round(float(np.median(cold)) * 1e6, 2),
+                         "min_us": round(float(cold.min()) * 1e6, 2),
+                         "gbs_median": round(call_bytes / float(np.median(cold)) / 1e9, 2),
+                         "note": f"each call after a 1 GiB device {'write' if args.cold_write else 'read'} "
+                                 f"(cold L2 and Infinity Cache), timed alone"}
+        print(f"[bench] cold calls: median {np.median(cold) * 1e6:.1f} us", file=sys.stderr, flush=True)
     if args.workload == "prefix":
         extra["unique_kv_gbs"] = round(2 * unique_tokens * Hkv * D * b / call_s / 1e9, 2)
         extra["unique_kv_note"] = "KV bytes of distinct tokens (shared prefix counted once per prompt) / call time"
@@ -454,6 +498,8 @@ def main():
         "decode_tokens_per_s": round(B * layers * K / el, 1),
         "decode_tokens_per_s_note": "sequences x layers per second (one query token per sequence per layer)",
         "pa_decode_us": round(call_s * 1e6, 2),
+        "pa_decode_us_median": round(float(np.median(durs)) * 1e6, 2),
+        "pa_decode_us_min": round(float(durs.min()) * 1e6, 2),
         "roofline": {
             "bound": "hbm",
             "kernel": (("pa_decode_append" if fused else "pa_decode") +
