@@ -168,6 +168,9 @@ def parse():
     p.add_argument("--shared", action="store_true",
                    help="prefix workload: pa_decode_shared with groups of sequences sharing their prefix blocks "
                         "(--partition-size > 0, default 256)")
+    p.add_argument("--stream-ref", action="store_true",
+                   help="only time a plain streaming read of 4 GiB (pa_ref_stream_read), the attainable read "
+                        "bandwidth the decode is compared with, and exit")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return p.parse_args()
@@ -182,6 +185,30 @@ def calibrate_copy():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}))
+
+
+def stream_ref(steps: int):
+    """GB/s of a plain streaming read of 4 GiB (pa_ref_stream_read: 16-byte
+    non-temporal loads, grid-stride, 8192 workgroups of 256 threads), mean
+    over ``steps`` passes: the attainable read bandwidth."""
+    import torch
+    import paged_kv_cache_49_amd as pa
+    n = 4 << 30
+    grid = 8192
+    x = torch.ones(n, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pa.ref_stream_read(x, sink, grid)
+    torch.cuda.synchronize()
+    e0, e1 = HipTimingEvent(), HipTimingEvent()
+    e0.record()
+    for _ in range(steps):
+        pa.ref_stream_read(x, sink, grid)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / steps
+    print(json.dumps({"stream_ref_bytes": n, "passes": steps, "grid": grid, "us_per_pass": round(s * 1e6, 1),
+                      "gbs": round(n / s / 1e9, 1), "pct_of_hbm_peak": round(100 * n / s / 1e9 / HBM_PEAK_GBS, 2)}))
 
 
 def cpu_baseline(wl, seconds: float):
@@ -399,6 +426,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.stream_ref:
+        stream_ref(max(args.steps, 5))
         return
 
     if args.workload != "gqa":

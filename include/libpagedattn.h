@@ -497,6 +497,18 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dty
                            int32_t num_groups, int32_t max_group_size, int32_t max_shared_len,
                            int32_t min_shared_len, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement aid (not part of the method): the device's attainable read
+ * bandwidth, the reference the decode's K/V bytes per second are compared
+ * with. Reads buf[0 .. bytes) once: 16-byte non-temporal loads, a
+ * grid-stride loop over `grid` workgroups of 256 threads, every word read
+ * XOR-folded into sink[grid * 256] (device uint32, caller-owned; its
+ * contents are meaningless). buf: device, 16-byte aligned, bytes a positive
+ * multiple of 16. Asynchronous on `stream`. Errors: PA_ERR_INVALID_ARGUMENT
+ * (checked before the launch), PA_ERR_DEVICE.
+ * ---------------------------------------------------------------------- */
+pa_status pa_ref_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

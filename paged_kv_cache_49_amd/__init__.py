@@ -520,6 +520,16 @@ def decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, c
     return out
 
 
+def ref_stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int, stream=None) -> None:
+    """pa_ref_stream_read (measurement aid): read all of the device tensor
+    ``buf`` once with a plain streaming kernel of ``grid`` workgroups;
+    ``sink`` = a device int32/uint32 tensor of grid * 256 elements."""
+    if sink.numel() < grid * 256 or sink.element_size() != 4:
+        raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, "sink needs grid * 256 32-bit elements")
+    _check(lib().pa_ref_stream_read(_dev(buf, "buf"), int(buf.numel() * buf.element_size()), _dev(sink, "sink"),
+                                    int(grid), _stream(stream)))
+
+
 def copy_blocks_between(dst: KVCache, src: KVCache, pairs, stream=None) -> None:
     """pa_copy_blocks_between: dst block pairs[i][1] <- src block
     pairs[i][0] (K and V). ``pairs`` int32 [N][2], a device tensor or host

@@ -104,6 +104,7 @@ SIGNATURES = {
     "pa_bm_host_stats": (c_int, [_P, _I32P, _I32P, _I32P, POINTER(c_int64), POINTER(c_int64)]),
     "pa_bm_host_free_stack": (c_int, [_P, _P, c_int32, _I32P]),
     "pa_copy_blocks_between": (c_int, [POINTER(PaKvCache), POINTER(PaKvCache), _P, c_int32, _P]),
+    "pa_ref_stream_read": (c_int, [_P, c_int64, _P, c_int32, _P]),
     "pa_bm_set_prefix_cache": (c_int, [_P, c_int32]),
     "pa_alloc_prompt": (c_int, [_P, c_int64, _P, c_int32, _P, _I32P]),
     "pa_bm_prefix_cache_stats": (c_int, [_P, _I32P, _I32P, POINTER(c_int64), POINTER(c_int64), POINTER(c_int64)]),

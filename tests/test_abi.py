@@ -499,3 +499,19 @@ def test_cache_ops_reject_bad_arguments_before_launch():
     c8 = _fake_cache(dtype=_lib.PA_FP8_E4M3, k_scale=0.01, v_scale=0.01)
     assert L.pa_reshape_and_cache(ctypes.byref(c8), 0x1000, 0x2000, _lib.PA_FP8_E4M3, 0x3000, 4, None) == \
         _lib.PA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("buf,nbytes,sink,grid", [
+    (None, 1024, 0x2000, 4),          # no buffer
+    (0x1000, 1024, None, 4),          # no sink
+    (0x1000, 0, 0x2000, 4),           # empty
+    (0x1000, 1000, 0x2000, 4),        # not a multiple of 16
+    (0x1008, 1024, 0x2000, 4),        # misaligned
+    (0x1000, 1024, 0x2000, 0),        # no workgroups
+    (0x1000, 1024, 0x2000, 1 << 21),  # too many
+])
+def test_ref_stream_read_rejects_bad_arguments_before_launch(buf, nbytes, sink, grid):
+    """The measurement aid validates on the host; nothing is launched (the
+    addresses are never dereferenced)."""
+    rc = pa.lib().pa_ref_stream_read(buf, nbytes, sink, grid, None)
+    assert rc == _lib.PA_ERR_INVALID_ARGUMENT
