@@ -410,9 +410,10 @@ pa_status pa_copy_blocks_between(const pa_kv_cache* dst, const pa_kv_cache* src,
  *   > 0    (a multiple of 16) each context is cut into partitions of that
  *          many tokens, one workgroup each, merged by a log-sum-exp
  *          reduction;
- *   PA_PARTITION_BALANCED  the batch's 16-token tiles (all sequences and KV
- *          heads) are divided evenly over the workgroups the device holds at
- *          once, each walking its share across sequence boundaries;
+ *   PA_PARTITION_BALANCED  the batch's tiles (16 tokens; 32 for fp8 pools)
+ *          of all sequences and KV heads are divided evenly over the
+ *          workgroups the device holds at once, each walking its share
+ *          across sequence boundaries;
  *          sequences cut between workgroups are merged as above. Pools with
  *          dim-major V only (else PA_ERR_UNSUPPORTED). A workgroup serves
  *          HW KV heads (the largest divisor of num_kv_heads up to 8) and

@@ -293,10 +293,12 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   const int n_hg = hkv / HW;
   if (sk_lds_bytes(B, HW, G, D) > kSkMaxLds)
     return fail(PA_ERR_UNSUPPORTED, "B = %d is too large for the balanced split (use partition_size > 0)", B);
-  // units (16-token tiles x head groups) must stay below 2^31
+  // units (tiles x head groups) must stay below 2^31; counted in 16-token
+  // tiles, an upper bound for the 32-token tiles of fp8 pools
   if (static_cast<int64_t>(B) * ((static_cast<int64_t>(max_context_len) + 15) / 16) * n_hg > 0x7fffffffLL)
     return fail(PA_ERR_UNSUPPORTED, "B x max_context_len is too large for the balanced split");
-  // the merge grid: one workgroup of D / 8 * kMergeGroups threads per (sequence, query head)
+  // the merge grid, at most one workgroup of D / 8 * kMergeGroups threads
+  // per (sequence, query head) (its split layout)
   if (static_cast<int64_t>(B) * num_q_heads * (D / 8 * kMergeGroups) > 0xffffffffLL)
     return fail(PA_ERR_UNSUPPORTED, "B x num_q_heads is too large for the balanced split");
   if (workspace == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "the balanced split needs a workspace");
