@@ -81,6 +81,15 @@ def test_fp8_32_token_units(gpu, wgs, D, bs, G, cap):
     _check(wl, f"cap={cap}")
 
 
+@pytest.mark.parametrize("hkv", [1, 3, 6])
+def test_fp8_head_groups(gpu, wgs, hkv):
+    """32-token fp8 units with one wave (Hkv 1) and odd workgroup widths
+    (3, 6), cut between a few workgroups."""
+    wgs(5)
+    wl = synth.random_case(2700 + hkv, [33, 700, 1, 1500, 95], 4 * hkv, hkv, 128, 16, "fp8")
+    _check(wl, "cap=5")
+
+
 @pytest.mark.parametrize("hkv", [1, 3, 6, 16, 24])
 @pytest.mark.parametrize("cap", [None, 5])
 def test_head_groups(gpu, wgs, hkv, cap):
