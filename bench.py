@@ -2,7 +2,8 @@
 
 Workload (seeded synthetic, no dataset): the GQA decode batch — 64
 sequences with context lengths U[512, 4096], 32 query heads over 8 KV heads
-(group 4), head_dim 128, 16-token blocks, bf16 K/V/q, a pool of all blocks
+(group 4), head_dim 128, 16-token blocks in the page's token-major KVBlock
+layout (``--v-layout dim`` for dim-major V), bf16 K/V/q, a pool of all blocks
 plus 10% spare with shuffled physical ids. ``--layers`` attention layers
 (default 4) each hold their own K/V pool and share one block table, as the
 layers of a model do; four layers keep the working set (~2.4 GB) far above
@@ -61,7 +62,7 @@ METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) + decode toke
 HBM_PEAK_GBS = 8000.0
 # sources of the kernels a bf16 pa_decode call runs (balanced split and partitions)
 KERNEL_SOURCES = ["decode_sk_kernel.h", "decode_vt_kernel.h", "decode_kernel.h", "decode_dispatch.h", "decode.hip",
-                  "device_common.h", "decode_sk_bf16.hip", "decode_vt_bf16.hip"]
+                  "device_common.h", "decode_sk_bf16.hip", "decode_sk_bf16_tv.hip", "decode_vt_bf16.hip"]
 
 
 def kernel_hash() -> str:
@@ -147,8 +148,9 @@ def parse():
     p.add_argument("--layers", type=int, default=4)
     p.add_argument("--partition-size", type=int, default=-1,
                    help="-1: balanced split (default); 0: no split; >0: partitions of that many tokens")
-    p.add_argument("--v-layout", choices=["dim", "token"], default="dim",
-                   help="in-block V layout: dim-major (matrix-core PV) or the token-major KVBlock layout")
+    p.add_argument("--v-layout", choices=["dim", "token"], default="token",
+                   help="in-block V layout: token-major (the KVBlock layout; default) or dim-major (fp8 pools use "
+                        "dim-major in the decode-call workloads: their balanced kernels need it)")
     p.add_argument("--separate-write", action="store_true",
                    help="write the new token with pa_reshape_and_cache, then pa_decode (default with the balanced "
                         "split: pa_decode_append, both in one launch)")
@@ -265,8 +267,10 @@ def bench_decode_calls(args):
         wl = synth.prefix_sharing(partial_tail=True)
         P, S = wl.prompts, wl.samples
         B, Hq, Hkv, D, bs, kv = P * S, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, "bf16"
+        if args.shared:
+            args.v_layout = "dim"  # pa_decode_shared reads dim-major V blocks
         bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
-        caches = [pa.KVCache.allocate(wl.num_blocks, bs, Hkv, D, kv, device=dev, v_layout="dim")
+        caches = [pa.KVCache.allocate(wl.num_blocks, bs, Hkv, D, kv, device=dev, v_layout=args.v_layout)
                   for _ in range(layers)]
         mb = int(-(-(int(wl.prefix_len.max() + wl.tail_len.max()) + 2) // bs))
         batch = PagedBatch(bm, caches, mb, B, device=dev)
@@ -297,8 +301,10 @@ def bench_decode_calls(args):
               else synth.mixed_lengths(block_size=args.block_size, kv_dtype=args.kv))
         B, Hq, Hkv, D, bs, kv = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.kv_dtype
         sc = 6.0 / 448.0 if kv == "fp8" else 1.0
+        if kv == "fp8":
+            args.v_layout = "dim"
         bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
-        caches = [pa.KVCache.allocate(wl.num_blocks, bs, Hkv, D, kv, device=dev, v_layout="dim", k_scale=sc,
+        caches = [pa.KVCache.allocate(wl.num_blocks, bs, Hkv, D, kv, device=dev, v_layout=args.v_layout, k_scale=sc,
                                       v_scale=sc) for _ in range(layers)]
         for s in range(B):
             n = int(wl.lengths[s])
@@ -397,7 +403,7 @@ def bench_decode_calls(args):
         "dtype": kv,
         "data": "synthetic (seeded lengths and block ids; K/V/q drawn N(0,1) on the device)",
         "config": {"workload": desc, "batch": B, "layers": layers, "num_q_heads": Hq, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": bs, "partition_size": ps, "v_layout": "dim",
+                   "head_dim": D, "block_size": bs, "partition_size": ps, "v_layout": args.v_layout,
                    "step": f"{layers} decode calls back to back (one per layer)",
                    "mean_context": round(float(L.mean()), 1)},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -474,7 +480,7 @@ def main():
     torch.cuda.synchronize()
     print("[bench] setup done", file=sys.stderr, flush=True)
 
-    fused = args.partition_size == pa.BALANCED and args.v_layout == "dim" and not args.separate_write
+    fused = args.partition_size == pa.BALANCED and not args.separate_write
     for _ in range(W):
         batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, fused=fused)
     torch.cuda.synchronize()

@@ -312,11 +312,13 @@ pa_status pa_bm_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity, int3
  *   PA_LAYOUT_DIM_MAJOR (V[HEADS][HEAD_DIM][BLOCK], the tokens of one head
  *     dimension contiguous; the V-cache layout vLLM uses for the same reason):
  *     v[blk * block_stride + (h * head_dim + d) * block_size + t]
- * The dim-major V layout lets the decode kernel feed V straight into the
- * matrix cores (the softmax-weighted sum contracts over tokens); [note]
- * block-size section: the best block granularity depends on the attention
- * kernel's vectorisation. Both layouts are supported explicitly; neither
- * falls back to the other.
+ * The softmax-weighted sum contracts over tokens, so the matrix cores want
+ * the tokens of one head dimension together: the dim-major layout stores
+ * them so; with the token-major layout the balanced split loads V rows like
+ * K rows and transposes each unit's V tile through LDS ([note] block-size
+ * section: the best block granularity depends on the attention kernel's
+ * vectorisation). Both layouts are supported explicitly; neither falls
+ * back to the other.
  * block_stride (elements) >= block_size * num_kv_heads * head_dim; separate
  * K and V pools use exactly that, the page's interleaved KVBlock uses twice
  * that with v = k + block_size * num_kv_heads * head_dim.
@@ -414,14 +416,16 @@ pa_status pa_copy_blocks_between(const pa_kv_cache* dst, const pa_kv_cache* src,
  *          of all sequences and KV heads are divided evenly over the
  *          workgroups the device holds at once, each walking its share
  *          across sequence boundaries;
- *          sequences cut between workgroups are merged as above. Pools with
- *          dim-major V only (else PA_ERR_UNSUPPORTED). A workgroup serves
- *          HW KV heads (the largest divisor of num_kv_heads up to 8) and
- *          keeps B + 1 ints and HW * G * head_dim floats in 64 KiB of LDS,
- *          which bounds B (12287 for 8 KV heads, G = 4, head_dim 128;
- *          beyond it PA_ERR_UNSUPPORTED). The grid depends on the current
- *          device's CU count, so size the workspace on the device that runs
- *          the call.
+ *          sequences cut between workgroups are merged as above. Dim-major
+ *          V, or token-major V with F16 / BF16 pools (else
+ *          PA_ERR_UNSUPPORTED). A workgroup serves HW KV heads (the largest
+ *          divisor of num_kv_heads up to 8) and keeps B + 1 ints and HW
+ *          per-wave regions (G * head_dim floats; token-major V: at least
+ *          16 x (head_dim + 16) 16-bit elements) in 64 KiB of LDS, which
+ *          bounds B (12287 for 8 KV heads, G = 4, head_dim 128, dim-major
+ *          V; 7167 token-major; beyond it PA_ERR_UNSUPPORTED). The grid
+ *          depends on the current device's CU count, so size the workspace
+ *          on the device that runs the call.
  * Splits need a workspace of pa_decode_workspace_size(...) bytes (device,
  * 256-byte aligned, contents need no initialisation); 0 bytes otherwise
  * (workspace may be NULL).
@@ -458,8 +462,8 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
  * copy-on-write pa_copy_blocks of the step first, on the same stream.
  *
  * The other arguments, the workspace and the errors are those of pa_decode
- * with partition_size = PA_PARTITION_BALANCED. F16 and BF16 pools with
- * dim-major V only (else PA_ERR_UNSUPPORTED); k_new / v_new 16-byte
+ * with partition_size = PA_PARTITION_BALANCED. F16 and BF16 pools, either
+ * V layout (else PA_ERR_UNSUPPORTED); k_new / v_new 16-byte
  * aligned, slot_mapping 8-byte aligned (else PA_ERR_INVALID_ARGUMENT).
  * ---------------------------------------------------------------------- */
 pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const void* v_new, pa_dtype src_dtype,

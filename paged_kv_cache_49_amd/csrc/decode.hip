@@ -285,13 +285,16 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   const int32_t D = cache->head_dim;
   const int32_t G = num_q_heads / hkv;
   const bool append = k_new != nullptr;
-  const SkLaunch launch = find_decode_sk(cache->dtype, D, cache->block_size, G, append);
+  const bool tv = cache->v_layout == PA_LAYOUT_TOKEN_MAJOR;
+  const SkLaunch launch = find_decode_sk(cache->dtype, cache->v_layout, D, cache->block_size, G, append);
   if (launch == nullptr)
-    return fail(PA_ERR_UNSUPPORTED, "no balanced decode%s kernel for pool dtype %d, head_dim %d, block_size %d, group %d",
-                append ? " + append" : "", (int)cache->dtype, D, cache->block_size, G);
+    return fail(PA_ERR_UNSUPPORTED,
+                "no balanced decode%s kernel for pool dtype %d, %s V, head_dim %d, block_size %d, group %d%s",
+                append ? " + append" : "", (int)cache->dtype, tv ? "token-major" : "dim-major", D, cache->block_size, G,
+                tv ? " (token-major V: F16 and BF16 pools)" : "");
   const int HW = sk_heads_per_wg(hkv);
   const int n_hg = hkv / HW;
-  if (sk_lds_bytes(B, HW, G, D) > kSkMaxLds)
+  if (sk_lds_bytes(B, HW, G, D, tv) > kSkMaxLds)
     return fail(PA_ERR_UNSUPPORTED, "B = %d is too large for the balanced split (use partition_size > 0)", B);
   // units (tiles x head groups) must stay below 2^31; counted in 16-token
   // tiles, an upper bound for the 32-token tiles of fp8 pools
@@ -457,8 +460,8 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
                 "partition_size %d must be 0, a positive multiple of 16 or PA_PARTITION_BALANCED", partition_size);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (hkv > 65535 || B > 65535) return fail(PA_ERR_INVALID_ARGUMENT, "B and num_kv_heads must be <= 65535");
-  if (balanced && cache->v_layout != PA_LAYOUT_DIM_MAJOR)
-    return fail(PA_ERR_UNSUPPORTED, "PA_PARTITION_BALANCED needs a pool with dim-major V blocks");
+  if (balanced && cache->v_layout != PA_LAYOUT_DIM_MAJOR && cache->dtype == PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "PA_PARTITION_BALANCED with token-major V blocks takes F16 or BF16 pools");
   const int64_t P = pa::partitions_for(max_context_len, partition_size);
   if (P > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many partitions");
   const size_t need = pa::workspace_bytes_for(B, num_q_heads, D, P);
@@ -618,8 +621,6 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const vo
   if (src_dtype != cache->dtype)
     return fail(PA_ERR_UNSUPPORTED, "k_new / v_new dtype %d differs from the pool dtype %d", (int)src_dtype,
                 (int)cache->dtype);
-  if (cache->v_layout != PA_LAYOUT_DIM_MAJOR)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode_append needs a pool with dim-major V blocks");
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(slot_mapping) % 8 != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "k_new / v_new must be 16-byte aligned, slot_mapping 8-byte aligned");

@@ -46,12 +46,22 @@ inline GroupLaunch find_decode_group(pa_dtype pool, int head_dim, int block_size
 SkLaunch find_decode_sk_f16(int head_dim, int block_size, int group, bool append);
 SkLaunch find_decode_sk_bf16(int head_dim, int block_size, int group, bool append);
 SkLaunch find_decode_sk_fp8(int head_dim, int block_size, int group, bool append);
+SkLaunch find_decode_sk_f16_tv(int head_dim, int block_size, int group, bool append);
+SkLaunch find_decode_sk_bf16_tv(int head_dim, int block_size, int group, bool append);
 
-inline SkLaunch find_decode_sk(pa_dtype pool, int head_dim, int block_size, int group, bool append) {
+// the balanced split's kernel for the pool's dtype and V layout (nullptr:
+// not supported; token-major V with 16-bit pools only)
+inline SkLaunch find_decode_sk(pa_dtype pool, pa_layout v_layout, int head_dim, int block_size, int group,
+                               bool append) {
+  const bool tv = v_layout == PA_LAYOUT_TOKEN_MAJOR;
   switch (pool) {
-    case PA_F16: return find_decode_sk_f16(head_dim, block_size, group, append);
-    case PA_BF16: return find_decode_sk_bf16(head_dim, block_size, group, append);
-    case PA_FP8_E4M3: return find_decode_sk_fp8(head_dim, block_size, group, append);
+    case PA_F16:
+      return tv ? find_decode_sk_f16_tv(head_dim, block_size, group, append)
+                : find_decode_sk_f16(head_dim, block_size, group, append);
+    case PA_BF16:
+      return tv ? find_decode_sk_bf16_tv(head_dim, block_size, group, append)
+                : find_decode_sk_bf16(head_dim, block_size, group, append);
+    case PA_FP8_E4M3: return tv ? nullptr : find_decode_sk_fp8(head_dim, block_size, group, append);
     default: return nullptr;
   }
 }

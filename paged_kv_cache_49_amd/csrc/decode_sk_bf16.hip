@@ -4,6 +4,6 @@
 
 namespace pa {
 SkLaunch find_decode_sk_bf16(int head_dim, int block_size, int group, bool append) {
-  return select_decode_sk<BF16, BF16>(head_dim, block_size, group, append);
+  return select_decode_sk<BF16, BF16, false>(head_dim, block_size, group, append);
 }
 }  // namespace pa

@@ -1,0 +1,10 @@
+// Balanced-split decode kernels for BF16 pools (q BF16) with token-major V blocks
+// (the V tile of a unit transposed through LDS): head_dim 64/128, block size
+// 8/16/32, query-head group 1/2/4/8.
+#include "decode_sk_kernel.h"
+
+namespace pa {
+SkLaunch find_decode_sk_bf16_tv(int head_dim, int block_size, int group, bool append) {
+  return select_decode_sk<BF16, BF16, true>(head_dim, block_size, group, append);
+}
+}  // namespace pa

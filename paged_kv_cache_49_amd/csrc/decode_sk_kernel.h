@@ -103,11 +103,42 @@ __device__ __forceinline__ int sk_find_seq(const int32_t* pref, int B, int r) {
   return lo;
 }
 
-// bytes of dynamic LDS: the tile prefix, then per wave one G x D fp32 tile
-inline size_t sk_lds_bytes(int B, int HW, int G, int D) {
-  const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
-  return pref + static_cast<size_t>(HW) * G * D * sizeof(float);
+// LDS of one wave, in floats: its G x D fp32 output tile; with token-major
+// V (tv) at least the 16 x (D + 16) 16-bit V tile too (the two share the
+// region: the V tile is dead when a segment is stored)
+__host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D, bool tv) {
+  const size_t out = static_cast<size_t>(G) * D;
+  const size_t vt = tv ? static_cast<size_t>(16) * (D + 16) / 2 : 0;
+  return out > vt ? out : vt;
 }
+
+// bytes of dynamic LDS: the tile prefix, then one region per wave
+inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool tv) {
+  const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
+  return pref + static_cast<size_t>(HW) * sk_wave_lds_floats(G, D, tv) * sizeof(float);
+}
+
+// Four 16-bit elements of a transposing LDS read (ds_read_b64_tr_b16): in
+// each 16-lane group, lane i gets element i % 4 of the 8 bytes that lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group point at, in
+// that order.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// the lane's V registers for one unit: dim-major runs (u32x2 per n-tile) or
+// token-major row pieces (u32x4, as K)
+template <bool TV>
+struct SkVSlot {
+  using type = u32x2;
+};
+template <>
+struct SkVSlot<true> {
+  using type = u32x4;
+};
 
 // A unit as the wave sees it (uniform values). len = valid tokens counted
 // from the unit's first position; virt = the append variant's virtual tile,
@@ -117,7 +148,7 @@ struct SkUnit {
   int virt, sblk, soff;
 };
 
-template <typename KV, typename QT, int D, int BS, int G, bool AP>
+template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV>
 __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
@@ -130,8 +161,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   constexpr int kE = TT / 4;
   constexpr int kTB = BS < TT ? TT / BS : 1;
   static_assert(!AP || TT == 16, "the append variant is for 16-bit pools");
-  // V of one head dim for the lane's kE tokens: 4 x 16-bit or 8 x fp8
-  using VSlot = u32x2;
+  static_assert(!TV || kB == 2, "token-major V on the balanced split: 16-bit pools");
+  // V per lane and unit: dim-major, one run of one head dim over the lane's
+  // kE tokens per n-tile (4 x 16-bit or 8 x fp8); token-major (TV), the
+  // lane's K-like pieces of its token row, transposed through LDS
+  using VSlot = typename SkVSlot<TV>::type;
+  constexpr int kVL = TV ? C::kKLoads : kNT;
+  constexpr int kVRow = D + 16;  // 16-bit elements per row of the LDS V tile (padded against bank conflicts)
   extern __shared__ int32_t sk_smem[];
   const int B = p.batch;
   int32_t* s_pref = sk_smem;  // [B + 1]
@@ -186,7 +222,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     return;
   }
 
-  float* s_out = s_out_all + wave * G * D;
+  float* s_out = s_out_all + wave * sk_wave_lds_floats(G, D, TV);
   const int col = lane & 15, j = lane >> 4;
   const int Hkv = p.num_kv_heads;
   const char* kbase = static_cast<const char*>(p.k_pool);
@@ -246,7 +282,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   auto block_id = [&](int id) { return static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks) ? id : 0; };
   // ---- loads of one unit into a ring slot; returns the unit
   auto load_unit = [&](const Batch& b, int x, u32x4 (&qr)[C::kKSteps], u32x4 (&kr)[kSub * C::kKLoads],
-                       VSlot (&vr)[kNT]) -> SkUnit {
+                       VSlot (&vr)[kVL]) -> SkUnit {
     const int o = x - b.ub;
     SkUnit un;
     un.seq = __builtin_amdgcn_readlane(b.seq, o);
@@ -323,14 +359,18 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       const int idv = pick(t4 / BS);
       vrun = vbase + static_cast<int64_t>(idv) * blk_bytes + ((static_cast<int64_t>(g) * D + col) * BS + t4 % BS) * kB;
     }
+    // token-major V: the lane's V row sits where its K row does, in the V pool
+    const char* vrow = vbase + (krow - kbase);
     int vstep = kVTileBytes;
     if constexpr (AP) {
       if (un.virt) {
         // every K row reads the new token's row (rows past the first are
-        // masked); lane (d, j) reads the 4-dim group holding v_new[d] (the
-        // compute step moves element d % 4 into the first token's place)
+        // masked); dim-major: lane (d, j) reads the 4-dim group holding
+        // v_new[d] (the compute step moves element d % 4 into the first
+        // token's place); token-major: every V row reads v_new's row
         krow = static_cast<const char*>(p.k_new) + (static_cast<int64_t>(un.seq) * Hkv + g) * D * kB;
         vrun = static_cast<const char*>(p.v_new) + ((static_cast<int64_t>(un.seq) * Hkv + g) * D + (col & ~3)) * kB;
+        vrow = static_cast<const char*>(p.v_new) + (static_cast<int64_t>(un.seq) * Hkv + g) * D * kB;
         vstep = 16 * kB;
       }
     }
@@ -342,8 +382,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         kr[s * C::kKLoads + i] = *reinterpret_cast<const u32x4*>(krow + s * 4 * tok_bytes + off);
       }
     }
+    if constexpr (TV) {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VSlot*>(vrun + nt * vstep);
+      for (int i = 0; i < C::kKLoads; ++i) vr[i] = *reinterpret_cast<const u32x4*>(vrow + 2 * qk_dim<2>(i, j));
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VSlot*>(vrun + nt * vstep);
+    }
     return un;
   };
 
@@ -413,7 +458,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   };
 
   auto compute = [&](int x, const SkUnit& un, const u32x4 (&qb)[C::kKSteps], const u32x4 (&kr)[kSub * C::kKLoads],
-                     const VSlot (&vr)[kNT]) {
+                     const VSlot (&vr)[kVL]) {
     const int tb = AP && un.virt ? 0 : un.tile * TT;
     const int L = un.len;
     // ---- S^T = K q^T, one 16-row tile per kSub; lane (head col, j) gets
@@ -482,12 +527,29 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       for (int e = 0; e < kE; e += 2)
         vmask[e / 2] = (t + e < L ? 0xffffu : 0u) | (t + e + 1 < L ? 0xffff0000u : 0u);
     }
+    // token-major V: the wave's rows go to its LDS tile ([16][kVRow]); lane
+    // (d, j) then reads tokens 4j .. 4j + 3 of head dim 16 nt + d with one
+    // transposing read per n-tile, its group's lanes pointing at rows
+    // 4j + lane / 4, dims 4 (lane % 4) ..
+    const uint16_t* vt_src = nullptr;
+    if constexpr (TV) {
+      uint16_t* vt = reinterpret_cast<uint16_t*>(s_out);
+#pragma unroll
+      for (int i = 0; i < C::kKLoads; ++i) *reinterpret_cast<u32x4*>(vt + col * kVRow + qk_dim<2>(i, j)) = vr[i];
+      wave_lds_sync();
+      vt_src = vt + (4 * j + (col >> 2)) * kVRow + 4 * (col & 3);
+    }
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       if constexpr (TT == 16) {
-        u32x2 vop = vr[nt];
-        if constexpr (AP) {
-          if (un.virt) vop = u32x2{virt_v(vr[nt]), 0u};
+        u32x2 vop;
+        if constexpr (TV) {
+          vop = lds_read_tr16(vt_src + 16 * nt);
+        } else {
+          vop = vr[nt];
+          if constexpr (AP) {
+            if (un.virt) vop = u32x2{virt_v(vr[nt]), 0u};
+          }
         }
         vop.x &= vmask[0];
         vop.y &= vmask[1];
@@ -510,11 +572,20 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 #pragma unroll
           for (int i = 0; i < C::kKLoads; ++i) *reinterpret_cast<u32x4*>(kdst + qk_dim<kB>(i, j) * kB) = kr[i];
         }
-        uint16_t* vdst = reinterpret_cast<uint16_t*>(const_cast<char*>(vbase) + static_cast<int64_t>(un.sblk) * blk_bytes) +
-                         (static_cast<int64_t>(g) * D + col) * BS + un.soff;
-        if (j == 0) {
+        if constexpr (TV) {
+          char* vdst = const_cast<char*>(vbase) + static_cast<int64_t>(un.sblk) * blk_bytes + un.soff * tok_bytes +
+                       static_cast<int64_t>(g) * D * kB;
+          if (col == 0) {
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) vdst[nt * 16 * BS] = static_cast<uint16_t>(virt_v(vr[nt]));
+            for (int i = 0; i < C::kKLoads; ++i) *reinterpret_cast<u32x4*>(vdst + 2 * qk_dim<2>(i, j)) = vr[i];
+          }
+        } else {
+          uint16_t* vdst = reinterpret_cast<uint16_t*>(const_cast<char*>(vbase) + static_cast<int64_t>(un.sblk) * blk_bytes) +
+                           (static_cast<int64_t>(g) * D + col) * BS + un.soff;
+          if (j == 0) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) vdst[nt * 16 * BS] = static_cast<uint16_t>(virt_v(vr[nt]));
+          }
         }
       }
     }
@@ -541,7 +612,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // is requested when the step starts.
   u32x4 q0[C::kKSteps], q1[C::kKSteps], q2[C::kKSteps];
   u32x4 k0[kSub * C::kKLoads], k1[kSub * C::kKLoads], k2[kSub * C::kKLoads];
-  VSlot v0[kNT], v1[kNT], v2[kNT];
+  VSlot v0[kVL], v1[kVL], v2[kVL];
   const int ulast = u1 - 1;
   Batch cur = resolve(u0);
   Batch nxt = resolve(min(u0 + 2, ulast));
@@ -577,16 +648,16 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 
 // Launch of the balanced kernel: W = resident workgroups (occupancy x CUs),
 // at most max_wgs. Writes the grid size used to *wgs.
-template <typename KV, typename QT, int D, int BS, int G, bool AP>
+template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV>
 hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
   const int HW = p.heads_per_wg;
-  const size_t lds = sk_lds_bytes(p.batch, HW, G, D);
+  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV);
   // occupancy per (HW, LDS in 4 KiB steps); racing writers store the same value
   static int cache[9][17];  // per instantiation
   const int lb = static_cast<int>((lds + 4095) / 4096);
   int occ = (HW <= 8 && lb <= 16) ? cache[HW][lb] : 0;
   if (occ <= 0) {
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, paged_decode_sk_kernel<KV, QT, D, BS, G, AP>,
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV>,
                                                                 64 * HW, lds);
     if (e != hipSuccess) return e;
     if (occ <= 0) return hipErrorInvalidConfiguration;
@@ -595,49 +666,53 @@ hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t
   int W = cus * occ;
   W = W < max_wgs ? W : max_wgs;
   *wgs = W;
-  hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G, AP>), dim3(W), dim3(64 * HW), lds, stream, p);
+  hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV>), dim3(W), dim3(64 * HW), lds, stream, p);
   return hipGetLastError();
 }
 
-template <typename KV, typename QT, int D, int BS, bool AP>
+template <typename KV, typename QT, int D, int BS, bool AP, bool TV>
 SkLaunch select_decode_sk_g(int G) {
   switch (G) {
-    case 1: return &launch_decode_sk<KV, QT, D, BS, 1, AP>;
-    case 2: return &launch_decode_sk<KV, QT, D, BS, 2, AP>;
-    case 4: return &launch_decode_sk<KV, QT, D, BS, 4, AP>;
-    case 8: return &launch_decode_sk<KV, QT, D, BS, 8, AP>;
+    case 1: return &launch_decode_sk<KV, QT, D, BS, 1, AP, TV>;
+    case 2: return &launch_decode_sk<KV, QT, D, BS, 2, AP, TV>;
+    case 4: return &launch_decode_sk<KV, QT, D, BS, 4, AP, TV>;
+    case 8: return &launch_decode_sk<KV, QT, D, BS, 8, AP, TV>;
     default: return nullptr;
   }
 }
 
-template <typename KV, typename QT, int D, bool AP>
+template <typename KV, typename QT, int D, bool AP, bool TV>
 SkLaunch select_decode_sk_bs(int BS, int G) {
   switch (BS) {
-    case 8: return select_decode_sk_g<KV, QT, D, 8, AP>(G);
-    case 16: return select_decode_sk_g<KV, QT, D, 16, AP>(G);
-    case 32: return select_decode_sk_g<KV, QT, D, 32, AP>(G);
+    case 8: return select_decode_sk_g<KV, QT, D, 8, AP, TV>(G);
+    case 16: return select_decode_sk_g<KV, QT, D, 16, AP, TV>(G);
+    case 32: return select_decode_sk_g<KV, QT, D, 32, AP, TV>(G);
     default: return nullptr;
   }
 }
 
-// append = the fused cache write (16-bit pools only)
-template <typename KV, typename QT>
+// append = the fused cache write; TV = token-major V (both 16-bit pools only)
+template <typename KV, typename QT, bool TV>
 SkLaunch select_decode_sk(int D, int BS, int G, bool append) {
-  if (append) {
-    if constexpr (KV::kBytes != 2) {
-      return nullptr;
-    } else {
-      switch (D) {
-        case 64: return select_decode_sk_bs<KV, QT, 64, true>(BS, G);
-        case 128: return select_decode_sk_bs<KV, QT, 128, true>(BS, G);
-        default: return nullptr;
+  if constexpr (TV && KV::kBytes != 2) {
+    return nullptr;
+  } else {
+    if (append) {
+      if constexpr (KV::kBytes != 2) {
+        return nullptr;
+      } else {
+        switch (D) {
+          case 64: return select_decode_sk_bs<KV, QT, 64, true, TV>(BS, G);
+          case 128: return select_decode_sk_bs<KV, QT, 128, true, TV>(BS, G);
+          default: return nullptr;
+        }
       }
     }
-  }
-  switch (D) {
-    case 64: return select_decode_sk_bs<KV, QT, 64, false>(BS, G);
-    case 128: return select_decode_sk_bs<KV, QT, 128, false>(BS, G);
-    default: return nullptr;
+    switch (D) {
+      case 64: return select_decode_sk_bs<KV, QT, 64, false, TV>(BS, G);
+      case 128: return select_decode_sk_bs<KV, QT, 128, false, TV>(BS, G);
+      default: return nullptr;
+    }
   }
 }
 

@@ -403,7 +403,9 @@ def _decode_status(cache, **kw):
     (dict(), dict(dtype=_lib.PA_FP8_E4M3, k_scale=0.0), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(B=0), dict(), _lib.PA_OK),                             # empty batch: nothing to do
     (dict(part=-2), dict(), _lib.PA_ERR_INVALID_ARGUMENT),       # negative, not BALANCED
-    (dict(part=-1), dict(), _lib.PA_ERR_UNSUPPORTED),            # balanced split needs dim-major V
+    (dict(part=-1), dict(dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1),
+     _lib.PA_ERR_UNSUPPORTED),                                   # balanced split, token-major V: 16-bit pools
+    (dict(part=-1), dict(), _lib.PA_ERR_INVALID_ARGUMENT),       # token-major V: no workspace
     (dict(part=-1), dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR), _lib.PA_ERR_INVALID_ARGUMENT),  # no workspace
     (dict(part=-1, B=20000, max_ctx=16), dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR),
      _lib.PA_ERR_UNSUPPORTED),                                   # prefix does not fit LDS
@@ -428,7 +430,7 @@ _DIM = dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR)
 
 
 @pytest.mark.parametrize("kw,cache_kw,want", [
-    (dict(), dict(), _lib.PA_ERR_UNSUPPORTED),                                    # token-major V
+    (dict(), dict(), _lib.PA_ERR_INVALID_ARGUMENT),                               # token-major V: no workspace
     (dict(), dict(_DIM, dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1), _lib.PA_ERR_UNSUPPORTED),  # fp8 pool
     (dict(src=_lib.PA_F16), _DIM, _lib.PA_ERR_UNSUPPORTED),                       # source dtype != pool dtype
     (dict(k_new=None), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),

@@ -37,12 +37,12 @@ def wgs(monkeypatch):
     return set_wgs
 
 
-def _setup(wl):
+def _setup(wl, v_layout="dim", layout="split"):
     """Two identical caches holding L - 1 tokens per sequence, the new
     token's slots, and the device tables / lengths after the allocation."""
     bm = pa.BlockManager(wl.num_blocks, wl.block_size, wl.free_order)
     caches = [pa.KVCache.allocate(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
-                                  fill=poison_fill(wl.kv_dtype), v_layout="dim") for _ in range(2)]
+                                  fill=poison_fill(wl.kv_dtype), v_layout=v_layout, layout=layout) for _ in range(2)]
     k_new, v_new, slots = [], [], []
     for s in range(wl.batch):
         k, v = wl.kv(s)
@@ -67,10 +67,10 @@ def _setup(wl):
             torch.tensor(slots, dtype=torch.int64).cuda(), tables, lens, int(wl.lengths.max()))
 
 
-def _run(wl, what):
+def _run(wl, what, v_layout="dim", layout="split"):
     say(f"append {wl.name} kv={wl.kv_dtype} D={wl.head_dim} bs={wl.block_size} Hkv={wl.num_kv_heads} "
-        f"G={wl.group} {what}")
-    (ca, cb), k_new, v_new, slots, tables, lens, max_ctx = _setup(wl)
+        f"G={wl.group} V {v_layout} {layout} {what}")
+    (ca, cb), k_new, v_new, slots, tables, lens, max_ctx = _setup(wl, v_layout, layout)
     q = wl.q().cuda()
     # two launches: the slot write, then the decode
     pa.reshape_and_cache(ca, k_new, v_new, slots)
@@ -103,6 +103,23 @@ def test_append_parity(gpu, wgs, kv, D, bs, G, hkv, cap):
     wgs(cap)
     wl = synth.random_case(3000 + D + bs + G + hkv, LENGTHS, G * hkv, hkv, D, bs, kv)
     _run(wl, f"cap={cap}")
+
+
+TOKEN_CASES = [
+    ("bf16", 128, 16, 4, 8, "split"),
+    ("f16", 64, 8, 2, 3, "interleaved"),
+    ("bf16", 128, 32, 8, 1, "interleaved"),
+]
+
+
+@pytest.mark.parametrize("cap", [None, 3])
+@pytest.mark.parametrize("kv,D,bs,G,hkv,layout", TOKEN_CASES, ids=lambda c: str(c))
+def test_append_token_major_v(gpu, wgs, kv, D, bs, G, hkv, layout, cap):
+    """The page's token-major V blocks (split pools and the interleaved
+    K-then-V block): the new V row is written like the K row."""
+    wgs(cap)
+    wl = synth.random_case(3100 + D + bs + G + hkv, LENGTHS, G * hkv, hkv, D, bs, kv)
+    _run(wl, f"cap={cap}", v_layout="token", layout=layout)
 
 
 def test_append_gqa_batch_rows(gpu):

@@ -36,10 +36,10 @@ def wgs(monkeypatch):
     return set_wgs
 
 
-def _check(wl, what=""):
+def _check(wl, what="", v_layout="dim", layout="split"):
     say(f"balanced {wl.name} kv={wl.kv_dtype} D={wl.head_dim} bs={wl.block_size} Hkv={wl.num_kv_heads} "
-        f"G={wl.group} {what}")
-    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout="dim")
+        f"G={wl.group} V {v_layout} {layout} {what}")
+    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout=v_layout, layout=layout)
     got = run_decode(wl, cache, tables, lens, max_ctx, BAL)
     ma, rl = H.assert_close(got, H.oracle_contiguous(wl), what=f"{wl.name} {what}")
     say(f"   max-abs {ma:.2e}  rel-L2 {rl:.2e}")
@@ -65,6 +65,36 @@ def test_parity_sweep(gpu, wgs, kv, D, bs, G, hkv, cap):
     wgs(cap)
     wl = synth.random_case(2000 + D + bs + G + hkv, LENGTHS, G * hkv, hkv, D, bs, kv)
     _check(wl, f"cap={cap}")
+
+
+TOKEN_CASES = [
+    ("bf16", 128, 16, 4, "split"),
+    ("f16", 64, 16, 1, "interleaved"),
+    ("bf16", 128, 8, 8, "split"),
+    ("bf16", 64, 32, 2, "interleaved"),
+    ("f16", 128, 32, 4, "split"),
+]
+
+
+@pytest.mark.parametrize("cap", [None, 1, 7])
+@pytest.mark.parametrize("hkv", [2, 8])
+@pytest.mark.parametrize("kv,D,bs,G,layout", TOKEN_CASES, ids=lambda c: str(c))
+def test_token_major_v(gpu, wgs, kv, D, bs, G, layout, hkv, cap):
+    """The page's token-major V blocks (split pools and the interleaved
+    K-then-V block), each unit's V rows transposed through LDS."""
+    wgs(cap)
+    wl = synth.random_case(2800 + D + bs + G + hkv, LENGTHS, G * hkv, hkv, D, bs, kv)
+    _check(wl, f"cap={cap}", v_layout="token", layout=layout)
+
+
+def test_token_major_v_matches_dim_major(gpu):
+    """The same logical data in both V layouts gives the same output up to
+    fp32 rounding order (the arithmetic is the same; only the operand path
+    differs)."""
+    wl = synth.random_case(2900, [300, 1500, 17, 4000], 32, 8, 128, 16, "bf16")
+    a = _check(wl, "dim", v_layout="dim")
+    b = _check(wl, "token", v_layout="token")
+    H.assert_close(b, a, what="token-major vs dim-major")
 
 
 FP8_LENGTHS = [1, 7, 8, 9, 31, 32, 33, 63, 64, 65, 777, 1601]

@@ -1,5 +1,6 @@
 """Full-size workloads on the GPU, in the launch configuration bench.py
-times (dim-major V, balanced split), against the fp64 oracle.
+times (token-major V, the page's block layout; balanced split), against the
+fp64 oracle.
 
 * GQA batch (64 seqs, L ~ U[512,4096], 32/8 heads): every output row.
 * long context (8 seqs, L ~ U[32768,131072]): every sequence, two KV heads
@@ -24,7 +25,7 @@ from tests.gpu_util import device_setup, run_decode, say
 pytestmark = pytest.mark.gpu
 
 BENCH_PARTITION = pa.BALANCED
-BENCH_V_LAYOUT = "dim"
+BENCH_V_LAYOUT = "token"  # the page's KVBlock layout; fp8 pools take dim-major V (their balanced kernels need it)
 
 
 @pytest.mark.parametrize("part", [BENCH_PARTITION, 512], ids=["balanced", "part512"])
@@ -123,7 +124,7 @@ def test_mixed_batch_block_and_dtype_sweep(gpu, mixed_values, bs, kv):
     wl = synth.mixed_lengths(bs, kv)
     wl._kv_cache.update(mixed_values)
     say(f"mixed batch bs={bs} kv={kv}: {wl.total_tokens()} tokens, scales {wl.kv_scales()}")
-    _, cache, tables, lens, mx = device_setup(wl, v_layout=BENCH_V_LAYOUT)
+    _, cache, tables, lens, mx = device_setup(wl, v_layout=BENCH_V_LAYOUT if kv != "fp8" else "dim")
     got = run_decode(wl, cache, tables, lens, mx, BENCH_PARTITION)
     ma, rl = H.assert_close(got, H.oracle_contiguous(wl), what=f"mixed bs={bs} {kv}")
     say(f"   max-abs {ma:.2e} rel-L2 {rl:.2e}")
