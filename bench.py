@@ -61,7 +61,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) + decode tokens/s"
 HBM_PEAK_GBS = 8000.0
 # sources of the kernels a bf16 pa_decode call runs (balanced split and partitions)
-KERNEL_SOURCES = ["decode_sk_kernel.h", "decode_vt_kernel.h", "decode_kernel.h", "decode_dispatch.h", "decode.hip",
+KERNEL_SOURCES = ["decode_sk_kernel.h", "decode_vt_kernel.h", "decode_common.h", "decode_dispatch.h", "decode.hip",
                   "device_common.h", "decode_sk_bf16.hip", "decode_sk_bf16_tv.hip", "decode_vt_bf16.hip"]
 
 
@@ -267,8 +267,6 @@ def bench_decode_calls(args):
         wl = synth.prefix_sharing(partial_tail=True)
         P, S = wl.prompts, wl.samples
         B, Hq, Hkv, D, bs, kv = P * S, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, "bf16"
-        if args.shared:
-            args.v_layout = "dim"  # pa_decode_shared reads dim-major V blocks
         bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
         caches = [pa.KVCache.allocate(wl.num_blocks, bs, Hkv, D, kv, device=dev, v_layout=args.v_layout)
                   for _ in range(layers)]
@@ -301,8 +299,8 @@ def bench_decode_calls(args):
               else synth.mixed_lengths(block_size=args.block_size, kv_dtype=args.kv))
         B, Hq, Hkv, D, bs, kv = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.kv_dtype
         sc = 6.0 / 448.0 if kv == "fp8" else 1.0
-        if kv == "fp8":
-            args.v_layout = "dim"
+        if kv == "fp8" and ps == pa.BALANCED:
+            args.v_layout = "dim"  # the balanced split takes token-major V for 16-bit pools only
         bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
         caches = [pa.KVCache.allocate(wl.num_blocks, bs, Hkv, D, kv, device=dev, v_layout=args.v_layout, k_scale=sc,
                                       v_scale=sc) for _ in range(layers)]

@@ -314,8 +314,8 @@ pa_status pa_bm_free_stack(const pa_bm* bm, int32_t* out, int32_t capacity, int3
  *     v[blk * block_stride + (h * head_dim + d) * block_size + t]
  * The softmax-weighted sum contracts over tokens, so the matrix cores want
  * the tokens of one head dimension together: the dim-major layout stores
- * them so; with the token-major layout the balanced split loads V rows like
- * K rows and transposes each unit's V tile through LDS ([note] block-size
+ * them so; with the token-major layout the kernels load V rows like K rows
+ * and transpose each V tile through LDS ([note] block-size
  * section: the best block granularity depends on the attention kernel's
  * vectorisation). Both layouts are supported explicitly; neither falls
  * back to the other.
@@ -492,8 +492,8 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const vo
  * gives wrong results for the rows involved (no out-of-bounds access).
  *
  * partition_size: a positive multiple of 16 and of block_size; the
- * workspace is pa_decode_workspace_size(..., partition_size). Pools with
- * dim-major V only. Other arguments and errors as pa_decode.
+ * workspace is pa_decode_workspace_size(..., partition_size). Either V
+ * layout, any pool dtype. Other arguments and errors as pa_decode.
  * ---------------------------------------------------------------------- */
 pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,

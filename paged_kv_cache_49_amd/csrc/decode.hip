@@ -17,7 +17,7 @@
 #include <cstdlib>
 #include <vector>
 
-#include "decode_kernel.h"
+#include "decode_common.h"
 #include "decode_shared_kernel.h"
 #include "decode_sk_kernel.h"
 #include "device_common.h"
@@ -547,7 +547,7 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
   if (sh != nullptr && sh->num_groups > 0 && sh->max_shared_len > 0) {
     // group units for the shared partitions, then the rest per sequence
     // (see decode_shared_kernel.h)
-    const pa::GroupLaunch glaunch = pa::find_decode_group(cache->dtype, D, bs, G);
+    const pa::GroupLaunch glaunch = pa::find_decode_group(cache->dtype, cache->v_layout, D, bs, G);
     if (glaunch == nullptr) return fail(PA_ERR_UNSUPPORTED, "no shared-prefix kernel for these shapes");
     pa::SharedParams sp{};
     sp.group_offsets = sh->group_offsets;
@@ -639,8 +639,6 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dty
   pa::clear_error();
   pa_status st = pa::validate_cache(cache);
   if (st != PA_OK) return st;
-  if (cache->v_layout != PA_LAYOUT_DIM_MAJOR)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared needs a pool with dim-major V blocks");
   if (partition_size <= 0 || partition_size % 16 != 0 || partition_size % cache->block_size != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "partition_size %d must be a positive multiple of 16 and of block_size %d",
                 partition_size, cache->block_size);

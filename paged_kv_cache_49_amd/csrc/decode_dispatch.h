@@ -11,34 +11,43 @@ namespace pa {
 
 struct DecodeParams;
 using DecodeLaunch = hipError_t (*)(const DecodeParams&, dim3 grid, hipStream_t stream);
-// balanced split (dim-major V only): the launcher sizes the grid from the
-// device's CU count and the kernel's occupancy, at most max_wgs workgroups,
-// and reports the grid it used in *wgs
+// balanced split: the launcher sizes the grid from the device's CU count and
+// the kernel's occupancy, at most max_wgs workgroups, and reports the grid it
+// used in *wgs
 struct SkParams;
 using SkLaunch = hipError_t (*)(const SkParams&, int cus, int max_wgs, hipStream_t stream, int* wgs);
 
-DecodeLaunch find_decode_f16(int head_dim, int block_size, int group);
-DecodeLaunch find_decode_bf16(int head_dim, int block_size, int group);
-DecodeLaunch find_decode_fp8(int head_dim, int block_size, int group);
-// kernels for dim-major V blocks (PV on the matrix cores)
+// partition kernels (QK and PV on the matrix cores): dim-major V blocks, and
+// token-major V blocks (_tv: each tile's V rows transposed through LDS)
 DecodeLaunch find_decode_vt_f16(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_vt_bf16(int head_dim, int block_size, int group);
 DecodeLaunch find_decode_vt_fp8(int head_dim, int block_size, int group);
+DecodeLaunch find_decode_vt_f16_tv(int head_dim, int block_size, int group);
+DecodeLaunch find_decode_vt_bf16_tv(int head_dim, int block_size, int group);
+DecodeLaunch find_decode_vt_fp8_tv(int head_dim, int block_size, int group);
 
-// append: the variant that also writes each sequence's newest token
-// (pa_decode_append; 16-bit pools only, nullptr otherwise)
-// shared-prefix group kernels (dim-major V)
+// shared-prefix group kernels (dim-major V; _tv: token-major V)
 struct SharedParams;
 using GroupLaunch = hipError_t (*)(const DecodeParams&, const SharedParams&, dim3 grid, hipStream_t stream);
 GroupLaunch find_decode_group_f16(int head_dim, int block_size, int group);
 GroupLaunch find_decode_group_bf16(int head_dim, int block_size, int group);
 GroupLaunch find_decode_group_fp8(int head_dim, int block_size, int group);
+GroupLaunch find_decode_group_f16_tv(int head_dim, int block_size, int group);
+GroupLaunch find_decode_group_bf16_tv(int head_dim, int block_size, int group);
+GroupLaunch find_decode_group_fp8_tv(int head_dim, int block_size, int group);
 
-inline GroupLaunch find_decode_group(pa_dtype pool, int head_dim, int block_size, int group) {
+inline GroupLaunch find_decode_group(pa_dtype pool, pa_layout v_layout, int head_dim, int block_size, int group) {
+  const bool tv = v_layout == PA_LAYOUT_TOKEN_MAJOR;
   switch (pool) {
-    case PA_F16: return find_decode_group_f16(head_dim, block_size, group);
-    case PA_BF16: return find_decode_group_bf16(head_dim, block_size, group);
-    case PA_FP8_E4M3: return find_decode_group_fp8(head_dim, block_size, group);
+    case PA_F16:
+      return tv ? find_decode_group_f16_tv(head_dim, block_size, group)
+                : find_decode_group_f16(head_dim, block_size, group);
+    case PA_BF16:
+      return tv ? find_decode_group_bf16_tv(head_dim, block_size, group)
+                : find_decode_group_bf16(head_dim, block_size, group);
+    case PA_FP8_E4M3:
+      return tv ? find_decode_group_fp8_tv(head_dim, block_size, group)
+                : find_decode_group_fp8(head_dim, block_size, group);
     default: return nullptr;
   }
 }
@@ -66,14 +75,16 @@ inline SkLaunch find_decode_sk(pa_dtype pool, pa_layout v_layout, int head_dim, 
   }
 }
 
+// the partition kernel for the pool's dtype and V layout
 inline DecodeLaunch find_decode(pa_dtype pool, pa_layout v_layout, int head_dim, int block_size, int group) {
-  const bool vt = v_layout == PA_LAYOUT_DIM_MAJOR;
+  const bool tv = v_layout == PA_LAYOUT_TOKEN_MAJOR;
   switch (pool) {
-    case PA_F16: return vt ? find_decode_vt_f16(head_dim, block_size, group) : find_decode_f16(head_dim, block_size, group);
+    case PA_F16:
+      return tv ? find_decode_vt_f16_tv(head_dim, block_size, group) : find_decode_vt_f16(head_dim, block_size, group);
     case PA_BF16:
-      return vt ? find_decode_vt_bf16(head_dim, block_size, group) : find_decode_bf16(head_dim, block_size, group);
+      return tv ? find_decode_vt_bf16_tv(head_dim, block_size, group) : find_decode_vt_bf16(head_dim, block_size, group);
     case PA_FP8_E4M3:
-      return vt ? find_decode_vt_fp8(head_dim, block_size, group) : find_decode_fp8(head_dim, block_size, group);
+      return tv ? find_decode_vt_fp8_tv(head_dim, block_size, group) : find_decode_vt_fp8(head_dim, block_size, group);
     default: return nullptr;
   }
 }

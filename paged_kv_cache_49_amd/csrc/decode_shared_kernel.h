@@ -47,7 +47,7 @@ struct SharedParams {
 };
 
 // One group unit; wg < sp.group_wgs; s_out = the wave's 16 x D floats.
-template <typename KV, typename QT, int D, int BS, int G>
+template <typename KV, typename QT, int D, int BS, int G, bool TV>
 __device__ __forceinline__ void group_unit(const DecodeParams& p, const SharedParams& sp, int wg, float* s_out) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
@@ -101,7 +101,7 @@ __device__ __forceinline__ void group_unit(const DecodeParams& p, const SharedPa
   f32x4 acc[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  vt_attend<KV, QT, D, BS, G>(p, bt, g, L, tok_begin, tok_begin + ps, id_first, qb, row_ok, m_w, l_w, acc);
+  vt_attend<KV, QT, D, BS, G, TV>(p, bt, g, L, tok_begin, tok_begin + ps, id_first, qb, row_ok, m_w, l_w, acc, s_out);
 
   // rows of this tile that belong to members: a prefix of the 16
   const int nrows = min(16, (gsize - rt * kMembersPerTile) * G);
@@ -124,51 +124,54 @@ __device__ __forceinline__ void group_unit(const DecodeParams& p, const SharedPa
   }
 }
 
-template <typename KV, typename QT, int D, int BS, int G>
+template <typename KV, typename QT, int D, int BS, int G, bool TV>
 __global__ __launch_bounds__(64) void paged_decode_shared_kernel(const DecodeParams p, const SharedParams sp) {
+  // 16 output rows of D floats; also the V tile's room (token-major V)
+  static_assert(vt_tile_floats(D) <= 16 * D, "the V tile fits the output tile");
   __shared__ float s_out[16 * D];
   const int wg = static_cast<int>(blockIdx.x);
   if (wg < sp.group_wgs) {
-    group_unit<KV, QT, D, BS, G>(p, sp, wg, s_out);
+    group_unit<KV, QT, D, BS, G, TV>(p, sp, wg, s_out);
   } else {
-    vt_unit<KV, QT, D, BS, G>(p, wg - sp.group_wgs, sp.pairs, s_out);
+    vt_unit<KV, QT, D, BS, G, TV>(p, wg - sp.group_wgs, sp.pairs, s_out);
   }
 }
 
 using GroupLaunch = hipError_t (*)(const DecodeParams&, const SharedParams&, dim3 grid, hipStream_t stream);
 
-template <typename KV, typename QT, int D, int BS, int G>
+template <typename KV, typename QT, int D, int BS, int G, bool TV>
 hipError_t launch_decode_group(const DecodeParams& p, const SharedParams& sp, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_shared_kernel<KV, QT, D, BS, G>), grid, dim3(64), 0, stream, p, sp);
+  hipLaunchKernelGGL((paged_decode_shared_kernel<KV, QT, D, BS, G, TV>), grid, dim3(64), 0, stream, p, sp);
   return hipGetLastError();
 }
 
-template <typename KV, typename QT, int D, int BS>
+template <typename KV, typename QT, int D, int BS, bool TV>
 GroupLaunch select_decode_group_g(int G) {
   switch (G) {
-    case 1: return &launch_decode_group<KV, QT, D, BS, 1>;
-    case 2: return &launch_decode_group<KV, QT, D, BS, 2>;
-    case 4: return &launch_decode_group<KV, QT, D, BS, 4>;
-    case 8: return &launch_decode_group<KV, QT, D, BS, 8>;
+    case 1: return &launch_decode_group<KV, QT, D, BS, 1, TV>;
+    case 2: return &launch_decode_group<KV, QT, D, BS, 2, TV>;
+    case 4: return &launch_decode_group<KV, QT, D, BS, 4, TV>;
+    case 8: return &launch_decode_group<KV, QT, D, BS, 8, TV>;
     default: return nullptr;
   }
 }
 
-template <typename KV, typename QT, int D>
+template <typename KV, typename QT, int D, bool TV>
 GroupLaunch select_decode_group_bs(int BS, int G) {
   switch (BS) {
-    case 8: return select_decode_group_g<KV, QT, D, 8>(G);
-    case 16: return select_decode_group_g<KV, QT, D, 16>(G);
-    case 32: return select_decode_group_g<KV, QT, D, 32>(G);
+    case 8: return select_decode_group_g<KV, QT, D, 8, TV>(G);
+    case 16: return select_decode_group_g<KV, QT, D, 16, TV>(G);
+    case 32: return select_decode_group_g<KV, QT, D, 32, TV>(G);
     default: return nullptr;
   }
 }
 
-template <typename KV, typename QT>
+// TV = token-major V blocks
+template <typename KV, typename QT, bool TV>
 GroupLaunch select_decode_group(int D, int BS, int G) {
   switch (D) {
-    case 64: return select_decode_group_bs<KV, QT, 64>(BS, G);
-    case 128: return select_decode_group_bs<KV, QT, 128>(BS, G);
+    case 64: return select_decode_group_bs<KV, QT, 64, TV>(BS, G);
+    case 128: return select_decode_group_bs<KV, QT, 128, TV>(BS, G);
     default: return nullptr;
   }
 }

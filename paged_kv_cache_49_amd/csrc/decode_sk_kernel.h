@@ -1,9 +1,10 @@
-// Paged decode attention over dim-major V blocks with the whole batch's
-// work divided evenly over persistent workgroups (balanced split).
+// Paged decode attention with the whole batch's work divided evenly over
+// persistent workgroups (balanced split); V blocks dim-major, or token-major
+// for 16-bit pools (TV, each tile's V rows transposed through LDS).
 //
 // [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
 // [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
-// Same result as the other decode kernels (decode_kernel.h states what is
+// Same result as the partition kernels (decode_common.h states what is
 // computed: softmax attention of each query head over its sequence's tokens
 // in logical order, gathered through the block table); the per-tile data
 // flow (QK and PV on the matrix cores, online softmax) is that of
@@ -104,11 +105,11 @@ __device__ __forceinline__ int sk_find_seq(const int32_t* pref, int B, int r) {
 }
 
 // LDS of one wave, in floats: its G x D fp32 output tile; with token-major
-// V (tv) at least the 16 x (D + 16) 16-bit V tile too (the two share the
-// region: the V tile is dead when a segment is stored)
+// V (tv) at least the unit's V tile too (VTile: the two share the region,
+// the V tile being dead when a segment is stored)
 __host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D, bool tv) {
   const size_t out = static_cast<size_t>(G) * D;
-  const size_t vt = tv ? static_cast<size_t>(16) * (D + 16) / 2 : 0;
+  const size_t vt = tv ? static_cast<size_t>(vt_tile_floats(D)) : 0;
   return out > vt ? out : vt;
 }
 
@@ -116,17 +117,6 @@ __host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D, boo
 inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool tv) {
   const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
   return pref + static_cast<size_t>(HW) * sk_wave_lds_floats(G, D, tv) * sizeof(float);
-}
-
-// Four 16-bit elements of a transposing LDS read (ds_read_b64_tr_b16): in
-// each 16-lane group, lane i gets element i % 4 of the 8 bytes that lanes
-// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group point at, in
-// that order.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-  return __builtin_bit_cast(u32x2, r);
 }
 
 // the lane's V registers for one unit: dim-major runs (u32x2 per n-tile) or
@@ -167,7 +157,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // lane's K-like pieces of its token row, transposed through LDS
   using VSlot = typename SkVSlot<TV>::type;
   constexpr int kVL = TV ? C::kKLoads : kNT;
-  constexpr int kVRow = D + 16;  // 16-bit elements per row of the LDS V tile (padded against bank conflicts)
+  constexpr int kVRow = VTile<D>::kRow;  // 16-bit elements per row of the LDS V tile
   extern __shared__ int32_t sk_smem[];
   const int B = p.batch;
   int32_t* s_pref = sk_smem;  // [B + 1]

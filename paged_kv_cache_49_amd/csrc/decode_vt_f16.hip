@@ -5,9 +5,9 @@
 
 namespace pa {
 DecodeLaunch find_decode_vt_f16(int head_dim, int block_size, int group) {
-  return select_decode_vt<F16, F16>(head_dim, block_size, group);
+  return select_decode_vt<F16, F16, false>(head_dim, block_size, group);
 }
 GroupLaunch find_decode_group_f16(int head_dim, int block_size, int group) {
-  return select_decode_group<F16, F16>(head_dim, block_size, group);
+  return select_decode_group<F16, F16, false>(head_dim, block_size, group);
 }
 }  // namespace pa

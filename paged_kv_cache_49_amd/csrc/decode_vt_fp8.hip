@@ -5,9 +5,9 @@
 
 namespace pa {
 DecodeLaunch find_decode_vt_fp8(int head_dim, int block_size, int group) {
-  return select_decode_vt<FP8, BF16>(head_dim, block_size, group);
+  return select_decode_vt<FP8, BF16, false>(head_dim, block_size, group);
 }
 GroupLaunch find_decode_group_fp8(int head_dim, int block_size, int group) {
-  return select_decode_group<FP8, BF16>(head_dim, block_size, group);
+  return select_decode_group<FP8, BF16, false>(head_dim, block_size, group);
 }
 }  // namespace pa

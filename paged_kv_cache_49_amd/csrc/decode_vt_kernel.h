@@ -1,11 +1,11 @@
-// Paged decode attention for pools whose V blocks are dim-major
-// (V[heads][head_dim][block]): both products on the matrix cores.
+// Paged decode attention with both products on the matrix cores, for pools
+// whose V blocks are dim-major (V[heads][head_dim][block]) or token-major
+// (the page's V[block][heads][head_dim], TV).
 //
 // [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
 // [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
-// Same result as paged_decode_kernel (see decode_kernel.h for what is
-// computed and for the block-table, partition and masking rules); only the
-// data flow differs. One wave64 workgroup per (partition, sequence, KV head).
+// decode_common.h states what is computed and the block-table and masking
+// rules. One wave64 workgroup per (partition, sequence, KV head).
 //
 // Per 16-token tile:
 //  * S^T = K q^T with v_mfma_f32_16x16x32 (A = the tile's K rows, one token
@@ -21,13 +21,17 @@
 //  * V: dim-major blocks give each lane the 4 consecutive tokens of one head
 //    dimension as one 8-byte load (a 16-dim tile of a 16-token block is 512
 //    contiguous bytes), which is exactly the B operand (k = tokens, n = dim).
+//    Token-major blocks (TV): the tile's V rows load like its K rows, go to
+//    the wave's LDS tile (fp8 widened to bf16 on the way) and come back
+//    transposed, one ds_read_b64_tr_b16 per 16-dim n-tile giving the same
+//    operand.
 //  * acc: one 16x16 fp32 tile per 16 head dims, rows = heads.
 // Unused weight rows (heads >= G) are zero; V elements of tokens past the
 // end are zeroed with masks (never multiplied by a zero weight), so NaN in
 // unused cache slots cannot reach the result.
 #pragma once
 
-#include "decode_kernel.h"
+#include "decode_common.h"
 
 namespace pa {
 
@@ -36,6 +40,42 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Four 16-bit elements of a transposing LDS read (ds_read_b64_tr_b16): in
+// each 16-lane group, lane i gets element i % 4 of the 8 bytes that lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group point at, in
+// that order.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// A 16-token V tile in LDS for the transposing reads: 16 rows of D 16-bit
+// elements, padded by 16 elements (the reads of a 16-lane group then hit
+// distinct banks). kVTileRow elements per row; vt_tile_floats(D) = its size
+// in floats.
+template <int D>
+struct VTile {
+  static constexpr int kRow = D + 16;
+};
+__host__ __device__ constexpr int vt_tile_floats(int D) { return 16 * (D + 16) / 2; }
+
+// V registers per lane and tile: dim-major runs (4 tokens of one head dim:
+// u32x2 for 16-bit pools, one dword for fp8), or token-major row pieces
+// (u32x4, as K)
+template <typename KV, bool TV>
+struct VtVRegs {
+  using type = u32x2;
+};
+template <>
+struct VtVRegs<FP8, false> {
+  using type = uint32_t;
+};
+template <typename KV>
+struct VtVRegs<KV, true> {
+  using type = u32x4;
+};
 
 template <typename T>
 __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c);
@@ -99,14 +139,18 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 //    after QK(t) has consumed K(t), and V(t+1) right after PV(t) has
 //    consumed V(t); loads complete in order, so QK(t+1) waits only for
 //    K(t+1) while V(t+1) is still in flight, and vice versa.
-template <typename KV, typename QT, int D, int BS, int G>
+// s_lds: the wave's LDS region (token-major V only; vt_tile_floats(D)
+// floats), free again when the call returns.
+template <typename KV, typename QT, int D, int BS, int G, bool TV>
 __device__ __forceinline__ void vt_attend(const DecodeParams& p, const int32_t* bt, int g, int L, int tok_begin,
                                           int tok_end, int id_first, const u32x4 (&qb)[D / 32], bool row_ok,
-                                          float& m_w, float& l_w, f32x4 (&acc)[D / 16]) {
+                                          float& m_w, float& l_w, f32x4 (&acc)[D / 16], float* s_lds) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
   constexpr int kNT = D / 16;
-  using VRaw = typename VVecT<KV>::raw_dm;
+  using VRaw = typename VtVRegs<KV, TV>::type;
+  constexpr int kVL = TV ? C::kKLoads : kNT;  // V loads per lane and tile
+  constexpr int kVRow = VTile<D>::kRow;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, j = lane >> 4;
   const char* kbase = static_cast<const char*>(p.k_pool);
@@ -158,28 +202,51 @@ __device__ __forceinline__ void vt_attend(const DecodeParams& p, const int32_t* 
         kr[i] = *reinterpret_cast<const u32x4*>(krow + (BS >= 16 ? off - qk_dim<kB>(0, j) * kB : off));
       }
     };
-    // V runs: 4 tokens of one head dim per lane and n-tile
-    auto load_v = [&](int tile, VRaw (&vr)[kNT]) {
+    // V: dim-major, runs of 4 tokens of one head dim per lane and n-tile;
+    // token-major, the lane's pieces of its token row, exactly as K
+    auto load_v = [&](int tile, VRaw (&vr)[kVL]) {
       const int tb = c0 + tile * 16;
-      const int t = tb + 4 * j;
-      const char* vrun;
-      if constexpr (BS >= 16) {
-        vrun = vbase + static_cast<int64_t>(phys_of(tb)) * blk_bytes + (tb % BS) * kB + voff_lane;
-      } else {
-        vrun = vbase + static_cast<int64_t>(phys_of(t)) * blk_bytes + vlane_bytes + (t % BS) * kB;
-      }
+      if constexpr (TV) {
+        const int t = tb + col;
+        const char* vrow;
+        if constexpr (BS >= 16) {
+          vrow = vbase + static_cast<int64_t>(phys_of(tb)) * blk_bytes + (tb % BS) * tok_bytes + koff_lane;
+        } else {
+          vrow = vbase + static_cast<int64_t>(phys_of(t)) * blk_bytes + (t % BS) * tok_bytes + khead_bytes;
+        }
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VRaw*>(vrun + nt * kVTileBytes);
+        for (int i = 0; i < C::kKLoads; ++i) {
+          const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
+          vr[i] = *reinterpret_cast<const u32x4*>(vrow + (BS >= 16 ? off - qk_dim<kB>(0, j) * kB : off));
+        }
+      } else {
+        const int t = tb + 4 * j;
+        const char* vrun;
+        if constexpr (BS >= 16) {
+          vrun = vbase + static_cast<int64_t>(phys_of(tb)) * blk_bytes + (tb % BS) * kB + voff_lane;
+        } else {
+          vrun = vbase + static_cast<int64_t>(phys_of(t)) * blk_bytes + vlane_bytes + (t % BS) * kB;
+        }
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VRaw*>(vrun + nt * kVTileBytes);
+      }
     };
 
     // Loads are staggered over single buffers: K(t+1) is requested right
     // after QK(t) has consumed K(t), and V(t+1) right after PV(t) has
     // consumed V(t). Loads complete in order, so QK(t+1) waits only for
     // K(t+1) while V(t+1) is still in flight, and vice versa.
+    // The requests stay where they are written (K before V, tile by tile):
+    // with token-major V its registers are free as soon as the rows are in
+    // LDS, and the scheduler would otherwise hoist V(t+1) above K(t+1), so
+    // that QK(t+1) waited for both.
     u32x4 kr[C::kKLoads];
-    VRaw vr[kNT];
+    VRaw vr[kVL];
+    __builtin_amdgcn_sched_barrier(0);
     load_k(0, kr);
+    __builtin_amdgcn_sched_barrier(0);
     load_v(0, vr);
+    __builtin_amdgcn_sched_barrier(0);
     for (int tile = 0; tile < ntiles; ++tile) {
       const int tb = c0 + tile * 16;
       const int next = tile + 1 < ntiles ? tile + 1 : tile;  // a missing next tile re-requests this one
@@ -197,7 +264,9 @@ __device__ __forceinline__ void vt_attend(const DecodeParams& p, const int32_t* 
           sacc = mfma_16x16x32<QT>(u32x4{b2.x, b2.y, b3.x, b3.y}, qb[2 * a + 1], sacc);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
       load_k(next, kr);
+      __builtin_amdgcn_sched_barrier(0);
       float sv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[r] = tb + 4 * j + r < tok_end ? sacc[r] * p.qk_scale_log2 : -INFINITY;
@@ -236,10 +305,36 @@ __device__ __forceinline__ void vt_attend(const DecodeParams& p, const int32_t* 
         vmask.x = (t < tok_end ? 0xffffu : 0u) | (t + 1 < tok_end ? 0xffff0000u : 0u);
         vmask.y = (t + 2 < tok_end ? 0xffffu : 0u) | (t + 3 < tok_end ? 0xffff0000u : 0u);
       }
+      // token-major V: the tile's rows into the wave's LDS tile (fp8 widened
+      // to bf16), then lane (d, j) reads tokens 4j .. 4j + 3 of head dim
+      // 16 nt + d with one transposing read per n-tile, its group's lanes
+      // pointing at rows 4j + lane / 4, dims 4 (lane % 4) ..
+      const uint16_t* vt_src = nullptr;
+      if constexpr (TV) {
+        uint16_t* vt = reinterpret_cast<uint16_t*>(s_lds);
+        if constexpr (kB == 2) {
+#pragma unroll
+          for (int i = 0; i < C::kKLoads; ++i)
+            *reinterpret_cast<u32x4*>(vt + col * kVRow + qk_dim<2>(i, j)) = vr[i];
+        } else {
+#pragma unroll
+          for (int a = 0; a < C::kKLoads; ++a) {
+            const u32x2 b0 = e4m3x4_to_bf16x4(vr[a].x), b1 = e4m3x4_to_bf16x4(vr[a].y);
+            const u32x2 b2 = e4m3x4_to_bf16x4(vr[a].z), b3 = e4m3x4_to_bf16x4(vr[a].w);
+            uint16_t* dst = vt + col * kVRow + qk_dim<1>(2 * a, j);
+            *reinterpret_cast<u32x4*>(dst) = u32x4{b0.x, b0.y, b1.x, b1.y};
+            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{b2.x, b2.y, b3.x, b3.y};
+          }
+        }
+        wave_lds_sync();
+        vt_src = vt + (4 * j + (col >> 2)) * kVRow + 4 * (col & 3);
+      }
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         u32x2 vop;
-        if constexpr (kB == 2) {
+        if constexpr (TV) {
+          vop = lds_read_tr16(vt_src + 16 * nt);
+        } else if constexpr (kB == 2) {
           vop = vr[nt];
         } else {
           vop = e4m3x4_to_bf16x4(vr[nt]);
@@ -249,7 +344,9 @@ __device__ __forceinline__ void vt_attend(const DecodeParams& p, const int32_t* 
         acc[nt] = mfma_16x16x16<QT>(phi, vop, acc[nt]);
         acc[nt] = mfma_16x16x16<QT>(plo, vop, acc[nt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
       load_v(next, vr);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -286,7 +383,7 @@ __device__ __forceinline__ float vt_normalise(const f32x4 (&acc)[D / 16], float 
 // p.shared_len (pa_decode_shared) partition indices count from the
 // sequence's first partition past its shared prefix (the shared ones are
 // computed once per group).
-template <typename KV, typename QT, int D, int BS, int G>
+template <typename KV, typename QT, int D, int BS, int G, bool TV>
 __device__ __forceinline__ void vt_unit(const DecodeParams& p, int wg, int pairs, float* s_out) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
@@ -342,7 +439,7 @@ __device__ __forceinline__ void vt_unit(const DecodeParams& p, int wg, int pairs
   f32x4 acc[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  vt_attend<KV, QT, D, BS, G>(p, bt, g, L, tok_begin, tok_end, id_first, qb, col < G, m_w, l_w, acc);
+  vt_attend<KV, QT, D, BS, G, TV>(p, bt, g, L, tok_begin, tok_end, id_first, qb, col < G, m_w, l_w, acc, s_out);
 
   // ---- epilogue: normalised rows through LDS for wide stores
   const float l_head = vt_normalise<D>(acc, l_w, p.v_scale, G, s_out);
@@ -367,44 +464,48 @@ __device__ __forceinline__ void vt_unit(const DecodeParams& p, int wg, int pairs
   }
 }
 
-template <typename KV, typename QT, int D, int BS, int G>
+template <typename KV, typename QT, int D, int BS, int G, bool TV>
 __global__ __launch_bounds__(64) void paged_decode_vt_kernel(const DecodeParams p) {
-  __shared__ float s_out[G * D];
-  vt_unit<KV, QT, D, BS, G>(p, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x) / p.num_partitions, s_out);
+  // the output tile (G x D floats), which holds the V tile while the unit
+  // runs (token-major V)
+  __shared__ float s_out[TV && vt_tile_floats(D) > G * D ? vt_tile_floats(D) : G * D];
+  vt_unit<KV, QT, D, BS, G, TV>(p, static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x) / p.num_partitions,
+                                s_out);
 }
 
-template <typename KV, typename QT, int D, int BS, int G>
+template <typename KV, typename QT, int D, int BS, int G, bool TV>
 hipError_t launch_decode_vt(const DecodeParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_vt_kernel<KV, QT, D, BS, G>), grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((paged_decode_vt_kernel<KV, QT, D, BS, G, TV>), grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <typename KV, typename QT, int D, int BS>
+template <typename KV, typename QT, int D, int BS, bool TV>
 DecodeLaunch select_decode_vt_g(int G) {
   switch (G) {
-    case 1: return &launch_decode_vt<KV, QT, D, BS, 1>;
-    case 2: return &launch_decode_vt<KV, QT, D, BS, 2>;
-    case 4: return &launch_decode_vt<KV, QT, D, BS, 4>;
-    case 8: return &launch_decode_vt<KV, QT, D, BS, 8>;
+    case 1: return &launch_decode_vt<KV, QT, D, BS, 1, TV>;
+    case 2: return &launch_decode_vt<KV, QT, D, BS, 2, TV>;
+    case 4: return &launch_decode_vt<KV, QT, D, BS, 4, TV>;
+    case 8: return &launch_decode_vt<KV, QT, D, BS, 8, TV>;
     default: return nullptr;
   }
 }
 
-template <typename KV, typename QT, int D>
+template <typename KV, typename QT, int D, bool TV>
 DecodeLaunch select_decode_vt_bs(int BS, int G) {
   switch (BS) {
-    case 8: return select_decode_vt_g<KV, QT, D, 8>(G);
-    case 16: return select_decode_vt_g<KV, QT, D, 16>(G);
-    case 32: return select_decode_vt_g<KV, QT, D, 32>(G);
+    case 8: return select_decode_vt_g<KV, QT, D, 8, TV>(G);
+    case 16: return select_decode_vt_g<KV, QT, D, 16, TV>(G);
+    case 32: return select_decode_vt_g<KV, QT, D, 32, TV>(G);
     default: return nullptr;
   }
 }
 
-template <typename KV, typename QT>
+// TV = token-major V blocks
+template <typename KV, typename QT, bool TV>
 DecodeLaunch select_decode_vt(int D, int BS, int G) {
   switch (D) {
-    case 64: return select_decode_vt_bs<KV, QT, 64>(BS, G);
-    case 128: return select_decode_vt_bs<KV, QT, 128>(BS, G);
+    case 64: return select_decode_vt_bs<KV, QT, 64, TV>(BS, G);
+    case 128: return select_decode_vt_bs<KV, QT, 128, TV>(BS, G);
     default: return nullptr;
   }
 }

@@ -459,7 +459,7 @@ def _shared_status(cache, **kw):
 
 
 @pytest.mark.parametrize("kw,cache_kw,want", [
-    (dict(), dict(), _lib.PA_ERR_UNSUPPORTED),                           # token-major V
+    (dict(part=0), dict(), _lib.PA_ERR_INVALID_ARGUMENT),                # token-major V: needs partitions too
     (dict(part=0), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                  # needs partitions
     (dict(part=24), _DIM, _lib.PA_ERR_INVALID_ARGUMENT),                 # not a multiple of 16
     (dict(part=16), dict(_DIM, block_size=32), _lib.PA_ERR_INVALID_ARGUMENT),  # not a multiple of block_size

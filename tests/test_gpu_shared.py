@@ -27,7 +27,7 @@ def _values(rng, shape, kv):
     return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(_T[kv])
 
 
-def _build(seed, prompts, samples, tail_max, G, hkv, D, bs, kv):
+def _build(seed, prompts, samples, tail_max, G, hkv, D, bs, kv, v_layout="dim"):
     """Prefill prompts, fork samples, append tails; returns everything a
     decode call and the oracle need."""
     rng = np.random.default_rng(seed)
@@ -43,7 +43,7 @@ def _build(seed, prompts, samples, tail_max, G, hkv, D, bs, kv):
     nb = total // bs + 4 * B + 16
     bm = pa.BlockManager(nb, bs, np.random.default_rng(seed + 1).permutation(nb).astype(np.int32))
     ks, vs = FP8_SCALES if kv == "fp8" else (1.0, 1.0)
-    cache = pa.KVCache.allocate(nb, bs, hkv, D, kv, fill=poison_fill(kv), v_layout="dim", k_scale=ks, v_scale=vs)
+    cache = pa.KVCache.allocate(nb, bs, hkv, D, kv, fill=poison_fill(kv), v_layout=v_layout, k_scale=ks, v_scale=vs)
     first_row = {}
     for row, (p, kp, vp, kt, vt) in enumerate(seqs):
         if p in first_row:
@@ -76,9 +76,9 @@ def _oracle(seqs, q, hkv, scale, kv):
     return out
 
 
-def _run(seed, prompts, samples, tail_max, G, hkv, D, bs, kv, ps, what=""):
-    say(f"shared {what}: prompts {prompts} x {samples} G={G} Hkv={hkv} D={D} bs={bs} {kv} ps={ps}")
-    bm, cache, seqs, tables, lens, q, mb = _build(seed, prompts, samples, tail_max, G, hkv, D, bs, kv)
+def _run(seed, prompts, samples, tail_max, G, hkv, D, bs, kv, ps, what="", v_layout="dim"):
+    say(f"shared {what}: prompts {prompts} x {samples} G={G} Hkv={hkv} D={D} bs={bs} {kv} ps={ps} V {v_layout}")
+    bm, cache, seqs, tables, lens, q, mb = _build(seed, prompts, samples, tail_max, G, hkv, D, bs, kv, v_layout)
     B = len(seqs)
     sp = bm.shared_prefixes(list(range(B)), ps)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
@@ -116,6 +116,19 @@ def test_shared_parity(gpu, kv, D, bs, G, hkv, ps):
     # partial last block; 1-member group, 17-member group (> 16 / G rows)
     sp = _run(4000 + D + bs + G, [1100, 700, 2000, 90, 1301], [3, 1, 17, 4, 5], 80, G, hkv, D, bs, kv, ps,
               what=f"{kv} D{D} bs{bs} G{G}")
+    assert sp.num_groups >= 2
+
+
+@pytest.mark.parametrize("kv,D,bs,G,hkv,ps", [
+    ("bf16", 128, 16, 4, 8, 512),
+    ("f16", 64, 8, 8, 2, 256),
+    ("fp8", 128, 32, 4, 4, 512),
+], ids=lambda c: str(c))
+def test_shared_token_major_v(gpu, kv, D, bs, G, hkv, ps):
+    """The page's token-major V blocks: each tile's V rows go through the
+    wave's LDS tile (fp8 widened to bf16) into the PV operand."""
+    sp = _run(4200 + D + bs + G, [1100, 700, 2000, 90, 1301], [3, 1, 17, 4, 5], 80, G, hkv, D, bs, kv, ps,
+              what=f"{kv} D{D} bs{bs} G{G}", v_layout="token")
     assert sp.num_groups >= 2
 
 
