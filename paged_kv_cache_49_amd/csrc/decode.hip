@@ -230,12 +230,32 @@ size_t workspace_bytes_for(int64_t B, int64_t Hq, int64_t D, int64_t P) {
 // At most kSkWavesPerCu waves of the balanced kernel per CU: it bounds the
 // grid, so the piece buffers can be sized before the launch.
 constexpr int kSkWavesPerCu = 32;
-constexpr size_t kSkMaxLds = 64 * 1024;
 
-// KV heads per workgroup: the largest divisor of num_kv_heads up to 8
-int sk_heads_per_wg(int hkv) {
+// LDS one workgroup of the balanced kernel may use: 64 KiB, or with the
+// stage of token-major V up to gfx950's 160 KiB, as far as the device allows
+// per workgroup (sk_device_lds)
+constexpr size_t kSkMaxLds = 64 * 1024;
+constexpr size_t kSkMaxLdsStage = 160 * 1024;
+
+// LDS the current device allows one workgroup (cached per device; 0 if it
+// cannot be read)
+size_t sk_device_lds() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return static_cast<size_t>(cache[dev]);
+  int n = 0, optin = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) == hipSuccess && optin > n) n = optin;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return static_cast<size_t>(n);
+}
+
+// KV heads per workgroup: the largest divisor of num_kv_heads up to 8 (a
+// power of two with token-major V: the stage splits a row slice by shifts)
+int sk_heads_per_wg(int hkv, bool tv) {
   for (int hw = 8; hw > 1; --hw)
-    if (hkv % hw == 0) return hw;
+    if (hkv % hw == 0 && (!tv || (hw & (hw - 1)) == 0)) return hw;
   return 1;
 }
 
@@ -292,9 +312,10 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
                 "no balanced decode%s kernel for pool dtype %d, %s V, head_dim %d, block_size %d, group %d%s",
                 append ? " + append" : "", (int)cache->dtype, tv ? "token-major" : "dim-major", D, cache->block_size, G,
                 tv ? " (token-major V: F16 and BF16 pools)" : "");
-  const int HW = sk_heads_per_wg(hkv);
+  const int HW = sk_heads_per_wg(hkv, tv);
   const int n_hg = hkv / HW;
-  if (sk_lds_bytes(B, HW, G, D, tv) > kSkMaxLds)
+  const size_t lds = sk_lds_bytes(B, HW, G, D, tv);
+  if (lds > (tv ? kSkMaxLdsStage : kSkMaxLds))
     return fail(PA_ERR_UNSUPPORTED, "B = %d is too large for the balanced split (use partition_size > 0)", B);
   // units (tiles x head groups) must stay below 2^31; counted in 16-token
   // tiles, an upper bound for the 32-token tiles of fp8 pools
@@ -307,6 +328,13 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   if (workspace == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "the balanced split needs a workspace");
   const int cus = device_cus();
   if (cus <= 0) return fail(PA_ERR_DEVICE, "cannot read the device's CU count");
+  if (lds > kSkMaxLds) {
+    const size_t dev_lds = sk_device_lds();
+    if (dev_lds == 0) return fail(PA_ERR_DEVICE, "cannot read the device's LDS size");
+    if (lds > dev_lds)
+      return fail(PA_ERR_UNSUPPORTED, "the balanced split needs %zu bytes of LDS per workgroup (device: %zu)", lds,
+                  dev_lds);
+  }
   const SkLayout lay = sk_layout(B, num_q_heads, hkv, D, cus);
   if (workspace == nullptr || workspace_bytes < lay.total)
     return fail(PA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed (got %zu)", lay.total,

@@ -104,19 +104,34 @@ __device__ __forceinline__ int sk_find_seq(const int32_t* pref, int B, int r) {
   return lo;
 }
 
-// LDS of one wave, in floats: its G x D fp32 output tile; with token-major
-// V (tv) at least the unit's V tile too (VTile: the two share the region,
-// the V tile being dead when a segment is stored)
-__host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D, bool tv) {
-  const size_t out = static_cast<size_t>(G) * D;
-  const size_t vt = tv ? static_cast<size_t>(vt_tile_floats(D)) : 0;
-  return out > vt ? out : vt;
+// LDS of one wave, in floats: its G x D fp32 output tile
+__host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D) { return static_cast<size_t>(G) * D; }
+
+// Token-major V (16-bit pools): the unit's K and V rows are staged in LDS as
+// two [16][S] tiles, S = HW * D * 2 bytes (the head group's slice of a token
+// row). Row pitches: K rows S + 16 bytes (the 16 lanes of a 16-byte operand
+// read, one row apart, then start 4 banks apart), V rows S + 32 bytes (a
+// 16-lane group of the transposing read touches 4 rows of 32 bytes, which
+// then sit 8 banks apart).
+__host__ __device__ inline constexpr int sk_stage_kpitch(int S) { return S + 16; }
+__host__ __device__ inline constexpr int sk_stage_vpitch(int S) { return S + 32; }
+__host__ __device__ inline constexpr size_t sk_stage_bytes(int HW, int D) {
+  return 16 * static_cast<size_t>(sk_stage_kpitch(HW * D * 2) + sk_stage_vpitch(HW * D * 2));
 }
 
-// bytes of dynamic LDS: the tile prefix, then one region per wave
+// bytes of dynamic LDS: the tile prefix, the stage (token-major V), then one
+// region per wave
 inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool tv) {
   const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
-  return pref + static_cast<size_t>(HW) * sk_wave_lds_floats(G, D, tv) * sizeof(float);
+  return pref + (tv ? sk_stage_bytes(HW, D) : 0) + static_cast<size_t>(HW) * sk_wave_lds_floats(G, D) * sizeof(float);
+}
+
+// Barrier for LDS written by some waves of the workgroup and read by others
+// (orders LDS accesses only: loads in flight stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // the lane's V registers for one unit: dim-major runs (u32x2 per n-tile) or
@@ -154,18 +169,25 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   static_assert(!TV || kB == 2, "token-major V on the balanced split: 16-bit pools");
   // V per lane and unit: dim-major, one run of one head dim over the lane's
   // kE tokens per n-tile (4 x 16-bit or 8 x fp8); token-major (TV), the
-  // lane's K-like pieces of its token row, transposed through LDS
+  // lane's share of the unit's rows, as K (see the stage below)
   using VSlot = typename SkVSlot<TV>::type;
   constexpr int kVL = TV ? C::kKLoads : kNT;
-  constexpr int kVRow = VTile<D>::kRow;  // 16-bit elements per row of the LDS V tile
+  // q per lane and unit: the QK operand (kKSteps pieces), or with the stage
+  // (TV) the wave's G x D q rows as 16-byte pieces (lane l, piece i: byte
+  // 16 (64 i + l) of the rows), rebuilt through the wave's LDS region
+  constexpr int kQBytes = G * D * 2;
+  constexpr int kQL = TV ? (kQBytes > 1024 ? kQBytes / 1024 : 1) : C::kKSteps;
+  constexpr int kQPitch = D * 2 + 16;  // bytes per q row in LDS (rows 4 banks apart)
+  static_assert(!TV || G * kQPitch <= static_cast<int>(sk_wave_lds_floats(G, D) * sizeof(float)),
+                "the q rows fit the wave's LDS region");
   extern __shared__ int32_t sk_smem[];
   const int B = p.batch;
   int32_t* s_pref = sk_smem;  // [B + 1]
-  float* s_out_all = reinterpret_cast<float*>(sk_smem + (B + 1 + 3) / 4 * 4);
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int HW = p.heads_per_wg;
+  char* stage = reinterpret_cast<char*>(sk_smem + (B + 1 + 3) / 4 * 4);  // token-major V only
+  float* s_out_all = reinterpret_cast<float*>(stage + (TV ? sk_stage_bytes(HW, D) : 0));
 
   // ---- plan: tiles per sequence, then their exclusive prefix (in place)
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
@@ -212,7 +234,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     return;
   }
 
-  float* s_out = s_out_all + wave * sk_wave_lds_floats(G, D, TV);
+  float* s_out = s_out_all + wave * sk_wave_lds_floats(G, D);
   const int col = lane & 15, j = lane >> 4;
   const int Hkv = p.num_kv_heads;
   const char* kbase = static_cast<const char*>(p.k_pool);
@@ -224,15 +246,31 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // of head dim `col` from token 4j
   const uint32_t koff_lane = static_cast<uint32_t>(col * tok_bytes + qk_dim<kB>(0, j) * kB);
   const uint32_t voff_lane = static_cast<uint32_t>((col * BS + 4 * j) * kB);
+  // Token-major V: the unit's K and V rows of the head group are read as
+  // whole rows, not in the MFMA layout (a wave reading its own head's 256
+  // bytes of 16 rows per instruction streams measurably slower than reading
+  // 1 KiB contiguous). The [16][S] slice is split evenly over the HW waves
+  // (kKLoads KiB each): lane piece i is byte f % S of row f / S,
+  // f = (wave * kKLoads + i) KiB + 16 lane. Each unit then goes through the
+  // LDS stage: written as loaded, read back per wave in the operand layouts.
+  // S is a power of two (HW is, for token-major V).
+  const int S = HW * D * kB;
+  const int s_log2 = __builtin_ctz(static_cast<unsigned>(S));
+  const int kpitch = sk_stage_kpitch(S), vpitch = sk_stage_vpitch(S);
+  char* stage_v = stage + 16 * kpitch;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto st_f = [&](int i) { return (wave_u * C::kKLoads + i) * 1024 + lane * 16; };
+  auto st_r = [&](int i) { return st_f(i) >> s_log2; };
+  auto st_cb = [&](int i) { return st_f(i) & (S - 1); };
 
   // ---- unit batches: lane i resolves unit ub + i (ub is uniform). The
   // length and block ids are kept as loaded (clamped when a unit is read
   // out), so nothing waits for these loads until the batch is used.
   struct Batch {
     int ub;
-    int seq, tile, len, hg;
+    int seq, tile, len, hg;  // append: tile = ~t for the virtual tile
     int id0, id1, id2, id3;  // the tile's blocks (the first kTB)
-    int virt, sblk, soff;  // append only
+    int64_t slot;            // append only: slot_mapping[seq] as loaded
   };
   // Lanes past the range resolve the range's last unit: every lane loads,
   // so the loads land in the batch registers with no merge that would wait.
@@ -245,33 +283,26 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     const int s = sk_find_seq(s_pref, B, r);
     const int t = r - s_pref[s];
     const int32_t* row = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
-    b.virt = AP && t == s_pref[s + 1] - s_pref[s] - 1;
+    const bool virt = AP && t == s_pref[s + 1] - s_pref[s] - 1;
     // (a virtual tile reads no cache block; its table index could lie past
     // the table's end)
-    const int blk_a = b.virt ? 0 : (t * TT) / BS;
+    const int blk_a = virt ? 0 : (t * TT) / BS;
     b.len = p.context_lens[s];
     b.id0 = row[blk_a];
-    if constexpr (AP) {
-      const int64_t sl = p.slot_mapping[s];
-      b.sblk = sl >= 0 ? static_cast<int>(sl / BS) : -1;
-      b.soff = sl >= 0 ? static_cast<int>(sl % BS) : 0;
-    } else {
-      b.sblk = -1;
-      b.soff = 0;
-    }
+    b.slot = AP ? p.slot_mapping[s] : -1;
     // the tile's further blocks; past the sequence's last block their
     // values are never used (those tokens are masked)
     b.id1 = kTB > 1 ? row[min(blk_a + 1, p.max_blocks - 1)] : 0;
     b.id2 = kTB > 2 ? row[min(blk_a + 2, p.max_blocks - 1)] : 0;
     b.id3 = kTB > 3 ? row[min(blk_a + 3, p.max_blocks - 1)] : 0;
     b.seq = s;
-    b.tile = t;
+    b.tile = virt ? ~t : t;
     b.hg = hg;
     return b;
   };
   auto block_id = [&](int id) { return static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks) ? id : 0; };
   // ---- loads of one unit into a ring slot; returns the unit
-  auto load_unit = [&](const Batch& b, int x, u32x4 (&qr)[C::kKSteps], u32x4 (&kr)[kSub * C::kKLoads],
+  auto load_unit = [&](const Batch& b, int x, u32x4 (&qr)[kQL], u32x4 (&kr)[kSub * C::kKLoads],
                        VSlot (&vr)[kVL]) -> SkUnit {
     const int o = x - b.ub;
     SkUnit un;
@@ -279,10 +310,23 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     un.tile = __builtin_amdgcn_readlane(b.tile, o);
     un.len = min(__builtin_amdgcn_readlane(b.len, o), p.len_cap);
     un.hg = __builtin_amdgcn_readlane(b.hg, o);
-    un.virt = AP ? __builtin_amdgcn_readlane(b.virt, o) : 0;
-    un.sblk = AP ? __builtin_amdgcn_readlane(b.sblk, o) : -1;
-    un.soff = AP ? __builtin_amdgcn_readlane(b.soff, o) : 0;
-    if (AP) un.len = un.virt ? 1 : un.len - 1;  // the virtual tile holds token L - 1 alone
+    un.virt = 0;
+    un.sblk = -1;
+    un.soff = 0;
+    if constexpr (AP) {
+      un.virt = un.tile < 0;
+      un.tile = un.virt ? ~un.tile : un.tile;
+      un.len = un.virt ? 1 : un.len - 1;  // the virtual tile holds token L - 1 alone
+      // the slot as loaded, split here (uniform) so the batch never waits
+      // for it; a slot outside the pool writes nothing
+      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b.slot), o));
+      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b.slot >> 32), o));
+      const int64_t sl = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+      if (sl >= 0 && sl / BS < p.num_blocks) {
+        un.sblk = static_cast<int>(sl / BS);
+        un.soff = static_cast<int>(sl % BS);
+      }
+    }
     // the tile's blocks (scalars, not an array: a select over an array
     // would become a per-lane indexed load from scratch)
     const int id0 = block_id(__builtin_amdgcn_readlane(b.id0, o));
@@ -313,73 +357,99 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // slot it consumes.
     {
       const int64_t head0 = static_cast<int64_t>(un.seq) * p.num_q_heads + static_cast<int64_t>(g) * G;
-      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
+      if constexpr (TV) {
+        // lanes past the rows' end repeat a piece (not used)
+        const char* qblk = static_cast<const char*>(p.q) + head0 * D * 2;
 #pragma unroll
-      for (int i = 0; i < C::kKSteps; ++i) qr[i] = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
-    }
-    // K row addresses and V run addresses of the unit's tile: from the cache,
-    // or (append variant) from the newest token's k_new / v_new row. Both
-    // cases issue the same load instructions, so the loads in flight per
-    // ring slot stay fixed and the compiler's waits stay tight.
-    const char* krow;  // lane's K row (QK tile 0) minus its first head-dim offset (see below)
-    const char* vrun;  // lane's V run for n-tile 0
-    if constexpr (TT == 32) {
-      // QK tile 0 row `col` is token 8 (col / 4) + col % 4 of the unit and
-      // tile 1 row `col` the token 4 past it (same block), so score lane
-      // group j holds tokens 8j .. 8j + 7 and the PV operand of lane (d, j)
-      // is the run of head dim d over those 8 tokens
-      const int tk = 8 * (col >> 2) + (col & 3);
-      const int tv = 8 * j;
-      const int tin = kTB == 1 ? (un.tile * TT) % BS : 0;
-      const int idk = pick(tk / BS);
-      const int idv = pick(tv / BS);
-      krow = kbase + static_cast<int64_t>(idk) * blk_bytes + (tin + tk % BS) * tok_bytes +
-             static_cast<int64_t>(g) * D * kB;
-      vrun = vbase + static_cast<int64_t>(idv) * blk_bytes + ((static_cast<int64_t>(g) * D + col) * BS + tin + tv % BS) * kB;
-    } else if constexpr (BS >= 16) {
-      const int tin = (un.tile * 16) % BS;
-      krow = kbase + static_cast<int64_t>(id0) * blk_bytes + tin * tok_bytes + static_cast<int64_t>(g) * D * kB +
-             koff_lane - qk_dim<kB>(0, j) * kB;
-      vrun = vbase + static_cast<int64_t>(id0) * blk_bytes + (static_cast<int64_t>(g) * D * BS + tin) * kB + voff_lane;
-    } else {
-      // a tile spans two blocks: tokens 0..BS-1 in the first, the rest in the second
-      const int idk = pick(col / BS);
-      krow = kbase + static_cast<int64_t>(idk) * blk_bytes + (col % BS) * tok_bytes + static_cast<int64_t>(g) * D * kB;
-      const int t4 = 4 * j;
-      const int idv = pick(t4 / BS);
-      vrun = vbase + static_cast<int64_t>(idv) * blk_bytes + ((static_cast<int64_t>(g) * D + col) * BS + t4 % BS) * kB;
-    }
-    // token-major V: the lane's V row sits where its K row does, in the V pool
-    const char* vrow = vbase + (krow - kbase);
-    int vstep = kVTileBytes;
-    if constexpr (AP) {
-      if (un.virt) {
-        // every K row reads the new token's row (rows past the first are
-        // masked); dim-major: lane (d, j) reads the 4-dim group holding
-        // v_new[d] (the compute step moves element d % 4 into the first
-        // token's place); token-major: every V row reads v_new's row
-        krow = static_cast<const char*>(p.k_new) + (static_cast<int64_t>(un.seq) * Hkv + g) * D * kB;
-        vrun = static_cast<const char*>(p.v_new) + ((static_cast<int64_t>(un.seq) * Hkv + g) * D + (col & ~3)) * kB;
-        vrow = static_cast<const char*>(p.v_new) + (static_cast<int64_t>(un.seq) * Hkv + g) * D * kB;
-        vstep = 16 * kB;
+        for (int i = 0; i < kQL; ++i) {
+          const int f = (64 * i + lane) * 16;
+          qr[i] = *reinterpret_cast<const u32x4*>(qblk + (f < kQBytes ? f : f % kQBytes));
+        }
+      } else {
+        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
+#pragma unroll
+        for (int i = 0; i < C::kKSteps; ++i) qr[i] = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
       }
     }
-#pragma unroll
-    for (int s = 0; s < kSub; ++s) {
+    // K and V addresses of the unit's rows: from the cache, or (append
+    // variant) from the newest token's k_new / v_new row. Both cases issue
+    // the same load instructions, so the loads in flight per ring slot stay
+    // fixed and the compiler's waits stay tight.
+    if constexpr (TV) {
+      // the head group's slice of the 16 rows (virtual tile: every row reads
+      // the new token's row; rows past the first are masked)
+      // uniform bases (the first block's row `tin`, or the new token's row)
+      // and 32-bit lane offsets; with 8-token blocks rows 8..15 lie in the
+      // tile's second block
+      const bool nv = AP && un.virt;
+      const int64_t hoff = static_cast<int64_t>(un.hg) * S;
+      const int tin = kTB == 1 ? (un.tile * 16) % BS : 0;
+      const int64_t base = nv ? (static_cast<int64_t>(un.seq) * Hkv * D) * kB + hoff
+                              : static_cast<int64_t>(id0) * blk_bytes + tin * tok_bytes + hoff;
+      const char* kb = (nv ? static_cast<const char*>(p.k_new) : kbase) + base;
+      const char* vb = (nv ? static_cast<const char*>(p.v_new) : vbase) + base;
+      const int64_t blk2 = kTB > 1 ? (static_cast<int64_t>(id1) - id0) * blk_bytes - BS * tok_bytes : 0;
 #pragma unroll
       for (int i = 0; i < C::kKLoads; ++i) {
-        const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
-        kr[s * C::kKLoads + i] = *reinterpret_cast<const u32x4*>(krow + s * 4 * tok_bytes + off);
+        const int r = st_r(i);
+        const uint32_t o = nv ? static_cast<uint32_t>(st_cb(i)) : static_cast<uint32_t>(r * tok_bytes + st_cb(i));
+        const int64_t o2 = kTB > 1 && !nv && r >= BS ? blk2 : 0;
+        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + o2 + o));
+        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + o2 + o));
       }
-    }
-    if constexpr (TV) {
-#pragma unroll
-      for (int i = 0; i < C::kKLoads; ++i) vr[i] = *reinterpret_cast<const u32x4*>(vrow + 2 * qk_dim<2>(i, j));
+      return un;
     } else {
+      const char* krow;  // lane's K row (QK tile 0) minus its first head-dim offset (see below)
+      const char* vrun;  // lane's V run for n-tile 0
+      if constexpr (TT == 32) {
+        // QK tile 0 row `col` is token 8 (col / 4) + col % 4 of the unit and
+        // tile 1 row `col` the token 4 past it (same block), so score lane
+        // group j holds tokens 8j .. 8j + 7 and the PV operand of lane (d, j)
+        // is the run of head dim d over those 8 tokens
+        const int tk = 8 * (col >> 2) + (col & 3);
+        const int tv = 8 * j;
+        const int tin = kTB == 1 ? (un.tile * TT) % BS : 0;
+        const int idk = pick(tk / BS);
+        const int idv = pick(tv / BS);
+        krow = kbase + static_cast<int64_t>(idk) * blk_bytes + (tin + tk % BS) * tok_bytes +
+               static_cast<int64_t>(g) * D * kB;
+        vrun = vbase + static_cast<int64_t>(idv) * blk_bytes + ((static_cast<int64_t>(g) * D + col) * BS + tin + tv % BS) * kB;
+      } else if constexpr (BS >= 16) {
+        const int tin = (un.tile * 16) % BS;
+        krow = kbase + static_cast<int64_t>(id0) * blk_bytes + tin * tok_bytes + static_cast<int64_t>(g) * D * kB +
+               koff_lane - qk_dim<kB>(0, j) * kB;
+        vrun = vbase + static_cast<int64_t>(id0) * blk_bytes + (static_cast<int64_t>(g) * D * BS + tin) * kB + voff_lane;
+      } else {
+        // a tile spans two blocks: tokens 0..BS-1 in the first, the rest in the second
+        const int idk = pick(col / BS);
+        krow = kbase + static_cast<int64_t>(idk) * blk_bytes + (col % BS) * tok_bytes + static_cast<int64_t>(g) * D * kB;
+        const int t4 = 4 * j;
+        const int idv = pick(t4 / BS);
+        vrun = vbase + static_cast<int64_t>(idv) * blk_bytes + ((static_cast<int64_t>(g) * D + col) * BS + t4 % BS) * kB;
+      }
+      int vstep = kVTileBytes;
+      if constexpr (AP) {
+        if (un.virt) {
+          // every K row reads the new token's row (rows past the first are
+          // masked); lane (d, j) reads the 4-dim group holding v_new[d] (the
+          // compute step moves element d % 4 into the first token's place)
+          krow = static_cast<const char*>(p.k_new) + (static_cast<int64_t>(un.seq) * Hkv + g) * D * kB;
+          vrun = static_cast<const char*>(p.v_new) + ((static_cast<int64_t>(un.seq) * Hkv + g) * D + (col & ~3)) * kB;
+          vstep = 16 * kB;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < kSub; ++s) {
+#pragma unroll
+        for (int i = 0; i < C::kKLoads; ++i) {
+          const int off = kB == 2 ? 2 * qk_dim<2>(i, j) : qk_dim<1>(2 * i, j);
+          kr[s * C::kKLoads + i] = *reinterpret_cast<const u32x4*>(krow + s * 4 * tok_bytes + off);
+        }
+      }
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) vr[nt] = *reinterpret_cast<const VSlot*>(vrun + nt * vstep);
+      return un;
     }
-    return un;
   };
 
   // ---- segment state. A segment is the run of units of one (head group,
@@ -447,10 +517,59 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     return (col & 1) ? (w2 >> 16) : (w2 & 0xffffu);
   };
 
-  auto compute = [&](int x, const SkUnit& un, const u32x4 (&qb)[C::kKSteps], const u32x4 (&kr)[kSub * C::kKLoads],
+  auto compute = [&](int x, const SkUnit& un, const u32x4 (&qr)[kQL], const u32x4 (&kr)[kSub * C::kKLoads],
                      const VSlot (&vr)[kVL]) {
     const int tb = AP && un.virt ? 0 : un.tile * TT;
     const int L = un.len;
+    // ---- token-major V: the unit's rows go to the stage as loaded; after
+    // the barrier each wave reads its head's K rows in the QK operand layout
+    // (lane (token col, j): the 16 bytes of dims qk_dim(i, j)) and later its
+    // V rows with the transposing read (lane (d, j): tokens 4j .. 4j + 3 of
+    // head dim 16 nt + d, its group's lanes pointing at rows 4j + lane / 4,
+    // dims 4 (lane % 4) ..)
+    u32x4 kop[TV ? C::kKSteps : 1];
+    u32x4 qb[C::kKSteps];  // the q rows as the QK B operand (columns >= G repeat row 0)
+    const uint16_t* vt_src = nullptr;
+    if constexpr (TV) {
+      char* qs = reinterpret_cast<char*>(s_out);
+#pragma unroll
+      for (int i = 0; i < kQL; ++i) {
+        const int f = (64 * i + lane) * 16;
+        if (f < kQBytes) *reinterpret_cast<u32x4*>(qs + (f / (D * 2)) * kQPitch + f % (D * 2)) = qr[i];
+      }
+#pragma unroll
+      for (int i = 0; i < C::kKLoads; ++i) {
+        *reinterpret_cast<u32x4*>(stage + st_r(i) * kpitch + st_cb(i)) = kr[i];
+        *reinterpret_cast<u32x4*>(stage_v + st_r(i) * vpitch + st_cb(i)) = vr[i];
+      }
+      // append: the new token's row of the head group into its cache slot,
+      // from the workgroup's pieces of row 0 (every row of the virtual tile
+      // holds it)
+      if constexpr (AP) {
+        if (un.virt && static_cast<uint32_t>(un.sblk) < static_cast<uint32_t>(p.num_blocks)) {
+          const int64_t dst = static_cast<int64_t>(un.sblk) * blk_bytes + un.soff * tok_bytes +
+                              static_cast<int64_t>(un.hg) * S;
+#pragma unroll
+          for (int i = 0; i < C::kKLoads; ++i) {
+            if (st_r(i) == 0) {
+              *reinterpret_cast<u32x4*>(const_cast<char*>(kbase) + dst + st_cb(i)) = kr[i];
+              *reinterpret_cast<u32x4*>(const_cast<char*>(vbase) + dst + st_cb(i)) = vr[i];
+            }
+          }
+        }
+      }
+      lds_barrier();
+      const char* qsrc = qs + (col < G ? col : 0) * kQPitch;
+#pragma unroll
+      for (int i = 0; i < C::kKSteps; ++i) qb[i] = *reinterpret_cast<const u32x4*>(qsrc + qk_dim<2>(i, j) * 2);
+      const char* ks = stage + col * kpitch + wave * D * kB;
+#pragma unroll
+      for (int i = 0; i < C::kKSteps; ++i) kop[i] = *reinterpret_cast<const u32x4*>(ks + qk_dim<2>(i, j) * kB);
+      vt_src = reinterpret_cast<const uint16_t*>(stage_v + (4 * j + (col >> 2)) * vpitch + wave * D * kB) + 4 * (col & 3);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kKSteps; ++i) qb[i] = qr[i];
+    }
     // ---- S^T = K q^T, one 16-row tile per kSub; lane (head col, j) gets
     // the scores of tokens kE * j + e, e = 4 * tile + row
     f32x4 sacc[kSub];
@@ -459,7 +578,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (kB == 2) {
 #pragma unroll
-        for (int i = 0; i < C::kKSteps; ++i) sacc[s] = mfma_16x16x32<QT>(kr[i], qb[i], sacc[s]);
+        for (int i = 0; i < C::kKSteps; ++i) sacc[s] = mfma_16x16x32<QT>(TV ? kop[i] : kr[i], qb[i], sacc[s]);
       } else {
 #pragma unroll
         for (int a = 0; a < C::kKLoads; ++a) {
@@ -517,18 +636,6 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       for (int e = 0; e < kE; e += 2)
         vmask[e / 2] = (t + e < L ? 0xffffu : 0u) | (t + e + 1 < L ? 0xffff0000u : 0u);
     }
-    // token-major V: the wave's rows go to its LDS tile ([16][kVRow]); lane
-    // (d, j) then reads tokens 4j .. 4j + 3 of head dim 16 nt + d with one
-    // transposing read per n-tile, its group's lanes pointing at rows
-    // 4j + lane / 4, dims 4 (lane % 4) ..
-    const uint16_t* vt_src = nullptr;
-    if constexpr (TV) {
-      uint16_t* vt = reinterpret_cast<uint16_t*>(s_out);
-#pragma unroll
-      for (int i = 0; i < C::kKLoads; ++i) *reinterpret_cast<u32x4*>(vt + col * kVRow + qk_dim<2>(i, j)) = vr[i];
-      wave_lds_sync();
-      vt_src = vt + (4 * j + (col >> 2)) * kVRow + 4 * (col & 3);
-    }
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       if constexpr (TT == 16) {
@@ -552,24 +659,18 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         acc[nt] = mfma_16x16x32<QT>(u32x4{plo[0], plo[1], plo[2], plo[3]}, vop, acc[nt]);
       }
     }
-    // ---- append: write the newest token's row into its cache slot
-    if constexpr (AP) {
+    // ---- append (dim-major V): write the newest token's row into its cache
+    // slot (token-major V: done with the stage write above)
+    if constexpr (AP && !TV) {
       if (un.virt && static_cast<uint32_t>(un.sblk) < static_cast<uint32_t>(p.num_blocks)) {
-        const int g = un.hg * HW + wave;
-        char* kdst = const_cast<char*>(kbase) + static_cast<int64_t>(un.sblk) * blk_bytes + un.soff * tok_bytes +
-                     static_cast<int64_t>(g) * D * kB;
-        if (col == 0) {
-#pragma unroll
-          for (int i = 0; i < C::kKLoads; ++i) *reinterpret_cast<u32x4*>(kdst + qk_dim<kB>(i, j) * kB) = kr[i];
-        }
-        if constexpr (TV) {
-          char* vdst = const_cast<char*>(vbase) + static_cast<int64_t>(un.sblk) * blk_bytes + un.soff * tok_bytes +
+        {
+          const int g = un.hg * HW + wave;
+          char* kdst = const_cast<char*>(kbase) + static_cast<int64_t>(un.sblk) * blk_bytes + un.soff * tok_bytes +
                        static_cast<int64_t>(g) * D * kB;
           if (col == 0) {
 #pragma unroll
-            for (int i = 0; i < C::kKLoads; ++i) *reinterpret_cast<u32x4*>(vdst + 2 * qk_dim<2>(i, j)) = vr[i];
+            for (int i = 0; i < C::kKLoads; ++i) *reinterpret_cast<u32x4*>(kdst + qk_dim<kB>(i, j) * kB) = kr[i];
           }
-        } else {
           uint16_t* vdst = reinterpret_cast<uint16_t*>(const_cast<char*>(vbase) + static_cast<int64_t>(un.sblk) * blk_bytes) +
                            (static_cast<int64_t>(g) * D + col) * BS + un.soff;
           if (j == 0) {
@@ -594,13 +695,25 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     }
   };
 
+  // after each unit: the waves stay in step (without it the oldest wave of
+  // each SIMD takes most issue slots and finishes far ahead); with the
+  // stage, every wave has also read the unit's rows before the next unit's
+  // rows overwrite them
+  auto unit_barrier = [&]() {
+    if constexpr (TV) {
+      lds_barrier();
+    } else {
+      __builtin_amdgcn_s_barrier();
+    }
+  };
+
   // ---- the ring: units x + 1 and x + 2 in flight while x is computed.
   // Loads are unconditional: past the range they repeat the last unit (an
   // L2 hit), so every path through the loop carries the same loads.
   // Batches: an outer step covers 63 units (21 ring iterations); its batch
   // holds the units it loads (uk + 2 .. uk + 65), and the next step's batch
   // is requested when the step starts.
-  u32x4 q0[C::kKSteps], q1[C::kKSteps], q2[C::kKSteps];
+  u32x4 q0[kQL], q1[kQL], q2[kQL];
   u32x4 k0[kSub * C::kKLoads], k1[kSub * C::kKLoads], k2[kSub * C::kKLoads];
   VSlot v0[kVL], v1[kVL], v2[kVL];
   const int ulast = u1 - 1;
@@ -623,13 +736,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     do {
       SkUnit n2 = load_unit(cur, min(u + 2, ulast), q2, k2, v2);
       compute(u, n0, q0, k0, v0);
-      __builtin_amdgcn_s_barrier();
+      unit_barrier();
       n0 = load_unit(cur, min(u + 3, ulast), q0, k0, v0);
       if (u + 1 <= ulast) compute(u + 1, n1, q1, k1, v1);
-      __builtin_amdgcn_s_barrier();
+      unit_barrier();
       n1 = load_unit(cur, min(u + 4, ulast), q1, k1, v1);
       if (u + 2 <= ulast) compute(u + 2, n2, q2, k2, v2);
-      __builtin_amdgcn_s_barrier();
+      unit_barrier();
       u += 3;
     } while (u < uend);
     uk += 63;
@@ -642,16 +755,26 @@ template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV>
 hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
   const int HW = p.heads_per_wg;
   const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV);
+  // more than 64 KiB of dynamic LDS (the stage of token-major V) must be
+  // allowed per kernel; racing callers set the same attribute
+  static int lds_allowed = 64 * 1024;  // per instantiation
+  if (static_cast<int>(lds) > lds_allowed) {
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    lds_allowed = static_cast<int>(lds);
+  }
   // occupancy per (HW, LDS in 4 KiB steps); racing writers store the same value
-  static int cache[9][17];  // per instantiation
+  static int cache[9][41];  // per instantiation
   const int lb = static_cast<int>((lds + 4095) / 4096);
-  int occ = (HW <= 8 && lb <= 16) ? cache[HW][lb] : 0;
+  int occ = (HW <= 8 && lb <= 40) ? cache[HW][lb] : 0;
   if (occ <= 0) {
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV>,
                                                                 64 * HW, lds);
     if (e != hipSuccess) return e;
     if (occ <= 0) return hipErrorInvalidConfiguration;
-    if (HW <= 8 && lb <= 16) cache[HW][lb] = occ;
+    if (HW <= 8 && lb <= 40) cache[HW][lb] = occ;
   }
   int W = cus * occ;
   W = W < max_wgs ? W : max_wgs;
