@@ -302,8 +302,14 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   };
   auto block_id = [&](int id) { return static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks) ? id : 0; };
   // ---- loads of one unit into a ring slot; returns the unit
+  // x may lie past the range: the last unit is read out and loaded again
+  // (nothing computes it; with token-major V every lane loads one 16-byte
+  // location instead, since the non-temporal loads would fetch the unit
+  // from memory again)
   auto load_unit = [&](const Batch& b, int x, u32x4 (&qr)[kQL], u32x4 (&kr)[kSub * C::kKLoads],
                        VSlot (&vr)[kVL]) -> SkUnit {
+    const bool past = x >= u1;
+    x = past ? u1 - 1 : x;
     const int o = x - b.ub;
     SkUnit un;
     un.seq = __builtin_amdgcn_readlane(b.seq, o);
@@ -394,8 +400,10 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         const int r = st_r(i);
         const uint32_t o = nv ? static_cast<uint32_t>(st_cb(i)) : static_cast<uint32_t>(r * tok_bytes + st_cb(i));
         const int64_t o2 = kTB > 1 && !nv && r >= BS ? blk2 : 0;
-        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + o2 + o));
-        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + o2 + o));
+        const char* kp = past ? kbase : kb + o2 + o;
+        const char* vp = past ? vbase : vb + o2 + o;
+        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
+        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
       }
       return un;
     } else {
@@ -709,7 +717,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 
   // ---- the ring: units x + 1 and x + 2 in flight while x is computed.
   // Loads are unconditional: past the range they repeat the last unit (an
-  // L2 hit), so every path through the loop carries the same loads.
+  // L2 hit; one location with token-major V), so every path through the
+  // loop carries the same loads.
   // Batches: an outer step covers 63 units (21 ring iterations); its batch
   // holds the units it loads (uk + 2 .. uk + 65), and the next step's batch
   // is requested when the step starts.
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // entry too
   SkUnit n0 = load_unit(cur, u0, q0, k0, v0);
   __builtin_amdgcn_sched_barrier(0);
-  SkUnit n1 = load_unit(cur, min(u0 + 1, ulast), q1, k1, v1);
+  SkUnit n1 = load_unit(cur, u0 + 1, q1, k1, v1);
   __builtin_amdgcn_sched_barrier(0);
   seg_begun = n0.tile == 0;
   int uk = u0;
@@ -734,13 +743,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     const int uend = min(uk + 63, u1);
     int u = uk;
     do {
-      SkUnit n2 = load_unit(cur, min(u + 2, ulast), q2, k2, v2);
+      SkUnit n2 = load_unit(cur, u + 2, q2, k2, v2);
       compute(u, n0, q0, k0, v0);
       unit_barrier();
-      n0 = load_unit(cur, min(u + 3, ulast), q0, k0, v0);
+      n0 = load_unit(cur, u + 3, q0, k0, v0);
       if (u + 1 <= ulast) compute(u + 1, n1, q1, k1, v1);
       unit_barrier();
-      n1 = load_unit(cur, min(u + 4, ulast), q1, k1, v1);
+      n1 = load_unit(cur, u + 4, q1, k1, v1);
       if (u + 2 <= ulast) compute(u + 2, n2, q2, k2, v2);
       unit_barrier();
       u += 3;
