@@ -232,8 +232,8 @@ size_t workspace_bytes_for(int64_t B, int64_t Hq, int64_t D, int64_t P) {
 constexpr int kSkWavesPerCu = 32;
 
 // LDS one workgroup of the balanced kernel may use: 64 KiB, or with the
-// stage of token-major V up to gfx950's 160 KiB, as far as the device allows
-// per workgroup (sk_device_lds)
+// stage (token-major V, fp8 pools) up to gfx950's 160 KiB, as far as the
+// device allows per workgroup (sk_device_lds)
 constexpr size_t kSkMaxLds = 64 * 1024;
 constexpr size_t kSkMaxLdsStage = 160 * 1024;
 
@@ -252,10 +252,10 @@ size_t sk_device_lds() {
 }
 
 // KV heads per workgroup: the largest divisor of num_kv_heads up to 8 (a
-// power of two with token-major V: the stage splits a row slice by shifts)
-int sk_heads_per_wg(int hkv, bool tv) {
+// power of two when staged: the stage splits a row slice by shifts)
+int sk_heads_per_wg(int hkv, bool staged) {
   for (int hw = 8; hw > 1; --hw)
-    if (hkv % hw == 0 && (!tv || (hw & (hw - 1)) == 0)) return hw;
+    if (hkv % hw == 0 && (!staged || (hw & (hw - 1)) == 0)) return hw;
   return 1;
 }
 
@@ -312,10 +312,12 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
                 "no balanced decode%s kernel for pool dtype %d, %s V, head_dim %d, block_size %d, group %d%s",
                 append ? " + append" : "", (int)cache->dtype, tv ? "token-major" : "dim-major", D, cache->block_size, G,
                 tv ? " (token-major V: F16 and BF16 pools)" : "");
-  const int HW = sk_heads_per_wg(hkv, tv);
+  // the kernel stages whole rows through LDS for token-major V and fp8 pools
+  const bool staged = tv || cache->dtype == PA_FP8_E4M3;
+  const int HW = sk_heads_per_wg(hkv, staged);
   const int n_hg = hkv / HW;
-  const size_t lds = sk_lds_bytes(B, HW, G, D, tv);
-  if (lds > (tv ? kSkMaxLdsStage : kSkMaxLds))
+  const size_t lds = sk_lds_bytes(B, HW, G, D, staged, cache->dtype == PA_FP8_E4M3 ? 1 : 2);
+  if (lds > (staged ? kSkMaxLdsStage : kSkMaxLds))
     return fail(PA_ERR_UNSUPPORTED, "B = %d is too large for the balanced split (use partition_size > 0)", B);
   // units (tiles x head groups) must stay below 2^31; counted in 16-token
   // tiles, an upper bound for the 32-token tiles of fp8 pools

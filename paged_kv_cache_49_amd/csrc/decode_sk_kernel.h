@@ -107,23 +107,31 @@ __device__ __forceinline__ int sk_find_seq(const int32_t* pref, int B, int r) {
 // LDS of one wave, in floats: its G x D fp32 output tile
 __host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D) { return static_cast<size_t>(G) * D; }
 
-// Token-major V (16-bit pools): the unit's K and V rows are staged in LDS as
-// two [16][S] tiles, S = HW * D * 2 bytes (the head group's slice of a token
-// row). Row pitches: K rows S + 16 bytes (the 16 lanes of a 16-byte operand
-// read, one row apart, then start 4 banks apart), V rows S + 32 bytes (a
-// 16-lane group of the transposing read touches 4 rows of 32 bytes, which
-// then sit 8 banks apart).
+// The stage: the unit's K and V as loaded (whole rows), in LDS. S = HW * D
+// * b bytes is the head group's slice of a token row.
+//  * 16-bit pools with token-major V: K and V as two [16][S] tiles. Row
+//    pitches: K rows S + 16 bytes (the 16 lanes of a 16-byte operand read,
+//    one row apart, then start 4 banks apart), V rows S + 32 bytes (a
+//    16-lane group of the transposing read touches 4 rows of 32 bytes,
+//    which then sit 8 banks apart).
+//  * fp8 pools (dim-major V): K as a [32][S] tile at pitch S + 16, rows
+//    16..31 shifted by 64 more bytes, so the permuted 32-token operand read
+//    (rows r and r + 16 in one 16-lane group) stays conflict free; V as the
+//    head group's [HW][D][BS] region of each of the unit's blocks, as
+//    loaded (32 S bytes).
 __host__ __device__ inline constexpr int sk_stage_kpitch(int S) { return S + 16; }
 __host__ __device__ inline constexpr int sk_stage_vpitch(int S) { return S + 32; }
-__host__ __device__ inline constexpr size_t sk_stage_bytes(int HW, int D) {
-  return 16 * static_cast<size_t>(sk_stage_kpitch(HW * D * 2) + sk_stage_vpitch(HW * D * 2));
+__host__ __device__ inline constexpr size_t sk_stage_bytes(int HW, int D, int kb) {
+  return kb == 2 ? 16 * static_cast<size_t>(sk_stage_kpitch(HW * D * 2) + sk_stage_vpitch(HW * D * 2))
+                 : 32 * static_cast<size_t>(sk_stage_kpitch(HW * D)) + 64 + 32 * static_cast<size_t>(HW * D);
 }
 
-// bytes of dynamic LDS: the tile prefix, the stage (token-major V), then one
-// region per wave
-inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool tv) {
+// bytes of dynamic LDS: the tile prefix, the stage (token-major V or fp8
+// pools: `staged`), then one region per wave
+inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool staged, int kb) {
   const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
-  return pref + (tv ? sk_stage_bytes(HW, D) : 0) + static_cast<size_t>(HW) * sk_wave_lds_floats(G, D) * sizeof(float);
+  return pref + (staged ? sk_stage_bytes(HW, D, kb) : 0) +
+         static_cast<size_t>(HW) * sk_wave_lds_floats(G, D) * sizeof(float);
 }
 
 // Barrier for LDS written by some waves of the workgroup and read by others
@@ -135,8 +143,8 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // the lane's V registers for one unit: dim-major runs (u32x2 per n-tile) or
-// token-major row pieces (u32x4, as K)
-template <bool TV>
+// pieces of the unit's V as loaded for the stage (u32x4, as K)
+template <bool STG>
 struct SkVSlot {
   using type = u32x2;
 };
@@ -167,18 +175,23 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   constexpr int kTB = BS < TT ? TT / BS : 1;
   static_assert(!AP || TT == 16, "the append variant is for 16-bit pools");
   static_assert(!TV || kB == 2, "token-major V on the balanced split: 16-bit pools");
+  // STG: the unit's K and V are loaded as whole rows / regions and go
+  // through the LDS stage (token-major V, and fp8 pools); otherwise each
+  // wave loads its head's K rows and V runs in the operand layouts
+  constexpr bool STG = TV || kB == 1;
+  constexpr int kKP = kSub * C::kKLoads;  // 16-byte K pieces per lane and unit
   // V per lane and unit: dim-major, one run of one head dim over the lane's
-  // kE tokens per n-tile (4 x 16-bit or 8 x fp8); token-major (TV), the
-  // lane's share of the unit's rows, as K (see the stage below)
-  using VSlot = typename SkVSlot<TV>::type;
-  constexpr int kVL = TV ? C::kKLoads : kNT;
-  // q per lane and unit: the QK operand (kKSteps pieces), or with the stage
-  // (TV) the wave's G x D q rows as 16-byte pieces (lane l, piece i: byte
+  // kE tokens per n-tile (4 x 16-bit or 8 x fp8); staged, the lane's share of
+  // the unit's V as loaded, as K (see the stage below)
+  using VSlot = typename SkVSlot<STG>::type;
+  constexpr int kVL = STG ? kKP : kNT;
+  // q per lane and unit: the QK operand (kKSteps pieces), or when staged
+  // the wave's G x D q rows as 16-byte pieces (lane l, piece i: byte
   // 16 (64 i + l) of the rows), rebuilt through the wave's LDS region
   constexpr int kQBytes = G * D * 2;
-  constexpr int kQL = TV ? (kQBytes > 1024 ? kQBytes / 1024 : 1) : C::kKSteps;
+  constexpr int kQL = STG ? (kQBytes > 1024 ? kQBytes / 1024 : 1) : C::kKSteps;
   constexpr int kQPitch = D * 2 + 16;  // bytes per q row in LDS (rows 4 banks apart)
-  static_assert(!TV || G * kQPitch <= static_cast<int>(sk_wave_lds_floats(G, D) * sizeof(float)),
+  static_assert(!STG || G * kQPitch <= static_cast<int>(sk_wave_lds_floats(G, D) * sizeof(float)),
                 "the q rows fit the wave's LDS region");
   extern __shared__ int32_t sk_smem[];
   const int B = p.batch;
@@ -186,8 +199,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int HW = p.heads_per_wg;
-  char* stage = reinterpret_cast<char*>(sk_smem + (B + 1 + 3) / 4 * 4);  // token-major V only
-  float* s_out_all = reinterpret_cast<float*>(stage + (TV ? sk_stage_bytes(HW, D) : 0));
+  char* stage = reinterpret_cast<char*>(sk_smem + (B + 1 + 3) / 4 * 4);  // STG only
+  float* s_out_all = reinterpret_cast<float*>(stage + (STG ? sk_stage_bytes(HW, D, kB) : 0));
 
   // ---- plan: tiles per sequence, then their exclusive prefix (in place)
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
@@ -246,22 +259,28 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // of head dim `col` from token 4j
   const uint32_t koff_lane = static_cast<uint32_t>(col * tok_bytes + qk_dim<kB>(0, j) * kB);
   const uint32_t voff_lane = static_cast<uint32_t>((col * BS + 4 * j) * kB);
-  // Token-major V: the unit's K and V rows of the head group are read as
-  // whole rows, not in the MFMA layout (a wave reading its own head's 256
-  // bytes of 16 rows per instruction streams measurably slower than reading
-  // 1 KiB contiguous). The [16][S] slice is split evenly over the HW waves
-  // (kKLoads KiB each): lane piece i is byte f % S of row f / S,
-  // f = (wave * kKLoads + i) KiB + 16 lane. Each unit then goes through the
-  // LDS stage: written as loaded, read back per wave in the operand layouts.
-  // S is a power of two (HW is, for token-major V).
+  // Staged (STG): the unit's K rows of the head group are read as whole
+  // rows, not in the MFMA layout (a wave reading its own head's slice of 16
+  // rows per instruction streams measurably slower than reading 1 KiB
+  // contiguous), and so is its V (token-major: rows as K; fp8 dim-major:
+  // the head group's [HW][D][BS] region of each block). The [TT][S] slice
+  // is split evenly over the HW waves (kKP KiB each): lane piece i is byte
+  // f % S of row f / S, f = (wave * kKP + i) KiB + 16 lane (dim-major V: byte
+  // f of the unit's regions). Each unit then goes through the LDS stage:
+  // written as loaded, read back per wave in the operand layouts. S is a
+  // power of two (HW is, when staged).
   const int S = HW * D * kB;
   const int s_log2 = __builtin_ctz(static_cast<unsigned>(S));
   const int kpitch = sk_stage_kpitch(S), vpitch = sk_stage_vpitch(S);
-  char* stage_v = stage + 16 * kpitch;
+  char* stage_v = stage + TT * kpitch + (TT == 32 ? 64 : 0);
+  const int SV = HW * D * BS * kB;  // dim-major V: the head group's region of one block
+  const int sv_log2 = __builtin_ctz(static_cast<unsigned>(SV));
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto st_f = [&](int i) { return (wave_u * C::kKLoads + i) * 1024 + lane * 16; };
+  auto st_f = [&](int i) { return (wave_u * kKP + i) * 1024 + lane * 16; };
   auto st_r = [&](int i) { return st_f(i) >> s_log2; };
   auto st_cb = [&](int i) { return st_f(i) & (S - 1); };
+  // LDS byte of K row r, byte b (fp8: rows 16..31 64 bytes further)
+  auto st_k = [&](int r, int b) { return r * kpitch + (TT == 32 ? (r >> 4) << 6 : 0) + b; };
 
   // ---- unit batches: lane i resolves unit ub + i (ub is uniform). The
   // length and block ids are kept as loaded (clamped when a unit is read
@@ -303,10 +322,10 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   auto block_id = [&](int id) { return static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks) ? id : 0; };
   // ---- loads of one unit into a ring slot; returns the unit
   // x may lie past the range: the last unit is read out and loaded again
-  // (nothing computes it; with token-major V every lane loads one 16-byte
+  // (nothing computes it; when staged every lane loads one 16-byte
   // location instead, since the non-temporal loads would fetch the unit
   // from memory again)
-  auto load_unit = [&](const Batch& b, int x, u32x4 (&qr)[kQL], u32x4 (&kr)[kSub * C::kKLoads],
+  auto load_unit = [&](const Batch& b, int x, u32x4 (&qr)[kQL], u32x4 (&kr)[kKP],
                        VSlot (&vr)[kVL]) -> SkUnit {
     const bool past = x >= u1;
     x = past ? u1 - 1 : x;
@@ -363,7 +382,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // slot it consumes.
     {
       const int64_t head0 = static_cast<int64_t>(un.seq) * p.num_q_heads + static_cast<int64_t>(g) * G;
-      if constexpr (TV) {
+      if constexpr (STG) {
         // lanes past the rows' end repeat a piece (not used)
         const char* qblk = static_cast<const char*>(p.q) + head0 * D * 2;
 #pragma unroll
@@ -404,6 +423,21 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         const char* vp = past ? vbase : vb + o2 + o;
         kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
         vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
+      }
+      return un;
+    } else if constexpr (STG) {
+      // fp8 pools: the head group's slice of the 32 K rows (kTB blocks of BS
+      // rows) and its dim-major V region of each of those blocks
+      const int64_t hoff = static_cast<int64_t>(un.hg) * S;
+      const int64_t voff = static_cast<int64_t>(un.hg) * SV;
+#pragma unroll
+      for (int i = 0; i < kKP; ++i) {
+        const int f = st_f(i);
+        const int r = f >> s_log2;
+        const int64_t ko = static_cast<int64_t>(pick(r / BS)) * blk_bytes + (r % BS) * tok_bytes + hoff + (f & (S - 1));
+        const int64_t vo = static_cast<int64_t>(pick(f >> sv_log2)) * blk_bytes + voff + (f & (SV - 1));
+        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(past ? kbase : kbase + ko));
+        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(past ? vbase : vbase + vo));
       }
       return un;
     } else {
@@ -525,7 +559,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     return (col & 1) ? (w2 >> 16) : (w2 & 0xffffu);
   };
 
-  auto compute = [&](int x, const SkUnit& un, const u32x4 (&qr)[kQL], const u32x4 (&kr)[kSub * C::kKLoads],
+  auto compute = [&](int x, const SkUnit& un, const u32x4 (&qr)[kQL], const u32x4 (&kr)[kKP],
                      const VSlot (&vr)[kVL]) {
     const int tb = AP && un.virt ? 0 : un.tile * TT;
     const int L = un.len;
@@ -535,10 +569,11 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // V rows with the transposing read (lane (d, j): tokens 4j .. 4j + 3 of
     // head dim 16 nt + d, its group's lanes pointing at rows 4j + lane / 4,
     // dims 4 (lane % 4) ..)
-    u32x4 kop[TV ? C::kKSteps : 1];
+    u32x4 kop[STG ? kKP : 1];
     u32x4 qb[C::kKSteps];  // the q rows as the QK B operand (columns >= G repeat row 0)
     const uint16_t* vt_src = nullptr;
-    if constexpr (TV) {
+    const char* v8_src = nullptr;
+    if constexpr (STG) {
       char* qs = reinterpret_cast<char*>(s_out);
 #pragma unroll
       for (int i = 0; i < kQL; ++i) {
@@ -546,9 +581,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         if (f < kQBytes) *reinterpret_cast<u32x4*>(qs + (f / (D * 2)) * kQPitch + f % (D * 2)) = qr[i];
       }
 #pragma unroll
-      for (int i = 0; i < C::kKLoads; ++i) {
-        *reinterpret_cast<u32x4*>(stage + st_r(i) * kpitch + st_cb(i)) = kr[i];
-        *reinterpret_cast<u32x4*>(stage_v + st_r(i) * vpitch + st_cb(i)) = vr[i];
+      for (int i = 0; i < kKP; ++i) {
+        *reinterpret_cast<u32x4*>(stage + st_k(st_r(i), st_cb(i))) = kr[i];
+        if constexpr (TV) {
+          *reinterpret_cast<u32x4*>(stage_v + st_r(i) * vpitch + st_cb(i)) = vr[i];
+        } else {
+          *reinterpret_cast<u32x4*>(stage_v + st_f(i)) = vr[i];
+        }
       }
       // append: the new token's row of the head group into its cache slot,
       // from the workgroup's pieces of row 0 (every row of the virtual tile
@@ -569,11 +608,26 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       lds_barrier();
       const char* qsrc = qs + (col < G ? col : 0) * kQPitch;
 #pragma unroll
-      for (int i = 0; i < C::kKSteps; ++i) qb[i] = *reinterpret_cast<const u32x4*>(qsrc + qk_dim<2>(i, j) * 2);
-      const char* ks = stage + col * kpitch + wave * D * kB;
+      for (int i = 0; i < C::kKSteps; ++i) qb[i] = *reinterpret_cast<const u32x4*>(qsrc + qk_dim<kB>(i, j) * 2);
+      if constexpr (TT == 16) {
+        const char* ks = stage + col * kpitch + wave * D * kB;
 #pragma unroll
-      for (int i = 0; i < C::kKSteps; ++i) kop[i] = *reinterpret_cast<const u32x4*>(ks + qk_dim<2>(i, j) * kB);
-      vt_src = reinterpret_cast<const uint16_t*>(stage_v + (4 * j + (col >> 2)) * vpitch + wave * D * kB) + 4 * (col & 3);
+        for (int i = 0; i < C::kKSteps; ++i) kop[i] = *reinterpret_cast<const u32x4*>(ks + qk_dim<2>(i, j) * kB);
+        vt_src = reinterpret_cast<const uint16_t*>(stage_v + (4 * j + (col >> 2)) * vpitch + wave * D * kB) + 4 * (col & 3);
+      } else {
+        // fp8: QK tile s row `col` is token 8 (col / 4) + col % 4 + 4 s; the
+        // PV operand of lane (d, j) is the run of head dim d over tokens
+        // 8j .. 8j + 7 (block part 8j / BS of the V stage)
+#pragma unroll
+        for (int s = 0; s < kSub; ++s) {
+          const int row = 8 * (col >> 2) + (col & 3) + 4 * s;
+#pragma unroll
+          for (int a = 0; a < C::kKLoads; ++a)
+            kop[s * C::kKLoads + a] =
+                *reinterpret_cast<const u32x4*>(stage + st_k(row, wave * D + qk_dim<1>(2 * a, j)));
+        }
+        v8_src = stage_v + ((8 * j) / BS) * SV + (wave * D + col) * BS + (8 * j) % BS;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < C::kKSteps; ++i) qb[i] = qr[i];
@@ -590,7 +644,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       } else {
 #pragma unroll
         for (int a = 0; a < C::kKLoads; ++a) {
-          const u32x4 kw = kr[s * C::kKLoads + a];
+          const u32x4 kw = STG ? kop[s * C::kKLoads + a] : kr[s * C::kKLoads + a];
           const u32x2 b0 = e4m3x4_to_bf16x4(kw.x), b1 = e4m3x4_to_bf16x4(kw.y);
           const u32x2 b2 = e4m3x4_to_bf16x4(kw.z), b3 = e4m3x4_to_bf16x4(kw.w);
           sacc[s] = mfma_16x16x32<QT>(u32x4{b0.x, b0.y, b1.x, b1.y}, qb[2 * a], sacc[s]);
@@ -661,7 +715,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         acc[nt] = mfma_16x16x16<QT>(u32x2{phi[0], phi[1]}, vop, acc[nt]);
         acc[nt] = mfma_16x16x16<QT>(u32x2{plo[0], plo[1]}, vop, acc[nt]);
       } else {
-        const u32x2 b0 = e4m3x4_to_bf16x4(vr[nt].x), b1 = e4m3x4_to_bf16x4(vr[nt].y);
+        u32x2 vv;
+        if constexpr (STG) {
+          vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * BS);
+        } else {
+          vv = vr[nt];
+        }
+        const u32x2 b0 = e4m3x4_to_bf16x4(vv.x), b1 = e4m3x4_to_bf16x4(vv.y);
         const u32x4 vop = {b0.x & vmask[0], b0.y & vmask[1], b1.x & vmask[2], b1.y & vmask[3]};
         acc[nt] = mfma_16x16x32<QT>(u32x4{phi[0], phi[1], phi[2], phi[3]}, vop, acc[nt]);
         acc[nt] = mfma_16x16x32<QT>(u32x4{plo[0], plo[1], plo[2], plo[3]}, vop, acc[nt]);
@@ -708,7 +768,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // stage, every wave has also read the unit's rows before the next unit's
   // rows overwrite them
   auto unit_barrier = [&]() {
-    if constexpr (TV) {
+    if constexpr (STG) {
       lds_barrier();
     } else {
       __builtin_amdgcn_s_barrier();
@@ -717,7 +777,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 
   // ---- the ring: units x + 1 and x + 2 in flight while x is computed.
   // Loads are unconditional: past the range they repeat the last unit (an
-  // L2 hit; one location with token-major V), so every path through the
+  // L2 hit; one location when staged), so every path through the
   // loop carries the same loads.
   // Batches: an outer step covers 63 units (21 ring iterations); its batch
   // holds the units it loads (uk + 2 .. uk + 65), and the next step's batch
@@ -763,8 +823,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV>
 hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
   const int HW = p.heads_per_wg;
-  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV);
-  // more than 64 KiB of dynamic LDS (the stage of token-major V) must be
+  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes);
+  // more than 64 KiB of dynamic LDS (the stage) must be
   // allowed per kernel; racing callers set the same attribute
   static int lds_allowed = 64 * 1024;  // per instantiation
   if (static_cast<int>(lds) > lds_allowed) {
