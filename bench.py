@@ -235,19 +235,38 @@ def cpu_baseline(wl, seconds: float):
     tables, lens = np.asarray(tables), np.asarray(lens)
     q = wl.q()
     nbytes = 2 * int(lens.sum()) * wl.num_kv_heads * wl.head_dim * 2
-    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
-    reps, t0 = 0, time.perf_counter()
-    while True:
+    affinity = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
+
+    def timed(budget: float):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oatt.paged_decode(q, kp, vp, tables, lens, wl.scale, wl.block_size, wl.kv_dtype)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 200:
+                return reps, el
+
+    # BLAS threads: the cores this process may run on; one untimed call
+    # first (first-touch page faults of the oracle's working arrays)
+    with threadpoolctl.threadpool_limits(affinity):
         oatt.paged_decode(q, kp, vp, tables, lens, wl.scale, wl.block_size, wl.kv_dtype)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 200:
-            break
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+        reps, el = timed(seconds)
+    with threadpoolctl.threadpool_limits(1):
+        reps1, el1 = timed(seconds / 3)
     return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"fp64 oracle paged_decode over all {B} sequences of one layer "
                       f"({int(lens.sum())} tokens, {nbytes / 1e6:.0f} MB of bf16 K/V), {reps} repeats in "
-                      f"{el:.1f} s; tokens/s {B * reps / el:.1f}"}
+                      f"{el:.1f} s; tokens/s {B * reps / el:.1f}",
+            "one_core_value": round(nbytes * reps1 / el1 / 1e9, 4),
+            "cpu_model": cpu_model, "affinity_cores": affinity}
 
 
 def bench_decode_calls(args):
@@ -485,6 +504,7 @@ def main():
     lens_before = L0 + W
 
     events = []
+    batch.host_seconds, batch.host_steps = 0.0, 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(K):
@@ -534,6 +554,8 @@ def main():
         "pa_decode_us": round(call_s * 1e6, 2),
         "pa_decode_us_median": round(float(np.median(durs)) * 1e6, 2),
         "pa_decode_us_min": round(float(durs.min()) * 1e6, 2),
+        "host_block_manager_us_per_step": round(batch.host_seconds / max(batch.host_steps, 1) * 1e6, 2),
+        "host_block_manager_note": "pa_alloc_batch + pa_bm_pack of the whole batch on the host, inside each step",
         "roofline": {
             "bound": "hbm",
             "kernel": (("pa_decode_append" if fused else "pa_decode") +

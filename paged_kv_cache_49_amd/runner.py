@@ -27,6 +27,7 @@ for the kernels of the step that last read it (two steps earlier).
 """
 from __future__ import annotations
 
+import time
 from typing import List, Optional, Sequence
 
 import numpy as np
@@ -81,6 +82,10 @@ class PagedBatch:
         self._turn = 0
         self._copy_stream = torch.cuda.Stream(device=device) if upload_stream else None
         self.last_cow_count = 0
+        # host time of the block-manager work of the steps (alloc_batch,
+        # pack, shared_prefixes), seconds, and the number of steps it covers
+        self.host_seconds = 0.0
+        self.host_steps = 0
 
     # -- setup ---------------------------------------------------------------
     def prefill(self, seq_id: int, ks: Sequence[torch.Tensor], vs: Sequence[torch.Tensor]) -> np.ndarray:
@@ -132,6 +137,7 @@ class PagedBatch:
         B = len(seq_ids)
         if ones is None:
             ones = np.ones(B, np.int32)
+        t_host = time.perf_counter()
         _, cows = self.bm.alloc_batch(seq_ids, ones, slot_out=st.slots_np, cow_out=st.cow_np)
         ncow = len(cows)
         self.bm.pack(seq_ids, self.max_blocks, self.pad, tables=st.tables_np, context_lens=st.lens_np)
@@ -142,6 +148,8 @@ class PagedBatch:
                 raise ValueError("shared steps need partition_size > 0 and fused=False")
             groups = self.bm.shared_prefixes(seq_ids, partition_size, group_offsets=st.goff_np,
                                              group_members=st.gmem_np, shared_len=st.shl_np)
+        self.host_seconds += time.perf_counter() - t_host
+        self.host_steps += 1
         compute = torch.cuda.current_stream(self.device)
         if st.copied is None:
             st.copied, st.consumed = torch.cuda.Event(), torch.cuda.Event()
