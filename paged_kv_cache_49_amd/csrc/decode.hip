@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "decode_common.h"
@@ -87,6 +88,7 @@ struct SkMergeParams {
   int32_t group;  // G
   int32_t head_dim;
   int32_t out_dtype;
+  int32_t piece_slots;  // piece slots per workgroup (2 balanced, 1 partition mode)
 };
 
 // piece groups of a split merge workgroup: group g takes pieces g, g + 16, ...
@@ -112,7 +114,7 @@ __device__ __forceinline__ void merge_pieces(const SkMergeParams& p, int HWG, in
       const bool valid = wv <= wl;
       const int wr = valid ? wv : wf;  // past wl: read wf's piece, weight 0
       const int slot = wr == wf ? first_slot : 0;
-      const int64_t pi = (static_cast<int64_t>(wr) * 2 + slot) * HWG + hq;
+      const int64_t pi = (static_cast<int64_t>(wr) * p.piece_slots + slot) * HWG + hq;
       pm[k] = valid ? p.piece_m[pi] : -INFINITY;
       pl[k] = p.piece_l[pi];
       const f32x4* po = reinterpret_cast<const f32x4*>(p.piece_o + pi * D + 8 * c);
@@ -220,10 +222,14 @@ int64_t partitions_for(int32_t max_context_len, int32_t partition_size) {
   return (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
 }
 
-size_t workspace_bytes_for(int64_t B, int64_t Hq, int64_t D, int64_t P) {
+// workspace of a partitioned call: per (sequence, query head, partition)
+// m, l, o[D], then (partition mode of the staged kernel) the merge
+// descriptors [num_kv_heads][B][2]
+size_t workspace_bytes_for(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int64_t P) {
   if (P <= 1) return 0;
   const size_t rows = static_cast<size_t>(B * Hq * P);
-  return 2 * align_up(rows * sizeof(float)) + align_up(rows * D * sizeof(float));
+  return 2 * align_up(rows * sizeof(float)) + align_up(rows * D * sizeof(float)) +
+         align_up(static_cast<size_t>(B * hkv) * 2 * sizeof(int32_t));
 }
 
 // ---- balanced split
@@ -296,11 +302,17 @@ SkLayout sk_layout(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int cus) {
 // resident workgroups, then the merge of sequences cut between them. The
 // arguments are validated by pa_decode.
 // With k_new != nullptr it is the append variant (pa_decode_append).
+// With partition_size >= 0 (num_parts partitions; 0: one per sequence) the
+// same kernel runs in partition mode: one workgroup per (head group,
+// sequence, partition), merged by the same merge kernel (the partitioned
+// path for token-major V and fp8 pools).
 pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, const void* q,
                           const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
                           int32_t num_q_heads, int32_t max_context_len, float qk_scale_log2, float v_scale,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream, const void* k_new = nullptr,
-                          const void* v_new = nullptr, const int64_t* slot_mapping = nullptr) {
+                          void* workspace, size_t workspace_bytes, hipStream_t stream, int32_t partition_size = -1,
+                          int64_t num_parts = 0, const void* k_new = nullptr, const void* v_new = nullptr,
+                          const int64_t* slot_mapping = nullptr) {
+  const bool part_mode = partition_size >= 0;
   const int32_t hkv = cache->num_kv_heads;
   const int32_t D = cache->head_dim;
   const int32_t G = num_q_heads / hkv;
@@ -314,7 +326,9 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
                 tv ? " (token-major V: F16 and BF16 pools)" : "");
   // the kernel stages whole rows through LDS for token-major V and fp8 pools
   const bool staged = tv || cache->dtype == PA_FP8_E4M3;
-  const int HW = sk_heads_per_wg(hkv, staged);
+  // partition mode: at most 4 KV heads per workgroup, so that two
+  // workgroups share a CU and overlap their starts
+  const int HW = part_mode ? std::min(sk_heads_per_wg(hkv, staged), 4) : sk_heads_per_wg(hkv, staged);
   const int n_hg = hkv / HW;
   const size_t lds = sk_lds_bytes(B, HW, G, D, staged, cache->dtype == PA_FP8_E4M3 ? 1 : 2);
   if (lds > (staged ? kSkMaxLdsStage : kSkMaxLds))
@@ -327,7 +341,7 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   // per (sequence, query head) (its split layout)
   if (static_cast<int64_t>(B) * num_q_heads * (D / 8 * kMergeGroups) > 0xffffffffLL)
     return fail(PA_ERR_UNSUPPORTED, "B x num_q_heads is too large for the balanced split");
-  if (workspace == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "the balanced split needs a workspace");
+  if (!part_mode && workspace == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "the balanced split needs a workspace");
   const int cus = device_cus();
   if (cus <= 0) return fail(PA_ERR_DEVICE, "cannot read the device's CU count");
   if (lds > kSkMaxLds) {
@@ -337,22 +351,37 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
       return fail(PA_ERR_UNSUPPORTED, "the balanced split needs %zu bytes of LDS per workgroup (device: %zu)", lds,
                   dev_lds);
   }
-  const SkLayout lay = sk_layout(B, num_q_heads, hkv, D, cus);
-  if (workspace == nullptr || workspace_bytes < lay.total)
-    return fail(PA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed (got %zu)", lay.total,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
-    return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  SkLayout lay{};
+  if (part_mode) {
+    // [m][l][o] per (sequence, query head, partition) = per piece row of
+    // workgroup ((hg * B + s) * P + part), then the descriptors (the caller
+    // checked the size; none is needed for one partition)
+    const size_t rows = static_cast<size_t>(B) * num_q_heads * num_parts;
+    lay.m = 0;
+    lay.l = align_up(rows * sizeof(float));
+    lay.o = 2 * align_up(rows * sizeof(float));
+    lay.desc = lay.o + align_up(rows * D * sizeof(float));
+  } else {
+    lay = sk_layout(B, num_q_heads, hkv, D, cus);
+    if (workspace == nullptr || workspace_bytes < lay.total)
+      return fail(PA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed (got %zu)", lay.total,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+      return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  }
+  const bool merge = !part_mode || num_parts > 1;
   char* ws = static_cast<char*>(workspace);
   SkParams p{};
   p.q = q;
   p.k_pool = cache->k;
   p.v_pool = cache->v;
   p.out = out;
-  p.piece_m = reinterpret_cast<float*>(ws + lay.m);
-  p.piece_l = reinterpret_cast<float*>(ws + lay.l);
-  p.piece_o = reinterpret_cast<float*>(ws + lay.o);
-  p.seg_desc = reinterpret_cast<int32_t*>(ws + lay.desc);
+  if (merge) {
+    p.piece_m = reinterpret_cast<float*>(ws + lay.m);
+    p.piece_l = reinterpret_cast<float*>(ws + lay.l);
+    p.piece_o = reinterpret_cast<float*>(ws + lay.o);
+    p.seg_desc = reinterpret_cast<int32_t*>(ws + lay.desc);
+  }
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.block_stride = cache->block_stride;
@@ -364,6 +393,14 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   p.batch = B;
   p.heads_per_wg = HW;
   p.num_head_groups = n_hg;
+  p.piece_slots = part_mode ? 1 : 2;
+  if (part_mode) {
+    // tiles per partition: 16 tokens (32 for fp8 pools; the caller keeps
+    // partition_size a multiple of it, or uses one partition)
+    const int tt = cache->dtype == PA_FP8_E4M3 ? 32 : 16;
+    p.part_tiles = num_parts > 1 ? partition_size / tt : std::max(1, (max_context_len + tt - 1) / tt);
+    p.num_parts = static_cast<int32_t>(num_parts);
+  }
   p.out_dtype = out_code;
   p.qk_scale_log2 = qk_scale_log2;
   p.v_scale = v_scale;
@@ -371,13 +408,18 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   p.v_new = v_new;
   p.slot_mapping = slot_mapping;
   int max_wgs = cus * kSkWavesPerCu / HW;
-  if (const char* cap = std::getenv("PA_SK_WGS")) {
+  if (part_mode) {
+    const int64_t grid = num_parts * B * n_hg;
+    if (grid > 0x7fffffffLL) return fail(PA_ERR_INVALID_ARGUMENT, "too many workgroups (%lld)", (long long)grid);
+    max_wgs = static_cast<int>(grid);
+  } else if (const char* cap = std::getenv("PA_SK_WGS")) {
     const int v = std::atoi(cap);
     if (v > 0 && v < max_wgs) max_wgs = v;
   }
   int wgs = 0;
   hipError_t e = launch(p, cus, max_wgs, stream, &wgs);
   if (e != hipSuccess) return fail(PA_ERR_DEVICE, "balanced decode launch: %s", hipGetErrorString(e));
+  if (!merge) return PA_OK;
   SkMergeParams m{};
   m.piece_m = p.piece_m;
   m.piece_l = p.piece_l;
@@ -392,9 +434,12 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   m.group = G;
   m.head_dim = D;
   m.out_dtype = out_code;
+  m.piece_slots = p.piece_slots;
   // segments that span many workgroups on average (fewer segments than a
-  // quarter of the workgroups) take the split merge
-  if (static_cast<int64_t>(B) * n_hg * 4 < wgs) {
+  // quarter of the workgroups) take the split merge; so does partition mode
+  // always, whose result must not depend on the rest of the batch (the
+  // merge layout sets the rounding order)
+  if (part_mode || static_cast<int64_t>(B) * n_hg * 4 < wgs) {
     const int64_t merge_wgs = static_cast<int64_t>(B) * n_hg * HW * G;
     hipLaunchKernelGGL(decode_sk_merge_kernel<true>, dim3(static_cast<uint32_t>(merge_wgs)), dim3(D / 8 * kMergeGroups),
                        0, stream, m);
@@ -423,13 +468,23 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_h
     return pa::sk_layout(B, num_q_heads, num_kv_heads, head_dim, cus).total;
   }
   if (max_context_len == 0) return 0;
-  return pa::workspace_bytes_for(B, num_q_heads, head_dim, pa::partitions_for(max_context_len, partition_size));
+  return pa::workspace_bytes_for(B, num_q_heads, num_kv_heads, head_dim,
+                                 pa::partitions_for(max_context_len, partition_size));
 }
 
 }  // extern "C"
 
 namespace pa {
 namespace {
+
+// whether the staged kernel can run a partitioned call of this shape (its
+// LDS holds the batch's tile prefix; a larger batch takes the partition
+// kernels)
+bool sk_partition_fits(const pa_kv_cache* cache, int32_t B, int32_t G) {
+  const bool fp8 = cache->dtype == PA_FP8_E4M3;
+  const int HW = std::min(sk_heads_per_wg(cache->num_kv_heads, true), 4);
+  return sk_lds_bytes(B, HW, G, cache->head_dim, true, fp8 ? 1 : 2) <= kSkMaxLdsStage;
+}
 
 // the group structure of pa_decode_shared
 struct SharedArgs {
@@ -494,7 +549,7 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
     return fail(PA_ERR_UNSUPPORTED, "PA_PARTITION_BALANCED with token-major V blocks takes F16 or BF16 pools");
   const int64_t P = pa::partitions_for(max_context_len, partition_size);
   if (P > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many partitions");
-  const size_t need = pa::workspace_bytes_for(B, num_q_heads, D, P);
+  const size_t need = pa::workspace_bytes_for(B, num_q_heads, hkv, D, P);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(PA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed (got %zu)", need,
@@ -542,9 +597,37 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
                     (long long)slots[i], t, (long long)want);
     }
   }
-  if (balanced) return pa::decode_balanced(cache, out, out_c, q, block_tables, max_blocks, context_lens, B,
-                                           num_q_heads, max_context_len, qk_scale_log2, v_scale, workspace,
-                                           workspace_bytes, s, k_new, v_new, slot_mapping);
+  if (balanced)
+    return pa::decode_balanced(cache, out, out_c, q, block_tables, max_blocks, context_lens, B, num_q_heads,
+                               max_context_len, qk_scale_log2, v_scale, workspace, workspace_bytes, s, -1, 0, k_new,
+                               v_new, slot_mapping);
+  // Partitions with token-major V (16-bit pools) or fp8 pools (partition_size
+  // a multiple of their 32-token units, or one partition) can run on the
+  // staged kernel in partition mode: one workgroup of up to 4 KV heads per
+  // partition, whole-row loads. It streams faster but its workgroups are
+  // coarse (a partition of 512 tokens is 1 MiB for 4 heads): it wins when
+  // few long sequences fill the device with many partitions each (long
+  // context: 663 -> 484 us), and loses to the one-wave partition kernels on
+  // batches of many shorter sequences (GQA, mixed, prefix batches). So: few
+  // segments per CU and at least 8 partitions. PA_PARTITION_PATH=staged /
+  // wave forces one path where both exist (a measurement aid).
+  const bool tv = cache->v_layout == PA_LAYOUT_TOKEN_MAJOR;
+  const bool staged_ok = sh == nullptr && ((tv && !fp8) || (fp8 && !tv && (P == 1 || partition_size % 32 == 0))) &&
+                         pa::sk_partition_fits(cache, B, G);
+  bool staged_part = false;
+  if (staged_ok) {
+    const int cus = pa::device_cus();
+    const int64_t n_hg = hkv / std::min(pa::sk_heads_per_wg(hkv, true), 4);
+    staged_part = cus > 0 && static_cast<int64_t>(B) * n_hg * 8 <= cus && P >= 8;
+    if (const char* path = std::getenv("PA_PARTITION_PATH")) {
+      if (std::strcmp(path, "staged") == 0) staged_part = true;
+      if (std::strcmp(path, "wave") == 0) staged_part = false;
+    }
+  }
+  if (staged_part)
+    return pa::decode_balanced(cache, out, out_c, q, block_tables, max_blocks, context_lens, B, num_q_heads,
+                               max_context_len, qk_scale_log2, v_scale, workspace, workspace_bytes, s,
+                               partition_size, P);
 
   pa::DecodeParams prm{};
   prm.q = q;

@@ -12,8 +12,8 @@ namespace pa {
 struct DecodeParams;
 using DecodeLaunch = hipError_t (*)(const DecodeParams&, dim3 grid, hipStream_t stream);
 // balanced split: the launcher sizes the grid from the device's CU count and
-// the kernel's occupancy, at most max_wgs workgroups, and reports the grid it
-// used in *wgs
+// the kernel's occupancy, at most max_wgs workgroups (partition mode:
+// exactly max_wgs), and reports the grid it used in *wgs
 struct SkParams;
 using SkLaunch = hipError_t (*)(const SkParams&, int cus, int max_wgs, hipStream_t stream, int* wgs);
 

@@ -79,6 +79,12 @@ struct SkParams {
   int32_t batch;
   int32_t heads_per_wg;     // HW
   int32_t num_head_groups;  // num_kv_heads / HW
+  // partition mode (part_tiles > 0): workgroup w takes the units of one
+  // (head group, sequence, partition) = ((hg * B + s) * num_parts + part),
+  // part_tiles units each; otherwise the balanced ranges
+  int32_t part_tiles;
+  int32_t num_parts;
+  int32_t piece_slots;      // piece slots per workgroup: 2 (balanced), 1 (partition mode)
   int32_t out_dtype;
   float qk_scale_log2;
   float v_scale;
@@ -234,11 +240,35 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   const int U = T * p.num_head_groups;  // the launch guarantees U < 2^31
   const int W = static_cast<int>(gridDim.x);
   const int w = static_cast<int>(blockIdx.x);
-  const int u0 = sk_range_start(w, U, W), u1 = sk_range_start(w + 1, U, W);
+  int u0, u1;
+  if (p.part_tiles > 0) {
+    // partition mode: the range is one partition of one segment; a partition
+    // past the sequence's end does nothing (no merge range reaches it)
+    const int part = w % p.num_parts;
+    const int rest = w / p.num_parts;
+    const int s = rest % B;
+    const int hg = rest / B;
+    const int nt = s_pref[s + 1] - s_pref[s];
+    const int t0 = part * p.part_tiles;
+    if (t0 >= nt) {
+      // a sequence without tokens: its head group's rows are zero (written
+      // here too, since one partition has no merge after it)
+      if (nt == 0 && part == 0) {
+        const int64_t row0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(hg) * HW * G;
+        for (int i = threadIdx.x; i < HW * G * D; i += blockDim.x) store_out(p.out, row0 * D + i, p.out_dtype, 0.f);
+      }
+      return;
+    }
+    u0 = hg * T + s_pref[s] + t0;
+    u1 = u0 + min(p.part_tiles, nt - t0);
+  } else {
+    u0 = sk_range_start(w, U, W);
+    u1 = sk_range_start(w + 1, U, W);
+  }
   if (u0 >= u1) {
     // no units: neutral slot-0 pieces (only when there are fewer units than workgroups)
     const int rows = HW * G;
-    const int64_t base = static_cast<int64_t>(w) * 2 * rows;
+    const int64_t base = static_cast<int64_t>(w) * p.piece_slots * rows;
     for (int i = threadIdx.x; i < rows; i += blockDim.x) {
       p.piece_m[base + i] = -INFINITY;
       p.piece_l[base + i] = 0.f;
@@ -522,7 +552,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     }
     wave_lds_sync();
     const int64_t head0 = static_cast<int64_t>(seg_seq) * p.num_q_heads + static_cast<int64_t>(seg_hg * HW + wave) * G;
-    const int64_t pbase = ((static_cast<int64_t>(w) * 2 + slot) * HW + wave) * G;
+    const int64_t pbase = ((static_cast<int64_t>(w) * p.piece_slots + slot) * HW + wave) * G;
     for (int i = lane * 8; i < G * D; i += 64 * 8) {
       float o[8];
 #pragma unroll
@@ -540,7 +570,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       p.piece_m[pbase + lane] = m_w;
       p.piece_l[pbase + lane] = l_head;
     }
-    if (wave == 0 && lane == 0) {
+    if (wave == 0 && lane == 0 && p.seg_desc != nullptr) {  // (none when no segment is cut)
       int32_t* desc = p.seg_desc + (static_cast<int64_t>(seg_hg) * B + seg_seq) * 2;
       if (complete) {
         desc[0] = -1;
@@ -845,7 +875,8 @@ hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t
     if (occ <= 0) return hipErrorInvalidConfiguration;
     if (HW <= 8 && lb <= 40) cache[HW][lb] = occ;
   }
-  int W = cus * occ;
+  // balanced: the resident workgroups; partition mode: one per partition
+  int W = p.part_tiles > 0 ? max_wgs : cus * occ;
   W = W < max_wgs ? W : max_wgs;
   *wgs = W;
   hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV>), dim3(W), dim3(64 * HW), lds, stream, p);

@@ -484,7 +484,9 @@ def test_workspace_size():
     assert f(64, 32, 8, 128, 4096, 0) == 0
     assert f(64, 32, 8, 128, 512, 512) == 0
     rows = 64 * 32 * 8
-    assert f(64, 32, 8, 128, 4096, 512) == 2 * ((rows * 4 + 255) // 256 * 256) + rows * 128 * 4
+    al = lambda n: (n + 255) // 256 * 256
+    # m, l, o per (sequence, query head, partition), then the merge descriptors [Hkv][B][2]
+    assert f(64, 32, 8, 128, 4096, 512) == 2 * al(rows * 4) + rows * 128 * 4 + al(64 * 8 * 2 * 4)
     # invalid sizes need nothing
     assert f(0, 32, 8, 128, 4096, 512) == 0
     assert f(64, 32, 0, 128, 4096, 512) == 0

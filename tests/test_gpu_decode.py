@@ -198,3 +198,26 @@ def test_lengths_beyond_max_context_are_clamped(gpu, v_layout):
     short._kv_cache[1] = wl.kv(1)
     short.lengths = np.array([128, 90])
     H.assert_close(got, H.oracle_contiguous(short))
+
+
+@pytest.mark.parametrize("path", ["staged", "wave"])
+@pytest.mark.parametrize("kv,v_layout", [("bf16", "token"), ("f16", "token"), ("fp8", "dim")])
+def test_partition_paths(gpu, monkeypatch, path, kv, v_layout):
+    """Partitioned calls run on the staged kernel in partition mode (one
+    workgroup per (KV head group, sequence, partition), merged by the
+    balanced split's merge) or on the one-wave partition kernels; the
+    library picks one from the batch shape, PA_PARTITION_PATH forces it.
+    Both against the oracle, on one partition, several and many; and a
+    partitioned row does not depend on the rest of the batch (bit for bit)."""
+    monkeypatch.setenv("PA_PARTITION_PATH", path)
+    wl = synth.random_case(1700, LENGTHS + [4096, 3000], 16, 4, 128, 16, kv)
+    for ps in (0, 256, 512):
+        _check(wl, ps, v_layout=v_layout)
+    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout=v_layout)
+    q = wl.q().cuda()
+    full = pa.decode(cache, q, tables, lens, max_ctx, wl.scale, 256, out_dtype=torch.float32)
+    rows = torch.tensor([2, 9, 10])
+    part = pa.decode(cache, q[rows].contiguous(), tables[rows.cuda()].contiguous(), lens[rows.cuda()].contiguous(),
+                     max_ctx, wl.scale, 256, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(part.cpu(), full.cpu()[rows]), "partitioned rows depend on the rest of the batch"
