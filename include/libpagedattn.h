@@ -411,7 +411,10 @@ pa_status pa_copy_blocks_between(const pa_kv_cache* dst, const pa_kv_cache* src,
  *   0      one workgroup per (sequence, KV head) walks the whole context;
  *   > 0    (a multiple of 16) each context is cut into partitions of that
  *          many tokens, one workgroup each, merged by a log-sum-exp
- *          reduction;
+ *          reduction (a workgroup per partition and KV head, or, for
+ *          batches of few long sequences with token-major V or fp8 pools,
+ *          per partition and group of up to 4 KV heads; either way a
+ *          row's result does not depend on the rest of the batch);
  *   PA_PARTITION_BALANCED  the batch's tiles (16 tokens; 32 for fp8 pools)
  *          of all sequences and KV heads are divided evenly over the
  *          workgroups the device holds at once, each walking its share
