@@ -30,6 +30,9 @@
  * back and validated before launch (slow; for debugging only).
  * PA_SK_WGS=n caps the grid of the balanced decode split at n workgroups
  * (for tests of the split itself; the result is the same up to rounding).
+ * PA_PARTITION_PATH=staged|wave picks, for partitioned pa_decode calls
+ * where both exist, the staged kernel or the one-wave partition kernels
+ * (normally chosen from the batch shape; for tests and measurements).
  */
 #ifndef LIBPAGEDATTN_H
 #define LIBPAGEDATTN_H
