@@ -1,6 +1,7 @@
 // Paged decode attention with the whole batch's work divided evenly over
-// persistent workgroups (balanced split); V blocks dim-major, or token-major
-// for 16-bit pools (TV, each tile's V rows transposed through LDS).
+// persistent workgroups (balanced split; also, in partition mode, one
+// workgroup per context partition); V blocks dim-major, or token-major for
+// 16-bit pools (TV, each tile's V rows transposed through LDS).
 //
 // [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
 // [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
@@ -27,18 +28,27 @@
 //  * append variant (AP): the newest token of each sequence (position
 //    L - 1) is not read from the cache but from k_new / v_new, as one extra
 //    unit per sequence holding a single valid row (the "virtual tile"); the
-//    wave that computes it also writes that row into the cache at
+//    workgroup that computes it also writes that row into the cache at
 //    slot_mapping[s]. The cache tiles then cover positions 0 .. L - 2. This
 //    is pa_reshape_and_cache followed by pa_decode in one launch.
+//  * loads, two forms. Staged (token-major V, and fp8 pools): the HW waves
+//    read the unit's K rows and V (token-major rows, or the dim-major
+//    region of each block) of the whole head group as contiguous 1 KiB
+//    spans with non-temporal loads; at compute time they go to an LDS
+//    stage and, after a workgroup barrier, each wave reads its head's
+//    operands from it (K in the QK layout, V through the transposing read
+//    or as 8-byte runs). Otherwise each wave loads its own head's K rows
+//    and dim-major V runs directly in the operand layouts.
 //  * unit batches: lane i of a batch resolves unit ub + i to its sequence,
 //    tile, length, head group and block id(s); the batch after it is
 //    requested one batch ahead, so block-table reads never stall the loads.
 //  * a 3-deep register ring keeps the q, K and V loads of two units in
 //    flight while a third unit is computed (q rides in the ring too, so a
-//    new segment never waits on a load issued behind the ring's). The waves
-//    of a workgroup pass a barrier after each unit: without it the oldest
-//    wave of each SIMD takes most issue slots and finishes far ahead, and
-//    the others end alone with few loads in flight.
+//    new segment never waits on a load issued behind the ring's; staged, as
+//    the wave's G x D rows, rebuilt through its LDS region). The waves of a
+//    workgroup pass a barrier after each unit: without it the oldest wave
+//    of each SIMD takes most issue slots and finishes far ahead, and the
+//    others end alone with few loads in flight.
 //  * a (head group, sequence) segment that ends inside the range is
 //    normalised and stored directly; a segment cut by the range's start or
 //    end leaves a partial (m, l, o) piece in slot 0 (it reaches back to the
@@ -50,6 +60,7 @@
 //    (wf, its piece in `slot`) and ends (wl, slot 0). Every workgroup in
 //    between holds a slot-0 piece; a workgroup with no units writes neutral
 //    slot-0 pieces (m = -inf, l = 0, o = 0), so a merge may include it.
+//    In partition mode a workgroup holds exactly one piece (one slot).
 #pragma once
 
 #include "decode_vt_kernel.h"
