@@ -149,8 +149,7 @@ def parse():
     p.add_argument("--partition-size", type=int, default=-1,
                    help="-1: balanced split (default); 0: no split; >0: partitions of that many tokens")
     p.add_argument("--v-layout", choices=["dim", "token"], default="token",
-                   help="in-block V layout: token-major (the KVBlock layout; default) or dim-major (fp8 pools use "
-                        "dim-major in the decode-call workloads: their balanced kernels need it)")
+                   help="in-block V layout: token-major (the KVBlock layout; default) or dim-major")
     p.add_argument("--separate-write", action="store_true",
                    help="write the new token with pa_reshape_and_cache, then pa_decode (default with the balanced "
                         "split: pa_decode_append, both in one launch)")
@@ -318,8 +317,6 @@ def bench_decode_calls(args):
               else synth.mixed_lengths(block_size=args.block_size, kv_dtype=args.kv))
         B, Hq, Hkv, D, bs, kv = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.kv_dtype
         sc = 6.0 / 448.0 if kv == "fp8" else 1.0
-        if kv == "fp8" and ps == pa.BALANCED:
-            args.v_layout = "dim"  # the balanced split takes token-major V for 16-bit pools only
         bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
         caches = [pa.KVCache.allocate(wl.num_blocks, bs, Hkv, D, kv, device=dev, v_layout=args.v_layout, k_scale=sc,
                                       v_scale=sc) for _ in range(layers)]

@@ -422,16 +422,16 @@ pa_status pa_copy_blocks_between(const pa_kv_cache* dst, const pa_kv_cache* src,
  *          of all sequences and KV heads are divided evenly over the
  *          workgroups the device holds at once, each walking its share
  *          across sequence boundaries;
- *          sequences cut between workgroups are merged as above. Dim-major
- *          V, or token-major V with F16 / BF16 pools (else
- *          PA_ERR_UNSUPPORTED). A workgroup serves HW KV heads (the largest
+ *          sequences cut between workgroups are merged as above. Either V
+ *          layout, every pool dtype. A workgroup serves HW KV heads (the largest
  *          divisor of num_kv_heads up to 8; with token-major V or an fp8
  *          pool the largest such power of two) and keeps B + 1 ints and HW
  *          per-wave regions of G * head_dim floats in LDS; with token-major
  *          V also the unit's K and V rows (2 x 16 rows of HW * head_dim
  *          16-bit elements, padded by 16 and 32 bytes), with an fp8 pool
  *          the unit's 32 K rows (padded) and its V (about 64 * HW *
- *          head_dim bytes in all). The LDS bounds B: 64 KiB for 16-bit
+ *          head_dim bytes in all; token-major V widened to bf16, about 96
+ *          * HW * head_dim). The LDS bounds B: 64 KiB for 16-bit
  *          pools with dim-major V (B <= 12287 for 8 KV heads, G = 4,
  *          head_dim 128), otherwise the device's LDS per workgroup (at
  *          most 160 KiB; token-major V: B <= 20287 for the same shapes on

@@ -323,14 +323,14 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
     return fail(PA_ERR_UNSUPPORTED,
                 "no balanced decode%s kernel for pool dtype %d, %s V, head_dim %d, block_size %d, group %d%s",
                 append ? " + append" : "", (int)cache->dtype, tv ? "token-major" : "dim-major", D, cache->block_size, G,
-                tv ? " (token-major V: F16 and BF16 pools)" : "");
+                append ? " (append: F16 and BF16 pools)" : "");
   // the kernel stages whole rows through LDS for token-major V and fp8 pools
   const bool staged = tv || cache->dtype == PA_FP8_E4M3;
   // partition mode: at most 4 KV heads per workgroup, so that two
   // workgroups share a CU and overlap their starts
   const int HW = part_mode ? std::min(sk_heads_per_wg(hkv, staged), 4) : sk_heads_per_wg(hkv, staged);
   const int n_hg = hkv / HW;
-  const size_t lds = sk_lds_bytes(B, HW, G, D, staged, cache->dtype == PA_FP8_E4M3 ? 1 : 2);
+  const size_t lds = sk_lds_bytes(B, HW, G, D, staged, cache->dtype == PA_FP8_E4M3 ? 1 : 2, tv);
   if (lds > (staged ? kSkMaxLdsStage : kSkMaxLds))
     return fail(PA_ERR_UNSUPPORTED, "B = %d is too large for the balanced split (use partition_size > 0)", B);
   // units (tiles x head groups) must stay below 2^31; counted in 16-token
@@ -483,7 +483,8 @@ namespace {
 bool sk_partition_fits(const pa_kv_cache* cache, int32_t B, int32_t G) {
   const bool fp8 = cache->dtype == PA_FP8_E4M3;
   const int HW = std::min(sk_heads_per_wg(cache->num_kv_heads, true), 4);
-  return sk_lds_bytes(B, HW, G, cache->head_dim, true, fp8 ? 1 : 2) <= kSkMaxLdsStage;
+  return sk_lds_bytes(B, HW, G, cache->head_dim, true, fp8 ? 1 : 2, cache->v_layout == PA_LAYOUT_TOKEN_MAJOR) <=
+         kSkMaxLdsStage;
 }
 
 // the group structure of pa_decode_shared
@@ -545,8 +546,6 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
                 "partition_size %d must be 0, a positive multiple of 16 or PA_PARTITION_BALANCED", partition_size);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (hkv > 65535 || B > 65535) return fail(PA_ERR_INVALID_ARGUMENT, "B and num_kv_heads must be <= 65535");
-  if (balanced && cache->v_layout != PA_LAYOUT_DIM_MAJOR && cache->dtype == PA_FP8_E4M3)
-    return fail(PA_ERR_UNSUPPORTED, "PA_PARTITION_BALANCED with token-major V blocks takes F16 or BF16 pools");
   const int64_t P = pa::partitions_for(max_context_len, partition_size);
   if (P > 0x7fffffff) return fail(PA_ERR_INVALID_ARGUMENT, "too many partitions");
   const size_t need = pa::workspace_bytes_for(B, num_q_heads, hkv, D, P);
@@ -601,8 +600,9 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
     return pa::decode_balanced(cache, out, out_c, q, block_tables, max_blocks, context_lens, B, num_q_heads,
                                max_context_len, qk_scale_log2, v_scale, workspace, workspace_bytes, s, -1, 0, k_new,
                                v_new, slot_mapping);
-  // Partitions with token-major V (16-bit pools) or fp8 pools (partition_size
-  // a multiple of their 32-token units, or one partition) can run on the
+  // Partitions with token-major V (16-bit pools) or fp8 pools (either V
+  // layout; partition_size a multiple of their 32-token units, or one
+  // partition) can run on the
   // staged kernel in partition mode: one workgroup of up to 4 KV heads per
   // partition, whole-row loads. It streams faster but its workgroups are
   // coarse (a partition of 512 tokens is 1 MiB for 4 heads): it wins when
@@ -612,7 +612,7 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
   // segments per CU and at least 8 partitions. PA_PARTITION_PATH=staged /
   // wave forces one path where both exist (a measurement aid).
   const bool tv = cache->v_layout == PA_LAYOUT_TOKEN_MAJOR;
-  const bool staged_ok = sh == nullptr && ((tv && !fp8) || (fp8 && !tv && (P == 1 || partition_size % 32 == 0))) &&
+  const bool staged_ok = sh == nullptr && ((tv && !fp8) || (fp8 && (P == 1 || partition_size % 32 == 0))) &&
                          pa::sk_partition_fits(cache, B, G);
   bool staged_part = false;
   if (staged_ok) {

@@ -57,9 +57,10 @@ SkLaunch find_decode_sk_bf16(int head_dim, int block_size, int group, bool appen
 SkLaunch find_decode_sk_fp8(int head_dim, int block_size, int group, bool append);
 SkLaunch find_decode_sk_f16_tv(int head_dim, int block_size, int group, bool append);
 SkLaunch find_decode_sk_bf16_tv(int head_dim, int block_size, int group, bool append);
+SkLaunch find_decode_sk_fp8_tv(int head_dim, int block_size, int group, bool append);
 
 // the balanced split's kernel for the pool's dtype and V layout (nullptr:
-// not supported; token-major V with 16-bit pools only)
+// not built)
 inline SkLaunch find_decode_sk(pa_dtype pool, pa_layout v_layout, int head_dim, int block_size, int group,
                                bool append) {
   const bool tv = v_layout == PA_LAYOUT_TOKEN_MAJOR;
@@ -70,7 +71,9 @@ inline SkLaunch find_decode_sk(pa_dtype pool, pa_layout v_layout, int head_dim, 
     case PA_BF16:
       return tv ? find_decode_sk_bf16_tv(head_dim, block_size, group, append)
                 : find_decode_sk_bf16(head_dim, block_size, group, append);
-    case PA_FP8_E4M3: return tv ? nullptr : find_decode_sk_fp8(head_dim, block_size, group, append);
+    case PA_FP8_E4M3:
+      return tv ? find_decode_sk_fp8_tv(head_dim, block_size, group, append)
+                : find_decode_sk_fp8(head_dim, block_size, group, append);
     default: return nullptr;
   }
 }

@@ -131,23 +131,25 @@ __host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D) { r
 //    one row apart, then start 4 banks apart), V rows S + 32 bytes (a
 //    16-lane group of the transposing read touches 4 rows of 32 bytes,
 //    which then sit 8 banks apart).
-//  * fp8 pools (dim-major V): K as a [32][S] tile at pitch S + 16, rows
-//    16..31 shifted by 64 more bytes, so the permuted 32-token operand read
-//    (rows r and r + 16 in one 16-lane group) stays conflict free; V as the
-//    head group's [HW][D][BS] region of each of the unit's blocks, as
-//    loaded (32 S bytes).
+//  * fp8 pools: K as a [32][S] tile at pitch S + 16, rows 16..31 shifted by
+//    64 more bytes, so the permuted 32-token operand read (rows r and r + 16
+//    in one 16-lane group) stays conflict free. V dim-major: the head
+//    group's [HW][D][BS] region of each of the unit's blocks, as loaded (32
+//    S bytes); token-major: the 32 rows widened to bf16 (pitch 2 S + 32, the
+//    transposing reads as for 16-bit pools).
 __host__ __device__ inline constexpr int sk_stage_kpitch(int S) { return S + 16; }
 __host__ __device__ inline constexpr int sk_stage_vpitch(int S) { return S + 32; }
-__host__ __device__ inline constexpr size_t sk_stage_bytes(int HW, int D, int kb) {
+__host__ __device__ inline constexpr size_t sk_stage_bytes(int HW, int D, int kb, bool tv) {
   return kb == 2 ? 16 * static_cast<size_t>(sk_stage_kpitch(HW * D * 2) + sk_stage_vpitch(HW * D * 2))
-                 : 32 * static_cast<size_t>(sk_stage_kpitch(HW * D)) + 64 + 32 * static_cast<size_t>(HW * D);
+                 : 32 * static_cast<size_t>(sk_stage_kpitch(HW * D)) + 64 +
+                       32 * static_cast<size_t>(tv ? sk_stage_vpitch(2 * HW * D) : HW * D);
 }
 
 // bytes of dynamic LDS: the tile prefix, the stage (token-major V or fp8
 // pools: `staged`), then one region per wave
-inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool staged, int kb) {
+inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool staged, int kb, bool tv) {
   const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
-  return pref + (staged ? sk_stage_bytes(HW, D, kb) : 0) +
+  return pref + (staged ? sk_stage_bytes(HW, D, kb, tv) : 0) +
          static_cast<size_t>(HW) * sk_wave_lds_floats(G, D) * sizeof(float);
 }
 
@@ -191,7 +193,6 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   constexpr int kE = TT / 4;
   constexpr int kTB = BS < TT ? TT / BS : 1;
   static_assert(!AP || TT == 16, "the append variant is for 16-bit pools");
-  static_assert(!TV || kB == 2, "token-major V on the balanced split: 16-bit pools");
   // STG: the unit's K and V are loaded as whole rows / regions and go
   // through the LDS stage (token-major V, and fp8 pools); otherwise each
   // wave loads its head's K rows and V runs in the operand layouts
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   const int wave = threadIdx.x >> 6;
   const int HW = p.heads_per_wg;
   char* stage = reinterpret_cast<char*>(sk_smem + (B + 1 + 3) / 4 * 4);  // STG only
-  float* s_out_all = reinterpret_cast<float*>(stage + (STG ? sk_stage_bytes(HW, D, kB) : 0));
+  float* s_out_all = reinterpret_cast<float*>(stage + (STG ? sk_stage_bytes(HW, D, kB, TV) : 0));
 
   // ---- plan: tiles per sequence, then their exclusive prefix (in place)
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // power of two (HW is, when staged).
   const int S = HW * D * kB;
   const int s_log2 = __builtin_ctz(static_cast<unsigned>(S));
-  const int kpitch = sk_stage_kpitch(S), vpitch = sk_stage_vpitch(S);
+  const int kpitch = sk_stage_kpitch(S), vpitch = sk_stage_vpitch(kB == 2 ? S : 2 * S);
   char* stage_v = stage + TT * kpitch + (TT == 32 ? 64 : 0);
   const int SV = HW * D * BS * kB;  // dim-major V: the head group's region of one block
   const int sv_log2 = __builtin_ctz(static_cast<unsigned>(SV));
@@ -441,7 +442,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // variant) from the newest token's k_new / v_new row. Both cases issue
     // the same load instructions, so the loads in flight per ring slot stay
     // fixed and the compiler's waits stay tight.
-    if constexpr (TV) {
+    if constexpr (TV && kB == 2) {
       // the head group's slice of the 16 rows (virtual tile: every row reads
       // the new token's row; rows past the first are masked)
       // uniform bases (the first block's row `tin`, or the new token's row)
@@ -468,7 +469,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       return un;
     } else if constexpr (STG) {
       // fp8 pools: the head group's slice of the 32 K rows (kTB blocks of BS
-      // rows) and its dim-major V region of each of those blocks
+      // rows), and of the 32 V rows (token-major) or its dim-major V region
+      // of each of those blocks
       const int64_t hoff = static_cast<int64_t>(un.hg) * S;
       const int64_t voff = static_cast<int64_t>(un.hg) * SV;
 #pragma unroll
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         const int f = st_f(i);
         const int r = f >> s_log2;
         const int64_t ko = static_cast<int64_t>(pick(r / BS)) * blk_bytes + (r % BS) * tok_bytes + hoff + (f & (S - 1));
-        const int64_t vo = static_cast<int64_t>(pick(f >> sv_log2)) * blk_bytes + voff + (f & (SV - 1));
+        const int64_t vo = TV ? ko : static_cast<int64_t>(pick(f >> sv_log2)) * blk_bytes + voff + (f & (SV - 1));
         kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(past ? kbase : kbase + ko));
         vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(past ? vbase : vbase + vo));
       }
@@ -624,8 +626,15 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 #pragma unroll
       for (int i = 0; i < kKP; ++i) {
         *reinterpret_cast<u32x4*>(stage + st_k(st_r(i), st_cb(i))) = kr[i];
-        if constexpr (TV) {
+        if constexpr (TV && kB == 2) {
           *reinterpret_cast<u32x4*>(stage_v + st_r(i) * vpitch + st_cb(i)) = vr[i];
+        } else if constexpr (TV) {
+          // fp8 token-major V: 16 codes -> 16 bf16, exact
+          const u32x2 a = e4m3x4_to_bf16x4(vr[i].x), b = e4m3x4_to_bf16x4(vr[i].y);
+          const u32x2 c = e4m3x4_to_bf16x4(vr[i].z), d = e4m3x4_to_bf16x4(vr[i].w);
+          char* dst = stage_v + st_r(i) * vpitch + 2 * st_cb(i);
+          *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b.x, b.y};
+          *reinterpret_cast<u32x4*>(dst + 16) = u32x4{c.x, c.y, d.x, d.y};
         } else {
           *reinterpret_cast<u32x4*>(stage_v + st_f(i)) = vr[i];
         }
@@ -667,7 +676,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
             kop[s * C::kKLoads + a] =
                 *reinterpret_cast<const u32x4*>(stage + st_k(row, wave * D + qk_dim<1>(2 * a, j)));
         }
-        v8_src = stage_v + ((8 * j) / BS) * SV + (wave * D + col) * BS + (8 * j) % BS;
+        if constexpr (TV) {
+          // tokens 8j .. 8j + 3 and 8j + 4 .. 8j + 7: two transposing reads
+          vt_src = reinterpret_cast<const uint16_t*>(stage_v + (8 * j + (col >> 2)) * vpitch + wave * D * 2) +
+                   4 * (col & 3);
+        } else {
+          v8_src = stage_v + ((8 * j) / BS) * SV + (wave * D + col) * BS + (8 * j) % BS;
+        }
       }
     } else {
 #pragma unroll
@@ -756,13 +771,20 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         acc[nt] = mfma_16x16x16<QT>(u32x2{phi[0], phi[1]}, vop, acc[nt]);
         acc[nt] = mfma_16x16x16<QT>(u32x2{plo[0], plo[1]}, vop, acc[nt]);
       } else {
-        u32x2 vv;
-        if constexpr (STG) {
-          vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * BS);
+        u32x2 b0, b1;  // the lane's 8 tokens of its head dim as bf16
+        if constexpr (TV) {
+          b0 = lds_read_tr16(vt_src + 16 * nt);
+          b1 = lds_read_tr16(vt_src + 4 * vpitch / 2 + 16 * nt);
         } else {
-          vv = vr[nt];
+          u32x2 vv;
+          if constexpr (STG) {
+            vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * BS);
+          } else {
+            vv = vr[nt];
+          }
+          b0 = e4m3x4_to_bf16x4(vv.x);
+          b1 = e4m3x4_to_bf16x4(vv.y);
         }
-        const u32x2 b0 = e4m3x4_to_bf16x4(vv.x), b1 = e4m3x4_to_bf16x4(vv.y);
         const u32x4 vop = {b0.x & vmask[0], b0.y & vmask[1], b1.x & vmask[2], b1.y & vmask[3]};
         acc[nt] = mfma_16x16x32<QT>(u32x4{phi[0], phi[1], phi[2], phi[3]}, vop, acc[nt]);
         acc[nt] = mfma_16x16x32<QT>(u32x4{plo[0], plo[1], plo[2], plo[3]}, vop, acc[nt]);
@@ -864,7 +886,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV>
 hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
   const int HW = p.heads_per_wg;
-  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes);
+  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes, TV);
   // more than 64 KiB of dynamic LDS (the stage) must be
   // allowed per kernel; racing callers set the same attribute
   static int lds_allowed = 64 * 1024;  // per instantiation
@@ -915,12 +937,10 @@ SkLaunch select_decode_sk_bs(int BS, int G) {
   }
 }
 
-// append = the fused cache write; TV = token-major V (both 16-bit pools only)
+// append = the fused cache write (16-bit pools only); TV = token-major V
 template <typename KV, typename QT, bool TV>
 SkLaunch select_decode_sk(int D, int BS, int G, bool append) {
-  if constexpr (TV && KV::kBytes != 2) {
-    return nullptr;
-  } else {
+  {
     if (append) {
       if constexpr (KV::kBytes != 2) {
         return nullptr;

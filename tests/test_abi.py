@@ -404,7 +404,7 @@ def _decode_status(cache, **kw):
     (dict(B=0), dict(), _lib.PA_OK),                             # empty batch: nothing to do
     (dict(part=-2), dict(), _lib.PA_ERR_INVALID_ARGUMENT),       # negative, not BALANCED
     (dict(part=-1), dict(dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1),
-     _lib.PA_ERR_UNSUPPORTED),                                   # balanced split, token-major V: 16-bit pools
+     _lib.PA_ERR_INVALID_ARGUMENT),                              # fp8, token-major V: no workspace
     (dict(part=-1), dict(), _lib.PA_ERR_INVALID_ARGUMENT),       # token-major V: no workspace
     (dict(part=-1), dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR), _lib.PA_ERR_INVALID_ARGUMENT),  # no workspace
     (dict(part=-1, B=20000, max_ctx=16), dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR),

@@ -100,24 +100,28 @@ def test_token_major_v_matches_dim_major(gpu):
 FP8_LENGTHS = [1, 7, 8, 9, 31, 32, 33, 63, 64, 65, 777, 1601]
 
 
+@pytest.mark.parametrize("v_layout", ["dim", "token"])
 @pytest.mark.parametrize("cap", [None, 1, 5])
 @pytest.mark.parametrize("D,bs,G", [(128, 8, 8), (128, 16, 4), (64, 32, 2), (128, 32, 8), (64, 8, 1)])
-def test_fp8_32_token_units(gpu, wgs, D, bs, G, cap):
+def test_fp8_32_token_units(gpu, wgs, D, bs, G, cap, v_layout):
     """fp8 pools take 32-token units (two 16-row QK tiles and one 32-deep PV
     step per unit): lengths on both sides of multiples of 8, 16 and 32, and
-    units that span 4, 2 or 1 blocks."""
+    units that span 4, 2 or 1 blocks; dim-major V (8-byte runs from the
+    stage) and token-major V (rows widened to bf16 in the stage, two
+    transposing reads per 16-dim tile)."""
     wgs(cap)
     wl = synth.random_case(2600 + D + bs + G, FP8_LENGTHS, 2 * G, 2, D, bs, "fp8")
-    _check(wl, f"cap={cap}")
+    _check(wl, f"cap={cap}", v_layout=v_layout)
 
 
+@pytest.mark.parametrize("v_layout", ["dim", "token"])
 @pytest.mark.parametrize("hkv", [1, 3, 6])
-def test_fp8_head_groups(gpu, wgs, hkv):
-    """32-token fp8 units with one wave (Hkv 1) and odd workgroup widths
-    (3, 6), cut between a few workgroups."""
+def test_fp8_head_groups(gpu, wgs, hkv, v_layout):
+    """32-token fp8 units with one wave (Hkv 1) and workgroups of a power of
+    two below Hkv (3 -> 1, 6 -> 2 heads), cut between a few workgroups."""
     wgs(5)
     wl = synth.random_case(2700 + hkv, [33, 700, 1, 1500, 95], 4 * hkv, hkv, 128, 16, "fp8")
-    _check(wl, "cap=5")
+    _check(wl, "cap=5", v_layout=v_layout)
 
 
 @pytest.mark.parametrize("hkv", [1, 3, 6, 16, 24])

@@ -25,7 +25,7 @@ from tests.gpu_util import device_setup, run_decode, say
 pytestmark = pytest.mark.gpu
 
 BENCH_PARTITION = pa.BALANCED
-BENCH_V_LAYOUT = "token"  # the page's KVBlock layout; fp8 pools take dim-major V (their balanced kernels need it)
+BENCH_V_LAYOUT = "token"  # the page's KVBlock layout
 
 
 @pytest.mark.parametrize("part", [BENCH_PARTITION, 512], ids=["balanced", "part512"])
@@ -124,7 +124,7 @@ def test_mixed_batch_block_and_dtype_sweep(gpu, mixed_values, bs, kv):
     wl = synth.mixed_lengths(bs, kv)
     wl._kv_cache.update(mixed_values)
     say(f"mixed batch bs={bs} kv={kv}: {wl.total_tokens()} tokens, scales {wl.kv_scales()}")
-    _, cache, tables, lens, mx = device_setup(wl, v_layout=BENCH_V_LAYOUT if kv != "fp8" else "dim")
+    _, cache, tables, lens, mx = device_setup(wl, v_layout=BENCH_V_LAYOUT)
     got = run_decode(wl, cache, tables, lens, mx, BENCH_PARTITION)
     ma, rl = H.assert_close(got, H.oracle_contiguous(wl), what=f"mixed bs={bs} {kv}")
     say(f"   max-abs {ma:.2e} rel-L2 {rl:.2e}")
