@@ -125,17 +125,20 @@ __device__ __forceinline__ int sk_find_seq(const int32_t* pref, int B, int r) {
 __host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D) { return static_cast<size_t>(G) * D; }
 
 // The stage: the unit's K and V as loaded (whole rows), in LDS. S = HW * D
-// * b bytes is the head group's slice of a token row.
+// * b bytes is the head group's slice of a token row. (Measured with the
+// LDS counters: the LDS serves 16-byte reads of 16 rows at 128 bytes per
+// cycle whatever the row offsets, as long as no two rows share their banks
+// outright; the transposing 8-byte read of 4 rows x 32 bytes per 16 lanes
+// runs at 256 bytes per cycle when those rows sit 8 banks apart.)
 //  * 16-bit pools with token-major V: K and V as two [16][S] tiles. Row
-//    pitches: K rows S + 16 bytes (the 16 lanes of a 16-byte operand read,
-//    one row apart, then start 4 banks apart), V rows S + 32 bytes (a
-//    16-lane group of the transposing read touches 4 rows of 32 bytes,
-//    which then sit 8 banks apart).
-//  * fp8 pools: K as a [32][S] tile at pitch S + 16, rows 16..31 shifted by
-//    64 more bytes, so the permuted 32-token operand read (rows r and r + 16
-//    in one 16-lane group) stays conflict free. V dim-major: the head
-//    group's [HW][D][BS] region of each of the unit's blocks, as loaded (32
-//    S bytes); token-major: the 32 rows widened to bf16 (pitch 2 S + 32, the
+//    pitches: K rows S + 16 bytes (a pitch of S would put all 16 rows of an
+//    operand read on the same banks), V rows S + 32 bytes (the 4 rows of a
+//    transposing read then sit 8 banks apart).
+//  * fp8 pools: K as a [32][S] tile at pitch S + 16 (rows 16..31 64 bytes
+//    further; measured to make no difference). V dim-major: the head group's [HW][D][BS] region of each
+//    of the unit's blocks, stored chunk-major ([HW][BS / 8][D][8 bytes]: an
+//    operand read of 16 head dims is then 128 contiguous bytes; 32 S bytes);
+//    token-major: the 32 rows widened to bf16 (pitch 2 S + 32, the
 //    transposing reads as for 16-bit pools).
 __host__ __device__ inline constexpr int sk_stage_kpitch(int S) { return S + 16; }
 __host__ __device__ inline constexpr int sk_stage_vpitch(int S) { return S + 32; }
@@ -636,7 +639,20 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
           *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b.x, b.y};
           *reinterpret_cast<u32x4*>(dst + 16) = u32x4{c.x, c.y, d.x, d.y};
         } else {
-          *reinterpret_cast<u32x4*>(stage_v + st_f(i)) = vr[i];
+          // dim-major V (fp8): chunk-major, [part][head][8-token chunk][dim]
+          // [8 bytes], so the 16 lanes of an operand read (16 head dims, one
+          // chunk) read 128 contiguous bytes
+          const int f = st_f(i);
+          const int off = f & (SV - 1);
+          char* hb = stage_v + (f - off) + (off / (D * BS)) * (D * BS);
+          const int rem = off % (D * BS);
+          const int d = rem / BS, t = rem % BS;
+          if constexpr (BS == 8) {
+            *reinterpret_cast<u32x4*>(hb + d * 8) = vr[i];  // dims d, d + 1
+          } else {
+            *reinterpret_cast<u32x2*>(hb + (t / 8) * (D * 8) + d * 8) = u32x2{vr[i].x, vr[i].y};
+            *reinterpret_cast<u32x2*>(hb + (t / 8 + 1) * (D * 8) + d * 8) = u32x2{vr[i].z, vr[i].w};
+          }
         }
       }
       // append: the new token's row of the head group into its cache slot,
@@ -681,7 +697,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
           vt_src = reinterpret_cast<const uint16_t*>(stage_v + (8 * j + (col >> 2)) * vpitch + wave * D * 2) +
                    4 * (col & 3);
         } else {
-          v8_src = stage_v + ((8 * j) / BS) * SV + (wave * D + col) * BS + (8 * j) % BS;
+          v8_src = stage_v + ((8 * j) / BS) * SV + wave * D * BS + (((8 * j) % BS) / 8) * (D * 8) + col * 8;
         }
       }
     } else {
@@ -778,7 +794,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         } else {
           u32x2 vv;
           if constexpr (STG) {
-            vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * BS);
+            vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * 8);
           } else {
             vv = vr[nt];
           }
