@@ -238,3 +238,23 @@ def test_workspace_reused_across_batches(gpu, wgs):
         out = pa.decode(cache, q, tables, lens, max_ctx, wl.scale, BAL, out_dtype=torch.float32, workspace=ws)
         torch.cuda.synchronize()
         H.assert_close(out.cpu().double().numpy(), H.oracle_contiguous(wl), what=f"reuse B={wl.batch} cap={cap}")
+
+
+def test_batch_at_the_lds_bound(gpu):
+    """The largest batch the balanced split takes with token-major V for 8
+    KV heads, G = 4, head_dim 128: its tile prefix fills the last bytes of
+    the 160 KiB of LDS a workgroup may use next to the stage (B = 20288 is
+    refused, see test_abi). Short sequences plus a few longer ones; sampled
+    rows against the oracle, every row finite."""
+    B = 20287
+    rng = np.random.default_rng(31)
+    lengths = rng.integers(1, 9, size=B)
+    lengths[[0, 7, B // 2, B - 1]] = [1, 200, 65, 33]
+    wl = synth.random_case(3300, lengths, 32, 8, 128, 16, "bf16")
+    say(f"balanced split at B = {B}")
+    _, cache, tables, lens, mx = device_setup(wl, v_layout="token")
+    got = run_decode(wl, cache, tables, lens, mx, pa.BALANCED)
+    assert np.isfinite(got).all()
+    rows = [0, 1, 7, 100, B // 2, B - 2, B - 1]
+    ref = H.oracle_contiguous(wl, seqs=rows)
+    H.assert_close(got[rows], ref[rows], what="B at the LDS bound")
