@@ -351,6 +351,18 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
       return fail(PA_ERR_UNSUPPORTED, "the balanced split needs %zu bytes of LDS per workgroup (device: %zu)", lds,
                   dev_lds);
   }
+  // staged: two stages (one barrier per unit instead of two) when the
+  // workgroups that hold 8 waves per CU still fit a CU's LDS with them
+  int stage_bufs = 1;
+  if (staged && G <= 4) {  // (the two-stage build exists for G <= 4)
+    const size_t lds2 = sk_lds_bytes(B, HW, G, D, true, cache->dtype == PA_FP8_E4M3 ? 1 : 2, tv, 2);
+    const size_t dev_lds = sk_device_lds();
+    const size_t per_cu = static_cast<size_t>(std::max(1, 8 / HW));
+    if (dev_lds > 0 && lds2 <= dev_lds && lds2 * per_cu <= kSkMaxLdsStage) stage_bufs = 2;
+    if (const char* v = std::getenv("PA_SK_STAGES")) {  // measurement aid
+      if (std::atoi(v) == 1) stage_bufs = 1;
+    }
+  }
   SkLayout lay{};
   if (part_mode) {
     // [m][l][o] per (sequence, query head, partition) = per piece row of
@@ -394,6 +406,7 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   p.heads_per_wg = HW;
   p.num_head_groups = n_hg;
   p.piece_slots = part_mode ? 1 : 2;
+  p.stage_bufs = stage_bufs;
   if (part_mode) {
     // tiles per partition: 16 tokens (32 for fp8 pools; the caller keeps
     // partition_size a multiple of it, or uses one partition)

@@ -96,6 +96,7 @@ struct SkParams {
   int32_t part_tiles;
   int32_t num_parts;
   int32_t piece_slots;      // piece slots per workgroup: 2 (balanced), 1 (partition mode)
+  int32_t stage_bufs;       // LDS stages (staged path): 2 = alternate per unit, one barrier per unit
   int32_t out_dtype;
   float qk_scale_log2;
   float v_scale;
@@ -148,11 +149,11 @@ __host__ __device__ inline constexpr size_t sk_stage_bytes(int HW, int D, int kb
                        32 * static_cast<size_t>(tv ? sk_stage_vpitch(2 * HW * D) : HW * D);
 }
 
-// bytes of dynamic LDS: the tile prefix, the stage (token-major V or fp8
+// bytes of dynamic LDS: the tile prefix, the stage(s) (token-major V or fp8
 // pools: `staged`), then one region per wave
-inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool staged, int kb, bool tv) {
+inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool staged, int kb, bool tv, int bufs = 1) {
   const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
-  return pref + (staged ? sk_stage_bytes(HW, D, kb, tv) : 0) +
+  return pref + (staged ? bufs * sk_stage_bytes(HW, D, kb, tv) : 0) +
          static_cast<size_t>(HW) * sk_wave_lds_floats(G, D) * sizeof(float);
 }
 
@@ -183,7 +184,8 @@ struct SkUnit {
   int virt, sblk, soff;
 };
 
-template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV>
+// NBUF: LDS stages of the staged path (2: units alternate between them)
+template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV, int NBUF>
 __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
@@ -221,7 +223,12 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   const int wave = threadIdx.x >> 6;
   const int HW = p.heads_per_wg;
   char* stage = reinterpret_cast<char*>(sk_smem + (B + 1 + 3) / 4 * 4);  // STG only
-  float* s_out_all = reinterpret_cast<float*>(stage + (STG ? sk_stage_bytes(HW, D, kB, TV) : 0));
+  // with two stages, unit x uses stage x % 2: the barrier after the stage
+  // write of unit x + 1 already orders unit x's reads before the next
+  // write into its stage, so no barrier is needed after a unit
+  static_assert(NBUF == 1 || (NBUF == 2 && (TV || kB == 1)), "two stages on the staged path only");
+  const int sbytes = STG ? static_cast<int>(sk_stage_bytes(HW, D, kB, TV)) : 0;
+  float* s_out_all = reinterpret_cast<float*>(stage + NBUF * sbytes);
 
   // ---- plan: tiles per sequence, then their exclusive prefix (in place)
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
@@ -609,6 +616,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
                      const VSlot (&vr)[kVL]) {
     const int tb = AP && un.virt ? 0 : un.tile * TT;
     const int L = un.len;
+    char* const stg = stage + (NBUF == 2 && (x & 1) ? sbytes : 0);  // this unit's stage
+    char* const stg_v = stg + (stage_v - stage);
     // ---- token-major V: the unit's rows go to the stage as loaded; after
     // the barrier each wave reads its head's K rows in the QK operand layout
     // (lane (token col, j): the 16 bytes of dims qk_dim(i, j)) and later its
@@ -628,14 +637,14 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       }
 #pragma unroll
       for (int i = 0; i < kKP; ++i) {
-        *reinterpret_cast<u32x4*>(stage + st_k(st_r(i), st_cb(i))) = kr[i];
+        *reinterpret_cast<u32x4*>(stg + st_k(st_r(i), st_cb(i))) = kr[i];
         if constexpr (TV && kB == 2) {
-          *reinterpret_cast<u32x4*>(stage_v + st_r(i) * vpitch + st_cb(i)) = vr[i];
+          *reinterpret_cast<u32x4*>(stg_v + st_r(i) * vpitch + st_cb(i)) = vr[i];
         } else if constexpr (TV) {
           // fp8 token-major V: 16 codes -> 16 bf16, exact
           const u32x2 a = e4m3x4_to_bf16x4(vr[i].x), b = e4m3x4_to_bf16x4(vr[i].y);
           const u32x2 c = e4m3x4_to_bf16x4(vr[i].z), d = e4m3x4_to_bf16x4(vr[i].w);
-          char* dst = stage_v + st_r(i) * vpitch + 2 * st_cb(i);
+          char* dst = stg_v + st_r(i) * vpitch + 2 * st_cb(i);
           *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b.x, b.y};
           *reinterpret_cast<u32x4*>(dst + 16) = u32x4{c.x, c.y, d.x, d.y};
         } else {
@@ -644,7 +653,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
           // chunk) read 128 contiguous bytes
           const int f = st_f(i);
           const int off = f & (SV - 1);
-          char* hb = stage_v + (f - off) + (off / (D * BS)) * (D * BS);
+          char* hb = stg_v + (f - off) + (off / (D * BS)) * (D * BS);
           const int rem = off % (D * BS);
           const int d = rem / BS, t = rem % BS;
           if constexpr (BS == 8) {
@@ -676,10 +685,10 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 #pragma unroll
       for (int i = 0; i < C::kKSteps; ++i) qb[i] = *reinterpret_cast<const u32x4*>(qsrc + qk_dim<kB>(i, j) * 2);
       if constexpr (TT == 16) {
-        const char* ks = stage + col * kpitch + wave * D * kB;
+        const char* ks = stg + col * kpitch + wave * D * kB;
 #pragma unroll
         for (int i = 0; i < C::kKSteps; ++i) kop[i] = *reinterpret_cast<const u32x4*>(ks + qk_dim<2>(i, j) * kB);
-        vt_src = reinterpret_cast<const uint16_t*>(stage_v + (4 * j + (col >> 2)) * vpitch + wave * D * kB) + 4 * (col & 3);
+        vt_src = reinterpret_cast<const uint16_t*>(stg_v + (4 * j + (col >> 2)) * vpitch + wave * D * kB) + 4 * (col & 3);
       } else {
         // fp8: QK tile s row `col` is token 8 (col / 4) + col % 4 + 4 s; the
         // PV operand of lane (d, j) is the run of head dim d over tokens
@@ -690,14 +699,14 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 #pragma unroll
           for (int a = 0; a < C::kKLoads; ++a)
             kop[s * C::kKLoads + a] =
-                *reinterpret_cast<const u32x4*>(stage + st_k(row, wave * D + qk_dim<1>(2 * a, j)));
+                *reinterpret_cast<const u32x4*>(stg + st_k(row, wave * D + qk_dim<1>(2 * a, j)));
         }
         if constexpr (TV) {
           // tokens 8j .. 8j + 3 and 8j + 4 .. 8j + 7: two transposing reads
-          vt_src = reinterpret_cast<const uint16_t*>(stage_v + (8 * j + (col >> 2)) * vpitch + wave * D * 2) +
+          vt_src = reinterpret_cast<const uint16_t*>(stg_v + (8 * j + (col >> 2)) * vpitch + wave * D * 2) +
                    4 * (col & 3);
         } else {
-          v8_src = stage_v + ((8 * j) / BS) * SV + wave * D * BS + (((8 * j) % BS) / 8) * (D * 8) + col * 8;
+          v8_src = stg_v + ((8 * j) / BS) * SV + wave * D * BS + (((8 * j) % BS) / 8) * (D * 8) + col * 8;
         }
       }
     } else {
@@ -848,7 +857,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // rows overwrite them
   auto unit_barrier = [&]() {
     if constexpr (STG) {
-      lds_barrier();
+      if constexpr (NBUF == 1) lds_barrier();
     } else {
       __builtin_amdgcn_s_barrier();
     }
@@ -897,18 +906,17 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   } while (uk <= ulast);
 }
 
-// Launch of the balanced kernel: W = resident workgroups (occupancy x CUs),
-// at most max_wgs. Writes the grid size used to *wgs.
-template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV>
-hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
+// One build of the balanced kernel (NBUF stages).
+template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV, int NBUF>
+hipError_t launch_decode_sk_n(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
   const int HW = p.heads_per_wg;
-  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes, TV);
+  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes, TV, NBUF);
   // more than 64 KiB of dynamic LDS (the stage) must be
   // allowed per kernel; racing callers set the same attribute
   static int lds_allowed = 64 * 1024;  // per instantiation
   if (static_cast<int>(lds) > lds_allowed) {
     const hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     lds_allowed = static_cast<int>(lds);
@@ -918,8 +926,8 @@ hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t
   const int lb = static_cast<int>((lds + 4095) / 4096);
   int occ = (HW <= 8 && lb <= 40) ? cache[HW][lb] : 0;
   if (occ <= 0) {
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV>,
-                                                                64 * HW, lds);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &occ, paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>, 64 * HW, lds);
     if (e != hipSuccess) return e;
     if (occ <= 0) return hipErrorInvalidConfiguration;
     if (HW <= 8 && lb <= 40) cache[HW][lb] = occ;
@@ -928,8 +936,20 @@ hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t
   int W = p.part_tiles > 0 ? max_wgs : cus * occ;
   W = W < max_wgs ? W : max_wgs;
   *wgs = W;
-  hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV>), dim3(W), dim3(64 * HW), lds, stream, p);
+  hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>), dim3(W), dim3(64 * HW), lds, stream, p);
   return hipGetLastError();
+}
+
+// Launch of the balanced kernel: W = resident workgroups (occupancy x CUs),
+// at most max_wgs. Writes the grid size used to *wgs. p.stage_bufs = 2
+// takes the two-stage build (built for the staged path with G <= 4, where
+// two stages can fit next to the wave regions).
+template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV>
+hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
+  if constexpr ((TV || KV::kBytes == 1) && G <= 4) {
+    if (p.stage_bufs > 1) return launch_decode_sk_n<KV, QT, D, BS, G, AP, TV, 2>(p, cus, max_wgs, stream, wgs);
+  }
+  return launch_decode_sk_n<KV, QT, D, BS, G, AP, TV, 1>(p, cus, max_wgs, stream, wgs);
 }
 
 template <typename KV, typename QT, int D, int BS, bool AP, bool TV>
