@@ -33,6 +33,8 @@
  * PA_PARTITION_PATH=staged|wave picks, for partitioned pa_decode calls
  * where both exist, the staged kernel or the one-wave partition kernels
  * (normally chosen from the batch shape; for tests and measurements).
+ * PA_SK_STAGES=1 keeps the staged kernel at one LDS stage where it would
+ * take two (for measurements; same result).
  */
 #ifndef LIBPAGEDATTN_H
 #define LIBPAGEDATTN_H
