@@ -22,7 +22,7 @@ from ._lib import PaBmStats, PaKvCache, lib
 __all__ = [
     "PagedAttnError", "OutOfBlocks", "UnknownSeq", "SeqExists", "Unsupported", "InvalidArgument",
     "DeviceError", "BlockManager", "KVCache", "reshape_and_cache", "copy_blocks", "decode",
-    "decode_workspace_size", "decode_append", "decode_shared", "SharedPrefixes", "copy_blocks_between", "lib",
+    "decode_workspace_size", "decode_append", "prepare_decode_append", "decode_shared", "SharedPrefixes", "copy_blocks_between", "lib",
     "BALANCED",
 ]
 
@@ -460,14 +460,15 @@ def decode(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_
     return out
 
 
-def decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
-                  q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
-                  scale: float, out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """pa_decode_append: write each sequence's newest token (k_new / v_new
-    [B][Hkv][D] at slot_mapping[s], the slot of token context_lens[s] - 1)
-    and run the balanced decode that includes it, in one launch. Returns
-    ``out`` [B][Hq][D]."""
+def prepare_decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                          q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,
+                          out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+                          stream=None):
+    """decode_append with its arguments marshalled now and the launch
+    deferred: returns a callable that issues pa_decode_append and returns
+    ``out`` (e.g. to time the launch alone). The tensors must stay alive
+    and unchanged in shape until it is called."""
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
@@ -479,14 +480,36 @@ def decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     desc = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    with torch.cuda.device(q.device):
-        _check(lib().pa_decode_append(ctypes.byref(desc), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _code(k_new),
-                                      _dev(slot_mapping, "slot_mapping"), _dev(out, "out"), _code(out),
-                                      _dev(q, "q"), _code(q), _dev(block_tables, "block_tables"),
-                                      int(block_tables.shape[1]), _dev(context_lens, "context_lens"), int(B),
-                                      int(Hq), int(max_context_len), float(scale), _dev(workspace, "workspace"),
-                                      ws_bytes, _stream(stream)))
-    return out
+    args = (ctypes.byref(desc), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _code(k_new),
+            _dev(slot_mapping, "slot_mapping"), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
+            _dev(block_tables, "block_tables"), int(block_tables.shape[1]), _dev(context_lens, "context_lens"),
+            int(B), int(Hq), int(max_context_len), float(scale), _dev(workspace, "workspace"), ws_bytes,
+            _stream(stream))
+    fn = lib().pa_decode_append
+    device = q.device
+
+    def launch() -> torch.Tensor:
+        if device.index == torch.cuda.current_device():
+            _check(fn(*args))
+        else:
+            with torch.cuda.device(device):
+                _check(fn(*args))
+        return out
+
+    launch.keep = (desc, workspace)  # what args point into
+    return launch
+
+
+def decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                  q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                  scale: float, out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode_append: write each sequence's newest token (k_new / v_new
+    [B][Hkv][D] at slot_mapping[s], the slot of token context_lens[s] - 1)
+    and run the balanced decode that includes it, in one launch. Returns
+    ``out`` [B][Hq][D]."""
+    return prepare_decode_append(cache, k_new, v_new, slot_mapping, q, block_tables, context_lens, max_context_len,
+                                 scale, out=out, out_dtype=out_dtype, workspace=workspace, stream=stream)()
 
 
 def decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
