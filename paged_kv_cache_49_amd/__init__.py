@@ -467,8 +467,8 @@ def prepare_decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tens
                           stream=None):
     """decode_append with its arguments marshalled now and the launch
     deferred: returns a callable that issues pa_decode_append and returns
-    ``out`` (e.g. to time the launch alone). The tensors must stay alive
-    and unchanged in shape until it is called."""
+    ``out`` (e.g. to time the launch alone). The callable holds the
+    tensors it points into; their shapes must not change before it runs."""
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
@@ -496,7 +496,7 @@ def prepare_decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tens
                 _check(fn(*args))
         return out
 
-    launch.keep = (desc, workspace)  # what args point into
+    launch.keep = (desc, workspace, cache, k_new, v_new, slot_mapping, q, block_tables, context_lens)  # args' memory
     return launch
 
 
