@@ -22,7 +22,7 @@ from ._lib import PaBmStats, PaKvCache, lib
 __all__ = [
     "PagedAttnError", "OutOfBlocks", "UnknownSeq", "SeqExists", "Unsupported", "InvalidArgument",
     "DeviceError", "BlockManager", "KVCache", "reshape_and_cache", "copy_blocks", "decode",
-    "decode_workspace_size", "decode_append", "prepare_decode_append", "decode_shared", "SharedPrefixes", "copy_blocks_between", "lib",
+    "decode_workspace_size", "decode_append", "prepare_decode", "prepare_decode_append", "prepare_decode_shared", "decode_shared", "SharedPrefixes", "copy_blocks_between", "lib",
     "BALANCED",
 ]
 
@@ -436,12 +436,28 @@ def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, head_
                                               int(max_context_len), int(partition_size)))
 
 
-def decode(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
-           max_context_len: int, scale: float, partition_size: int = 0, out: Optional[torch.Tensor] = None,
-           out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
-           stream=None) -> torch.Tensor:
-    """Paged decode attention; returns ``out`` [B][Hq][D]. A workspace is
-    allocated with torch when the split needs one and none is given."""
+def _deferred(fn, args, device: torch.device, out: torch.Tensor, keep):
+    """A callable that issues fn(*args) on ``device`` and returns ``out``;
+    it holds ``keep``, the objects args point into."""
+    def launch() -> torch.Tensor:
+        if device.index == torch.cuda.current_device():
+            _check(fn(*args))
+        else:
+            with torch.cuda.device(device):
+                _check(fn(*args))
+        return out
+
+    launch.keep = keep
+    return launch
+
+
+def prepare_decode(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                   max_context_len: int, scale: float, partition_size: int = 0, out: Optional[torch.Tensor] = None,
+                   out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """decode with its arguments marshalled now and the launch deferred:
+    returns a callable that issues pa_decode and returns ``out`` (e.g. to
+    time the launch alone). The callable holds the tensors it points into;
+    their shapes must not change before it runs."""
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
@@ -451,13 +467,21 @@ def decode(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     desc = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    with torch.cuda.device(q.device):
-        _check(lib().pa_decode(ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
-                               _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
-                               _dev(context_lens, "context_lens"), int(B), int(Hq), int(max_context_len),
-                               float(scale), int(partition_size), _dev(workspace, "workspace"), ws_bytes,
-                               _stream(stream)))
-    return out
+    args = (ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
+            _dev(block_tables, "block_tables"), int(block_tables.shape[1]), _dev(context_lens, "context_lens"),
+            int(B), int(Hq), int(max_context_len), float(scale), int(partition_size), _dev(workspace, "workspace"),
+            ws_bytes, _stream(stream))
+    return _deferred(lib().pa_decode, args, q.device, out, (desc, workspace, cache, q, block_tables, context_lens))
+
+
+def decode(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+           max_context_len: int, scale: float, partition_size: int = 0, out: Optional[torch.Tensor] = None,
+           out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Paged decode attention; returns ``out`` [B][Hq][D]. A workspace is
+    allocated with torch when the split needs one and none is given."""
+    return prepare_decode(cache, q, block_tables, context_lens, max_context_len, scale, partition_size, out=out,
+                          out_dtype=out_dtype, workspace=workspace, stream=stream)()
 
 
 def prepare_decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
@@ -485,19 +509,8 @@ def prepare_decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tens
             _dev(block_tables, "block_tables"), int(block_tables.shape[1]), _dev(context_lens, "context_lens"),
             int(B), int(Hq), int(max_context_len), float(scale), _dev(workspace, "workspace"), ws_bytes,
             _stream(stream))
-    fn = lib().pa_decode_append
-    device = q.device
-
-    def launch() -> torch.Tensor:
-        if device.index == torch.cuda.current_device():
-            _check(fn(*args))
-        else:
-            with torch.cuda.device(device):
-                _check(fn(*args))
-        return out
-
-    launch.keep = (desc, workspace, cache, k_new, v_new, slot_mapping, q, block_tables, context_lens)  # args' memory
-    return launch
+    return _deferred(lib().pa_decode_append, args, q.device, out,
+                     (desc, workspace, cache, k_new, v_new, slot_mapping, q, block_tables, context_lens))
 
 
 def decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
@@ -512,14 +525,14 @@ def decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot
                                  scale, out=out, out_dtype=out_dtype, workspace=workspace, stream=stream)()
 
 
-def decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
-                  max_context_len: int, scale: float, partition_size: int, group_offsets: torch.Tensor,
-                  group_members: torch.Tensor, shared_len: torch.Tensor, num_groups: int, max_group_size: int,
-                  max_shared_len: int, min_shared_len: int = 0, out: Optional[torch.Tensor] = None,
-                  out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
-                  stream=None) -> torch.Tensor:
-    """pa_decode_shared: decode with each group's shared prefix read once
-    for all its rows (group arrays on the device, int32). Returns ``out``."""
+def prepare_decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          max_context_len: int, scale: float, partition_size: int, group_offsets: torch.Tensor,
+                          group_members: torch.Tensor, shared_len: torch.Tensor, num_groups: int,
+                          max_group_size: int, max_shared_len: int, min_shared_len: int = 0,
+                          out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """decode_shared with its arguments marshalled now and the launch
+    deferred (see prepare_decode)."""
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
@@ -532,15 +545,29 @@ def decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, c
             raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, f"{name} must be int32")
     desc = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    with torch.cuda.device(q.device):
-        _check(lib().pa_decode_shared(ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
-                                      _dev(block_tables, "block_tables"), int(block_tables.shape[1]),
-                                      _dev(context_lens, "context_lens"), int(B), int(Hq), int(max_context_len),
-                                      float(scale), int(partition_size), _dev(group_offsets, "group_offsets"),
-                                      _dev(group_members, "group_members"), _dev(shared_len, "shared_len"),
-                                      int(num_groups), int(max_group_size), int(max_shared_len),
-                                      int(min_shared_len), _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
-    return out
+    args = (ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
+            _dev(block_tables, "block_tables"), int(block_tables.shape[1]), _dev(context_lens, "context_lens"),
+            int(B), int(Hq), int(max_context_len), float(scale), int(partition_size),
+            _dev(group_offsets, "group_offsets"), _dev(group_members, "group_members"), _dev(shared_len, "shared_len"),
+            int(num_groups), int(max_group_size), int(max_shared_len), int(min_shared_len),
+            _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    return _deferred(lib().pa_decode_shared, args, q.device, out,
+                     (desc, workspace, cache, q, block_tables, context_lens, group_offsets, group_members,
+                      shared_len))
+
+
+def decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                  max_context_len: int, scale: float, partition_size: int, group_offsets: torch.Tensor,
+                  group_members: torch.Tensor, shared_len: torch.Tensor, num_groups: int, max_group_size: int,
+                  max_shared_len: int, min_shared_len: int = 0, out: Optional[torch.Tensor] = None,
+                  out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """pa_decode_shared: decode with each group's shared prefix read once
+    for all its rows (group arrays on the device, int32). Returns ``out``."""
+    return prepare_decode_shared(cache, q, block_tables, context_lens, max_context_len, scale, partition_size,
+                                 group_offsets, group_members, shared_len, num_groups, max_group_size,
+                                 max_shared_len, min_shared_len, out=out, out_dtype=out_dtype, workspace=workspace,
+                                 stream=stream)()
 
 
 def ref_stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int, stream=None) -> None:

@@ -33,8 +33,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (BALANCED, BlockManager, KVCache, copy_blocks, decode, decode_append, decode_shared,
-               prepare_decode_append,
+from . import (BALANCED, BlockManager, KVCache, copy_blocks, prepare_decode, prepare_decode_append,
+               prepare_decode_shared,
                decode_workspace_size, reshape_and_cache)
 
 
@@ -176,26 +176,24 @@ class PagedBatch:
             if timed:
                 mk = make_event or (lambda: torch.cuda.Event(enable_timing=True))
                 ev = (mk(), mk())
+            # arguments marshalled before the start event, so the timed
+            # interval holds the launch alone (no host work)
             if fused:
                 if partition_size != BALANCED:
                     raise ValueError("fused steps use the balanced split (partition_size = BALANCED)")
-                # arguments marshalled before the start event, so the timed
-                # interval holds the launch alone (no host work)
                 launch = prepare_decode_append(c, k_new[i], v_new[i], st.slots[:B], q[i], tables, lens, max_ctx,
                                                scale, out=outs[i], workspace=workspace)
-                if timed:
-                    ev[0].record()
-                launch()
-            elif timed:
-                ev[0].record()
-            if fused:
-                pass
             elif groups is not None:
-                decode_shared(c, q[i], tables, lens, max_ctx, scale, partition_size, st.goff, st.gmem[:B],
-                              st.shl[:B], groups.num_groups, groups.max_group_size, groups.max_shared_len,
-                              groups.min_shared_len, out=outs[i], workspace=workspace)
+                launch = prepare_decode_shared(c, q[i], tables, lens, max_ctx, scale, partition_size, st.goff,
+                                               st.gmem[:B], st.shl[:B], groups.num_groups, groups.max_group_size,
+                                               groups.max_shared_len, groups.min_shared_len, out=outs[i],
+                                               workspace=workspace)
             else:
-                decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i], workspace=workspace)
+                launch = prepare_decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i],
+                                        workspace=workspace)
+            if timed:
+                ev[0].record()
+            launch()
             if timed:
                 ev[1].record()
                 decode_events.append(ev)
