@@ -221,3 +221,23 @@ def test_partition_paths(gpu, monkeypatch, path, kv, v_layout):
                      max_ctx, wl.scale, 256, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(part.cpu(), full.cpu()[rows]), "partitioned rows depend on the rest of the batch"
+
+
+def test_deferred_launches_match_direct_calls(gpu):
+    """prepare_decode marshals the arguments and returns the bare launch
+    (prepare_decode_append's runs in every runner-driven step): running it
+    after the caller has dropped the tensors it was prepared with gives the
+    direct call's output bit for bit."""
+    say("deferred launches")
+    wl = synth.random_case(3400, [700, 1, 2049, 300], 32, 8, 128, 16, "bf16")
+    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout="token")
+    q = wl.q().cuda()
+    for ps in (pa.BALANCED, 512, 0):
+        direct = pa.decode(cache, q, tables, lens, max_ctx, wl.scale, ps, out_dtype=torch.float32)
+        launch = pa.prepare_decode(cache, q.clone(), tables.clone(), lens.clone(), max_ctx, wl.scale, ps,
+                                   out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        later = launch()
+        torch.cuda.synchronize()
+        assert torch.equal(direct, later), f"partition_size {ps}"
+    H.assert_close(later.cpu().double().numpy(), H.oracle_contiguous(wl), what="deferred")
