@@ -140,6 +140,43 @@ class HipTimingEvent:
             self.h = None
 
 
+def step_timeline(tms, origin, t0: float, wall: float, layers: int) -> dict:
+    """Per-step timeline of timed PagedBatch steps: host phase stamps
+    (relative to t0, microseconds), the device span of each step on the
+    compute stream (from ``origin``, recorded at t0), layer 0's call time,
+    and the device idle gap before each step; plus a summary."""
+    rows = []
+    prev_end = 0.0
+    for i, tm in enumerate(tms):
+        h = {k: round((v - t0) * 1e6, 1) for k, v in tm.host.items()}
+        g0 = origin.elapsed_time(tm.start) * 1e3
+        g1 = origin.elapsed_time(tm.end) * 1e3
+        call = tm.calls[0][0].elapsed_time(tm.calls[0][1]) * 1e3
+        rows.append({"step": i, "host_us": h, "gpu_start_us": round(g0, 1), "gpu_end_us": round(g1, 1),
+                     "gpu_span_us": round(g1 - g0, 1), "gap_before_us": round(g0 - prev_end, 1),
+                     "call0_us": round(call, 1)})
+        prev_end = g1
+    span = np.array([r["gpu_span_us"] for r in rows])
+    gap = np.array([r["gap_before_us"] for r in rows])
+    host = np.array([r["host_us"]["launched"] - r["host_us"]["enter"] for r in rows])
+    bm = np.array([r["host_us"]["block_manager"] - r["host_us"]["staging_free"] for r in rows])
+    wait = np.array([r["host_us"]["staging_free"] - r["host_us"]["enter"] for r in rows])
+    launch = np.array([r["host_us"]["launched"] - r["host_us"]["upload"] for r in rows])
+    summary = {
+        "wall_us_per_step": round(wall / len(rows) * 1e6, 1),
+        "gpu_span_us_mean": round(float(span.mean()), 1),
+        "gpu_gap_us_mean": round(float(gap[1:].mean()) if len(gap) > 1 else 0.0, 1),
+        "first_step_gap_us": round(float(gap[0]), 1),
+        "host_us_per_step_mean": round(float(host.mean()), 1),
+        "host_staging_wait_us_mean": round(float(wait.mean()), 1),
+        "host_block_manager_us_mean": round(float(bm.mean()), 1),
+        "host_launch_us_mean": round(float(launch.mean()), 1),
+        "note": "gpu span: compute-stream events at a step's start (after its upload wait) and end, "
+                f"{layers} layers; gap: device idle between steps; host: Python time inside step()",
+    }
+    return {"summary": summary, "steps": rows}
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -172,6 +209,8 @@ def parse():
     p.add_argument("--stream-ref", action="store_true",
                    help="only time a plain streaming read of 4 GiB (pa_ref_stream_read), the attainable read "
                         "bandwidth the decode is compared with, and exit")
+    p.add_argument("--timeline", default=None,
+                   help="GQA step: write the per-step host and device timeline (JSON) to this file")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return p.parse_args()
@@ -457,7 +496,7 @@ def main():
 
     import paged_kv_cache_49_amd as pa
     import synth
-    from paged_kv_cache_49_amd.runner import PagedBatch, workspace_for
+    from paged_kv_cache_49_amd.runner import PagedBatch, StepTiming, workspace_for
 
     pa.lib()
     torch.cuda.set_device(0)
@@ -495,26 +534,35 @@ def main():
     print("[bench] setup done", file=sys.stderr, flush=True)
 
     fused = args.partition_size == pa.BALANCED and not args.separate_write
-    for _ in range(W):
-        batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, fused=fused)
+    # every timing event (warm-up and timed steps) exists before the first
+    # step: the warm-up runs exactly the timed path, events included, and no
+    # event is created inside the timed region
+    warm_tm = [StepTiming(HipTimingEvent) for _ in range(W)]
+    step_tm = [StepTiming(HipTimingEvent) for _ in range(K)]
+    origin = HipTimingEvent()
+    for tm in warm_tm:
+        batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, timing=tm, fused=fused)
     torch.cuda.synchronize()
     lens_before = L0 + W
 
-    events = []
     batch.host_seconds, batch.host_steps = 0.0, 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(K):
-        batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, decode_events=events,
-                   event_layers=(0,), make_event=HipTimingEvent, fused=fused)
+    origin.record()
+    for tm in step_tm:
+        batch.step(ids, k_new, v_new, q, outs, wl.scale, args.partition_size, ws, ones, timing=tm, fused=fused)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     el = t1 - t0
+    timeline = step_timeline(step_tm, origin, t0, el, layers)
+    if args.timeline:
+        with open(args.timeline, "w") as fh:
+            json.dump(timeline, fh, indent=1)
 
     kv_row = 2 * Hkv * D * 2  # K and V bytes of one token of one sequence (bf16)
     step_bytes = [layers * kv_row * int((lens_before + i + 1).sum()) for i in range(K)]
     total_bytes = float(sum(step_bytes))
-    durs = np.array([a.elapsed_time(b) for a, b in events]) * 1e-3  # seconds
+    durs = np.array([tm.calls[0][0].elapsed_time(tm.calls[0][1]) for tm in step_tm]) * 1e-3  # seconds
     per_call_bytes = total_bytes / (K * layers)  # every layer of a step reads the same bytes
     call_s = float(durs.mean())
     achieved = per_call_bytes / call_s / 1e9
@@ -553,6 +601,9 @@ def main():
         "pa_decode_us_min": round(float(durs.min()) * 1e6, 2),
         "host_block_manager_us_per_step": round(batch.host_seconds / max(batch.host_steps, 1) * 1e6, 2),
         "host_block_manager_note": "pa_alloc_batch + pa_bm_pack of the whole batch on the host, inside each step",
+        "gpu_busy_frac": round(layers * call_s / (el / K), 4),
+        "gpu_busy_note": "layers x mean pa_decode call time / step wall time",
+        "step_timeline": timeline["summary"],
         "roofline": {
             "bound": "hbm",
             "kernel": (("pa_decode_append" if fused else "pa_decode") +

@@ -76,10 +76,10 @@ int32_t pa_abi_version(void);
 /* ------------------------------------------------------------------------
  * Host block manager.
  *
- * [course] §2 "The insight": the KV cache is a pool of same-size physical
- * blocks; blocks are allocated on demand as a sequence grows and freed as
- * soon as it finishes; each sequence's block table maps its logical token
- * positions to scattered physical blocks. [note] 最小模型: growth takes one
+ * [course] §2 "The insight": the KV cache lives in a pool of physical
+ * blocks of one size; a sequence takes a block only when its tokens need
+ * one and returns all of them when it is done; its block table names the
+ * physical block behind each logical block. [note] 最小模型: growth takes one
  * more block, release returns the sequence's own blocks; [note] block-size
  * section: a sequence of L tokens holds ceil(L / block_size) blocks.
  * [course] §2 "The bonus: block sharing (copy-on-write)" and [note] prefix
@@ -352,7 +352,7 @@ typedef struct pa_kv_cache {
 } pa_kv_cache;
 
 /* Write the K/V rows of T new tokens into their slots ([course] §2 primer:
- * each request's KV grows one token at a time; [course] §2 "The insight").
+ * each decode step adds one token's K/V; [course] §2 "The insight").
  * k_new, v_new: device [T][num_kv_heads][head_dim], contiguous, 16-byte
  * aligned, of src_dtype. slot_mapping: device int64[T]; token i goes to
  * block slot/block_size, row slot%block_size; a negative slot skips the
@@ -389,7 +389,7 @@ pa_status pa_copy_blocks_between(const pa_kv_cache* dst, const pa_kv_cache* src,
 
 /* ------------------------------------------------------------------------
  * Decode attention through the block tables ([course] §2 "The insight":
- * the kernel follows the table to gather K/V during the dot product;
+ * keys and values are looked up through the table as attention runs;
  * [note] 最小模型: physical blocks are read in logical token order; [note]
  * "why it works": the result is ordinary attention).
  *

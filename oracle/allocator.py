@@ -1,11 +1,11 @@
 """Block manager model — oracle for the host allocator.
 
 What the pages fix:
-* [course] §2 "The insight": a pool of same-size physical blocks in GPU
-  memory; blocks are allocated on demand as a sequence grows and freed
-  immediately when it finishes; each sequence's block table maps its
-  logical positions to scattered physical blocks. At most one block per
-  sequence is partially filled.
+* [course] §2 "The insight": physical blocks, all of one size, form a
+  pool; a sequence takes a new block only when its tokens overflow the
+  blocks it holds, and hands its blocks back the moment it is done; a
+  per-sequence table says which physical block holds each logical block.
+  Only a sequence's last block can be partly empty.
 * [note] 最小模型 ("minimal model"): growing a request only allocates one more
   block; a finished request releases its own blocks.
 * [note] section "block size 是容量与 kernel 的共同参数": a request of

@@ -2,12 +2,12 @@
 
 What the paged path computes, as the pages state it:
 
-* [course] §2 "The insight: page the KV cache like OS virtual memory": the
-  KV cache is cut into fixed-size blocks held in one pool; each sequence has
-  a block table from its logical blocks to physical block ids, and the
-  attention kernel follows that indirection to gather K/V during the dot
-  product. The pool layout printed there is K[BLOCK][HEADS][HEAD_DIM] per
-  block (token-major inside a block).
+* [course] §2 "The insight: page the KV cache like OS virtual memory": one
+  pool holds the KV cache as blocks of a fixed size; a per-sequence table
+  names the physical block behind each logical block, and attention looks
+  every key and value up through that table while it computes the scores.
+  The block layout the section prints is K[BLOCK][HEADS][HEAD_DIM]
+  (token-major inside a block).
 * [note] section 最小模型 ("minimal model"): the kernel reads the block table
   and visits the (possibly scattered) physical blocks in logical token order.
 * [note] section 它为什么有效 ("why it works"): paging is not an algorithm that

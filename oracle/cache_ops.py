@@ -1,6 +1,6 @@
 """Cache write and block copy — oracle models on the pools' storage bits.
 
-* Write ([course] §2 primer: each request's KV grows one token at a time;
+* Write ([course] §2 primer: decoding adds one token's K/V per step;
   [course] §2 "The insight": blocks of 16 tokens' K and V in a pool; [note]
   最小模型: growing a request only needs one more block): token i's K and V
   rows go to physical block ``slot // bs``, in-block row ``slot % bs``; a

@@ -461,10 +461,11 @@ def prepare_decode(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, 
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
-    with torch.cuda.device(q.device):
-        need = decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:  # (a given workspace is sized by the library's own check)
+        with torch.cuda.device(q.device):
+            need = decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, partition_size)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     desc = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
@@ -498,10 +499,11 @@ def prepare_decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tens
         out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
     if slot_mapping.dtype != torch.int64:
         raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, "slot_mapping must be int64")
-    with torch.cuda.device(q.device):
-        need = decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, BALANCED)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:  # (a given workspace is sized by the library's own check)
+        with torch.cuda.device(q.device):
+            need = decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, BALANCED)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     desc = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (ctypes.byref(desc), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _code(k_new),
@@ -536,10 +538,11 @@ def prepare_decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.T
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
-    with torch.cuda.device(q.device):
-        need = decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:  # (a given workspace is sized by the library's own check)
+        with torch.cuda.device(q.device):
+            need = decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, partition_size)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     for name, t in (("group_offsets", group_offsets), ("group_members", group_members), ("shared_len", shared_len)):
         if t.dtype != torch.int32:
             raise InvalidArgument(_lib.PA_ERR_INVALID_ARGUMENT, f"{name} must be int32")

@@ -4,9 +4,9 @@
 // [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
 // [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
 //
-// [course] §2 "The insight": blocks are allocated on demand and freed as
-// soon as a sequence finishes; the per-sequence table maps logical positions
-// to physical blocks. [note] block-size section: ceil(L / block_size) blocks
+// [course] §2 "The insight": a sequence gets a block only when it needs
+// one and returns its blocks when it is done; its table names the physical
+// block behind each logical block. [note] block-size section: ceil(L / block_size) blocks
 // per sequence. [course] §2 "The bonus" and [note] prefix sharing section:
 // forked sequences share blocks under refcounts; a block is copied only when
 // a branch writes into it. The choices the pages leave open (LIFO order,

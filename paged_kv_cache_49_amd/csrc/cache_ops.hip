@@ -4,7 +4,7 @@
 // [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
 // [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
 //
-// Write: [course] §2 primer (the KV cache grows one token at a time) and §2
+// Write: [course] §2 primer (each decode step adds one token's K/V) and §2
 // "The insight" (each block holds K[BLOCK][HEADS][HEAD_DIM] and V likewise):
 // token i's rows land in block slot/bs, row slot%bs.
 // Copy: [course] §2 "The bonus: block sharing (copy-on-write)" and [note]

@@ -3,8 +3,8 @@
 // [course] = "PagedAttention", Phase 7 · Document 04 · Production Serving;
 // [note] = "PagedAttention" LLM study note (lux-666-github-io.pages.dev).
 //
-// What every decode kernel computes ([course] §2 "The insight": the kernel
-// follows the block table to gather K/V during the dot product; [note]
+// What every decode kernel computes ([course] §2 "The insight": keys and
+// values are fetched through the block table as attention runs; [note]
 // 最小模型: blocks are visited in logical token order; [note] "why it works":
 // the result is ordinary attention): for the G query heads h of KV head g
 // and the tokens t of one piece of a sequence,

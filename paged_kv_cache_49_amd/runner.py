@@ -82,11 +82,42 @@ class PagedBatch:
         self._stage = [_Staging(batch, self.max_blocks, device) for _ in range(2)]
         self._turn = 0
         self._copy_stream = torch.cuda.Stream(device=device) if upload_stream else None
+        if self._copy_stream is not None:
+            self._warm_upload_path()
         self.last_cow_count = 0
         # host time of the block-manager work of the steps (alloc_batch,
         # pack, shared_prefixes), seconds, and the number of steps it covers
         self.host_seconds = 0.0
         self.host_steps = 0
+
+    def _warm_upload_path(self, rounds: int = 12) -> None:
+        """Queue ``rounds`` metadata uploads on the copy stream, each behind
+        compute-stream work that has not finished yet, and wait for all.
+
+        Measured on MI355X (ROCm 7.2): one of the first few pinned
+        host-to-device copies queued on a second stream behind unfinished
+        work of the compute stream blocks the calling thread for about 5 ms,
+        once per process, while the GPU idles (plain hipMemcpyAsync behaves
+        the same; copies queued without such a pending dependency do not
+        trigger it). Taking that cost here keeps it out of the decode
+        steps. The staging buffers' contents are overwritten by every
+        step."""
+        compute = torch.cuda.current_stream(self.device)
+        cs = self._copy_stream
+        busy = torch.empty(16 << 20, dtype=torch.int32, device=self.device)
+        ready = [torch.cuda.Event(), torch.cuda.Event()]
+        copied = [torch.cuda.Event(), torch.cuda.Event()]
+        for i in range(rounds):
+            st = self._stage[i % 2]
+            for _ in range(4):
+                busy.fill_(i)  # work the upload waits for, still running when it is queued
+            ready[i % 2].record(compute)
+            cs.wait_event(ready[i % 2])
+            with torch.cuda.stream(cs):
+                st.dev.copy_(st.host, non_blocking=True)
+            copied[i % 2].record(cs)
+            compute.wait_event(copied[i % 2])
+        torch.cuda.synchronize(self.device)
 
     # -- setup ---------------------------------------------------------------
     def prefill(self, seq_id: int, ks: Sequence[torch.Tensor], vs: Sequence[torch.Tensor]) -> np.ndarray:
@@ -117,24 +148,27 @@ class PagedBatch:
     def step(self, seq_ids: np.ndarray, k_new: Sequence[torch.Tensor], v_new: Sequence[torch.Tensor],
              q: Sequence[torch.Tensor], outs: Sequence[torch.Tensor], scale: float, partition_size: int,
              workspace: Optional[torch.Tensor] = None, ones: Optional[np.ndarray] = None,
-             decode_events: Optional[list] = None, event_layers: Optional[Sequence[int]] = None,
-             make_event=None, fused: bool = False, shared: bool = False) -> int:
+             timing: Optional["StepTiming"] = None, fused: bool = False, shared: bool = False) -> int:
         """Append one token to each of ``seq_ids`` in every layer and run
         decode attention for it. Returns the batch's max context length.
-        With ``decode_events`` (a list), a (start, end) pair of HIP events
-        recorded around the pa_decode call of each layer in
-        ``event_layers`` (default: every layer) is appended to it; the events
-        come from ``make_event()`` (default: torch timing events), which must
-        return objects with ``record()`` on the current stream.
+        With ``timing`` (a StepTiming, its events created beforehand), the
+        step records host timestamps of its phases and device events at its
+        start and end on the compute stream and around the decode call of
+        each layer the StepTiming names.
 
         ``shared=True``: the rows whose tables start with the same blocks
         (forks of one prompt) are grouped (pa_bm_shared_prefixes, granule =
         ``partition_size``) and decoded with pa_decode_shared, which reads
         each group's shared partitions once."""
+        tm = timing
+        if tm is not None:
+            tm.host["enter"] = time.perf_counter()
         st = self._stage[self._turn]
         self._turn ^= 1
         if st.copied is not None:
             st.copied.synchronize()  # the pinned buffer's previous upload is done
+        if tm is not None:
+            tm.host["staging_free"] = time.perf_counter()
         B = len(seq_ids)
         if ones is None:
             ones = np.ones(B, np.int32)
@@ -149,8 +183,11 @@ class PagedBatch:
                 raise ValueError("shared steps need partition_size > 0 and fused=False")
             groups = self.bm.shared_prefixes(seq_ids, partition_size, group_offsets=st.goff_np,
                                              group_members=st.gmem_np, shared_len=st.shl_np)
-        self.host_seconds += time.perf_counter() - t_host
+        t_bm = time.perf_counter()
+        self.host_seconds += t_bm - t_host
         self.host_steps += 1
+        if tm is not None:
+            tm.host["block_manager"] = t_bm
         compute = torch.cuda.current_stream(self.device)
         if st.copied is None:
             st.copied, st.consumed = torch.cuda.Event(), torch.cuda.Event()
@@ -164,6 +201,9 @@ class PagedBatch:
                 st.dev.copy_(st.host, non_blocking=True)
             st.copied.record(cs)
             compute.wait_event(st.copied)
+        if tm is not None:
+            tm.host["upload"] = time.perf_counter()
+            tm.start.record()  # on the compute stream, after the wait for the upload
         self.last_cow_count = ncow
         tables = st.tables if B == st.B else st.tables[:B]
         lens = st.lens[:B]
@@ -172,10 +212,7 @@ class PagedBatch:
                 copy_blocks(c, st.cow[:ncow])
             if not fused:
                 reshape_and_cache(c, k_new[i], v_new[i], st.slots[:B])
-            timed = decode_events is not None and (event_layers is None or i in event_layers)
-            if timed:
-                mk = make_event or (lambda: torch.cuda.Event(enable_timing=True))
-                ev = (mk(), mk())
+            ev = tm.calls.get(i) if tm is not None else None
             # arguments marshalled before the start event, so the timed
             # interval holds the launch alone (no host work)
             if fused:
@@ -191,14 +228,32 @@ class PagedBatch:
             else:
                 launch = prepare_decode(c, q[i], tables, lens, max_ctx, scale, partition_size, out=outs[i],
                                         workspace=workspace)
-            if timed:
+            if ev is not None:
                 ev[0].record()
             launch()
-            if timed:
+            if ev is not None:
                 ev[1].record()
-                decode_events.append(ev)
         st.consumed.record(compute)
+        if tm is not None:
+            tm.end.record()
+            tm.host["launched"] = time.perf_counter()
         return max_ctx
+
+
+class StepTiming:
+    """Timing of one PagedBatch.step, its events created up front (so that
+    creating them costs nothing inside a timed region): ``start`` / ``end``
+    recorded on the compute stream at the step's start (after its wait for
+    the metadata upload) and end, ``calls[layer]`` = (start, end) around
+    that layer's decode launch, and ``host`` = perf_counter() stamps of the
+    step's phases (enter, staging_free, block_manager, upload, launched).
+    ``make_event()`` returns an object with ``record()`` (on the current
+    stream) and ``elapsed_time(other)`` in milliseconds."""
+
+    def __init__(self, make_event, call_layers: Sequence[int] = (0,)):
+        self.start, self.end = make_event(), make_event()
+        self.calls = {int(i): (make_event(), make_event()) for i in call_layers}
+        self.host: dict = {}
 
 
 def workspace_for(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
