@@ -24,8 +24,11 @@ Modules:
   allocator  — the block manager: free stack, refcounts, on-demand growth,
                fork, copy-on-write, release
 
-Parity pins: every function here is checked in ``tests/test_oracle_*.py``
-against brute force, closed forms, the pages' worked examples and
-invariants; none is "parity unpinned".
+Parity pins: every function, and every storage-format branch of the
+attention decoder (f16, bf16, fp8), is checked in ``tests/test_oracle_*.py``
+against something other than the oracle itself: torch's
+scaled_dot_product_attention and float8 cast, closed forms, values worked
+out by hand, the pages' worked examples and invariants; planted mistakes
+(``test_planted_mistake_is_caught``) show the pins reject plausible bugs.
 """
 from . import allocator, attention, cache_ops, fp8  # noqa: F401

@@ -41,12 +41,15 @@ def _sdpa_all(wl):
 
 
 def _random_cases():
+    """Random tiny cases over block sizes and group sizes, each with an f16
+    and a bf16 pool (the two 16-bit storage formats decode differently)."""
     cases = []
     rng = np.random.default_rng(7)
     for i, (bs, g, hkv, d) in enumerate([(1, 1, 2, 16), (2, 2, 2, 8), (4, 4, 2, 16), (16, 4, 1, 32),
                                          (16, 1, 3, 8), (4, 2, 2, 24), (8, 8, 1, 16)]):
         lengths = rng.integers(1, 41, size=3)
-        cases.append(synth.random_case(100 + i, lengths, g * hkv, hkv, d, bs, "f16"))
+        for dt in ("f16", "bf16"):
+            cases.append(synth.random_case(100 + i, lengths, g * hkv, hkv, d, bs, dt))
     return cases
 
 
@@ -57,7 +60,7 @@ def test_tiny_workload_matches_sdpa():
     assert np.abs(got - ref).max() <= 1e-12
 
 
-@pytest.mark.parametrize("wl", _random_cases(), ids=lambda w: f"{w.name}-bs{w.block_size}-g{w.group}")
+@pytest.mark.parametrize("wl", _random_cases(), ids=lambda w: f"{w.name}-{w.kv_dtype}-bs{w.block_size}-g{w.group}")
 def test_random_cases_match_sdpa(wl):
     got = H.oracle_paged(wl)
     ref = _sdpa_all(wl)
@@ -71,6 +74,29 @@ def test_fp8_cache_matches_sdpa_on_dequantised_values():
     got = H.oracle_paged(wl)
     ref = _sdpa_all(wl)
     assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_bf16_pool_bits_decode_by_hand():
+    """bf16 storage is the top half of an IEEE binary32: sign, 8 exponent
+    bits (bias 127), 7 fraction bits. Values worked out by hand."""
+    bits = np.array([0x3F80, 0xC000, 0x3FC0, 0x0001, 0x0080, 0x7F7F, 0x8000, 0x4049, 0x3E00], np.uint16)
+    want = np.array([1.0, -2.0, 1.5,
+                     2.0 ** -133,                      # smallest subnormal: 2^-126 * 2^-7
+                     2.0 ** -126,                      # smallest normal
+                     (2.0 - 2.0 ** -7) * 2.0 ** 127,   # largest finite
+                     -0.0, 3.140625,                   # 1.5703125 * 2
+                     0.125])
+    got = oatt.pool_values(bits, "bf16")
+    assert np.array_equal(got, want)
+    assert np.signbit(got[6])
+
+
+def test_bf16_pool_matches_sdpa_on_the_source_values():
+    """A bf16 pool written through the slot model and decoded by the oracle
+    gives SDPA's result on the source tensors' own values (torch's bf16 ->
+    fp64 conversion, a route that does not use the oracle's decoder)."""
+    wl = synth.random_case(12, [1, 16, 17, 40], 8, 2, 32, 16, "bf16")
+    assert np.abs(H.oracle_paged(wl) - _sdpa_all(wl)).max() <= 1e-12
 
 
 def test_single_token_returns_its_value_exactly():
@@ -239,6 +265,12 @@ def _mut_decode_head_mod(q, k_seq, v_seq, scale, num_kv_heads):
     return out
 
 
+def _mut_pool_values_bf16_shift(pool_bits, kv_dtype, scale=1.0):
+    if kv_dtype == "bf16":
+        return (pool_bits.astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+    return oatt.__dict__["_orig_pool_values"](pool_bits, kv_dtype, scale)
+
+
 MUTANTS = {
     "gather-block-offset-swapped": ("gather_sequence", _mut_gather_swapped),
     "gather-drops-last-token": ("gather_sequence", _mut_gather_short),
@@ -247,15 +279,20 @@ MUTANTS = {
     "softmax-unnormalised": ("attend", _mut_attend_unnormalised),
     "softmax-wrong-axis": ("attend", _mut_attend_wrong_axis),
     "head-group-modulo": ("decode_contiguous", _mut_decode_head_mod),
+    "bf16-decode-shift": ("pool_values", _mut_pool_values_bf16_shift),
 }
 
 
+@pytest.mark.parametrize("kv_dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_planted_mistake_is_caught(name, monkeypatch):
+def test_planted_mistake_is_caught(name, kv_dtype, monkeypatch):
     attr, fn = MUTANTS[name]
+    if name.startswith("bf16") and kv_dtype != "bf16":
+        pytest.skip("a bf16-only mistake")
     monkeypatch.setitem(oatt.__dict__, "_orig_gather", oatt.gather_sequence)
     monkeypatch.setitem(oatt.__dict__, "_orig_attend", oatt.attend)
-    wl = synth.random_case(31, [19, 40, 6], 8, 2, 16, 4, "f16")
+    monkeypatch.setitem(oatt.__dict__, "_orig_pool_values", oatt.pool_values)
+    wl = synth.random_case(31, [19, 40, 6], 8, 2, 16, 4, kv_dtype)
     ref = _sdpa_all(wl)
     monkeypatch.setattr(oatt, attr, fn)
     got = H.oracle_paged(wl)
