@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -460,6 +460,31 @@ pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, con
                     const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
                     int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, result and errors as pa_decode, without the workspace:
+ * the partial results of a split go to a scratch array the library holds on
+ * every GPU it runs on (64 MiB each, kept until the process ends; its
+ * address is looked up once per device, on the first call there). Nothing
+ * is allocated: no hipMalloc / hipFree, no library allocation.
+ *
+ * Limits: PA_PARTITION_BALANCED sizes its partial results for the
+ * workgroups it launches (far below 64 MiB for every supported shape on
+ * MI355X); a partitioned call (partition_size >= 0) whose
+ * pa_decode_workspace_size exceeds 64 MiB returns PA_ERR_INVALID_ARGUMENT
+ * before any launch. No scratch content carries over between calls: every
+ * location a call reads it wrote itself earlier in the same call.
+ *
+ * Calls that overlap on one GPU (two streams, or two host threads without
+ * ordering between their streams) share that GPU's scratch and race: order
+ * them on one stream. PA_ERR_DEVICE if the scratch address cannot be read.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode_noalloc(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
+                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                            int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
+                            void* stream);
 
 /* ------------------------------------------------------------------------
  * One decode step's cache write and attention in a single launch: the

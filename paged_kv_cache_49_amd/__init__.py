@@ -485,6 +485,22 @@ def decode(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_
                           out_dtype=out_dtype, workspace=workspace, stream=stream)()
 
 
+def decode_noalloc(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                   max_context_len: int, scale: float, partition_size: int = 0, out: Optional[torch.Tensor] = None,
+                   out_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
+    """pa_decode_noalloc: decode with the library's static per-GPU scratch
+    instead of a workspace (the library allocates nothing). Calls that
+    overlap on one GPU race on that scratch. Returns ``out``."""
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    desc = cache.desc()
+    args = (ctypes.byref(desc), _dev(out, "out"), _code(out), _dev(q, "q"), _code(q),
+            _dev(block_tables, "block_tables"), int(block_tables.shape[1]), _dev(context_lens, "context_lens"),
+            int(B), int(Hq), int(max_context_len), float(scale), int(partition_size), _stream(stream))
+    return _deferred(lib().pa_decode_noalloc, args, q.device, out, (desc, cache, q, block_tables, context_lens))()
+
+
 def prepare_decode_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
                           q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                           max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,

@@ -13,9 +13,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "decode_common.h"
@@ -282,11 +284,9 @@ struct SkLayout {
 };
 
 // workspace of the balanced split: merge descriptors [head groups][B][2],
-// then per piece row (workgroup, slot, query head of the group) m, l, o[D]
-SkLayout sk_layout(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int cus) {
-  const int64_t G = Hq / hkv;
-  // W * HW <= cus * kSkWavesPerCu, and a workgroup holds 2 * HW * G rows
-  const size_t rows = static_cast<size_t>(cus) * kSkWavesPerCu * 2 * G;
+// then per piece row (workgroup, slot, query head of the group) m, l, o[D],
+// for `rows` piece rows
+SkLayout sk_layout_rows(int64_t B, int64_t hkv, int64_t D, size_t rows) {
   SkLayout L{};
   L.desc = 0;
   L.m = align_up(static_cast<size_t>(B) * hkv * 2 * sizeof(int32_t));
@@ -294,6 +294,13 @@ SkLayout sk_layout(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int cus) {
   L.o = L.l + align_up(rows * sizeof(float));
   L.total = L.o + align_up(rows * D * sizeof(float));
   return L;
+}
+
+// the layout pa_decode_workspace_size promises: W * HW <= cus *
+// kSkWavesPerCu, and a workgroup holds 2 * HW * G rows
+SkLayout sk_layout(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int cus) {
+  const int64_t G = Hq / hkv;
+  return sk_layout_rows(B, hkv, D, static_cast<size_t>(cus) * kSkWavesPerCu * 2 * G);
 }
 
 }  // namespace
@@ -311,7 +318,7 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
                           int32_t num_q_heads, int32_t max_context_len, float qk_scale_log2, float v_scale,
                           void* workspace, size_t workspace_bytes, hipStream_t stream, int32_t partition_size = -1,
                           int64_t num_parts = 0, const void* k_new = nullptr, const void* v_new = nullptr,
-                          const int64_t* slot_mapping = nullptr) {
+                          const int64_t* slot_mapping = nullptr, bool fit_workspace = false) {
   const bool part_mode = partition_size >= 0;
   const int32_t hkv = cache->num_kv_heads;
   const int32_t D = cache->head_dim;
@@ -364,6 +371,9 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
     }
   }
   SkLayout lay{};
+  // grid bound of the balanced split (the launch takes at most the resident
+  // workgroups, fewer if max_wgs is lower)
+  int max_wgs = cus * kSkWavesPerCu / HW;
   if (part_mode) {
     // [m][l][o] per (sequence, query head, partition) = per piece row of
     // workgroup ((hg * B + s) * P + part), then the descriptors (the caller
@@ -375,6 +385,22 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
     lay.desc = lay.o + align_up(rows * D * sizeof(float));
   } else {
     lay = sk_layout(B, num_q_heads, hkv, D, cus);
+    if (fit_workspace && workspace != nullptr && workspace_bytes < lay.total) {
+      // a fixed buffer (pa_decode_noalloc): size the pieces for as many
+      // workgroups as it holds, which bounds the grid; the launch takes
+      // fewer only when that is below the resident workgroups
+      const size_t per_wg = static_cast<size_t>(2) * HW * G;  // piece rows of a workgroup
+      const size_t fixed = align_up(static_cast<size_t>(B) * hkv * 2 * sizeof(int32_t)) + 3 * kAlign;
+      const size_t wg_bytes = per_wg * (2 + static_cast<size_t>(D)) * sizeof(float);
+      int64_t fit = workspace_bytes > fixed ? static_cast<int64_t>((workspace_bytes - fixed) / wg_bytes) : 0;
+      fit = std::min<int64_t>(fit, max_wgs);
+      while (fit > 0 && sk_layout_rows(B, hkv, D, static_cast<size_t>(fit) * per_wg).total > workspace_bytes) --fit;
+      if (fit <= 0)
+        return fail(PA_ERR_INVALID_ARGUMENT, "the balanced split of B = %d needs more than %zu bytes of scratch", B,
+                    workspace_bytes);
+      max_wgs = static_cast<int>(fit);
+      lay = sk_layout_rows(B, hkv, D, static_cast<size_t>(fit) * per_wg);
+    }
     if (workspace == nullptr || workspace_bytes < lay.total)
       return fail(PA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed (got %zu)", lay.total,
                   workspace == nullptr ? (size_t)0 : workspace_bytes);
@@ -420,7 +446,6 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   p.k_new = k_new;
   p.v_new = v_new;
   p.slot_mapping = slot_mapping;
-  int max_wgs = cus * kSkWavesPerCu / HW;
   if (part_mode) {
     const int64_t grid = num_parts * B * n_hg;
     if (grid > 0x7fffffffLL) return fail(PA_ERR_INVALID_ARGUMENT, "too many workgroups (%lld)", (long long)grid);
@@ -508,13 +533,50 @@ struct SharedArgs {
   int32_t num_groups, max_group_size, max_shared_len, min_shared_len;
 };
 
+// ---- the scratch of pa_decode_noalloc: device memory the library owns,
+// kScratchBytes on every GPU whose code object is loaded (held until the
+// process ends). Host code never passes the array's name to a kernel or a
+// copy: it is a host-side stand-in, not the device address. Each device's
+// address comes from hipGetSymbolAddress with that device current, once,
+// and is kept per device.
+constexpr size_t kScratchBytes = 64ull << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+pa_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_DEVICE, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(PA_ERR_DEVICE, "device %d: hipGetSymbolAddress(scratch): %s", dev, hipGetErrorString(e));
+      if (reinterpret_cast<uintptr_t>(p) % kAlign != 0)
+        return fail(PA_ERR_DEVICE, "device %d: the scratch is not %zu-byte aligned", dev, kAlign);
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PA_OK;
+}
+
 // pa_decode; pa_decode_append when k_new != nullptr and pa_decode_shared
-// when sh != nullptr (their own arguments are validated by them)
+// when sh != nullptr (their own arguments are validated by them).
+// fit_workspace (pa_decode_noalloc): the balanced split sizes its pieces for
+// the workgroups the given buffer holds instead of requiring the bound
+// pa_decode_workspace_size promises.
 pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
                       const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
                       int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
                       void* workspace, size_t workspace_bytes, void* stream, const void* k_new, const void* v_new,
-                      const int64_t* slot_mapping, const SharedArgs* sh = nullptr) {
+                      const int64_t* slot_mapping, const SharedArgs* sh = nullptr, bool fit_workspace = false) {
   pa_status st = pa::validate_cache(cache);
   if (st != PA_OK) return st;
   if (B < 0) return fail(PA_ERR_INVALID_ARGUMENT, "B = %d is negative", B);
@@ -612,7 +674,7 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
   if (balanced)
     return pa::decode_balanced(cache, out, out_c, q, block_tables, max_blocks, context_lens, B, num_q_heads,
                                max_context_len, qk_scale_log2, v_scale, workspace, workspace_bytes, s, -1, 0, k_new,
-                               v_new, slot_mapping);
+                               v_new, slot_mapping, fit_workspace);
   // Partitions with token-major V (16-bit pools) or fp8 pools (either V
   // layout; partition_size a multiple of their 32-token units, or one
   // partition) can run on the
@@ -754,6 +816,31 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const vo
   return pa::decode_impl(cache, out, out_dtype, q, q_dtype, block_tables, max_blocks, context_lens, B, num_q_heads,
                          max_context_len, scale, PA_PARTITION_BALANCED, workspace, workspace_bytes, stream, k_new,
                          v_new, slot_mapping);
+}
+
+pa_status pa_decode_noalloc(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
+                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                            int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
+                            void* stream) {
+  pa::clear_error();
+  pa_status st = pa::validate_cache(cache);
+  if (st != PA_OK) return st;
+  if (B <= 0) return B < 0 ? fail(PA_ERR_INVALID_ARGUMENT, "B = %d is negative", B) : PA_OK;
+  if (partition_size != PA_PARTITION_BALANCED && num_q_heads > 0 && max_context_len >= 0 && partition_size >= 0) {
+    const size_t need = pa::workspace_bytes_for(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                                pa::partitions_for(max_context_len, partition_size));
+    if (need > pa::kScratchBytes)
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "pa_decode_noalloc: this partitioned call needs %zu bytes of scratch; the library's static scratch "
+                  "holds %zu (use pa_decode with a workspace, or a larger partition_size)",
+                  need, pa::kScratchBytes);
+  }
+  void* ws = nullptr;
+  st = pa::scratch_of_current_device(&ws);
+  if (st != PA_OK) return st;
+  return pa::decode_impl(cache, out, out_dtype, q, q_dtype, block_tables, max_blocks, context_lens, B, num_q_heads,
+                         max_context_len, scale, partition_size, ws, pa::kScratchBytes, stream, nullptr, nullptr,
+                         nullptr, nullptr, /*fit_workspace=*/true);
 }
 
 pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
