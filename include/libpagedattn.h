@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -102,7 +102,12 @@ int32_t pa_abi_version(void);
  * ---------------------------------------------------------------------- */
 typedef struct pa_bm pa_bm;
 
-typedef struct pa_bm_stats {
+/* Counters of a manager ([note] section "prefix sharing 的边界": production
+ * monitoring should track how many blocks are shared and how many
+ * copy-on-write copies happen; [course] §4: pool occupancy is the capacity
+ * signal). num_seqs (live sequences) is one field more than the counters
+ * those passages name; `reserved` keeps the 64-bit fields aligned. */
+typedef struct pa_bm_stats_s {
   int32_t num_blocks; /* pool size */
   int32_t num_free;   /* blocks on the free stack */
   int32_t num_used;   /* blocks with refcount > 0 */
@@ -111,7 +116,7 @@ typedef struct pa_bm_stats {
   int32_t reserved;
   int64_t cow_copies; /* copy-on-write pairs reported so far */
   int64_t forks;      /* successful pa_fork calls */
-} pa_bm_stats;
+} pa_bm_stats_t;
 
 /* Create a manager for a pool of num_blocks blocks of block_size tokens.
  * initial_free_order: host int32[num_blocks], a permutation of
@@ -275,7 +280,9 @@ pa_status pa_bm_shared_prefixes(const pa_bm* bm, const int64_t* seq_ids, int32_t
                                 int32_t* group_offsets, int32_t* group_members, int32_t* shared_len,
                                 int32_t* num_groups, int32_t* max_group_size, int32_t* max_shared_len);
 
-pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out);
+/* The manager's counters (pa_bm_stats_t above) into *out (host).
+ * Errors: PA_ERR_INVALID_ARGUMENT (NULL bm or out). */
+pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out);
 
 /* KV memory use of the resident sequences, and the two baselines the pages
  * compare ([course] §2 primer and "The insight": a contiguous max-context
@@ -452,7 +459,11 @@ pa_status pa_copy_blocks_between(const pa_kv_cache* dst, const pa_kv_cache* src,
 
 /* Workspace bytes pa_decode needs for these sizes and partition_size (0
  * when no workspace is needed or the sizes are invalid). For
- * PA_PARTITION_BALANCED it reads the current device's CU count. */
+ * PA_PARTITION_BALANCED it reads the current device's CU count.
+ * num_kv_heads is needed because the sizes depend on the grouping: the
+ * balanced split keeps G = num_q_heads / num_kv_heads rows per wave and
+ * per piece, and both splits keep num_kv_heads x B merge descriptors; a
+ * size taken without it would have to assume G = num_q_heads. */
 size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size);
 

@@ -314,7 +314,7 @@ class BlockManager:
 
     def stats(self) -> dict:
         s = PaBmStats()
-        _check(lib().pa_bm_stats_get(self._h, ctypes.byref(s)))
+        _check(lib().pa_bm_stats(self._h, ctypes.byref(s)))
         return {f: getattr(s, f) for f, _ in PaBmStats._fields_ if f != "reserved"}
 
     def refcounts(self) -> list:

@@ -30,7 +30,7 @@ PA_LAYOUT_TOKEN_MAJOR = 0
 PA_LAYOUT_DIM_MAJOR = 1
 
 PA_PARTITION_BALANCED = -1
-PA_ABI_VERSION = 3
+PA_ABI_VERSION = 4
 
 
 class PaKvCache(ctypes.Structure):
@@ -94,7 +94,7 @@ SIGNATURES = {
     "pa_seq_info": (c_int, [_P, c_int64, _I32P, _I32P]),
     "pa_seq_blocks": (c_int, [_P, c_int64, _P, c_int32, _I32P]),
     "pa_pack_block_tables": (c_int, [_P, _P, c_int32, c_int32, c_int32, _P, _P]),
-    "pa_bm_stats_get": (c_int, [_P, POINTER(PaBmStats)]),
+    "pa_bm_stats": (c_int, [_P, POINTER(PaBmStats)]),
     "pa_bm_refcounts": (c_int, [_P, _P]),
     "pa_bm_free_stack": (c_int, [_P, _P, c_int32, _I32P]),
     "pa_bm_set_host_pool": (c_int, [_P, c_int32]),

@@ -686,10 +686,10 @@ pa_status pa_bm_usage_get(const pa_bm* bm, int32_t max_context_len, pa_bm_usage*
   PA_GUARD_END
 }
 
-pa_status pa_bm_stats_get(const pa_bm* bm, pa_bm_stats* out) {
+pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out) {
   pa::clear_error();
   if (bm == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "bm or out is NULL");
-  pa_bm_stats s{};
+  pa_bm_stats_t s{};
   s.num_blocks = bm->num_blocks;
   s.num_free = static_cast<int32_t>(bm->free_stack.size());
   for (int32_t r : bm->refcnt) {

@@ -25,6 +25,27 @@ def _declared_functions():
     return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(pa_\w+)\s*\(", text, flags=re.M)))
 
 
+# The calls the boundary names for the method: block manager, cache write,
+# block copy, decode, workspace size, status strings.
+BOUNDARY = ["pa_status_string", "pa_last_error", "pa_bm_create", "pa_bm_destroy", "pa_alloc", "pa_free", "pa_fork",
+            "pa_seq_info", "pa_pack_block_tables", "pa_bm_stats", "pa_reshape_and_cache", "pa_copy_blocks",
+            "pa_decode_workspace_size", "pa_decode"]
+
+
+def test_boundary_names_are_declared_and_exported():
+    names = set(_declared_functions())
+    handle = ctypes.CDLL(_lib.LIB_PATH)
+    for n in BOUNDARY:
+        assert n in names, f"{n} is not declared in libpagedattn.h"
+        assert hasattr(handle, n), f"{n} is not exported"
+    text = open(HEADER).read()
+    assert re.search(r"\}\s*pa_bm_stats_t;", text), "the stats struct is pa_bm_stats_t"
+    assert re.search(r"pa_status pa_bm_stats\(const pa_bm\* bm, pa_bm_stats_t\* out\);", text)
+    # the one signature change: the workspace size takes num_kv_heads too
+    assert re.search(r"size_t pa_decode_workspace_size\(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, "
+                     r"int32_t head_dim,\s*int32_t max_context_len, int32_t partition_size\);", text)
+
+
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert len(names) >= 19
