@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -56,6 +56,9 @@ typedef enum pa_status {
   PA_ERR_SEQ_EXISTS = 4,       /* fork target already live */
   PA_ERR_UNSUPPORTED = 5,      /* dtype / head_dim / block_size / group combination not built */
   PA_ERR_DEVICE = 6,           /* a HIP call failed (launch error, bad stream) */
+  PA_ERR_OUT_OF_HOST_MEMORY = 7, /* a host allocation of the block manager failed: pa_alloc and
+                                    pa_alloc_batch changed nothing; after another call the manager
+                                    may be partly updated and should be destroyed */
 } pa_status;
 
 typedef enum pa_dtype {

@@ -59,6 +59,10 @@ class DeviceError(PagedAttnError):
     pass
 
 
+class OutOfHostMemory(PagedAttnError):
+    pass
+
+
 _ERRORS = {
     _lib.PA_ERR_INVALID_ARGUMENT: InvalidArgument,
     _lib.PA_ERR_OUT_OF_BLOCKS: OutOfBlocks,
@@ -66,6 +70,7 @@ _ERRORS = {
     _lib.PA_ERR_SEQ_EXISTS: SeqExists,
     _lib.PA_ERR_UNSUPPORTED: Unsupported,
     _lib.PA_ERR_DEVICE: DeviceError,
+    _lib.PA_ERR_OUT_OF_HOST_MEMORY: OutOfHostMemory,
 }
 
 

@@ -4,6 +4,14 @@ Every translation unit under csrc/ is compiled to an object file in
 parallel (HIP sources for the device and the host, plain C++ sources for the
 host only) and linked into ``paged_kv_cache_49_amd/libpagedattn.so``.
 Usage: ``python -m paged_kv_cache_49_amd.build`` (or build() from Python).
+
+``--sanitize`` instead builds the host-only parts (the block manager and
+the status code, plain C++) with g++ under AddressSanitizer +
+UndefinedBehaviorSanitizer and under ThreadSanitizer, as
+``_build/sanitize/libpagedattn_host_{asan,tsan}.so``. They export the
+block-manager half of the C ABI; load one with ``PA_LIBRARY=<path>`` and the
+matching runtime preloaded (``LD_PRELOAD=$(gcc -print-file-name=libasan.so)``).
+No device code is built with a sanitizer.
 """
 from __future__ import annotations
 
@@ -70,6 +78,38 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+# host-only sources (no HIP), and the flags of each sanitizer build
+HOST_SOURCES = ["block_manager.cpp", "status.cpp"]
+SANITIZE = {
+    "asan": ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"],
+    "tsan": ["-fsanitize=thread"],
+}
+
+
+def sanitize_flags(kind: str) -> list:
+    """g++ flags of a sanitizer build of host code (``asan``: ASan + UBSan)."""
+    return ["-std=c++17", "-O1", "-g", "-pthread", f"-I{INCLUDE}", f"-I{CSRC}", *SANITIZE[kind]]
+
+
+def build_sanitized(kind: str, verbose: bool = False) -> str:
+    """The host-only library (block manager + status) built with g++ under
+    ``kind`` (``asan`` or ``tsan``); returns its path."""
+    out_dir = os.path.join(BUILD, "sanitize")
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, f"libpagedattn_host_{kind}.so")
+    cmd = ["g++", *sanitize_flags(kind), "-shared", "-fPIC", *[os.path.join(CSRC, f) for f in HOST_SOURCES],
+           "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized host build ({kind}) failed:\n{r.stdout}{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
-    path = build(verbose="-v" in sys.argv)
-    print(path)
+    if "--sanitize" in sys.argv:
+        for k in SANITIZE:
+            print(build_sanitized(k, verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -124,7 +124,7 @@ using pa::fail;
 #define PA_GUARD_END                                                        \
   }                                                                         \
   catch (const std::bad_alloc&) {                                           \
-    return fail(PA_ERR_INVALID_ARGUMENT, "host memory allocation failed");  \
+    return fail(PA_ERR_OUT_OF_HOST_MEMORY, "host memory allocation failed"); \
   }
 
 pa_status plan_and_apply(pa_bm* bm, const int64_t* ids, int32_t n, const int32_t* ntok, int64_t* slots,
@@ -134,6 +134,10 @@ pa_status plan_and_apply(pa_bm* bm, const int64_t* ids, int32_t n, const int32_t
   std::unordered_set<int64_t> seen;
   seen.reserve(static_cast<size_t>(n) * 2);
   std::unordered_map<int32_t, int32_t> pending;  // shared tail -> copies already planned from it
+  // every host allocation of the request happens in this phase, before any
+  // state changes: entries of new sequences (moved into the table below
+  // without allocating) and room for each table's growth
+  std::unordered_map<int64_t, pa_bm::Seq> fresh;
   int64_t need = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (ntok[i] < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_new_tokens[%d] = %d is negative", i, ntok[i]);
@@ -146,6 +150,10 @@ pa_status plan_and_apply(pa_bm* bm, const int64_t* ids, int32_t n, const int32_t
     if (len + ntok[i] > INT32_MAX)
       return fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld would exceed INT32_MAX tokens", (long long)ids[i]);
     need += bm->blocks_for(len + ntok[i]) - bm->blocks_for(len);
+    if (it == bm->seqs.end())
+      fresh[ids[i]].blocks.reserve(static_cast<size_t>(bm->blocks_for(ntok[i])));
+    else
+      it->second.blocks.reserve(static_cast<size_t>(bm->blocks_for(len + ntok[i])));
     if (ntok[i] > 0 && len % bs != 0) {
       const int32_t tail = it->second.blocks.back();
       int32_t& already = pending[tail];
@@ -158,12 +166,15 @@ pa_status plan_and_apply(pa_bm* bm, const int64_t* ids, int32_t n, const int32_t
   if (need > bm->available())
     return fail(PA_ERR_OUT_OF_BLOCKS, "request needs %lld blocks, %lld free of %d", (long long)need,
                 (long long)bm->available(), bm->num_blocks);
+  bm->seqs.reserve(bm->seqs.size() + fresh.size());  // no rehash while applying
 
-  // ---- apply: cannot fail from here on (capacity reserved up front)
+  // ---- apply: cannot fail from here on (blocks and host memory reserved above)
   int32_t ncow = 0;
   int64_t out = 0;
   for (int32_t i = 0; i < n; ++i) {
-    pa_bm::Seq& s = bm->seqs[ids[i]];
+    auto found = bm->seqs.find(ids[i]);
+    if (found == bm->seqs.end()) found = bm->seqs.insert(fresh.extract(ids[i])).position;
+    pa_bm::Seq& s = found->second;
     const int32_t add = ntok[i];
     if (add > 0 && s.len % bs != 0 && bm->refcnt[s.blocks.back()] > 1) {
       const int32_t old = s.blocks.back();

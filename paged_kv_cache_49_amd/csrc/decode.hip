@@ -248,15 +248,17 @@ constexpr size_t kSkMaxLdsStage = 160 * 1024;
 // LDS the current device allows one workgroup (cached per device; 0 if it
 // cannot be read)
 size_t sk_device_lds() {
-  static int cache[64];
+  static DeviceIntCache cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return static_cast<size_t>(cache[dev]);
-  int n = 0, optin = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) == hipSuccess && optin > n) n = optin;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
-  return static_cast<size_t>(n);
+  const int n = cache.get(dev, [dev]() {
+    int v = 0, optin = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) == hipSuccess && optin > v)
+      v = optin;
+    return v;
+  });
+  return n > 0 ? static_cast<size_t>(n) : 0;
 }
 
 // KV heads per workgroup: the largest divisor of num_kv_heads up to 8 (a
@@ -269,14 +271,14 @@ int sk_heads_per_wg(int hkv, bool staged) {
 
 // CUs of the current device (cached per device)
 int device_cus() {
-  static int cache[64];
+  static DeviceIntCache cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
-  return n;
+  const int n = cache.get(dev, [dev]() {
+    int v = 0;
+    return hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? v : 0;
+  });
+  return n > 0 ? n : 0;
 }
 
 struct SkLayout {
@@ -542,7 +544,6 @@ struct SharedArgs {
 constexpr size_t kScratchBytes = 64ull << 20;
 __device__ __align__(256) char scratch[kScratchBytes];
 
-constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_addr[kMaxDevices];
 std::mutex g_scratch_mu;
 

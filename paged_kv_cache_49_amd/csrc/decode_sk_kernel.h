@@ -64,6 +64,7 @@
 #pragma once
 
 #include "decode_vt_kernel.h"
+#include "host_cache.h"
 
 namespace pa {
 
@@ -911,27 +912,29 @@ template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV, int 
 hipError_t launch_decode_sk_n(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
   const int HW = p.heads_per_wg;
   const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes, TV, NBUF);
-  // more than 64 KiB of dynamic LDS (the stage) must be
-  // allowed per kernel; racing callers set the same attribute
-  static int lds_allowed = 64 * 1024;  // per instantiation
-  if (static_cast<int>(lds) > lds_allowed) {
-    const hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    lds_allowed = static_cast<int>(lds);
-  }
-  // occupancy per (HW, LDS in 4 KiB steps); racing writers store the same value
-  static int cache[9][41];  // per instantiation
+  const void* fn = reinterpret_cast<const void*>(paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  // more than 64 KiB of dynamic LDS (the stage) must be allowed per kernel
+  // and device; the grant only grows (host_cache.h)
+  static LdsGrant grant(64 * 1024);  // per instantiation
+  if (!grant.ensure(dev, static_cast<int>(lds), [&](int bytes) {
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        return e == hipSuccess;
+      }))
+    return e;
+  // occupancy per (HW, LDS in 4 KiB steps)
+  static IntTable<9, 41> occupancy;  // per instantiation
   const int lb = static_cast<int>((lds + 4095) / 4096);
-  int occ = (HW <= 8 && lb <= 40) ? cache[HW][lb] : 0;
-  if (occ <= 0) {
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &occ, paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>, 64 * HW, lds);
-    if (e != hipSuccess) return e;
-    if (occ <= 0) return hipErrorInvalidConfiguration;
-    if (HW <= 8 && lb <= 40) cache[HW][lb] = occ;
-  }
+  const int occ = occupancy.get(HW, lb, [&]() {
+    int n = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>,
+                                                     64 * HW, lds);
+    return e == hipSuccess ? n : 0;
+  });
+  if (e != hipSuccess) return e;
+  if (occ <= 0) return hipErrorInvalidConfiguration;
   // balanced: the resident workgroups, less those of one CU in 32 (one
   // per XCD on MI355X; measured: the GQA batch's call 1% faster, long and
   // mixed batches unchanged); partition mode: one per partition

@@ -22,12 +22,11 @@ pa_status fail(pa_status status, const char* fmt, ...) {
 
 void clear_error() { g_last_error[0] = '\0'; }
 
+// read at every call, so a process can switch it (the cost is one
+// environment lookup per device entry point)
 bool debug_enabled() {
-  static const bool on = [] {
-    const char* v = std::getenv("PA_DEBUG");
-    return v != nullptr && std::strcmp(v, "1") == 0;
-  }();
-  return on;
+  const char* v = std::getenv("PA_DEBUG");
+  return v != nullptr && std::strcmp(v, "1") == 0;
 }
 
 }  // namespace pa
@@ -43,6 +42,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_SEQ_EXISTS: return "PA_ERR_SEQ_EXISTS";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_DEVICE: return "PA_ERR_DEVICE";
+    case PA_ERR_OUT_OF_HOST_MEMORY: return "PA_ERR_OUT_OF_HOST_MEMORY";
   }
   return "PA_ERR_UNKNOWN_STATUS";
 }
