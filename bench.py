@@ -388,7 +388,10 @@ def bench_decode_calls(args):
     else:
         call = lambda c: pa.decode(c, q, tables, lens, max_ctx, wl.scale, ps, out=out, workspace=ws)
         kernel = ("pa_decode (paged_decode_sk_kernel + decode_sk_merge_kernel)" if ps < 0 else
-                  "pa_decode (partition kernel + decode_reduce_kernel)" if ps > 0 else "pa_decode (one partition)")
+                  f"pa_decode (partitions of {ps} tokens: the staged kernel in partition mode + "
+                  f"decode_sk_merge_kernel, or the one-wave partition kernel + decode_reduce_kernel; "
+                  f"PA_PARTITION_PATH={os.environ.get('PA_PARTITION_PATH', 'auto')})" if ps > 0
+                  else "pa_decode (one partition)")
     torch.cuda.synchronize()
     print(f"[bench] {args.workload}: B={B} tokens={int(L.sum())} layers={layers} KV {call_bytes / 1e6:.0f} MB/call",
           file=sys.stderr, flush=True)

@@ -3,8 +3,9 @@ times (token-major V, the page's block layout; balanced split), against the
 fp64 oracle.
 
 * GQA batch (64 seqs, L ~ U[512,4096], 32/8 heads): every output row.
-* long context (8 seqs, L ~ U[32768,131072]): every sequence, two KV heads
-  per sequence (the oracle runs one KV head at a time).
+* long context (8 seqs, L ~ U[32768,131072]): every KV head of every
+  sequence (the oracle runs one KV head at a time), on the balanced split
+  and on 512-token partitions through both partition paths.
 * prefix sharing (16 prompts x 8 samples): fork, copy-on-write on the
   shared partial tail, per-sample tails, one appended token, decode; the
   copy count and every output row are checked.
@@ -41,22 +42,47 @@ def test_gqa_batch_full(gpu, part):
     H.assert_close(got16, H.oracle_contiguous(wl), what="gqa bf16 out")
 
 
-def test_long_context_sampled_heads(gpu):
+@pytest.fixture(scope="module")
+def long_case(gpu):
+    """The long-context batch on the device, and the fp64 oracle's output
+    for every (sequence, query head), computed one KV head at a time."""
     wl = synth.long_context()
     say(f"long context: lengths {wl.lengths.tolist()}")
     _, cache, tables, lens, mx = device_setup(wl, v_layout=BENCH_V_LAYOUT)
-    got = run_decode(wl, cache, tables, lens, mx, BENCH_PARTITION)
     q = oatt.to_f64(wl.q())
+    G = wl.group
+    ref = np.zeros_like(q)
+    for s in range(wl.batch):
+        k, v = wl.kv(s)
+        for g in range(wl.num_kv_heads):
+            heads = slice(g * G, (g + 1) * G)
+            ref[s, heads] = oatt.attend(q[s, heads], oatt.to_f64(k[:, g]), oatt.to_f64(v[:, g]), wl.scale)
+        wl._kv_cache.pop(s, None)  # (host memory: one sequence's K/V at a time)
+    say("   oracle done")
+    return wl, cache, tables, lens, mx, ref
+
+
+@pytest.mark.parametrize("part,path", [(BENCH_PARTITION, None), (512, "staged"), (512, "wave")],
+                         ids=["balanced", "part512-staged", "part512-wave"])
+def test_long_context_every_head(long_case, monkeypatch, part, path):
+    """Every KV head of every sequence. With 512-token partitions a sequence
+    has up to 256 of them: the staged kernel's split merge then reads its
+    pieces in two rounds of 128, the one-wave kernels' reduce walks all."""
+    wl, cache, tables, lens, mx, ref = long_case
+    if path is not None:
+        monkeypatch.setenv("PA_PARTITION_PATH", path)
+    say(f"long context: partition {part} path {path}, max partitions {-(-int(wl.lengths.max()) // 512)}")
+    got = run_decode(wl, cache, tables, lens, mx, part)
+    assert np.isfinite(got).all()
     G = wl.group
     worst = 0.0
     for s in range(wl.batch):
-        k, v = wl.kv(s)
-        for g in (0, wl.num_kv_heads - 1):
+        for g in range(wl.num_kv_heads):
             heads = slice(g * G, (g + 1) * G)
-            ref = oatt.attend(q[s, heads], oatt.to_f64(k[:, g]), oatt.to_f64(v[:, g]), wl.scale)
-            ma, rl = H.assert_close(got[s, heads], ref, what=f"long seq {s} head {g}")
+            _, rl = H.assert_close(got[s, heads], ref[s, heads], what=f"long seq {s} KV head {g}")
             worst = max(worst, rl)
-    say(f"   worst rel-L2 {worst:.2e}")
+    ma, rl = H.assert_close(got, ref, what="long context, whole output")
+    say(f"   max-abs {ma:.2e} rel-L2 {rl:.2e}; worst (seq, head) rel-L2 {worst:.2e}")
 
 
 @pytest.mark.parametrize("partial_tail", [True, False], ids=["prefix-2048+r", "prefix-2048"])
