@@ -140,14 +140,16 @@ __host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D) { r
 //    further; measured to make no difference). V dim-major: the head group's [HW][D][BS] region of each
 //    of the unit's blocks, stored chunk-major ([HW][BS / 8][D][8 bytes]: an
 //    operand read of 16 head dims is then 128 contiguous bytes; 32 S bytes);
-//    token-major: the 32 rows widened to bf16 (pitch 2 S + 32, the
-//    transposing reads as for 16-bit pools).
+//    token-major: the 32 rows as loaded, laid out like K, read back with
+//    the 8-bit transposing read (ds_read_b64_tr_b8: a 16-lane group reads
+//    8 rows x 16 bytes, rows 4 banks apart) and widened to bf16 in
+//    registers.
 __host__ __device__ inline constexpr int sk_stage_kpitch(int S) { return S + 16; }
 __host__ __device__ inline constexpr int sk_stage_vpitch(int S) { return S + 32; }
 __host__ __device__ inline constexpr size_t sk_stage_bytes(int HW, int D, int kb, bool tv) {
   return kb == 2 ? 16 * static_cast<size_t>(sk_stage_kpitch(HW * D * 2) + sk_stage_vpitch(HW * D * 2))
                  : 32 * static_cast<size_t>(sk_stage_kpitch(HW * D)) + 64 +
-                       32 * static_cast<size_t>(tv ? sk_stage_vpitch(2 * HW * D) : HW * D);
+                       (tv ? 32 * static_cast<size_t>(sk_stage_kpitch(HW * D)) + 64 : 32 * static_cast<size_t>(HW * D));
 }
 
 // bytes of dynamic LDS: the tile prefix, the stage(s) (token-major V or fp8
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // power of two (HW is, when staged).
   const int S = HW * D * kB;
   const int s_log2 = __builtin_ctz(static_cast<unsigned>(S));
-  const int kpitch = sk_stage_kpitch(S), vpitch = sk_stage_vpitch(kB == 2 ? S : 2 * S);
+  const int kpitch = sk_stage_kpitch(S), vpitch = sk_stage_vpitch(S);  // (vpitch: 16-bit V rows)
   char* stage_v = stage + TT * kpitch + (TT == 32 ? 64 : 0);
   const int SV = HW * D * BS * kB;  // dim-major V: the head group's region of one block
   const int sv_log2 = __builtin_ctz(static_cast<unsigned>(SV));
@@ -642,12 +644,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         if constexpr (TV && kB == 2) {
           *reinterpret_cast<u32x4*>(stg_v + st_r(i) * vpitch + st_cb(i)) = vr[i];
         } else if constexpr (TV) {
-          // fp8 token-major V: 16 codes -> 16 bf16, exact
-          const u32x2 a = e4m3x4_to_bf16x4(vr[i].x), b = e4m3x4_to_bf16x4(vr[i].y);
-          const u32x2 c = e4m3x4_to_bf16x4(vr[i].z), d = e4m3x4_to_bf16x4(vr[i].w);
-          char* dst = stg_v + st_r(i) * vpitch + 2 * st_cb(i);
-          *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b.x, b.y};
-          *reinterpret_cast<u32x4*>(dst + 16) = u32x4{c.x, c.y, d.x, d.y};
+          // fp8 token-major V: the codes as loaded, laid out like K
+          *reinterpret_cast<u32x4*>(stg_v + st_k(st_r(i), st_cb(i))) = vr[i];
         } else {
           // dim-major V (fp8): chunk-major, [part][head][8-token chunk][dim]
           // [8 bytes], so the 16 lanes of an operand read (16 head dims, one
@@ -703,9 +701,10 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
                 *reinterpret_cast<const u32x4*>(stg + st_k(row, wave * D + qk_dim<1>(2 * a, j)));
         }
         if constexpr (TV) {
-          // tokens 8j .. 8j + 3 and 8j + 4 .. 8j + 7: two transposing reads
-          vt_src = reinterpret_cast<const uint16_t*>(stg_v + (8 * j + (col >> 2)) * vpitch + wave * D * 2) +
-                   4 * (col & 3);
+          // one 8-bit transposing read per 16-dim tile: lane m of group j
+          // points at row 8j + m / 2, dims 8 (m % 2) .. of the tile, and
+          // lane `col` receives dim col of tokens 8j .. 8j + 7
+          v8_src = stg_v + st_k(8 * j + (col >> 1), wave * D + 8 * (col & 1));
         } else {
           v8_src = stg_v + ((8 * j) / BS) * SV + wave * D * BS + (((8 * j) % BS) / 8) * (D * 8) + col * 8;
         }
@@ -799,8 +798,9 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       } else {
         u32x2 b0, b1;  // the lane's 8 tokens of its head dim as bf16
         if constexpr (TV) {
-          b0 = lds_read_tr16(vt_src + 16 * nt);
-          b1 = lds_read_tr16(vt_src + 4 * vpitch / 2 + 16 * nt);
+          const u32x2 codes = lds_read_tr8(v8_src + 16 * nt);  // tokens 8j .. 8j + 7, dim col
+          b0 = e4m3x4_to_bf16x4(codes.x);
+          b1 = e4m3x4_to_bf16x4(codes.y);
         } else {
           u32x2 vv;
           if constexpr (STG) {

@@ -51,6 +51,17 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// Eight 8-bit elements of a transposing LDS read (ds_read_b64_tr_b8): in
+// each 16-lane group, lane i gets element i % 8 of the 8 bytes that lanes
+// i / 8, 2 + i / 8, 4 + i / 8, ..., 14 + i / 8 of the group point at, in
+// that order (element k in byte k of the result).
+__device__ __forceinline__ u32x2 lds_read_tr8(const char* p) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 // A 16-token V tile in LDS for the transposing reads: 16 rows of D 16-bit
 // elements, padded by 16 elements (the reads of a 16-lane group then hit
 // distinct banks). kVTileRow elements per row; vt_tile_floats(D) = its size
