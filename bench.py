@@ -619,6 +619,7 @@ def main():
         "pa_decode_us_min": round(float(durs.min()) * 1e6, 2),
         "host_block_manager_us_per_step": round(batch.host_seconds / max(batch.host_steps, 1) * 1e6, 2),
         "host_block_manager_note": "pa_alloc_batch + pa_bm_pack of the whole batch on the host, inside each step",
+        "setup_upload_stalls_s": batch.warm_stalls,
         "gpu_busy_frac": round(layers * call_s / (el / K), 4),
         "gpu_busy_note": "layers x mean pa_decode call time / step wall time",
         "step_timeline": timeline["summary"],

@@ -90,31 +90,38 @@ class PagedBatch:
         self.host_seconds = 0.0
         self.host_steps = 0
 
-    def _warm_upload_path(self, rounds: int = 12) -> None:
+    def _warm_upload_path(self, rounds: int = 16) -> None:
         """Queue ``rounds`` metadata uploads on the copy stream, each behind
-        compute-stream work that has not finished yet, and wait for all.
+        compute-stream work that is certain to be still running (1 GiB of
+        fills, ~0.2 ms), and wait for all.
 
-        Measured on MI355X (ROCm 7.2): one of the first few pinned
-        host-to-device copies queued on a second stream behind unfinished
-        work of the compute stream blocks the calling thread for about 5 ms,
-        once per process, while the GPU idles (plain hipMemcpyAsync behaves
-        the same; copies queued without such a pending dependency do not
-        trigger it). Taking that cost here keeps it out of the decode
-        steps. The staging buffers' contents are overwritten by every
-        step."""
+        Measured on MI355X (ROCm 7.2): besides the first pinned
+        host-to-device copy of a process, one of the first few copies queued
+        on a second stream behind unfinished work of the compute stream
+        blocks the calling thread for ~6 ms while the GPU idles (plain
+        hipMemcpyAsync behaves the same); whether a copy meets unfinished
+        work depends on timing, so a short warm-up can miss it and leave the
+        stall to a later decode step. Taking it here keeps it out of the
+        steps. ``warm_stalls`` records the enqueue times above 1 ms (seconds).
+        The staging buffers' contents are overwritten by every step."""
         compute = torch.cuda.current_stream(self.device)
         cs = self._copy_stream
-        busy = torch.empty(16 << 20, dtype=torch.int32, device=self.device)
+        busy = torch.empty(64 << 20, dtype=torch.int32, device=self.device)
         ready = [torch.cuda.Event(), torch.cuda.Event()]
         copied = [torch.cuda.Event(), torch.cuda.Event()]
+        self.warm_stalls = []
         for i in range(rounds):
             st = self._stage[i % 2]
             for _ in range(4):
                 busy.fill_(i)  # work the upload waits for, still running when it is queued
             ready[i % 2].record(compute)
             cs.wait_event(ready[i % 2])
+            t0 = time.perf_counter()
             with torch.cuda.stream(cs):
                 st.dev.copy_(st.host, non_blocking=True)
+            dt = time.perf_counter() - t0
+            if dt > 1e-3:
+                self.warm_stalls.append(round(dt, 4))
             copied[i % 2].record(cs)
             compute.wait_event(copied[i % 2])
         torch.cuda.synchronize(self.device)
