@@ -744,10 +744,18 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
     sp.shared_len = sh->shared_len;
     sp.num_groups = sh->num_groups;
     sp.row_tiles = (sh->max_group_size * G + 15) / 16;
+    // two row tiles per group unit when a group has more than 16 rows: every
+    // shared K/V tile is loaded once per KV head (PA_SHARED_TILES=1 forces
+    // one, a measurement aid)
+    sp.tiles_per_wg = sp.row_tiles > 1 ? 2 : 1;
+    if (const char* t = std::getenv("PA_SHARED_TILES")) {
+      if (std::atoi(t) == 1) sp.tiles_per_wg = 1;
+    }
+    sp.row_sets = (sp.row_tiles + sp.tiles_per_wg - 1) / sp.tiles_per_wg;
     sp.shared_parts = sh->max_shared_len / partition_size;
     sp.pairs = B * hkv;
     const int64_t units = static_cast<int64_t>(sp.shared_parts) * sh->num_groups * hkv;
-    const int64_t gwgs = (units + 7) / 8 * 8 * sp.row_tiles;
+    const int64_t gwgs = (units + 7) / 8 * 8 * sp.row_sets;
     // partitions past the shared prefix: at most P - min_shared_len / ps per sequence
     const int64_t twgs = (P - sh->min_shared_len / partition_size) * static_cast<int64_t>(B) * hkv;
     if (gwgs + twgs > 0x7fffffff)

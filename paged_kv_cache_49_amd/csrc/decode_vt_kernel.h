@@ -152,10 +152,15 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 //    K(t+1) while V(t+1) is still in flight, and vice versa.
 // s_lds: the wave's LDS region (token-major V only; vt_tile_floats(D)
 // floats), free again when the call returns.
-template <typename KV, typename QT, int D, int BS, int G, bool TV>
+// CT column tiles: the wave attends CT sets of 16 q rows to the same
+// tokens (qb[ct], row_ok[ct], m_w[ct], l_w[ct], acc[ct]); each tile's K and
+// V are loaded, staged and converted once and used for every set (the
+// shared-prefix group units, whose rows outnumber 16).
+template <typename KV, typename QT, int D, int BS, int G, bool TV, int CT = 1>
 __device__ __forceinline__ void vt_attend(const DecodeParams& p, const int32_t* bt, int g, int L, int tok_begin,
-                                          int tok_end, int id_first, const u32x4 (&qb)[D / 32], bool row_ok,
-                                          float& m_w, float& l_w, f32x4 (&acc)[D / 16], float* s_lds) {
+                                          int tok_end, int id_first, const u32x4 (&qb)[CT][D / 32],
+                                          const bool (&row_ok)[CT], float (&m_w)[CT], float (&l_w)[CT],
+                                          f32x4 (&acc)[CT][D / 16], float* s_lds) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
   constexpr int kNT = D / 16;
@@ -261,53 +266,65 @@ __device__ __forceinline__ void vt_attend(const DecodeParams& p, const int32_t* 
     for (int tile = 0; tile < ntiles; ++tile) {
       const int tb = c0 + tile * 16;
       const int next = tile + 1 < ntiles ? tile + 1 : tile;  // a missing next tile re-requests this one
-      // ---- S^T = K q^T
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      // ---- S^T = K q^T (per column tile; fp8 K widened once)
+      f32x4 sacc[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (kB == 2) {
 #pragma unroll
-        for (int i = 0; i < C::kKSteps; ++i) sacc = mfma_16x16x32<QT>(kr[i], qb[i], sacc);
+        for (int i = 0; i < C::kKSteps; ++i)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) sacc[ct] = mfma_16x16x32<QT>(kr[i], qb[ct][i], sacc[ct]);
       } else {
 #pragma unroll
         for (int a = 0; a < C::kKLoads; ++a) {
           const u32x2 b0 = e4m3x4_to_bf16x4(kr[a].x), b1 = e4m3x4_to_bf16x4(kr[a].y);
           const u32x2 b2 = e4m3x4_to_bf16x4(kr[a].z), b3 = e4m3x4_to_bf16x4(kr[a].w);
-          sacc = mfma_16x16x32<QT>(u32x4{b0.x, b0.y, b1.x, b1.y}, qb[2 * a], sacc);
-          sacc = mfma_16x16x32<QT>(u32x4{b2.x, b2.y, b3.x, b3.y}, qb[2 * a + 1], sacc);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            sacc[ct] = mfma_16x16x32<QT>(u32x4{b0.x, b0.y, b1.x, b1.y}, qb[ct][2 * a], sacc[ct]);
+            sacc[ct] = mfma_16x16x32<QT>(u32x4{b2.x, b2.y, b3.x, b3.y}, qb[ct][2 * a + 1], sacc[ct]);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
       load_k(next, kr);
       __builtin_amdgcn_sched_barrier(0);
-      float sv[4];
+      u32x2 phi[CT], plo[CT];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = tb + 4 * j + r < tok_end ? sacc[r] * p.qk_scale_log2 : -INFINITY;
+      for (int ct = 0; ct < CT; ++ct) {
+        float sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[r] = tb + 4 * j + r < tok_end ? sacc[ct][r] * p.qk_scale_log2 : -INFINITY;
 
-      // ---- online softmax (head = col)
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const bool need = row_ok && mx > m_w + C::kSlack;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float a = need ? __builtin_amdgcn_exp2f(m_w - mx) : 1.0f;
-        m_w = need ? mx : m_w;
-        l_w *= a;
+        // ---- online softmax (row = col of this column tile)
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const bool need = row_ok[ct] && mx > m_w[ct] + C::kSlack;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float a = need ? __builtin_amdgcn_exp2f(m_w[ct] - mx) : 1.0f;
+          m_w[ct] = need ? mx : m_w[ct];
+          l_w[ct] *= a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(a, 4 * j + r, 64);  // factor of row 4j + r (held by lane 4j + r)
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) acc[ct][nt][r] *= ar;
+          }
+        }
+        float pw[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(a, 4 * j + r, 64);  // factor of head 4j + r (held by lane 4j + r)
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) acc[nt][r] *= ar;
+          pw[r] = row_ok[ct] ? __builtin_amdgcn_exp2f(sv[r] - m_w[ct]) : 0.f;
+          l_w[ct] += pw[r];
         }
+        const uint32_t h0 = pack2<QT>(pw[0], pw[1]), h1 = pack2<QT>(pw[2], pw[3]);
+        const uint32_t l0 = pack2<QT>(pw[0] - half_lo<QT>(h0), pw[1] - half_hi<QT>(h0));
+        const uint32_t l1 = pack2<QT>(pw[2] - half_lo<QT>(h1), pw[3] - half_hi<QT>(h1));
+        phi[ct] = u32x2{h0, h1};
+        plo[ct] = u32x2{l0, l1};
       }
-      float pw[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pw[r] = row_ok ? __builtin_amdgcn_exp2f(sv[r] - m_w) : 0.f;
-        l_w += pw[r];
-      }
-      const uint32_t h0 = pack2<QT>(pw[0], pw[1]), h1 = pack2<QT>(pw[2], pw[3]);
-      const uint32_t l0 = pack2<QT>(pw[0] - half_lo<QT>(h0), pw[1] - half_hi<QT>(h0));
-      const uint32_t l1 = pack2<QT>(pw[2] - half_lo<QT>(h1), pw[3] - half_hi<QT>(h1));
-      const u32x2 phi = {h0, h1}, plo = {l0, l1};
 
       // ---- PV: acc[h][d] += sum_t w[h][t] V[t][d]
       u32x2 vmask = {0xffffffffu, 0xffffffffu};
@@ -352,8 +369,11 @@ __device__ __forceinline__ void vt_attend(const DecodeParams& p, const int32_t* 
         }
         vop.x &= vmask.x;
         vop.y &= vmask.y;
-        acc[nt] = mfma_16x16x16<QT>(phi, vop, acc[nt]);
-        acc[nt] = mfma_16x16x16<QT>(plo, vop, acc[nt]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          acc[ct][nt] = mfma_16x16x16<QT>(phi[ct], vop, acc[ct][nt]);
+          acc[ct][nt] = mfma_16x16x16<QT>(plo[ct], vop, acc[ct][nt]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       load_v(next, vr);
@@ -435,25 +455,26 @@ __device__ __forceinline__ void vt_unit(const DecodeParams& p, int wg, int pairs
   const int col = lane & 15, j = lane >> 4;
 
   // q rows as the B operand of S^T = K q^T (columns >= G are zero)
-  u32x4 qb[C::kKSteps];
+  u32x4 qb[1][C::kKSteps];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
 #pragma unroll
     for (int i = 0; i < C::kKSteps; ++i) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
-      qb[i] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
+      qb[0][i] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
-  float m_w = -INFINITY;
-  float l_w = 0.f;
-  f32x4 acc[kNT];
+  float m_w[1] = {-INFINITY};
+  float l_w[1] = {0.f};
+  const bool row_ok[1] = {col < G};
+  f32x4 acc[1][kNT];
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  vt_attend<KV, QT, D, BS, G, TV>(p, bt, g, L, tok_begin, tok_end, id_first, qb, col < G, m_w, l_w, acc, s_out);
+  for (int nt = 0; nt < kNT; ++nt) acc[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  vt_attend<KV, QT, D, BS, G, TV>(p, bt, g, L, tok_begin, tok_end, id_first, qb, row_ok, m_w, l_w, acc, s_out);
 
   // ---- epilogue: normalised rows through LDS for wide stores
-  const float l_head = vt_normalise<D>(acc, l_w, p.v_scale, G, s_out);
+  const float l_head = vt_normalise<D>(acc[0], l_w[0], p.v_scale, G, s_out);
   for (int i = lane * 8; i < G * D; i += 64 * 8) {
     float o[8];
 #pragma unroll
@@ -470,7 +491,7 @@ __device__ __forceinline__ void vt_unit(const DecodeParams& p, int wg, int pairs
   }
   if (nparts > 1 && lane < G) {
     const int64_t pi = (head0 + lane) * p.num_partitions + part;
-    p.part_m[pi] = m_w;
+    p.part_m[pi] = m_w[0];
     p.part_l[pi] = l_head;
   }
 }
