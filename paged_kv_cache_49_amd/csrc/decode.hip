@@ -363,7 +363,7 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   // staged: two stages (one barrier per unit instead of two) when the
   // workgroups that hold 8 waves per CU still fit a CU's LDS with them
   int stage_bufs = 1;
-  if (staged && G <= 4) {  // (the two-stage build exists for G <= 4)
+  if (staged) {
     const size_t lds2 = sk_lds_bytes(B, HW, G, D, true, cache->dtype == PA_FP8_E4M3 ? 1 : 2, tv, 2);
     const size_t dev_lds = sk_device_lds();
     const size_t per_cu = static_cast<size_t>(std::max(1, 8 / HW));

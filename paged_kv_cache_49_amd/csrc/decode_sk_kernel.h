@@ -123,8 +123,11 @@ __device__ __forceinline__ int sk_find_seq(const int32_t* pref, int B, int r) {
   return lo;
 }
 
-// LDS of one wave, in floats: its G x D fp32 output tile
-__host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D) { return static_cast<size_t>(G) * D; }
+// LDS of one wave, in floats: its G q rows (D 16-bit elements each, rows
+// padded by 16 bytes), through which the staged path rebuilds q
+__host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D) {
+  return static_cast<size_t>(G) * (2 * D + 16) / 4;
+}
 
 // The stage: the unit's K and V as loaded (whole rows), in LDS. S = HW * D
 // * b bytes is the head group's slice of a token row. (Measured with the
@@ -562,34 +565,28 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // store the segment that just ended: final output, or a partial piece
+  // store the segment that just ended: final output, or a partial piece,
+  // straight from the accumulators (lane (col, j) holds rows 4j .. 4j + 3,
+  // head dim 16 nt + col; 16 lanes store 16 consecutive dims)
   auto flush = [&](int seg_seq, int seg_hg, bool complete, bool ends_here, int slot) {
     float l_head = l_w + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_w), 0x401F));
     l_head += __shfl_xor(l_head, 32, 64);
+    const int64_t head0 = static_cast<int64_t>(seg_seq) * p.num_q_heads + static_cast<int64_t>(seg_hg * HW + wave) * G;
+    const int64_t pbase = ((static_cast<int64_t>(w) * p.piece_slots + slot) * HW + wave) * G;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * j + r;
       const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
       if (h < G) {
         const float inv = p.v_scale / lr;
+        if (complete) {
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) s_out[h * D + nt * 16 + col] = acc[nt][r] * inv;
-      }
-    }
-    wave_lds_sync();
-    const int64_t head0 = static_cast<int64_t>(seg_seq) * p.num_q_heads + static_cast<int64_t>(seg_hg * HW + wave) * G;
-    const int64_t pbase = ((static_cast<int64_t>(w) * p.piece_slots + slot) * HW + wave) * G;
-    for (int i = lane * 8; i < G * D; i += 64 * 8) {
-      float o[8];
+          for (int nt = 0; nt < kNT; ++nt) store_out(p.out, (head0 + h) * D + nt * 16 + col, p.out_dtype, acc[nt][r] * inv);
+        } else {
+          float* po = p.piece_o + (pbase + h) * D + col;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = s_out[i + e];
-      const int h = i / D, d = i % D;
-      if (complete) {
-        store_out8(p.out, (head0 + h) * D + d, p.out_dtype, o);
-      } else {
-        float* po = p.piece_o + (pbase + h) * D + d;
-        *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
+          for (int nt = 0; nt < kNT; ++nt) po[nt * 16] = acc[nt][r] * inv;
+        }
       }
     }
     if (!complete && lane < G) {
@@ -605,7 +602,6 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         if (ends_here) desc[1] = w;
       }
     }
-    wave_lds_sync();
   };
 
   // append: the new token's element v_new[d] (d = lane's dim) out of the
@@ -948,11 +944,10 @@ hipError_t launch_decode_sk_n(const SkParams& p, int cus, int max_wgs, hipStream
 
 // Launch of the balanced kernel: W = resident workgroups (occupancy x CUs),
 // at most max_wgs. Writes the grid size used to *wgs. p.stage_bufs = 2
-// takes the two-stage build (built for the staged path with G <= 4, where
-// two stages can fit next to the wave regions).
+// takes the two-stage build (built for the staged path).
 template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV>
 hipError_t launch_decode_sk(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
-  if constexpr ((TV || KV::kBytes == 1) && G <= 4) {
+  if constexpr (TV || KV::kBytes == 1) {
     if (p.stage_bufs > 1) return launch_decode_sk_n<KV, QT, D, BS, G, AP, TV, 2>(p, cus, max_wgs, stream, wgs);
   }
   return launch_decode_sk_n<KV, QT, D, BS, G, AP, TV, 1>(p, cus, max_wgs, stream, wgs);
