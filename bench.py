@@ -73,21 +73,33 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes (read + written) of one pa_decode call from the committed
-    counter summary, and their ratio to the algorithmic bytes of the counted
-    calls; (None, None) when the kernel sources changed since the counters
-    were taken."""
-    path = os.path.join(ROOT, "profiles", "decode_gqa_traffic.json")
+def load_profile():
+    """The committed profile of the GQA decode step (profiles/decode_gqa_profile.json:
+    rocprofv3 kernel-trace durations of the balanced kernel (K1) and its merge
+    (K2), calibrated FETCH_SIZE / WRITE_SIZE per call, and the algorithmic
+    bytes per call of the profiled run), or None when the kernel sources
+    changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "decode_gqa_profile.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None, None
-    if t.get("kernel_hash") != kernel_hash():
-        return None, None
-    hbm, alg = t.get("hbm_bytes_per_call"), t.get("algorithmic_bytes_per_call_of_counted_run")
-    return hbm, (round(hbm / alg, 4) if hbm and alg else None)
+        return None
+    return t if t.get("kernel_hash") == kernel_hash() else None
+
+
+def algorithmic_bytes(lens, block_size: int, hq: int, hkv: int, d: int, kv_bytes: int, out_bytes: int,
+                      appended: bool) -> int:
+    """Bytes one decode call must move at the least: per sequence the K and V
+    rows of its valid tokens, its block-table entries, its q rows and its
+    output rows, plus (a call that appends) the new token's row written
+    into the cache, and the lengths (and slots) arrays."""
+    lens = np.asarray(lens, np.int64)
+    kv = 2 * int(lens.sum()) * hkv * d * kv_bytes
+    tables = 4 * int((-(-lens // block_size)).sum())
+    qo = len(lens) * hq * d * (2 + out_bytes)
+    new_rows = len(lens) * 2 * hkv * d * kv_bytes if appended else 0
+    return kv + tables + qo + new_rows + 4 * len(lens) + (8 * len(lens) if appended else 0)
 
 
 class HipTimingEvent:
@@ -394,6 +406,7 @@ def bench_decode_calls(args):
                 f"head_dim 128, block {bs}, KV {kv}, q bf16")
     b = 1 if kv == "fp8" else 2
     call_bytes = 2 * int(L.sum()) * Hkv * D * b
+    alg_call = algorithmic_bytes(L, bs, Hq, Hkv, D, b, 2, False)
     q = torch.randn(B, Hq, D, generator=gen, device=dev).bfloat16()
     out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
     ws = workspace_for(B, Hq, Hkv, D, max_ctx, ps, device=dev)
@@ -481,9 +494,12 @@ def bench_decode_calls(args):
         "decode_tokens_per_s": round(B / call_s, 1),
         "decode_tokens_per_s_note": "sequences per second of one layer's call",
         "pa_decode_us": round(call_s * 1e6, 2),
-        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(value, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_call": call_bytes},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(alg_call / call_s / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(alg_call / call_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "frac_events": round(alg_call / call_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_call": alg_call,
+                     "algorithmic_note": "K/V rows of the valid tokens (logical: shared blocks counted per "
+                                         "sequence), table entries, q and out rows, lengths"},
         "cpu_baseline": None,
         **extra,
     }
@@ -582,9 +598,12 @@ def main():
     total_bytes = float(sum(step_bytes))
     durs = np.array([tm.calls[0][0].elapsed_time(tm.calls[0][1]) for tm in step_tm]) * 1e-3  # seconds
     per_call_bytes = total_bytes / (K * layers)  # every layer of a step reads the same bytes
+    # all bytes a call moves at the least (K/V, tables, q, out, the appended row), mean over the timed calls
+    alg_call = float(np.mean([algorithmic_bytes(lens_before + i + 1, bs, Hq, Hkv, D, 2, 2, fused)
+                              for i in range(K)]))
     call_s = float(durs.mean())
-    achieved = per_call_bytes / call_s / 1e9
-    traffic, traffic_ratio = load_traffic()
+    achieved = alg_call / call_s / 1e9
+    prof = load_profile()
     value = total_bytes / el / 1e9
     print(f"[bench] {K} steps in {el * 1e3:.2f} ms; pa_decode mean {call_s * 1e6:.1f} us "
           f"(min {durs.min() * 1e6:.1f}, max {durs.max() * 1e6:.1f})", file=sys.stderr, flush=True)
@@ -632,10 +651,19 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "traffic_unit": "bytes per pa_decode call (FETCH_SIZE + WRITE_SIZE, calibrated)",
-            "traffic_per_algorithmic_byte": traffic_ratio,
-            "algorithmic_bytes_per_call": round(per_call_bytes),
+            "traffic": prof["traffic"]["bytes_per_call"] if prof else None,
+            "traffic_unit": "HBM bytes per call (FETCH_SIZE + WRITE_SIZE of K1 + K2, calibrated on a 1 GiB copy)",
+            "traffic_per_algorithmic_byte": prof["traffic"]["per_algorithmic_byte"] if prof else None,
+            "algorithmic_bytes_per_call": round(alg_call),
+            "algorithmic_note": "per call: K/V rows of the valid tokens, block-table entries, q and out rows, "
+                                "the appended token's K/V row, lengths and slots; achieved = that / the mean "
+                                "HIP-event duration of layer 0's call (both launches and the gap between them)",
+            "frac_events": round(achieved / HBM_PEAK_GBS, 4),
+            "frac_kernel": prof["frac_kernel"] if prof else None,
+            "frac_kernel_note": ("algorithmic bytes per call of the profiled run / the rocprofv3 average duration "
+                                 "of K1 (paged_decode_sk_kernel) and of K1 + K2 (+ decode_sk_merge_kernel), "
+                                 "from profiles/decode_gqa_profile.json" if prof else
+                                 "kernel sources changed since the committed profile: not recomputed"),
         },
         "cpu_baseline": None,
     }

@@ -339,7 +339,7 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   // workgroups share a CU and overlap their starts
   const int HW = part_mode ? std::min(sk_heads_per_wg(hkv, staged), 4) : sk_heads_per_wg(hkv, staged);
   const int n_hg = hkv / HW;
-  const size_t lds = sk_lds_bytes(B, HW, G, D, staged, cache->dtype == PA_FP8_E4M3 ? 1 : 2, tv);
+  const size_t lds = sk_lds_bytes(B, HW, G, D, staged, cache->dtype == PA_FP8_E4M3 ? 1 : 2, tv, 1, append);
   if (lds > (staged ? kSkMaxLdsStage : kSkMaxLds))
     return fail(PA_ERR_UNSUPPORTED, "B = %d is too large for the balanced split (use partition_size > 0)", B);
   // units (tiles x head groups) must stay below 2^31; counted in 16-token
@@ -364,7 +364,7 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   // workgroups that hold 8 waves per CU still fit a CU's LDS with them
   int stage_bufs = 1;
   if (staged) {
-    const size_t lds2 = sk_lds_bytes(B, HW, G, D, true, cache->dtype == PA_FP8_E4M3 ? 1 : 2, tv, 2);
+    const size_t lds2 = sk_lds_bytes(B, HW, G, D, true, cache->dtype == PA_FP8_E4M3 ? 1 : 2, tv, 2, append);
     const size_t dev_lds = sk_device_lds();
     const size_t per_cu = static_cast<size_t>(std::max(1, 8 / HW));
     if (dev_lds > 0 && lds2 <= dev_lds && lds2 * per_cu <= kSkMaxLdsStage) stage_bufs = 2;

@@ -124,9 +124,13 @@ __device__ __forceinline__ int sk_find_seq(const int32_t* pref, int B, int r) {
 }
 
 // LDS of one wave, in floats: its G q rows (D 16-bit elements each, rows
-// padded by 16 bytes), through which the staged path rebuilds q
-__host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D) {
-  return static_cast<size_t>(G) * (2 * D + 16) / 4;
+// padded by 16 bytes), through which the staged path rebuilds q; with
+// lds_flush also its G x D fp32 output tile (the same memory), through which
+// a finished segment is stored with 16-byte stores (the append variant: a
+// flush straight from the accumulators keeps more addresses live, and its
+// build then spilled)
+__host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D, bool lds_flush = false) {
+  return lds_flush ? static_cast<size_t>(G) * D : static_cast<size_t>(G) * (2 * D + 16) / 4;
 }
 
 // The stage: the unit's K and V as loaded (whole rows), in LDS. S = HW * D
@@ -157,10 +161,11 @@ __host__ __device__ inline constexpr size_t sk_stage_bytes(int HW, int D, int kb
 
 // bytes of dynamic LDS: the tile prefix, the stage(s) (token-major V or fp8
 // pools: `staged`), then one region per wave
-inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool staged, int kb, bool tv, int bufs = 1) {
+inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool staged, int kb, bool tv, int bufs = 1,
+                           bool append = false) {
   const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
   return pref + (staged ? bufs * sk_stage_bytes(HW, D, kb, tv) : 0) +
-         static_cast<size_t>(HW) * sk_wave_lds_floats(G, D) * sizeof(float);
+         static_cast<size_t>(HW) * sk_wave_lds_floats(G, D, append) * sizeof(float);
 }
 
 // Barrier for LDS written by some waves of the workgroup and read by others
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   constexpr int kQBytes = G * D * 2;
   constexpr int kQL = STG ? (kQBytes > 1024 ? kQBytes / 1024 : 1) : C::kKSteps;
   constexpr int kQPitch = D * 2 + 16;  // bytes per q row in LDS (rows 4 banks apart)
-  static_assert(!STG || G * kQPitch <= static_cast<int>(sk_wave_lds_floats(G, D) * sizeof(float)),
+  static_assert(!STG || G * kQPitch <= static_cast<int>(sk_wave_lds_floats(G, D, AP) * sizeof(float)),
                 "the q rows fit the wave's LDS region");
   extern __shared__ int32_t sk_smem[];
   const int B = p.batch;
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     return;
   }
 
-  float* s_out = s_out_all + wave * sk_wave_lds_floats(G, D);
+  float* s_out = s_out_all + wave * sk_wave_lds_floats(G, D, AP);
   const int col = lane & 15, j = lane >> 4;
   const int Hkv = p.num_kv_heads;
   const char* kbase = static_cast<const char*>(p.k_pool);
@@ -565,27 +570,58 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // store the segment that just ended: final output, or a partial piece,
-  // straight from the accumulators (lane (col, j) holds rows 4j .. 4j + 3,
-  // head dim 16 nt + col; 16 lanes store 16 consecutive dims)
+  // store the segment that just ended: final output, or a partial piece.
+  // Lane (col, j) holds rows 4j .. 4j + 3, head dim 16 nt + col. The append
+  // variant goes through its LDS output tile (16-byte stores); the others
+  // store straight from the accumulators (16 lanes write 16 consecutive
+  // dims; segment ends are rare, and this needs no LDS tile).
   auto flush = [&](int seg_seq, int seg_hg, bool complete, bool ends_here, int slot) {
     float l_head = l_w + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_w), 0x401F));
     l_head += __shfl_xor(l_head, 32, 64);
     const int64_t head0 = static_cast<int64_t>(seg_seq) * p.num_q_heads + static_cast<int64_t>(seg_hg * HW + wave) * G;
     const int64_t pbase = ((static_cast<int64_t>(w) * p.piece_slots + slot) * HW + wave) * G;
+    if constexpr (AP) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * j + r;
-      const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
-      if (h < G) {
-        const float inv = p.v_scale / lr;
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * j + r;
+        const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
+        if (h < G) {
+          const float inv = p.v_scale / lr;
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) s_out[h * D + nt * 16 + col] = acc[nt][r] * inv;
+        }
+      }
+      wave_lds_sync();
+      for (int i = lane * 8; i < G * D; i += 64 * 8) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = s_out[i + e];
+        const int h = i / D, d = i % D;
         if (complete) {
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) store_out(p.out, (head0 + h) * D + nt * 16 + col, p.out_dtype, acc[nt][r] * inv);
+          store_out8(p.out, (head0 + h) * D + d, p.out_dtype, o);
         } else {
-          float* po = p.piece_o + (pbase + h) * D + col;
+          float* po = p.piece_o + (pbase + h) * D + d;
+          *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        }
+      }
+      wave_lds_sync();
+    } else {
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) po[nt * 16] = acc[nt][r] * inv;
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * j + r;
+        const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
+        if (h < G) {
+          const float inv = p.v_scale / lr;
+          if (complete) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt)
+              store_out(p.out, (head0 + h) * D + nt * 16 + col, p.out_dtype, acc[nt][r] * inv);
+          } else {
+            float* po = p.piece_o + (pbase + h) * D + col;
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) po[nt * 16] = acc[nt][r] * inv;
+          }
         }
       }
     }
@@ -907,7 +943,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV, int NBUF>
 hipError_t launch_decode_sk_n(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
   const int HW = p.heads_per_wg;
-  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes, TV, NBUF);
+  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes, TV, NBUF, AP);
   const void* fn = reinterpret_cast<const void*>(paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
