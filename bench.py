@@ -409,10 +409,13 @@ def bench_decode_calls(args):
     alg_call = algorithmic_bytes(L, bs, Hq, Hkv, D, b, 2, False)
     q = torch.randn(B, Hq, D, generator=gen, device=dev).bfloat16()
     out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
-    ws = workspace_for(B, Hq, Hkv, D, max_ctx, ps, device=dev)
-    if args.workload == "prefix" and args.shared:
+    shared = args.workload == "prefix" and args.shared
+    ws = workspace_for(B, Hq, Hkv, D, max_ctx, ps, device=dev, shared=shared)
+    if shared:
         call = lambda c: pa.decode_shared(c, q, tables, lens, max_ctx, wl.scale, ps, *sargs, out=out, workspace=ws)
-        kernel = "pa_decode_shared (paged_decode_shared_kernel + decode_reduce_kernel)"
+        kernel = ("pa_decode_shared (token-major V or fp8: the cascade, paged_decode_sk_kernel<..., cascade> + "
+                  "decode_cascade_merge_kernel; dim-major 16-bit V: paged_decode_shared_kernel + "
+                  f"decode_reduce_kernel; PA_SHARED_PATH={os.environ.get('PA_SHARED_PATH', 'auto')})")
     else:
         call = lambda c: pa.decode(c, q, tables, lens, max_ctx, wl.scale, ps, out=out, workspace=ws)
         kernel = ("pa_decode (paged_decode_sk_kernel + decode_sk_merge_kernel)" if ps < 0 else

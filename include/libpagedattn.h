@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -470,6 +470,15 @@ pa_status pa_copy_blocks_between(const pa_kv_cache* dst, const pa_kv_cache* src,
 size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size);
 
+/* Workspace bytes pa_decode_shared needs (0 when partition_size <= 0 or the
+ * sizes are invalid): at least pa_decode_workspace_size(...), and what its
+ * cascade needs for any grouping of the B rows on the current device (per
+ * row the two partial states, per CU the partial pieces of one workgroup
+ * of up to 8 KV heads x 32 query rows). A deviation from the proposed
+ * boundary, which has no shared-prefix call. */
+size_t pa_decode_shared_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size);
+
 pa_status pa_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
                     const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
                     int32_t num_q_heads, int32_t max_context_len, float scale, int32_t partition_size,
@@ -528,10 +537,10 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const vo
 /* ------------------------------------------------------------------------
  * Decode attention with shared prefixes read once per group ([course] §2
  * "The bonus": forked sequences share the prompt's blocks; [note]
- * prefix-sharing section). The result is that of pa_decode with the same
- * arguments and partition_size; what differs is the K/V traffic: each
- * partition of a group's shared prefix is read once for all the group's
- * query rows, instead of once per member.
+ * prefix-sharing section). The result is that of pa_decode on the same
+ * batch (up to rounding); what differs is the K/V traffic: a group's
+ * shared prefix is read once for all the group's query rows, instead of
+ * once per member.
  *
  * Groups (device arrays, typically from pa_bm_shared_prefixes): group gi's
  * batch rows are group_members[group_offsets[gi] .. group_offsets[gi + 1]);
@@ -544,9 +553,22 @@ pa_status pa_decode_append(const pa_kv_cache* cache, const void* k_new, const vo
  * when some row is in no group) size the launch. PA_DEBUG=1 checks all of this; otherwise a violation
  * gives wrong results for the rows involved (no out-of-bounds access).
  *
- * partition_size: a positive multiple of 16 and of block_size; the
- * workspace is pa_decode_workspace_size(..., partition_size). Either V
- * layout, any pool dtype. Other arguments and errors as pa_decode.
+ * partition_size: a positive multiple of 16 and of block_size (the unit
+ * of shared_len); the workspace is pa_decode_shared_workspace_size(...,
+ * partition_size) bytes. Either V layout, any pool dtype. Other arguments
+ * and errors as pa_decode.
+ *
+ * Two implementations, the same attention up to rounding:
+ *  - the cascade (token-major V or fp8 pools, groups of at most 32 / G
+ *    rows, the batch's plan in LDS): the balanced split runs over the
+ *    groups' prefixes (each read once, with all the group's query rows) and
+ *    the rows' own tokens as one workload, then each row's two partial
+ *    softmax states are merged (log-sum-exp; [note] prefix-sharing
+ *    section: the shared part is computed once and reused);
+ *  - otherwise, or with a workspace of only pa_decode_workspace_size(...)
+ *    bytes, partitions of partition_size tokens: each partition of a
+ *    group's shared prefix is read once for all its rows, the rest per
+ *    row, merged by the partition reduce.
  * ---------------------------------------------------------------------- */
 pa_status pa_decode_shared(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* q, pa_dtype q_dtype,
                            const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,

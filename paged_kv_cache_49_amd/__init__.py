@@ -22,7 +22,7 @@ from ._lib import PaBmStats, PaKvCache, lib
 __all__ = [
     "PagedAttnError", "OutOfBlocks", "UnknownSeq", "SeqExists", "Unsupported", "InvalidArgument",
     "DeviceError", "BlockManager", "KVCache", "reshape_and_cache", "copy_blocks", "decode",
-    "decode_workspace_size", "decode_append", "prepare_decode", "prepare_decode_append", "prepare_decode_shared", "decode_shared", "SharedPrefixes", "copy_blocks_between", "lib",
+    "decode_workspace_size", "decode_shared_workspace_size", "decode_append", "prepare_decode", "prepare_decode_append", "prepare_decode_shared", "decode_shared", "SharedPrefixes", "copy_blocks_between", "lib",
     "BALANCED",
 ]
 
@@ -441,6 +441,13 @@ def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, head_
                                               int(max_context_len), int(partition_size)))
 
 
+def decode_shared_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                 max_context_len: int, partition_size: int) -> int:
+    """Workspace bytes of pa_decode_shared (on the current device)."""
+    return int(lib().pa_decode_shared_workspace_size(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                                                     int(max_context_len), int(partition_size)))
+
+
 def _deferred(fn, args, device: torch.device, out: torch.Tensor, keep):
     """A callable that issues fn(*args) on ``device`` and returns ``out``;
     it holds ``keep``, the objects args point into."""
@@ -561,7 +568,7 @@ def prepare_decode_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.T
         out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
     if workspace is None:  # (a given workspace is sized by the library's own check)
         with torch.cuda.device(q.device):
-            need = decode_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, partition_size)
+            need = decode_shared_workspace_size(B, Hq, cache.num_kv_heads, D, max_context_len, partition_size)
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     for name, t in (("group_offsets", group_offsets), ("group_members", group_members), ("shared_len", shared_len)):

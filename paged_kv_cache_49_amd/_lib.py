@@ -37,7 +37,7 @@ PA_LAYOUT_TOKEN_MAJOR = 0
 PA_LAYOUT_DIM_MAJOR = 1
 
 PA_PARTITION_BALANCED = -1
-PA_ABI_VERSION = 5
+PA_ABI_VERSION = 6
 
 
 class PaKvCache(ctypes.Structure):
@@ -121,6 +121,7 @@ SIGNATURES = {
     "pa_reshape_and_cache": (c_int, [POINTER(PaKvCache), _P, _P, c_int, _P, c_int32, _P]),
     "pa_copy_blocks": (c_int, [POINTER(PaKvCache), _P, c_int32, _P]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "pa_decode_shared_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode": (c_int, [POINTER(PaKvCache), _P, c_int, _P, c_int, _P, c_int32, _P, c_int32, c_int32,
                           c_int32, c_float, c_int32, _P, c_size_t, _P]),
     "pa_decode_noalloc": (c_int, [POINTER(PaKvCache), _P, c_int, _P, c_int, _P, c_int32, _P, c_int32, c_int32,

@@ -217,6 +217,86 @@ __global__ __launch_bounds__(1024) void decode_sk_merge_kernel(const SkMergePara
   store_out8(p.out, orow * D + 8 * c, p.out_dtype, o);
 }
 
+// ---- the cascade's merge (pa_decode_shared on the balanced kernel): each
+// row's output is the log-sum-exp merge of its prefix part (its group's
+// shared tokens) and its tail part (its own tokens), each part either a
+// state row (one workgroup completed it) or pieces (cut between
+// workgroups; piece rows RW = 32 per wave: the prefix's member-major rows,
+// or a tail's G heads).
+struct CasMergeParams {
+  SkMergeParams pieces;  // piece arrays, slots, shape, lengths, out
+  const float* state_m;  // [2][B][num_q_heads]: prefix part, then tail part
+  const float* state_l;
+  const float* state_o;  // [2][B][num_q_heads][D]
+  const int32_t* row_map;  // [B][4]: group (or -1), place in the group, has a tail
+  int32_t num_groups;
+};
+
+constexpr int kCasPieceRows = 32;  // piece rows per wave (two 16-row tiles)
+
+// grid = B x num_kv_heads (row-major), one thread per 8 head dims of each
+// query head of the KV head
+__global__ __launch_bounds__(512) void decode_cascade_merge_kernel(const CasMergeParams p) {
+  const SkMergeParams& m = p.pieces;
+  const int G = m.group;
+  const int HW = m.heads_per_wg;
+  const int HWG = HW * G;
+  const int D = m.head_dim;
+  const int tpr = D / 8;
+  const int B = m.batch;
+  const int hkv = m.num_q_heads / G;
+  const int s = static_cast<int>(blockIdx.x) / hkv;
+  const int g = static_cast<int>(blockIdx.x) % hkv;
+  const int hg = g / HW, wave = g % HW;
+  const int t = static_cast<int>(threadIdx.x);
+  const int h = t / tpr;
+  const int c = t % tpr;
+  if (h >= G) return;
+  const int hq = wave * G + h;
+  const int64_t head = static_cast<int64_t>(hg) * HWG + hq;
+  const int64_t orow = static_cast<int64_t>(s) * m.num_q_heads + head;
+  const int L = min(m.context_lens[s], m.len_cap);
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (L <= 0) {
+    store_out8(m.out, orow * D + 8 * c, m.out_dtype, o);
+    return;
+  }
+  const int NG = p.num_groups;
+  const int NV = NG + B;
+  const int32_t* rm = p.row_map + 4 * static_cast<int64_t>(s);
+  const int gi = rm[0], mi = rm[1], has_tail = rm[2];
+  float run_m = -INFINITY, den = 0.f;
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // part `part` of segment v; r = the row among the wave's piece rows
+  auto add_part = [&](int part, int v, int r) {
+    const int32_t* desc = m.seg_desc + (static_cast<int64_t>(hg) * NV + v) * 2;
+    const int32_t d0 = desc[0], d1 = desc[1];
+    if (d0 != -1) {
+      merge_pieces(m, m.heads_per_wg * kCasPieceRows, wave * kCasPieceRows + r, c, d0 & 0x7fffffff, d1,
+                   static_cast<int>(static_cast<uint32_t>(d0) >> 31), 0, 1, run_m, den, num);
+      return;
+    }
+    const int64_t row = (static_cast<int64_t>(part) * B + s) * m.num_q_heads + head;
+    const float pm = p.state_m[row];
+    const float pl = p.state_l[row];
+    const f32x4* po = reinterpret_cast<const f32x4*>(p.state_o + row * D + 8 * c);
+    const f32x4 pa = po[0], pb = po[1];
+    const float cm = fmaxf(run_m, pm);
+    const float r0 = run_m > -INFINITY ? __builtin_amdgcn_exp2f(run_m - cm) : 0.f;
+    const float wt = pm > -INFINITY ? pl * __builtin_amdgcn_exp2f(pm - cm) : 0.f;
+    den = den * r0 + wt;
+    const float v8[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) num[e] = fmaf(wt, v8[e], num[e] * r0);
+    run_m = cm;
+  };
+  if (has_tail) add_part(1, NG + s, h);
+  if (gi >= 0) add_part(0, gi, mi * G + h);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = den > 0.f ? num[e] / den : 0.f;
+  store_out8(m.out, orow * D + 8 * c, m.out_dtype, o);
+}
+
 int out_code(pa_dtype t) { return t == PA_F32 ? 2 : (t == PA_BF16 ? 1 : 0); }
 
 int64_t partitions_for(int32_t max_context_len, int32_t partition_size) {
@@ -303,6 +383,39 @@ SkLayout sk_layout_rows(int64_t B, int64_t hkv, int64_t D, size_t rows) {
 SkLayout sk_layout(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int cus) {
   const int64_t G = Hq / hkv;
   return sk_layout_rows(B, hkv, D, static_cast<size_t>(cus) * kSkWavesPerCu * 2 * G);
+}
+
+// workspace of the cascade (pa_decode_shared on the balanced kernel):
+// merge descriptors [head groups][num_groups + B][2], the row map [B][4],
+// the state rows m, l [2][B][Hq] and o [2][B][Hq][D], then the pieces: per
+// piece row (workgroup, slot, wave, 32 rows) m, l, o[D], for `wgs`
+// workgroups of hw waves
+struct CasLayout {
+  size_t desc, map, sm, sl, so, pm, pl, po, total;
+};
+CasLayout cas_layout(int64_t B, int64_t Hq, int64_t hkv, int64_t hw, int64_t D, int64_t groups, int64_t wgs) {
+  CasLayout L{};
+  const size_t srows = static_cast<size_t>(2 * B * Hq);
+  const size_t prows = static_cast<size_t>(wgs * 2 * hw * kCasPieceRows);
+  L.desc = 0;
+  L.map = align_up(static_cast<size_t>((hkv / hw) * (groups + B) * 2) * sizeof(int32_t));
+  L.sm = L.map + align_up(static_cast<size_t>(B) * 4 * sizeof(int32_t));
+  L.sl = L.sm + align_up(srows * sizeof(float));
+  L.so = L.sl + align_up(srows * sizeof(float));
+  L.pm = L.so + align_up(srows * D * sizeof(float));
+  L.pl = L.pm + align_up(prows * sizeof(float));
+  L.po = L.pl + align_up(prows * sizeof(float));
+  L.total = L.po + align_up(prows * D * sizeof(float));
+  return L;
+}
+
+// the cascade workspace pa_decode_workspace_size promises for partitioned
+// calls: any grouping of the batch (at most B groups), one workgroup of 8
+// waves per CU (the cascade's 8-wave workgroups use more than half of a
+// SIMD's registers, so at most that many are resident)
+size_t cas_workspace_bound(int64_t B, int64_t Hq, int64_t hkv, int64_t D, int cus) {
+  const int64_t hw = sk_heads_per_wg(static_cast<int>(hkv), true);
+  return cas_layout(B, Hq, hkv, hw, D, B, static_cast<int64_t>(cus) * std::max<int64_t>(1, 8 / hw)).total;
 }
 
 }  // namespace
@@ -492,6 +605,126 @@ pa_status decode_balanced(const pa_kv_cache* cache, void* out, int out_code, con
   return PA_OK;
 }
 
+// pa_decode_shared on the balanced kernel's cascade variant (see
+// decode_sk_kernel.h): one launch over the prefixes of the groups and the
+// tails of the rows, then decode_cascade_merge_kernel. Returns
+// PA_ERR_UNSUPPORTED without launching anything when this shape has no
+// cascade build or does not fit it (the caller then takes the
+// shared-prefix partition kernels). Arguments are validated by the caller.
+pa_status decode_cascade(const pa_kv_cache* cache, void* out, int out_code, const void* q,
+                         const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t B,
+                         int32_t num_q_heads, int32_t max_context_len, float qk_scale_log2, float v_scale,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         const int32_t* group_offsets, const int32_t* group_members, const int32_t* shared_len,
+                         int32_t num_groups, int32_t max_group_size) {
+  const int32_t hkv = cache->num_kv_heads;
+  const int32_t D = cache->head_dim;
+  const int32_t G = num_q_heads / hkv;
+  const bool tv = cache->v_layout == PA_LAYOUT_TOKEN_MAJOR;
+  const bool fp8 = cache->dtype == PA_FP8_E4M3;
+  const SkLaunch launch = find_decode_cas(cache->dtype, cache->v_layout, D, cache->block_size, G);
+  // a prefix unit holds a group's rows in two 16-row tiles
+  if (launch == nullptr || static_cast<int64_t>(max_group_size) * G > kCasPieceRows)
+    return PA_ERR_UNSUPPORTED;
+  const int HW = sk_heads_per_wg(hkv, true);
+  const int n_hg = hkv / HW;
+  const int kb = fp8 ? 1 : 2;
+  const size_t lds = sk_lds_bytes(B, HW, G, D, true, kb, tv, 1, false, num_groups);
+  const size_t dev_lds = sk_device_lds();
+  const int cus = device_cus();
+  if (dev_lds == 0 || lds > dev_lds || lds > kSkMaxLdsStage || cus <= 0) return PA_ERR_UNSUPPORTED;
+  // units: tiles of the tails (at most the rows' tiles plus one each) and
+  // of the prefixes (at most max_context_len each), per head group
+  const int64_t tiles = (static_cast<int64_t>(B) + num_groups) * ((static_cast<int64_t>(max_context_len) + 15) / 16 + 1);
+  if (tiles * n_hg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  int stage_bufs = 1;
+  {
+    const size_t lds2 = sk_lds_bytes(B, HW, G, D, true, kb, tv, 2, false, num_groups);
+    if (lds2 <= dev_lds && lds2 * static_cast<size_t>(std::max(1, 8 / HW)) <= kSkMaxLdsStage) stage_bufs = 2;
+  }
+  // pieces for as many workgroups as the workspace holds (at most the
+  // resident ones)
+  int64_t wgs = static_cast<int64_t>(cus) * kSkWavesPerCu / HW;
+  if (const char* cap = std::getenv("PA_SK_WGS")) {  // measurement aid
+    const int v = std::atoi(cap);
+    if (v > 0 && v < wgs) wgs = v;
+  }
+  while (wgs > 0 && cas_layout(B, num_q_heads, hkv, HW, D, num_groups, wgs).total > workspace_bytes) {
+    const size_t fixed = cas_layout(B, num_q_heads, hkv, HW, D, num_groups, 0).total;
+    const size_t per_wg = static_cast<size_t>(2) * HW * kCasPieceRows * (2 + static_cast<size_t>(D)) * sizeof(float);
+    const int64_t fit = workspace_bytes > fixed ? static_cast<int64_t>((workspace_bytes - fixed) / per_wg) : 0;
+    wgs = std::min(wgs - 1, fit);
+  }
+  // fewer than one workgroup per CU: the partition kernels serve better
+  if (wgs < cus) return PA_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const CasLayout lay = cas_layout(B, num_q_heads, hkv, HW, D, num_groups, wgs);
+  char* ws = static_cast<char*>(workspace);
+  SkParams p{};
+  p.q = q;
+  p.k_pool = cache->k;
+  p.v_pool = cache->v;
+  p.out = out;
+  p.piece_m = reinterpret_cast<float*>(ws + lay.pm);
+  p.piece_l = reinterpret_cast<float*>(ws + lay.pl);
+  p.piece_o = reinterpret_cast<float*>(ws + lay.po);
+  p.seg_desc = reinterpret_cast<int32_t*>(ws + lay.desc);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.block_stride = cache->block_stride;
+  p.num_blocks = cache->num_blocks;
+  p.num_kv_heads = hkv;
+  p.num_q_heads = num_q_heads;
+  p.max_blocks = max_blocks;
+  p.len_cap = max_context_len;
+  p.batch = B;
+  p.heads_per_wg = HW;
+  p.num_head_groups = n_hg;
+  p.piece_slots = 2;
+  p.stage_bufs = stage_bufs;
+  p.out_dtype = out_code;
+  p.qk_scale_log2 = qk_scale_log2;
+  p.v_scale = v_scale;
+  p.group_offsets = group_offsets;
+  p.group_members = group_members;
+  p.shared_len = shared_len;
+  p.state_m = reinterpret_cast<float*>(ws + lay.sm);
+  p.state_l = reinterpret_cast<float*>(ws + lay.sl);
+  p.state_o = reinterpret_cast<float*>(ws + lay.so);
+  p.row_map = reinterpret_cast<int32_t*>(ws + lay.map);
+  p.num_groups = num_groups;
+  int used = 0;
+  hipError_t e = launch(p, cus, static_cast<int>(wgs), stream, &used);
+  if (e != hipSuccess) return fail(PA_ERR_DEVICE, "cascade decode launch: %s", hipGetErrorString(e));
+  CasMergeParams m{};
+  m.pieces.piece_m = p.piece_m;
+  m.pieces.piece_l = p.piece_l;
+  m.pieces.piece_o = p.piece_o;
+  m.pieces.seg_desc = p.seg_desc;
+  m.pieces.context_lens = context_lens;
+  m.pieces.out = out;
+  m.pieces.len_cap = max_context_len;
+  m.pieces.batch = B;
+  m.pieces.num_q_heads = num_q_heads;
+  m.pieces.heads_per_wg = HW;
+  m.pieces.group = G;
+  m.pieces.head_dim = D;
+  m.pieces.out_dtype = out_code;
+  m.pieces.piece_slots = 2;
+  m.state_m = p.state_m;
+  m.state_l = p.state_l;
+  m.state_o = p.state_o;
+  m.row_map = p.row_map;
+  m.num_groups = num_groups;
+  const int merge_threads = (G * D / 8 + 63) / 64 * 64;
+  hipLaunchKernelGGL(decode_cascade_merge_kernel, dim3(static_cast<uint32_t>(B) * hkv), dim3(merge_threads), 0, stream,
+                     m);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_DEVICE, "cascade merge launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 }  // namespace pa
 
 using pa::fail;
@@ -510,6 +743,17 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_h
   if (max_context_len == 0) return 0;
   return pa::workspace_bytes_for(B, num_q_heads, num_kv_heads, head_dim,
                                  pa::partitions_for(max_context_len, partition_size));
+}
+
+size_t pa_decode_shared_workspace_size(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0) return 0;
+  const size_t part =
+      pa_decode_workspace_size(B, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+  if (part == 0 || num_q_heads % num_kv_heads != 0) return part;
+  const int cus = pa::device_cus();
+  if (cus <= 0) return 0;
+  return std::max(part, pa::cas_workspace_bound(B, num_q_heads, num_kv_heads, head_dim, cus));
 }
 
 }  // extern "C"
@@ -704,6 +948,24 @@ pa_status decode_impl(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, c
     return pa::decode_balanced(cache, out, out_c, q, block_tables, max_blocks, context_lens, B, num_q_heads,
                                max_context_len, qk_scale_log2, v_scale, workspace, workspace_bytes, s,
                                partition_size, P);
+  // shared prefixes: the cascade on the balanced kernel where it is built
+  // and fits, else the shared-prefix partition kernels below
+  // (PA_SHARED_PATH=partition / cascade forces one; cascade fails with
+  // PA_ERR_UNSUPPORTED where it cannot run: measurement and test aids)
+  if (sh != nullptr && sh->num_groups > 0 && sh->max_shared_len > 0) {
+    const char* path = std::getenv("PA_SHARED_PATH");
+    if (path == nullptr || std::strcmp(path, "partition") != 0) {
+      const pa_status cs = pa::decode_cascade(cache, out, out_c, q, block_tables, max_blocks, context_lens, B,
+                                              num_q_heads, max_context_len, qk_scale_log2, v_scale, workspace,
+                                              workspace_bytes, s, sh->group_offsets, sh->group_members,
+                                              sh->shared_len, sh->num_groups, sh->max_group_size);
+      if (cs != PA_ERR_UNSUPPORTED) return cs;
+      if (path != nullptr && std::strcmp(path, "cascade") == 0)
+        return fail(PA_ERR_UNSUPPORTED,
+                    "PA_SHARED_PATH=cascade: no cascade for this call (token-major V or fp8 pools, at most 32 "
+                    "rows per group, the batch's plan in LDS, a workspace of pa_decode_shared_workspace_size)");
+    }
+  }
 
   pa::DecodeParams prm{};
   prm.q = q;

@@ -78,6 +78,24 @@ inline SkLaunch find_decode_sk(pa_dtype pool, pa_layout v_layout, int head_dim, 
   }
 }
 
+// the cascade variant of the balanced kernel (pa_decode_shared): built on
+// the staged path, token-major V or fp8 pools (nullptr otherwise)
+SkLaunch find_decode_cas_fp8(int head_dim, int block_size, int group);
+SkLaunch find_decode_cas_f16_tv(int head_dim, int block_size, int group);
+SkLaunch find_decode_cas_bf16_tv(int head_dim, int block_size, int group);
+SkLaunch find_decode_cas_fp8_tv(int head_dim, int block_size, int group);
+
+inline SkLaunch find_decode_cas(pa_dtype pool, pa_layout v_layout, int head_dim, int block_size, int group) {
+  const bool tv = v_layout == PA_LAYOUT_TOKEN_MAJOR;
+  switch (pool) {
+    case PA_F16: return tv ? find_decode_cas_f16_tv(head_dim, block_size, group) : nullptr;
+    case PA_BF16: return tv ? find_decode_cas_bf16_tv(head_dim, block_size, group) : nullptr;
+    case PA_FP8_E4M3:
+      return tv ? find_decode_cas_fp8_tv(head_dim, block_size, group) : find_decode_cas_fp8(head_dim, block_size, group);
+    default: return nullptr;
+  }
+}
+
 // the partition kernel for the pool's dtype and V layout
 inline DecodeLaunch find_decode(pa_dtype pool, pa_layout v_layout, int head_dim, int block_size, int group) {
   const bool tv = v_layout == PA_LAYOUT_TOKEN_MAJOR;

@@ -42,10 +42,10 @@
 //  * unit batches: lane i of a batch resolves unit ub + i to its sequence,
 //    tile, length, head group and block id(s); the batch after it is
 //    requested one batch ahead, so block-table reads never stall the loads.
-//  * a 3-deep register ring keeps the q, K and V loads of two units in
-//    flight while a third unit is computed (q rides in the ring too, so a
-//    new segment never waits on a load issued behind the ring's; staged, as
-//    the wave's G x D rows, rebuilt through its LDS region). The waves of a
+//  * a 2-slot register ring keeps the q, K and V loads of the next unit in
+//    flight while one unit is computed (q rides in the ring too, so a new
+//    segment never waits on a load issued behind the ring's; staged, as the
+//    wave's G x D rows, rebuilt through its LDS region). The waves of a
 //    workgroup pass a barrier after each unit: without it the oldest wave
 //    of each SIMD takes most issue slots and finishes far ahead, and the
 //    others end alone with few loads in flight.
@@ -61,7 +61,26 @@
 //    between holds a slot-0 piece; a workgroup with no units writes neutral
 //    slot-0 pieces (m = -inf, l = 0, o = 0), so a merge may include it.
 //    In partition mode a workgroup holds exactly one piece (one slot).
+//
+// Cascade variant (CAS, for pa_decode_shared;
+// [course] §2 "The bonus": forked sequences share the prompt's blocks;
+// [note] prefix-sharing section). The same persistent ranges run over
+// "virtual sequences" instead of sequences: first one per group, the
+// group's shared prefix (tokens [0, S) in whole units, read through the
+// first member's table), then one per batch row, the row's own tokens
+// [S, L). A prefix unit computes two 16-row q tiles per wave: row r of the
+// pair is member r / G of the group, query head r % G of the wave's KV head,
+// so each shared K/V tile is read once for every member. Softmax attention
+// over the row's tokens is the log-sum-exp merge of its two parts, so each
+// part leaves its partial (m, l, o): a segment one workgroup completed as a
+// state row of its batch row, a cut segment as pieces; decode_cascade_merge_
+// kernel (decode.hip) merges prefix and tail of every row. A prefix
+// segment's q rows (two tiles) sit in the wave's LDS region from the
+// segment's first unit in the range on; the two tiles are computed one
+// after the other on the unit's K and V operands.
 #pragma once
+
+#include <type_traits>
 
 #include "decode_vt_kernel.h"
 #include "host_cache.h"
@@ -101,6 +120,20 @@ struct SkParams {
   int32_t out_dtype;
   float qk_scale_log2;
   float v_scale;
+  // cascade only: the groups (group gi's rows are group_members[
+  // group_offsets[gi] .. group_offsets[gi + 1]), each row's shared length,
+  // the state rows of completed segments ([part][B][num_q_heads], part 0 =
+  // prefix, 1 = tail) and the merge's row map ([B][4]: group of the row's
+  // prefix part or -1, the row's place in that group, whether the row has
+  // a tail part)
+  const int32_t* group_offsets;
+  const int32_t* group_members;
+  const int32_t* shared_len;
+  float* state_m;
+  float* state_l;
+  float* state_o;
+  int32_t* row_map;
+  int32_t num_groups;
 };
 
 // first unit of workgroup w's range; the range of w is [start(w), start(w + 1))
@@ -128,9 +161,12 @@ __device__ __forceinline__ int sk_find_seq(const int32_t* pref, int B, int r) {
 // lds_flush also its G x D fp32 output tile (the same memory), through which
 // a finished segment is stored with 16-byte stores (the append variant: a
 // flush straight from the accumulators keeps more addresses live, and its
-// build then spilled)
-__host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D, bool lds_flush = false) {
-  return lds_flush ? static_cast<size_t>(G) * D : static_cast<size_t>(G) * (2 * D + 16) / 4;
+// build then spilled); cascade: 32 q rows (the two row tiles of a prefix
+// unit, written when its segment starts)
+__host__ __device__ inline constexpr size_t sk_wave_lds_floats(int G, int D, bool lds_flush = false,
+                                                                bool cas = false) {
+  return cas ? static_cast<size_t>(32) * (2 * D + 16) / 4
+             : (lds_flush ? static_cast<size_t>(G) * D : static_cast<size_t>(G) * (2 * D + 16) / 4);
 }
 
 // The stage: the unit's K and V as loaded (whole rows), in LDS. S = HW * D
@@ -159,13 +195,23 @@ __host__ __device__ inline constexpr size_t sk_stage_bytes(int HW, int D, int kb
                        (tv ? 32 * static_cast<size_t>(sk_stage_kpitch(HW * D)) + 64 : 32 * static_cast<size_t>(HW * D));
 }
 
-// bytes of dynamic LDS: the tile prefix, the stage(s) (token-major V or fp8
+// ints of the plan in LDS (a multiple of 4): the tile prefix over the
+// sequences [B + 1]; the cascade (cas_groups = its number of groups NG,
+// NV = NG + B virtual sequences) holds the prefix [NV + 1], per virtual
+// sequence its table row or first tail unit [NV], the group offsets
+// [NG + 1], the members [B], each row's shared length [B] and its place in
+// a group [B]
+__host__ __device__ inline constexpr int sk_plan_ints(int B, int cas_groups) {
+  return ((cas_groups >= 0 ? 3 * cas_groups + 5 * B + 2 : B + 1) + 3) / 4 * 4;
+}
+
+// bytes of dynamic LDS: the plan, the stage(s) (token-major V or fp8
 // pools: `staged`), then one region per wave
 inline size_t sk_lds_bytes(int B, int HW, int G, int D, bool staged, int kb, bool tv, int bufs = 1,
-                           bool append = false) {
-  const size_t pref = (static_cast<size_t>(B) + 1 + 3) / 4 * 4 * sizeof(int32_t);
+                           bool append = false, int cas_groups = -1) {
+  const size_t pref = static_cast<size_t>(sk_plan_ints(B, cas_groups)) * sizeof(int32_t);
   return pref + (staged ? bufs * sk_stage_bytes(HW, D, kb, tv) : 0) +
-         static_cast<size_t>(HW) * sk_wave_lds_floats(G, D, append) * sizeof(float);
+         static_cast<size_t>(HW) * sk_wave_lds_floats(G, D, append, cas_groups >= 0) * sizeof(float);
 }
 
 // Barrier for LDS written by some waves of the workgroup and read by others
@@ -190,18 +236,27 @@ struct SkVSlot<true> {
 // A unit as the wave sees it (uniform values). len = valid tokens counted
 // from the unit's first position; virt = the append variant's virtual tile,
 // whose slot block / offset are sblk / soff.
+// Cascade: pre = a prefix unit; first = the first unit of its virtual
+// sequence; qsrc = where a prefix unit that needs new q rows finds them
+// (0: none needed, 1: the spare set, 2: loaded at compute time).
 struct SkUnit {
   int seq, tile, len, hg;
   int virt, sblk, soff;
+  int pre, first, qsrc;
 };
 
-// NBUF: LDS stages of the staged path (2: units alternate between them)
-template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV, int NBUF>
+// NBUF: LDS stages of the staged path (2: units alternate between them);
+// CAS: the cascade variant (no append)
+template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV, int NBUF, bool CAS>
 __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) {
   using C = DecodeCfg<KV, D, BS, G>;
   constexpr int kB = C::kB;
   constexpr int kNT = D / 16;
   static_assert(G <= 16, "at most 16 query heads per KV head");
+  static_assert(!(CAS && AP), "the cascade has no append variant");
+  // q row tiles per wave (two for prefix units), piece rows per wave
+  constexpr int CT = CAS ? 2 : 1;
+  constexpr int RW = CAS ? 16 * CT : G;
   // tokens per unit, 16-row QK tiles per unit, scores per lane (lane group
   // j holds tokens kE * j .. kE * j + kE - 1), blocks one unit spans
   constexpr int TT = kB == 1 ? 32 : 16;
@@ -225,15 +280,25 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   constexpr int kQBytes = G * D * 2;
   constexpr int kQL = STG ? (kQBytes > 1024 ? kQBytes / 1024 : 1) : C::kKSteps;
   constexpr int kQPitch = D * 2 + 16;  // bytes per q row in LDS (rows 4 banks apart)
-  static_assert(!STG || G * kQPitch <= static_cast<int>(sk_wave_lds_floats(G, D, AP) * sizeof(float)),
+  static_assert(!STG || (CAS ? 16 * CT : G) * kQPitch <= static_cast<int>(sk_wave_lds_floats(G, D, AP, CAS) * sizeof(float)),
                 "the q rows fit the wave's LDS region");
+  static_assert(!CAS || STG, "the cascade is built on the staged path");
   extern __shared__ int32_t sk_smem[];
   const int B = p.batch;
-  int32_t* s_pref = sk_smem;  // [B + 1]
+  // virtual sequences: the batch rows, or (cascade) NG group prefixes and
+  // then the B rows' tails
+  const int NG = CAS ? p.num_groups : 0;
+  const int NV = NG + B;
+  int32_t* s_pref = sk_smem;            // [NV + 1]
+  int32_t* s_aux = s_pref + NV + 1;     // cascade: [NV] table row (prefix) / first tail unit
+  int32_t* s_goff = s_aux + NV;         // cascade: [NG + 1]
+  int32_t* s_mem = s_goff + NG + 1;     // cascade: [B]
+  int32_t* s_shl = s_mem + B;           // cascade: [B] shared tokens of each row, whole units
+  int32_t* s_in = s_shl + B;            // cascade: [B] group * 32 + place of each member row, or -1
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int HW = p.heads_per_wg;
-  char* stage = reinterpret_cast<char*>(sk_smem + (B + 1 + 3) / 4 * 4);  // STG only
+  char* stage = reinterpret_cast<char*>(sk_smem + sk_plan_ints(B, CAS ? NG : -1));  // STG only
   // with two stages, unit x uses stage x % 2: the barrier after the stage
   // write of unit x + 1 already orders unit x's reads before the next
   // write into its stage, so no barrier is needed after a unit
@@ -241,17 +306,65 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   const int sbytes = STG ? static_cast<int>(sk_stage_bytes(HW, D, kB, TV)) : 0;
   float* s_out_all = reinterpret_cast<float*>(stage + NBUF * sbytes);
 
-  // ---- plan: tiles per sequence, then their exclusive prefix (in place)
-  for (int i = threadIdx.x; i < B; i += blockDim.x) {
-    int L = p.context_lens[i];
-    L = L < p.len_cap ? L : p.len_cap;
-    // append: the cache holds L - 1 tokens, plus the virtual tile
-    s_pref[i] = L > 0 ? (AP ? ((L + 14) >> 4) + 1 : (L + TT - 1) / TT) : 0;
+  // ---- plan: tiles per (virtual) sequence, then their exclusive prefix (in place)
+  if constexpr (CAS) {
+    // a row's shared tokens in whole units (at most the launch bound, so the
+    // prefix reads stay inside the first member's table); its tail is the
+    // rest. Group offsets and member ids are clamped or checked before use:
+    // inconsistent groups give wrong rows, never an access out of bounds.
+    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+      int L = p.context_lens[i];
+      L = L < p.len_cap ? L : p.len_cap;
+      int sh = p.shared_len[i];
+      sh = sh < 0 ? 0 : (sh < p.len_cap ? sh : p.len_cap);
+      sh = sh / TT * TT;
+      s_shl[i] = sh;
+      s_pref[NG + i] = L > sh ? (L - sh + TT - 1) / TT : 0;
+      s_aux[NG + i] = sh / TT;
+      s_in[i] = -1;
+    }
+    for (int i = threadIdx.x; i <= NG; i += blockDim.x) {
+      const int o = p.group_offsets[i];
+      s_goff[i] = o < 0 ? 0 : (o < B ? o : B);
+    }
+    __syncthreads();
+    const int nmem = s_goff[NG];
+    for (int k = threadIdx.x; k < nmem; k += blockDim.x) s_mem[k] = p.group_members[k];
+    __syncthreads();
+    for (int v = threadIdx.x; v < NG; v += blockDim.x) {
+      const int m0 = s_goff[v];
+      const int first = s_goff[v + 1] > m0 && m0 < nmem ? s_mem[m0] : -1;
+      const bool ok = static_cast<unsigned>(first) < static_cast<unsigned>(B);
+      s_pref[v] = ok ? s_shl[first] / TT : 0;
+      s_aux[v] = ok ? first : 0;
+    }
+    __syncthreads();
+    // member slot k -> its row's place: the group holding slot k (the last
+    // offset at or below k), if that group has a prefix part and the row
+    // fits the prefix units' RW / G members
+    for (int k = threadIdx.x; k < nmem; k += blockDim.x) {
+      const int s = s_mem[k];
+      if (static_cast<unsigned>(s) >= static_cast<unsigned>(B) || NG == 0) continue;
+      int lo = 0, hi = NG - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_goff[mid] <= k) lo = mid; else hi = mid - 1;
+      }
+      const int mi = k - s_goff[lo];
+      if (mi >= 0 && k < s_goff[lo + 1] && mi * G < RW && s_pref[lo] > 0) s_in[s] = lo * 32 + mi;
+    }
+  } else {
+    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+      int L = p.context_lens[i];
+      L = L < p.len_cap ? L : p.len_cap;
+      // append: the cache holds L - 1 tokens, plus the virtual tile
+      s_pref[i] = L > 0 ? (AP ? ((L + 14) >> 4) + 1 : (L + TT - 1) / TT) : 0;
+    }
   }
   __syncthreads();
   if (wave == 0) {
-    const int per = (B + 63) / 64;
-    const int i0 = lane * per, i1 = min(B, i0 + per);
+    const int per = (NV + 63) / 64;
+    const int i0 = lane * per, i1 = min(NV, i0 + per);
     int run = 0;
     for (int i = i0; i < i1; ++i) run += s_pref[i];
     int incl = run;
@@ -266,13 +379,24 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       s_pref[i] = acc_t;
       acc_t += c;
     }
-    if (lane == 63) s_pref[B] = incl;
+    if (lane == 63) s_pref[NV] = incl;
   }
   __syncthreads();
-  const int T = s_pref[B];
+  const int T = s_pref[NV];
   const int U = T * p.num_head_groups;  // the launch guarantees U < 2^31
   const int W = static_cast<int>(gridDim.x);
   const int w = static_cast<int>(blockIdx.x);
+  if constexpr (CAS) {
+    // the merge's row map; this workgroup writes rows w, w + W, ...
+    for (int s = w + W * static_cast<int>(threadIdx.x); s < B; s += W * static_cast<int>(blockDim.x)) {
+      const int e = s_in[s];
+      int32_t* rm = p.row_map + 4 * static_cast<int64_t>(s);
+      rm[0] = e >= 0 ? e / 32 : -1;
+      rm[1] = e >= 0 ? e % 32 : 0;
+      rm[2] = s_pref[NG + s + 1] > s_pref[NG + s] ? 1 : 0;
+      rm[3] = 0;
+    }
+  }
   int u0, u1;
   if (p.part_tiles > 0) {
     // partition mode: the range is one partition of one segment; a partition
@@ -300,7 +424,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   }
   if (u0 >= u1) {
     // no units: neutral slot-0 pieces (only when there are fewer units than workgroups)
-    const int rows = HW * G;
+    const int rows = HW * RW;
     const int64_t base = static_cast<int64_t>(w) * p.piece_slots * rows;
     for (int i = threadIdx.x; i < rows; i += blockDim.x) {
       p.piece_m[base + i] = -INFINITY;
@@ -310,7 +434,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     return;
   }
 
-  float* s_out = s_out_all + wave * sk_wave_lds_floats(G, D, AP);
+  float* s_out = s_out_all + wave * sk_wave_lds_floats(G, D, AP, CAS);
   const int col = lane & 15, j = lane >> 4;
   const int Hkv = p.num_kv_heads;
   const char* kbase = static_cast<const char*>(p.k_pool);
@@ -351,6 +475,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   struct Batch {
     int ub;
     int seq, tile, len, hg;  // append: tile = ~t for the virtual tile
+    int first;               // cascade: the first unit of its virtual sequence
     int id0, id1, id2, id3;  // the tile's blocks (the first kTB)
     int64_t slot;            // append only: slot_mapping[seq] as loaded
   };
@@ -362,14 +487,20 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     const int u = min(ub + lane, u1 - 1);
     const int hg = u / T;
     const int r = u - hg * T;
-    const int s = sk_find_seq(s_pref, B, r);
+    const int s = sk_find_seq(s_pref, NV, r);
     const int t = r - s_pref[s];
-    const int32_t* row = p.block_tables + static_cast<int64_t>(s) * p.max_blocks;
+    // cascade: a prefix reads its first member's table from token 0 on
+    // (its length: its units' tokens), a tail its own row's table from its
+    // first unit on (tile = the unit's position in the row)
+    const bool pre = CAS && s < NG;
+    const int trow = CAS ? (pre ? s_aux[s] : s - NG) : s;
+    const int ta = CAS && !pre ? t + s_aux[s] : t;
+    const int32_t* row = p.block_tables + static_cast<int64_t>(trow) * p.max_blocks;
     const bool virt = AP && t == s_pref[s + 1] - s_pref[s] - 1;
     // (a virtual tile reads no cache block; its table index could lie past
     // the table's end)
-    const int blk_a = virt ? 0 : (t * TT) / BS;
-    b.len = p.context_lens[s];
+    const int blk_a = virt ? 0 : (ta * TT) / BS;
+    b.len = pre ? (s_pref[s + 1] - s_pref[s]) * TT : p.context_lens[trow];
     b.id0 = row[blk_a];
     b.slot = AP ? p.slot_mapping[s] : -1;
     // the tile's further blocks; past the sequence's last block their
@@ -378,7 +509,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     b.id2 = kTB > 2 ? row[min(blk_a + 2, p.max_blocks - 1)] : 0;
     b.id3 = kTB > 3 ? row[min(blk_a + 3, p.max_blocks - 1)] : 0;
     b.seq = s;
-    b.tile = virt ? ~t : t;
+    b.tile = virt ? ~t : ta;
+    b.first = t == 0;
     b.hg = hg;
     return b;
   };
@@ -401,6 +533,17 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     un.virt = 0;
     un.sblk = -1;
     un.soff = 0;
+    un.pre = 0;
+    un.first = 0;
+    un.qsrc = 0;
+    if constexpr (CAS) {
+      // a prefix unit needs its segment's q rows when it is the segment's
+      // first unit, or the range's (loaded at compute time, or for the
+      // range's first unit before the ring starts)
+      un.pre = un.seq < NG;
+      un.first = __builtin_amdgcn_readlane(b.first, o);
+      un.qsrc = un.pre && !past && un.first && x != u0 ? 2 : 0;
+    }
     if constexpr (AP) {
       un.virt = un.tile < 0;
       un.tile = un.virt ? ~un.tile : un.tile;
@@ -444,7 +587,9 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // carries a fixed number of loads and no wait ever covers more than the
     // slot it consumes.
     {
-      const int64_t head0 = static_cast<int64_t>(un.seq) * p.num_q_heads + static_cast<int64_t>(g) * G;
+      // (cascade: a tail's batch row; a prefix unit loads row 0's, unused)
+      const int qseq = CAS ? (un.pre ? 0 : un.seq - NG) : un.seq;
+      const int64_t head0 = static_cast<int64_t>(qseq) * p.num_q_heads + static_cast<int64_t>(g) * G;
       if constexpr (STG) {
         // lanes past the rows' end repeat a piece (not used)
         const char* qblk = static_cast<const char*>(p.q) + head0 * D * 2;
@@ -564,73 +709,157 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   bool seg_first = true;  // reaches back to u0
   bool seg_begun = true;  // starts inside the range (set from the first unit below)
 
-  float m_w = -INFINITY;  // running reference max of head `col` (log2 domain)
-  float l_w = 0.f;        // this lane's share of head `col`'s weight sum
-  f32x4 acc[kNT];
+  // per q row tile ct (one, or two for cascade prefix units): running
+  // reference max of row `col` (log2 domain), this lane's share of its
+  // weight sum, the output accumulators
+  float m_w[CT], l_w[CT];
+  f32x4 acc[CT][kNT];
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < CT; ++ct) {
+    m_w[ct] = -INFINITY;
+    l_w[ct] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) acc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  int pre_rows = 0;  // cascade: q rows of the current prefix segment
+
+  // cascade: the q rows of prefix segment v for this wave's KV head in
+  // head group hg, as the QK B operands of the two row tiles; row r =
+  // 16 ct + col is member r / G of the group, query head r % G. Rows past
+  // the group (or a member id outside the batch) read row 0's q: their
+  // weights are forced to zero. Returns the valid rows.
+  using PreQ = u32x4[CT][C::kKSteps];
+  auto fetch_prefix_q = [&](int v, int hg, PreQ& dst) -> int {
+    const int m0 = s_goff[v];
+    const int gsz = max(0, s_goff[v + 1] - m0);
+    const int64_t gq = static_cast<int64_t>(hg * HW + wave) * G;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int r = ct * 16 + col;
+      int mem = r / G < gsz ? s_mem[m0 + r / G] : 0;
+      mem = static_cast<unsigned>(mem) < static_cast<unsigned>(B) ? mem : 0;
+      const uint16_t* qrow =
+          static_cast<const uint16_t*>(p.q) + (mem * static_cast<int64_t>(p.num_q_heads) + gq + r % G) * D;
+#pragma unroll
+      for (int i = 0; i < C::kKSteps; ++i) dst[ct][i] = *reinterpret_cast<const u32x4*>(qrow + qk_dim<kB>(i, j));
+    }
+    return min(gsz, RW / G) * G;
+  };
+  // ... into the wave's q rows in LDS (read back per unit like a tail's)
+  auto store_prefix_q = [&](const PreQ& src) {
+    char* qs = reinterpret_cast<char*>(s_out);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int i = 0; i < C::kKSteps; ++i)
+        *reinterpret_cast<u32x4*>(qs + (ct * 16 + col) * kQPitch + qk_dim<kB>(i, j) * 2) = src[ct][i];
+    }
+  };
 
   // store the segment that just ended: final output, or a partial piece.
   // Lane (col, j) holds rows 4j .. 4j + 3, head dim 16 nt + col. The append
   // variant goes through its LDS output tile (16-byte stores); the others
   // store straight from the accumulators (16 lanes write 16 consecutive
-  // dims; segment ends are rare, and this needs no LDS tile).
+  // dims; segment ends are rare, and this needs no LDS tile). Cascade: a
+  // completed segment leaves its partial (m, l, o) as state rows of its
+  // batch rows (part 0: prefix, 1: tail), a cut one a piece of RW rows.
   auto flush = [&](int seg_seq, int seg_hg, bool complete, bool ends_here, int slot) {
-    float l_head = l_w + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_w), 0x401F));
-    l_head += __shfl_xor(l_head, 32, 64);
-    const int64_t head0 = static_cast<int64_t>(seg_seq) * p.num_q_heads + static_cast<int64_t>(seg_hg * HW + wave) * G;
-    const int64_t pbase = ((static_cast<int64_t>(w) * p.piece_slots + slot) * HW + wave) * G;
-    if constexpr (AP) {
+    const int64_t pbase = ((static_cast<int64_t>(w) * p.piece_slots + slot) * HW + wave) * RW;
+    if constexpr (CAS) {
+      const bool pre = seg_seq < NG;
+      const int nrows = pre ? pre_rows : G;
+      const int64_t gq = static_cast<int64_t>(seg_hg * HW + wave) * G;
+      const int m0 = pre ? s_goff[seg_seq] : 0;
+      const int64_t part = pre ? 0 : 1;
+      // state row of wave row rr: (batch row, query head), or -1 (a member
+      // id outside the batch)
+      auto state_row = [&](int rr) -> int64_t {
+        const int srow = pre ? s_mem[m0 + rr / G] : seg_seq - NG;
+        if (static_cast<unsigned>(srow) >= static_cast<unsigned>(B)) return -1;
+        return (part * B + srow) * p.num_q_heads + gq + rr % G;
+      };
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * j + r;
-        const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
-        if (h < G) {
-          const float inv = p.v_scale / lr;
+      for (int ct = 0; ct < CT; ++ct) {
+        if (ct > 0 && !pre) break;
+        const float l_head = pair32_sum(pair16_sum(l_w[ct]));
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) s_out[h * D + nt * 16 + col] = acc[nt][r] * inv;
+        for (int r = 0; r < 4; ++r) {
+          const int rr = ct * 16 + 4 * j + r;
+          const float lr = __shfl(l_head, 4 * j + r, 64);  // lane h (row 0) holds row h's sum
+          if (rr < nrows) {
+            const float inv = p.v_scale / lr;
+            const int64_t row = complete ? state_row(rr) : pbase + rr;
+            if (row >= 0) {
+              float* po = (complete ? p.state_o : p.piece_o) + row * D + col;
+#pragma unroll
+              for (int nt = 0; nt < kNT; ++nt) po[nt * 16] = acc[ct][nt][r] * inv;
+            }
+          }
         }
-      }
-      wave_lds_sync();
-      for (int i = lane * 8; i < G * D; i += 64 * 8) {
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = s_out[i + e];
-        const int h = i / D, d = i % D;
-        if (complete) {
-          store_out8(p.out, (head0 + h) * D + d, p.out_dtype, o);
-        } else {
-          float* po = p.piece_o + (pbase + h) * D + d;
-          *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
-          *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
-        }
-      }
-      wave_lds_sync();
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * j + r;
-        const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
-        if (h < G) {
-          const float inv = p.v_scale / lr;
-          if (complete) {
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt)
-              store_out(p.out, (head0 + h) * D + nt * 16 + col, p.out_dtype, acc[nt][r] * inv);
-          } else {
-            float* po = p.piece_o + (pbase + h) * D + col;
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) po[nt * 16] = acc[nt][r] * inv;
+        if (lane < 16 && ct * 16 + lane < nrows) {
+          const int64_t row = complete ? state_row(ct * 16 + lane) : pbase + ct * 16 + lane;
+          if (row >= 0) {
+            (complete ? p.state_m : p.piece_m)[row] = m_w[ct];
+            (complete ? p.state_l : p.piece_l)[row] = l_head;
           }
         }
       }
-    }
-    if (!complete && lane < G) {
-      p.piece_m[pbase + lane] = m_w;
-      p.piece_l[pbase + lane] = l_head;
+    } else {
+      const float l_head = pair32_sum(pair16_sum(l_w[0]));
+      const int64_t head0 =
+          static_cast<int64_t>(seg_seq) * p.num_q_heads + static_cast<int64_t>(seg_hg * HW + wave) * G;
+      if constexpr (AP) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * j + r;
+          const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
+          if (h < G) {
+            const float inv = p.v_scale / lr;
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) s_out[h * D + nt * 16 + col] = acc[0][nt][r] * inv;
+          }
+        }
+        wave_lds_sync();
+        for (int i = lane * 8; i < G * D; i += 64 * 8) {
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = s_out[i + e];
+          const int h = i / D, d = i % D;
+          if (complete) {
+            store_out8(p.out, (head0 + h) * D + d, p.out_dtype, o);
+          } else {
+            float* po = p.piece_o + (pbase + h) * D + d;
+            *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
+          }
+        }
+        wave_lds_sync();
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * j + r;
+          const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
+          if (h < G) {
+            const float inv = p.v_scale / lr;
+            if (complete) {
+#pragma unroll
+              for (int nt = 0; nt < kNT; ++nt)
+                store_out(p.out, (head0 + h) * D + nt * 16 + col, p.out_dtype, acc[0][nt][r] * inv);
+            } else {
+              float* po = p.piece_o + (pbase + h) * D + col;
+#pragma unroll
+              for (int nt = 0; nt < kNT; ++nt) po[nt * 16] = acc[0][nt][r] * inv;
+            }
+          }
+        }
+      }
+      if (!complete && lane < G) {
+        p.piece_m[pbase + lane] = m_w[0];
+        p.piece_l[pbase + lane] = l_head;
+      }
     }
     if (wave == 0 && lane == 0 && p.seg_desc != nullptr) {  // (none when no segment is cut)
-      int32_t* desc = p.seg_desc + (static_cast<int64_t>(seg_hg) * B + seg_seq) * 2;
+      int32_t* desc = p.seg_desc + (static_cast<int64_t>(seg_hg) * NV + seg_seq) * 2;
       if (complete) {
         desc[0] = -1;
       } else {
@@ -647,10 +876,40 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     return (col & 1) ? (w2 >> 16) : (w2 & 0xffffu);
   };
 
+  // staged: the wave's K rows of a unit in the QK operand layout, from the
+  // unit's stage (lane (token col, j): the 16 bytes of dims qk_dim(i, j);
+  // fp8: QK tile s row `col` is token 8 (col / 4) + col % 4 + 4 s)
+  auto read_kop = [&](const char* stg, u32x4 (&kop)[STG ? kKP : 1]) {
+    if constexpr (STG) {
+      if constexpr (TT == 16) {
+        const char* ks = stg + col * kpitch + wave * D * kB;
+#pragma unroll
+        for (int i = 0; i < C::kKSteps; ++i) kop[i] = *reinterpret_cast<const u32x4*>(ks + qk_dim<2>(i, j) * kB);
+      } else {
+#pragma unroll
+        for (int s = 0; s < kSub; ++s) {
+          const int row = 8 * (col >> 2) + (col & 3) + 4 * s;
+#pragma unroll
+          for (int a = 0; a < C::kKLoads; ++a)
+            kop[s * C::kKLoads + a] =
+                *reinterpret_cast<const u32x4*>(stg + st_k(row, wave * D + qk_dim<1>(2 * a, j)));
+        }
+      }
+    }
+  };
+
   auto compute = [&](int x, const SkUnit& un, const u32x4 (&qr)[kQL], const u32x4 (&kr)[kKP],
                      const VSlot (&vr)[kVL]) {
     const int tb = AP && un.virt ? 0 : un.tile * TT;
     const int L = un.len;
+    const bool upre = CAS && un.pre;  // (uniform) a cascade prefix unit: both row tiles
+    if constexpr (CAS) {
+      if (un.qsrc == 2) {
+        PreQ qt;
+        pre_rows = fetch_prefix_q(un.seq, un.hg, qt);
+        store_prefix_q(qt);
+      }
+    }
     char* const stg = stage + (NBUF == 2 && (x & 1) ? sbytes : 0);  // this unit's stage
     char* const stg_v = stg + (stage_v - stage);
     // ---- token-major V: the unit's rows go to the stage as loaded; after
@@ -660,15 +919,16 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // head dim 16 nt + d, its group's lanes pointing at rows 4j + lane / 4,
     // dims 4 (lane % 4) ..)
     u32x4 kop[STG ? kKP : 1];
-    u32x4 qb[C::kKSteps];  // the q rows as the QK B operand (columns >= G repeat row 0)
     const uint16_t* vt_src = nullptr;
     const char* v8_src = nullptr;
+    char* const qs = reinterpret_cast<char*>(s_out);  // the wave's q rows (staged)
     if constexpr (STG) {
-      char* qs = reinterpret_cast<char*>(s_out);
+      if (!upre) {
 #pragma unroll
-      for (int i = 0; i < kQL; ++i) {
-        const int f = (64 * i + lane) * 16;
-        if (f < kQBytes) *reinterpret_cast<u32x4*>(qs + (f / (D * 2)) * kQPitch + f % (D * 2)) = qr[i];
+        for (int i = 0; i < kQL; ++i) {
+          const int f = (64 * i + lane) * 16;
+          if (f < kQBytes) *reinterpret_cast<u32x4*>(qs + (f / (D * 2)) * kQPitch + f % (D * 2)) = qr[i];
+        }
       }
 #pragma unroll
       for (int i = 0; i < kKP; ++i) {
@@ -712,26 +972,12 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         }
       }
       lds_barrier();
-      const char* qsrc = qs + (col < G ? col : 0) * kQPitch;
-#pragma unroll
-      for (int i = 0; i < C::kKSteps; ++i) qb[i] = *reinterpret_cast<const u32x4*>(qsrc + qk_dim<kB>(i, j) * 2);
+      read_kop(stg, kop);
       if constexpr (TT == 16) {
-        const char* ks = stg + col * kpitch + wave * D * kB;
-#pragma unroll
-        for (int i = 0; i < C::kKSteps; ++i) kop[i] = *reinterpret_cast<const u32x4*>(ks + qk_dim<2>(i, j) * kB);
         vt_src = reinterpret_cast<const uint16_t*>(stg_v + (4 * j + (col >> 2)) * vpitch + wave * D * kB) + 4 * (col & 3);
       } else {
-        // fp8: QK tile s row `col` is token 8 (col / 4) + col % 4 + 4 s; the
-        // PV operand of lane (d, j) is the run of head dim d over tokens
-        // 8j .. 8j + 7 (block part 8j / BS of the V stage)
-#pragma unroll
-        for (int s = 0; s < kSub; ++s) {
-          const int row = 8 * (col >> 2) + (col & 3) + 4 * s;
-#pragma unroll
-          for (int a = 0; a < C::kKLoads; ++a)
-            kop[s * C::kKLoads + a] =
-                *reinterpret_cast<const u32x4*>(stg + st_k(row, wave * D + qk_dim<1>(2 * a, j)));
-        }
+        // fp8: the PV operand of lane (d, j) is the run of head dim d over
+        // tokens 8j .. 8j + 7 (block part 8j / BS of the V stage)
         if constexpr (TV) {
           // one 8-bit transposing read per 16-dim tile: lane m of group j
           // points at row 8j + m / 2, dims 8 (m % 2) .. of the tile, and
@@ -741,66 +987,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
           v8_src = stg_v + ((8 * j) / BS) * SV + wave * D * BS + (((8 * j) % BS) / 8) * (D * 8) + col * 8;
         }
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::kKSteps; ++i) qb[i] = qr[i];
     }
-    // ---- S^T = K q^T, one 16-row tile per kSub; lane (head col, j) gets
-    // the scores of tokens kE * j + e, e = 4 * tile + row
-    f32x4 sacc[kSub];
-#pragma unroll
-    for (int s = 0; s < kSub; ++s) {
-      sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (kB == 2) {
-#pragma unroll
-        for (int i = 0; i < C::kKSteps; ++i) sacc[s] = mfma_16x16x32<QT>(TV ? kop[i] : kr[i], qb[i], sacc[s]);
-      } else {
-#pragma unroll
-        for (int a = 0; a < C::kKLoads; ++a) {
-          const u32x4 kw = STG ? kop[s * C::kKLoads + a] : kr[s * C::kKLoads + a];
-          const u32x2 b0 = e4m3x4_to_bf16x4(kw.x), b1 = e4m3x4_to_bf16x4(kw.y);
-          const u32x2 b2 = e4m3x4_to_bf16x4(kw.z), b3 = e4m3x4_to_bf16x4(kw.w);
-          sacc[s] = mfma_16x16x32<QT>(u32x4{b0.x, b0.y, b1.x, b1.y}, qb[2 * a], sacc[s]);
-          sacc[s] = mfma_16x16x32<QT>(u32x4{b2.x, b2.y, b3.x, b3.y}, qb[2 * a + 1], sacc[s]);
-        }
-      }
-    }
-    float sv[kE];
-#pragma unroll
-    for (int e = 0; e < kE; ++e) sv[e] = tb + kE * j + e < L ? sacc[e / 4][e % 4] * p.qk_scale_log2 : -INFINITY;
-    // ---- online softmax (head = col)
-    float mx = sv[0];
-#pragma unroll
-    for (int e = 1; e < kE; ++e) mx = fmaxf(mx, sv[e]);
-    mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mx), 0x401F)));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool need = col < G && mx > m_w + C::kSlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float a = need ? __builtin_amdgcn_exp2f(m_w - mx) : 1.0f;
-      m_w = need ? mx : m_w;
-      l_w *= a;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(a, 4 * j + r, 64);
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) acc[nt][r] *= ar;
-      }
-    }
-    float pw[kE];
-#pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      pw[e] = col < G ? __builtin_amdgcn_exp2f(sv[e] - m_w) : 0.f;
-      l_w += pw[e];
-    }
-    // weights as two 16-bit terms (hi + lo), the PV A operand: row = head,
-    // k = the lane's kE tokens
-    uint32_t phi[kE / 2], plo[kE / 2];
-#pragma unroll
-    for (int e = 0; e < kE; e += 2) {
-      phi[e / 2] = pack2<QT>(pw[e], pw[e + 1]);
-      plo[e / 2] = pack2<QT>(pw[e] - half_lo<QT>(phi[e / 2]), pw[e + 1] - half_hi<QT>(phi[e / 2]));
-    }
-    // ---- PV; V elements past the end are zeroed (the pool may hold
+    // ---- PV masks: V elements past the end are zeroed (the pool may hold
     // anything there, and 0 * NaN would poison the sum)
     uint32_t vmask[kE / 2];
 #pragma unroll
@@ -811,41 +999,184 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       for (int e = 0; e < kE; e += 2)
         vmask[e / 2] = (t + e < L ? 0xffffu : 0u) | (t + e + 1 < L ? 0xffff0000u : 0u);
     }
+    // ---- per q row tile ct: QK, online softmax, PV. A cascade prefix unit
+    // runs both tiles on the same K and V operands, one after the other
+    // (interleaving the two chains needs more than the 256 VGPRs of two
+    // waves per SIMD: the build spilled 21-59 of them).
+    // QK: S^T = K q^T, one 16-row tile per kSub; lane (row col, j) gets the
+    // scores of tokens kE * j + e, e = 4 * tile + row
+    auto qk = [&](auto ctc, f32x4 (&sacc)[kSub]) {
+      constexpr int ct = decltype(ctc)::value;
+      // the q rows as the QK B operand (a wave's G heads: columns >= G
+      // repeat row 0; a prefix segment: rows 16 ct ..)
+      u32x4 qb[C::kKSteps];
+      if constexpr (STG) {
+        const char* qsrc = qs + (upre ? ct * 16 + col : (col < G ? col : 0)) * kQPitch;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      if constexpr (TT == 16) {
-        u32x2 vop;
-        if constexpr (TV) {
-          vop = lds_read_tr16(vt_src + 16 * nt);
-        } else {
-          vop = vr[nt];
-          if constexpr (AP) {
-            if (un.virt) vop = u32x2{virt_v(vr[nt]), 0u};
-          }
-        }
-        vop.x &= vmask[0];
-        vop.y &= vmask[1];
-        acc[nt] = mfma_16x16x16<QT>(u32x2{phi[0], phi[1]}, vop, acc[nt]);
-        acc[nt] = mfma_16x16x16<QT>(u32x2{plo[0], plo[1]}, vop, acc[nt]);
+        for (int i = 0; i < C::kKSteps; ++i) qb[i] = *reinterpret_cast<const u32x4*>(qsrc + qk_dim<kB>(i, j) * 2);
       } else {
-        u32x2 b0, b1;  // the lane's 8 tokens of its head dim as bf16
-        if constexpr (TV) {
-          const u32x2 codes = lds_read_tr8(v8_src + 16 * nt);  // tokens 8j .. 8j + 7, dim col
-          b0 = e4m3x4_to_bf16x4(codes.x);
-          b1 = e4m3x4_to_bf16x4(codes.y);
+#pragma unroll
+        for (int i = 0; i < C::kKSteps; ++i) qb[i] = qr[i];
+      }
+#pragma unroll
+      for (int s = 0; s < kSub; ++s) {
+        sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kB == 2) {
+#pragma unroll
+          for (int i = 0; i < C::kKSteps; ++i) sacc[s] = mfma_16x16x32<QT>(TV ? kop[i] : kr[i], qb[i], sacc[s]);
         } else {
-          u32x2 vv;
-          if constexpr (STG) {
-            vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * 8);
-          } else {
-            vv = vr[nt];
+#pragma unroll
+          for (int a = 0; a < C::kKLoads; ++a) {
+            const u32x4 kw = STG ? kop[s * C::kKLoads + a] : kr[s * C::kKLoads + a];
+            const u32x2 b0 = e4m3x4_to_bf16x4(kw.x), b1 = e4m3x4_to_bf16x4(kw.y);
+            const u32x2 b2 = e4m3x4_to_bf16x4(kw.z), b3 = e4m3x4_to_bf16x4(kw.w);
+            sacc[s] = mfma_16x16x32<QT>(u32x4{b0.x, b0.y, b1.x, b1.y}, qb[2 * a], sacc[s]);
+            sacc[s] = mfma_16x16x32<QT>(u32x4{b2.x, b2.y, b3.x, b3.y}, qb[2 * a + 1], sacc[s]);
           }
-          b0 = e4m3x4_to_bf16x4(vv.x);
-          b1 = e4m3x4_to_bf16x4(vv.y);
         }
-        const u32x4 vop = {b0.x & vmask[0], b0.y & vmask[1], b1.x & vmask[2], b1.y & vmask[3]};
-        acc[nt] = mfma_16x16x32<QT>(u32x4{phi[0], phi[1], phi[2], phi[3]}, vop, acc[nt]);
-        acc[nt] = mfma_16x16x32<QT>(u32x4{plo[0], plo[1], plo[2], plo[3]}, vop, acc[nt]);
+      }
+    };
+    // online softmax (row = col); rows holding a q row: the wave's G heads,
+    // or a prefix segment's rows. Weights as two 16-bit terms (hi + lo), the
+    // PV A operand: row = q row, k = the lane's kE tokens.
+    auto softmax = [&](auto ctc, const f32x4 (&sacc)[kSub], uint32_t (&phi)[kE / 2], uint32_t (&plo)[kE / 2]) {
+      constexpr int ct = decltype(ctc)::value;
+      const bool rok = CAS && upre ? ct * 16 + col < pre_rows : col < G;
+      float sv[kE];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) sv[e] = tb + kE * j + e < L ? sacc[e / 4][e % 4] * p.qk_scale_log2 : -INFINITY;
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < kE; ++e) mx = fmaxf(mx, sv[e]);
+      mx = pair32_max(pair16_max(mx));
+      const bool need = rok && mx > m_w[ct] + C::kSlack;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float a = need ? __builtin_amdgcn_exp2f(m_w[ct] - mx) : 1.0f;
+        m_w[ct] = need ? mx : m_w[ct];
+        l_w[ct] *= a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(a, 4 * j + r, 64);
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) acc[ct][nt][r] *= ar;
+        }
+      }
+      float pw[kE];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) {
+        pw[e] = rok ? __builtin_amdgcn_exp2f(sv[e] - m_w[ct]) : 0.f;
+        l_w[ct] += pw[e];
+      }
+#pragma unroll
+      for (int e = 0; e < kE; e += 2) {
+        phi[e / 2] = pack2<QT>(pw[e], pw[e + 1]);
+        plo[e / 2] = pack2<QT>(pw[e] - half_lo<QT>(phi[e / 2]), pw[e + 1] - half_hi<QT>(phi[e / 2]));
+      }
+    };
+    // PV of tile 0
+    auto pv = [&](auto ntc, const uint32_t (&phi)[CT][kE / 2], const uint32_t (&plo)[CT][kE / 2]) {
+      constexpr int NT = decltype(ntc)::value;
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        if constexpr (TT == 16) {
+          u32x2 vop;
+          if constexpr (TV) {
+            vop = lds_read_tr16(vt_src + 16 * nt);
+          } else {
+            vop = vr[nt];
+            if constexpr (AP) {
+              if (un.virt) vop = u32x2{virt_v(vr[nt]), 0u};
+            }
+          }
+          vop.x &= vmask[0];
+          vop.y &= vmask[1];
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            acc[ct][nt] = mfma_16x16x16<QT>(u32x2{phi[ct][0], phi[ct][1]}, vop, acc[ct][nt]);
+            acc[ct][nt] = mfma_16x16x16<QT>(u32x2{plo[ct][0], plo[ct][1]}, vop, acc[ct][nt]);
+          }
+        } else {
+          u32x2 b0, b1;  // the lane's 8 tokens of its head dim as bf16
+          if constexpr (TV) {
+            const u32x2 codes = lds_read_tr8(v8_src + 16 * nt);  // tokens 8j .. 8j + 7, dim col
+            b0 = e4m3x4_to_bf16x4(codes.x);
+            b1 = e4m3x4_to_bf16x4(codes.y);
+          } else {
+            u32x2 vv;
+            if constexpr (STG) {
+              vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * 8);
+            } else {
+              vv = vr[nt];
+            }
+            b0 = e4m3x4_to_bf16x4(vv.x);
+            b1 = e4m3x4_to_bf16x4(vv.y);
+          }
+          const u32x4 vop = {b0.x & vmask[0], b0.y & vmask[1], b1.x & vmask[2], b1.y & vmask[3]};
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            acc[ct][nt] = mfma_16x16x32<QT>(u32x4{phi[ct][0], phi[ct][1], phi[ct][2], phi[ct][3]}, vop, acc[ct][nt]);
+            acc[ct][nt] = mfma_16x16x32<QT>(u32x4{plo[ct][0], plo[ct][1], plo[ct][2], plo[ct][3]}, vop, acc[ct][nt]);
+          }
+        }
+      }
+    };
+    // PV of tile 1 alone (its own V operand reads)
+    auto pv1 = [&](const uint32_t (&phi)[CT][kE / 2], const uint32_t (&plo)[CT][kE / 2]) {
+      if constexpr (CT > 1) {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          if constexpr (TT == 16) {
+            u32x2 vop;
+            if constexpr (TV) {
+              vop = lds_read_tr16(vt_src + 16 * nt);
+            } else {
+              vop = vr[nt];
+            }
+            vop.x &= vmask[0];
+            vop.y &= vmask[1];
+            acc[1][nt] = mfma_16x16x16<QT>(u32x2{phi[1][0], phi[1][1]}, vop, acc[1][nt]);
+            acc[1][nt] = mfma_16x16x16<QT>(u32x2{plo[1][0], plo[1][1]}, vop, acc[1][nt]);
+          } else {
+            u32x2 b0, b1;
+            if constexpr (TV) {
+              const u32x2 codes = lds_read_tr8(v8_src + 16 * nt);
+              b0 = e4m3x4_to_bf16x4(codes.x);
+              b1 = e4m3x4_to_bf16x4(codes.y);
+            } else {
+              u32x2 vv;
+              if constexpr (STG) {
+                vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * 8);
+              } else {
+                vv = vr[nt];
+              }
+              b0 = e4m3x4_to_bf16x4(vv.x);
+              b1 = e4m3x4_to_bf16x4(vv.y);
+            }
+            const u32x4 vop = {b0.x & vmask[0], b0.y & vmask[1], b1.x & vmask[2], b1.y & vmask[3]};
+            acc[1][nt] = mfma_16x16x32<QT>(u32x4{phi[1][0], phi[1][1], phi[1][2], phi[1][3]}, vop, acc[1][nt]);
+            acc[1][nt] = mfma_16x16x32<QT>(u32x4{plo[1][0], plo[1][1], plo[1][2], plo[1][3]}, vop, acc[1][nt]);
+          }
+        }
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    uint32_t phi[CT][kE / 2], plo[CT][kE / 2];
+    {
+      f32x4 s0[kSub];
+      qk(I0{}, s0);
+      softmax(I0{}, s0, phi[0], plo[0]);
+      pv(I1{}, phi, plo);
+    }
+    if constexpr (CAS) {
+      if (upre) {
+        // (the K operand is read again: holding it across the first tile's
+        // softmax and PV costs more registers than the reads)
+        read_kop(stg, kop);
+        f32x4 s1[kSub];
+        qk(I1{}, s1);
+        softmax(I1{}, s1, phi[1], plo[1]);
+        pv1(phi, plo);
       }
     }
     // ---- append (dim-major V): write the newest token's row into its cache
@@ -876,10 +1207,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       if (x + 1 < u1) {
         seg_first = false;
         seg_begun = true;
-        m_w = -INFINITY;
-        l_w = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < CT; ++ct) {
+          m_w[ct] = -INFINITY;
+          l_w[ct] = 0.f;
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) acc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
   };
@@ -896,55 +1230,63 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     }
   };
 
-  // ---- the ring: units x + 1 and x + 2 in flight while x is computed.
-  // Loads are unconditional: past the range they repeat the last unit (an
-  // L2 hit; one location when staged), so every path through the
-  // loop carries the same loads.
-  // Batches: an outer step covers 63 units (21 ring iterations); its batch
-  // holds the units it loads (uk + 2 .. uk + 65), and the next step's batch
+  // ---- the ring: unit x + 1 in flight while x is computed (measured: a
+  // third slot, two units in flight, was 1-5% slower on every workload and
+  // held ~40 more VGPRs). Loads are unconditional: past the range they
+  // repeat the last unit (an L2 hit; one location when staged), so every
+  // path through the loop carries the same loads.
+  // Batches: an outer step covers 62 units (31 ring iterations); its batch
+  // holds the units it loads (uk + 1 .. uk + 64), and the next step's batch
   // is requested when the step starts.
-  u32x4 q0[kQL], q1[kQL], q2[kQL];
-  u32x4 k0[kSub * C::kKLoads], k1[kSub * C::kKLoads], k2[kSub * C::kKLoads];
-  VSlot v0[kVL], v1[kVL], v2[kVL];
+  u32x4 q0[kQL], q1[kQL];
+  u32x4 k0[kSub * C::kKLoads], k1[kSub * C::kKLoads];
+  VSlot v0[kVL], v1[kVL];
   const int ulast = u1 - 1;
   Batch cur = resolve(u0);
-  Batch nxt = resolve(min(u0 + 2, ulast));
-  // the prologue issues its loads in the loop's order (K then V, unit by
-  // unit), so the wait counts the compiler derives for the loop hold on
-  // entry too
+  Batch nxt = resolve(min(u0 + 1, ulast));
+  // cascade: the range's first unit, if a prefix unit, needs its segment's
+  // q rows: loaded ahead of the ring's loads (so waiting for them waits
+  // for nothing else) and stored once those are out
+  PreQ q_first;
+  const int v_first = CAS ? __builtin_amdgcn_readlane(cur.seq, 0) : 0;
+  if constexpr (CAS) {
+    if (v_first < NG) pre_rows = fetch_prefix_q(v_first, __builtin_amdgcn_readlane(cur.hg, 0), q_first);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the prologue issues its loads in the loop's order (K then V), so the
+  // wait counts the compiler derives for the loop hold on entry too
   SkUnit n0 = load_unit(cur, u0, q0, k0, v0);
   __builtin_amdgcn_sched_barrier(0);
-  SkUnit n1 = load_unit(cur, u0 + 1, q1, k1, v1);
-  __builtin_amdgcn_sched_barrier(0);
-  seg_begun = n0.tile == 0;
+  if constexpr (CAS) {
+    if (v_first < NG) store_prefix_q(q_first);
+  }
+  seg_begun = CAS ? n0.first != 0 : n0.tile == 0;
   int uk = u0;
   do {
     cur = nxt;
-    nxt = resolve(min(uk + 65, ulast));
-    const int uend = min(uk + 63, u1);
+    nxt = resolve(min(uk + 63, ulast));
+    const int uend = min(uk + 62, u1);
     int u = uk;
     do {
-      SkUnit n2 = load_unit(cur, u + 2, q2, k2, v2);
+      SkUnit n1 = load_unit(cur, u + 1, q1, k1, v1);
       compute(u, n0, q0, k0, v0);
       unit_barrier();
-      n0 = load_unit(cur, u + 3, q0, k0, v0);
+      n0 = load_unit(cur, u + 2, q0, k0, v0);
       if (u + 1 <= ulast) compute(u + 1, n1, q1, k1, v1);
       unit_barrier();
-      n1 = load_unit(cur, u + 4, q1, k1, v1);
-      if (u + 2 <= ulast) compute(u + 2, n2, q2, k2, v2);
-      unit_barrier();
-      u += 3;
+      u += 2;
     } while (u < uend);
-    uk += 63;
+    uk += 62;
   } while (uk <= ulast);
 }
 
-// One build of the balanced kernel (NBUF stages).
-template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV, int NBUF>
+// One build of the balanced kernel (NBUF stages), or of its cascade variant.
+template <typename KV, typename QT, int D, int BS, int G, bool AP, bool TV, int NBUF, bool CAS = false>
 hipError_t launch_decode_sk_n(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
   const int HW = p.heads_per_wg;
-  const size_t lds = sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes, TV, NBUF, AP);
-  const void* fn = reinterpret_cast<const void*>(paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>);
+  const size_t lds =
+      sk_lds_bytes(p.batch, HW, G, D, TV || KV::kBytes == 1, KV::kBytes, TV, NBUF, AP, CAS ? p.num_groups : -1);
+  const void* fn = reinterpret_cast<const void*>(paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF, CAS>);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -961,7 +1303,7 @@ hipError_t launch_decode_sk_n(const SkParams& p, int cus, int max_wgs, hipStream
   const int lb = static_cast<int>((lds + 4095) / 4096);
   const int occ = occupancy.get(HW, lb, [&]() {
     int n = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF, CAS>,
                                                      64 * HW, lds);
     return e == hipSuccess ? n : 0;
   });
@@ -974,7 +1316,8 @@ hipError_t launch_decode_sk_n(const SkParams& p, int cus, int max_wgs, hipStream
   int W = p.part_tiles > 0 ? max_wgs : used_cus * occ;
   W = W < max_wgs ? W : max_wgs;
   *wgs = W;
-  hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF>), dim3(W), dim3(64 * HW), lds, stream, p);
+  hipLaunchKernelGGL((paged_decode_sk_kernel<KV, QT, D, BS, G, AP, TV, NBUF, CAS>), dim3(W), dim3(64 * HW), lds,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -1030,6 +1373,46 @@ SkLaunch select_decode_sk(int D, int BS, int G, bool append) {
       case 128: return select_decode_sk_bs<KV, QT, 128, false, TV>(BS, G);
       default: return nullptr;
     }
+  }
+}
+
+// ---- the cascade variant (pa_decode_shared)
+template <typename KV, typename QT, int D, int BS, int G, bool TV>
+hipError_t launch_decode_cas(const SkParams& p, int cus, int max_wgs, hipStream_t stream, int* wgs) {
+  if constexpr (TV || KV::kBytes == 1) {
+    if (p.stage_bufs > 1) return launch_decode_sk_n<KV, QT, D, BS, G, false, TV, 2, true>(p, cus, max_wgs, stream, wgs);
+  }
+  return launch_decode_sk_n<KV, QT, D, BS, G, false, TV, 1, true>(p, cus, max_wgs, stream, wgs);
+}
+
+// (built on the staged path: token-major V, or fp8 pools)
+template <typename KV, typename QT, int D, int BS, bool TV>
+SkLaunch select_decode_cas_g(int G) {
+  static_assert(TV || KV::kBytes == 1, "the cascade is built on the staged path");
+  switch (G) {
+    case 1: return &launch_decode_cas<KV, QT, D, BS, 1, TV>;
+    case 2: return &launch_decode_cas<KV, QT, D, BS, 2, TV>;
+    case 4: return &launch_decode_cas<KV, QT, D, BS, 4, TV>;
+    case 8: return &launch_decode_cas<KV, QT, D, BS, 8, TV>;
+    default: return nullptr;
+  }
+}
+
+template <typename KV, typename QT, bool TV>
+SkLaunch select_decode_cas(int D, int BS, int G) {
+  auto by_bs = [&](auto d) -> SkLaunch {
+    constexpr int kD = decltype(d)::value;
+    switch (BS) {
+      case 8: return select_decode_cas_g<KV, QT, kD, 8, TV>(G);
+      case 16: return select_decode_cas_g<KV, QT, kD, 16, TV>(G);
+      case 32: return select_decode_cas_g<KV, QT, kD, 32, TV>(G);
+      default: return nullptr;
+    }
+  };
+  switch (D) {
+    case 64: return by_bs(std::integral_constant<int, 64>{});
+    case 128: return by_bs(std::integral_constant<int, 128>{});
+    default: return nullptr;
   }
 }
 

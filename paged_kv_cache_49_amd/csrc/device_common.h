@@ -121,6 +121,48 @@ __device__ __forceinline__ f32x4 mfma_16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // Output element conversion by runtime dtype code (0 f16, 1 bf16, 2 f32).
+// Max / sum over the lane pairs (l, l ^ 16) and (l, l ^ 32) on the VALU.
+// v_permlane16_swap / v_permlane32_swap exchange rows of 16 (32) lanes
+// between two registers; given x in both, every lane ends with its own x
+// in one and its partner's in the other, the order depending on the lane
+// (checked on gfx950), so the max or sum of the two is the pair's, equal on
+// both lanes (a + b = b + a). Same results as ds_swizzle / ds_bpermute,
+// without their LDS round trips. Written as inline asm (an exchange of two
+// registers, no memory access): the compiler's builtin folds max(r0, r1) of
+// its two results to r0, which the hardware does not return. The s_nop
+// gives the two wait states the compiler puts between a VALU write of an
+// operand and these instructions.
+__device__ __forceinline__ void pair_swap16(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void pair_swap32(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float pair16_max(float x) {
+  float a, b;
+  pair_swap16(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  float a, b;
+  pair_swap32(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  float a, b;
+  pair_swap16(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  float a, b;
+  pair_swap32(x, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ void store_out(void* out, int64_t idx, int dtype, float v) {
   if (dtype == 2) {
     static_cast<float*>(out)[idx] = v;

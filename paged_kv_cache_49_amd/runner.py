@@ -33,9 +33,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (BALANCED, BlockManager, KVCache, copy_blocks, prepare_decode, prepare_decode_append,
-               prepare_decode_shared,
-               decode_workspace_size, reshape_and_cache)
+from . import (BALANCED, BlockManager, KVCache, copy_blocks, decode_shared_workspace_size, decode_workspace_size,
+               prepare_decode, prepare_decode_append, prepare_decode_shared, reshape_and_cache)
 
 
 class _Staging:
@@ -264,7 +263,10 @@ class StepTiming:
 
 
 def workspace_for(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
-                  partition_size: int, device="cuda") -> Optional[torch.Tensor]:
+                  partition_size: int, device="cuda", shared: bool = False) -> Optional[torch.Tensor]:
+    """A workspace for decode calls of these sizes (shared=True: one that
+    also serves decode_shared)."""
+    size = decode_shared_workspace_size if shared else decode_workspace_size
     with torch.cuda.device(device):
-        n = decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size)
+        n = size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None

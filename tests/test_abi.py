@@ -430,8 +430,10 @@ def _decode_status(cache, **kw):
     (dict(part=-1), dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR), _lib.PA_ERR_INVALID_ARGUMENT),  # no workspace
     (dict(part=-1, B=20000, max_ctx=16), dict(v_layout=_lib.PA_LAYOUT_DIM_MAJOR),
      _lib.PA_ERR_UNSUPPORTED),                                   # prefix does not fit LDS
-    (dict(part=-1, B=20288, max_ctx=16), dict(), _lib.PA_ERR_UNSUPPORTED),  # token-major: beyond 160 KiB
-    (dict(part=-1, B=20287, max_ctx=16), dict(), _lib.PA_ERR_INVALID_ARGUMENT),  # fits; no workspace
+    # token-major, 8 KV heads, G 4, D 128: tile prefix 16 * ceil((B + 1) / 4) bytes + one stage (66304) + 8 wave
+    # regions of 4 q rows (8704) is at most 160 KiB up to B = 22207
+    (dict(part=-1, B=22208, max_ctx=16), dict(), _lib.PA_ERR_UNSUPPORTED),  # token-major: beyond 160 KiB
+    (dict(part=-1, B=22207, max_ctx=16), dict(), _lib.PA_ERR_INVALID_ARGUMENT),  # fits; no workspace
 ])
 def test_decode_rejects_bad_arguments_before_launch(kw, cache_kw, want):
     assert _decode_status(_fake_cache(**cache_kw), **kw) == want

@@ -132,14 +132,79 @@ def test_shared_token_major_v(gpu, kv, D, bs, G, hkv, ps):
     assert sp.num_groups >= 2
 
 
-def test_shared_prefix_sharing_workload(gpu):
+# The cascade (the balanced kernel over the groups' prefixes and the rows'
+# tails, merged per row): groups of at most 32 / G rows on token-major V or
+# fp8 pools, forced with PA_SHARED_PATH=cascade (an error if a case could
+# not take it). Shapes: one and two head groups per workgroup set (Hkv 16),
+# 1, 2, 4 and 8 KV heads per workgroup (Hkv 3 -> 1), fp8 prefixes rounded
+# down to 32-token units (granule 16), short prefixes (a workgroup's range
+# then crosses several prefix segments), a batch with fewer units than
+# workgroups, block sizes 8 / 16 / 32.
+CAS_CASES = [
+    # kv, D, bs, G, hkv, ps, V layout, prompt lengths, samples per prompt
+    ("bf16", 128, 16, 4, 8, 256, "token", [1100, 700, 2000, 90, 1301], [3, 1, 8, 4, 5]),
+    ("f16", 64, 8, 8, 2, 16, "token", [300, 40, 77, 129], [4, 3, 2, 4]),
+    ("bf16", 128, 32, 1, 4, 32, "token", [600, 33, 95], [32, 5, 2]),
+    ("fp8", 128, 16, 8, 4, 16, "dim", [1100, 48, 400], [4, 3, 2]),
+    ("fp8", 64, 32, 4, 16, 64, "token", [700, 200, 65], [8, 2, 3]),
+    ("bf16", 128, 16, 2, 16, 16, "token", [50, 20, 33, 17, 64, 18], [16, 2, 3, 5, 2, 7]),
+    ("f16", 128, 16, 4, 8, 16, "token", [40], [2]),
+    ("fp8", 128, 8, 2, 8, 16, "token", [513, 256, 31], [16, 4, 9]),
+    ("bf16", 64, 16, 2, 3, 16, "token", [100, 70], [6, 3]),
+]
+
+
+@pytest.mark.parametrize("kv,D,bs,G,hkv,ps,layout,prompts,samples", CAS_CASES, ids=lambda c: str(c))
+def test_shared_cascade(gpu, monkeypatch, kv, D, bs, G, hkv, ps, layout, prompts, samples):
+    monkeypatch.setenv("PA_SHARED_PATH", "cascade")
+    sp = _run(4300 + D + bs + G + hkv, prompts, samples, 40, G, hkv, D, bs, kv, ps,
+              what=f"cascade {kv} D{D} bs{bs} G{G} Hkv{hkv}", v_layout=layout)
+    assert sp.num_groups >= 1 and sp.max_group_size * G <= 32
+
+
+def test_shared_cascade_refuses_large_groups(gpu, monkeypatch):
+    """A group of more than 32 / G rows has no cascade: forced, the call
+    fails; by default it takes the shared-prefix partition kernels."""
+    monkeypatch.setenv("PA_SHARED_PATH", "cascade")
+    with pytest.raises(pa.Unsupported):
+        _run(4400, [300, 200], [9, 2], 20, 4, 8, 128, 16, "bf16", 16, what="cascade, 9 x 4 rows", v_layout="token")
+    monkeypatch.delenv("PA_SHARED_PATH")
+    _run(4400, [300, 200], [9, 2], 20, 4, 8, 128, 16, "bf16", 16, what="9 x 4 rows, default", v_layout="token")
+
+
+def test_shared_cascade_matches_partition_path(gpu, monkeypatch):
+    """The same call on both paths (cascade and partition kernels) agrees to
+    the parity tolerance on every row."""
+    kw = dict(seed=4500, prompts=[900, 333, 1500], samples=[8, 3, 6], tail_max=70, G=4, hkv=8, D=128, bs=16,
+              kv="bf16", v_layout="token")
+    bm, cache, seqs, tables, lens, q, mb = _build(kw["seed"], kw["prompts"], kw["samples"], kw["tail_max"], kw["G"],
+                                                  kw["hkv"], kw["D"], kw["bs"], kw["kv"], kw["v_layout"])
+    B = len(seqs)
+    sp = bm.shared_prefixes(list(range(B)), 256)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+    scale = float(np.float32(1.0 / np.sqrt(kw["D"])))
+    args = (cache, q.cuda(), dev(tables), dev(lens), int(lens.max()), scale, 256, dev(sp.offsets), dev(sp.members),
+            dev(sp.shared_len), sp.num_groups, sp.max_group_size, sp.max_shared_len, sp.min_shared_len)
+    outs = {}
+    for path in ("cascade", "partition"):
+        monkeypatch.setenv("PA_SHARED_PATH", path)
+        say(f"shared: {path} path")
+        outs[path] = pa.decode_shared(*args, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    H.assert_close(outs["cascade"].cpu().double().numpy(), outs["partition"].cpu().double().numpy(),
+                   what="cascade vs partition path")
+
+
+@pytest.mark.parametrize("layout", ["dim", "token"])
+def test_shared_prefix_sharing_workload(gpu, layout):
     """The 16 prompts x 8 samples workload (2048 + r shared tokens, tails
-    U[0, 256], one new token), partitions of 512, all rows vs the oracle."""
+    U[0, 256], one new token), partitions of 512, all rows vs the oracle
+    (token-major V: the cascade)."""
     wl = synth.prefix_sharing(partial_tail=True)
     P, S, hkv, D, bs = wl.prompts, wl.samples, wl.num_kv_heads, wl.head_dim, wl.block_size
-    say("shared: prefix-sharing workload")
+    say(f"shared: prefix-sharing workload, V {layout}")
     bm = pa.BlockManager(wl.num_blocks, bs, wl.free_order)
-    cache = pa.KVCache.allocate(wl.num_blocks, bs, hkv, D, "bf16", fill=float("nan"), v_layout="dim")
+    cache = pa.KVCache.allocate(wl.num_blocks, bs, hkv, D, "bf16", fill=float("nan"), v_layout=layout)
     for p in range(P):
         k, v = wl.prefix_kv(p)
         sl, _ = bm.alloc(p * S, len(k))
@@ -188,16 +253,17 @@ def test_no_groups_is_plain_decode(gpu):
     H.assert_close(got.cpu().double().numpy(), H.oracle_contiguous(wl), what="no groups")
 
 
-def test_runner_shared_steps(gpu):
+@pytest.mark.parametrize("layout", ["dim", "token"])
+def test_runner_shared_steps(gpu, layout):
     """PagedBatch.step(shared=True): groups computed from the block manager
     at every step, uploaded with the step's metadata; two steps in a row
     against the oracle."""
     from paged_kv_cache_49_amd.runner import PagedBatch, workspace_for
     wl = synth.prefix_sharing(prompts=4, samples=5, prefix=1024, partial_tail=True, max_tail=60)
     P, S, hkv, D, bs = wl.prompts, wl.samples, wl.num_kv_heads, wl.head_dim, wl.block_size
-    say("shared: runner steps")
+    say(f"shared: runner steps, V {layout}")
     bm = pa.BlockManager(wl.num_blocks + 64, bs, None)
-    cache = pa.KVCache.allocate(wl.num_blocks + 64, bs, hkv, D, "bf16", fill=float("nan"), v_layout="dim")
+    cache = pa.KVCache.allocate(wl.num_blocks + 64, bs, hkv, D, "bf16", fill=float("nan"), v_layout=layout)
     mb = int(-(-(int(wl.prefix_len.max() + wl.tail_len.max()) + 4) // bs))
     batch = PagedBatch(bm, [cache], mb, P * S)
     for p in range(P):
@@ -214,7 +280,7 @@ def test_runner_shared_steps(gpu):
             own_k[p * S + i], own_v[p * S + i] = [kt[:n]], [vt[:n]]
     B = P * S
     rng = np.random.default_rng(11)
-    ws = workspace_for(B, wl.num_q_heads, hkv, D, mb * bs, 512)
+    ws = workspace_for(B, wl.num_q_heads, hkv, D, mb * bs, 512, shared=True)
     for step in range(2):
         kn = _values(rng, (B, hkv, D), "bf16")
         vn = _values(rng, (B, hkv, D), "bf16")
