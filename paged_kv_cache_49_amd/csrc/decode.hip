@@ -100,12 +100,12 @@ constexpr int kMergeGroups = 16;
 // k_step, ... (up to wl) of one segment, query head hq, head dims 8c..8c+7.
 // The segment's descriptor (written by the balanced kernel, see
 // decode_sk_kernel.h) names the workgroups wf..wl that hold its pieces:
-// wf's in slot first_slot, the others' in slot 0. Up to 8 pieces are read
-// per round of loads.
+// wf's in slot first_slot, the others' in slot 0. Up to kChunk pieces are
+// read per round of loads.
+template <int kChunk = 8>
 __device__ __forceinline__ void merge_pieces(const SkMergeParams& p, int HWG, int hq, int c, int wf, int wl,
                                              int first_slot, int k_first, int k_step, float& run_m, float& den,
                                              float (&num)[8]) {
-  constexpr int kChunk = 8;
   const int D = p.head_dim;
   for (int k0 = k_first; wf + k0 <= wl; k0 += k_step * kChunk) {
     float pm[kChunk], pl[kChunk];
@@ -233,9 +233,12 @@ struct CasMergeParams {
 };
 
 constexpr int kCasPieceRows = 32;  // piece rows per wave (two 16-row tiles)
+constexpr int kCasMergeGroups = 4;  // piece groups of a cascade merge workgroup
 
-// grid = B x num_kv_heads (row-major), one thread per 8 head dims of each
-// query head of the KV head
+// grid = B x num_kv_heads (row-major); kCasMergeGroups groups of G x D / 8
+// threads (one per 8 head dims of each query head of the KV head): group g
+// merges pieces g, g + 4, ... of each part (a state row counts as group 0's
+// one piece), then group 0 combines the four partial merges through LDS.
 __global__ __launch_bounds__(512) void decode_cascade_merge_kernel(const CasMergeParams p) {
   const SkMergeParams& m = p.pieces;
   const int G = m.group;
@@ -249,33 +252,41 @@ __global__ __launch_bounds__(512) void decode_cascade_merge_kernel(const CasMerg
   const int g = static_cast<int>(blockIdx.x) % hkv;
   const int hg = g / HW, wave = g % HW;
   const int t = static_cast<int>(threadIdx.x);
-  const int h = t / tpr;
+  const int per = G * tpr;  // threads per piece group
+  const int pg = t / per;
+  const int h = (t % per) / tpr;
   const int c = t % tpr;
-  if (h >= G) return;
+  const bool active = pg < kCasMergeGroups;
   const int hq = wave * G + h;
   const int64_t head = static_cast<int64_t>(hg) * HWG + hq;
   const int64_t orow = static_cast<int64_t>(s) * m.num_q_heads + head;
   const int L = min(m.context_lens[s], m.len_cap);
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (L <= 0) {
-    store_out8(m.out, orow * D + 8 * c, m.out_dtype, o);
+    if (active && pg == 0) store_out8(m.out, orow * D + 8 * c, m.out_dtype, o);
     return;
   }
   const int NG = p.num_groups;
   const int NV = NG + B;
+  // the row map and both descriptors (the prefix's at a valid place even
+  // for rows without a prefix: the cascade runs with groups)
   const int32_t* rm = p.row_map + 4 * static_cast<int64_t>(s);
+  const int32_t* tdesc = m.seg_desc + (static_cast<int64_t>(hg) * NV + NG + s) * 2;
   const int gi = rm[0], mi = rm[1], has_tail = rm[2];
+  const int32_t t0 = tdesc[0], t1 = tdesc[1];
+  const int32_t* pdesc = m.seg_desc + (static_cast<int64_t>(hg) * NV + (gi >= 0 ? gi : 0)) * 2;
+  const int32_t p0 = pdesc[0], p1 = pdesc[1];
   float run_m = -INFINITY, den = 0.f;
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // part `part` of segment v; r = the row among the wave's piece rows
-  auto add_part = [&](int part, int v, int r) {
-    const int32_t* desc = m.seg_desc + (static_cast<int64_t>(hg) * NV + v) * 2;
-    const int32_t d0 = desc[0], d1 = desc[1];
+  // part `part` with descriptor {d0, d1}; r = the row among the wave's
+  // piece rows
+  auto add_part = [&](int part, int32_t d0, int32_t d1, int r) {
     if (d0 != -1) {
-      merge_pieces(m, m.heads_per_wg * kCasPieceRows, wave * kCasPieceRows + r, c, d0 & 0x7fffffff, d1,
-                   static_cast<int>(static_cast<uint32_t>(d0) >> 31), 0, 1, run_m, den, num);
+      merge_pieces<4>(m, HW * kCasPieceRows, wave * kCasPieceRows + r, c, d0 & 0x7fffffff, d1,
+                      static_cast<int>(static_cast<uint32_t>(d0) >> 31), pg, kCasMergeGroups, run_m, den, num);
       return;
     }
+    if (pg != 0) return;
     const int64_t row = (static_cast<int64_t>(part) * B + s) * m.num_q_heads + head;
     const float pm = p.state_m[row];
     const float pl = p.state_l[row];
@@ -290,10 +301,34 @@ __global__ __launch_bounds__(512) void decode_cascade_merge_kernel(const CasMerg
     for (int e = 0; e < 8; ++e) num[e] = fmaf(wt, v8[e], num[e] * r0);
     run_m = cm;
   };
-  if (has_tail) add_part(1, NG + s, h);
-  if (gi >= 0) add_part(0, gi, mi * G + h);
+  if (active) {
+    if (has_tail) add_part(1, t0, t1, h);
+    if (gi >= 0) add_part(0, p0, p1, mi * G + h);
+  }
+  // combine the groups' partial merges (G x D floats each)
+  __shared__ float s_m[kCasMergeGroups][8], s_den[kCasMergeGroups][8];
+  __shared__ float s_num[kCasMergeGroups][8 * 128];
+  if (active) {
+    if (c == 0) {
+      s_m[pg][h] = run_m;
+      s_den[pg][h] = den;
+    }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = den > 0.f ? num[e] / den : 0.f;
+    for (int e = 0; e < 8; ++e) s_num[pg][h * D + 8 * c + e] = num[e];
+  }
+  __syncthreads();
+  if (!active || pg != 0) return;
+  float mx = s_m[0][h];
+  for (int k = 1; k < kCasMergeGroups; ++k) mx = fmaxf(mx, s_m[k][h]);
+  float dsum = 0.f, acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < kCasMergeGroups; ++k) {
+    const float w = s_m[k][h] > -INFINITY ? __builtin_amdgcn_exp2f(s_m[k][h] - mx) : 0.f;
+    dsum = fmaf(w, s_den[k][h], dsum);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc8[e] = fmaf(w, s_num[k][h * D + 8 * c + e], acc8[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = dsum > 0.f ? acc8[e] / dsum : 0.f;
   store_out8(m.out, orow * D + 8 * c, m.out_dtype, o);
 }
 
@@ -717,7 +752,7 @@ pa_status decode_cascade(const pa_kv_cache* cache, void* out, int out_code, cons
   m.state_o = p.state_o;
   m.row_map = p.row_map;
   m.num_groups = num_groups;
-  const int merge_threads = (G * D / 8 + 63) / 64 * 64;
+  const int merge_threads = (kCasMergeGroups * G * D / 8 + 63) / 64 * 64;
   hipLaunchKernelGGL(decode_cascade_merge_kernel, dim3(static_cast<uint32_t>(B) * hkv), dim3(merge_threads), 0, stream,
                      m);
   e = hipGetLastError();
