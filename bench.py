@@ -636,6 +636,8 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B * layers * K / el, 1),
         "decode_tokens_per_s_note": "sequences x layers per second (one query token per sequence per layer)",
+        "decode_tokens_per_s_call": round(B / call_s, 1),
+        "decode_tokens_per_s_call_note": "B / mean pa_decode call time (sequences one call decodes per second)",
         "pa_decode_us": round(call_s * 1e6, 2),
         "pa_decode_us_median": round(float(np.median(durs)) * 1e6, 2),
         "pa_decode_us_min": round(float(durs.min()) * 1e6, 2),
