@@ -243,6 +243,7 @@ struct SkUnit {
   int seq, tile, len, hg;
   int virt, sblk, soff;
   int pre, first, qsrc;
+  int qld;  // staged: the unit carries its segment's q rows (loaded, to be stored)
 };
 
 // NBUF: LDS stages of the staged path (2: units alternate between them);
@@ -280,6 +281,12 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   constexpr int kQBytes = G * D * 2;
   constexpr int kQL = STG ? (kQBytes > 1024 ? kQBytes / 1024 : 1) : C::kKSteps;
   constexpr int kQPitch = D * 2 + 16;  // bytes per q row in LDS (rows 4 banks apart)
+  // rows of a segment's output per pass through the wave's LDS region (the
+  // append variant's holds G x D floats, the others' G q rows: half the
+  // output rows); 0: stored from the registers
+  constexpr int kTileRows = CAS ? 0 : AP ? G : G >= 4 ? G / 2 : 0;
+  static_assert(kTileRows * D * 4 <= static_cast<int>(sk_wave_lds_floats(G, D, AP, CAS) * sizeof(float)),
+                "an output pass fits the wave's LDS region");
   static_assert(!STG || (CAS ? 16 * CT : G) * kQPitch <= static_cast<int>(sk_wave_lds_floats(G, D, AP, CAS) * sizeof(float)),
                 "the q rows fit the wave's LDS region");
   static_assert(!CAS || STG, "the cascade is built on the staged path");
@@ -582,12 +589,17 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     };
     const int g = un.hg * HW + wave;
     // the unit's q rows (B operand of S^T = K q^T); columns >= G repeat head
-    // 0 (finite logits whose weights are forced to zero). Every unit loads
-    // them (cache hits after the first unit of a segment), so each ring slot
-    // carries a fixed number of loads and no wait ever covers more than the
-    // slot it consumes.
+    // 0 (finite logits whose weights are forced to zero). Staged, they go
+    // to the wave's LDS rows, where they stay for the rest of the segment:
+    // only a segment's first unit (or the range's) needs them (measured:
+    // reloading them with every unit cost 2-4.5% on every workload). The
+    // other units still issue the loads, all lanes at one address (a single
+    // cache line), so every unit issues the same loads and the waits the
+    // compiler counts for a slot never cover the next slot's loads.
+    // Cascade prefix units take their rows from their own path.
+    un.qld = !past && (CAS ? (!un.pre && (x == u0 || un.first != 0)) : (x == u0 || un.tile == 0));
     {
-      // (cascade: a tail's batch row; a prefix unit loads row 0's, unused)
+      // (cascade: a tail's batch row)
       const int qseq = CAS ? (un.pre ? 0 : un.seq - NG) : un.seq;
       const int64_t head0 = static_cast<int64_t>(qseq) * p.num_q_heads + static_cast<int64_t>(g) * G;
       if constexpr (STG) {
@@ -596,7 +608,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
 #pragma unroll
         for (int i = 0; i < kQL; ++i) {
           const int f = (64 * i + lane) * 16;
-          qr[i] = *reinterpret_cast<const u32x4*>(qblk + (f < kQBytes ? f : f % kQBytes));
+          const char* qp = un.qld ? qblk + (f < kQBytes ? f : f % kQBytes) : qblk;
+          qr[i] = *reinterpret_cast<const u32x4*>(qp);
         }
       } else {
         const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (head0 + (col < G ? col : 0)) * D;
@@ -722,6 +735,28 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     for (int nt = 0; nt < kNT; ++nt) acc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   int pre_rows = 0;  // cascade: q rows of the current prefix segment
+  // the segment state back to empty, for the segment starting at the next unit
+  auto reset_segment = [&]() {
+    seg_first = false;
+    seg_begun = true;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      m_w[ct] = -INFINITY;
+      l_w[ct] = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) acc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // Staged path: the stores of a segment end (and the append's cache write)
+  // wait for the next unit and are issued once its rows have been written
+  // to the stage. A store issued while the next unit's loads are in flight
+  // holds up the wait for those loads until the store completes (the waits
+  // count loads and stores alike, in order); measured, 1-3 us per segment
+  // end, 7-8% of the call on the mixed-length batches.
+  // (pending when pf_seq / ap_blk >= 0; pf_bits: complete, ends here,
+  // begun, slot; ap_oh: token offset | head group << 8)
+  int pf_seq = -1, pf_hg = 0, pf_bits = 0, pf_rows = 0;
+  int ap_blk = -1, ap_oh = 0;
 
   // cascade: the q rows of prefix segment v for this wave's KV head in
   // head group hg, as the QK B operands of the two row tiles; row r =
@@ -757,17 +792,20 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   };
 
   // store the segment that just ended: final output, or a partial piece.
-  // Lane (col, j) holds rows 4j .. 4j + 3, head dim 16 nt + col. The append
-  // variant goes through its LDS output tile (16-byte stores); the others
-  // store straight from the accumulators (16 lanes write 16 consecutive
-  // dims; segment ends are rare, and this needs no LDS tile). Cascade: a
-  // completed segment leaves its partial (m, l, o) as state rows of its
-  // batch rows (part 0: prefix, 1: tail), a cut one a piece of RW rows.
-  auto flush = [&](int seg_seq, int seg_hg, bool complete, bool ends_here, int slot) {
+  // Lane (col, j) holds rows 4j .. 4j + 3, head dim 16 nt + col. Through
+  // the wave's LDS region (kTileRows rows at a time: all G rows when it
+  // holds G x D floats, the append variant's, else half), the rows leave as
+  // 16-byte stores; otherwise (G < 4, the cascade) each lane stores its
+  // elements (16 lanes write 16 consecutive dims). Cascade: a completed
+  // segment leaves its partial (m, l, o) as state rows of its batch rows
+  // (part 0: prefix, 1: tail), a cut one a piece of RW rows. begun: the
+  // segment starts inside the range; prows: a cascade prefix segment's q
+  // rows. The wave's q rows in LDS are overwritten.
+  auto flush = [&](int seg_seq, int seg_hg, bool complete, bool ends_here, int slot, bool begun, int prows) {
     const int64_t pbase = ((static_cast<int64_t>(w) * p.piece_slots + slot) * HW + wave) * RW;
     if constexpr (CAS) {
       const bool pre = seg_seq < NG;
-      const int nrows = pre ? pre_rows : G;
+      const int nrows = pre ? prows : G;
       const int64_t gq = static_cast<int64_t>(seg_hg * HW + wave) * G;
       const int m0 = pre ? s_goff[seg_seq] : 0;
       const int64_t part = pre ? 0 : 1;
@@ -808,49 +846,74 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       const float l_head = pair32_sum(pair16_sum(l_w[0]));
       const int64_t head0 =
           static_cast<int64_t>(seg_seq) * p.num_q_heads + static_cast<int64_t>(seg_hg * HW + wave) * G;
-      if constexpr (AP) {
+      // the rows' scales: v_scale / l on the lane holding row h's sum (lane
+      // h < 16), then to the lanes holding the row's outputs (a segment end
+      // is a short chain of dependent steps that every wave of the
+      // workgroup runs at once: measured, it cost ~2 us per segment end
+      // with a division per row and per-element conversions)
+      const float inv_h = p.v_scale * __builtin_amdgcn_rcpf(l_head);
+      float inv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = 4 * j + r;
-          const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
-          if (h < G) {
-            const float inv = p.v_scale / lr;
+      for (int r = 0; r < 4; ++r) inv[r] = __shfl(inv_h, 4 * j + r, 64);
+      if constexpr (kTileRows > 0) {
+        // element type of the rows: fp32 (pieces, float output), bf16, f16
+        const int odt = complete ? p.out_dtype : 2;
+        float* const o32 = complete ? static_cast<float*>(p.out) + head0 * D : p.piece_o + pbase * D;
+        uint16_t* const o16 = static_cast<uint16_t*>(p.out) + head0 * D;
+        constexpr int kPass = (kTileRows * D + 511) / 512;  // 8 elements per lane per pass
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) s_out[h * D + nt * 16 + col] = acc[0][nt][r] * inv;
-          }
-        }
-        wave_lds_sync();
-        for (int i = lane * 8; i < G * D; i += 64 * 8) {
-          float o[8];
+        for (int h0 = 0; h0 < G; h0 += kTileRows) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = s_out[i + e];
-          const int h = i / D, d = i % D;
-          if (complete) {
-            store_out8(p.out, (head0 + h) * D + d, p.out_dtype, o);
-          } else {
-            float* po = p.piece_o + (pbase + h) * D + d;
-            *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
-            *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
-          }
-        }
-        wave_lds_sync();
-      } else {
+          for (int r = 0; r < 4; ++r) {
+            const int h = 4 * j + r;
+            if (h >= h0 && h < h0 + kTileRows) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = 4 * j + r;
-          const float lr = __shfl(l_head, h, 64);  // lane h (row 0) holds head h's sum
-          if (h < G) {
-            const float inv = p.v_scale / lr;
-            if (complete) {
-#pragma unroll
-              for (int nt = 0; nt < kNT; ++nt)
-                store_out(p.out, (head0 + h) * D + nt * 16 + col, p.out_dtype, acc[0][nt][r] * inv);
-            } else {
-              float* po = p.piece_o + (pbase + h) * D + col;
-#pragma unroll
-              for (int nt = 0; nt < kNT; ++nt) po[nt * 16] = acc[0][nt][r] * inv;
+              for (int nt = 0; nt < kNT; ++nt) s_out[(h - h0) * D + nt * 16 + col] = acc[0][nt][r] * inv[r];
             }
           }
+          wave_lds_sync();
+#pragma unroll
+          for (int it = 0; it < kPass; ++it) {
+            const int i = it * 512 + lane * 8;
+            if ((kTileRows * D) % 512 == 0 || i < kTileRows * D) {
+              const f32x4 a = *reinterpret_cast<const f32x4*>(s_out + i);
+              const f32x4 b = *reinterpret_cast<const f32x4*>(s_out + i + 4);
+              const int64_t e = static_cast<int64_t>(h0) * D + i;  // element of the rows
+              if (odt == 2) {
+                *reinterpret_cast<f32x4*>(o32 + e) = a;
+                *reinterpret_cast<f32x4*>(o32 + e + 4) = b;
+              } else if (odt == 1) {
+                *reinterpret_cast<u32x4*>(o16 + e) =
+                    u32x4{pack2<BF16>(a.x, a.y), pack2<BF16>(a.z, a.w), pack2<BF16>(b.x, b.y), pack2<BF16>(b.z, b.w)};
+              } else {
+                *reinterpret_cast<u32x4*>(o16 + e) =
+                    u32x4{pack2<F16>(a.x, a.y), pack2<F16>(a.z, a.w), pack2<F16>(b.x, b.y), pack2<F16>(b.z, b.w)};
+              }
+            }
+          }
+          wave_lds_sync();
+        }
+      } else {
+        // one loop per element type: fp32 rows (pieces, or a float output),
+        // bf16 or f16 output rows
+        auto rows = [&](auto* o, auto cvt) {  // (G < 4)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int h = 4 * j + r;
+            if (h < G) {
+#pragma unroll
+              for (int nt = 0; nt < kNT; ++nt) o[h * D + nt * 16 + col] = cvt(acc[0][nt][r] * inv[r]);
+            }
+          }
+        };
+        if (!complete || p.out_dtype == 2) {
+          rows(complete ? static_cast<float*>(p.out) + head0 * D : p.piece_o + pbase * D, [](float v) { return v; });
+        } else if (p.out_dtype == 1) {
+          rows(static_cast<uint16_t*>(p.out) + head0 * D,
+               [](float v) { return static_cast<uint16_t>(f32_to_bf16_bits(v)); });
+        } else {
+          rows(static_cast<uint16_t*>(p.out) + head0 * D,
+               [](float v) { return static_cast<uint16_t>(f32_to_f16_bits(v)); });
         }
       }
       if (!complete && lane < G) {
@@ -863,7 +926,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       if (complete) {
         desc[0] = -1;
       } else {
-        if (seg_begun) desc[0] = static_cast<int32_t>(static_cast<uint32_t>(w) | (static_cast<uint32_t>(slot) << 31));
+        if (begun) desc[0] = static_cast<int32_t>(static_cast<uint32_t>(w) | (static_cast<uint32_t>(slot) << 31));
         if (ends_here) desc[1] = w;
       }
     }
@@ -923,13 +986,6 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     const char* v8_src = nullptr;
     char* const qs = reinterpret_cast<char*>(s_out);  // the wave's q rows (staged)
     if constexpr (STG) {
-      if (!upre) {
-#pragma unroll
-        for (int i = 0; i < kQL; ++i) {
-          const int f = (64 * i + lane) * 16;
-          if (f < kQBytes) *reinterpret_cast<u32x4*>(qs + (f / (D * 2)) * kQPitch + f % (D * 2)) = qr[i];
-        }
-      }
 #pragma unroll
       for (int i = 0; i < kKP; ++i) {
         *reinterpret_cast<u32x4*>(stg + st_k(st_r(i), st_cb(i))) = kr[i];
@@ -957,18 +1013,59 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       }
       // append: the new token's row of the head group into its cache slot,
       // from the workgroup's pieces of row 0 (every row of the virtual tile
-      // holds it)
+      // holds it). With two stages it waits for the next unit and is taken
+      // from the previous unit's stage, intact until this unit's barrier.
       if constexpr (AP) {
-        if (un.virt && static_cast<uint32_t>(un.sblk) < static_cast<uint32_t>(p.num_blocks)) {
-          const int64_t dst = static_cast<int64_t>(un.sblk) * blk_bytes + un.soff * tok_bytes +
-                              static_cast<int64_t>(un.hg) * S;
+        auto cache_row = [&](int blk, int off, int hg) {
+          return static_cast<int64_t>(blk) * blk_bytes + off * tok_bytes + static_cast<int64_t>(hg) * S;
+        };
+        if constexpr (NBUF == 2) {
+          if (ap_blk >= 0) {
+            const char* ps = stage + (x & 1 ? 0 : sbytes);  // the previous unit's stage
+            const int64_t dst = cache_row(ap_blk, ap_oh & 255, ap_oh >> 8);
 #pragma unroll
-          for (int i = 0; i < C::kKLoads; ++i) {
-            if (st_r(i) == 0) {
-              *reinterpret_cast<u32x4*>(const_cast<char*>(kbase) + dst + st_cb(i)) = kr[i];
-              *reinterpret_cast<u32x4*>(const_cast<char*>(vbase) + dst + st_cb(i)) = vr[i];
+            for (int i = 0; i < C::kKLoads; ++i) {
+              if (st_r(i) == 0) {
+                *reinterpret_cast<u32x4*>(const_cast<char*>(kbase) + dst + st_cb(i)) =
+                    *reinterpret_cast<const u32x4*>(ps + st_k(0, st_cb(i)));
+                *reinterpret_cast<u32x4*>(const_cast<char*>(vbase) + dst + st_cb(i)) =
+                    *reinterpret_cast<const u32x4*>(ps + (stage_v - stage) + st_cb(i));
+              }
+            }
+            ap_blk = -1;
+          }
+        }
+        if (un.virt && static_cast<uint32_t>(un.sblk) < static_cast<uint32_t>(p.num_blocks)) {
+          if (NBUF == 2 && x + 1 < u1) {
+            ap_blk = un.sblk;
+            ap_oh = un.soff | (un.hg << 8);
+          } else {
+            const int64_t dst = cache_row(un.sblk, un.soff, un.hg);
+#pragma unroll
+            for (int i = 0; i < C::kKLoads; ++i) {
+              if (st_r(i) == 0) {
+                *reinterpret_cast<u32x4*>(const_cast<char*>(kbase) + dst + st_cb(i)) = kr[i];
+                *reinterpret_cast<u32x4*>(const_cast<char*>(vbase) + dst + st_cb(i)) = vr[i];
+              }
             }
           }
+        }
+      }
+      // the previous unit's segment end, then this unit's q rows (if it
+      // starts a segment) into the wave's LDS region the end passed through.
+      // Both come after the stage writes, which wait for the last of this
+      // unit's loads: no store is issued before that wait, and the q rows
+      // (loaded first) have landed by then.
+      if (pf_seq >= 0) {
+        flush(pf_seq, pf_hg, pf_bits & 1, (pf_bits >> 1) & 1, pf_bits >> 3, (pf_bits >> 2) & 1, pf_rows);
+        reset_segment();
+        pf_seq = -1;
+      }
+      if (!upre && un.qld) {
+#pragma unroll
+        for (int i = 0; i < kQL; ++i) {
+          const int f = (64 * i + lane) * 16;
+          if (f < kQBytes) *reinterpret_cast<u32x4*>(qs + (f / (D * 2)) * kQPitch + f % (D * 2)) = qr[i];
         }
       }
       lds_barrier();
@@ -1200,20 +1297,20 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         }
       }
     }
-    // ---- end of a segment: store it, then start the next one at x + 1
+    // ---- end of a segment: store it (staged: with the next unit, see
+    // above), then start the next one at x + 1
     const bool seq_end = AP ? un.virt != 0 : un.tile == (L + TT - 1) / TT - 1;
     if (seq_end || x + 1 == u1) {
-      flush(un.seq, un.hg, seg_begun && seq_end, seq_end, seg_first ? 0 : 1);
-      if (x + 1 < u1) {
-        seg_first = false;
-        seg_begun = true;
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          m_w[ct] = -INFINITY;
-          l_w[ct] = 0.f;
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) acc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+      const bool complete = seg_begun && seq_end;
+      const int slot = seg_first ? 0 : 1;
+      if (STG && x + 1 < u1) {
+        pf_seq = un.seq;
+        pf_hg = un.hg;
+        pf_bits = (complete ? 1 : 0) | (seq_end ? 2 : 0) | (seg_begun ? 4 : 0) | (slot << 3);
+        pf_rows = pre_rows;
+      } else {
+        flush(un.seq, un.hg, complete, seq_end, slot, seg_begun, pre_rows);
+        if (x + 1 < u1) reset_segment();
       }
     }
   };
