@@ -1304,10 +1304,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
       const bool complete = seg_begun && seq_end;
       const int slot = seg_first ? 0 : 1;
       if (STG && x + 1 < u1) {
-        pf_seq = un.seq;
-        pf_hg = un.hg;
-        pf_bits = (complete ? 1 : 0) | (seq_end ? 2 : 0) | (seg_begun ? 4 : 0) | (slot << 3);
-        pf_rows = pre_rows;
+        // (uniform values; kept in scalar registers, so the stores branch
+        // on them as a wave)
+        pf_seq = __builtin_amdgcn_readfirstlane(un.seq);
+        pf_hg = __builtin_amdgcn_readfirstlane(un.hg);
+        pf_bits = __builtin_amdgcn_readfirstlane((complete ? 1 : 0) | (seq_end ? 2 : 0) | (seg_begun ? 4 : 0) |
+                                                 (slot << 3));
+        pf_rows = __builtin_amdgcn_readfirstlane(pre_rows);
       } else {
         flush(un.seq, un.hg, complete, seq_end, slot, seg_begun, pre_rows);
         if (x + 1 < u1) reset_segment();
