@@ -795,7 +795,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
   // Lane (col, j) holds rows 4j .. 4j + 3, head dim 16 nt + col. Through
   // the wave's LDS region (kTileRows rows at a time: all G rows when it
   // holds G x D floats, the append variant's, else half), the rows leave as
-  // 16-byte stores; otherwise (G < 4, the cascade) each lane stores its
+  // 4-element stores; otherwise (G < 4, the cascade) each lane stores its
   // elements (16 lanes write 16 consecutive dims). Cascade: a completed
   // segment leaves its partial (m, l, o) as state rows of its batch rows
   // (part 0: prefix, 1: tail), a cut one a piece of RW rows. begun: the
@@ -860,7 +860,9 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         const int odt = complete ? p.out_dtype : 2;
         float* const o32 = complete ? static_cast<float*>(p.out) + head0 * D : p.piece_o + pbase * D;
         uint16_t* const o16 = static_cast<uint16_t*>(p.out) + head0 * D;
-        constexpr int kPass = (kTileRows * D + 511) / 512;  // 8 elements per lane per pass
+        // 4 elements per lane per round: 16-byte LDS reads of consecutive
+        // lanes are conflict free
+        constexpr int kRounds = (kTileRows * D + 255) / 256;
 #pragma unroll
         for (int h0 = 0; h0 < G; h0 += kTileRows) {
 #pragma unroll
@@ -873,21 +875,17 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
           }
           wave_lds_sync();
 #pragma unroll
-          for (int it = 0; it < kPass; ++it) {
-            const int i = it * 512 + lane * 8;
-            if ((kTileRows * D) % 512 == 0 || i < kTileRows * D) {
+          for (int it = 0; it < kRounds; ++it) {
+            const int i = it * 256 + lane * 4;
+            if ((kTileRows * D) % 256 == 0 || i < kTileRows * D) {
               const f32x4 a = *reinterpret_cast<const f32x4*>(s_out + i);
-              const f32x4 b = *reinterpret_cast<const f32x4*>(s_out + i + 4);
               const int64_t e = static_cast<int64_t>(h0) * D + i;  // element of the rows
               if (odt == 2) {
                 *reinterpret_cast<f32x4*>(o32 + e) = a;
-                *reinterpret_cast<f32x4*>(o32 + e + 4) = b;
               } else if (odt == 1) {
-                *reinterpret_cast<u32x4*>(o16 + e) =
-                    u32x4{pack2<BF16>(a.x, a.y), pack2<BF16>(a.z, a.w), pack2<BF16>(b.x, b.y), pack2<BF16>(b.z, b.w)};
+                *reinterpret_cast<u32x2*>(o16 + e) = u32x2{pack2<BF16>(a.x, a.y), pack2<BF16>(a.z, a.w)};
               } else {
-                *reinterpret_cast<u32x4*>(o16 + e) =
-                    u32x4{pack2<F16>(a.x, a.y), pack2<F16>(a.z, a.w), pack2<F16>(b.x, b.y), pack2<F16>(b.z, b.w)};
+                *reinterpret_cast<u32x2*>(o16 + e) = u32x2{pack2<F16>(a.x, a.y), pack2<F16>(a.z, a.w)};
               }
             }
           }
