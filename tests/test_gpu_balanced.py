@@ -177,6 +177,36 @@ def test_16bit_outputs(gpu, wgs, out_dtype, cap):
     H.assert_close(got, H.oracle_contiguous(wl), what=f"{out_dtype} cap={cap}")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("cap", [None, 3])
+def test_staged_segment_ends(gpu, wgs, out_dtype, G, cap):
+    """Token-major V (the staged path) stores a segment that ends inside a
+    range together with the next unit: through the wave's LDS region, half
+    the group's rows a pass (G >= 4), or from the registers (G < 4). Short
+    sequences put several ends into one range, the cap cuts segments into
+    pieces; every output type."""
+    wgs(cap)
+    wl = synth.random_case(2600 + G, [5, 300, 17, 900, 1, 40, 2000, 33], 2 * G, 2, 128, 16, "bf16")
+    say(f"staged segment ends G={G} out={out_dtype} cap={cap}")
+    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout="token")
+    got = run_decode(wl, cache, tables, lens, max_ctx, BAL, out_dtype)
+    H.assert_close(got, H.oracle_contiguous(wl), what=f"G={G} {out_dtype} cap={cap}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_fp8_segment_ends_16bit_outputs(gpu, wgs, out_dtype, v_layout):
+    """fp8 pools (32-token units, staged either V layout) with 16-bit
+    outputs and many segment ends per range."""
+    wgs(5)
+    wl = synth.random_case(2700, [5, 300, 17, 900, 1, 40, 2000, 33], 16, 2, 128, 16, "fp8")
+    say(f"fp8 segment ends V {v_layout} out={out_dtype}")
+    _, cache, tables, lens, max_ctx = device_setup(wl, v_layout=v_layout)
+    got = run_decode(wl, cache, tables, lens, max_ctx, BAL, out_dtype)
+    H.assert_close(got, H.oracle_contiguous(wl), what=f"fp8 {v_layout} {out_dtype}")
+
+
 def test_agrees_with_partitions_and_is_deterministic(gpu):
     wl = synth.random_case(2600, [3, 129, 700, 1500, 4000], 32, 8, 128, 16, "bf16")
     _, cache, tables, lens, max_ctx = device_setup(wl, v_layout="dim")
