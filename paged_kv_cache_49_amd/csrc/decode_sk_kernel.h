@@ -980,6 +980,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
     // head dim 16 nt + d, its group's lanes pointing at rows 4j + lane / 4,
     // dims 4 (lane % 4) ..)
     u32x4 kop[STG ? kKP : 1];
+    u32x2 vpre[STG ? kNT : 1];  // staged: the unit's V operands (see below)
     const uint16_t* vt_src = nullptr;
     const char* v8_src = nullptr;
     char* const qs = reinterpret_cast<char*>(s_out);  // the wave's q rows (staged)
@@ -1082,6 +1083,20 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
           v8_src = stg_v + ((8 * j) / BS) * SV + wave * D * BS + (((8 * j) % BS) / 8) * (D * 8) + col * 8;
         }
       }
+      // the V operands of every n-tile (both q tiles of a cascade prefix
+      // unit use them), read with the K operands: issued one n-tile at a
+      // time inside the PV loop, each read's latency sat between two pairs
+      // of MFMAs
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        if constexpr (TT == 16) {
+          vpre[nt] = lds_read_tr16(vt_src + 16 * nt);
+        } else if constexpr (TV) {
+          vpre[nt] = lds_read_tr8(v8_src + 16 * nt);
+        } else {
+          vpre[nt] = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * 8);
+        }
+      }
     }
     // ---- PV masks: V elements past the end are zeroed (the pool may hold
     // anything there, and 0 * NaN would poison the sum)
@@ -1176,7 +1191,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         if constexpr (TT == 16) {
           u32x2 vop;
           if constexpr (TV) {
-            vop = lds_read_tr16(vt_src + 16 * nt);
+            vop = vpre[nt];
           } else {
             vop = vr[nt];
             if constexpr (AP) {
@@ -1193,13 +1208,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         } else {
           u32x2 b0, b1;  // the lane's 8 tokens of its head dim as bf16
           if constexpr (TV) {
-            const u32x2 codes = lds_read_tr8(v8_src + 16 * nt);  // tokens 8j .. 8j + 7, dim col
+            const u32x2 codes = vpre[nt];  // tokens 8j .. 8j + 7, dim col
             b0 = e4m3x4_to_bf16x4(codes.x);
             b1 = e4m3x4_to_bf16x4(codes.y);
           } else {
             u32x2 vv;
             if constexpr (STG) {
-              vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * 8);
+              vv = vpre[nt];
             } else {
               vv = vr[nt];
             }
@@ -1215,7 +1230,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         }
       }
     };
-    // PV of tile 1 alone (its own V operand reads)
+    // PV of tile 1 alone (the same V operands)
     auto pv1 = [&](const uint32_t (&phi)[CT][kE / 2], const uint32_t (&plo)[CT][kE / 2]) {
       if constexpr (CT > 1) {
 #pragma unroll
@@ -1223,7 +1238,7 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
           if constexpr (TT == 16) {
             u32x2 vop;
             if constexpr (TV) {
-              vop = lds_read_tr16(vt_src + 16 * nt);
+              vop = vpre[nt];
             } else {
               vop = vr[nt];
             }
@@ -1234,13 +1249,13 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
           } else {
             u32x2 b0, b1;
             if constexpr (TV) {
-              const u32x2 codes = lds_read_tr8(v8_src + 16 * nt);
+              const u32x2 codes = vpre[nt];
               b0 = e4m3x4_to_bf16x4(codes.x);
               b1 = e4m3x4_to_bf16x4(codes.y);
             } else {
               u32x2 vv;
               if constexpr (STG) {
-                vv = *reinterpret_cast<const u32x2*>(v8_src + nt * 16 * 8);
+                vv = vpre[nt];
               } else {
                 vv = vr[nt];
               }
