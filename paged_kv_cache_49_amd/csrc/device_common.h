@@ -82,6 +82,15 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
+// Four E4M3 bytes -> four f16 values (v_cvt_scalef32_pk_f16_fp8, exact: f16
+// holds every E4M3 value).
+__device__ __forceinline__ u32x2 e4m3x4_to_f16x4(uint32_t w) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const h2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // Four E4M3 bytes -> four fp32 values (v_cvt_pk_f32_fp8, exact).
 __device__ __forceinline__ f32x4 e4m3x4_to_f32x4(uint32_t w) {
   const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
