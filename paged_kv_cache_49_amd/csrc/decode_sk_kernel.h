@@ -1193,7 +1193,10 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
         }
       }
     };
-    // PV of tile 0
+    // PV of tile 0. 16-token units: one v_mfma_f32_16x16x32 per n-tile
+    // takes both weight terms, its k slots of lane group j holding the hi
+    // and then the lo weights of tokens 4j .. 4j + 3 against the same V
+    // values twice (the two 16x16x16 products in one instruction)
     auto pv = [&](auto ntc, const uint32_t (&phi)[CT][kE / 2], const uint32_t (&plo)[CT][kE / 2]) {
       constexpr int NT = decltype(ntc)::value;
 #pragma unroll
@@ -1212,8 +1215,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
           vop.y &= vmask[1];
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) {
-            acc[ct][nt] = mfma_16x16x16<QT>(u32x2{phi[ct][0], phi[ct][1]}, vop, acc[ct][nt]);
-            acc[ct][nt] = mfma_16x16x16<QT>(u32x2{plo[ct][0], plo[ct][1]}, vop, acc[ct][nt]);
+            acc[ct][nt] = mfma_16x16x32<QT>(u32x4{phi[ct][0], phi[ct][1], plo[ct][0], plo[ct][1]},
+                                            u32x4{vop.x, vop.y, vop.x, vop.y}, acc[ct][nt]);
           }
         } else {
           u32x2 b0, b1;  // the lane's 8 tokens of its head dim as bf16
@@ -1253,8 +1256,8 @@ __global__ __launch_bounds__(512) void paged_decode_sk_kernel(const SkParams p) 
             }
             vop.x &= vmask[0];
             vop.y &= vmask[1];
-            acc[1][nt] = mfma_16x16x16<QT>(u32x2{phi[1][0], phi[1][1]}, vop, acc[1][nt]);
-            acc[1][nt] = mfma_16x16x16<QT>(u32x2{plo[1][0], plo[1][1]}, vop, acc[1][nt]);
+            acc[1][nt] = mfma_16x16x32<QT>(u32x4{phi[1][0], phi[1][1], plo[1][0], plo[1][1]},
+                                           u32x4{vop.x, vop.y, vop.x, vop.y}, acc[1][nt]);
           } else {
             u32x2 b0, b1;
             if constexpr (TV) {
